@@ -1,0 +1,201 @@
+/*
+ * tq.h -- C ABI of the MI355X TurboQuant library (libtq.so).
+ *
+ * What the library computes (pages cited by title and section):
+ *  - [ebisuda] "TurboQuant: Google's 6x KV Cache Compression Algorithm Gains
+ *    Open-Source Momentum", section 第1段階：PolarQuant: rotate every vector by
+ *    a random orthogonal matrix (QR of a Gaussian matrix), then quantize each
+ *    rotated coordinate with a precomputed, data-oblivious Lloyd-Max codebook;
+ *    no per-block scale or zero point.
+ *  - [ebisuda] section 第2段階：QJL残差補正: a 1-bit QJL sketch of the residual
+ *    corrects the inner-product bias of stage 1.
+ *  - [hakusoku] "TurboQuant: 極限圧縮によるAI効率の再定義", section QJL: the
+ *    sketch keeps only sign bits and is paired with a full-precision query.
+ *  - [gemilab] TurboQuant technical deep dive, section Attention機構:
+ *    softmax(q K^T / sqrt(d_k)) V over the cached K/V.
+ *
+ * Conventions
+ *  - Pointers named d_* are device pointers owned by the caller; the library
+ *    never allocates, frees or retains them. Pointers named h_* are host
+ *    pointers, read or written only during the call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Hot
+ *    calls only enqueue work on it and never synchronize; tq_ctx_create and
+ *    tq_ctx_destroy synchronize the device.
+ *  - Every call validates its arguments before launching anything. On failure
+ *    it returns a non-zero tq_status, writes no output, and sets a message
+ *    readable with tq_last_error() (thread-local). A failed kernel launch
+ *    returns TQ_ERR_HIP. No C++ exception crosses this boundary.
+ *  - The library runs on the device that is current when tq_ctx_create is
+ *    called; later calls must be made with that device current.
+ *  - Dimensions: d is a multiple of 32 in [32, 4096]; the sketch has m = d
+ *    rows (the sizes the workloads fix); MSE bit widths are 1..4.
+ *
+ * Packed formats (fixed by this library; the pages fix none)
+ *  Keys (B MSE bits + 1 QJL bit per coordinate), one record per vector,
+ *  W = d/32 coordinate groups:
+ *    bits  uint32 [n][W][B+1]: for group w, word p < B holds bit p of the
+ *          codebook index of coordinate 32w+k at bit k; word B holds the QJL
+ *          sign bit of sketch row 32w+k at bit k (1 = non-negative).
+ *    norms float32 [n][2] = (||k||, ||r||), r the rotated-domain residual.
+ *    A zero vector has an all-zero record.
+ *  Values (B MSE bits per coordinate, no sketch), token-major 32-token
+ *  blocks:
+ *    bits  uint32 [n/32][d][B]: word [t/32][j][p] holds bit p of the index of
+ *          token t, coordinate j, at bit t%32.
+ *    norms float32 [n] = ||v||.
+ *  Bytes per token at d = 128: keys 56 (b=3) / 72 (b=4); 3-bit values 52.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_ARG = 1,          /* invalid argument (NULL, size, stride, dtype) */
+  TQ_ERR_UNSUPPORTED = 2,  /* valid but not supported (d, bits, heads)      */
+  TQ_ERR_CAPACITY = 3,     /* cache full / workspace too small              */
+  TQ_ERR_HIP = 4,          /* HIP runtime or launch failure                 */
+  TQ_ERR_NOMEM = 5         /* host or device allocation failed (ctx only)   */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+#define TQ_MAX_BITS 4
+#define TQ_MAX_DIM 4096
+
+/* Lloyd-Max codebook for one rotated coordinate of a d-dimensional unit
+ * vector ([ebisuda] 第1段階: the coordinate law is Beta, close to N(0,1/d)).
+ * Density used: f_d(x) = (1-x^2)^((d-3)/2) / B(1/2,(d-1)/2) on [-1,1].
+ * centroid[0..2^bits-1] ascending, fp32 of the fp64 fixed point (made exactly
+ * antisymmetric); boundary[i] = fp32 of the fp64 midpoint of centroids i,i+1;
+ * a coordinate y gets index #{i : boundary[i] <= y}. walsh[] holds the odd
+ * Walsh coefficients of the centroid table (see tq_ctx internals) and
+ * distortion the per-coordinate MSE of the stored table under f_d. */
+typedef struct {
+  int32_t d;
+  int32_t bits;
+  float centroid[16];
+  float boundary[15];
+  float walsh[8];
+  double distortion;
+} tq_codebook;
+
+/* Host only, deterministic, no GPU. d in [3, TQ_MAX_DIM], bits in [1, 4].
+ * Errors: TQ_ERR_ARG (out NULL), TQ_ERR_UNSUPPORTED (d or bits out of range). */
+tq_status tq_codebook_build(int32_t d, int32_t bits, tq_codebook *out);
+
+/* Host only, no GPU: the fp32 rotation tq_ctx_create would use for the
+ * row-major d x d float64 Gaussian matrix h_g (Householder QR, Q made unique
+ * by a positive diag(R), sign(0)=+1; [ebisuda] 第1段階), written row-major to
+ * h_out (d*d floats, caller-owned). d in [2, TQ_MAX_DIM].
+ * Errors: TQ_ERR_ARG (NULL), TQ_ERR_UNSUPPORTED (d). */
+tq_status tq_rotation_build(int32_t d, const double *h_g, float *h_out);
+
+/* Library context: the rotation Pi (d x d), the sketch S (d x d) and the
+ * codebooks for bits 1..4, on host and device. Immutable after creation and
+ * safe to share across streams on its device. */
+typedef struct tq_ctx tq_ctx;
+
+/* h_g_rot, h_g_sketch: row-major d x d float64 matrices of i.i.d. N(0,1)
+ * draws supplied by the caller (the random numbers the method draws).
+ * Pi = Q diag(sign(diag R)) from the Householder QR of h_g_rot (sign(0)=+1),
+ * rounded to fp32, used as y = Pi u ([ebisuda] 第1段階); S = fp32(h_g_sketch)
+ * ([gemilab] QJLの応用). Synchronizes the current device.
+ * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d), TQ_ERR_NOMEM, TQ_ERR_HIP. */
+tq_status tq_ctx_create(int32_t d, const double *h_g_rot, const double *h_g_sketch, tq_ctx **out);
+tq_status tq_ctx_destroy(tq_ctx *ctx);
+int32_t tq_ctx_dim(const tq_ctx *ctx);
+/* Host copies of the fp32 tables (either output may be NULL). */
+tq_status tq_ctx_export(const tq_ctx *ctx, float *h_rot, float *h_sketch);
+tq_status tq_ctx_codebook(const tq_ctx *ctx, int32_t bits, tq_codebook *out);
+
+/* A packed array of key or value records (formats above). */
+typedef struct {
+  uint32_t *bits;  /* d_: keys [n][W][B+1]; values [n/32][d][B]     */
+  float *norms;    /* d_: keys [n][2]; values [n]                    */
+  int64_t n;       /* record capacity; a multiple of 32 for values   */
+  int32_t mse_bits;/* B, 1..4                                        */
+  int32_t is_key;  /* 1 = key format (with QJL signs), 0 = values    */
+} tq_packed;
+
+/* Quantize vectors ([ebisuda] 第1段階 and, for keys, 第2段階).
+ * Input element (s, t, j) is at d_x[s*x_stream_stride + t*x_token_stride + j]
+ * (strides in elements, j contiguous) for s < n_streams, t < n_tokens.
+ * Its record goes to index s*out_stream_stride + out_offset + t of `out`.
+ * Keys: norm, rotation, codebook index, residual r (rotated domain), ||r||,
+ * sign(S r). Values: norm, rotation, codebook index; a value call writes
+ * whole 32-token blocks, so out_offset and out_stream_stride must be
+ * multiples of 32 (bits of tokens past n_tokens in the last block are 0).
+ * d_work: device workspace of tq_quantize_ws_bytes() bytes (keys only; may
+ * be NULL for values).
+ * Errors: TQ_ERR_ARG (NULL, negative sizes, records out of range, alignment),
+ * TQ_ERR_UNSUPPORTED (bits), TQ_ERR_CAPACITY (workspace), TQ_ERR_HIP. */
+size_t tq_quantize_ws_bytes(const tq_ctx *ctx, int64_t n_streams, int64_t n_tokens, int32_t is_key);
+tq_status tq_quantize_kv(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int64_t n_streams, int64_t n_tokens,
+                         int64_t x_stream_stride, int64_t x_token_stride, const tq_packed *out,
+                         int64_t out_stream_stride, int64_t out_offset, void *d_work, size_t work_bytes,
+                         void *stream);
+
+/* KV cache: records of stream (b, h) at [(b*kv_heads + h)*capacity + t].
+ * capacity is a multiple of 32. d_seq_len[b] is the number of valid tokens of
+ * every KV head of sequence b. host_max_len is an upper bound of all
+ * d_seq_len kept by the caller after prefill and advanced by
+ * tq_append_token; it sizes the decode launch and guards capacity. */
+typedef struct {
+  tq_packed k, v;
+  int32_t batch, kv_heads, capacity;
+  int32_t *d_seq_len;
+  int32_t host_max_len;
+} tq_kv_cache;
+
+/* Append one token per sequence: quantize d_k[b][h][:] / d_v[b][h][:]
+ * (contiguous [batch][kv_heads][d]) and write them at position d_seq_len[b]
+ * of stream (b, h), then increment d_seq_len[b] (O(1) append; the cache
+ * requirement is stated in the fractal KV-archive summary on gist.science).
+ * Increments cache->host_max_len.
+ * Errors: TQ_ERR_ARG, TQ_ERR_CAPACITY (host_max_len + 1 > capacity),
+ * TQ_ERR_HIP. */
+tq_status tq_append_token(const tq_ctx *ctx, tq_kv_cache *cache, const void *d_k, const void *d_v, tq_dtype dtype,
+                          void *stream);
+
+/* One decode step ([gemilab] Attention機構 with the estimator of [ebisuda]
+ * 第2段階): for every sequence b and query head h (KV head h / (q_heads /
+ * kv_heads)), out[b][h] = sum_t p_t v_hat_t with p = softmax(scale * s_t)
+ * over t < d_seq_len[b], s_t the TurboQuant score of q against key t, and
+ * v_hat_t = ||v_t|| Pi^T c[idx_t]. d_q: [batch][q_heads][d]; d_out: fp32
+ * [batch][q_heads][d]. q_heads must be a multiple of kv_heads. A sequence
+ * with length 0 gets a zero output.
+ * d_ws: workspace of tq_attention_decode_ws_bytes() bytes.
+ * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d != 128, group > 16),
+ * TQ_ERR_CAPACITY (workspace), TQ_ERR_HIP. */
+size_t tq_attention_decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads);
+tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_q, tq_dtype dtype,
+                              int32_t q_heads, float scale, float *d_out, void *d_ws, size_t ws_bytes,
+                              void *stream);
+
+/* Scores of nq queries against n packed keys ([ebisuda] 第2段階; [hakusoku]
+ * QJL: full-precision query, low-precision data):
+ *   s[q][t] = ||k_t|| (<Pi q, c[idx_t]> + sqrt(pi/2)/m ||r_t|| <S Pi q, 2 sigma_t - 1>).
+ * d_q: [nq][d]. If d_scores is non-NULL it receives fp32 [nq][n]. If topk > 0
+ * (<= 64), d_top_idx/d_top_val receive [nq][topk] ordered by (-score, index).
+ * d_ws: workspace of tq_scores_ws_bytes() bytes.
+ * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY (workspace),
+ * TQ_ERR_HIP. */
+size_t tq_scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores);
+tq_status tq_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t nq, const tq_packed *keys,
+                    float *d_scores, int32_t topk, int32_t *d_top_idx, float *d_top_val, void *d_ws,
+                    size_t ws_bytes, void *stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char *tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

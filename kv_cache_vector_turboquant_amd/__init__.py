@@ -1,0 +1,356 @@
+"""Python binding of libtq, the MI355X TurboQuant library.
+
+Argument marshalling only: every step of the hot path runs in the HIP kernels
+of libtq.so, reached through its C ABI (include/tq.h). torch supplies device
+memory and the current HIP stream. There is no CPU fallback: importing this
+package fails if libtq.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python kv_cache_vector_turboquant_amd/build.py` "
+        "(or __graft_entry__.build()); there is no CPU fallback")
+
+# torch ships its own HIP runtime. Loading torch first makes libtq.so bind to
+# that already-loaded runtime, so the process has exactly one HIP runtime and
+# torch-allocated pointers and streams are valid in libtq's kernels. (Loading
+# libtq.so first would bring in a second runtime that cannot open the device.)
+try:
+    import torch as _torch_mod  # noqa: F401
+except ImportError:  # pure C-ABI use without torch
+    _torch_mod = None
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+TQ_OK, TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_HIP, TQ_ERR_NOMEM = range(6)
+TQ_F32, TQ_BF16 = 0, 1
+_c_i32, _c_i64, _c_f32, _c_vp, _c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"tq status {status}: {msg}")
+        self.status = status
+
+
+class CCodebook(ctypes.Structure):
+    _fields_ = [("d", _c_i32), ("bits", _c_i32), ("centroid", ctypes.c_float * 16),
+                ("boundary", ctypes.c_float * 15), ("walsh", ctypes.c_float * 8), ("distortion", ctypes.c_double)]
+
+
+class CPacked(ctypes.Structure):
+    _fields_ = [("bits", _c_vp), ("norms", _c_vp), ("n", _c_i64), ("mse_bits", _c_i32), ("is_key", _c_i32)]
+
+
+class CCache(ctypes.Structure):
+    _fields_ = [("k", CPacked), ("v", CPacked), ("batch", _c_i32), ("kv_heads", _c_i32), ("capacity", _c_i32),
+                ("d_seq_len", _c_vp), ("host_max_len", _c_i32)]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_sig("tq_last_error", ctypes.c_char_p, [])
+_sig("tq_codebook_build", _c_i32, [_c_i32, _c_i32, ctypes.POINTER(CCodebook)])
+_sig("tq_rotation_build", _c_i32, [_c_i32, _c_vp, _c_vp])
+_sig("tq_ctx_create", _c_i32, [_c_i32, _c_vp, _c_vp, ctypes.POINTER(_c_vp)])
+_sig("tq_ctx_destroy", _c_i32, [_c_vp])
+_sig("tq_ctx_dim", _c_i32, [_c_vp])
+_sig("tq_ctx_export", _c_i32, [_c_vp, _c_vp, _c_vp])
+_sig("tq_ctx_codebook", _c_i32, [_c_vp, _c_i32, ctypes.POINTER(CCodebook)])
+_sig("tq_quantize_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64, _c_i32])
+_sig("tq_quantize_kv", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(CPacked),
+                                _c_i64, _c_i64, _c_vp, _c_sz, _c_vp])
+_sig("tq_append_token", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_i32, _c_vp])
+_sig("tq_attention_decode_ws_bytes", _c_sz, [_c_vp, ctypes.POINTER(CCache), _c_i32])
+_sig("tq_attention_decode", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp,
+                                     _c_sz, _c_vp])
+_sig("tq_scores_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64, _c_i32, _c_i32])
+_sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked), _c_vp, _c_i32, _c_vp, _c_vp,
+                           _c_vp, _c_sz, _c_vp])
+
+EXPORTED_SYMBOLS = [
+    "tq_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
+    "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_append_token", "tq_attention_decode_ws_bytes",
+    "tq_attention_decode", "tq_scores_ws_bytes", "tq_scores", "tq_last_error",
+]
+
+
+def last_error() -> str:
+    return (_lib.tq_last_error() or b"").decode()
+
+
+def _check(status: int):
+    if status != TQ_OK:
+        raise TQError(status, last_error())
+
+
+def lib():
+    """The loaded ctypes library (for tests of the raw C ABI)."""
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# Host-only calls
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Codebook:
+    d: int
+    bits: int
+    centroids: np.ndarray
+    boundaries: np.ndarray
+    walsh: np.ndarray
+    distortion: float
+
+
+def _cb_from_c(c: CCodebook) -> Codebook:
+    L = 1 << c.bits
+    return Codebook(c.d, c.bits, np.array(c.centroid[:L], np.float32), np.array(c.boundary[:L - 1], np.float32),
+                    np.array(c.walsh[:L // 2], np.float32), c.distortion)
+
+
+def codebook_build(d: int, bits: int) -> Codebook:
+    c = CCodebook()
+    _check(_lib.tq_codebook_build(d, bits, ctypes.byref(c)))
+    return _cb_from_c(c)
+
+
+def rotation_build(g: np.ndarray) -> np.ndarray:
+    """Host-only: the fp32 rotation the library derives from Gaussian matrix g."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    d = g.shape[0]
+    out = np.empty((d, d), np.float32)
+    _check(_lib.tq_rotation_build(d, g.ctypes.data, out.ctypes.data))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Context and packed arrays
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+class Context:
+    """Rotation, sketch and codebooks on the current device.
+
+    The Gaussian matrices the method draws come from `g_rot` / `g_sketch`
+    (float64 d x d host arrays); by default they are drawn from the seeded
+    generator in `synth` so that the CPU oracle can receive the same draws.
+    """
+
+    def __init__(self, d: int, seed: int = 0, g_rot: np.ndarray | None = None, g_sketch: np.ndarray | None = None):
+        if g_rot is None or g_sketch is None:
+            import synth
+            g_rot = synth.gaussian_matrix(seed, synth.TAG_ROTATION, d, d) if g_rot is None else g_rot
+            g_sketch = synth.gaussian_matrix(seed, synth.TAG_SKETCH, d, d) if g_sketch is None else g_sketch
+        gr = np.ascontiguousarray(g_rot, dtype=np.float64)
+        gs = np.ascontiguousarray(g_sketch, dtype=np.float64)
+        if gr.shape != (d, d) or gs.shape != (d, d):
+            raise ValueError("Gaussian matrices must be d x d")
+        h = _c_vp()
+        _check(_lib.tq_ctx_create(d, gr.ctypes.data, gs.ctypes.data, ctypes.byref(h)))
+        self._h = h
+        self.d = d
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            _lib.tq_ctx_destroy(self._h)
+            self._h = _c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def export(self):
+        rot = np.empty((self.d, self.d), np.float32)
+        sk = np.empty((self.d, self.d), np.float32)
+        _check(_lib.tq_ctx_export(self._h, rot.ctypes.data, sk.ctypes.data))
+        return rot, sk
+
+    def codebook(self, bits: int) -> Codebook:
+        c = CCodebook()
+        _check(_lib.tq_ctx_codebook(self._h, bits, ctypes.byref(c)))
+        return _cb_from_c(c)
+
+
+class Packed:
+    """Device arrays of packed key or value records (format in include/tq.h)."""
+
+    def __init__(self, n: int, d: int, bits: int, is_key: bool, device="cuda"):
+        torch = _torch()
+        if not is_key and n % 32:
+            raise ValueError("value capacity must be a multiple of 32")
+        W = d // 32
+        self.n, self.d, self.bits, self.is_key = n, d, bits, is_key
+        if is_key:
+            self.words = torch.zeros((n, W, bits + 1), dtype=torch.int32, device=device)
+            self.norms = torch.zeros((n, 2), dtype=torch.float32, device=device)
+        else:
+            self.words = torch.zeros((n // 32, d, bits), dtype=torch.int32, device=device)
+            self.norms = torch.zeros((n,), dtype=torch.float32, device=device)
+
+    def c(self) -> CPacked:
+        return CPacked(self.words.data_ptr(), self.norms.data_ptr(), self.n, self.bits, 1 if self.is_key else 0)
+
+    def host(self):
+        """(uint32 words, float32 norms) copied to host numpy arrays."""
+        return self.words.cpu().numpy().view(np.uint32), self.norms.cpu().numpy()
+
+
+def quantize_ws_bytes(ctx: Context, n_streams: int, n_tokens: int, is_key: bool) -> int:
+    return int(_lib.tq_quantize_ws_bytes(ctx.handle, n_streams, n_tokens, 1 if is_key else 0))
+
+
+def quantize_kv(ctx: Context, x, out: Packed, n_streams: int | None = None, n_tokens: int | None = None,
+                x_stream_stride: int | None = None, x_token_stride: int | None = None,
+                out_stream_stride: int = 0, out_offset: int = 0, work=None):
+    """Quantize x into `out`. x is [n, d] (one stream) or [streams, tokens, d]
+    (any strides with d contiguous)."""
+    torch = _torch()
+    if x.dim() == 2:
+        x3 = x.unsqueeze(0)
+    else:
+        x3 = x
+    S = x3.shape[0] if n_streams is None else n_streams
+    T = x3.shape[1] if n_tokens is None else n_tokens
+    xs = x3.stride(0) if x_stream_stride is None else x_stream_stride
+    xt = x3.stride(1) if x_token_stride is None else x_token_stride
+    if x3.stride(-1) != 1:
+        raise ValueError("the last dimension of x must be contiguous")
+    if out_stream_stride == 0:
+        out_stream_stride = T
+    ws = None
+    nbytes = 0
+    if out.is_key:
+        nbytes = quantize_ws_bytes(ctx, S, T, True)
+        ws = work if work is not None else torch.empty(max(nbytes, 4), dtype=torch.uint8, device=x.device)
+    cp = out.c()
+    _check(_lib.tq_quantize_kv(ctx.handle, x.data_ptr(), _dtype_code(x), S, T, xs, xt, ctypes.byref(cp),
+                               out_stream_stride, out_offset, ws.data_ptr() if ws is not None else None,
+                               ws.numel() if ws is not None else 0, _stream_ptr()))
+
+
+class KVCache:
+    """Packed KV cache: records of stream (b, h) at (b*kv_heads + h)*capacity + t."""
+
+    def __init__(self, batch: int, kv_heads: int, capacity: int, d: int, key_bits: int, value_bits: int,
+                 device="cuda"):
+        torch = _torch()
+        if capacity % 32:
+            raise ValueError("capacity must be a multiple of 32")
+        n = batch * kv_heads * capacity
+        self.k = Packed(n, d, key_bits, True, device)
+        self.v = Packed(n, d, value_bits, False, device)
+        self.seq_len = torch.zeros((batch,), dtype=torch.int32, device=device)
+        self.batch, self.kv_heads, self.capacity, self.d = batch, kv_heads, capacity, d
+        self.host_max_len = 0
+
+    def c(self) -> CCache:
+        return CCache(self.k.c(), self.v.c(), self.batch, self.kv_heads, self.capacity, self.seq_len.data_ptr(),
+                      self.host_max_len)
+
+    def prefill(self, ctx: Context, k, v):
+        """k, v: [batch, kv_heads, tokens, d] (d contiguous). Quantizes all tokens
+        to positions 0..tokens-1 and sets every sequence length to `tokens`."""
+        B, H, T, d = k.shape
+        assert (B, H) == (self.batch, self.kv_heads) and d == self.d and T <= self.capacity
+        assert k.is_contiguous() and v.is_contiguous(), "prefill expects contiguous [batch, kv_heads, tokens, d]"
+        kf = k.reshape(B * H, T, d)
+        vf = v.reshape(B * H, T, d)
+        quantize_kv(ctx, kf, self.k, n_streams=B * H, n_tokens=T, x_stream_stride=k.stride(1),
+                    x_token_stride=k.stride(2), out_stream_stride=self.capacity, out_offset=0)
+        quantize_kv(ctx, vf, self.v, n_streams=B * H, n_tokens=T, x_stream_stride=v.stride(1),
+                    x_token_stride=v.stride(2), out_stream_stride=self.capacity, out_offset=0)
+        self.seq_len.fill_(T)
+        self.host_max_len = T
+
+    def append(self, ctx: Context, k, v):
+        """k, v: [batch, kv_heads, d] contiguous, one new token per sequence."""
+        assert k.is_contiguous() and v.is_contiguous() and k.dtype == v.dtype
+        cc = self.c()
+        _check(_lib.tq_append_token(ctx.handle, ctypes.byref(cc), k.data_ptr(), v.data_ptr(), _dtype_code(k),
+                                    _stream_ptr()))
+        self.host_max_len = cc.host_max_len
+
+    def decode_ws_bytes(self, ctx: Context, q_heads: int) -> int:
+        cc = self.c()
+        return int(_lib.tq_attention_decode_ws_bytes(ctx.handle, ctypes.byref(cc), q_heads))
+
+    def decode(self, ctx: Context, q, scale: float | None = None, out=None, ws=None):
+        """q: [batch, q_heads, d] contiguous. Returns fp32 [batch, q_heads, d]."""
+        torch = _torch()
+        assert q.is_contiguous()
+        B, Hq, d = q.shape
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        need = self.decode_ws_bytes(ctx, Hq)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+        cc = self.c()
+        _check(_lib.tq_attention_decode(ctx.handle, ctypes.byref(cc), q.data_ptr(), _dtype_code(q), Hq,
+                                        float(scale), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr()))
+        return out
+
+
+def scores_ws_bytes(ctx: Context, nq: int, n: int, topk: int, want_scores: bool) -> int:
+    return int(_lib.tq_scores_ws_bytes(ctx.handle, nq, n, topk, 1 if want_scores else 0))
+
+
+def scores(ctx: Context, q, keys: Packed, want_scores: bool = True, topk: int = 0, ws=None):
+    """q: [nq, d] contiguous. Returns (scores [nq, n] or None, top_idx, top_val)."""
+    torch = _torch()
+    assert q.is_contiguous() and keys.is_key
+    nq = q.shape[0]
+    sc = torch.empty((nq, keys.n), dtype=torch.float32, device=q.device) if want_scores else None
+    ti = torch.empty((nq, max(topk, 1)), dtype=torch.int32, device=q.device) if topk else None
+    tv = torch.empty((nq, max(topk, 1)), dtype=torch.float32, device=q.device) if topk else None
+    need = scores_ws_bytes(ctx, nq, keys.n, topk, want_scores)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    kp = keys.c()
+    _check(_lib.tq_scores(ctx.handle, q.data_ptr(), _dtype_code(q), nq, ctypes.byref(kp),
+                          sc.data_ptr() if sc is not None else None, topk,
+                          ti.data_ptr() if ti is not None else None, tv.data_ptr() if tv is not None else None,
+                          ws.data_ptr(), ws.numel(), _stream_ptr()))
+    return sc, ti, tv

@@ -1,0 +1,494 @@
+// Host side of libtq: codebook construction, rotation setup, context
+// management and argument validation for every C-ABI entry point.
+//
+// Pages cited by title and section:
+//  [ebisuda] "TurboQuant: Google's 6x KV Cache Compression Algorithm Gains
+//            Open-Source Momentum", sections 第1段階 / 第2段階.
+//  [gemilab] TurboQuant technical deep dive, section QJLの応用.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string &msg) { g_last_error = msg; }
+
+tq_status fail(tq_status s, const std::string &msg) {
+  g_last_error = msg;
+  return s;
+}
+
+tq_status hip_fail(hipError_t e, const char *what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return TQ_ERR_HIP;
+}
+
+int walsh_subset(int bits, int i) {
+  int k = 0;
+  for (int pc = 1; pc <= bits; pc += 2)
+    for (int s = 1; s < (1 << bits); ++s)
+      if (__builtin_popcount(s) == pc) {
+        if (k == i) return s;
+        ++k;
+      }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Coordinate law of a rotated unit vector ([ebisuda] 第1段階: Beta, close to
+// N(0, 1/d)): f_d(x) = (1-x^2)^((d-3)/2) / B(1/2, (d-1)/2) on [-1, 1], i.e.
+// (1+x)/2 ~ Beta(a, a) with a = (d-1)/2.
+// ---------------------------------------------------------------------------
+
+static double log_beta(double a, double b) { return std::lgamma(a) + std::lgamma(b) - std::lgamma(a + b); }
+
+// Regularized incomplete beta I_x(a, b) from its continued fraction (DLMF
+// 8.17.22), evaluated with the modified Lentz method; the reflection
+// I_x(a,b) = 1 - I_{1-x}(b,a) keeps x below the convergence switch point.
+static double inc_beta(double a, double b, double x) {
+  if (x <= 0.0) return 0.0;
+  if (x >= 1.0) return 1.0;
+  if (x > (a + 1.0) / (a + b + 2.0)) return 1.0 - inc_beta(b, a, 1.0 - x);
+  const double tiny = 1e-300;
+  double f = 1.0, C = 1.0, D = 0.0;
+  for (int j = 1; j < 20000; ++j) {
+    double dj;
+    if (j & 1) {
+      int m = (j - 1) / 2;
+      dj = -(a + m) * (a + b + m) * x / ((a + 2.0 * m) * (a + 2.0 * m + 1.0));
+    } else {
+      int m = j / 2;
+      dj = m * (b - m) * x / ((a + 2.0 * m - 1.0) * (a + 2.0 * m));
+    }
+    D = 1.0 + dj * D;
+    if (std::fabs(D) < tiny) D = tiny;
+    C = 1.0 + dj / C;
+    if (std::fabs(C) < tiny) C = tiny;
+    D = 1.0 / D;
+    double delta = C * D;
+    f *= delta;
+    if (std::fabs(delta - 1.0) < 1e-16) break;
+  }
+  double logpre = a * std::log(x) + b * std::log1p(-x) - log_beta(a, b);
+  return std::exp(logpre) / (a * f);
+}
+
+static double coord_cdf(int d, double x) {
+  if (x <= -1.0) return 0.0;
+  if (x >= 1.0) return 1.0;
+  double a = 0.5 * (d - 1);
+  return inc_beta(a, a, 0.5 * (1.0 + x));
+}
+
+// (1 - x^2)^((d-1)/2) / B(1/2, (d-1)/2); antiderivative pieces of x f_d(x).
+static double w_fun(int d, double x) {
+  if (std::fabs(x) >= 1.0) return 0.0;
+  return std::exp(0.5 * (d - 1) * std::log1p(-x * x) - log_beta(0.5, 0.5 * (d - 1)));
+}
+
+// Integral of x f_d over [a, b]: (w(a) - w(b)) / (d - 1).
+static double first_moment(int d, double a, double b) { return (w_fun(d, a) - w_fun(d, b)) / (d - 1); }
+
+// Integral of x^2 f_d over [a, b], integrating by parts once:
+// [a w(a) - b w(b)]/(d-1) + B(1/2,(d+1)/2)/((d-1) B(1/2,(d-1)/2)) (F_{d+2}(b) - F_{d+2}(a)).
+static double second_moment(int d, double a, double b) {
+  double ratio = std::exp(log_beta(0.5, 0.5 * (d + 1)) - log_beta(0.5, 0.5 * (d - 1))) / (d - 1);
+  return (a * w_fun(d, a) - b * w_fun(d, b)) / (d - 1) + ratio * (coord_cdf(d + 2, b) - coord_cdf(d + 2, a));
+}
+
+static double coord_quantile(int d, double p) {
+  double lo = -1.0, hi = 1.0;
+  for (int it = 0; it < 200; ++it) {
+    double mid = 0.5 * (lo + hi);
+    if (coord_cdf(d, mid) < p) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+// Lloyd-Max ([ebisuda] 第1段階: continuous 1-D k-means minimizing MSE at a
+// given bit width; precomputed per bit width, data-oblivious). Start from the
+// centroids of 2^bits equal-mass cells, then alternate midpoint boundaries
+// and conditional-mean centroids until no centroid moves by 1e-14; finally
+// make the table exactly antisymmetric (f_d is even).
+static std::vector<double> lloyd_max(int d, int bits) {
+  const int L = 1 << bits;
+  std::vector<double> e(L + 1), c(L);
+  e[0] = -1.0;
+  e[L] = 1.0;
+  for (int i = 1; i < L; ++i) e[i] = coord_quantile(d, double(i) / L);
+  for (int i = 0; i < L; ++i)
+    c[i] = first_moment(d, e[i], e[i + 1]) / (coord_cdf(d, e[i + 1]) - coord_cdf(d, e[i]));
+  for (int it = 0; it < 200000; ++it) {
+    for (int i = 1; i < L; ++i) e[i] = 0.5 * (c[i - 1] + c[i]);
+    double delta = 0.0;
+    for (int i = 0; i < L; ++i) {
+      double mass = coord_cdf(d, e[i + 1]) - coord_cdf(d, e[i]);
+      double cn = first_moment(d, e[i], e[i + 1]) / mass;
+      delta = std::max(delta, std::fabs(cn - c[i]));
+      c[i] = cn;
+    }
+    if (delta < 1e-14) break;
+  }
+  std::vector<double> s(L);
+  for (int i = 0; i < L; ++i) s[i] = 0.5 * (c[i] - c[L - 1 - i]);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Rotation: Householder QR of the caller's Gaussian matrix, fp64.
+// ---------------------------------------------------------------------------
+
+// Returns Pi = Q diag(sign(diag R)) (sign(0) = +1), row-major, as fp32.
+static std::vector<float> rotation_from_gaussian(int n, const double *g) {
+  std::vector<double> A((size_t)n * n), Q((size_t)n * n, 0.0);  // column-major
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) A[(size_t)j * n + i] = g[(size_t)i * n + j];
+  std::vector<std::vector<double>> V(n);
+  std::vector<double> tau(n, 0.0), rdiag(n, 0.0);
+  const unsigned hw = std::max(1u, std::min(8u, std::thread::hardware_concurrency()));
+
+  auto apply = [&](double *M, int k, int j0, int j1) {  // columns [j0, j1) of M <- H_k M
+    const double *v = V[k].data();
+    const int len = n - k;
+    for (int j = j0; j < j1; ++j) {
+      double *col = M + (size_t)j * n + k;
+      double s = 0.0;
+      for (int i = 0; i < len; ++i) s += v[i] * col[i];
+      s *= tau[k];
+      for (int i = 0; i < len; ++i) col[i] -= s * v[i];
+    }
+  };
+  auto parallel_apply = [&](double *M, int k, int j0, int j1) {
+    int cols = j1 - j0;
+    if (cols < 256 || hw == 1) {
+      apply(M, k, j0, j1);
+      return;
+    }
+    std::vector<std::thread> th;
+    int per = (cols + hw - 1) / hw;
+    for (unsigned t = 0; t < hw; ++t) {
+      int a = j0 + (int)t * per, b = std::min(j1, a + per);
+      if (a < b) th.emplace_back(apply, M, k, a, b);
+    }
+    for (auto &t : th) t.join();
+  };
+
+  for (int k = 0; k < n; ++k) {
+    double *x = A.data() + (size_t)k * n + k;
+    const int len = n - k;
+    double nrm2 = 0.0;
+    for (int i = 0; i < len; ++i) nrm2 += x[i] * x[i];
+    double nrm = std::sqrt(nrm2);
+    double alpha = (x[0] > 0.0) ? -nrm : nrm;  // R_kk; v = x - alpha e1 avoids cancellation
+    V[k].assign(x, x + len);
+    V[k][0] -= alpha;
+    double vn2 = 0.0;
+    for (int i = 0; i < len; ++i) vn2 += V[k][i] * V[k][i];
+    tau[k] = vn2 > 0.0 ? 2.0 / vn2 : 0.0;
+    rdiag[k] = alpha;
+    if (k + 1 < n) parallel_apply(A.data(), k, k + 1, n);
+  }
+  for (int i = 0; i < n; ++i) Q[(size_t)i * n + i] = 1.0;
+  for (int k = n - 1; k >= 0; --k) parallel_apply(Q.data(), k, k, n);
+  std::vector<float> pi((size_t)n * n);
+  for (int j = 0; j < n; ++j) {
+    double sgn = rdiag[j] < 0.0 ? -1.0 : 1.0;
+    for (int i = 0; i < n; ++i) pi[(size_t)i * n + j] = (float)(sgn * Q[(size_t)j * n + i]);
+  }
+  return pi;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char *tq_last_error(void) { return g_last_error.c_str(); }
+
+tq_status tq_codebook_build(int32_t d, int32_t bits, tq_codebook *out) {
+  if (!out) return fail(TQ_ERR_ARG, "tq_codebook_build: out is NULL");
+  if (d < 3 || d > TQ_MAX_DIM) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook_build: d must be in [3, 4096]");
+  if (bits < 1 || bits > TQ_MAX_BITS) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook_build: bits must be in [1, 4]");
+  const int L = 1 << bits;
+  std::vector<double> c = lloyd_max(d, bits);
+  tq_codebook cb;
+  std::memset(&cb, 0, sizeof(cb));
+  cb.d = d;
+  cb.bits = bits;
+  for (int i = 0; i < L; ++i) cb.centroid[i] = (float)c[i];
+  for (int i = 0; i + 1 < L; ++i) cb.boundary[i] = (float)(0.5 * (c[i] + c[i + 1]));
+  // Odd Walsh coefficients of the stored table: c[idx] = sum_S w_S prod_{p in S}(2 b_p - 1).
+  for (int i = 0; i < (L >> 1); ++i) {
+    int S = walsh_subset(bits, i);
+    double acc = 0.0;
+    for (int idx = 0; idx < L; ++idx) {
+      int par = __builtin_popcount(~idx & S) & 1;  // number of zero bits in S
+      acc += (par ? -1.0 : 1.0) * (double)cb.centroid[idx];
+    }
+    cb.walsh[i] = (float)(acc / L);
+  }
+  // Analytic per-coordinate MSE of the stored tables.
+  double D = 0.0;
+  for (int i = 0; i < L; ++i) {
+    double a = i == 0 ? -1.0 : (double)cb.boundary[i - 1];
+    double b = i == L - 1 ? 1.0 : (double)cb.boundary[i];
+    double ci = cb.centroid[i];
+    double m0 = coord_cdf(d, b) - coord_cdf(d, a);
+    D += second_moment(d, a, b) - 2.0 * ci * first_moment(d, a, b) + ci * ci * m0;
+  }
+  cb.distortion = D;
+  *out = cb;
+  return TQ_OK;
+}
+
+tq_status tq_rotation_build(int32_t d, const double *h_g, float *h_out) {
+  if (!h_g || !h_out) return fail(TQ_ERR_ARG, "tq_rotation_build: NULL argument");
+  if (d < 2 || d > TQ_MAX_DIM) return fail(TQ_ERR_UNSUPPORTED, "tq_rotation_build: d must be in [2, 4096]");
+  std::vector<float> pi = rotation_from_gaussian(d, h_g);
+  std::memcpy(h_out, pi.data(), pi.size() * sizeof(float));
+  return TQ_OK;
+}
+
+tq_status tq_ctx_create(int32_t d, const double *h_g_rot, const double *h_g_sketch, tq_ctx **out) {
+  if (!out || !h_g_rot || !h_g_sketch) return fail(TQ_ERR_ARG, "tq_ctx_create: NULL argument");
+  *out = nullptr;
+  if (d < 32 || d > TQ_MAX_DIM || (d % 32) != 0)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_ctx_create: d must be a multiple of 32 in [32, 4096]");
+  tq_ctx *ctx = new (std::nothrow) tq_ctx();
+  if (!ctx) return fail(TQ_ERR_NOMEM, "tq_ctx_create: host allocation failed");
+  ctx->d = d;
+  hipError_t e = hipGetDevice(&ctx->device);
+  if (e != hipSuccess) {
+    delete ctx;
+    return hip_fail(e, "tq_ctx_create: hipGetDevice");
+  }
+  ctx->rot = rotation_from_gaussian(d, h_g_rot);
+  ctx->sketch.resize((size_t)d * d);
+  for (size_t i = 0; i < (size_t)d * d; ++i) ctx->sketch[i] = (float)h_g_sketch[i];
+  std::memset(&ctx->h_tables, 0, sizeof(ctx->h_tables));
+  for (int b = 1; b <= TQ_MAX_BITS; ++b) {
+    tq_status s = tq_codebook_build(d, b, &ctx->cb[b]);
+    if (s != TQ_OK) {
+      delete ctx;
+      return s;
+    }
+    const int L = 1 << b;
+    for (int i = 0; i < L; ++i) ctx->h_tables.centroid[b][i] = ctx->cb[b].centroid[i];
+    for (int i = 0; i + 1 < L; ++i) ctx->h_tables.boundary[b][i] = ctx->cb[b].boundary[i];
+    for (int i = L - 1; i < 16; ++i) ctx->h_tables.boundary[b][i] = INFINITY;
+    for (int i = 0; i < (L >> 1); ++i) ctx->h_tables.walsh[b][i] = ctx->cb[b].walsh[i];
+    ctx->h_tables.ctop[b] = ctx->cb[b].centroid[L - 1];
+  }
+  const size_t mat = (size_t)d * d * sizeof(float);
+  if ((e = hipMalloc(&ctx->d_rot, mat)) != hipSuccess || (e = hipMalloc(&ctx->d_sketch, mat)) != hipSuccess ||
+      (e = hipMalloc(&ctx->d_tables, sizeof(DeviceTables))) != hipSuccess) {
+    tq_ctx_destroy(ctx);
+    return fail(TQ_ERR_NOMEM, std::string("tq_ctx_create: hipMalloc: ") + hipGetErrorString(e));
+  }
+  if ((e = hipMemcpy(ctx->d_rot, ctx->rot.data(), mat, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(ctx->d_sketch, ctx->sketch.data(), mat, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(ctx->d_tables, &ctx->h_tables, sizeof(DeviceTables), hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipDeviceSynchronize()) != hipSuccess) {
+    tq_ctx_destroy(ctx);
+    return hip_fail(e, "tq_ctx_create: upload");
+  }
+  *out = ctx;
+  return TQ_OK;
+}
+
+tq_status tq_ctx_destroy(tq_ctx *ctx) {
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_ctx_destroy: NULL ctx");
+  (void)hipDeviceSynchronize();
+  if (ctx->d_rot) (void)hipFree(ctx->d_rot);
+  if (ctx->d_sketch) (void)hipFree(ctx->d_sketch);
+  if (ctx->d_tables) (void)hipFree(ctx->d_tables);
+  delete ctx;
+  return TQ_OK;
+}
+
+int32_t tq_ctx_dim(const tq_ctx *ctx) { return ctx ? ctx->d : 0; }
+
+tq_status tq_ctx_export(const tq_ctx *ctx, float *h_rot, float *h_sketch) {
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_ctx_export: NULL ctx");
+  if (h_rot) std::memcpy(h_rot, ctx->rot.data(), ctx->rot.size() * sizeof(float));
+  if (h_sketch) std::memcpy(h_sketch, ctx->sketch.data(), ctx->sketch.size() * sizeof(float));
+  return TQ_OK;
+}
+
+tq_status tq_ctx_codebook(const tq_ctx *ctx, int32_t bits, tq_codebook *out) {
+  if (!ctx || !out) return fail(TQ_ERR_ARG, "tq_ctx_codebook: NULL argument");
+  if (bits < 1 || bits > TQ_MAX_BITS) return fail(TQ_ERR_UNSUPPORTED, "tq_ctx_codebook: bits must be in [1, 4]");
+  *out = ctx->cb[bits];
+  return TQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Hot-path entry points: validation, then one asynchronous launch sequence.
+// ---------------------------------------------------------------------------
+
+static tq_status check_device(const tq_ctx *ctx, const char *fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (dev != ctx->device) return fail(TQ_ERR_ARG, std::string(fn) + ": current device differs from the context's");
+  return TQ_OK;
+}
+
+static tq_status check_packed(const tq_ctx *ctx, const tq_packed *p, int want_key, const char *fn) {
+  if (!p || !p->bits || !p->norms) return fail(TQ_ERR_ARG, std::string(fn) + ": packed array or its pointers NULL");
+  if (p->mse_bits < 1 || p->mse_bits > TQ_MAX_BITS)
+    return fail(TQ_ERR_UNSUPPORTED, std::string(fn) + ": mse_bits must be in [1, 4]");
+  if ((p->is_key != 0) != (want_key != 0))
+    return fail(TQ_ERR_ARG, std::string(fn) + (want_key ? ": expected a key array" : ": expected a value array"));
+  if (p->n < 0) return fail(TQ_ERR_ARG, std::string(fn) + ": negative record count");
+  if (!p->is_key && (p->n % 32) != 0) return fail(TQ_ERR_ARG, std::string(fn) + ": value capacity must be a multiple of 32");
+  (void)ctx;
+  return TQ_OK;
+}
+
+size_t tq_quantize_ws_bytes(const tq_ctx *ctx, int64_t n_streams, int64_t n_tokens, int32_t is_key) {
+  if (!ctx || !is_key || n_streams <= 0 || n_tokens <= 0) return 0;
+  return (size_t)n_streams * (size_t)n_tokens * (size_t)ctx->d * sizeof(float);
+}
+
+tq_status tq_quantize_kv(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int64_t n_streams, int64_t n_tokens,
+                         int64_t x_stream_stride, int64_t x_token_stride, const tq_packed *out,
+                         int64_t out_stream_stride, int64_t out_offset, void *d_work, size_t work_bytes,
+                         void *stream) {
+  const char *fn = "tq_quantize_kv";
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_quantize_kv: NULL ctx");
+  if (!out) return fail(TQ_ERR_ARG, "tq_quantize_kv: NULL out");
+  tq_status s = check_packed(ctx, out, out->is_key, fn);
+  if (s != TQ_OK) return s;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_quantize_kv: dtype must be TQ_F32 or TQ_BF16");
+  if (n_streams < 0 || n_tokens < 0 || out_offset < 0 || out_stream_stride < 0 || x_stream_stride < 0 ||
+      x_token_stride < 0)
+    return fail(TQ_ERR_ARG, "tq_quantize_kv: negative size, stride or offset");
+  if (n_streams == 0 || n_tokens == 0) return TQ_OK;
+  if (!d_x) return fail(TQ_ERR_ARG, "tq_quantize_kv: NULL input");
+  if (x_token_stride < ctx->d && n_tokens > 1) return fail(TQ_ERR_ARG, "tq_quantize_kv: token stride < d");
+  if ((x_token_stride % 8) != 0 || (x_stream_stride % 8) != 0 || ((uintptr_t)d_x % 16) != 0)
+    return fail(TQ_ERR_ARG, "tq_quantize_kv: input must be 16-byte aligned with strides that are multiples of 8");
+  if (n_streams > 65535) return fail(TQ_ERR_UNSUPPORTED, "tq_quantize_kv: at most 65535 streams per call");
+  if (n_streams > 1 && out_stream_stride < out_offset + n_tokens)
+    return fail(TQ_ERR_ARG, "tq_quantize_kv: output streams overlap (out_stream_stride < out_offset + n_tokens)");
+  int64_t last = (n_streams - 1) * out_stream_stride + out_offset + n_tokens;
+  if (last > out->n) return fail(TQ_ERR_ARG, "tq_quantize_kv: records past the end of the output array");
+  if (!out->is_key && ((out_offset % 32) != 0 || (out_stream_stride % 32) != 0))
+    return fail(TQ_ERR_ARG, "tq_quantize_kv: value offsets and stream strides must be multiples of 32");
+  if (out->is_key) {
+    size_t need = tq_quantize_ws_bytes(ctx, n_streams, n_tokens, 1);
+    if (!d_work || work_bytes < need)
+      return fail(TQ_ERR_CAPACITY, "tq_quantize_kv: key workspace smaller than tq_quantize_ws_bytes()");
+  }
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  hipError_t e;
+  if (out->is_key)
+    e = launch_quantize_keys(ctx, d_x, dtype == TQ_BF16, n_streams, n_tokens, x_stream_stride, x_token_stride, out,
+                             out_stream_stride, out_offset, (float *)d_work, (hipStream_t)stream);
+  else
+    e = launch_quantize_values(ctx, d_x, dtype == TQ_BF16, n_streams, n_tokens, x_stream_stride, x_token_stride,
+                               out, out_stream_stride, out_offset, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
+}
+
+static tq_status check_cache(const tq_ctx *ctx, const tq_kv_cache *c, const char *fn) {
+  if (!c) return fail(TQ_ERR_ARG, std::string(fn) + ": NULL cache");
+  tq_status s = check_packed(ctx, &c->k, 1, fn);
+  if (s == TQ_OK) s = check_packed(ctx, &c->v, 0, fn);
+  if (s != TQ_OK) return s;
+  if (c->batch <= 0 || c->kv_heads <= 0 || c->capacity <= 0 || (c->capacity % 32) != 0)
+    return fail(TQ_ERR_ARG, std::string(fn) + ": batch, kv_heads > 0 and capacity a positive multiple of 32 required");
+  int64_t recs = (int64_t)c->batch * c->kv_heads * c->capacity;
+  if (c->k.n < recs || c->v.n < recs) return fail(TQ_ERR_ARG, std::string(fn) + ": record arrays smaller than batch*kv_heads*capacity");
+  if (!c->d_seq_len) return fail(TQ_ERR_ARG, std::string(fn) + ": NULL d_seq_len");
+  if (c->host_max_len < 0 || c->host_max_len > c->capacity)
+    return fail(TQ_ERR_ARG, std::string(fn) + ": host_max_len outside [0, capacity]");
+  return TQ_OK;
+}
+
+tq_status tq_append_token(const tq_ctx *ctx, tq_kv_cache *cache, const void *d_k, const void *d_v, tq_dtype dtype,
+                          void *stream) {
+  const char *fn = "tq_append_token";
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_append_token: NULL ctx");
+  tq_status s = check_cache(ctx, cache, fn);
+  if (s != TQ_OK) return s;
+  if (!d_k || !d_v) return fail(TQ_ERR_ARG, "tq_append_token: NULL input");
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_append_token: dtype must be TQ_F32 or TQ_BF16");
+  if (ctx->d != 128) return fail(TQ_ERR_UNSUPPORTED, "tq_append_token: d must be 128");
+  if (cache->host_max_len + 1 > cache->capacity) return fail(TQ_ERR_CAPACITY, "tq_append_token: cache is full");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  hipError_t e = launch_append(ctx, cache, d_k, d_v, dtype == TQ_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  cache->host_max_len += 1;
+  return TQ_OK;
+}
+
+size_t tq_attention_decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads) {
+  if (!ctx || !cache || q_heads <= 0 || cache->kv_heads <= 0 || (q_heads % cache->kv_heads) != 0) return 0;
+  return decode_ws_bytes(ctx, cache, q_heads, nullptr, nullptr);
+}
+
+tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_q, tq_dtype dtype,
+                              int32_t q_heads, float scale, float *d_out, void *d_ws, size_t ws_bytes,
+                              void *stream) {
+  const char *fn = "tq_attention_decode";
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_attention_decode: NULL ctx");
+  tq_status s = check_cache(ctx, cache, fn);
+  if (s != TQ_OK) return s;
+  if (!d_q || !d_out) return fail(TQ_ERR_ARG, "tq_attention_decode: NULL query or output");
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_attention_decode: dtype must be TQ_F32 or TQ_BF16");
+  if (q_heads <= 0 || (q_heads % cache->kv_heads) != 0)
+    return fail(TQ_ERR_ARG, "tq_attention_decode: q_heads must be a positive multiple of kv_heads");
+  if (q_heads / cache->kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_attention_decode: at most 16 query heads per KV head");
+  if (ctx->d != 128) return fail(TQ_ERR_UNSUPPORTED, "tq_attention_decode: d must be 128");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_ARG, "tq_attention_decode: scale must be finite");
+  size_t need = tq_attention_decode_ws_bytes(ctx, cache, q_heads);
+  if (!d_ws || ws_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_attention_decode: workspace smaller than tq_attention_decode_ws_bytes()");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  hipError_t e = launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
+}
+
+size_t tq_scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores) {
+  if (!ctx || nq <= 0 || n <= 0 || topk < 0) return 0;
+  return scores_ws_bytes(ctx, nq, n, topk, want_scores);
+}
+
+tq_status tq_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t nq, const tq_packed *keys,
+                    float *d_scores, int32_t topk, int32_t *d_top_idx, float *d_top_val, void *d_ws,
+                    size_t ws_bytes, void *stream) {
+  const char *fn = "tq_scores";
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_scores: NULL ctx");
+  tq_status s = check_packed(ctx, keys, 1, fn);
+  if (s != TQ_OK) return s;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_scores: dtype must be TQ_F32 or TQ_BF16");
+  if (nq < 0 || topk < 0) return fail(TQ_ERR_ARG, "tq_scores: negative nq or topk");
+  if (topk > 64) return fail(TQ_ERR_UNSUPPORTED, "tq_scores: topk must be <= 64");
+  if (topk > keys->n) return fail(TQ_ERR_ARG, "tq_scores: topk larger than the number of keys");
+  if (!d_scores && topk == 0) return fail(TQ_ERR_ARG, "tq_scores: nothing requested (no scores, topk = 0)");
+  if (topk > 0 && (!d_top_idx || !d_top_val)) return fail(TQ_ERR_ARG, "tq_scores: NULL top-k output");
+  if (nq == 0 || keys->n == 0) return TQ_OK;
+  if (!d_q) return fail(TQ_ERR_ARG, "tq_scores: NULL queries");
+  if (((uintptr_t)d_q % 16) != 0) return fail(TQ_ERR_ARG, "tq_scores: queries must be 16-byte aligned");
+  if ((keys->n + 127) / 128 > 65535 * 1024LL) return fail(TQ_ERR_UNSUPPORTED, "tq_scores: too many keys");
+  size_t need = scores_ws_bytes(ctx, nq, keys->n, topk, d_scores != nullptr);
+  if (!d_ws || ws_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_scores: workspace smaller than tq_scores_ws_bytes()");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  hipError_t e = launch_scores(ctx, d_q, dtype == TQ_BF16, nq, keys, d_scores, topk, d_top_idx, d_top_val, d_ws,
+                               (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
+}
+
+}  // extern "C"

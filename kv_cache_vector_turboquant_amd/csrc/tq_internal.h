@@ -1,0 +1,64 @@
+// Internal declarations shared by the host code and the HIP kernels of libtq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+// Per bit width (index = bits, 1..4): stored codebook tables in the layout the
+// kernels read. walsh[] are the odd Walsh coefficients of the centroid table,
+// in the subset order of walsh_subset(bits, i); ctop = centroid[2^bits - 1]
+// (the sum of all walsh coefficients).
+struct DeviceTables {
+  float centroid[TQ_MAX_BITS + 1][16];
+  float boundary[TQ_MAX_BITS + 1][16];
+  float walsh[TQ_MAX_BITS + 1][8];
+  float ctop[TQ_MAX_BITS + 1];
+};
+
+// i-th odd-cardinality subset of {0..bits-1} (as a bit mask), ordered by
+// (popcount, value); there are 2^(bits-1) of them.
+int walsh_subset(int bits, int i);
+
+void set_error(const std::string &msg);
+tq_status fail(tq_status s, const std::string &msg);
+tq_status hip_fail(hipError_t e, const char *what);
+
+}  // namespace tq
+
+struct tq_ctx {
+  int32_t d = 0;
+  int device = 0;
+  std::vector<float> rot;     // host fp32 Pi, row-major d x d
+  std::vector<float> sketch;  // host fp32 S, row-major d x d
+  tq_codebook cb[TQ_MAX_BITS + 1];
+  float *d_rot = nullptr;
+  float *d_sketch = nullptr;
+  tq::DeviceTables *d_tables = nullptr;
+  tq::DeviceTables h_tables;
+};
+
+namespace tq {
+// Kernel launchers (tq_kernels.hip). All return hipSuccess or the launch error.
+hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams, int64_t n_tokens,
+                                int64_t xs, int64_t xt, const tq_packed *out, int64_t os, int64_t oo, float *work,
+                                hipStream_t st);
+hipError_t launch_quantize_values(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams,
+                                  int64_t n_tokens, int64_t xs, int64_t xt, const tq_packed *out, int64_t os,
+                                  int64_t oo, hipStream_t st);
+hipError_t launch_append(const tq_ctx *ctx, const tq_kv_cache *cache, const void *k, const void *v, int is_bf16,
+                         hipStream_t st);
+size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int *chunk_out,
+                       int *nchunks_out);
+hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
+                         float scale, float *out, void *ws, hipStream_t st);
+size_t scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores);
+hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_packed *keys,
+                         float *scores, int32_t topk, int32_t *top_idx, float *top_val, void *ws, hipStream_t st);
+}  // namespace tq

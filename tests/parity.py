@@ -1,0 +1,75 @@
+"""Comparison rules between GPU results and the oracle (test helpers).
+
+Packed codes and sign bits: bit-exact, except at most 1e-4 of coordinates
+whose oracle value lies within 1e-5 of a decision boundary (codes: the fp64
+rotated coordinate y against the stored boundaries; signs: the fp64 sketch
+value z against 0). A vector with an excused code flip has a different
+residual, so its sign bits and ||r|| are not compared (the cascade).
+Scores: |ds| <= 1e-3 |s| or |ds| <= 1e-6 ||q|| ||x||. Attention: 2e-3 max-abs.
+"""
+import numpy as np
+
+from oracle import turboquant as T
+
+BAND = 1e-5
+MAX_FRAC = 1e-4
+
+
+def boundary_distance(y: np.ndarray, cb) -> np.ndarray:
+    b = cb.boundaries.astype(np.float64)
+    return np.min(np.abs(y[..., None] - b), axis=-1)
+
+
+def check_codes(g_idx, enc, cb, what="codes"):
+    """Returns the boolean (n,) mask of vectors with an excused code flip."""
+    flips = g_idx != enc.idx
+    nflip = int(flips.sum())
+    if nflip:
+        dist = boundary_distance(enc.y, cb)
+        bad = flips & ~(dist < BAND)
+        assert not bad.any(), f"{what}: {int(bad.sum())} code mismatches outside the boundary band"
+        assert np.all(np.abs(g_idx[flips] - enc.idx[flips]) == 1), f"{what}: non-adjacent code flip"
+    assert nflip <= MAX_FRAC * g_idx.size, f"{what}: {nflip} excused flips > {MAX_FRAC} of {g_idx.size}"
+    return flips.any(axis=1)
+
+
+def check_key_records(words, norms, enc, cb, bits, d):
+    g_idx, g_sig = T.unpack_keys(words, d, bits)
+    cascade = check_codes(g_idx, enc, cb, "key codes")
+    live = ~cascade
+    sflip = (g_sig != enc.sigma) & live[:, None]
+    if sflip.any():
+        bad = sflip & ~(np.abs(enc.z) < BAND)
+        assert not bad.any(), f"sign mismatches outside the band: {int(bad.sum())}"
+    assert sflip.sum() <= MAX_FRAC * g_sig.size
+    n_ref = enc.norm
+    assert np.all(np.abs(norms[:, 0] - n_ref) <= 2e-6 * n_ref + 1e-30), "||k|| mismatch"
+    rr = enc.rho[live]
+    assert np.all(np.abs(norms[live, 1] - rr) <= 2e-5 * rr + 1e-7), "||r|| mismatch"
+    return int(cascade.sum()), int(sflip.sum())
+
+
+def check_value_records(words, norms, enc, cb, bits, d, n):
+    g_idx = T.unpack_values(words, d, bits, n)
+    check_codes(g_idx, enc, cb, "value codes")
+    n_ref = enc.norm
+    assert np.all(np.abs(norms[:n] - n_ref) <= 2e-6 * n_ref + 1e-30), "||v|| mismatch"
+
+
+def check_scores(s_gpu, s_ref, qnorm, xnorm):
+    tol = np.maximum(1e-3 * np.abs(s_ref), 1e-6 * np.outer(qnorm, xnorm))
+    err = np.abs(s_gpu - s_ref)
+    assert np.all(err <= tol), f"score mismatch: worst excess {np.max(err - tol)}"
+
+
+def check_topk(idx_gpu, val_gpu, s_ref, k, qnorm, xnorm):
+    """Top-k sets equal up to near-ties; reported values match the oracle's."""
+    for q in range(s_ref.shape[0]):
+        ref = T.topk(s_ref[q], k)
+        got = idx_gpu[q][:k]
+        tol = 1e-6 * qnorm[q] * np.max(xnorm) + 1e-3 * abs(s_ref[q][ref[-1]])
+        kth = s_ref[q][ref[-1]]
+        for t in set(got.tolist()) ^ set(ref.tolist()):
+            assert abs(s_ref[q][t] - kth) <= tol, f"query {q}: top-k differs beyond a near-tie"
+        assert np.all(np.abs(val_gpu[q][:k] - s_ref[q][got]) <= np.maximum(1e-3 * np.abs(s_ref[q][got]), tol))
+        assert np.all(np.diff(val_gpu[q][:k]) <= 0)

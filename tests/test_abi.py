@@ -1,0 +1,109 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol include/tq.h
+declares, its host-only setup matches the oracle, and argument validation
+returns status codes before touching a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import turboquant as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+tq = pytest.importorskip("kv_cache_vector_turboquant_amd", reason="libtq.so not built")
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert "tq_quantize_kv" in names and "tq_attention_decode" in names
+    lib = tq.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(tq.EXPORTED_SYMBOLS) == names
+
+
+@pytest.mark.parametrize("d,bits", [(3, 1), (3, 2), (64, 3), (128, 1), (128, 2), (128, 3), (128, 4), (1536, 3),
+                                    (1536, 4)])
+def test_codebook_matches_oracle(d, bits):
+    lib_cb = tq.codebook_build(d, bits)
+    o = T.codebook(d, bits)
+    # independent implementations of the same fixed point agree after fp32 rounding
+    assert np.array_equal(lib_cb.centroids, o.centroids)
+    assert np.array_equal(lib_cb.boundaries, o.boundaries)
+    assert abs(lib_cb.distortion - o.distortion) <= 1e-9 * o.distortion
+
+
+@pytest.mark.parametrize("d,bits", [(128, 1), (128, 2), (128, 3), (128, 4)])
+def test_walsh_coefficients_reproduce_table(d, bits):
+    """The odd Walsh expansion the kernels use: c[idx] = sum_S w_S prod_{p in S}(2 b_p - 1)."""
+    cb = tq.codebook_build(d, bits)
+    L = 1 << bits
+    subsets = sorted([s for s in range(1, L) if bin(s).count("1") % 2 == 1], key=lambda s: (bin(s).count("1"), s))
+    for idx in range(L):
+        val = 0.0
+        for w, S in zip(cb.walsh.astype(np.float64), subsets):
+            chi = 1.0
+            for p in range(bits):
+                if S >> p & 1:
+                    chi *= 1.0 if (idx >> p) & 1 else -1.0
+            val += w * chi
+        assert abs(val - cb.centroids[idx]) <= 2e-7 * abs(cb.centroids[idx])
+
+
+@pytest.mark.parametrize("d", [32, 128, 1536])
+def test_rotation_matches_oracle(d):
+    G = synth.gaussian_matrix(0, synth.TAG_ROTATION, d, d)
+    lib_pi = tq.rotation_build(G)
+    o_pi = T.rotation_from_gaussian(G)
+    ulp = np.abs(lib_pi.view(np.int32).astype(np.int64) - o_pi.view(np.int32))
+    assert ulp.max() <= 1
+    assert np.count_nonzero(ulp) <= 1e-5 * d * d + 1
+    assert np.max(np.abs(lib_pi.astype(np.float64).T @ lib_pi.astype(np.float64) - np.eye(d))) <= 1e-5
+
+
+def test_host_errors():
+    lib = tq.lib()
+    cb = tq.CCodebook()
+    assert lib.tq_codebook_build(2, 3, ctypes.byref(cb)) == tq.TQ_ERR_UNSUPPORTED
+    assert "d must be" in tq.last_error()
+    assert lib.tq_codebook_build(128, 5, ctypes.byref(cb)) == tq.TQ_ERR_UNSUPPORTED
+    assert lib.tq_codebook_build(128, 0, ctypes.byref(cb)) == tq.TQ_ERR_UNSUPPORTED
+    assert lib.tq_codebook_build(128, 3, None) == tq.TQ_ERR_ARG
+    out = np.zeros(4, np.float32)
+    assert lib.tq_rotation_build(2, None, out.ctypes.data) == tq.TQ_ERR_ARG
+    g = np.zeros((8, 8))
+    assert lib.tq_rotation_build(1, g.ctypes.data, out.ctypes.data) == tq.TQ_ERR_UNSUPPORTED
+    with pytest.raises(tq.TQError):
+        tq.codebook_build(128, 9)
+
+
+def test_hot_entry_points_reject_null_context():
+    lib = tq.lib()
+    p = tq.CPacked(None, None, 0, 3, 1)
+    assert lib.tq_quantize_kv(None, None, 0, 1, 1, 128, 128, ctypes.byref(p), 0, 0, None, 0, None) == tq.TQ_ERR_ARG
+    c = tq.CCache()
+    assert lib.tq_append_token(None, ctypes.byref(c), None, None, 0, None) == tq.TQ_ERR_ARG
+    assert lib.tq_attention_decode(None, ctypes.byref(c), None, 0, 4, 1.0, None, None, 0, None) == tq.TQ_ERR_ARG
+    assert lib.tq_scores(None, None, 0, 1, ctypes.byref(p), None, 10, None, None, None, 0, None) == tq.TQ_ERR_ARG
+    assert lib.tq_ctx_destroy(None) == tq.TQ_ERR_ARG
+    assert lib.tq_quantize_ws_bytes(None, 1, 1, 1) == 0
+    assert tq.last_error() != ""
+
+
+def test_ctx_create_argument_errors():
+    lib = tq.lib()
+    h = ctypes.c_void_p()
+    g = np.zeros((128, 128))
+    assert lib.tq_ctx_create(128, None, g.ctypes.data, ctypes.byref(h)) == tq.TQ_ERR_ARG
+    assert lib.tq_ctx_create(100, g.ctypes.data, g.ctypes.data, ctypes.byref(h)) == tq.TQ_ERR_UNSUPPORTED
+    assert lib.tq_ctx_create(128, g.ctypes.data, g.ctypes.data, None) == tq.TQ_ERR_ARG
