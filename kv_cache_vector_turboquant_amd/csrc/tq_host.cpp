@@ -292,11 +292,35 @@ tq_status tq_ctx_create(int32_t d, const double *h_g_rot, const double *h_g_sket
   }
   const size_t mat = (size_t)d * d * sizeof(float);
   if ((e = hipMalloc(&ctx->d_rot, mat)) != hipSuccess || (e = hipMalloc(&ctx->d_sketch, mat)) != hipSuccess ||
+      (e = hipMalloc(&ctx->d_rot_t, mat)) != hipSuccess || (e = hipMalloc(&ctx->d_sketch_t, mat)) != hipSuccess ||
+      (e = hipMalloc(&ctx->d_rs_t, 2 * mat)) != hipSuccess ||
       (e = hipMalloc(&ctx->d_tables, sizeof(DeviceTables))) != hipSuccess) {
     tq_ctx_destroy(ctx);
     return fail(TQ_ERR_NOMEM, std::string("tq_ctx_create: hipMalloc: ") + hipGetErrorString(e));
   }
+  std::vector<float> rt((size_t)d * d), st((size_t)d * d), rst((size_t)2 * d * d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      rt[(size_t)j * d + i] = ctx->rot[(size_t)i * d + j];
+      st[(size_t)j * d + i] = ctx->sketch[(size_t)i * d + j];
+    }
+  // S Pi in fp64 from the fp32 tables, rounded to fp32; stored with Pi as [Pi ; S Pi]^T
+  // (only the d = 128 decode path reads it)
+  for (int i = 0; i < (d == 128 ? d : 0); ++i) {
+    std::vector<double> row(d, 0.0);
+    for (int k = 0; k < d; ++k) {
+      const double sik = ctx->sketch[(size_t)i * d + k];
+      for (int j = 0; j < d; ++j) row[j] += sik * (double)ctx->rot[(size_t)k * d + j];
+    }
+    for (int j = 0; j < d; ++j) {
+      rst[(size_t)j * 2 * d + i] = ctx->rot[(size_t)i * d + j];
+      rst[(size_t)j * 2 * d + d + i] = (float)row[j];
+    }
+  }
   if ((e = hipMemcpy(ctx->d_rot, ctx->rot.data(), mat, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(ctx->d_rot_t, rt.data(), mat, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(ctx->d_sketch_t, st.data(), mat, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(ctx->d_rs_t, rst.data(), 2 * mat, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(ctx->d_sketch, ctx->sketch.data(), mat, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(ctx->d_tables, &ctx->h_tables, sizeof(DeviceTables), hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipDeviceSynchronize()) != hipSuccess) {
@@ -313,6 +337,9 @@ tq_status tq_ctx_destroy(tq_ctx *ctx) {
   if (ctx->d_rot) (void)hipFree(ctx->d_rot);
   if (ctx->d_sketch) (void)hipFree(ctx->d_sketch);
   if (ctx->d_tables) (void)hipFree(ctx->d_tables);
+  if (ctx->d_rot_t) (void)hipFree(ctx->d_rot_t);
+  if (ctx->d_sketch_t) (void)hipFree(ctx->d_sketch_t);
+  if (ctx->d_rs_t) (void)hipFree(ctx->d_rs_t);
   delete ctx;
   return TQ_OK;
 }

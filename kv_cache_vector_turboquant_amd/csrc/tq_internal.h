@@ -40,6 +40,9 @@ struct tq_ctx {
   tq_codebook cb[TQ_MAX_BITS + 1];
   float *d_rot = nullptr;
   float *d_sketch = nullptr;
+  float *d_rot_t = nullptr;     // Pi^T, row-major (coalesced matrix-vector products)
+  float *d_sketch_t = nullptr;  // S^T, row-major
+  float *d_rs_t = nullptr;      // [Pi ; S Pi]^T: d x 2d row-major (query rotation and sketch in one pass)
   tq::DeviceTables *d_tables = nullptr;
   tq::DeviceTables h_tables;
 };

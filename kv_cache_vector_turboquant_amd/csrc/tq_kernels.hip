@@ -34,6 +34,7 @@ namespace tq {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef int i4v __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
@@ -538,16 +539,25 @@ hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t 
 // it expands over odd Walsh functions: c[idx] = sum_S w_S prod_{p in S} s_p,
 // and prod_{p in S} s_p = 2 (XOR of planes in S) - 1. Hence
 //   sum_j q_j c[idx_j] = sum_S w_S (2 M_S - sum_j q_j),  M_S = sum_j q_j mask_S,j.
-// The query (and, for values, the softmax weight) is split into exact signed
-// int8 digits (fixed point, 3 digits = 23-24 bits), the masks are 0/1 bytes
-// made from a plane word w as (w >> q) & 0x01010101, and every masked sum is an
-// exact int32 from v_mfma_i32_16x16x64_i8. A fragment row = 4*head + digit.
+// Keys: with chi = 2 mask - 1 in {-1, +1}, sum_j q_j c[idx_j] = sum_S w_S sum_j
+// q_j chi_S,j. The query is fixed point, split into 8 signed base-8 digits held
+// as fp6 (e2m3) A operands; the signed masks are fp4 (e2m1) B operands built
+// from a plane word w with one shift, and and xor per 8 coordinates; the MFMA
+// is v_mfma_scale_f32_16x16x128_f8f6f4 with per-row block scales 2^(3 digit),
+// so A row (4*head + slot) accumulates digits slot and slot+4 exactly and the
+// four rows of a head sum to sum_j Q_j chi_j.
+// Values: the softmax weight is fixed point with 3 signed int8 digits, the
+// masks are 0/1 bytes made as (w >> q) & 0x01010101, and every masked sum is an
+// exact int32 from v_mfma_i32_16x16x64_i8; A row = 4*head + digit.
 // ---------------------------------------------------------------------------
 
-constexpr int DD = 128;          // head dim
-constexpr int DW = DD / 32;      // 32-coordinate groups
-constexpr float QMAX = 8323072.f;  // |fixed-point query| bound with 3 signed digits
+constexpr int DD = 128;            // head dim
+constexpr int DW = DD / 32;        // 32-coordinate groups
+constexpr float QMAX = 7190000.f;  // |fixed-point query| bound with 8 signed base-8 digits in [-4, 3]
+typedef int i8v __attribute__((ext_vector_type(8)));
 constexpr float WSCALE = 4194304.f;  // 2^22: fixed point of the value weights
+constexpr int KTPW = 2;            // key tiles (16 tokens each) per wave per round (double-buffered)
+constexpr int VGPI = 2;            // 128-token value groups per iteration
 
 struct DecodeArgs {
   const uint32_t *kbits;
@@ -563,28 +573,33 @@ struct DecodeArgs {
   const DeviceTables *tables;
   const void *q;
   int q_bf16;
-  const float *rot, *sketch;
-  int8_t *qfrag;         // [stream*hgroups][2][2][64][16]
-  float *qconst;         // [stream*hgroups][4][4]: scale_r, scale_s, Qsum (int bits), Qssum (int bits)
+  const float *rot, *rs_t;  // rs_t: [Pi ; S Pi]^T, 128 x 256 row-major
+  uint32_t *qfrag;       // [stream*hgroups][2 (q_rot, q_s)][2 (digits 0-3, 4-7)][64 lanes][8] fp6 fragments
+  float *qconst;         // [stream*hgroups][4][4]: scale_r, scale_s, -, -
   float *partial;        // [batch*q_heads][nchunks][DD + 2]
   float *out;
 };
 
-__device__ __forceinline__ int8_t sdigit(int v) { return (int8_t)(((v & 0xFF) ^ 0x80) - 0x80); }
+__device__ __forceinline__ int sdigit(int v) { return ((v & 0xFF) ^ 0x80) - 0x80; }
+
+// The i-th odd-cardinality subset of the B planes, ordered by (popcount, value).
+__host__ __device__ constexpr int walsh_mask(int B, int i) {
+  return i < B ? (1 << i) : (B == 3 ? 7 : (i == 4 ? 7 : i == 5 ? 11 : i == 6 ? 13 : 14));
+}
 
 // One block per (stream, head group): q_rot = Pi q, q_s = S q_rot for up to 4
 // heads, fixed-point split and A-fragment layout.
-__global__ void __launch_bounds__(256) decode_prep_kernel(DecodeArgs a) {
-  __shared__ float qf[4][DD], qr[4][DD], qs[4][DD];
-  __shared__ int qi[2][4][DD];
-  __shared__ float mx[2][4];
+__global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
+  __shared__ float qf[4][DD], qr[4][DD], qs[4][DD], part2[4][2 * DD];
+  __shared__ int8_t qd[2][4][DD][8];  // base-8 digits of the fixed-point q_rot / q_s
+  __shared__ float mx[2][4];  // max |q_rot|, max |q_s| per head
   const int tid = threadIdx.x;
   const int sg = blockIdx.x;  // stream * hgroups + hg
   const int hg = sg % a.hgroups, stream = sg / a.hgroups;
   const int b = stream / a.kv_heads, kvh = stream % a.kv_heads;
   const int h0 = kvh * a.group + hg * 4;
   const int nh = min(4, a.group - hg * 4);
-  for (int e = tid; e < 4 * DD; e += 256) {
+  for (int e = tid; e < 4 * DD; e += 512) {
     const int hh = e / DD, j = e % DD;
     float v = 0.f;
     if (hh < nh) {
@@ -594,64 +609,83 @@ __global__ void __launch_bounds__(256) decode_prep_kernel(DecodeArgs a) {
     qf[hh][j] = v;
   }
   __syncthreads();
-  for (int e = tid; e < 4 * DD; e += 256) {
-    const int hh = e / DD, j = e % DD;
-    float acc = 0.f;
-    for (int k = 0; k < DD; ++k) acc += a.rot[j * DD + k] * qf[hh][k];
-    qr[hh][j] = acc;
+  // thread (r, k half): row r of [Pi ; S Pi] (r < 128: q_rot, else q_s) against the
+  // four queries over half of k; the transposed matrix makes the reads coalesced over r
+  {
+    const int r = tid & 255, kh = tid >> 8;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 32
+    for (int k = kh * 64; k < kh * 64 + 64; ++k) {
+      const float m = a.rs_t[k * 2 * DD + r];
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) acc[hh] += m * qf[hh][k];
+    }
+    if (kh == 1) {
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) part2[hh][r] = acc[hh];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const float v = acc[hh] + part2[hh][r];
+        if (r < DD) qr[hh][r] = v;
+        else qs[hh][r - DD] = v;
+      }
+    }
   }
   __syncthreads();
-  for (int e = tid; e < 4 * DD; e += 256) {
-    const int hh = e / DD, i = e % DD;
-    float acc = 0.f;
-    for (int k = 0; k < DD; ++k) acc += a.sketch[i * DD + k] * qr[hh][k];
-    qs[hh][i] = acc;
+  if (tid < 256) {
+    // max |.| per (type, head): wave w reduces (type, head pair) rows
+    const int lane = tid & 63, w = tid >> 6, T = w >> 1;
+    for (int hh = (w & 1) * 2; hh < (w & 1) * 2 + 2; ++hh) {
+      const float *row = T ? qs[hh] : qr[hh];
+      float m = fmaxf(fabsf(row[lane]), fabsf(row[lane + 64]));
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if (lane == 0) mx[T][hh] = m;
+    }
   }
   __syncthreads();
-  if (tid < 8) {
-    const int T = tid >> 2, hh = tid & 3;
-    float m = 0.f;
-    for (int j = 0; j < DD; ++j) m = fmaxf(m, fabsf(T ? qs[hh][j] : qr[hh][j]));
-    mx[T][hh] = m;
-  }
-  __syncthreads();
-  for (int e = tid; e < 2 * 4 * DD; e += 256) {
+  for (int e = tid; e < 2 * 4 * DD; e += 512) {
     const int T = e / (4 * DD), hh = (e / DD) & 3, j = e % DD;
     const float m = mx[T][hh];
     const float v = T ? qs[hh][j] : qr[hh][j];
-    qi[T][hh][j] = m > 0.f ? (int)rintf(v * (QMAX / m)) : 0;
+    int q = m > 0.f ? (int)rintf(v * (QMAX / m)) : 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // balanced base-8 digits in [-4, 3]
+      const int dv = ((q + 4) & 7) - 4;
+      qd[T][hh][j][k] = (int8_t)dv;
+      q = (q - dv) >> 3;
+    }
   }
-  __syncthreads();
   if (tid < 8) {
     const int T = tid >> 2, hh = tid & 3;
-    int sum = 0;
-    for (int j = 0; j < DD; ++j) sum += qi[T][hh][j];
     float *qc = a.qconst + ((int64_t)sg * 4 + hh) * 4;
     const float m = mx[T][hh];
     qc[T] = m > 0.f ? m / QMAX : 0.f;
-    qc[2 + T] = __int_as_float(sum);
   }
-  {
-    // fragment (T, instr, lane): 16 digits of row (4*hh + dig), k-slot 4q'+b <-> coordinate 32g + 4i + q' + 8b
+  __syncthreads();
+  if (tid < 256) {
+    // fragment (T, instr, lane): 32 fp6 digits of row (4*hh + slot), digit 4*instr + slot;
+    // element s = 8q + i <-> coordinate 32g + 4i + q (the fp4 mask order), 6 bits at bit 6s
     const int T = tid >> 7, ins = (tid >> 6) & 1, L = tid & 63;
-    const int g = L >> 4, row = L & 15, hh = row >> 2, dig = row & 3;
-    uint32_t wv[4];
-    for (int qq = 0; qq < 4; ++qq) {
-      uint32_t w = 0;
-      for (int bb = 0; bb < 4; ++bb) {
-        const int j = 32 * g + 4 * ins + qq + 8 * bb;
-        int v = qi[T][hh][j];
-        int d0 = sdigit(v);
-        int v1 = (v - d0) >> 8;
-        int d1 = sdigit(v1);
-        int d2 = (v1 - d1) >> 8;
-        const int dv = dig == 0 ? d0 : dig == 1 ? d1 : dig == 2 ? d2 : 0;
-        w |= ((uint32_t)(dv & 0xFF)) << (8 * bb);
-      }
-      wv[qq] = w;
+    const int g = L >> 4, row = L & 15, hh = row >> 2, dig = 4 * ins + (row & 3);
+    uint32_t dw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int j = 32 * g + 4 * (e & 7) + (e >> 3);
+      const int dv = qd[T][hh][j][dig];
+    const uint32_t mag = (uint32_t)(dv < 0 ? -dv : dv);
+      // e2m3: 1 -> 0b001000, 2 -> 0b010000, 3 -> 0b010100, 4 -> 0b011000; sign bit 0b100000
+      const uint32_t code = (mag == 0 ? 0u : mag == 1 ? 0x08u : mag == 2 ? 0x10u : mag == 3 ? 0x14u : 0x18u) |
+                            (dv < 0 ? 0x20u : 0u);
+      const int bit = 6 * e;
+      dw[bit >> 5] |= code << (bit & 31);
+      if ((bit & 31) > 26) dw[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(a.qfrag + ((((int64_t)sg * 2 + T) * 2 + ins) * 64 + L) * 16);
-    *dst = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    uint4 *dst = reinterpret_cast<uint4 *>(a.qfrag + ((((int64_t)sg * 2 + T) * 2 + ins) * 64 + L) * 8);
+    dst[0] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    dst[1] = make_uint4(dw[4], dw[5], 0u, 0u);
   }
 }
 
@@ -666,10 +700,23 @@ __device__ __forceinline__ void mask_bytes(uint32_t m, i4v &lo, i4v &hi) {
   hi[3] = (int)((m >> 7) & 0x01010101u);
 }
 
-__device__ __forceinline__ uint32_t xor_planes(const uint32_t *pl, int S) {
+// Signed fp4 mask of a 32-coordinate plane word: element 8q + i (nibble i of
+// dword q) is +1 (0x2) if bit 4i + q of w is set, else -1 (0xA).
+__device__ __forceinline__ i8v mask_fp4_pm(uint32_t w) {
+  i8v b;
+  b[0] = (int)(((w << 3) & 0x88888888u) ^ 0xAAAAAAAAu);
+  b[1] = (int)(((w << 2) & 0x88888888u) ^ 0xAAAAAAAAu);
+  b[2] = (int)(((w << 1) & 0x88888888u) ^ 0xAAAAAAAAu);
+  b[3] = (int)((w & 0x88888888u) ^ 0xAAAAAAAAu);
+  b[4] = b[5] = b[6] = b[7] = 0;
+  return b;
+}
+
+template <int NP>
+__device__ __forceinline__ uint32_t xor_planes(const uint32_t (&pl)[NP], int S) {
   uint32_t m = 0;
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
+  for (int p = 0; p < NP && p < 4; ++p)
     if (S & (1 << p)) m ^= pl[p];
   return m;
 }
@@ -681,11 +728,12 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   constexpr int KM = 1 << (KB - 1);  // key Walsh masks
   constexpr int VM = 1 << (VB - 1);  // value Walsh masks
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float *lg = reinterpret_cast<float *>(smem);                         // [4][chunk]
-  int8_t *av = reinterpret_cast<int8_t *>(smem + 4 * a.chunk * 4);     // [chunk/128][2][64][16]
-  __shared__ float red[4][4];
+  float *lg = reinterpret_cast<float *>(smem);                         // [4][chunk] + 64 spare
+  float *vnl = lg + 4 * a.chunk + 64;                                  // [chunk] value norms
+  int8_t *av = reinterpret_cast<int8_t *>(smem + (5 * a.chunk + 64) * 4);  // [chunk/128][2][64][16]
+  __shared__ float red[4];
   __shared__ double wsum[4];
-  __shared__ float hmax[4], hsum[4], vmaxs;
+  __shared__ float hmax[4], hsum[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x;
@@ -711,96 +759,128 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int64_t srec = (int64_t)stream * a.capacity;
   const float *wk = a.tables->walsh[KB];
   const float *wv = a.tables->walsh[VB];
+  const int ngrp = (n + 127) >> 7;
+  // zero the value A fragments (rows of absent heads and pad digits stay zero)
+  for (int e = tid; e < ngrp * 2 * 64; e += 256) reinterpret_cast<uint4 *>(av)[e] = make_uint4(0, 0, 0, 0);
 
   // ---- phase K: logits of all tokens of the chunk (log2 units) ----
-  const int8_t *qf = a.qfrag + (int64_t)sg * 2 * 2 * 64 * 16;
-  const i4v aqr0 = *reinterpret_cast<const i4v *>(qf + ((0 * 2 + 0) * 64 + lane) * 16);
-  const i4v aqr1 = *reinterpret_cast<const i4v *>(qf + ((0 * 2 + 1) * 64 + lane) * 16);
-  const i4v aqs0 = *reinterpret_cast<const i4v *>(qf + ((1 * 2 + 0) * 64 + lane) * 16);
-  const i4v aqs1 = *reinterpret_cast<const i4v *>(qf + ((1 * 2 + 1) * 64 + lane) * 16);
+  const uint32_t *qf = a.qfrag + (int64_t)sg * 2 * 2 * 64 * 8;
+  auto ldfrag = [&](int T, int ins) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(qf + ((T * 2 + ins) * 64 + lane) * 8);
+    const uint4 x = p[0], y = p[1];
+    i8v v;
+    v[0] = (int)x.x; v[1] = (int)x.y; v[2] = (int)x.z; v[3] = (int)x.w;
+    v[4] = (int)y.x; v[5] = (int)y.y; v[6] = 0; v[7] = 0;
+    return v;
+  };
+  const i8v aqr0 = ldfrag(0, 0), aqr1 = ldfrag(0, 1), aqs0 = ldfrag(1, 0), aqs1 = ldfrag(1, 1);
+  const int sc0 = 127 + 3 * (lane & 3), sc1 = sc0 + 12;  // e8m0 row scales 2^(3 digit)
   const int tn = lane & 15, G = lane >> 4;  // MFMA column (token), row group (head)
   const float *qc = a.qconst + ((int64_t)sg * 4 + G) * 4;
   const float sr = qc[0], ss = qc[1];
-  const int qsum = __float_as_int(qc[2]), qssum = __float_as_int(qc[3]);
+  float wkr[KM];
+#pragma unroll
+  for (int mi = 0; mi < KM; ++mi) wkr[mi] = wk[mi];
+  // the logit store below is unconditional (invalid lanes write a spare slot)
+  // so that no loop-invariant load is sunk into a branch inside the loop
+  const int spare = 4 * a.chunk + lane;
   float vmx = 0.f;
   const int ntile = (n + 15) >> 4;
-  for (int tile = wave; tile < ntile; tile += 4) {
-    const int tl = tile * 16 + tn;
-    const bool valid = tl < n;
-    const int64_t rec = srec + t0 + tl;
-    uint32_t pl[5] = {0, 0, 0, 0, 0};
-    float2 kn = make_float2(0.f, 0.f);
-    if (valid) {
-      const uint32_t *src = a.kbits + (rec * DW + G) * (KB + 1);
+  struct KBuf {
+    uint32_t pl[KTPW][KB + 1];
+    float2 kn[KTPW];
+    float vn[KTPW];
+  };
+  auto kload = [&](int base, KBuf &bf) {
 #pragma unroll
-      for (int p = 0; p <= KB; ++p) pl[p] = src[p];
-      kn = *reinterpret_cast<const float2 *>(a.knorm + 2 * rec);
-      if (G == 0) vmx = fmaxf(vmx, a.vnorm[rec]);
-    }
-    float code = 0.f;
+    for (int u = 0; u < KTPW; ++u) {
+      const int tl = (base + u) * 16 + tn;
+      const int64_t rec = srec + t0 + tl;
+      bf.kn[u] = make_float2(0.f, 0.f);
+      bf.vn[u] = 0.f;
 #pragma unroll
-    for (int mi = 0; mi < KM; ++mi) {
-      const int S = (mi < KB) ? (1 << mi) : (KB == 3 ? 7 : (mi == 4 ? 7 : mi == 5 ? 11 : mi == 6 ? 13 : 14));
-      i4v lo, hi, acc = {0, 0, 0, 0};
-      mask_bytes(xor_planes(pl, S), lo, hi);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aqr0, lo, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aqr1, hi, acc, 0, 0, 0);
-      const int T = 2 * combine_digits(acc) - qsum;
-      code += wk[mi] * (float)T;
+      for (int p = 0; p <= KB; ++p) bf.pl[u][p] = 0u;
+      if (tl < n) {
+        const uint32_t *src = a.kbits + (rec * DW + G) * (KB + 1);
+        if constexpr (KB == 3) {
+          const uint4 w4 = *reinterpret_cast<const uint4 *>(src);
+          bf.pl[u][0] = w4.x; bf.pl[u][1] = w4.y; bf.pl[u][2] = w4.z; bf.pl[u][3] = w4.w;
+        } else {
+#pragma unroll
+          for (int p = 0; p <= KB; ++p) bf.pl[u][p] = src[p];
+        }
+        bf.kn[u] = *reinterpret_cast<const float2 *>(a.knorm + 2 * rec);
+        if (G == 0) bf.vn[u] = a.vnorm[rec];
+      }
     }
-    int Ts;
-    {
-      i4v lo, hi, acc = {0, 0, 0, 0};
-      mask_bytes(pl[KB], lo, hi);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aqs0, lo, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aqs1, hi, acc, 0, 0, 0);
-      Ts = 2 * combine_digits(acc) - qssum;
+  };
+  KBuf cur;
+  if (wave * KTPW < ntile) kload(wave * KTPW, cur);
+  for (int base = wave * KTPW; base < ntile; base += 4 * KTPW) {
+    KBuf nxt;
+    if (base + 4 * KTPW < ntile) kload(base + 4 * KTPW, nxt);  // next round in flight during this one
+#pragma unroll
+    for (int u = 0; u < KTPW; ++u) {
+      const int tl = (base + u) * 16 + tn;
+      // all signed masked sums first (independent accumulators keep the MFMA pipe busy)
+      f4v acc[KM + 1];
+#pragma unroll
+      for (int mi = 0; mi <= KM; ++mi) {
+        const i8v bm = mask_fp4_pm(mi < KM ? xor_planes(cur.pl[u], walsh_mask(KB, mi)) : cur.pl[u][KB]);
+        acc[mi] = f4v{0.f, 0.f, 0.f, 0.f};
+        acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr0 : aqs0, bm, acc[mi], 2, 4, 0, sc0,
+                                                                   0, 127);
+        acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr1 : aqs1, bm, acc[mi], 2, 4, 0, sc1,
+                                                                   0, 127);
+      }
+      float code = 0.f;
+#pragma unroll
+      for (int mi = 0; mi < KM; ++mi) code += wkr[mi] * ((acc[mi][0] + acc[mi][1]) + (acc[mi][2] + acc[mi][3]));
+      const float Ts = (acc[KM][0] + acc[KM][1]) + (acc[KM][2] + acc[KM][3]);
+      const float s = cur.kn[u].x * (sr * code + a.qjl_scale * cur.kn[u].y * ss * Ts);
+      lg[(G < nh && tl < n) ? G * a.chunk + tl : spare] = s * a.scale_log2;
+      if (G == 0 && tl < n) {
+        vnl[tl] = cur.vn[u];
+        vmx = fmaxf(vmx, cur.vn[u]);
+      }
     }
-    const float s = kn.x * (sr * code + a.qjl_scale * kn.y * ss * (float)Ts);
-    if (G < nh && valid) lg[G * a.chunk + tl] = s * a.scale_log2;
+    cur = nxt;
   }
-  // wave max of the value norms
   for (int off = 32; off > 0; off >>= 1) vmx = fmaxf(vmx, __shfl_xor(vmx, off));
-  if (lane == 0) red[0][wave] = vmx;
-  // zero the value A fragments
-  const int ngrp = (n + 127) >> 7;
-  for (int e = tid; e < ngrp * 2 * 64 * 16 / 16; e += 256) reinterpret_cast<uint4 *>(av)[e] = make_uint4(0, 0, 0, 0);
+  if (lane == 0) red[wave] = vmx;
   __syncthreads();
-  if (tid == 0) vmaxs = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  // per-head max: wave w handles head w
+  const float vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // ---- softmax: wave w owns head w; weights -> fixed-point value digits ----
+  const float wq = vmax > 0.f ? WSCALE / vmax : 0.f;
   if (wave < nh) {
     float m = -INFINITY;
     for (int t = lane; t < n; t += 64) m = fmaxf(m, lg[wave * a.chunk + t]);
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) hmax[wave] = m;
-  }
-  __syncthreads();
-  // ---- softmax weights -> fixed-point value digits ----
-  const float vmax = vmaxs;
-  const float wq = vmax > 0.f ? WSCALE / vmax : 0.f;
-  if (wave < nh) {
-    const float m = hmax[wave];
+    // token t = lane + 64 i lands in fragment byte
+    //   (i>>1)*2048 + ins*1024 + gg*256 + head*64 + qq*4 + bb, with q = t&7, ins = q>>2,
+    //   qq = q&3, bb = (t>>3)&3, gg = (t>>5)&3: the lane-dependent part is fixed.
+    const int lbase = (((lane >> 2) & 1) << 10) | (((lane >> 5) & 1) << 8) | (wave << 6) | ((lane & 3) << 2) |
+                      ((lane >> 3) & 3);
     float l = 0.f;
-    double ws = 0.0;
-    for (int t = lane; t < n; t += 64) {
+    int wsi = 0;
+    for (int i = 0, t = lane; t < n; ++i, t += 64) {
       const float p = exp2f(lg[wave * a.chunk + t] - m);
       l += p;
-      const float w = p * a.vnorm[srec + t0 + t];
-      const int W = (int)rintf(w * wq);
-      ws += (double)W;
-      const uint32_t u = (uint32_t)W + 0x808080u;
-      const int grp = t >> 7, tp = t & 127, gg = tp >> 5, rem = tp & 31, q = rem & 7, bb = rem >> 3;
-      const int ins = q >> 2, qq = q & 3;
-      int8_t *base = av + (((grp * 2 + ins) * 64 + gg * 16 + 4 * wave) * 16) + 4 * qq + bb;
-      base[0] = (int8_t)((u & 0xFF) ^ 0x80);
-      base[16] = (int8_t)(((u >> 8) & 0xFF) ^ 0x80);
-      base[32] = (int8_t)(((u >> 16) & 0xFF) ^ 0x80);
+      const int W = (int)rintf(p * vnl[t] * wq);
+      wsi += W;
+      const uint32_t x = ((uint32_t)W + 0x808080u) ^ 0x808080u;  // three signed base-256 digits
+      int8_t *dst = av + lbase + ((i >> 1) << 11) + ((i & 1) << 9);
+      dst[0] = (int8_t)x;
+      dst[16] = (int8_t)(x >> 8);
+      dst[32] = (int8_t)(x >> 16);
     }
+    double ws = (double)wsi;
     for (int off = 32; off > 0; off >>= 1) {
       l += __shfl_xor(l, off);
       ws += __shfl_xor(ws, off);
     }
     if (lane == 0) {
+      hmax[wave] = m;
       hsum[wave] = l;
       wsum[wave] = ws;
     }
@@ -814,29 +894,50 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int mi = 0; mi < VM; ++mi) accv[nt][mi] = i4v{0, 0, 0, 0};
   const int vn = lane & 15, vg = lane >> 4;  // coordinate column, token block in the 128-token group
-  for (int grp = 0; grp < ngrp; ++grp) {
-    const i4v a0 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 0) * 64 + lane) * 16);
-    const i4v a1 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 1) * 64 + lane) * 16);
-    const int tb = grp * 128 + vg * 32;  // first token of this lane's block, chunk-relative
+  struct VBuf {
+    uint32_t pl[VGPI][2][VB];
+  };
+  auto vload = [&](int grp0, VBuf &bf) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int j = wave * 32 + nt * 16 + vn;
-      uint32_t pl[4] = {0, 0, 0, 0};
-      if (tb < n) {
-        const int64_t blk = (srec + t0 + tb) >> 5;
-        const uint32_t *src = a.vbits + (blk * DD + j) * VB;
+    for (int gi = 0; gi < VGPI; ++gi) {
+      const int tb = (grp0 + gi) * 128 + vg * 32;  // first token of this lane's block, chunk-relative
 #pragma unroll
-        for (int p = 0; p < VB; ++p) pl[p] = src[p];
-      }
+      for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-      for (int mi = 0; mi < VM; ++mi) {
-        const int S = (mi < VB) ? (1 << mi) : (VB == 3 ? 7 : (mi == 4 ? 7 : mi == 5 ? 11 : mi == 6 ? 13 : 14));
-        i4v lo, hi;
-        mask_bytes(xor_planes(pl, S), lo, hi);
-        accv[nt][mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo, accv[nt][mi], 0, 0, 0);
-        accv[nt][mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi, accv[nt][mi], 0, 0, 0);
+        for (int p = 0; p < VB; ++p) bf.pl[gi][nt][p] = 0u;
+        if (tb < n) {
+          const int j = wave * 32 + nt * 16 + vn;
+          const int64_t blk = (srec + t0 + tb) >> 5;
+          const uint32_t *src = a.vbits + (blk * DD + j) * VB;
+#pragma unroll
+          for (int p = 0; p < VB; ++p) bf.pl[gi][nt][p] = src[p];
+        }
       }
     }
+  };
+  VBuf vcur;
+  vload(0, vcur);
+  for (int grp0 = 0; grp0 < ngrp; grp0 += VGPI) {
+    VBuf vnxt;
+    if (grp0 + VGPI < ngrp) vload(grp0 + VGPI, vnxt);
+#pragma unroll
+    for (int gi = 0; gi < VGPI; ++gi) {
+      const int grp = grp0 + gi;
+      if (grp >= ngrp) break;
+      const i4v a0 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 0) * 64 + lane) * 16);
+      const i4v a1 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 1) * 64 + lane) * 16);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+        for (int mi = 0; mi < VM; ++mi) {
+          i4v lo, hi;
+          mask_bytes(xor_planes(vcur.pl[gi][nt], walsh_mask(VB, mi)), lo, hi);
+          accv[nt][mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo, accv[nt][mi], 0, 0, 0);
+          accv[nt][mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi, accv[nt][mi], 0, 0, 0);
+        }
+      }
+    }
+    vcur = vnxt;
   }
   // flush: lane (coordinate vn, head vg) holds digits 0..2 of every mask sum
   if (vg < nh) {
@@ -860,28 +961,58 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   }
 }
 
-__global__ void __launch_bounds__(128) decode_merge_kernel(DecodeArgs a) {
-  __shared__ float orot[DD];
-  const int bh = blockIdx.x;  // b * q_heads + h
-  const int j = threadIdx.x;
-  const float *p = a.partial + (int64_t)bh * a.nchunks * (DD + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, p[c * (DD + 2) + DD]);
-  float L = 0.f, o = 0.f;
-  if (M > -INFINITY) {
-    for (int c = 0; c < a.nchunks; ++c) {
-      const float m = p[c * (DD + 2) + DD];
-      if (m == -INFINITY) continue;
-      const float f = exp2f(m - M);
-      L += f * p[c * (DD + 2) + DD + 1];
-      o += f * p[c * (DD + 2) + j];
+// One block per (sequence, KV head, head group), thread = (head, coordinate):
+// online log-sum-exp merge of the chunks (loads issued in batches), then
+// o = Pi^T o_rot.
+__global__ void __launch_bounds__(8 * DD) decode_merge_kernel(DecodeArgs a) {
+  constexpr int CB = 8;
+  __shared__ float orot[4][DD], half[4][DD];
+  const int sg = blockIdx.x;
+  const int hg = sg % a.hgroups, stream = sg / a.hgroups;
+  const int b = stream / a.kv_heads;
+  const int h0 = (stream % a.kv_heads) * a.group + hg * 4;
+  const int nh = min(4, a.group - hg * 4);
+  const int kh = threadIdx.x >> 9, hh = (threadIdx.x >> 7) & 3, j = threadIdx.x & (DD - 1);
+  if (kh == 0) {
+    float val = 0.f;
+    if (hh < nh) {
+      const float *p = a.partial + ((int64_t)b * a.q_heads + h0 + hh) * a.nchunks * (DD + 2);
+      float M = -INFINITY, L = 0.f, O = 0.f;
+      for (int c0 = 0; c0 < a.nchunks; c0 += CB) {
+        float mv[CB], lv[CB], ov[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+          const int c = c0 + u;
+          mv[u] = -INFINITY;
+          lv[u] = ov[u] = 0.f;
+          if (c < a.nchunks) {
+            mv[u] = p[c * (DD + 2) + DD];
+            lv[u] = p[c * (DD + 2) + DD + 1];
+            ov[u] = p[c * (DD + 2) + j];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+          if (mv[u] == -INFINITY) continue;
+          const float Mn = fmaxf(M, mv[u]);
+          const float f0 = (M == -INFINITY) ? 0.f : exp2f(M - Mn), f1 = exp2f(mv[u] - Mn);
+          L = L * f0 + lv[u] * f1;
+          O = O * f0 + ov[u] * f1;
+          M = Mn;
+        }
+      }
+      val = L > 0.f ? O / L : 0.f;
     }
+    orot[hh][j] = val;
   }
-  orot[j] = L > 0.f ? o / L : 0.f;
   __syncthreads();
+  // o = Pi^T o_rot: column j of Pi (coalesced over j), k split in halves
   float acc = 0.f;
-  for (int k = 0; k < DD; ++k) acc += a.rot[k * DD + j] * orot[k];  // o = Pi^T o_rot
-  a.out[(int64_t)bh * DD + j] = acc;
+#pragma unroll 16
+  for (int k = kh * 64; k < kh * 64 + 64; ++k) acc += a.rot[k * DD + j] * orot[hh][k];
+  if (kh == 1) half[hh][j] = acc;
+  __syncthreads();
+  if (kh == 0 && hh < nh) a.out[((int64_t)b * a.q_heads + h0 + hh) * DD + j] = acc + half[hh][j];
 }
 
 size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int *chunk_out,
@@ -896,7 +1027,7 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
   if (chunk_out) *chunk_out = chunk;
   if (nchunks_out) *nchunks_out = nchunks;
   size_t b = 0;
-  b += (size_t)streams * 2 * 2 * 64 * 16;  // qfrag
+  b += (size_t)streams * 2 * 2 * 64 * 32;  // qfrag (fp6 fragments, 8 dwords per lane)
   b = (b + 255) & ~(size_t)255;
   b += (size_t)streams * 16 * sizeof(float);  // qconst
   b = (b + 255) & ~(size_t)255;
@@ -936,49 +1067,50 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.q = q;
   a.q_bf16 = is_bf16;
   a.rot = ctx->d_rot;
-  a.sketch = ctx->d_sketch;
+  a.rs_t = ctx->d_rs_t;
   const int streams = cache->batch * cache->kv_heads * a.hgroups;
   char *p = (char *)ws;
-  a.qfrag = (int8_t *)p;
-  p += (((size_t)streams * 2 * 2 * 64 * 16) + 255) & ~(size_t)255;
+  a.qfrag = (uint32_t *)p;
+  p += (((size_t)streams * 2 * 2 * 64 * 32) + 255) & ~(size_t)255;
   a.qconst = (float *)p;
   p += (((size_t)streams * 16 * sizeof(float)) + 255) & ~(size_t)255;
   a.partial = (float *)p;
   a.out = out;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(streams), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(streams), dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t shm = (size_t)4 * chunk * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;
+  const size_t shm = (size_t)(5 * chunk + 64) * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;
   dim3 grid(nchunks, streams);
   const int kb = cache->k.mse_bits, vb = cache->v.mse_bits;
-  if (kb == 3 && vb == 3) e = launch_decode_kv<3, 3>(a, grid, shm, st);
-  else if (kb == 2 && vb == 3) e = launch_decode_kv<2, 3>(a, grid, shm, st);
-  else if (kb == 2 && vb == 2) e = launch_decode_kv<2, 2>(a, grid, shm, st);
-  else if (kb == 1 && vb == 3) e = launch_decode_kv<1, 3>(a, grid, shm, st);
-  else if (kb == 3 && vb == 2) e = launch_decode_kv<3, 2>(a, grid, shm, st);
-  else if (kb == 4 && vb == 4) e = launch_decode_kv<4, 4>(a, grid, shm, st);
-  else if (kb == 4 && vb == 3) e = launch_decode_kv<4, 3>(a, grid, shm, st);
-  else if (kb == 1 && vb == 1) e = launch_decode_kv<1, 1>(a, grid, shm, st);
+#define TQ_DEC(K_, V_) else if (kb == K_ && vb == V_) e = launch_decode_kv<K_, V_>(a, grid, shm, st);
+  if (false) {
+  }
+  TQ_DEC(1, 1) TQ_DEC(1, 2) TQ_DEC(1, 3) TQ_DEC(1, 4)
+  TQ_DEC(2, 1) TQ_DEC(2, 2) TQ_DEC(2, 3) TQ_DEC(2, 4)
+  TQ_DEC(3, 1) TQ_DEC(3, 2) TQ_DEC(3, 3) TQ_DEC(3, 4)
+  TQ_DEC(4, 1) TQ_DEC(4, 2) TQ_DEC(4, 3) TQ_DEC(4, 4)
   else return hipErrorInvalidValue;
+#undef TQ_DEC
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(cache->batch * q_heads), dim3(DD), 0, st, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(streams), dim3(8 * DD), 0, st, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Append: one block of 128 threads (thread = coordinate) per (b, h) stream.
+// Append: one block of 128 threads (thread = coordinate) per (b, h) stream; a
+// second launch advances the sequence lengths once every stream has read them.
 // ---------------------------------------------------------------------------
 
 struct AppendArgs {
   const void *k, *v;
   int bf16;
-  const float *rot, *sketch;
+  const float *rot_t, *sketch_t;
   const DeviceTables *tables;
   uint32_t *kbits;
   float *knorm;
   uint32_t *vbits;
   float *vnorm;
-  const int32_t *seq_len;
+  int32_t *seq_len;
   int kB, vB, kv_heads, capacity;
 };
 
@@ -991,76 +1123,72 @@ __device__ __forceinline__ float block_sum128(float v, float *red) {
   return r;
 }
 
-__global__ void __launch_bounds__(128) append_kernel(AppendArgs a) {
-  __shared__ float xs[DD], rs[DD];
+__global__ void __launch_bounds__(DD) append_kernel(AppendArgs a) {
+  __shared__ float xs[DD], rs[DD], vs[DD];
   __shared__ float red[2];
   const int stream = blockIdx.x, j = threadIdx.x, lane = j & 63, wv = j >> 6;
   const int b = stream / a.kv_heads;
   const int t = a.seq_len[b];
   if (t >= a.capacity) return;
   const int64_t rec = (int64_t)stream * a.capacity + t;
-  // ---- key ----
-  {
-    const int64_t off = (int64_t)stream * DD + j;
-    const float x = a.bf16 ? bf16f(((const uint16_t *)a.k)[off]) : ((const float *)a.k)[off];
-    xs[j] = x;
-    const float nrm = sqrtf(block_sum128(x * x, red));  // also orders the xs writes
-    float y = 0.f;
-    for (int k = 0; k < DD; ++k) y += a.rot[j * DD + k] * xs[k];
-    const bool live = nrm > 0.f;
-    y = live ? y / nrm : 0.f;
-    const int L = 1 << a.kB;
-    int idx = 0;
-    for (int i = 0; i < L - 1; ++i) idx += (y >= a.tables->boundary[a.kB][i]) ? 1 : 0;
-    if (!live) idx = 0;
-    const float r = live ? y - a.tables->centroid[a.kB][idx] : 0.f;
-    rs[j] = r;
-    const float rho = sqrtf(block_sum128(r * r, red));
-    float z = 0.f;
-    for (int k = 0; k < DD; ++k) z += a.sketch[j * DD + k] * rs[k];
-    const bool sg = live && z >= 0.f;
-    uint32_t words[5];
-    for (int p = 0; p < a.kB; ++p) {
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(((idx >> p) & 1) != 0);
-      words[p] = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
-    }
-    {
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(sg);
-      words[a.kB] = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
-    }
-    if ((lane & 31) == 0) {
-      const int w = wv * 2 + (lane >> 5);
-      uint32_t *dst = a.kbits + (rec * DW + w) * (a.kB + 1);
-      for (int p = 0; p <= a.kB; ++p) dst[p] = words[p];
-    }
-    if (j == 0) {
-      a.knorm[2 * rec] = nrm;
-      a.knorm[2 * rec + 1] = live ? rho : 0.f;
-    }
+  const int64_t off = (int64_t)stream * DD + j;
+  const float x = a.bf16 ? bf16f(((const uint16_t *)a.k)[off]) : ((const float *)a.k)[off];
+  const float xv = a.bf16 ? bf16f(((const uint16_t *)a.v)[off]) : ((const float *)a.v)[off];
+  xs[j] = x;
+  vs[j] = xv;
+  const float nrm = sqrtf(block_sum128(x * x, red));  // also orders the xs / vs writes
+  const float nv = sqrtf(block_sum128(xv * xv, red));
+  float y = 0.f, yv = 0.f;
+#pragma unroll 16
+  for (int k = 0; k < DD; ++k) {
+    const float p = a.rot_t[k * DD + j];  // Pi[j][k], coalesced over j
+    y += p * xs[k];
+    yv += p * vs[k];
   }
-  __syncthreads();
-  // ---- value ----
+  // ---- key: codes, residual, sketch signs ----
+  const bool live = nrm > 0.f;
+  y = live ? y / nrm : 0.f;
+  int idx = 0;
+  for (int i = 0; i < (1 << a.kB) - 1; ++i) idx += (y >= a.tables->boundary[a.kB][i]) ? 1 : 0;
+  if (!live) idx = 0;
+  const float r = live ? y - a.tables->centroid[a.kB][idx] : 0.f;
+  rs[j] = r;
+  const float rho = sqrtf(block_sum128(r * r, red));
+  float z = 0.f;
+#pragma unroll 16
+  for (int k = 0; k < DD; ++k) z += a.sketch_t[k * DD + j] * rs[k];
+  const bool sg = live && z >= 0.f;
+  uint32_t words[5];
+  for (int p = 0; p < a.kB; ++p) {
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(((idx >> p) & 1) != 0);
+    words[p] = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
+  }
   {
-    const int64_t off = (int64_t)stream * DD + j;
-    const float x = a.bf16 ? bf16f(((const uint16_t *)a.v)[off]) : ((const float *)a.v)[off];
-    xs[j] = x;
-    const float nrm = sqrtf(block_sum128(x * x, red));
-    float y = 0.f;
-    for (int k = 0; k < DD; ++k) y += a.rot[j * DD + k] * xs[k];
-    const bool live = nrm > 0.f;
-    y = live ? y / nrm : 0.f;
-    const int L = 1 << a.vB;
-    int idx = 0;
-    for (int i = 0; i < L - 1; ++i) idx += (y >= a.tables->boundary[a.vB][i]) ? 1 : 0;
-    if (!live) idx = 0;
-    const int64_t blk = rec >> 5;
-    const int pos = (int)(rec & 31);
-    uint32_t *dst = a.vbits + (blk * DD + j) * a.vB;
-    for (int p = 0; p < a.vB; ++p) {
-      const uint32_t bit = (uint32_t)((idx >> p) & 1) << pos;
-      dst[p] = (pos == 0) ? bit : ((dst[p] & ~(1u << pos)) | bit);
-    }
-    if (j == 0) a.vnorm[rec] = nrm;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(sg);
+    words[a.kB] = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
+  }
+  if ((lane & 31) == 0) {
+    const int w = wv * 2 + (lane >> 5);
+    uint32_t *dst = a.kbits + (rec * DW + w) * (a.kB + 1);
+    for (int p = 0; p <= a.kB; ++p) dst[p] = words[p];
+  }
+  if (j == 0) {
+    a.knorm[2 * rec] = nrm;
+    a.knorm[2 * rec + 1] = live ? rho : 0.f;
+    a.vnorm[rec] = nv;
+  }
+  // ---- value: codes into the token-major word of this coordinate ----
+  const bool livev = nv > 0.f;
+  yv = livev ? yv / nv : 0.f;
+  int iv = 0;
+  for (int i = 0; i < (1 << a.vB) - 1; ++i) iv += (yv >= a.tables->boundary[a.vB][i]) ? 1 : 0;
+  if (!livev) iv = 0;
+  const int64_t blk = rec >> 5;
+  const int pos = (int)(rec & 31);
+  uint32_t *dst = a.vbits + (blk * DD + j) * a.vB;
+  for (int p = 0; p < a.vB; ++p) {
+    const uint32_t bit = (uint32_t)((iv >> p) & 1) << pos;
+    dst[p] = (pos == 0) ? bit : ((dst[p] & ~(1u << pos)) | bit);
   }
 }
 
@@ -1075,8 +1203,8 @@ hipError_t launch_append(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.k = k;
   a.v = v;
   a.bf16 = is_bf16;
-  a.rot = ctx->d_rot;
-  a.sketch = ctx->d_sketch;
+  a.rot_t = ctx->d_rot_t;
+  a.sketch_t = ctx->d_sketch_t;
   a.tables = ctx->d_tables;
   a.kbits = cache->k.bits;
   a.knorm = cache->k.norms;
