@@ -1,15 +1,18 @@
 """Benchmark of the TurboQuant hot path on one MI355X.
 
-Workload (one "step" = one pass of the whole hot path over one batch):
-batched serving step with 64 sequences x 8192-token context, 8 KV heads,
-32 query heads, head_dim 128, bf16 K/V; prefill quantize of all 64 x 8 x 8192
-K and V vectors (keys b=4: 3-bit Lloyd-Max + 1-bit QJL; values 3-bit), then
-128 decode steps, each appending one quantized token per sequence and running
-decode attention over the packed cache.
+Default workload (`--workload serving`, one "step" = one pass of the whole hot
+path over one batch): batched serving step with 64 sequences x 8192-token
+context, 8 KV heads, 32 query heads, head_dim 128, bf16 K/V; prefill quantize
+of all 64 x 8 x 8192 K and V vectors (keys b=4: 3-bit Lloyd-Max + 1-bit QJL;
+values 3-bit), then 128 decode steps, each appending one quantized token per
+sequence and running decode attention over the packed cache.
 
-Prints ONE JSON line. `value` = attention-score keys/s of the whole step
-(KV-head tokens scored by decode attention, divided by the step time,
-prefill included). Inputs are resident in HBM before the timed region.
+Prints ONE JSON line. For the serving step `value` = attention-score keys/s of
+the whole step (KV-head tokens scored by decode attention divided by the step
+time, prefill included). Inputs are resident in HBM before the timed region.
+
+Other workloads (`--workload gqa|single|search|tiny`) measure the other
+shapes with the same reporting.
 """
 import argparse
 import json
@@ -25,6 +28,10 @@ import numpy as np  # noqa: E402
 
 METRIC = "attention-score keys/s over packed KV (% HBM peak); quantize vectors/s"
 HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3
+KEY_B4 = 72   # bytes per key record at d=128, b=4 (48 code + 16 sign + 8 norm bytes)
+KEY_B3 = 56   # b=3
+VAL_B3 = 52   # 3-bit value record at d=128 (48 code + 4 norm bytes)
 
 
 def parse():
@@ -32,34 +39,64 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", choices=["serving", "gqa", "single", "search", "tiny"], default="serving")
     ap.add_argument("--data", choices=["outlier", "gaussian"], default="outlier")
-    ap.add_argument("--batch", type=int, default=64)
-    ap.add_argument("--ctx", type=int, default=8192)
-    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--kbits", type=int, default=3, help="MSE bits of the keys (b = kbits + 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
 
 
-def cpu_baseline(args, d, kv_heads, group, kbits, vbits, total_keys_per_step, vectors_per_step, decode_tokens):
-    """The oracle as it stands, on a bounded sample of the same workload: whole
-    (sequence, KV head) streams of the prefill (encode 8192 K + 8192 V vectors)
-    and their decode attention for the 4 query heads of that KV head over the
-    full context. Extrapolated to the step: quantize all prefill vectors, plus
-    128 decodes over every stream."""
+def threads_used():
+    try:
+        n = int(os.environ.get("OMP_NUM_THREADS", "0"))
+        return n or len(os.sched_getaffinity(0))
+    except Exception:
+        return os.cpu_count()
+
+
+class Timer:
+    """HIP-event timing on torch's current stream (the stream every tq_* call runs on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+
+    def __call__(self, fn):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        fn()
+        e1.record(self.stream)
+        return (e0, e1)
+
+
+def ms(ev):
+    return ev[0].elapsed_time(ev[1])
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of the workload
+# ---------------------------------------------------------------------------
+
+def oracle_stream_rates(d, L, group, kbits, vbits, seconds, data):
+    """Encode L K + L V vectors of whole streams and run their decode for
+    `group` query heads, until `seconds` of CPU work; returns rates."""
     import synth
     from oracle import turboquant as T
     Pi = T.rotation_from_gaussian(synth.gaussian_matrix(0, synth.TAG_ROTATION, d, d))
     S = T.sketch_from_gaussian(synth.gaussian_matrix(0, synth.TAG_SKETCH, d, d))
     cbk, cbv = T.codebook(d, kbits), T.codebook(d, vbits)
-    L = args.ctx
     t_enc = t_dec = 0.0
-    n_enc = n_dec = 0
-    streams = 0
+    n_enc = n_dec = streams = 0
     t_start = time.perf_counter()
-    while time.perf_counter() - t_start < args.cpu_seconds:
-        K = synth.outlier_kv(0, (streams, 91), synth.TAG_SCALES_K, (L, d))
-        V = synth.outlier_kv(0, (streams, 92), synth.TAG_SCALES_V, (L, d))
+    while time.perf_counter() - t_start < seconds or streams == 0:
+        if data == "outlier":
+            K = synth.outlier_kv(0, (streams, 91), synth.TAG_SCALES_K, (L, d))
+            V = synth.outlier_kv(0, (streams, 92), synth.TAG_SCALES_V, (L, d))
+        else:
+            K = synth.gaussian(0, (streams, 91), (L, d), "bf16")
+            V = synth.gaussian(0, (streams, 92), (L, d), "bf16")
         Q = synth.outlier_kv(0, (streams, 93), synth.TAG_SCALES_K, (group, d))
         t0 = time.perf_counter()
         keys = T.pack_keys(T.encode(K, Pi, cbk, S), kbits)
@@ -72,20 +109,202 @@ def cpu_baseline(args, d, kv_heads, group, kbits, vbits, total_keys_per_step, ve
         n_enc += 2 * L
         n_dec += L
         streams += 1
-    enc_rate = n_enc / t_enc           # vectors/s
-    dec_rate = n_dec / t_dec           # KV-head tokens/s (with `group` query heads each)
-    step_s = vectors_per_step / enc_rate + decode_tokens / dec_rate
-    try:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    except Exception:
-        threads = os.cpu_count()
-    return {
-        "value": total_keys_per_step / step_s, "unit": "keys/s", "cores": threads, "kind": "oracle",
-        "sample": f"{streams} whole streams (encode {L} K + {L} V vectors, decode {group} query heads over {L} "
-                  f"tokens) in {t_enc + t_dec:.1f} s; extrapolated to the step "
-                  f"(oracle quantize {enc_rate:.0f} vectors/s, decode {dec_rate:.0f} keys/s)",
-        "quantize_vectors_per_s": enc_rate, "decode_keys_per_s": dec_rate,
+    return n_enc / t_enc, n_dec / t_dec, streams, t_enc + t_dec
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+def kv_inputs(torch, synth, args, shape, tags, scale_tag):
+    if args.data == "outlier":
+        return synth.torch_outlier_kv(0, tags, scale_tag, shape, torch.bfloat16, "cuda")
+    return synth.torch_gaussian(0, tags, shape, torch.bfloat16, "cuda")
+
+
+def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text):
+    """Prefill quantize of B x H x L K/V, then NS x (append + decode)."""
+    d, kbits, vbits = 128, args.kbits, 3
+    cap = ((L + NS + 31) // 32) * 32
+    ctx = tq.Context(d, 0)
+    K = kv_inputs(torch, synth, args, (B, H, L, d), (3, synth.TAG_KEYS), synth.TAG_SCALES_K)
+    V = kv_inputs(torch, synth, args, (B, H, L, d), (3, synth.TAG_VALUES), synth.TAG_SCALES_V)
+    KA = kv_inputs(torch, synth, args, (max(NS, 1), B, H, d), (3, synth.TAG_APPEND_K), synth.TAG_SCALES_K)
+    VA = kv_inputs(torch, synth, args, (max(NS, 1), B, H, d), (3, synth.TAG_APPEND_V), synth.TAG_SCALES_V)
+    QS = kv_inputs(torch, synth, args, (max(NS, 1), B, Hq, d), (3, synth.TAG_QUERIES), synth.TAG_SCALES_K)
+    cache = tq.KVCache(B, H, cap, d, kbits, vbits)
+    kwork = torch.empty(tq.quantize_ws_bytes(ctx, B * H, L, True), dtype=torch.uint8, device="cuda")
+    cache.host_max_len = cap
+    dws = torch.empty(cache.decode_ws_bytes(ctx, Hq), dtype=torch.uint8, device="cuda")
+    cache.host_max_len = 0
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    timer = Timer(torch)
+    n_dec = max(NS, 1)
+
+    def prefill():
+        tq.quantize_kv(ctx, K.view(B * H, L, d), cache.k, out_stream_stride=cap, work=kwork)
+        tq.quantize_kv(ctx, V.view(B * H, L, d), cache.v, out_stream_stride=cap)
+        cache.seq_len.fill_(L)
+        cache.host_max_len = L
+
+    dec_events = []
+
+    def step(record):
+        prefill()
+        for i in range(n_dec):
+            if NS > 0:
+                cache.append(ctx, KA[i], VA[i])
+            n = L + (i + 1 if NS > 0 else 0)
+            if record:
+                dec_events.append((timer(lambda: cache.decode(ctx, QS[i], out=out, ws=dws)), n))
+            else:
+                cache.decode(ctx, QS[i], out=out, ws=dws)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    pre_ev = timer(prefill)
+    torch.cuda.synchronize()
+    prefill_ms = ms(pre_ev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    whole = timer(lambda: [step(True) for _ in range(args.steps)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ms(whole) / args.steps
+    keys_per_step = sum(B * H * (L + (i + 1 if NS > 0 else 0)) for i in range(n_dec))
+    rec_bytes = (KEY_B4 if kbits == 3 else KEY_B3 if kbits == 2 else (d // 32) * (kbits + 1) * 4 + 8) + VAL_B3
+    dec_ms = np.array([ms(e) for e, _ in dec_events])
+    dec_bytes = np.array([B * H * n * rec_bytes for _, n in dec_events], dtype=np.float64)
+    avg_ms = float(dec_ms.mean())
+    achieved = float(dec_bytes.mean()) / (avg_ms / 1e3) / 1e9
+    vectors = 2 * B * H * L
+    res = {
+        "metric": METRIC, "value": keys_per_step / (ms_per_step / 1e3), "unit": "keys/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32+fp6/fp4/i8 exact-digit MFMA",
+        "data": f"synthetic ({args.data}-channel bf16 K/V, seeded)",
+        "config": {"workload": cfg_text, "batch": B, "context": L, "decode_steps": NS, "kv_heads": H,
+                   "q_heads": Hq, "head_dim": d, "key_bits": kbits + 1, "value_bits": vbits,
+                   "parallelism": "none (1 GPU)"},
+        "quantize_vectors_per_s": vectors / (prefill_ms / 1e3), "prefill_ms": prefill_ms,
+        "decode_keys_per_s": float(B * H * sum(n for _, n in dec_events) / (dec_ms.sum() / 1e3)),
+        "decode_ms_per_launch": avg_ms, "wall_s_timed": wall,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tq_attention_decode (decode_prep_kernel + decode_kernel + decode_merge_kernel)",
+                     "algorithmic_bytes_per_launch": float(dec_bytes.mean()), "avg_launch_ms": avg_ms,
+                     "bytes_per_kv_token": rec_bytes},
     }
+    if not args.no_cpu_baseline:
+        enc_rate, dec_rate, streams, secs = oracle_stream_rates(d, min(L, 8192), Hq // H, kbits, vbits,
+                                                               args.cpu_seconds, args.data)
+        step_s = vectors / enc_rate + keys_per_step / dec_rate
+        res["cpu_baseline"] = {
+            "value": keys_per_step / step_s, "unit": "keys/s", "cores": threads_used(), "kind": "oracle",
+            "sample": f"{streams} whole (sequence, KV head) streams of {min(L, 8192)} tokens: oracle encode of "
+                      f"their K and V vectors and decode for {Hq // H} query heads, {secs:.1f} s of CPU work; "
+                      f"extrapolated to the step at {enc_rate:.0f} vectors/s and {dec_rate:.0f} keys/s",
+            "quantize_vectors_per_s": enc_rate, "decode_keys_per_s": dec_rate}
+    return res
+
+
+def run_search(args, torch, tq, synth):
+    """Vector search: 1e6 unit-norm Gaussian vectors at d=1536 quantized at b=4,
+    1000 queries scored against all of them, top-10 each."""
+    d, N, NQ, K = 1536, 1_000_000, 1000, 10
+    ctx = tq.Context(d, 0)
+    X = synth.torch_unit_gaussian(0, (4, synth.TAG_DB), (N, d), "cuda")
+    Qd = synth.torch_unit_gaussian(0, (4, synth.TAG_QUERIES), (NQ, d), "cuda")
+    keys = tq.Packed(N, d, 3, True)
+    work = torch.empty(tq.quantize_ws_bytes(ctx, 1, N, True), dtype=torch.uint8, device="cuda")
+    sws = torch.empty(tq.scores_ws_bytes(ctx, NQ, N, K, False), dtype=torch.uint8, device="cuda")
+    timer = Timer(torch)
+    ev = {"q": [], "s": []}
+
+    def step(record):
+        a = timer(lambda: tq.quantize_kv(ctx, X, keys, work=work))
+        b = timer(lambda: tq.scores(ctx, Qd, keys, want_scores=False, topk=K, ws=sws))
+        if record:
+            ev["q"].append(a)
+            ev["s"].append(b)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    whole = timer(lambda: [step(True) for _ in range(args.steps)])
+    torch.cuda.synchronize()
+    ms_per_step = ms(whole) / args.steps
+    q_ms = float(np.mean([ms(e) for e in ev["q"]]))
+    s_ms = float(np.mean([ms(e) for e in ev["s"]]))
+    _, ti, _ = tq.scores(ctx, Qd, keys, want_scores=False, topk=K, ws=sws)
+    exact = torch.empty((NQ, K), dtype=torch.int64, device="cuda")
+    for q0 in range(0, NQ, 100):
+        exact[q0:q0 + 100] = torch.topk(Qd[q0:q0 + 100] @ X.T, K, dim=1).indices
+    hits = sum(len(set(a) & set(b)) for a, b in zip(ti.cpu().numpy().tolist(), exact.cpu().numpy().tolist()))
+    score_flops = 2.0 * NQ * N * 2 * d
+    quant_flops = 2.0 * N * d * (d + d)
+    res = {
+        "metric": "vector search pair-scores/s (top-10 fused); quantize vectors/s", "value": NQ * N / (ms_per_step / 1e3),
+        "unit": "pair-scores/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic (unit-norm Gaussian, seeded)",
+        "config": {"workload": "vector_search: 1e6 x d=1536 unit Gaussian, b=4, 1000 queries, top-10", "n": N, "d": d, "queries": NQ},
+        "quantize_vectors_per_s": N / (q_ms / 1e3), "quantize_ms": q_ms, "scores_topk_ms": s_ms,
+        "recall_at_10": hits / (NQ * K),
+        "roofline": {"bound": "mfma", "achieved": score_flops / (s_ms / 1e3) / 1e12, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": score_flops / (s_ms / 1e3) / 1e12 / FP32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "tq_scores (query prep GEMMs + packed-key score GEMM + top-k)",
+                     "quantize_tflops": quant_flops / (q_ms / 1e3) / 1e12},
+    }
+    if not args.no_cpu_baseline:
+        import synth as sy
+        from oracle import turboquant as T
+        Pi = T.rotation_from_gaussian(sy.gaussian_matrix(0, sy.TAG_ROTATION, d, d))
+        S = T.sketch_from_gaussian(sy.gaussian_matrix(0, sy.TAG_SKETCH, d, d))
+        cb = T.codebook(d, 3)
+        Xs = sy.unit_gaussian(0, (4, 99), (4096, d))
+        Qs = sy.unit_gaussian(0, (4, 98), (100, d))
+        t0 = time.perf_counter()
+        enc = T.encode(Xs, Pi, cb, S)
+        t1 = time.perf_counter()
+        q_rot, q_s = T.query_prep(Qs, Pi, S)
+        sc = T.scores_from_parts(q_rot, q_s, enc.idx, enc.sigma, enc.norm, enc.rho, cb, d)
+        [T.topk(r, K) for r in sc]
+        t2 = time.perf_counter()
+        enc_rate, pair_rate = 4096 / (t1 - t0), 100 * 4096 / (t2 - t1)
+        res["cpu_baseline"] = {"value": NQ * N / (N / enc_rate + NQ * N / pair_rate), "unit": "pair-scores/s",
+                               "cores": threads_used(), "kind": "oracle",
+                               "sample": f"encode 4096 vectors and score/top-10 100 queries against them "
+                                         f"({t2 - t0:.1f} s); extrapolated to the step",
+                               "quantize_vectors_per_s": enc_rate, "pair_scores_per_s": pair_rate}
+    return res
+
+
+def run_tiny(args, torch, tq, synth):
+    """4096 fp32 keys at d=128, b=3; 16 queries; the 16 x 4096 score matrix."""
+    d = 128
+    ctx = tq.Context(d, 0)
+    X = torch.from_numpy(synth.gaussian(0, (0, synth.TAG_KEYS), (4096, d))).cuda()
+    Q = torch.from_numpy(synth.gaussian(0, (0, synth.TAG_QUERIES), (16, d))).cuda()
+    keys = tq.Packed(4096, d, 2, True)
+    timer = Timer(torch)
+    evs = []
+
+    def step():
+        tq.quantize_kv(ctx, X, keys)
+        tq.scores(ctx, Q, keys)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        evs.append(timer(step))
+    torch.cuda.synchronize()
+    ms_per_step = float(np.mean([ms(e) for e in evs]))
+    return {"metric": "tiny reference: quantize + 16x4096 scores (cache-resident, launch-bound)", "value": 4096 / (ms_per_step / 1e3),
+            "unit": "vectors/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "tiny_reference: 4096 x d=128 fp32 N(0,1), b=3, 16 queries"}, "roofline": None}
 
 
 def main():
@@ -100,117 +319,23 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
-    dev = "cuda"
-    d, kv_heads, q_heads, kbits, vbits = 128, 8, 32, 3, 3
-    B, L, NS = args.batch, args.ctx, args.decode_steps
-    cap = ((L + NS + 31) // 32) * 32
-    group = q_heads // kv_heads
-    ctx = tq.Context(d, 0)
-
-    # ---- inputs resident in HBM (seeded, synthetic) ----
-    gen = synth.torch_outlier_kv if args.data == "outlier" else None
-
-    def kv(tags, scale_tag, shape):
-        if gen is not None:
-            return gen(0, tags, scale_tag, shape, torch.bfloat16, dev)
-        return synth.torch_gaussian(0, tags, shape, torch.bfloat16, dev)
-
-    K = kv((3, synth.TAG_KEYS), synth.TAG_SCALES_K, (B, kv_heads, L, d))
-    V = kv((3, synth.TAG_VALUES), synth.TAG_SCALES_V, (B, kv_heads, L, d))
-    KA = kv((3, synth.TAG_APPEND_K), synth.TAG_SCALES_K, (NS, B, kv_heads, d))
-    VA = kv((3, synth.TAG_APPEND_V), synth.TAG_SCALES_V, (NS, B, kv_heads, d))
-    QS = kv((3, synth.TAG_QUERIES), synth.TAG_SCALES_K, (NS, B, q_heads, d))
-    cache = tq.KVCache(B, kv_heads, cap, d, kbits, vbits)
-    kwork = torch.empty(tq.quantize_ws_bytes(ctx, B * kv_heads, L, True), dtype=torch.uint8, device=dev)
-    cache.host_max_len = L + NS
-    dws = torch.empty(cache.decode_ws_bytes(ctx, q_heads), dtype=torch.uint8, device=dev)
-    cache.host_max_len = 0
-    out = torch.empty((B, q_heads, d), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def prefill():
-        tq.quantize_kv(ctx, K.view(B * kv_heads, L, d), cache.k, out_stream_stride=cap, work=kwork)
-        tq.quantize_kv(ctx, V.view(B * kv_heads, L, d), cache.v, out_stream_stride=cap)
-        cache.seq_len.fill_(L)
-        cache.host_max_len = L
-
-    ev_dec = []
-
-    def step(record=False):
-        prefill()
-        for i in range(NS):
-            cache.append(ctx, KA[i], VA[i])
-            if record:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                cache.decode(ctx, QS[i], out=out, ws=dws)
-                e1.record(stream)
-                ev_dec.append((e0, e1, L + i + 1))
-            else:
-                cache.decode(ctx, QS[i], out=out, ws=dws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # prefill-only timing (quantize vectors/s), outside the step loop
-    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    pe0.record(stream)
-    prefill()
-    pe1.record(stream)
-    torch.cuda.synchronize()
-    prefill_ms = pe0.elapsed_time(pe1)
-
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    for _ in range(args.steps):
-        step(record=True)
-    s1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = s0.elapsed_time(s1)
-    ms_per_step = total_ms / args.steps
-
-    keys_per_step = sum(B * kv_heads * (L + i + 1) for i in range(NS))
-    value = keys_per_step / (ms_per_step / 1e3)
-    vectors_per_step = 2 * B * kv_heads * L
-    # dominant kernel: decode attention (prep + chunked score/softmax/value + merge launches)
-    dec_ms = [e0.elapsed_time(e1) for (e0, e1, _) in ev_dec]
-    dec_bytes = [B * kv_heads * n * (T_KEY_BYTES + T_VAL_BYTES) for (_, _, n) in ev_dec]
-    avg_ms = float(np.mean(dec_ms))
-    avg_bytes = float(np.mean(dec_bytes))
-    achieved = avg_bytes / (avg_ms / 1e3) / 1e9
-    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "tq_attention_decode (decode_prep + decode_kernel<3,3> + decode_merge)",
-            "algorithmic_bytes_per_launch": avg_bytes, "avg_launch_ms": avg_ms}
-    res = {
-        "metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32+i8", "data": f"synthetic ({args.data}-channel bf16 K/V, seeded)",
-        "config": {"workload": f"batched_serving_step: {B} seq x {L} ctx, {kv_heads} KV heads, {q_heads} q heads, "
-                               f"d={d}, keys b=4 (3+1 QJL), values 3-bit, prefill quantize + {NS} x "
-                               f"(append + decode attention)",
-                   "batch": B, "context": L, "decode_steps": NS, "kv_heads": kv_heads, "q_heads": q_heads,
-                   "head_dim": d, "parallelism": "none (1 GPU)"},
-        "quantize_vectors_per_s": vectors_per_step / (prefill_ms / 1e3),
-        "prefill_ms": prefill_ms,
-        "decode_keys_per_s": float(np.sum([B * kv_heads * n for (_, _, n) in ev_dec]) / (np.sum(dec_ms) / 1e3)),
-        "wall_s_timed": wall,
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        decode_tokens = keys_per_step
-        res["cpu_baseline"] = cpu_baseline(args, d, kv_heads, group, kbits, vbits, keys_per_step,
-                                           vectors_per_step, decode_tokens)
+    if args.workload == "serving":
+        res = run_decode_workload(args, torch, tq, synth, 64, 8, 32, 8192, 128, "serving",
+                                  "batched_serving_step: 64 seq x 8192 ctx, 8 KV heads, 32 q heads, d=128, "
+                                  f"keys b={args.kbits + 1}, values 3-bit, prefill quantize + 128 x (append + decode)")
+    elif args.workload == "gqa":
+        res = run_decode_workload(args, torch, tq, synth, 4, 8, 32, 131072, 0, "gqa",
+                                  "gqa_layer: batch 4 x 131072 ctx, 8 KV heads, 32 q heads, d=128, "
+                                  f"keys b={args.kbits + 1}, values 3-bit, prefill quantize + 1 decode")
+    elif args.workload == "single":
+        res = run_decode_workload(args, torch, tq, synth, 1, 1, 1, 32768, 0, "single",
+                                  "single_head_decode: 32768 ctx, d=128, keys b=4, values 3-bit, quantize + 1 decode")
+    elif args.workload == "search":
+        res = run_search(args, torch, tq, synth)
+    else:
+        res = run_tiny(args, torch, tq, synth)
     print(json.dumps(res), flush=True)
 
-
-# algorithmic bytes per KV-head token at d = 128: key record 72 B (48 B codes + 16 B signs + 8 B norms),
-# value record 52 B (48 B codes + 4 B norm)
-T_KEY_BYTES = 72
-T_VAL_BYTES = 52
 
 if __name__ == "__main__":
     main()
