@@ -44,7 +44,21 @@ def parse():
     ap.add_argument("--kbits", type=int, default=3, help="MSE bits of the keys (b = kbits + 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run 5 device-to-device copies of this many MiB (a plain copy kernel of known size, "
+                         "the calibration of the rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_probe(torch, mib):
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "copies": 5}), flush=True)
 
 
 def threads_used():
@@ -319,6 +333,9 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.copy_probe_mib > 0:
+        copy_probe(torch, args.copy_probe_mib)
+        return
     if args.workload == "serving":
         res = run_decode_workload(args, torch, tq, synth, 64, 8, 32, 8192, 128, "serving",
                                   "batched_serving_step: 64 seq x 8192 ctx, 8 KV heads, 32 q heads, d=128, "

@@ -13,10 +13,13 @@ LIB = os.path.join(HERE, "libtq.so")
 SOURCES = ["tq_host.cpp", "tq_kernels.hip"]
 
 # Packed FP32 VALU ops are disabled for device code; the host pass warns that
-# it does not know the feature, which is harmless.
+# it does not know the feature, which is harmless. MFMA results go to ordinary
+# VGPRs (no accumulation registers): reading them back then costs no
+# v_accvgpr_read per element, and the decode kernels fit four waves per SIMD.
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-result",
 ]
 

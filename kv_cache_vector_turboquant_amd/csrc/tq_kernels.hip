@@ -15,9 +15,10 @@
 //                      epilogues: key codes + residual, key QJL signs, value
 //                      codes (token-major), plain store, and packed-key scores.
 //  decode_prep_kernel  rotates/sketches the decode queries and splits them into
-//                      exact int8 digits laid out as MFMA A fragments.
-//  decode_kernel       split-K decode attention over packed K/V: scores and
-//                      value sums run on int8 MFMA over 0/1 bit masks.
+//                      exact fp6 digits laid out as MFMA A fragments.
+//  decode_kernel       split-K decode attention over packed K/V: key scores on
+//                      fp6 x fp4 MFMA, value sums on int8 MFMA, both over bit
+//                      masks.
 //  decode_merge_kernel log-sum-exp merge of the chunks and inverse rotation.
 //  append_kernel       quantizes one K and one V vector per stream in place.
 //  topk_kernel         per-query top-k by (-score, index).
@@ -537,27 +538,39 @@ hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t 
 // Scores and value sums are linear in 0/1 masks of the packed bit-planes. The
 // centroid table is antisymmetric (c[L-1-i] = -c[i]), so with s_p = 2 b_p - 1
 // it expands over odd Walsh functions: c[idx] = sum_S w_S prod_{p in S} s_p,
-// and prod_{p in S} s_p = 2 (XOR of planes in S) - 1. Hence
+// and prod_{p in S} s_p = 2 (XOR of planes in S) - 1 = chi_S. Hence
 //   sum_j q_j c[idx_j] = sum_S w_S (2 M_S - sum_j q_j),  M_S = sum_j q_j mask_S,j.
-// Keys: with chi = 2 mask - 1 in {-1, +1}, sum_j q_j c[idx_j] = sum_S w_S sum_j
-// q_j chi_S,j. The query is fixed point, split into 8 signed base-8 digits held
-// as fp6 (e2m3) A operands; the signed masks are fp4 (e2m1) B operands built
-// from a plane word w with one shift, and and xor per 8 coordinates; the MFMA
-// is v_mfma_scale_f32_16x16x128_f8f6f4 with per-row block scales 2^(3 digit),
-// so A row (4*head + slot) accumulates digits slot and slot+4 exactly and the
-// four rows of a head sum to sum_j Q_j chi_j.
-// Values: the softmax weight is fixed point with 3 signed int8 digits, the
-// masks are 0/1 bytes made as (w >> q) & 0x01010101, and every masked sum is an
-// exact int32 from v_mfma_i32_16x16x64_i8; A row = 4*head + digit.
+//
+// Keys (v_mfma_scale_f32_16x16x128_f8f6f4, fp6 A x fp4 B): the query is fixed
+// point, split into 8 signed base-8 digits. A row (4*head + slot) carries digit
+// slot (first instruction) and slot+4 (second), with e8m0 row scales 2^(3 digit).
+// The B operand of a plane word w is four dwords of 0/1 fp4 nibbles, each made
+// by one AND (one shift and AND for the last): nibble i of dword q holds bit
+// 4i+q of w at nibble bit 0, 1, 2, 2 (values 0.5, 1, 2, 2 for q = 0..3). The A
+// digits of element (q, i) are pre-scaled by 1, 1/2, 1/4, 1/4 (all exact in
+// e2m3), so every product is d * b / 2; the B scale 2^2 makes each row
+// accumulate 2 sum_j Q_j b_j, and the accumulator starts at -sum_j Q_j (per
+// slot), so each row ends at sum_j Q_j chi_j of its digit slot, exactly (every
+// partial sum is a multiple of 2^(3 slot) below 2^(3 slot + 23)).
+//
+// Values (v_mfma_i32_16x16x64_i8): token t of a 32-token block sits at bit
+// t % 32 of the plane word, bit q + 8 k' for q = t % 8. The B bytes are w AND
+// (0x01010101 << q): one AND per four tokens, byte values b * 2^q (q = 7 gives
+// -128 b). The A digits compensate per token: the weight p * |v| is fixed point
+// at 2^29 (relative to the chunk's largest |v|), divided by 2^q before
+// rounding (negated for q = 7), and split into four signed base-256 digits,
+// A row = 4*head + digit. Every weight keeps at least 22 bits; the int32 sums
+// are exact, and o = unit * sum_S w_S (2 M_S - sum_t E_t) in double.
 // ---------------------------------------------------------------------------
 
 constexpr int DD = 128;            // head dim
 constexpr int DW = DD / 32;        // 32-coordinate groups
 constexpr float QMAX = 7190000.f;  // |fixed-point query| bound with 8 signed base-8 digits in [-4, 3]
 typedef int i8v __attribute__((ext_vector_type(8)));
-constexpr float WSCALE = 4194304.f;  // 2^22: fixed point of the value weights
+constexpr float WSCALE = 536870912.f;  // 2^29: fixed point of the value weights
 constexpr int KTPW = 2;            // key tiles (16 tokens each) per wave per round (double-buffered)
 constexpr int VGPI = 2;            // 128-token value groups per iteration
+constexpr int QC = 2;              // per-head query constants: units of the q_rot and q_s digits
 
 struct DecodeArgs {
   const uint32_t *kbits;
@@ -575,50 +588,69 @@ struct DecodeArgs {
   int q_bf16;
   const float *rot, *rs_t;  // rs_t: [Pi ; S Pi]^T, 128 x 256 row-major
   uint32_t *qfrag;       // [stream*hgroups][2 (q_rot, q_s)][2 (digits 0-3, 4-7)][64 lanes][8] fp6 fragments
-  float *qconst;         // [stream*hgroups][4][4]: scale_r, scale_s, -, -
+  float *qconst;         // [stream*hgroups][4][QC]: units of the fixed-point q_rot, q_s
   float *partial;        // [batch*q_heads][nchunks][DD + 2]
   float *out;
 };
-
-__device__ __forceinline__ int sdigit(int v) { return ((v & 0xFF) ^ 0x80) - 0x80; }
 
 // The i-th odd-cardinality subset of the B planes, ordered by (popcount, value).
 __host__ __device__ constexpr int walsh_mask(int B, int i) {
   return i < B ? (1 << i) : (B == 3 ? 7 : (i == 4 ? 7 : i == 5 ? 11 : i == 6 ? 13 : 14));
 }
 
+// e2m3 code of |digit| * f for f = 1, 1/2, 1/4 (f index fi = 0, 1, 2), |digit| <= 4:
+// f = 1: 1 -> 0x08, 2 -> 0x10, 3 -> 0x14, 4 -> 0x18; f = 1/2: code 4m; f = 1/4: code 2m.
+__device__ __forceinline__ uint32_t fp6_mag(uint32_t mag, int fi) {
+  const uint32_t c1 = mag <= 1u ? (mag << 3) : (8u + (mag << 2));
+  return fi == 0 ? c1 : (mag << (fi == 1 ? 2 : 1));
+}
+
 // One block per (stream, head group): q_rot = Pi q, q_s = S q_rot for up to 4
 // heads, fixed-point split and A-fragment layout.
+template <typename QT>
+__device__ __forceinline__ float qload(const QT *q, int64_t i) {
+  if constexpr (sizeof(QT) == 2) return bf16f(q[i]);
+  else return q[i];
+}
+
+template <typename QT>
 __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
-  __shared__ float qf[4][DD], qr[4][DD], qs[4][DD], part2[4][2 * DD];
-  __shared__ int8_t qd[2][4][DD][8];  // base-8 digits of the fixed-point q_rot / q_s
-  __shared__ float mx[2][4];  // max |q_rot|, max |q_s| per head
+  __shared__ __attribute__((aligned(16))) float qk[DD][4];  // the queries, [coordinate][head]
+  __shared__ float part2[4][2 * DD];
+  __shared__ float qv[2][4][DD];  // q_rot, q_s
+  __shared__ float mx[2][4];      // max |q_rot|, max |q_s| per head
+  // fp6 codes, one per byte: [type][head][digit][32-coordinate group g][element e],
+  // element e = 8q + i <-> coordinate 32g + 4i + q (the fp4 mask order)
+  __shared__ __attribute__((aligned(16))) uint8_t cl[2][4][8][4][32];
   const int tid = threadIdx.x;
   const int sg = blockIdx.x;  // stream * hgroups + hg
   const int hg = sg % a.hgroups, stream = sg / a.hgroups;
   const int b = stream / a.kv_heads, kvh = stream % a.kv_heads;
   const int h0 = kvh * a.group + hg * 4;
   const int nh = min(4, a.group - hg * 4);
-  for (int e = tid; e < 4 * DD; e += 512) {
-    const int hh = e / DD, j = e % DD;
-    float v = 0.f;
-    if (hh < nh) {
-      const int64_t off = ((int64_t)b * a.q_heads + h0 + hh) * DD + j;
-      v = a.q_bf16 ? bf16f(((const uint16_t *)a.q)[off]) : ((const float *)a.q)[off];
-    }
-    qf[hh][j] = v;
+  // thread (r, k half) owns row r of [Pi ; S Pi] (r < 128: q_rot, else q_s) over
+  // half of k: its 64 matrix entries (transposed matrix: reads coalesced over r)
+  // are all requested before the queries are staged
+  const int r = tid & 255, kh = tid >> 8;
+  float mrow[64];
+#pragma unroll
+  for (int u = 0; u < 64; ++u) mrow[u] = a.rs_t[(kh * 64 + u) * 2 * DD + r];
+  const QT *q = reinterpret_cast<const QT *>(a.q) + ((int64_t)b * a.q_heads + h0) * DD;
+  {
+    const int hh = tid >> 7, k = tid & (DD - 1);
+    qk[k][hh] = hh < nh ? qload(q, (int64_t)hh * DD + k) : 0.f;
   }
   __syncthreads();
-  // thread (r, k half): row r of [Pi ; S Pi] (r < 128: q_rot, else q_s) against the
-  // four queries over half of k; the transposed matrix makes the reads coalesced over r
+  // one 16-byte LDS broadcast gives the four query entries of a k
   {
-    const int r = tid & 255, kh = tid >> 8;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 32
-    for (int k = kh * 64; k < kh * 64 + 64; ++k) {
-      const float m = a.rs_t[k * 2 * DD + r];
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) acc[hh] += m * qf[hh][k];
+    for (int u = 0; u < 64; ++u) {
+      const float4 qq = *reinterpret_cast<const float4 *>(qk[kh * 64 + u]);
+      acc[0] = fmaf(mrow[u], qq.x, acc[0]);
+      acc[1] = fmaf(mrow[u], qq.y, acc[1]);
+      acc[2] = fmaf(mrow[u], qq.z, acc[2]);
+      acc[3] = fmaf(mrow[u], qq.w, acc[3]);
     }
     if (kh == 1) {
 #pragma unroll
@@ -627,11 +659,7 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
     __syncthreads();
     if (kh == 0) {
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const float v = acc[hh] + part2[hh][r];
-        if (r < DD) qr[hh][r] = v;
-        else qs[hh][r - DD] = v;
-      }
+      for (int hh = 0; hh < 4; ++hh) qv[r >> 7][hh][r & (DD - 1)] = acc[hh] + part2[hh][r];
     }
   }
   __syncthreads();
@@ -639,49 +667,57 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
     // max |.| per (type, head): wave w reduces (type, head pair) rows
     const int lane = tid & 63, w = tid >> 6, T = w >> 1;
     for (int hh = (w & 1) * 2; hh < (w & 1) * 2 + 2; ++hh) {
-      const float *row = T ? qs[hh] : qr[hh];
+      const float *row = qv[T][hh];
       float m = fmaxf(fabsf(row[lane]), fabsf(row[lane + 64]));
       for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
       if (lane == 0) mx[T][hh] = m;
     }
   }
   __syncthreads();
-  for (int e = tid; e < 2 * 4 * DD; e += 512) {
-    const int T = e / (4 * DD), hh = (e / DD) & 3, j = e % DD;
-    const float m = mx[T][hh];
-    const float v = T ? qs[hh][j] : qr[hh][j];
-    int q = m > 0.f ? (int)rintf(v * (QMAX / m)) : 0;
+  {
+    // thread (head, coordinate): balanced base-8 digits in [-4, 3] of both query
+    // types, stored as e2m3 codes of digit * (1, 1/2, 1/4, 1/4)[j % 4]
+    const int hh = tid >> 7, j = tid & (DD - 1);
+    const int g = j >> 5, e = 8 * (j & 3) + ((j >> 2) & 7), fi = min(j & 3, 2);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {  // balanced base-8 digits in [-4, 3]
-      const int dv = ((q + 4) & 7) - 4;
-      qd[T][hh][j][k] = (int8_t)dv;
-      q = (q - dv) >> 3;
+    for (int T = 0; T < 2; ++T) {
+      const float m = mx[T][hh];
+      int qi = m > 0.f ? (int)rintf(qv[T][hh][j] * (QMAX / m)) : 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int dv = ((qi + 4) & 7) - 4;
+        qi = (qi - dv) >> 3;
+        cl[T][hh][k][g][e] = (uint8_t)(fp6_mag((uint32_t)(dv < 0 ? -dv : dv), fi) | (dv < 0 ? 0x20u : 0u));
+      }
     }
   }
   if (tid < 8) {
     const int T = tid >> 2, hh = tid & 3;
-    float *qc = a.qconst + ((int64_t)sg * 4 + hh) * 4;
     const float m = mx[T][hh];
-    qc[T] = m > 0.f ? m / QMAX : 0.f;
+    a.qconst[((int64_t)sg * 4 + hh) * QC + T] = m > 0.f ? m / QMAX : 0.f;
   }
   __syncthreads();
   if (tid < 256) {
-    // fragment (T, instr, lane): 32 fp6 digits of row (4*hh + slot), digit 4*instr + slot;
-    // element s = 8q + i <-> coordinate 32g + 4i + q (the fp4 mask order), 6 bits at bit 6s
+    // fragment (T, instr, lane): the 32 codes of row (4*hh + slot), digit 4*instr + slot,
+    // packed at 6 bits each (element e at bit 6e): every 4 codes make 24 bits
     const int T = tid >> 7, ins = (tid >> 6) & 1, L = tid & 63;
     const int g = L >> 4, row = L & 15, hh = row >> 2, dig = 4 * ins + (row & 3);
-    uint32_t dw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const uint4 *src = reinterpret_cast<const uint4 *>(&cl[T][hh][dig][g][0]);
+    const uint4 c0 = src[0], c1 = src[1];
+    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    uint32_t t24[8];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int j = 32 * g + 4 * (e & 7) + (e >> 3);
-      const int dv = qd[T][hh][j][dig];
-    const uint32_t mag = (uint32_t)(dv < 0 ? -dv : dv);
-      // e2m3: 1 -> 0b001000, 2 -> 0b010000, 3 -> 0b010100, 4 -> 0b011000; sign bit 0b100000
-      const uint32_t code = (mag == 0 ? 0u : mag == 1 ? 0x08u : mag == 2 ? 0x10u : mag == 3 ? 0x14u : 0x18u) |
-                            (dv < 0 ? 0x20u : 0u);
-      const int bit = 6 * e;
-      dw[bit >> 5] |= code << (bit & 31);
-      if ((bit & 31) > 26) dw[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+    for (int m = 0; m < 8; ++m) {
+      const uint32_t w = cw[m];
+      t24[m] = (w & 0x3Fu) | ((w >> 2) & 0xFC0u) | ((w >> 4) & 0x3F000u) | ((w >> 6) & 0xFC0000u);
+    }
+    uint32_t dw[6];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // 4 chunks of 24 bits -> 3 dwords
+      const uint32_t *t = t24 + 4 * h;
+      dw[3 * h + 0] = t[0] | (t[1] << 24);
+      dw[3 * h + 1] = (t[1] >> 8) | (t[2] << 16);
+      dw[3 * h + 2] = (t[2] >> 16) | (t[3] << 8);
     }
     uint4 *dst = reinterpret_cast<uint4 *>(a.qfrag + ((((int64_t)sg * 2 + T) * 2 + ins) * 64 + L) * 8);
     dst[0] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
@@ -689,25 +725,28 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
   }
 }
 
-__device__ __forceinline__ void mask_bytes(uint32_t m, i4v &lo, i4v &hi) {
+// Value B bytes of a token-major plane word: byte k' of dword q is bit q + 8k'
+// of m, left in place (value b * 2^q; -128 b for q = 7).
+__device__ __forceinline__ void mask_bytes_pow2(uint32_t m, i4v &lo, i4v &hi) {
   lo[0] = (int)(m & 0x01010101u);
-  lo[1] = (int)((m >> 1) & 0x01010101u);
-  lo[2] = (int)((m >> 2) & 0x01010101u);
-  lo[3] = (int)((m >> 3) & 0x01010101u);
-  hi[0] = (int)((m >> 4) & 0x01010101u);
-  hi[1] = (int)((m >> 5) & 0x01010101u);
-  hi[2] = (int)((m >> 6) & 0x01010101u);
-  hi[3] = (int)((m >> 7) & 0x01010101u);
+  lo[1] = (int)(m & 0x02020202u);
+  lo[2] = (int)(m & 0x04040404u);
+  lo[3] = (int)(m & 0x08080808u);
+  hi[0] = (int)(m & 0x10101010u);
+  hi[1] = (int)(m & 0x20202020u);
+  hi[2] = (int)(m & 0x40404040u);
+  hi[3] = (int)(m & 0x80808080u);
 }
 
-// Signed fp4 mask of a 32-coordinate plane word: element 8q + i (nibble i of
-// dword q) is +1 (0x2) if bit 4i + q of w is set, else -1 (0xA).
-__device__ __forceinline__ i8v mask_fp4_pm(uint32_t w) {
+// Key B operand of a 32-coordinate plane word: element 8q + i (nibble i of
+// dword q) is bit 4i + q of w as a 0/1 fp4 value scaled by 0.5, 1, 2, 2 for
+// q = 0..3 (the A digits carry the inverse factors).
+__device__ __forceinline__ i8v mask_fp4_01(uint32_t w) {
   i8v b;
-  b[0] = (int)(((w << 3) & 0x88888888u) ^ 0xAAAAAAAAu);
-  b[1] = (int)(((w << 2) & 0x88888888u) ^ 0xAAAAAAAAu);
-  b[2] = (int)(((w << 1) & 0x88888888u) ^ 0xAAAAAAAAu);
-  b[3] = (int)((w & 0x88888888u) ^ 0xAAAAAAAAu);
+  b[0] = (int)(w & 0x11111111u);
+  b[1] = (int)(w & 0x22222222u);
+  b[2] = (int)(w & 0x44444444u);
+  b[3] = (int)((w >> 1) & 0x44444444u);
   b[4] = b[5] = b[6] = b[7] = 0;
   return b;
 }
@@ -721,17 +760,97 @@ __device__ __forceinline__ uint32_t xor_planes(const uint32_t (&pl)[NP], int S) 
   return m;
 }
 
-__device__ __forceinline__ int combine_digits(const i4v &acc) { return acc[0] + (acc[1] << 8) + (acc[2] << 16); }
+// One block of 1024 threads per (stream, head group): log-sum-exp merge of the
+// chunk partials, then o = Pi^T o_rot. The chunks are split over four thread
+// groups (max pass, then scaled sums), so long contexts keep many loads in flight.
+__global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
+  constexpr int MG = 4, CB = 8;
+  __shared__ float gmax[MG][4], gl[MG][4];
+  __shared__ float po[MG][4][DD];
+  __shared__ float orot[4][DD];
+  __shared__ float pk[8][4][DD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int sg = blockIdx.x;
+  const int hg = sg % a.hgroups, stream = sg / a.hgroups;
+  const int b = stream / a.kv_heads;
+  const int h0 = (stream % a.kv_heads) * a.group + hg * 4;
+  const int nh = min(4, a.group - hg * 4);
+  const int cg = tid >> 8, hh = (tid >> 6) & 3;  // chunk group, head (one wave per pair)
+  const int nc = a.nchunks;
+  const float *p = a.partial + ((int64_t)b * a.q_heads + h0 + min(hh, nh - 1)) * nc * (DD + 2);
+  // global max of the chunk maxima of this head
+  float m = -INFINITY;
+  for (int c = cg * 64 + lane; c < nc; c += MG * 64) m = fmaxf(m, p[(int64_t)c * (DD + 2) + DD]);
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) gmax[cg][hh] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(gmax[0][hh], gmax[1][hh]), fmaxf(gmax[2][hh], gmax[3][hh]));
+  // this group's chunks c = cg (mod 4): lane owns coordinates lane and lane + 64
+  float O0 = 0.f, O1 = 0.f, L = 0.f;
+  for (int c0 = cg; c0 < nc; c0 += MG * CB) {
+    float mv[CB], lv[CB], o0[CB], o1[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int c = min(c0 + u * MG, nc - 1);
+      const float *pc = p + (int64_t)c * (DD + 2);
+      mv[u] = c0 + u * MG < nc ? pc[DD] : -INFINITY;
+      lv[u] = pc[DD + 1];
+      o0[u] = pc[lane];
+      o1[u] = pc[lane + 64];
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const float f = mv[u] == -INFINITY ? 0.f : exp2f(mv[u] - M);
+      L = fmaf(f, lv[u], L);
+      O0 = fmaf(f, o0[u], O0);
+      O1 = fmaf(f, o1[u], O1);
+    }
+  }
+  po[cg][hh][lane] = O0;
+  po[cg][hh][lane + 64] = O1;
+  if (lane == 0) gl[cg][hh] = L;
+  __syncthreads();
+  if (tid < 4 * DD) {
+    const int h = tid >> 7, j = tid & (DD - 1);
+    const float Lh = (gl[0][h] + gl[1][h]) + (gl[2][h] + gl[3][h]);
+    const float Oh = (po[0][h][j] + po[1][h][j]) + (po[2][h][j] + po[3][h][j]);
+    orot[h][j] = (h < nh && Lh > 0.f) ? Oh / Lh : 0.f;
+  }
+  __syncthreads();
+  // o = Pi^T o_rot: column j of Pi (coalesced over j), k split in eight slices
+  {
+    const int j = tid & (DD - 1), kg = tid >> 7;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = kg * 16; k < kg * 16 + 16; ++k) {
+      const float r = a.rot[k * DD + j];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) acc[h] = fmaf(r, orot[h][k], acc[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pk[kg][h][j] = acc[h];
+  }
+  __syncthreads();
+  if (tid < 4 * DD) {
+    const int h = tid >> 7, j = tid & (DD - 1);
+    if (h < nh) {
+      float o = 0.f;
+#pragma unroll
+      for (int kg = 0; kg < 8; ++kg) o += pk[kg][h][j];
+      a.out[((int64_t)b * a.q_heads + h0 + h) * DD + j] = o;
+    }
+  }
+}
 
 template <int KB, int VB>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   constexpr int KM = 1 << (KB - 1);  // key Walsh masks
   constexpr int VM = 1 << (VB - 1);  // value Walsh masks
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float *lg = reinterpret_cast<float *>(smem);                         // [4][chunk] + 64 spare
-  float *vnl = lg + 4 * a.chunk + 64;                                  // [chunk] value norms
-  int8_t *av = reinterpret_cast<int8_t *>(smem + (5 * a.chunk + 64) * 4);  // [chunk/128][2][64][16]
-  __shared__ float red[4];
+  float *lg = reinterpret_cast<float *>(smem);                   // [4][chunk] logits (log2 units)
+  float *vnl = lg + 4 * a.chunk;                                 // [chunk] value norms
+  int8_t *av = reinterpret_cast<int8_t *>(smem + 5 * a.chunk * 4);  // [chunk/128][2][64][16] value A fragments
+  __shared__ float red[4], lred[4][4];
   __shared__ double wsum[4];
   __shared__ float hmax[4], hsum[4];
 
@@ -753,55 +872,65 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       const int hh = e / (DD + 2), j = e % (DD + 2);
       part(hh)[j] = (j == DD) ? -INFINITY : 0.f;
     }
-    return;
-  }
-  const int n = t1 - t0;
-  const int64_t srec = (int64_t)stream * a.capacity;
-  const float *wk = a.tables->walsh[KB];
-  const float *wv = a.tables->walsh[VB];
-  const int ngrp = (n + 127) >> 7;
-  // zero the value A fragments (rows of absent heads and pad digits stay zero)
-  for (int e = tid; e < ngrp * 2 * 64; e += 256) reinterpret_cast<uint4 *>(av)[e] = make_uint4(0, 0, 0, 0);
+  } else {
+    const int n = t1 - t0;
+    const int64_t srec = (int64_t)stream * a.capacity;
+    const float *wk = a.tables->walsh[KB];
+    const float *wv = a.tables->walsh[VB];
+    const int ngrp = (n + 127) >> 7;
+    // zero the value A fragments (rows of absent heads stay zero)
+    for (int e = tid; e < ngrp * 2 * 64; e += 256) reinterpret_cast<uint4 *>(av)[e] = make_uint4(0, 0, 0, 0);
 
-  // ---- phase K: logits of all tokens of the chunk (log2 units) ----
-  const uint32_t *qf = a.qfrag + (int64_t)sg * 2 * 2 * 64 * 8;
-  auto ldfrag = [&](int T, int ins) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(qf + ((T * 2 + ins) * 64 + lane) * 8);
-    const uint4 x = p[0], y = p[1];
-    i8v v;
-    v[0] = (int)x.x; v[1] = (int)x.y; v[2] = (int)x.z; v[3] = (int)x.w;
-    v[4] = (int)y.x; v[5] = (int)y.y; v[6] = 0; v[7] = 0;
-    return v;
-  };
-  const i8v aqr0 = ldfrag(0, 0), aqr1 = ldfrag(0, 1), aqs0 = ldfrag(1, 0), aqs1 = ldfrag(1, 1);
-  const int sc0 = 127 + 3 * (lane & 3), sc1 = sc0 + 12;  // e8m0 row scales 2^(3 digit)
-  const int tn = lane & 15, G = lane >> 4;  // MFMA column (token), row group (head)
-  const float *qc = a.qconst + ((int64_t)sg * 4 + G) * 4;
-  const float sr = qc[0], ss = qc[1];
-  float wkr[KM];
+    // ---- phase K: logits of all tokens of the chunk (log2 units) ----
+    const uint32_t *qf = a.qfrag + (int64_t)sg * 2 * 2 * 64 * 8;
+    auto ldfrag = [&](int T, int ins) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(qf + ((T * 2 + ins) * 64 + lane) * 8);
+      const uint4 x = p[0], y = p[1];
+      i8v v;
+      v[0] = (int)x.x; v[1] = (int)x.y; v[2] = (int)x.z; v[3] = (int)x.w;
+      v[4] = (int)y.x; v[5] = (int)y.y; v[6] = 0; v[7] = 0;
+      return v;
+    };
+    const i8v aqr0 = ldfrag(0, 0), aqr1 = ldfrag(0, 1), aqs0 = ldfrag(1, 0), aqs1 = ldfrag(1, 1);
+    const int sc0 = 127 + 3 * (lane & 3), sc1 = sc0 + 12;  // e8m0 row scales 2^(3 digit)
+    const int tn = lane & 15, G = lane >> 4;  // MFMA column (token), row group (head)
+    const float *qc = a.qconst + ((int64_t)sg * 4 + G) * QC;
+    // accumulator start -sum_j Q_j per digit slot: the A fragments against an
+    // all-ones mask (B scale 2^1 undoes the 1/2 of every product), exact
+    f4v init_r, init_s;
+    {
+      const i8v ones = mask_fp4_01(0xFFFFFFFFu);
+      const f4v z = {0.f, 0.f, 0.f, 0.f};
+      init_r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr0, ones, z, 2, 4, 0, sc0, 0, 128);
+      init_r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr1, ones, init_r, 2, 4, 0, sc1, 0, 128);
+      init_s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs0, ones, z, 2, 4, 0, sc0, 0, 128);
+      init_s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs1, ones, init_s, 2, 4, 0, sc1, 0, 128);
+      init_r = -init_r;
+      init_s = -init_s;
+    }
+    // logit (log2 units) = |k| (sum_S wr_S T_S + qs |r| T_QJL) with the query units,
+    // the softmax scale and the QJL constant folded into the per-lane weights
+    const float sr = qc[0] * a.scale_log2, qs = qc[1] * a.qjl_scale * a.scale_log2;
+    float wkr[KM];
 #pragma unroll
-  for (int mi = 0; mi < KM; ++mi) wkr[mi] = wk[mi];
-  // the logit store below is unconditional (invalid lanes write a spare slot)
-  // so that no loop-invariant load is sunk into a branch inside the loop
-  const int spare = 4 * a.chunk + lane;
-  float vmx = 0.f;
-  const int ntile = (n + 15) >> 4;
-  struct KBuf {
-    uint32_t pl[KTPW][KB + 1];
-    float2 kn[KTPW];
-    float vn[KTPW];
-  };
-  auto kload = [&](int base, KBuf &bf) {
+    for (int mi = 0; mi < KM; ++mi) wkr[mi] = wk[mi] * sr;
+    float vmx = 0.f, lmx = -INFINITY;
+    const int ntile = (n + 15) >> 4;
+    // records of the chunk: uniform bases, 32-bit lane offsets; lanes past the end
+    // re-read token n-1, so every store below stays unconditional and harmless
+    const uint32_t *kb0 = a.kbits + (srec + t0) * DW * (KB + 1);
+    const float2 *kn0 = reinterpret_cast<const float2 *>(a.knorm) + (srec + t0);
+    const float *vn0 = a.vnorm + (srec + t0);
+    struct KBuf {
+      uint32_t pl[KTPW][KB + 1];
+      float2 kn[KTPW];
+      float vn[KTPW];
+    };
+    auto kload = [&](int base, KBuf &bf) {
 #pragma unroll
-    for (int u = 0; u < KTPW; ++u) {
-      const int tl = (base + u) * 16 + tn;
-      const int64_t rec = srec + t0 + tl;
-      bf.kn[u] = make_float2(0.f, 0.f);
-      bf.vn[u] = 0.f;
-#pragma unroll
-      for (int p = 0; p <= KB; ++p) bf.pl[u][p] = 0u;
-      if (tl < n) {
-        const uint32_t *src = a.kbits + (rec * DW + G) * (KB + 1);
+      for (int u = 0; u < KTPW; ++u) {
+        const int tc = min((base + u) * 16 + tn, n - 1);
+        const uint32_t *src = kb0 + (tc * DW + G) * (KB + 1);
         if constexpr (KB == 3) {
           const uint4 w4 = *reinterpret_cast<const uint4 *>(src);
           bf.pl[u][0] = w4.x; bf.pl[u][1] = w4.y; bf.pl[u][2] = w4.z; bf.pl[u][3] = w4.w;
@@ -809,210 +938,174 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int p = 0; p <= KB; ++p) bf.pl[u][p] = src[p];
         }
-        bf.kn[u] = *reinterpret_cast<const float2 *>(a.knorm + 2 * rec);
-        if (G == 0) bf.vn[u] = a.vnorm[rec];
+        bf.kn[u] = kn0[tc];
+        bf.vn[u] = vn0[tc];
       }
-    }
-  };
-  KBuf cur;
-  if (wave * KTPW < ntile) kload(wave * KTPW, cur);
-  for (int base = wave * KTPW; base < ntile; base += 4 * KTPW) {
-    KBuf nxt;
-    if (base + 4 * KTPW < ntile) kload(base + 4 * KTPW, nxt);  // next round in flight during this one
+    };
+    auto kcompute = [&](int base, const KBuf &cur) {
 #pragma unroll
-    for (int u = 0; u < KTPW; ++u) {
-      const int tl = (base + u) * 16 + tn;
-      // all signed masked sums first (independent accumulators keep the MFMA pipe busy)
-      f4v acc[KM + 1];
+      for (int u = 0; u < KTPW; ++u) {
+        const int tc = min((base + u) * 16 + tn, n - 1);
+        // all masked sums first (independent accumulators keep the MFMA pipe busy)
+        f4v acc[KM + 1];
 #pragma unroll
-      for (int mi = 0; mi <= KM; ++mi) {
-        const i8v bm = mask_fp4_pm(mi < KM ? xor_planes(cur.pl[u], walsh_mask(KB, mi)) : cur.pl[u][KB]);
-        acc[mi] = f4v{0.f, 0.f, 0.f, 0.f};
-        acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr0 : aqs0, bm, acc[mi], 2, 4, 0, sc0,
-                                                                   0, 127);
-        acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr1 : aqs1, bm, acc[mi], 2, 4, 0, sc1,
-                                                                   0, 127);
-      }
-      float code = 0.f;
+        for (int mi = 0; mi <= KM; ++mi) {
+          const i8v bm = mask_fp4_01(mi < KM ? xor_planes(cur.pl[u], walsh_mask(KB, mi)) : cur.pl[u][KB]);
+          acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr0 : aqs0, bm, mi < KM ? init_r : init_s,
+                                                                     2, 4, 0, sc0, 0, 129);
+          acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr1 : aqs1, bm, acc[mi], 2, 4, 0, sc1,
+                                                                     0, 129);
+        }
+        float code = 0.f;
 #pragma unroll
-      for (int mi = 0; mi < KM; ++mi) code += wkr[mi] * ((acc[mi][0] + acc[mi][1]) + (acc[mi][2] + acc[mi][3]));
-      const float Ts = (acc[KM][0] + acc[KM][1]) + (acc[KM][2] + acc[KM][3]);
-      const float s = cur.kn[u].x * (sr * code + a.qjl_scale * cur.kn[u].y * ss * Ts);
-      lg[(G < nh && tl < n) ? G * a.chunk + tl : spare] = s * a.scale_log2;
-      if (G == 0 && tl < n) {
-        vnl[tl] = cur.vn[u];
+        for (int mi = 0; mi < KM; ++mi) code += wkr[mi] * ((acc[mi][0] + acc[mi][1]) + (acc[mi][2] + acc[mi][3]));
+        const float Ts = (acc[KM][0] + acc[KM][1]) + (acc[KM][2] + acc[KM][3]);
+        const float s = cur.kn[u].x * fmaf(cur.kn[u].y * Ts, qs, code);
+        lg[G * a.chunk + tc] = s;
+        lmx = fmaxf(lmx, s);
+        vnl[tc] = cur.vn[u];
         vmx = fmaxf(vmx, cur.vn[u]);
       }
+    };
+    // two buffers in turn: the next round's loads are in flight during this one
+    constexpr int KSTEP = 4 * KTPW;
+    KBuf kb_a, kb_b;
+    int kbase = wave * KTPW;
+    if (kbase < ntile) kload(kbase, kb_a);
+    while (kbase < ntile) {
+      if (kbase + KSTEP < ntile) kload(kbase + KSTEP, kb_b);
+      kcompute(kbase, kb_a);
+      kbase += KSTEP;
+      if (kbase >= ntile) break;
+      if (kbase + KSTEP < ntile) kload(kbase + KSTEP, kb_a);
+      kcompute(kbase, kb_b);
+      kbase += KSTEP;
     }
-    cur = nxt;
-  }
-  for (int off = 32; off > 0; off >>= 1) vmx = fmaxf(vmx, __shfl_xor(vmx, off));
-  if (lane == 0) red[wave] = vmx;
-  __syncthreads();
-  const float vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // ---- softmax: wave w owns head w; weights -> fixed-point value digits ----
-  const float wq = vmax > 0.f ? WSCALE / vmax : 0.f;
-  if (wave < nh) {
-    float m = -INFINITY;
-    for (int t = lane; t < n; t += 64) m = fmaxf(m, lg[wave * a.chunk + t]);
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    // token t = lane + 64 i lands in fragment byte
-    //   (i>>1)*2048 + ins*1024 + gg*256 + head*64 + qq*4 + bb, with q = t&7, ins = q>>2,
-    //   qq = q&3, bb = (t>>3)&3, gg = (t>>5)&3: the lane-dependent part is fixed.
-    const int lbase = (((lane >> 2) & 1) << 10) | (((lane >> 5) & 1) << 8) | (wave << 6) | ((lane & 3) << 2) |
-                      ((lane >> 3) & 3);
-    float l = 0.f;
-    int wsi = 0;
-    for (int i = 0, t = lane; t < n; ++i, t += 64) {
-      const float p = exp2f(lg[wave * a.chunk + t] - m);
-      l += p;
-      const int W = (int)rintf(p * vnl[t] * wq);
-      wsi += W;
-      const uint32_t x = ((uint32_t)W + 0x808080u) ^ 0x808080u;  // three signed base-256 digits
-      int8_t *dst = av + lbase + ((i >> 1) << 11) + ((i & 1) << 9);
-      dst[0] = (int8_t)x;
-      dst[16] = (int8_t)(x >> 8);
-      dst[32] = (int8_t)(x >> 16);
+    // chunk maxima: |v| over all lanes; logits per head (lanes of one row group)
+    for (int off = 32; off > 0; off >>= 1) vmx = fmaxf(vmx, __shfl_xor(vmx, off));
+    for (int off = 8; off > 0; off >>= 1) lmx = fmaxf(lmx, __shfl_xor(lmx, off));
+    if (lane == 0) red[wave] = vmx;
+    if (tn == 0) lred[wave][G] = lmx;
+    __syncthreads();
+    const float vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    // ---- softmax: wave w owns head w; weights -> fixed-point value digits ----
+    if (wave < nh) {
+      const float m = fmaxf(fmaxf(lred[0][wave], lred[1][wave]), fmaxf(lred[2][wave], lred[3][wave]));
+      // token t = lane + 64 i: q = t & 7 = lane & 7 is fixed per lane, and so is
+      // its weight scale 2^(29 - q) / vmax (negated for q = 7, whose B byte is -128)
+      const int qv = lane & 7;
+      const float wq = vmax > 0.f ? ldexpf(WSCALE / vmax, -qv) * (qv == 7 ? -1.f : 1.f) : 0.f;
+      // token t lands in fragment byte
+      //   (i>>1)*2048 + ins*1024 + gg*256 + head*64 + qq*4 + bb, with q = t&7, ins = q>>2,
+      //   qq = q&3, bb = (t>>3)&3, gg = (t>>5)&3: the lane-dependent part is fixed.
+      const int lbase = (((lane >> 2) & 1) << 10) | (((lane >> 5) & 1) << 8) | (wave << 6) | ((lane & 3) << 2) |
+                        ((lane >> 3) & 3);
+      float l = 0.f;
+      int64_t wsi = 0;
+      for (int i = 0, t = lane; t < n; ++i, t += 64) {
+        const float p = __builtin_amdgcn_exp2f(lg[wave * a.chunk + t] - m);  // <= 1; tiny values round to W = 0
+        l += p;
+        const int W = (int)rintf(p * vnl[t] * wq);
+        wsi += W;
+        const uint32_t x = ((uint32_t)W + 0x80808080u) ^ 0x80808080u;  // four signed base-256 digits
+        int8_t *dst = av + lbase + ((i >> 1) << 11) + ((i & 1) << 9);
+        dst[0] = (int8_t)x;
+        dst[16] = (int8_t)(x >> 8);
+        dst[32] = (int8_t)(x >> 16);
+        dst[48] = (int8_t)(x >> 24);
+      }
+      // effective weight of the lane's tokens: W * 2^q (W * -128 for q = 7); exact in double
+      double ws = (double)wsi * (qv == 7 ? -128.0 : (double)(1 << qv));
+      for (int off = 32; off > 0; off >>= 1) {
+        l += __shfl_xor(l, off);
+        ws += __shfl_xor(ws, off);
+      }
+      if (lane == 0) {
+        hmax[wave] = m;
+        hsum[wave] = l;
+        wsum[wave] = ws;
+      }
     }
-    double ws = (double)wsi;
-    for (int off = 32; off > 0; off >>= 1) {
-      l += __shfl_xor(l, off);
-      ws += __shfl_xor(ws, off);
-    }
-    if (lane == 0) {
-      hmax[wave] = m;
-      hsum[wave] = l;
-      wsum[wave] = ws;
-    }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- phase V: value sums on MFMA; wave w owns coordinates 32w .. 32w+31 ----
-  i4v accv[2][VM];
+    // ---- phase V: value sums on MFMA; wave w owns coordinates 32w .. 32w+31 ----
+    i4v accv[2][VM];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int mi = 0; mi < VM; ++mi) accv[nt][mi] = i4v{0, 0, 0, 0};
-  const int vn = lane & 15, vg = lane >> 4;  // coordinate column, token block in the 128-token group
-  struct VBuf {
-    uint32_t pl[VGPI][2][VB];
-  };
-  auto vload = [&](int grp0, VBuf &bf) {
+      for (int mi = 0; mi < VM; ++mi) accv[nt][mi] = i4v{0, 0, 0, 0};
+    const int vn = lane & 15, vg = lane >> 4;  // coordinate column, token block in the 128-token group
+    struct VBuf {
+      uint32_t pl[VGPI][2][VB];
+    };
+    // blocks of the chunk from a uniform base; a block past the end re-reads the
+    // last one (its tokens carry zero weights)
+    const uint32_t *vb0 = a.vbits + ((srec + t0) >> 5) * DD * VB;
+    const int lastblk = (n - 1) >> 5;
+    auto vload = [&](int grp0, VBuf &bf) {
 #pragma unroll
-    for (int gi = 0; gi < VGPI; ++gi) {
-      const int tb = (grp0 + gi) * 128 + vg * 32;  // first token of this lane's block, chunk-relative
+      for (int gi = 0; gi < VGPI; ++gi) {
+        const int blk = min((grp0 + gi) * 4 + vg, lastblk);  // this lane's 32-token block, chunk-relative
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-        for (int p = 0; p < VB; ++p) bf.pl[gi][nt][p] = 0u;
-        if (tb < n) {
-          const int j = wave * 32 + nt * 16 + vn;
-          const int64_t blk = (srec + t0 + tb) >> 5;
-          const uint32_t *src = a.vbits + (blk * DD + j) * VB;
+        for (int nt = 0; nt < 2; ++nt) {
+          const uint32_t *src = vb0 + (blk * DD + wave * 32 + nt * 16 + vn) * VB;
 #pragma unroll
           for (int p = 0; p < VB; ++p) bf.pl[gi][nt][p] = src[p];
         }
       }
-    }
-  };
-  VBuf vcur;
-  vload(0, vcur);
-  for (int grp0 = 0; grp0 < ngrp; grp0 += VGPI) {
-    VBuf vnxt;
-    if (grp0 + VGPI < ngrp) vload(grp0 + VGPI, vnxt);
+    };
+    auto vcompute = [&](int grp0, const VBuf &vcur) {
 #pragma unroll
-    for (int gi = 0; gi < VGPI; ++gi) {
-      const int grp = grp0 + gi;
-      if (grp >= ngrp) break;
-      const i4v a0 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 0) * 64 + lane) * 16);
-      const i4v a1 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 1) * 64 + lane) * 16);
+      for (int gi = 0; gi < VGPI; ++gi) {
+        const int grp = grp0 + gi;
+        if (grp >= ngrp) break;
+        const i4v a0 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 0) * 64 + lane) * 16);
+        const i4v a1 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 1) * 64 + lane) * 16);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-        for (int mi = 0; mi < VM; ++mi) {
-          i4v lo, hi;
-          mask_bytes(xor_planes(vcur.pl[gi][nt], walsh_mask(VB, mi)), lo, hi);
-          accv[nt][mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo, accv[nt][mi], 0, 0, 0);
-          accv[nt][mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi, accv[nt][mi], 0, 0, 0);
-        }
-      }
-    }
-    vcur = vnxt;
-  }
-  // flush: lane (coordinate vn, head vg) holds digits 0..2 of every mask sum
-  if (vg < nh) {
-    const double W = wsum[vg];
-    const double unit = (double)vmax / (double)WSCALE;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      double o = 0.0;
-#pragma unroll
-      for (int mi = 0; mi < VM; ++mi) {
-        const i4v &x = accv[nt][mi];
-        const double M = (double)x[0] + 256.0 * (double)x[1] + 65536.0 * (double)x[2];
-        o += (double)wv[mi] * (2.0 * M - W);
-      }
-      part(vg)[wave * 32 + nt * 16 + vn] = (float)(o * unit);
-    }
-  }
-  if (tid < nh) {
-    part(tid)[DD] = hmax[tid];
-    part(tid)[DD + 1] = hsum[tid];
-  }
-}
-
-// One block per (sequence, KV head, head group), thread = (head, coordinate):
-// online log-sum-exp merge of the chunks (loads issued in batches), then
-// o = Pi^T o_rot.
-__global__ void __launch_bounds__(8 * DD) decode_merge_kernel(DecodeArgs a) {
-  constexpr int CB = 8;
-  __shared__ float orot[4][DD], half[4][DD];
-  const int sg = blockIdx.x;
-  const int hg = sg % a.hgroups, stream = sg / a.hgroups;
-  const int b = stream / a.kv_heads;
-  const int h0 = (stream % a.kv_heads) * a.group + hg * 4;
-  const int nh = min(4, a.group - hg * 4);
-  const int kh = threadIdx.x >> 9, hh = (threadIdx.x >> 7) & 3, j = threadIdx.x & (DD - 1);
-  if (kh == 0) {
-    float val = 0.f;
-    if (hh < nh) {
-      const float *p = a.partial + ((int64_t)b * a.q_heads + h0 + hh) * a.nchunks * (DD + 2);
-      float M = -INFINITY, L = 0.f, O = 0.f;
-      for (int c0 = 0; c0 < a.nchunks; c0 += CB) {
-        float mv[CB], lv[CB], ov[CB];
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-          const int c = c0 + u;
-          mv[u] = -INFINITY;
-          lv[u] = ov[u] = 0.f;
-          if (c < a.nchunks) {
-            mv[u] = p[c * (DD + 2) + DD];
-            lv[u] = p[c * (DD + 2) + DD + 1];
-            ov[u] = p[c * (DD + 2) + j];
+          for (int mi = 0; mi < VM; ++mi) {
+            i4v lo, hi;
+            mask_bytes_pow2(xor_planes(vcur.pl[gi][nt], walsh_mask(VB, mi)), lo, hi);
+            accv[nt][mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo, accv[nt][mi], 0, 0, 0);
+            accv[nt][mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi, accv[nt][mi], 0, 0, 0);
           }
         }
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-          if (mv[u] == -INFINITY) continue;
-          const float Mn = fmaxf(M, mv[u]);
-          const float f0 = (M == -INFINITY) ? 0.f : exp2f(M - Mn), f1 = exp2f(mv[u] - Mn);
-          L = L * f0 + lv[u] * f1;
-          O = O * f0 + ov[u] * f1;
-          M = Mn;
-        }
       }
-      val = L > 0.f ? O / L : 0.f;
+    };
+    VBuf vb_a, vb_b;
+    int vbase = 0;
+    vload(0, vb_a);
+    while (vbase < ngrp) {
+      if (vbase + VGPI < ngrp) vload(vbase + VGPI, vb_b);
+      vcompute(vbase, vb_a);
+      vbase += VGPI;
+      if (vbase >= ngrp) break;
+      if (vbase + VGPI < ngrp) vload(vbase + VGPI, vb_a);
+      vcompute(vbase, vb_b);
+      vbase += VGPI;
     }
-    orot[hh][j] = val;
+    // flush: lane (coordinate vn, head vg) holds digits 0..3 of every mask sum
+    if (vg < nh) {
+      const double W = wsum[vg];
+      const double unit = (double)vmax / (double)WSCALE;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        double o = 0.0;
+#pragma unroll
+        for (int mi = 0; mi < VM; ++mi) {
+          const i4v &x = accv[nt][mi];
+          const double M = (double)x[0] + 256.0 * (double)x[1] + 65536.0 * (double)x[2] + 16777216.0 * (double)x[3];
+          o += (double)wv[mi] * (2.0 * M - W);
+        }
+        part(vg)[wave * 32 + nt * 16 + vn] = (float)(o * unit);
+      }
+    }
+    if (tid < nh) {
+      part(tid)[DD] = hmax[tid];
+      part(tid)[DD + 1] = hsum[tid];
+    }
   }
-  __syncthreads();
-  // o = Pi^T o_rot: column j of Pi (coalesced over j), k split in halves
-  float acc = 0.f;
-#pragma unroll 16
-  for (int k = kh * 64; k < kh * 64 + 64; ++k) acc += a.rot[k * DD + j] * orot[hh][k];
-  if (kh == 1) half[hh][j] = acc;
-  __syncthreads();
-  if (kh == 0 && hh < nh) a.out[((int64_t)b * a.q_heads + h0 + hh) * DD + j] = acc + half[hh][j];
 }
 
 size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int *chunk_out,
@@ -1029,7 +1122,7 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
   size_t b = 0;
   b += (size_t)streams * 2 * 2 * 64 * 32;  // qfrag (fp6 fragments, 8 dwords per lane)
   b = (b + 255) & ~(size_t)255;
-  b += (size_t)streams * 16 * sizeof(float);  // qconst
+  b += (size_t)streams * 4 * QC * sizeof(float);  // qconst
   b = (b + 255) & ~(size_t)255;
   b += (size_t)cache->batch * q_heads * nchunks * (DD + 2) * sizeof(float);  // partials
   (void)ctx;
@@ -1073,13 +1166,16 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.qfrag = (uint32_t *)p;
   p += (((size_t)streams * 2 * 2 * 64 * 32) + 255) & ~(size_t)255;
   a.qconst = (float *)p;
-  p += (((size_t)streams * 16 * sizeof(float)) + 255) & ~(size_t)255;
+  p += (((size_t)streams * 4 * QC * sizeof(float)) + 255) & ~(size_t)255;
   a.partial = (float *)p;
   a.out = out;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(streams), dim3(512), 0, st, a);
+  if (is_bf16)
+    hipLaunchKernelGGL(decode_prep_kernel<uint16_t>, dim3(streams), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_prep_kernel<float>, dim3(streams), dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t shm = (size_t)(5 * chunk + 64) * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;
+  const size_t shm = (size_t)5 * chunk * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;
   dim3 grid(nchunks, streams);
   const int kb = cache->k.mse_bits, vb = cache->v.mse_bits;
 #define TQ_DEC(K_, V_) else if (kb == K_ && vb == V_) e = launch_decode_kv<K_, V_>(a, grid, shm, st);
@@ -1092,7 +1188,7 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   else return hipErrorInvalidValue;
 #undef TQ_DEC
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(streams), dim3(8 * DD), 0, st, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(streams), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
