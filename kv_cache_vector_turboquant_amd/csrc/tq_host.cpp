@@ -260,6 +260,19 @@ tq_status tq_rotation_build(int32_t d, const double *h_g, float *h_out) {
   return TQ_OK;
 }
 
+// bf16 with round-to-nearest-even of a finite fp32 value, and back
+static uint16_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+static float bf16_value(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
 tq_status tq_ctx_create(int32_t d, const double *h_g_rot, const double *h_g_sketch, tq_ctx **out) {
   if (!out || !h_g_rot || !h_g_sketch) return fail(TQ_ERR_ARG, "tq_ctx_create: NULL argument");
   *out = nullptr;
@@ -317,6 +330,29 @@ tq_status tq_ctx_create(int32_t d, const double *h_g_rot, const double *h_g_sket
       rst[(size_t)j * 2 * d + d + i] = (float)row[j];
     }
   }
+  // d = 128: Pi as three bf16 parts and S as two, for the bf16-MFMA quantizer
+  if (d == 128) {
+    std::vector<uint16_t> r3((size_t)3 * d * d), s2((size_t)2 * d * d);
+    for (size_t i = 0; i < (size_t)d * d; ++i) {
+      float rem = ctx->rot[i];
+      for (int p = 0; p < 3; ++p) {
+        r3[(size_t)p * d * d + i] = bf16_rne(rem);
+        rem -= bf16_value(r3[(size_t)p * d * d + i]);
+      }
+      rem = ctx->sketch[i];
+      for (int p = 0; p < 2; ++p) {
+        s2[(size_t)p * d * d + i] = bf16_rne(rem);
+        rem -= bf16_value(s2[(size_t)p * d * d + i]);
+      }
+    }
+    if ((e = hipMalloc(&ctx->d_rot3, r3.size() * 2)) != hipSuccess ||
+        (e = hipMalloc(&ctx->d_sk2, s2.size() * 2)) != hipSuccess ||
+        (e = hipMemcpy(ctx->d_rot3, r3.data(), r3.size() * 2, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(ctx->d_sk2, s2.data(), s2.size() * 2, hipMemcpyHostToDevice)) != hipSuccess) {
+      tq_ctx_destroy(ctx);
+      return hip_fail(e, "tq_ctx_create: bf16 parts");
+    }
+  }
   if ((e = hipMemcpy(ctx->d_rot, ctx->rot.data(), mat, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(ctx->d_rot_t, rt.data(), mat, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(ctx->d_sketch_t, st.data(), mat, hipMemcpyHostToDevice)) != hipSuccess ||
@@ -340,6 +376,8 @@ tq_status tq_ctx_destroy(tq_ctx *ctx) {
   if (ctx->d_rot_t) (void)hipFree(ctx->d_rot_t);
   if (ctx->d_sketch_t) (void)hipFree(ctx->d_sketch_t);
   if (ctx->d_rs_t) (void)hipFree(ctx->d_rs_t);
+  if (ctx->d_rot3) (void)hipFree(ctx->d_rot3);
+  if (ctx->d_sk2) (void)hipFree(ctx->d_sk2);
   delete ctx;
   return TQ_OK;
 }

@@ -43,6 +43,8 @@ struct tq_ctx {
   float *d_rot_t = nullptr;     // Pi^T, row-major (coalesced matrix-vector products)
   float *d_sketch_t = nullptr;  // S^T, row-major
   float *d_rs_t = nullptr;      // [Pi ; S Pi]^T: d x 2d row-major (query rotation and sketch in one pass)
+  uint16_t *d_rot3 = nullptr;   // d = 128: Pi as three bf16 parts (hi, mid, lo), [3][d][d]
+  uint16_t *d_sk2 = nullptr;    // d = 128: S as two bf16 parts (hi, lo), [2][d][d]
   tq::DeviceTables *d_tables = nullptr;
   tq::DeviceTables h_tables;
 };

@@ -333,10 +333,369 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused quantize for d = 128 and bf16 input, one work-group per 64 tokens.
+//
+// Both products run on bf16 MFMA (16x16x32). The input is exact in bf16 and Pi
+// is split into three bf16 parts (hi + mid + lo carry its 24 bits), so
+// y = Pi x accumulates in fp32 exactly as an fp32 GEMM would, up to rounding
+// order. For keys the residual r = y - c[idx] and S are split into two parts
+// each (hi*hi + hi*lo + lo*hi): z = S r is then accurate to ~2^-17 relative,
+// which only decides signs of |z| far below the 1e-5 band. The residual never
+// leaves the chip: it is staged in LDS as bf16 (hi, lo) between the products.
+//
+// Codes come from |y| against the positive boundaries (the table is
+// antisymmetric and its middle boundary is 0): mag = #{t_j <= |y|}, idx =
+// L/2 + mag for y >= 0, L/2 - 1 - mag for y < 0 (only exact ties differ from
+// #{t_i <= y}). Code bytes (bit 7 = QJL sign for keys) are staged in LDS and a
+// last pass gathers them into the bit-plane words.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int QT = 64;   // tokens per work-group
+constexpr int QD = 128;  // vector dimension of this path
+constexpr int QW = QD / 32;
+
+struct Q128Args {
+  const uint16_t *x;       // bf16 input
+  int64_t n_tokens, xs, xt;  // tokens per stream; stream / token strides (elements)
+  const uint16_t *rot3;    // [3][128][128] bf16 parts of Pi: [part][output coordinate][k]
+  const uint16_t *sk2;     // [2][128][128] bf16 parts of S: [part][sketch row][coordinate]
+  const DeviceTables *tables;
+  uint32_t *bits_out;
+  float *norms_out;
+  int64_t os, oo;          // output stream stride and offset (records)
+};
+
+__device__ __forceinline__ bf16x8 ld_bf8(const uint16_t *p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float sumsq8(bf16x8 v) {
+  const uint4 u = __builtin_bit_cast(uint4, v);
+  float s = 0.f;
+  s = fmaf(bf_lo(u.x), bf_lo(u.x), s); s = fmaf(bf_hi(u.x), bf_hi(u.x), s);
+  s = fmaf(bf_lo(u.y), bf_lo(u.y), s); s = fmaf(bf_hi(u.y), bf_hi(u.y), s);
+  s = fmaf(bf_lo(u.z), bf_lo(u.z), s); s = fmaf(bf_hi(u.z), bf_hi(u.z), s);
+  s = fmaf(bf_lo(u.w), bf_lo(u.w), s); s = fmaf(bf_hi(u.w), bf_hi(u.w), s);
+  return s;
+}
+
+// bf16 with round-to-nearest-even (inputs are finite)
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Bit p of each of the 4 bytes of w, gathered into bits 0..3 (byte k -> bit k).
+__device__ __forceinline__ uint32_t gather4(uint32_t w, int p) {
+  return (((w >> p) & 0x01010101u) * 0x01020408u) >> 24;
+}
+
+// LDS swizzle of 16-byte granules: row r of `gran` granules, granule g at g ^ (r & mask)
+__device__ __forceinline__ int swz(int row, int gran_per_row, int g, int mask) {
+  return row * gran_per_row + (g ^ (row & mask));
+}
+
+template <bool KEYS, int B>
+__global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
+  constexpr int H = 1 << (B - 1);  // centroids per sign
+  // code bytes (keys: bit 7 = QJL sign): keys [token][coordinate] (8 granules per token),
+  // values [coordinate][token] (4 granules per coordinate)
+  __shared__ __attribute__((aligned(16))) uint32_t stage[QT * QD / 4];
+  // keys: residual parts, [token][coordinate] bf16 (16 granules per token row)
+  __shared__ __attribute__((aligned(16))) uint16_t rt[KEYS ? 2 : 1][KEYS ? QT * QD : 8];
+  __shared__ float nrm[QT];
+  __shared__ float rho2[4][QT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, kq = lane >> 4;
+  const int64_t s = blockIdx.y, t0 = (int64_t)blockIdx.x * QT;
+  const int nv = (int)min((int64_t)QT, a.n_tokens - t0);
+  const uint16_t *xb = a.x + s * a.xs + t0 * a.xt;
+  // positive boundaries and centroid magnitudes
+  float tp[H > 1 ? H - 1 : 1], cm[H];
+#pragma unroll
+  for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
+#pragma unroll
+  for (int j = 0; j < H; ++j) cm[j] = a.tables->centroid[B][H + j];
+
+  // ---- product 1: wave w owns output coordinates 32w .. 32w+31 (blocks cb) for the 64 tokens (blocks tb)
+  f4v acc[2][4];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  struct Frag1 {
+    bf16x8 x[4], p[2][3];
+  };
+  auto load1 = [&](int ks, Frag1 &f) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) f.x[tb] = ld_bf8(xb + (int64_t)min(tb * 16 + c16, nv - 1) * a.xt + ks * 32 + kq * 8);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp)
+        f.p[cb][sp] = ld_bf8(a.rot3 + ((sp * QD) + 32 * wave + 16 * cb + c16) * QD + ks * 32 + kq * 8);
+  };
+  auto comp1 = [&](const Frag1 &f) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) ss[tb] += sumsq8(f.x[tb]);
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          acc[cb][tb] = KEYS ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.p[cb][sp], f.x[tb], acc[cb][tb], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.x[tb], f.p[cb][sp], acc[cb][tb], 0, 0, 0);
+  };
+  {
+    Frag1 fa, fb;
+    load1(0, fa);
+    load1(1, fb);
+    comp1(fa);
+    load1(2, fa);
+    comp1(fb);
+    load1(3, fb);
+    comp1(fa);
+    comp1(fb);
+  }
+  // token norms: lanes of one c16 hold the four k quarters
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    ss[tb] += __shfl_xor(ss[tb], 16);
+    ss[tb] += __shfl_xor(ss[tb], 32);
+  }
+  if (wave == 0 && kq == 0) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) nrm[tb * 16 + c16] = sqrtf(ss[tb]);
+  }
+  if constexpr (!KEYS) __syncthreads();
+
+  // code of y: byte idx, centroid value
+  auto code = [&](float y, uint32_t &idx) {
+    const float ay = fabsf(y);
+    int mag = 0;
+    float c = cm[0];
+#pragma unroll
+    for (int j = 0; j < H - 1; ++j) {
+      const bool ge = ay >= tp[j];
+      mag += ge ? 1 : 0;
+      c = ge ? cm[j + 1] : c;
+    }
+    const bool neg = y < 0.f;
+    idx = (uint32_t)(neg ? H - 1 - mag : H + mag);
+    return neg ? -c : c;
+  };
+
+  if constexpr (KEYS) {
+    // acc[cb][tb][r] = y[coordinate 32w + 16cb + 4kq + r][token tb*16 + c16] * |x|
+    float rp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int tok = tb * 16 + c16;
+      const float n = sqrtf(ss[tb]);
+      const float inv = n > 0.f ? 1.f / n : 0.f;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int c0 = 32 * wave + 16 * cb + 4 * kq;  // first of the lane's 4 coordinates
+        uint32_t bytes = 0, hi2[2] = {0, 0}, lo2[2] = {0, 0};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float y = acc[cb][tb][r] * inv;
+          uint32_t idx;
+          const float res = y - code(y, idx);
+          bytes |= idx << (8 * r);
+          rp[tb] = fmaf(res, res, rp[tb]);
+          const uint32_t h = to_bf16(res);
+          const uint32_t l = to_bf16(res - __uint_as_float(h << 16));
+          hi2[r >> 1] |= h << (16 * (r & 1));
+          lo2[r >> 1] |= l << (16 * (r & 1));
+        }
+        // code bytes of 4 coordinates: granule c0 / 16, dword (c0 / 4) % 4
+        stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
+        // residual parts: granule c0 / 8 of 16, half (c0 / 4) % 2
+        const int gr = swz(tok, 16, c0 >> 3, 15) * 8 + ((c0 >> 2) & 1) * 4;
+        *reinterpret_cast<uint2 *>(&rt[0][gr]) = make_uint2(hi2[0], hi2[1]);
+        *reinterpret_cast<uint2 *>(&rt[1][gr]) = make_uint2(lo2[0], lo2[1]);
+      }
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      rp[tb] += __shfl_xor(rp[tb], 16);
+      rp[tb] += __shfl_xor(rp[tb], 32);
+    }
+    if (kq == 0) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) rho2[wave][tb * 16 + c16] = rp[tb];
+    }
+    __syncthreads();
+    // ---- product 2: z[sketch row 32w + 16cb + 4kq + r][token] = S r, signs into bit 7 of the code bytes
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 rh[4], rl[4], sa[2][2];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int g = swz(tb * 16 + c16, 16, ks * 4 + kq, 15) * 8;
+        rh[tb] = ld_bf8(&rt[0][g]);
+        rl[tb] = ld_bf8(&rt[1][g]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp)
+          sa[cb][sp] = ld_bf8(a.sk2 + ((sp * QD) + 32 * wave + 16 * cb + c16) * QD + ks * 32 + kq * 8);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          acc[cb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[cb][0], rh[tb], acc[cb][tb], 0, 0, 0);
+          acc[cb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[cb][0], rl[tb], acc[cb][tb], 0, 0, 0);
+          acc[cb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[cb][1], rh[tb], acc[cb][tb], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int tok = tb * 16 + c16;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int c0 = 32 * wave + 16 * cb + 4 * kq;
+        uint32_t sg = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sg |= (acc[cb][tb][r] >= 0.f ? 0x80u : 0u) << (8 * r);
+        atomicOr(&stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)], sg);
+      }
+    }
+    __syncthreads();
+    // ---- pack: thread (token, 32-coordinate group) -> B code planes + the sign plane
+    {
+      const int tok = tid >> 2, g = tid & 3;
+      if (tok < nv) {
+        const int64_t rec = s * a.os + a.oo + t0 + tok;
+        const float n = nrm[tok];
+        uint32_t w[B + 1];
+        if (n > 0.f) {
+          const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g, 7) * 4]);
+          const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g + 1, 7) * 4]);
+          const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+          for (int p = 0; p <= B; ++p) {
+            const int bit = p < B ? p : 7;
+            uint32_t word = 0;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) word |= gather4(d8[m], bit) << (4 * m);
+            w[p] = word;
+          }
+        } else {
+#pragma unroll
+          for (int p = 0; p <= B; ++p) w[p] = 0u;
+        }
+        uint32_t *dst = a.bits_out + (rec * QW + g) * (B + 1);
+        if constexpr (B == 3) {
+          *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+          for (int p = 0; p <= B; ++p) dst[p] = w[p];
+        }
+        if (g == 0) {
+          const float rho = sqrtf((rho2[0][tok] + rho2[1][tok]) + (rho2[2][tok] + rho2[3][tok]));
+          *reinterpret_cast<float2 *>(a.norms_out + 2 * rec) = n > 0.f ? make_float2(n, rho) : make_float2(0.f, 0.f);
+        }
+      }
+    }
+  } else {
+    // acc[cb][tb][r] = y[token tb*16 + 4kq + r][coordinate 32w + 16cb + c16] * |x|
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      float inv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float n = nrm[tb * 16 + 4 * kq + r];
+        inv[r] = n > 0.f ? 1.f / n : 0.f;
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int j = 32 * wave + 16 * cb + c16;
+        uint32_t bytes = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t idx;
+          (void)code(acc[cb][tb][r] * inv[r], idx);
+          bytes |= idx << (8 * r);
+        }
+        // tokens tb*16 + 4kq .. +3 of coordinate j: granule tb, dword kq
+        stage[swz(j, 4, tb, 3) * 4 + kq] = bytes;
+      }
+    }
+    __syncthreads();
+    // ---- pack: thread (coordinate, 32-token block) -> B token-major code planes
+    const uint64_t lmask = __builtin_amdgcn_ballot_w64(lane < nv && nrm[lane] > 0.f);  // live tokens
+    {
+      const int j = tid >> 1, hb = tid & 1;
+      const int nb = nv - 32 * hb;  // valid tokens of this block
+      if (nb > 0) {
+        const uint32_t live = (uint32_t)(lmask >> (32 * hb));
+        const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(j, 4, 2 * hb, 3) * 4]);
+        const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(j, 4, 2 * hb + 1, 3) * 4]);
+        const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        const int64_t blk = (s * a.os + a.oo + t0) / 32 + hb;
+        uint32_t *dst = a.bits_out + (blk * QD + j) * B;
+#pragma unroll
+        for (int p = 0; p < B; ++p) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) word |= gather4(d8[m], p) << (4 * m);
+          dst[p] = word & live;
+        }
+      }
+      if (tid < nv) a.norms_out[s * a.os + a.oo + t0 + tid] = nrm[tid];
+    }
+  }
+}
+
+template <bool KEYS>
+static hipError_t launch_quant128(const Q128Args &q, int bits, dim3 grid, hipStream_t st) {
+  switch (bits) {
+    case 1: hipLaunchKernelGGL((quant128_kernel<KEYS, 1>), grid, dim3(256), 0, st, q); break;
+    case 2: hipLaunchKernelGGL((quant128_kernel<KEYS, 2>), grid, dim3(256), 0, st, q); break;
+    case 3: hipLaunchKernelGGL((quant128_kernel<KEYS, 3>), grid, dim3(256), 0, st, q); break;
+    case 4: hipLaunchKernelGGL((quant128_kernel<KEYS, 4>), grid, dim3(256), 0, st, q); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+static hipError_t quant128(const tq_ctx *ctx, bool keys, const void *x, int64_t n_streams, int64_t n_tokens,
+                           int64_t xs, int64_t xt, const tq_packed *out, int64_t os, int64_t oo, hipStream_t st) {
+  Q128Args q = {};
+  q.x = (const uint16_t *)x;
+  q.n_tokens = n_tokens;
+  q.xs = xs;
+  q.xt = xt;
+  q.rot3 = ctx->d_rot3;
+  q.sk2 = ctx->d_sk2;
+  q.tables = ctx->d_tables;
+  q.bits_out = out->bits;
+  q.norms_out = out->norms;
+  q.os = os;
+  q.oo = oo;
+  dim3 grid((unsigned)((n_tokens + QT - 1) / QT), (unsigned)n_streams);
+  return keys ? launch_quant128<true>(q, out->mse_bits, grid, st) : launch_quant128<false>(q, out->mse_bits, grid, st);
+}
+
 hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams, int64_t n_tokens,
                                 int64_t xs, int64_t xt, const tq_packed *out, int64_t os, int64_t oo, float *work,
                                 hipStream_t st) {
   const int d = ctx->d;
+  if (d == QD && is_bf16 && ctx->d_rot3) return quant128(ctx, true, x, n_streams, n_tokens, xs, xt, out, os, oo, st);
   GemmArgs g = {};
   g.a = {x, xt, n_tokens, is_bf16};
   g.a_stream_stride = xs;
@@ -372,6 +731,7 @@ hipError_t launch_quantize_values(const tq_ctx *ctx, const void *x, int is_bf16,
                                   int64_t n_tokens, int64_t xs, int64_t xt, const tq_packed *out, int64_t os,
                                   int64_t oo, hipStream_t st) {
   const int d = ctx->d;
+  if (d == QD && is_bf16 && ctx->d_rot3) return quant128(ctx, false, x, n_streams, n_tokens, xs, xt, out, os, oo, st);
   GemmArgs g = {};
   g.a = {ctx->d_rot, d, d, 0};
   g.a_stream_stride = 0;
