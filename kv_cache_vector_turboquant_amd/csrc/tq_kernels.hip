@@ -371,23 +371,27 @@ __device__ __forceinline__ bf16x8 ld_bf8(const uint16_t *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
 }
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float sumsq8(bf16x8 v) {
+// sum of squares of 8 bf16 values (products exact, fp32 accumulation)
+__device__ __forceinline__ float sumsq8(bf16x8 v, float s) {
   const uint4 u = __builtin_bit_cast(uint4, v);
-  float s = 0.f;
-  s = fmaf(bf_lo(u.x), bf_lo(u.x), s); s = fmaf(bf_hi(u.x), bf_hi(u.x), s);
-  s = fmaf(bf_lo(u.y), bf_lo(u.y), s); s = fmaf(bf_hi(u.y), bf_hi(u.y), s);
-  s = fmaf(bf_lo(u.z), bf_lo(u.z), s); s = fmaf(bf_hi(u.z), bf_hi(u.z), s);
-  s = fmaf(bf_lo(u.w), bf_lo(u.w), s); s = fmaf(bf_hi(u.w), bf_hi(u.w), s);
-  return s;
+  const bf16x2 p0 = __builtin_bit_cast(bf16x2, u.x), p1 = __builtin_bit_cast(bf16x2, u.y);
+  const bf16x2 p2 = __builtin_bit_cast(bf16x2, u.z), p3 = __builtin_bit_cast(bf16x2, u.w);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(p3, p3, s, false);
 }
 
-// bf16 with round-to-nearest-even (inputs are finite)
-__device__ __forceinline__ uint32_t to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// two fp32 values as bf16 (round to nearest even) hi parts packed in a dword,
+// and the bf16 parts of what is left
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  const bf16x2 h = {(__bf16)a, (__bf16)b};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xFFFF0000u);
+  const bf16x2 l = {(__bf16)ra, (__bf16)rb};
+  lo = __builtin_bit_cast(uint32_t, l);
 }
 
 // Bit p of each of the 4 bytes of w, gathered into bits 0..3 (byte k -> bit k).
@@ -408,7 +412,7 @@ __global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
   __shared__ __attribute__((aligned(16))) uint32_t stage[QT * QD / 4];
   // keys: residual parts, [token][coordinate] bf16 (16 granules per token row)
   __shared__ __attribute__((aligned(16))) uint16_t rt[KEYS ? 2 : 1][KEYS ? QT * QD : 8];
-  __shared__ float nrm[QT];
+  __shared__ float nrm[QT], ninv[QT];
   __shared__ float rho2[4][QT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
@@ -432,18 +436,26 @@ __global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
   struct Frag1 {
     bf16x8 x[4], p[2][3];
   };
+  // row pointers of the lane: its token of each block (rows past the end re-read
+  // the last token) and its coordinate of each block in every part of Pi
+  const uint16_t *xrow[4], *prow[2][3];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) xrow[tb] = xb + (int64_t)min(tb * 16 + c16, nv - 1) * a.xt + kq * 8;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp) prow[cb][sp] = a.rot3 + (sp * QD + 32 * wave + 16 * cb + c16) * QD + kq * 8;
   auto load1 = [&](int ks, Frag1 &f) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) f.x[tb] = ld_bf8(xb + (int64_t)min(tb * 16 + c16, nv - 1) * a.xt + ks * 32 + kq * 8);
+    for (int tb = 0; tb < 4; ++tb) f.x[tb] = ld_bf8(xrow[tb] + ks * 32);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int sp = 0; sp < 3; ++sp)
-        f.p[cb][sp] = ld_bf8(a.rot3 + ((sp * QD) + 32 * wave + 16 * cb + c16) * QD + ks * 32 + kq * 8);
+      for (int sp = 0; sp < 3; ++sp) f.p[cb][sp] = ld_bf8(prow[cb][sp] + ks * 32);
   };
   auto comp1 = [&](const Frag1 &f) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) ss[tb] += sumsq8(f.x[tb]);
+    for (int tb = 0; tb < 4; ++tb) ss[tb] = sumsq8(f.x[tb], ss[tb]);
 #pragma unroll
     for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
@@ -472,24 +484,28 @@ __global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
   }
   if (wave == 0 && kq == 0) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) nrm[tb * 16 + c16] = sqrtf(ss[tb]);
+    for (int tb = 0; tb < 4; ++tb) {
+      const float n = sqrtf(ss[tb]);
+      nrm[tb * 16 + c16] = n;
+      ninv[tb * 16 + c16] = n > 0.f ? 1.f / n : 0.f;
+    }
   }
   if constexpr (!KEYS) __syncthreads();
 
-  // code of y: byte idx, centroid value
+  // code of y: idx = H + mag (y >= 0) or its mirror 2H - 1 - (H + mag) (y < 0); the
+  // centroid is the magnitude table entry with the sign of y
   auto code = [&](float y, uint32_t &idx) {
     const float ay = fabsf(y);
-    int mag = 0;
+    uint32_t mag = 0;
     float c = cm[0];
 #pragma unroll
     for (int j = 0; j < H - 1; ++j) {
       const bool ge = ay >= tp[j];
-      mag += ge ? 1 : 0;
+      mag += (uint32_t)ge;
       c = ge ? cm[j + 1] : c;
     }
-    const bool neg = y < 0.f;
-    idx = (uint32_t)(neg ? H - 1 - mag : H + mag);
-    return neg ? -c : c;
+    idx = ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
+    return __builtin_copysignf(c, y);
   };
 
   if constexpr (KEYS) {
@@ -503,19 +519,18 @@ __global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const int c0 = 32 * wave + 16 * cb + 4 * kq;  // first of the lane's 4 coordinates
-        uint32_t bytes = 0, hi2[2] = {0, 0}, lo2[2] = {0, 0};
+        uint32_t bytes = 0, hi2[2], lo2[2];
+        float res[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float y = acc[cb][tb][r] * inv;
           uint32_t idx;
-          const float res = y - code(y, idx);
+          res[r] = y - code(y, idx);
           bytes |= idx << (8 * r);
-          rp[tb] = fmaf(res, res, rp[tb]);
-          const uint32_t h = to_bf16(res);
-          const uint32_t l = to_bf16(res - __uint_as_float(h << 16));
-          hi2[r >> 1] |= h << (16 * (r & 1));
-          lo2[r >> 1] |= l << (16 * (r & 1));
+          rp[tb] = fmaf(res[r], res[r], rp[tb]);
         }
+        split2(res[0], res[1], hi2[0], lo2[0]);
+        split2(res[2], res[3], hi2[1], lo2[1]);
         // code bytes of 4 coordinates: granule c0 / 16, dword (c0 / 4) % 4
         stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
         // residual parts: granule c0 / 8 of 16, half (c0 / 4) % 2
@@ -539,6 +554,11 @@ __global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
+    const uint16_t *srow[2][2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) srow[cb][sp] = a.sk2 + (sp * QD + 32 * wave + 16 * cb + c16) * QD + kq * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 rh[4], rl[4], sa[2][2];
@@ -552,7 +572,7 @@ __global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp)
-          sa[cb][sp] = ld_bf8(a.sk2 + ((sp * QD) + 32 * wave + 16 * cb + c16) * QD + ks * 32 + kq * 8);
+          sa[cb][sp] = ld_bf8(srow[cb][sp] + ks * 32);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -615,12 +635,8 @@ __global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
     // acc[cb][tb][r] = y[token tb*16 + 4kq + r][coordinate 32w + 16cb + c16] * |x|
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      float inv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float n = nrm[tb * 16 + 4 * kq + r];
-        inv[r] = n > 0.f ? 1.f / n : 0.f;
-      }
+      const float4 inv4 = *reinterpret_cast<const float4 *>(&ninv[tb * 16 + 4 * kq]);
+      const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const int j = 32 * wave + 16 * cb + c16;
