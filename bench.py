@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--kbits", type=int, default=3, help="MSE bits of the keys (b = kbits + 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--separate-append", action="store_true",
+                    help="serving step: tq_append_token then tq_attention_decode instead of tq_decode_step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run 5 device-to-device copies of this many MiB (a plain copy kernel of known size, "
                          "the calibration of the rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -149,7 +151,9 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     cache = tq.KVCache(B, H, cap, d, kbits, vbits)
     kwork = torch.empty(tq.quantize_ws_bytes(ctx, B * H, L, True), dtype=torch.uint8, device="cuda")
     cache.host_max_len = cap
-    dws = torch.empty(cache.decode_ws_bytes(ctx, Hq), dtype=torch.uint8, device="cuda")
+    fused = NS > 0 and not args.separate_append
+    dws = torch.empty(max(cache.decode_ws_bytes(ctx, Hq), cache.decode_step_ws_bytes(ctx, Hq)), dtype=torch.uint8,
+                      device="cuda")
     cache.host_max_len = 0
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     timer = Timer(torch)
@@ -166,13 +170,18 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     def step(record):
         prefill()
         for i in range(n_dec):
-            if NS > 0:
-                cache.append(ctx, KA[i], VA[i])
             n = L + (i + 1 if NS > 0 else 0)
-            if record:
-                dec_events.append((timer(lambda: cache.decode(ctx, QS[i], out=out, ws=dws)), n))
+            if fused:
+                # one serving step: append the new K/V token and decode with it (tq_decode_step)
+                call = lambda: cache.decode_step(ctx, KA[i], VA[i], QS[i], out=out, ws=dws)  # noqa: E731
             else:
-                cache.decode(ctx, QS[i], out=out, ws=dws)
+                if NS > 0:
+                    cache.append(ctx, KA[i], VA[i])
+                call = lambda: cache.decode(ctx, QS[i], out=out, ws=dws)  # noqa: E731
+            if record:
+                dec_events.append((timer(call), n))
+            else:
+                call()
 
     for _ in range(args.warmup):
         step(False)
@@ -206,7 +215,9 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         "decode_ms_per_launch": avg_ms, "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "tq_attention_decode (decode_prep_kernel + decode_kernel + decode_merge_kernel)",
+                     "kernel": ("tq_decode_step (decode_prep_kernel with the append + decode_kernel + "
+                                "decode_merge_kernel)" if fused else
+                                "tq_attention_decode (decode_prep_kernel + decode_kernel + decode_merge_kernel)"),
                      "algorithmic_bytes_per_launch": float(dec_bytes.mean()), "avg_launch_ms": avg_ms,
                      "bytes_per_kv_token": rec_bytes},
     }

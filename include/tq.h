@@ -179,6 +179,23 @@ tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const
                               int32_t q_heads, float scale, float *d_out, void *d_ws, size_t ws_bytes,
                               void *stream);
 
+/* Fused serving step: the same result as tq_append_token(d_k, d_v) followed by
+ * tq_attention_decode(d_q) on the same stream (the new token is attended),
+ * in three launches instead of five: the query preparation encodes the new
+ * token of each stream, decode reads the post-append lengths from the
+ * workspace, and the merge launch advances d_seq_len. d_k, d_v: contiguous
+ * [batch][kv_heads][d]; d_q: [batch][q_heads][d]; all of `dtype`. Increments
+ * cache->host_max_len. The O(1) append requirement is the one stated in the
+ * fractal KV-archive summary on gist.science.
+ * d_ws: workspace of tq_decode_step_ws_bytes() bytes (not shared with a
+ * concurrent call).
+ * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d != 128, group > 16),
+ * TQ_ERR_CAPACITY (cache full or workspace too small), TQ_ERR_HIP. */
+size_t tq_decode_step_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads);
+tq_status tq_decode_step(const tq_ctx *ctx, tq_kv_cache *cache, const void *d_k, const void *d_v, const void *d_q,
+                         tq_dtype dtype, int32_t q_heads, float scale, float *d_out, void *d_ws, size_t ws_bytes,
+                         void *stream);
+
 /* Scores of nq queries against n packed keys ([ebisuda] 第2段階; [hakusoku]
  * QJL: full-precision query, low-precision data):
  *   s[q][t] = ||k_t|| (<Pi q, c[idx_t]> + sqrt(pi/2)/m ||r_t|| <S Pi q, 2 sigma_t - 1>).

@@ -78,6 +78,9 @@ _sig("tq_quantize_kv", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c
                                 _c_i64, _c_i64, _c_vp, _c_sz, _c_vp])
 _sig("tq_append_token", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_i32, _c_vp])
 _sig("tq_attention_decode_ws_bytes", _c_sz, [_c_vp, ctypes.POINTER(CCache), _c_i32])
+_sig("tq_decode_step_ws_bytes", _c_sz, [_c_vp, ctypes.POINTER(CCache), _c_i32])
+_sig("tq_decode_step", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_f32, _c_vp,
+                                _c_vp, _c_sz, _c_vp])
 _sig("tq_attention_decode", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp,
                                      _c_sz, _c_vp])
 _sig("tq_scores_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64, _c_i32, _c_i32])
@@ -87,7 +90,8 @@ _sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked)
 EXPORTED_SYMBOLS = [
     "tq_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
     "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_append_token", "tq_attention_decode_ws_bytes",
-    "tq_attention_decode", "tq_scores_ws_bytes", "tq_scores", "tq_last_error",
+    "tq_attention_decode", "tq_decode_step_ws_bytes", "tq_decode_step", "tq_scores_ws_bytes", "tq_scores",
+    "tq_last_error",
 ]
 
 
@@ -330,6 +334,31 @@ class KVCache:
         cc = self.c()
         _check(_lib.tq_attention_decode(ctx.handle, ctypes.byref(cc), q.data_ptr(), _dtype_code(q), Hq,
                                         float(scale), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr()))
+        return out
+
+    def decode_step_ws_bytes(self, ctx: Context, q_heads: int) -> int:
+        cc = self.c()
+        return int(_lib.tq_decode_step_ws_bytes(ctx.handle, ctypes.byref(cc), q_heads))
+
+    def decode_step(self, ctx: Context, k, v, q, scale: float | None = None, out=None, ws=None):
+        """Fused serving step: append k, v ([batch, kv_heads, d]) then decode q
+        ([batch, q_heads, d]) with the new token attended. Returns fp32 [batch, q_heads, d]."""
+        torch = _torch()
+        assert k.is_contiguous() and v.is_contiguous() and q.is_contiguous()
+        assert k.dtype == v.dtype == q.dtype
+        B, Hq, d = q.shape
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        need = self.decode_step_ws_bytes(ctx, Hq)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+        cc = self.c()
+        _check(_lib.tq_decode_step(ctx.handle, ctypes.byref(cc), k.data_ptr(), v.data_ptr(), q.data_ptr(),
+                                   _dtype_code(q), Hq, float(scale), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                   _stream_ptr()))
+        self.host_max_len = cc.host_max_len
         return out
 
 

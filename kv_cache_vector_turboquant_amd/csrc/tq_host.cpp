@@ -526,6 +526,40 @@ tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const
   return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 
+size_t tq_decode_step_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads) {
+  if (!ctx || !cache || q_heads <= 0 || cache->kv_heads <= 0 || (q_heads % cache->kv_heads) != 0) return 0;
+  tq_kv_cache after = *cache;
+  after.host_max_len = std::min(cache->host_max_len + 1, cache->capacity);
+  return decode_ws_bytes(ctx, &after, q_heads, nullptr, nullptr);
+}
+
+tq_status tq_decode_step(const tq_ctx *ctx, tq_kv_cache *cache, const void *d_k, const void *d_v, const void *d_q,
+                         tq_dtype dtype, int32_t q_heads, float scale, float *d_out, void *d_ws, size_t ws_bytes,
+                         void *stream) {
+  const char *fn = "tq_decode_step";
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_decode_step: NULL ctx");
+  tq_status s = check_cache(ctx, cache, fn);
+  if (s != TQ_OK) return s;
+  if (!d_k || !d_v || !d_q || !d_out) return fail(TQ_ERR_ARG, "tq_decode_step: NULL input or output");
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_decode_step: dtype must be TQ_F32 or TQ_BF16");
+  if (q_heads <= 0 || (q_heads % cache->kv_heads) != 0)
+    return fail(TQ_ERR_ARG, "tq_decode_step: q_heads must be a positive multiple of kv_heads");
+  if (q_heads / cache->kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_step: at most 16 query heads per KV head");
+  if (ctx->d != 128) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_step: d must be 128");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_ARG, "tq_decode_step: scale must be finite");
+  if (cache->host_max_len + 1 > cache->capacity) return fail(TQ_ERR_CAPACITY, "tq_decode_step: cache is full");
+  size_t need = tq_decode_step_ws_bytes(ctx, cache, q_heads);
+  if (!d_ws || ws_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_decode_step: workspace smaller than tq_decode_step_ws_bytes()");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  tq_kv_cache after = *cache;
+  after.host_max_len = cache->host_max_len + 1;
+  hipError_t e = launch_decode(ctx, &after, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream,
+                               d_k, d_v);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  cache->host_max_len += 1;
+  return TQ_OK;
+}
+
 size_t tq_scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores) {
   if (!ctx || nq <= 0 || n <= 0 || topk < 0) return 0;
   return scores_ws_bytes(ctx, nq, n, topk, want_scores);

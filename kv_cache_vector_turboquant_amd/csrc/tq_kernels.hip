@@ -967,6 +967,13 @@ struct DecodeArgs {
   float *qconst;         // [stream*hgroups][4][QC]: units of the fixed-point q_rot, q_s
   float *partial;        // [batch*q_heads][nchunks][DD + 2]
   float *out;
+  // fused step: the prep launch first appends each stream's new K/V token
+  const void *ka, *va;   // [batch][kv_heads][DD], the query dtype
+  const float *sk;       // S, row-major
+  uint32_t *kbits_w, *vbits_w;
+  float *knorm_w, *vnorm_w;
+  int32_t *wlen;         // [batch] length after the append; read by decode_kernel instead of seq_len
+  int32_t *len_inc;      // lengths the merge kernel advances (fused step only)
 };
 
 // The i-th odd-cardinality subset of the B planes, ordered by (popcount, value).
@@ -981,17 +988,99 @@ __device__ __forceinline__ uint32_t fp6_mag(uint32_t mag, int fi) {
   return fi == 0 ? c1 : (mag << (fi == 1 ? 2 : 1));
 }
 
-// One block per (stream, head group): q_rot = Pi q, q_s = S q_rot for up to 4
-// heads, fixed-point split and A-fragment layout.
 template <typename QT>
 __device__ __forceinline__ float qload(const QT *q, int64_t i) {
   if constexpr (sizeof(QT) == 2) return bf16f(q[i]);
   else return q[i];
 }
 
-template <typename QT>
+// Fused step: encodes a stream's new token as record `pos` (called by the whole
+// 512-thread block). ykv holds Pi k and Pi v ([2][DD], LDS), red[0..3] the wave
+// sums of k^2 (0, 1) and v^2 (2, 3); zp is LDS scratch of 4 x DD floats.
+__device__ __forceinline__ void append_token(const DecodeArgs &a, int stream, int pos, int tid, float *ykv, float *zp,
+                                             float *red) {
+  const int64_t rec = (int64_t)stream * a.capacity + pos;
+  const float nk = sqrtf(red[0] + red[1]), nv = sqrtf(red[2] + red[3]);
+  const int kB = a.kbitsB, vB = a.vbitsB;
+  const int lane = tid & 63, w = tid >> 6;
+  int idx = 0;
+  if (tid < DD) {
+    // key coordinate j: code, residual (kept in ykv row 0), |r|^2
+    const bool live = nk > 0.f;
+    const float y = live ? ykv[tid] / nk : 0.f;
+    for (int i = 0; i < (1 << kB) - 1; ++i) idx += (y >= a.tables->boundary[kB][i]) ? 1 : 0;
+    if (!live) idx = 0;
+    const float r = live ? y - a.tables->centroid[kB][idx] : 0.f;
+    ykv[tid] = r;
+    float r2 = r * r;
+    for (int off = 32; off > 0; off >>= 1) r2 += __shfl_xor(r2, off);
+    if (lane == 0) red[4 + w] = r2;
+  } else if (tid < 2 * DD) {
+    // value coordinate j: code bits into the token-major words of its 32-token block
+    const int j = tid - DD;
+    const bool live = nv > 0.f;
+    const float y = live ? ykv[DD + j] / nv : 0.f;
+    int iv = 0;
+    for (int i = 0; i < (1 << vB) - 1; ++i) iv += (y >= a.tables->boundary[vB][i]) ? 1 : 0;
+    if (!live) iv = 0;
+    const int bit_pos = (int)(rec & 31);
+    uint32_t *dst = a.vbits_w + ((rec >> 5) * DD + j) * vB;
+    for (int p = 0; p < vB; ++p) {
+      const uint32_t bit = (uint32_t)((iv >> p) & 1) << bit_pos;
+      dst[p] = (bit_pos == 0) ? bit : ((dst[p] & ~(1u << bit_pos)) | bit);
+    }
+  }
+  __syncthreads();
+  {
+    // z = S r: thread (sketch row i, coordinate quarter)
+    const int i = tid & (DD - 1), qq = tid >> 7;
+    const float4 *srow = reinterpret_cast<const float4 *>(a.sk + (int64_t)i * DD + 32 * qq);
+    const float *rr = ykv + 32 * qq;
+    float z = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 sv = srow[u];
+      z = fmaf(sv.x, rr[4 * u], z);
+      z = fmaf(sv.y, rr[4 * u + 1], z);
+      z = fmaf(sv.z, rr[4 * u + 2], z);
+      z = fmaf(sv.w, rr[4 * u + 3], z);
+    }
+    zp[qq * DD + i] = z;
+  }
+  __syncthreads();
+  if (tid < DD) {
+    const float z = (zp[tid] + zp[DD + tid]) + (zp[2 * DD + tid] + zp[3 * DD + tid]);
+    const bool live = nk > 0.f;
+    uint32_t words[5];
+    for (int p = 0; p < kB; ++p) {
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(((idx >> p) & 1) != 0);
+      words[p] = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
+    }
+    const uint64_t sbal = __builtin_amdgcn_ballot_w64(live && z >= 0.f);
+    words[kB] = (lane < 32) ? (uint32_t)sbal : (uint32_t)(sbal >> 32);
+    if ((lane & 31) == 0) {
+      uint32_t *dst = a.kbits_w + (rec * DW + w * 2 + (lane >> 5)) * (kB + 1);
+      for (int p = 0; p <= kB; ++p) dst[p] = words[p];
+    }
+    if (tid == 0) {
+      a.knorm_w[2 * rec] = nk;
+      a.knorm_w[2 * rec + 1] = live ? sqrtf(red[4] + red[5]) : 0.f;
+      a.vnorm_w[rec] = nv;
+    }
+  }
+}
+
+// One block per (stream, head group): q_rot = Pi q, q_s = S q_rot for up to 4
+// heads, fixed-point split and A-fragment layout. With APPEND (fused step) the
+// stream's new K/V token is encoded first, reusing the Pi rows of the block.
+
+template <typename QT, bool APPEND>
 __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) float qk[DD][4];  // the queries, [coordinate][head]
+  // the queries [coordinate][head]; fused step: the new k, v as "heads" 4 and 5
+  __shared__ __attribute__((aligned(16))) float qk[DD][APPEND ? 8 : 4];
+  __shared__ float ykv[APPEND ? 2 : 1][DD];  // Pi k, Pi v; then the key residual in row 0
+  __shared__ float zp[APPEND ? 4 : 1][DD];   // partial S r over four coordinate quarters
+  __shared__ float red[8];
   __shared__ float part2[4][2 * DD];
   __shared__ float qv[2][4][DD];  // q_rot, q_s
   __shared__ float mx[2][4];      // max |q_rot|, max |q_s| per head
@@ -1016,10 +1105,27 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
     const int hh = tid >> 7, k = tid & (DD - 1);
     qk[k][hh] = hh < nh ? qload(q, (int64_t)hh * DD + k) : 0.f;
   }
+  // fused step: stream's new token (block hg = 0 of the stream), position = current length
+  const bool app = APPEND && hg == 0;
+  int pos = 0;
+  if constexpr (APPEND) {
+    pos = a.seq_len[b];
+    if (app && tid < 2 * DD) {
+      const int which = tid >> 7, k = tid & (DD - 1);
+      const QT *src = reinterpret_cast<const QT *>(which ? a.va : a.ka) + (int64_t)stream * DD;
+      const float x = qload(src, k);
+      qk[k][4 + which] = x;
+      float sq = x * x;  // |k|^2 (waves 0, 1) and |v|^2 (waves 2, 3)
+      for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+      if ((tid & 63) == 0) red[tid >> 6] = sq;
+    }
+    if (tid == 0 && kvh == 0 && hg == 0) a.wlen[b] = min(pos + 1, a.capacity);
+  }
   __syncthreads();
   // one 16-byte LDS broadcast gives the four query entries of a k
   {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float ak = 0.f, av = 0.f;  // fused step: the rows against the new k and v (used for r < 128)
 #pragma unroll
     for (int u = 0; u < 64; ++u) {
       const float4 qq = *reinterpret_cast<const float4 *>(qk[kh * 64 + u]);
@@ -1027,18 +1133,34 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
       acc[1] = fmaf(mrow[u], qq.y, acc[1]);
       acc[2] = fmaf(mrow[u], qq.z, acc[2]);
       acc[3] = fmaf(mrow[u], qq.w, acc[3]);
+      if constexpr (APPEND) {
+        const float2 x = *reinterpret_cast<const float2 *>(&qk[kh * 64 + u][4]);
+        ak = fmaf(mrow[u], x.x, ak);
+        av = fmaf(mrow[u], x.y, av);
+      }
     }
     if (kh == 1) {
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) part2[hh][r] = acc[hh];
+      if (APPEND && app && r < DD) {
+        ykv[0][r] = ak;
+        ykv[1][r] = av;
+      }
     }
     __syncthreads();
     if (kh == 0) {
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) qv[r >> 7][hh][r & (DD - 1)] = acc[hh] + part2[hh][r];
+      if (APPEND && app && r < DD) {
+        ykv[0][r] += ak;
+        ykv[1][r] += av;
+      }
     }
   }
   __syncthreads();
+  if constexpr (APPEND) {
+    if (app && pos < a.capacity) append_token(a, stream, pos, tid, &ykv[0][0], &zp[0][0], red);
+  }
   if (tid < 256) {
     // max |.| per (type, head): wave w reduces (type, head pair) rows
     const int lane = tid & 63, w = tid >> 6, T = w >> 1;
@@ -1151,6 +1273,8 @@ __global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
   const int b = stream / a.kv_heads;
   const int h0 = (stream % a.kv_heads) * a.group + hg * 4;
   const int nh = min(4, a.group - hg * 4);
+  // fused step: the appended token is now part of every stream of sequence b
+  if (a.len_inc && tid == 0 && hg == 0 && stream % a.kv_heads == 0 && a.len_inc[b] < a.capacity) a.len_inc[b] += 1;
   const int cg = tid >> 8, hh = (tid >> 6) & 3;  // chunk group, head (one wave per pair)
   const int nc = a.nchunks;
   const float *p = a.partial + ((int64_t)b * a.q_heads + h0 + min(hh, nh - 1)) * nc * (DD + 2);
@@ -1236,7 +1360,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int hg = sg % a.hgroups, stream = sg / a.hgroups;
   const int b = stream / a.kv_heads;
   const int nh = min(4, a.group - hg * 4);
-  const int len = a.seq_len[b];
+  const int len = a.wlen ? a.wlen[b] : a.seq_len[b];
   const int t0 = c * a.chunk;
   const int t1 = min(len, t0 + a.chunk);
   const int h0 = (stream % a.kv_heads) * a.group + hg * 4;
@@ -1501,6 +1625,8 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
   b += (size_t)streams * 4 * QC * sizeof(float);  // qconst
   b = (b + 255) & ~(size_t)255;
   b += (size_t)cache->batch * q_heads * nchunks * (DD + 2) * sizeof(float);  // partials
+  b = (b + 255) & ~(size_t)255;
+  b += (size_t)cache->batch * sizeof(int32_t);  // fused step: lengths after the append
   (void)ctx;
   return b;
 }
@@ -1512,7 +1638,7 @@ static hipError_t launch_decode_kv(const DecodeArgs &a, dim3 grid, size_t shm, h
 }
 
 hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
-                         float scale, float *out, void *ws, hipStream_t st) {
+                         float scale, float *out, void *ws, hipStream_t st, const void *k_new, const void *v_new) {
   int chunk = 0, nchunks = 0;
   decode_ws_bytes(ctx, cache, q_heads, &chunk, &nchunks);
   DecodeArgs a = {};
@@ -1544,11 +1670,28 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.qconst = (float *)p;
   p += (((size_t)streams * 4 * QC * sizeof(float)) + 255) & ~(size_t)255;
   a.partial = (float *)p;
+  p += (((size_t)cache->batch * q_heads * nchunks * (DD + 2) * sizeof(float)) + 255) & ~(size_t)255;
   a.out = out;
+  const bool step = k_new != nullptr;
+  if (step) {
+    // fused step: the prep launch appends the new token; decode reads the new
+    // lengths from the workspace and the merge launch advances seq_len
+    a.ka = k_new;
+    a.va = v_new;
+    a.sk = ctx->d_sketch;
+    a.kbits_w = cache->k.bits;
+    a.vbits_w = cache->v.bits;
+    a.knorm_w = cache->k.norms;
+    a.vnorm_w = cache->v.norms;
+    a.wlen = (int32_t *)p;
+    a.len_inc = cache->d_seq_len;
+  }
   if (is_bf16)
-    hipLaunchKernelGGL(decode_prep_kernel<uint16_t>, dim3(streams), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((step ? decode_prep_kernel<uint16_t, true> : decode_prep_kernel<uint16_t, false>), dim3(streams),
+                       dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL(decode_prep_kernel<float>, dim3(streams), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((step ? decode_prep_kernel<float, true> : decode_prep_kernel<float, false>), dim3(streams),
+                       dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t shm = (size_t)5 * chunk * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;

@@ -344,6 +344,57 @@ def test_append_tokens(c128, dtype):
         assert np.all(np.abs(gvn[s * cap + L0:s * cap + L0 + NA] - enc_v.norm) <= 2e-6 * enc_v.norm)
 
 
+@pytest.mark.parametrize("dtype,hq", [("bf16", 8), ("f32", 4)])
+def test_decode_step_appends_and_attends(c128, dtype, hq):
+    """Fused serving step: prefill 37 oracle-packed tokens, then 40 decode steps
+    (append one token per sequence and attend with it). Appended records match
+    the oracle's encoding, lengths advance, and sampled steps' outputs match the
+    oracle attention over the records the cache holds after that step."""
+    ctx, Pi, S = c128
+    B, H, cap, L0, NA = 2, 2, 96, 37, 40
+    g = hq // H
+    K = synth.outlier_kv(11, (1,), synth.TAG_SCALES_K, (B, H, L0 + NA, 128), dtype)
+    V = synth.outlier_kv(11, (2,), synth.TAG_SCALES_V, (B, H, L0 + NA, 128), dtype)
+    Q = synth.outlier_kv(11, (3,), synth.TAG_SCALES_K, (NA, B, hq, 128), dtype)
+    cbk, cbv, kw, kn, vw, vn = _oracle_cache(K[:, :, :L0], V[:, :, :L0], Pi, S, 3, 3, cap)
+    cache = tq.KVCache(B, H, cap, 128, 3, 3)
+    _upload(cache.k, kw, kn)
+    _upload(cache.v, vw, vn)
+    cache.seq_len.fill_(L0)
+    cache.host_max_len = L0
+    scale = 1.0 / math.sqrt(128)
+    ws = torch.empty(cache.decode_step_ws_bytes(ctx, hq) + 1024, dtype=torch.uint8, device=DEV)
+    for t in range(NA):
+        out = cache.decode_step(ctx, _dev(K[:, :, L0 + t], dtype).contiguous(), _dev(V[:, :, L0 + t], dtype).contiguous(),
+                                _dev(Q[t], dtype).contiguous(), scale, ws=ws)
+        if t not in (0, 17, NA - 1):
+            continue
+        o = out.cpu().numpy()
+        gkw, gkn = cache.k.host()
+        gvw, gvn = cache.v.host()
+        n = L0 + t + 1
+        assert cache.seq_len.cpu().tolist() == [n] * B
+        for s in range(B * H):
+            b, h = divmod(s, H)
+            keys = {"bits": gkw[s * cap:s * cap + n], "norms": gkn[s * cap:s * cap + n]}
+            vals = {"bits": gvw[s * cap // 32:(s + 1) * cap // 32], "norms": gvn[s * cap:s * cap + n]}
+            ref = T.attention_decode(Q[t, b, h * g:(h + 1) * g], Pi, S, cbk, cbv, keys, vals, n, scale)
+            assert np.max(np.abs(o[b, h * g:(h + 1) * g] - ref)) <= 2e-3, f"step {t} b={b} h={h}"
+    torch.cuda.synchronize()
+    assert cache.seq_len.cpu().tolist() == [L0 + NA] * B and cache.host_max_len == L0 + NA
+    gkw, gkn = cache.k.host()
+    gvw, gvn = cache.v.host()
+    for s in range(B * H):
+        b, h = divmod(s, H)
+        assert np.array_equal(gkw[s * cap:s * cap + L0], kw[s * cap:s * cap + L0])
+        enc_k = T.encode(K[b, h, L0:], Pi, cbk, S)
+        P.check_key_records(gkw[s * cap + L0:s * cap + L0 + NA], gkn[s * cap + L0:s * cap + L0 + NA], enc_k, cbk, 3, 128)
+        g_idx = T.unpack_values(gvw[s * cap // 32:(s + 1) * cap // 32], 128, 3, L0 + NA)
+        enc_v = T.encode(V[b, h, L0:], Pi, cbv)
+        P.check_codes(g_idx[L0:], enc_v, cbv, "appended value codes")
+        assert np.all(np.abs(gvn[s * cap + L0:s * cap + L0 + NA] - enc_v.norm) <= 2e-6 * enc_v.norm)
+
+
 def test_append_rejects_full_cache(c128):
     ctx, _, _ = c128
     cache = tq.KVCache(1, 1, 32, 128, 3, 3)
