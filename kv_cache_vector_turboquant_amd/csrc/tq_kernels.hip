@@ -358,7 +358,7 @@ constexpr int QW = QD / 32;
 
 struct Q128Args {
   const uint16_t *x;       // bf16 input
-  int64_t n_tokens, xs, xt;  // tokens per stream; stream / token strides (elements)
+  int64_t n_streams, n_tokens, xs, xt;  // tokens per stream; stream / token strides (elements)
   const uint16_t *rot3;    // [3][128][128] bf16 parts of Pi: [part][output coordinate][k]
   const uint16_t *sk2;     // [2][128][128] bf16 parts of S: [part][sketch row][coordinate]
   const DeviceTables *tables;
@@ -404,96 +404,54 @@ __device__ __forceinline__ int swz(int row, int gran_per_row, int g, int mask) {
   return row * gran_per_row + (g ^ (row & mask));
 }
 
-template <bool KEYS, int B>
-__global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
+// NW waves per work-group; wave w owns the RB = 8 / NW blocks of 16 output
+// coordinates 16 (w RB + rb) (keys: also those sketch rows). Keys run eight waves
+// (their Pi and S parts fill ~200 VGPRs: one work-group per compute unit),
+// values four (two work-groups per compute unit overlap one's MFMA phase with
+// the other's epilogue).
+template <bool KEYS, int B, int NW>
+__global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   constexpr int H = 1 << (B - 1);  // centroids per sign
+  constexpr int RB = 8 / NW;       // row blocks per wave
+  constexpr int NT = 64 * NW;      // threads
+  constexpr int XG = QT * 16 / NT; // X granules per thread
+  // X tile: token row t (64 rows of 16 granules of 8 bf16), granule g at t * 16 + (g ^ (t & 15))
+  __shared__ __attribute__((aligned(16))) uint4 xs[QT * 16];
   // code bytes (keys: bit 7 = QJL sign): keys [token][coordinate] (8 granules per token),
   // values [coordinate][token] (4 granules per coordinate)
   __shared__ __attribute__((aligned(16))) uint32_t stage[QT * QD / 4];
   // keys: residual parts, [token][coordinate] bf16 (16 granules per token row)
   __shared__ __attribute__((aligned(16))) uint16_t rt[KEYS ? 2 : 1][KEYS ? QT * QD : 8];
   __shared__ float nrm[QT], ninv[QT];
-  __shared__ float rho2[4][QT];
+  __shared__ float rho2[NW][QT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
-  const int64_t s = blockIdx.y, t0 = (int64_t)blockIdx.x * QT;
-  const int nv = (int)min((int64_t)QT, a.n_tokens - t0);
-  const uint16_t *xb = a.x + s * a.xs + t0 * a.xt;
+  const int64_t tps = (a.n_tokens + QT - 1) / QT, total = tps * a.n_streams;
   // positive boundaries and centroid magnitudes
   float tp[H > 1 ? H - 1 : 1], cm[H];
 #pragma unroll
   for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
 #pragma unroll
   for (int j = 0; j < H; ++j) cm[j] = a.tables->centroid[B][H + j];
-
-  // ---- product 1: wave w owns output coordinates 32w .. 32w+31 (blocks cb) for the 64 tokens (blocks tb)
-  f4v acc[2][4];
+  // the wave's rows of the Pi parts (and of the S parts for keys) stay in registers
+  // for every tile the work-group processes
+  bf16x8 pf[RB][4][3];
+  bf16x8 sf[KEYS ? RB : 1][KEYS ? 4 : 1][2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = 16 * (wave * RB + rb) + c16;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
-  struct Frag1 {
-    bf16x8 x[4], p[2][3];
-  };
-  // row pointers of the lane: its token of each block (rows past the end re-read
-  // the last token) and its coordinate of each block in every part of Pi
-  const uint16_t *xrow[4], *prow[2][3];
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) xrow[tb] = xb + (int64_t)min(tb * 16 + c16, nv - 1) * a.xt + kq * 8;
+      for (int sp = 0; sp < 3; ++sp) pf[rb][ks][sp] = ld_bf8(a.rot3 + (sp * QD + r) * QD + ks * 32 + kq * 8);
+      if constexpr (KEYS) {
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int sp = 0; sp < 3; ++sp) prow[cb][sp] = a.rot3 + (sp * QD + 32 * wave + 16 * cb + c16) * QD + kq * 8;
-  auto load1 = [&](int ks, Frag1 &f) {
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) f.x[tb] = ld_bf8(xrow[tb] + ks * 32);
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int sp = 0; sp < 3; ++sp) f.p[cb][sp] = ld_bf8(prow[cb][sp] + ks * 32);
-  };
-  auto comp1 = [&](const Frag1 &f) {
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) ss[tb] = sumsq8(f.x[tb], ss[tb]);
-#pragma unroll
-    for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-          acc[cb][tb] = KEYS ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.p[cb][sp], f.x[tb], acc[cb][tb], 0, 0, 0)
-                             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.x[tb], f.p[cb][sp], acc[cb][tb], 0, 0, 0);
-  };
-  {
-    Frag1 fa, fb;
-    load1(0, fa);
-    load1(1, fb);
-    comp1(fa);
-    load1(2, fa);
-    comp1(fb);
-    load1(3, fb);
-    comp1(fa);
-    comp1(fb);
-  }
-  // token norms: lanes of one c16 hold the four k quarters
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    ss[tb] += __shfl_xor(ss[tb], 16);
-    ss[tb] += __shfl_xor(ss[tb], 32);
-  }
-  if (wave == 0 && kq == 0) {
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const float n = sqrtf(ss[tb]);
-      nrm[tb * 16 + c16] = n;
-      ninv[tb * 16 + c16] = n > 0.f ? 1.f / n : 0.f;
+        for (int sp = 0; sp < 2; ++sp) sf[rb][ks][sp] = ld_bf8(a.sk2 + (sp * QD + r) * QD + ks * 32 + kq * 8);
+      }
     }
   }
-  if constexpr (!KEYS) __syncthreads();
-
   // code of y: idx = H + mag (y >= 0) or its mirror 2H - 1 - (H + mag) (y < 0); the
-  // centroid is the magnitude table entry with the sign of y
+  // centroid is the magnitude table entry with the sign of y (one select chain each)
   auto code = [&](float y, uint32_t &idx) {
     const float ay = fabsf(y);
     uint32_t mag = 0;
@@ -501,198 +459,287 @@ __global__ void __launch_bounds__(256) quant128_kernel(Q128Args a) {
 #pragma unroll
     for (int j = 0; j < H - 1; ++j) {
       const bool ge = ay >= tp[j];
-      mag += (uint32_t)ge;
+      mag = ge ? (uint32_t)(j + 1) : mag;
       c = ge ? cm[j + 1] : c;
     }
     idx = ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
     return __builtin_copysignf(c, y);
   };
+  // X granule P (0..1023) of tile tl, for slot P of the swizzled LDS tile (rows past
+  // the stream's end re-read its last token)
+  auto x_granule = [&](int64_t tl, int P) {
+    const int64_t st = tl / tps, tt0 = (tl % tps) * QT;
+    const int last = (int)min((int64_t)QT, a.n_tokens - tt0) - 1;
+    const int t = P >> 4, g = (P & 15) ^ (t & 15);
+    return *reinterpret_cast<const uint4 *>(a.x + st * a.xs + (tt0 + min(t, last)) * a.xt + g * 8);
+  };
 
-  if constexpr (KEYS) {
-    // acc[cb][tb][r] = y[coordinate 32w + 16cb + 4kq + r][token tb*16 + c16] * |x|
-    float rp[4] = {0.f, 0.f, 0.f, 0.f};
+  // work-groups loop over (stream, 64-token tile) pairs (tiles of stream s are
+  // s * tps .. s * tps + tps - 1); the next tile's X is loaded into registers
+  // while the current one is processed, and written to LDS once every wave is
+  // past its reads of the current X
+  int64_t tile = blockIdx.x;
+  if (tile >= total) return;
+  uint4 xr[XG];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int tok = tb * 16 + c16;
-      const float n = sqrtf(ss[tb]);
-      const float inv = n > 0.f ? 1.f / n : 0.f;
+  for (int i = 0; i < XG; ++i) xs[i * NT + tid] = x_granule(tile, i * NT + tid);
+  for (; tile < total; tile += gridDim.x) {
+    const int64_t s = tile / tps, t0 = (tile % tps) * QT;
+    const int nv = (int)min((int64_t)QT, a.n_tokens - t0);
+    const bool more = tile + gridDim.x < total;
+    __syncthreads();  // this tile's X (and the previous tile's LDS traffic is done)
+    if (more) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int c0 = 32 * wave + 16 * cb + 4 * kq;  // first of the lane's 4 coordinates
-        uint32_t bytes = 0, hi2[2], lo2[2];
-        float res[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float y = acc[cb][tb][r] * inv;
-          uint32_t idx;
-          res[r] = y - code(y, idx);
-          bytes |= idx << (8 * r);
-          rp[tb] = fmaf(res[r], res[r], rp[tb]);
-        }
-        split2(res[0], res[1], hi2[0], lo2[0]);
-        split2(res[2], res[3], hi2[1], lo2[1]);
-        // code bytes of 4 coordinates: granule c0 / 16, dword (c0 / 4) % 4
-        stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
-        // residual parts: granule c0 / 8 of 16, half (c0 / 4) % 2
-        const int gr = swz(tok, 16, c0 >> 3, 15) * 8 + ((c0 >> 2) & 1) * 4;
-        *reinterpret_cast<uint2 *>(&rt[0][gr]) = make_uint2(hi2[0], hi2[1]);
-        *reinterpret_cast<uint2 *>(&rt[1][gr]) = make_uint2(lo2[0], lo2[1]);
-      }
+      for (int i = 0; i < XG; ++i) xr[i] = x_granule(tile + gridDim.x, i * NT + tid);
     }
+
+    // ---- product 1: the wave's output coordinates for the 64 tokens (blocks tb)
+    f4v acc[RB][4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      rp[tb] += __shfl_xor(rp[tb], 16);
-      rp[tb] += __shfl_xor(rp[tb], 32);
-    }
-    if (kq == 0) {
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) rho2[wave][tb * 16 + c16] = rp[tb];
-    }
-    __syncthreads();
-    // ---- product 2: z[sketch row 32w + 16cb + 4kq + r][token] = S r, signs into bit 7 of the code bytes
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
-    const uint16_t *srow[2][2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) srow[cb][sp] = a.sk2 + (sp * QD + 32 * wave + 16 * cb + c16) * QD + kq * 8;
+      for (int tb = 0; tb < 4; ++tb) acc[rb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 rh[4], rl[4], sa[2][2];
+      bf16x8 xf[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const int g = swz(tb * 16 + c16, 16, ks * 4 + kq, 15) * 8;
-        rh[tb] = ld_bf8(&rt[0][g]);
-        rl[tb] = ld_bf8(&rt[1][g]);
+        const int t = tb * 16 + c16;
+        xf[tb] = __builtin_bit_cast(bf16x8, xs[t * 16 + ((ks * 4 + kq) ^ (t & 15))]);
+        ss[tb] = sumsq8(xf[tb], ss[tb]);
       }
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
-          sa[cb][sp] = ld_bf8(srow[cb][sp] + ks * 32);
+        for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+          for (int tb = 0; tb < 4; ++tb)
+            acc[rb][tb] = KEYS ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[rb][ks][sp], xf[tb], acc[rb][tb], 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[tb], pf[rb][ks][sp], acc[rb][tb], 0, 0, 0);
+    }
+    // token norms: lanes of one c16 hold the four k quarters
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      ss[tb] += __shfl_xor(ss[tb], 16);
+      ss[tb] += __shfl_xor(ss[tb], 32);
+    }
+    if (wave == 0 && kq == 0) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const float n = sqrtf(ss[tb]);
+        nrm[tb * 16 + c16] = n;
+        ninv[tb * 16 + c16] = n > 0.f ? 1.f / n : 0.f;
+      }
+    }
+
+    if constexpr (KEYS) {
+      // acc[rb][tb][r] = |x| y[coordinate 16 (wave RB + rb) + 4kq + r][token tb*16 + c16]
+      float rp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int tok = tb * 16 + c16;
+        const float n = sqrtf(ss[tb]);
+        const float inv = n > 0.f ? 1.f / n : 0.f;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int c0 = 16 * (wave * RB + rb) + 4 * kq;  // first of the lane's 4 coordinates
+          uint32_t bytes = 0, hi2[2], lo2[2];
+          float res[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float y = acc[rb][tb][r] * inv;
+            uint32_t idx;
+            res[r] = y - code(y, idx);
+            bytes |= idx << (8 * r);
+            rp[tb] = fmaf(res[r], res[r], rp[tb]);
+          }
+          split2(res[0], res[1], hi2[0], lo2[0]);
+          split2(res[2], res[3], hi2[1], lo2[1]);
+          // code bytes of 4 coordinates: granule c0 / 16, dword (c0 / 4) % 4
+          stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
+          // residual parts: granule c0 / 8 of 16, half (c0 / 4) % 2
+          const int gr = swz(tok, 16, c0 >> 3, 15) * 8 + ((c0 >> 2) & 1) * 4;
+          *reinterpret_cast<uint2 *>(&rt[0][gr]) = make_uint2(hi2[0], hi2[1]);
+          *reinterpret_cast<uint2 *>(&rt[1][gr]) = make_uint2(lo2[0], lo2[1]);
+        }
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        rp[tb] += __shfl_xor(rp[tb], 16);
+        rp[tb] += __shfl_xor(rp[tb], 32);
+      }
+      if (kq == 0) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) rho2[wave][tb * 16 + c16] = rp[tb];
+      }
+      __syncthreads();
+      // ---- product 2: z[sketch row][token] = S r, signs into bit 7 of the code bytes
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[rb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-          acc[cb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[cb][0], rh[tb], acc[cb][tb], 0, 0, 0);
-          acc[cb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[cb][0], rl[tb], acc[cb][tb], 0, 0, 0);
-          acc[cb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[cb][1], rh[tb], acc[cb][tb], 0, 0, 0);
+          const int g = swz(tb * 16 + c16, 16, ks * 4 + kq, 15) * 8;
+          const bf16x8 rh = ld_bf8(&rt[0][g]), rl = ld_bf8(&rt[1][g]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[rb][ks][0], rh, acc[rb][tb], 0, 0, 0);
+            acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[rb][ks][0], rl, acc[rb][tb], 0, 0, 0);
+            acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[rb][ks][1], rh, acc[rb][tb], 0, 0, 0);
+          }
         }
-    }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int tok = tb * 16 + c16;
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int c0 = 32 * wave + 16 * cb + 4 * kq;
-        uint32_t sg = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sg |= (acc[cb][tb][r] >= 0.f ? 0x80u : 0u) << (8 * r);
-        atomicOr(&stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)], sg);
       }
-    }
-    __syncthreads();
-    // ---- pack: thread (token, 32-coordinate group) -> B code planes + the sign plane
-    {
-      const int tok = tid >> 2, g = tid & 3;
-      if (tok < nv) {
-        const int64_t rec = s * a.os + a.oo + t0 + tok;
-        const float n = nrm[tok];
-        uint32_t w[B + 1];
-        if (n > 0.f) {
-          const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g, 7) * 4]);
-          const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g + 1, 7) * 4]);
-          const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-          for (int p = 0; p <= B; ++p) {
-            const int bit = p < B ? p : 7;
+      for (int rb = 0; rb < RB; ++rb) {
+        const int c0 = 16 * (wave * RB + rb) + 4 * kq;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const int tok = tb * 16 + c16;
+          uint32_t sg = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sg |= (acc[rb][tb][r] >= 0.f ? 0x80u : 0u) << (8 * r);
+          atomicOr(&stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)], sg);
+        }
+      }
+      __syncthreads();
+      if (more) {  // every wave is past its reads of this tile's X
+#pragma unroll
+        for (int i = 0; i < XG; ++i) xs[i * NT + tid] = xr[i];
+      }
+      // ---- pack: thread (token, 32-coordinate group) -> B code planes + the sign plane
+      if (tid < 4 * QT) {
+        const int tok = tid >> 2, g = tid & 3;
+        if (tok < nv) {
+          const int64_t rec = s * a.os + a.oo + t0 + tok;
+          const float n = nrm[tok];
+          uint32_t w[B + 1];
+          if (n > 0.f) {
+            const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g, 7) * 4]);
+            const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g + 1, 7) * 4]);
+            const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+            for (int p = 0; p <= B; ++p) {
+              const int bit = p < B ? p : 7;
+              uint32_t word = 0;
+#pragma unroll
+              for (int m = 0; m < 8; ++m) word |= gather4(d8[m], bit) << (4 * m);
+              w[p] = word;
+            }
+          } else {
+#pragma unroll
+            for (int p = 0; p <= B; ++p) w[p] = 0u;
+          }
+          uint32_t *dst = a.bits_out + (rec * QW + g) * (B + 1);
+          if constexpr (B == 3) {
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+          } else {
+#pragma unroll
+            for (int p = 0; p <= B; ++p) dst[p] = w[p];
+          }
+          if (g == 0) {
+            float r2 = 0.f;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) r2 += rho2[v][tok];
+            *reinterpret_cast<float2 *>(a.norms_out + 2 * rec) =
+                n > 0.f ? make_float2(n, sqrtf(r2)) : make_float2(0.f, 0.f);
+          }
+        }
+      }
+    } else {
+      __syncthreads();  // norms of every token
+      // acc[rb][tb][r] = |x| y[token tb*16 + 4kq + r][coordinate 16 (wave RB + rb) + c16]
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const float4 inv4 = *reinterpret_cast<const float4 *>(&ninv[tb * 16 + 4 * kq]);
+        const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int j = 16 * (wave * RB + rb) + c16;
+          uint32_t bytes = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            uint32_t idx;
+            (void)code(acc[rb][tb][r] * inv[r], idx);
+            bytes |= idx << (8 * r);
+          }
+          // tokens tb*16 + 4kq .. +3 of coordinate j: granule tb, dword kq
+          stage[swz(j, 4, tb, 3) * 4 + kq] = bytes;
+        }
+      }
+      __syncthreads();
+      if (more) {  // every wave is past its reads of this tile's X
+#pragma unroll
+        for (int i = 0; i < XG; ++i) xs[i * NT + tid] = xr[i];
+      }
+      // ---- pack: thread (coordinate, 32-token block) -> B token-major code planes
+      if (tid < 4 * QT) {
+        const uint64_t lmask = __builtin_amdgcn_ballot_w64(lane < nv && nrm[lane] > 0.f);  // live tokens
+        const int jj = tid >> 1, hb = tid & 1;
+        const int nb = nv - 32 * hb;  // valid tokens of this block
+        if (nb > 0) {
+          const uint32_t live = (uint32_t)(lmask >> (32 * hb));
+          const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb, 3) * 4]);
+          const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb + 1, 3) * 4]);
+          const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+          const int64_t blk = (s * a.os + a.oo + t0) / 32 + hb;
+          uint32_t *dst = a.bits_out + (blk * QD + jj) * B;
+#pragma unroll
+          for (int p = 0; p < B; ++p) {
             uint32_t word = 0;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) word |= gather4(d8[m], bit) << (4 * m);
-            w[p] = word;
+            for (int m = 0; m < 8; ++m) word |= gather4(d8[m], p) << (4 * m);
+            dst[p] = word & live;
           }
-        } else {
-#pragma unroll
-          for (int p = 0; p <= B; ++p) w[p] = 0u;
         }
-        uint32_t *dst = a.bits_out + (rec * QW + g) * (B + 1);
-        if constexpr (B == 3) {
-          *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-#pragma unroll
-          for (int p = 0; p <= B; ++p) dst[p] = w[p];
-        }
-        if (g == 0) {
-          const float rho = sqrtf((rho2[0][tok] + rho2[1][tok]) + (rho2[2][tok] + rho2[3][tok]));
-          *reinterpret_cast<float2 *>(a.norms_out + 2 * rec) = n > 0.f ? make_float2(n, rho) : make_float2(0.f, 0.f);
-        }
+        if (tid < nv) a.norms_out[s * a.os + a.oo + t0 + tid] = nrm[tid];
       }
     }
-  } else {
-    // acc[cb][tb][r] = y[token tb*16 + 4kq + r][coordinate 32w + 16cb + c16] * |x|
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const float4 inv4 = *reinterpret_cast<const float4 *>(&ninv[tb * 16 + 4 * kq]);
-      const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int j = 32 * wave + 16 * cb + c16;
-        uint32_t bytes = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t idx;
-          (void)code(acc[cb][tb][r] * inv[r], idx);
-          bytes |= idx << (8 * r);
-        }
-        // tokens tb*16 + 4kq .. +3 of coordinate j: granule tb, dword kq
-        stage[swz(j, 4, tb, 3) * 4 + kq] = bytes;
-      }
-    }
-    __syncthreads();
-    // ---- pack: thread (coordinate, 32-token block) -> B token-major code planes
-    const uint64_t lmask = __builtin_amdgcn_ballot_w64(lane < nv && nrm[lane] > 0.f);  // live tokens
-    {
-      const int j = tid >> 1, hb = tid & 1;
-      const int nb = nv - 32 * hb;  // valid tokens of this block
-      if (nb > 0) {
-        const uint32_t live = (uint32_t)(lmask >> (32 * hb));
-        const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(j, 4, 2 * hb, 3) * 4]);
-        const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(j, 4, 2 * hb + 1, 3) * 4]);
-        const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        const int64_t blk = (s * a.os + a.oo + t0) / 32 + hb;
-        uint32_t *dst = a.bits_out + (blk * QD + j) * B;
-#pragma unroll
-        for (int p = 0; p < B; ++p) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) word |= gather4(d8[m], p) << (4 * m);
-          dst[p] = word & live;
-        }
-      }
-      if (tid < nv) a.norms_out[s * a.os + a.oo + t0 + tid] = nrm[tid];
-    }
+    // the staging buffers are reused only after the next iteration's first barrier
   }
 }
 
+// Persistent launch: as many work-groups as fit on the device at once (registers
+// decide: keys one per compute unit, values two), at most one per tile.
+template <bool KEYS, int B>
+static hipError_t launch_quant128_b(const Q128Args &q, hipStream_t st) {
+  constexpr int NW = KEYS ? 8 : 4;
+  static int resident = 0;  // work-groups resident on the device
+  if (resident == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess ||
+        (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess ||
+        (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant128_kernel<KEYS, B, NW>, 64 * NW, 0)) !=
+            hipSuccess)
+      return e;
+    resident = std::max(1, cus * std::max(1, per_cu));
+  }
+  const int64_t tiles = ((q.n_tokens + QT - 1) / QT) * q.n_streams;
+  const unsigned nwg = (unsigned)std::min<int64_t>(tiles, resident);
+  hipLaunchKernelGGL((quant128_kernel<KEYS, B, NW>), dim3(nwg), dim3(64 * NW), 0, st, q);
+  return hipGetLastError();
+}
+
 template <bool KEYS>
-static hipError_t launch_quant128(const Q128Args &q, int bits, dim3 grid, hipStream_t st) {
+static hipError_t launch_quant128(const Q128Args &q, int bits, hipStream_t st) {
   switch (bits) {
-    case 1: hipLaunchKernelGGL((quant128_kernel<KEYS, 1>), grid, dim3(256), 0, st, q); break;
-    case 2: hipLaunchKernelGGL((quant128_kernel<KEYS, 2>), grid, dim3(256), 0, st, q); break;
-    case 3: hipLaunchKernelGGL((quant128_kernel<KEYS, 3>), grid, dim3(256), 0, st, q); break;
-    case 4: hipLaunchKernelGGL((quant128_kernel<KEYS, 4>), grid, dim3(256), 0, st, q); break;
+    case 1: return launch_quant128_b<KEYS, 1>(q, st);
+    case 2: return launch_quant128_b<KEYS, 2>(q, st);
+    case 3: return launch_quant128_b<KEYS, 3>(q, st);
+    case 4: return launch_quant128_b<KEYS, 4>(q, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 static hipError_t quant128(const tq_ctx *ctx, bool keys, const void *x, int64_t n_streams, int64_t n_tokens,
                            int64_t xs, int64_t xt, const tq_packed *out, int64_t os, int64_t oo, hipStream_t st) {
   Q128Args q = {};
   q.x = (const uint16_t *)x;
+  q.n_streams = n_streams;
   q.n_tokens = n_tokens;
   q.xs = xs;
   q.xt = xt;
@@ -703,8 +750,7 @@ static hipError_t quant128(const tq_ctx *ctx, bool keys, const void *x, int64_t 
   q.norms_out = out->norms;
   q.os = os;
   q.oo = oo;
-  dim3 grid((unsigned)((n_tokens + QT - 1) / QT), (unsigned)n_streams);
-  return keys ? launch_quant128<true>(q, out->mse_bits, grid, st) : launch_quant128<false>(q, out->mse_bits, grid, st);
+  return keys ? launch_quant128<true>(q, out->mse_bits, st) : launch_quant128<false>(q, out->mse_bits, st);
 }
 
 hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams, int64_t n_tokens,
