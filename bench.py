@@ -91,6 +91,31 @@ def ms(ev):
     return ev[0].elapsed_time(ev[1])
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_vector_turboquant_amd", "csrc", "tq_kernels.hip")
+
+
+def measured_traffic(tag):
+    """HBM bytes per launch of a kernel from its committed counter summary
+    (profiles/<tag>_traffic.md: FETCH_SIZE and WRITE_SIZE per dispatch, scaled
+    by the copy-kernel calibration), or None when there is none or the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{tag}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    with open(KERNEL_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample of the workload
 # ---------------------------------------------------------------------------
@@ -166,6 +191,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         cache.host_max_len = L
 
     dec_events = []
+    kev = []  # per timed call: events around its score/attention kernel
 
     def step(record):
         prefill()
@@ -179,7 +205,9 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
                     cache.append(ctx, KA[i], VA[i])
                 call = lambda: cache.decode(ctx, QS[i], out=out, ws=dws)  # noqa: E731
             if record:
-                dec_events.append((timer(call), n))
+                k_ev = kev[len(dec_events)]
+                tq.time_next_decode(*k_ev)
+                dec_events.append((timer(call), k_ev, n))
             else:
                 call()
 
@@ -189,18 +217,33 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     pre_ev = timer(prefill)
     torch.cuda.synchronize()
     prefill_ms = ms(pre_ev)
+    # timed region: K whole steps, events only around them (an event recorded
+    # between the launches of a call would stall the launches behind it)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    whole = timer(lambda: [step(True) for _ in range(args.steps)])
+    whole = timer(lambda: [step(False) for _ in range(args.steps)])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ms(whole) / args.steps
+    # launch timing, right after: one more identical step with events around
+    # each call and around each call's decode_kernel (created beforehand)
+    for _ in range(n_dec):
+        pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in pair:
+            e.record()
+        kev.append(pair)
+    torch.cuda.synchronize()
+    step(True)
+    torch.cuda.synchronize()
     keys_per_step = sum(B * H * (L + (i + 1 if NS > 0 else 0)) for i in range(n_dec))
     rec_bytes = (KEY_B4 if kbits == 3 else KEY_B3 if kbits == 2 else (d // 32) * (kbits + 1) * 4 + 8) + VAL_B3
-    dec_ms = np.array([ms(e) for e, _ in dec_events])
-    dec_bytes = np.array([B * H * n * rec_bytes for _, n in dec_events], dtype=np.float64)
+    dec_ms = np.array([ms(e) for e, _, _ in dec_events])
+    kern_ms = np.array([ms(k) for _, k, _ in dec_events])
+    dec_bytes = np.array([B * H * n * rec_bytes for _, _, n in dec_events], dtype=np.float64)
     avg_ms = float(dec_ms.mean())
-    achieved = float(dec_bytes.mean()) / (avg_ms / 1e3) / 1e9
+    kern_avg_ms = float(kern_ms.mean())
+    achieved = float(dec_bytes.mean()) / (kern_avg_ms / 1e3) / 1e9
+    traffic = measured_traffic(f"decode_kernel_{name}")
     vectors = 2 * B * H * L
     res = {
         "metric": METRIC, "value": keys_per_step / (ms_per_step / 1e3), "unit": "keys/s", "n_gpus": 1,
@@ -211,15 +254,19 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
                    "q_heads": Hq, "head_dim": d, "key_bits": kbits + 1, "value_bits": vbits,
                    "parallelism": "none (1 GPU)"},
         "quantize_vectors_per_s": vectors / (prefill_ms / 1e3), "prefill_ms": prefill_ms,
-        "decode_keys_per_s": float(B * H * sum(n for _, n in dec_events) / (dec_ms.sum() / 1e3)),
-        "decode_ms_per_launch": avg_ms, "wall_s_timed": wall,
+        "decode_keys_per_s": float(B * H * sum(n for _, _, n in dec_events) / (dec_ms.sum() / 1e3)),
+        "decode_call_ms": avg_ms, "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": ("tq_decode_step (decode_prep_kernel with the append + decode_kernel + "
-                                "decode_merge_kernel)" if fused else
-                                "tq_attention_decode (decode_prep_kernel + decode_kernel + decode_merge_kernel)"),
-                     "algorithmic_bytes_per_launch": float(dec_bytes.mean()), "avg_launch_ms": avg_ms,
-                     "bytes_per_kv_token": rec_bytes},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": f"decode_kernel<{kbits},{vbits}> (score/attention over the packed cache)",
+                     "algorithmic_bytes_per_launch": float(dec_bytes.mean()), "avg_launch_ms": kern_avg_ms,
+                     "bytes_per_kv_token": rec_bytes,
+                     "call": ("tq_decode_step: decode_prep_kernel (query prep + append), decode_kernel, "
+                              "decode_merge_kernel" if fused else
+                              "tq_attention_decode: decode_prep_kernel, decode_kernel, decode_merge_kernel"),
+                     "call_ms": avg_ms, "call_gbs": float(dec_bytes.mean()) / (avg_ms / 1e3) / 1e9,
+                     "timing": ("HIP events on the launch stream around every decode_kernel launch of one "
+                                "step run right after the timed steps, same inputs and launch configuration")},
     }
     if not args.no_cpu_baseline:
         enc_rate, dec_rate, streams, secs = oracle_stream_rates(d, min(L, 8192), Hq // H, kbits, vbits,

@@ -209,6 +209,17 @@ tq_status tq_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t 
                     float *d_scores, int32_t topk, int32_t *d_top_idx, float *d_top_val, void *d_ws,
                     size_t ws_bytes, void *stream);
 
+/* Kernel timing, a measurement aid. Arms the calling thread so that its next
+ * tq_attention_decode or tq_decode_step records start_event on its stream
+ * right before the score/attention kernel (after the query preparation) and
+ * stop_event right after it (before the merge of the chunk partials); that
+ * call then disarms the thread. The events are hipEvent_t handles created
+ * and owned by the caller (with timing enabled, for hipEventElapsedTime).
+ * Both NULL disarms. A call that fails before its launches leaves the thread
+ * disarmed.
+ * Errors: TQ_ERR_ARG (exactly one of the two is NULL). */
+tq_status tq_time_next_decode(void *start_event, void *stop_event);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char *tq_last_error(void);
 

@@ -83,6 +83,7 @@ _sig("tq_decode_step", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_
                                 _c_vp, _c_sz, _c_vp])
 _sig("tq_attention_decode", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp,
                                      _c_sz, _c_vp])
+_sig("tq_time_next_decode", _c_i32, [_c_vp, _c_vp])
 _sig("tq_scores_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64, _c_i32, _c_i32])
 _sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked), _c_vp, _c_i32, _c_vp, _c_vp,
                            _c_vp, _c_sz, _c_vp])
@@ -90,8 +91,8 @@ _sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked)
 EXPORTED_SYMBOLS = [
     "tq_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
     "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_append_token", "tq_attention_decode_ws_bytes",
-    "tq_attention_decode", "tq_decode_step_ws_bytes", "tq_decode_step", "tq_scores_ws_bytes", "tq_scores",
-    "tq_last_error",
+    "tq_attention_decode", "tq_decode_step_ws_bytes", "tq_decode_step", "tq_time_next_decode", "tq_scores_ws_bytes",
+    "tq_scores", "tq_last_error",
 ]
 
 
@@ -107,6 +108,23 @@ def _check(status: int):
 def lib():
     """The loaded ctypes library (for tests of the raw C ABI)."""
     return _lib
+
+
+def time_next_decode(start=None, stop=None):
+    """Arm this thread's next decode call (KVCache.decode / decode_step) to record
+    `start` and `stop` (torch.cuda.Event(enable_timing=True)) around its
+    score/attention kernel, on that call's stream; no arguments disarm. An event
+    that was never recorded has no device handle yet, so each one is recorded once
+    here first (on the current stream) to create it."""
+    if (start is None) != (stop is None):
+        raise ValueError("time_next_decode: pass both events or neither")
+    if start is None:
+        _check(_lib.tq_time_next_decode(None, None))
+        return
+    for ev in (start, stop):
+        if not ev.cuda_event:
+            ev.record()
+    _check(_lib.tq_time_next_decode(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)))
 
 
 # ---------------------------------------------------------------------------

@@ -216,6 +216,24 @@ extern "C" {
 
 const char *tq_last_error(void) { return g_last_error.c_str(); }
 
+// events armed by tq_time_next_decode on this thread (both NULL when disarmed)
+static thread_local hipEvent_t g_decode_ev[2] = {nullptr, nullptr};
+
+tq_status tq_time_next_decode(void *start_event, void *stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(TQ_ERR_ARG, "tq_time_next_decode: pass both events or neither");
+  g_decode_ev[0] = (hipEvent_t)start_event;
+  g_decode_ev[1] = (hipEvent_t)stop_event;
+  return TQ_OK;
+}
+
+// takes the armed events (if any) and disarms the thread
+static void take_decode_events(hipEvent_t ev[2]) {
+  ev[0] = g_decode_ev[0];
+  ev[1] = g_decode_ev[1];
+  g_decode_ev[0] = g_decode_ev[1] = nullptr;
+}
+
 tq_status tq_codebook_build(int32_t d, int32_t bits, tq_codebook *out) {
   if (!out) return fail(TQ_ERR_ARG, "tq_codebook_build: out is NULL");
   if (d < 3 || d > TQ_MAX_DIM) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook_build: d must be in [3, 4096]");
@@ -509,6 +527,8 @@ tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const
                               int32_t q_heads, float scale, float *d_out, void *d_ws, size_t ws_bytes,
                               void *stream) {
   const char *fn = "tq_attention_decode";
+  hipEvent_t ev[2];
+  take_decode_events(ev);
   if (!ctx) return fail(TQ_ERR_ARG, "tq_attention_decode: NULL ctx");
   tq_status s = check_cache(ctx, cache, fn);
   if (s != TQ_OK) return s;
@@ -522,7 +542,8 @@ tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const
   size_t need = tq_attention_decode_ws_bytes(ctx, cache, q_heads);
   if (!d_ws || ws_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_attention_decode: workspace smaller than tq_attention_decode_ws_bytes()");
   if ((s = check_device(ctx, fn)) != TQ_OK) return s;
-  hipError_t e = launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream);
+  hipError_t e = launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream,
+                               nullptr, nullptr, ev[0], ev[1]);
   return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 
@@ -537,6 +558,8 @@ tq_status tq_decode_step(const tq_ctx *ctx, tq_kv_cache *cache, const void *d_k,
                          tq_dtype dtype, int32_t q_heads, float scale, float *d_out, void *d_ws, size_t ws_bytes,
                          void *stream) {
   const char *fn = "tq_decode_step";
+  hipEvent_t ev[2];
+  take_decode_events(ev);
   if (!ctx) return fail(TQ_ERR_ARG, "tq_decode_step: NULL ctx");
   tq_status s = check_cache(ctx, cache, fn);
   if (s != TQ_OK) return s;
@@ -554,7 +577,7 @@ tq_status tq_decode_step(const tq_ctx *ctx, tq_kv_cache *cache, const void *d_k,
   tq_kv_cache after = *cache;
   after.host_max_len = cache->host_max_len + 1;
   hipError_t e = launch_decode(ctx, &after, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream,
-                               d_k, d_v);
+                               d_k, d_v, ev[0], ev[1]);
   if (e != hipSuccess) return hip_fail(e, fn);
   cache->host_max_len += 1;
   return TQ_OK;

@@ -62,10 +62,11 @@ hipError_t launch_append(const tq_ctx *ctx, const tq_kv_cache *cache, const void
 size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int *chunk_out,
                        int *nchunks_out);
 // With k_new / v_new non-NULL (fused step) the new token of every stream is
-// appended first and the sequence lengths advance by one.
+// appended first and the sequence lengths advance by one. Non-NULL ev0 / ev1 are
+// recorded on st right before / after the score/attention kernel.
 hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
                          float scale, float *out, void *ws, hipStream_t st, const void *k_new = nullptr,
-                         const void *v_new = nullptr);
+                         const void *v_new = nullptr, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores);
 hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_packed *keys,
                          float *scores, int32_t topk, int32_t *top_idx, float *top_val, void *ws, hipStream_t st);

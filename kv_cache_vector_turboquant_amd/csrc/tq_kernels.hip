@@ -1684,7 +1684,8 @@ static hipError_t launch_decode_kv(const DecodeArgs &a, dim3 grid, size_t shm, h
 }
 
 hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
-                         float scale, float *out, void *ws, hipStream_t st, const void *k_new, const void *v_new) {
+                         float scale, float *out, void *ws, hipStream_t st, const void *k_new, const void *v_new,
+                         hipEvent_t ev0, hipEvent_t ev1) {
   int chunk = 0, nchunks = 0;
   decode_ws_bytes(ctx, cache, q_heads, &chunk, &nchunks);
   DecodeArgs a = {};
@@ -1743,6 +1744,7 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   const size_t shm = (size_t)5 * chunk * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;
   dim3 grid(nchunks, streams);
   const int kb = cache->k.mse_bits, vb = cache->v.mse_bits;
+  if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
 #define TQ_DEC(K_, V_) else if (kb == K_ && vb == V_) e = launch_decode_kv<K_, V_>(a, grid, shm, st);
   if (false) {
   }
@@ -1753,6 +1755,7 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   else return hipErrorInvalidValue;
 #undef TQ_DEC
   if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(streams), dim3(1024), 0, st, a);
   return hipGetLastError();
 }

@@ -100,6 +100,14 @@ def test_hot_entry_points_reject_null_context():
     assert tq.last_error() != ""
 
 
+def test_time_next_decode_arguments():
+    lib = tq.lib()
+    assert lib.tq_time_next_decode(ctypes.c_void_p(16), None) == tq.TQ_ERR_ARG
+    assert "both events" in tq.last_error()
+    assert lib.tq_time_next_decode(None, ctypes.c_void_p(16)) == tq.TQ_ERR_ARG
+    assert lib.tq_time_next_decode(None, None) == tq.TQ_OK
+
+
 def test_ctx_create_argument_errors():
     lib = tq.lib()
     h = ctypes.c_void_p()

@@ -395,6 +395,39 @@ def test_decode_step_appends_and_attends(c128, dtype, hq):
         assert np.all(np.abs(gvn[s * cap + L0:s * cap + L0 + NA] - enc_v.norm) <= 2e-6 * enc_v.norm)
 
 
+def test_decode_kernel_timing_events(c128):
+    """tq_time_next_decode: the armed events bracket the score/attention kernel of
+    the next decode call only (inside that call's own time), and the output is the
+    same as an unarmed call's."""
+    ctx, _, _ = c128
+    B, H, hq, cap, L = 2, 2, 8, 2048, 2000
+    K = synth.outlier_kv(12, (1,), synth.TAG_SCALES_K, (B, H, L, 128), "bf16")
+    V = synth.outlier_kv(12, (2,), synth.TAG_SCALES_V, (B, H, L, 128), "bf16")
+    Q = synth.outlier_kv(12, (3,), synth.TAG_SCALES_K, (B, hq, 128), "bf16")
+    cache = tq.KVCache(B, H, cap, 128, 3, 3)
+    tq.quantize_kv(ctx, _dev(K, "bf16").view(B * H, L, 128), cache.k, out_stream_stride=cap,
+                   work=torch.empty(tq.quantize_ws_bytes(ctx, B * H, L, True), dtype=torch.uint8, device=DEV))
+    tq.quantize_kv(ctx, _dev(V, "bf16").view(B * H, L, 128), cache.v, out_stream_stride=cap)
+    cache.seq_len.fill_(L)
+    cache.host_max_len = L
+    q = _dev(Q, "bf16").contiguous()
+    ref = cache.decode(ctx, q).clone()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    tq.time_next_decode(ev[1], ev[2])
+    out = cache.decode(ctx, q)
+    ev[3].record()
+    torch.cuda.synchronize()
+    kern, call = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    assert 0.0 < kern <= call
+    assert torch.equal(out, ref)
+    # the thread is disarmed: the next call records nothing into these events
+    e_end = ev[2].elapsed_time(ev[3])
+    cache.decode(ctx, q)
+    torch.cuda.synchronize()
+    assert ev[2].elapsed_time(ev[3]) == e_end
+
+
 def test_append_rejects_full_cache(c128):
     ctx, _, _ = c128
     cache = tq.KVCache(1, 1, 32, 128, 3, 3)
