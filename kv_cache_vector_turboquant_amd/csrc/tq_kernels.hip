@@ -1400,7 +1400,8 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   __shared__ double wsum[4];
   __shared__ float hmax[4], hsum[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   const int c = blockIdx.x;
   const int sg = blockIdx.y;
   const int hg = sg % a.hgroups, stream = sg / a.hgroups;
@@ -1424,6 +1425,40 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const float *wk = a.tables->walsh[KB];
     const float *wv = a.tables->walsh[VB];
     const int ngrp = (n + 127) >> 7;
+    const int tn = lane & 15, G = lane >> 4;  // MFMA column (token), row group (head)
+    // records of the chunk: uniform bases and unsigned 32-bit byte offsets per lane
+    // (base + zero-extended offset addressing); lanes past the end re-read token
+    // n-1, so every store below stays unconditional and harmless
+    const char *kb0 = reinterpret_cast<const char *>(a.kbits + (srec + t0) * DW * (KB + 1));
+    const char *kn0 = reinterpret_cast<const char *>(a.knorm + 2 * (srec + t0));
+    const char *vn0 = reinterpret_cast<const char *>(a.vnorm + (srec + t0));
+    const uint32_t kgo = (uint32_t)(G * (KB + 1) * 4);  // the lane's 32-coordinate group in a record
+    struct KBuf {
+      uint32_t pl[KTPW][KB + 1];
+      float2 kn[KTPW];
+      float vn[KTPW];
+      uint32_t tc[KTPW];
+    };
+    auto kload = [&](int base, KBuf &bf) {
+#pragma unroll
+      for (int u = 0; u < KTPW; ++u) {
+        const uint32_t tc = (uint32_t)min((base + u) * 16 + tn, n - 1);
+        bf.tc[u] = tc;
+        const char *src = kb0 + (tc * (uint32_t)(DW * (KB + 1) * 4) + kgo);
+        if constexpr (KB == 3) {
+          const uint4 w4 = *reinterpret_cast<const uint4 *>(src);
+          bf.pl[u][0] = w4.x; bf.pl[u][1] = w4.y; bf.pl[u][2] = w4.z; bf.pl[u][3] = w4.w;
+        } else {
+#pragma unroll
+          for (int p = 0; p <= KB; ++p) bf.pl[u][p] = reinterpret_cast<const uint32_t *>(src)[p];
+        }
+        bf.kn[u] = *reinterpret_cast<const float2 *>(kn0 + (tc << 3));
+        bf.vn[u] = *reinterpret_cast<const float *>(vn0 + (tc << 2));
+      }
+    };
+    // the wave's first key tiles are requested before anything else
+    KBuf kb_a, kb_b;
+    kload(wave * KTPW, kb_a);
     // zero the value A fragments (rows of absent heads stay zero)
     for (int e = tid; e < ngrp * 2 * 64; e += 256) reinterpret_cast<uint4 *>(av)[e] = make_uint4(0, 0, 0, 0);
 
@@ -1439,7 +1474,6 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     };
     const i8v aqr0 = ldfrag(0, 0), aqr1 = ldfrag(0, 1), aqs0 = ldfrag(1, 0), aqs1 = ldfrag(1, 1);
     const int sc0 = 127 + 3 * (lane & 3), sc1 = sc0 + 12;  // e8m0 row scales 2^(3 digit)
-    const int tn = lane & 15, G = lane >> 4;  // MFMA column (token), row group (head)
     const float *qc = a.qconst + ((int64_t)sg * 4 + G) * QC;
     // accumulator start -sum_j Q_j per digit slot: the A fragments against an
     // all-ones mask (B scale 2^1 undoes the 1/2 of every product), exact
@@ -1462,36 +1496,11 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     for (int mi = 0; mi < KM; ++mi) wkr[mi] = wk[mi] * sr;
     float vmx = 0.f, lmx = -INFINITY;
     const int ntile = (n + 15) >> 4;
-    // records of the chunk: uniform bases, 32-bit lane offsets; lanes past the end
-    // re-read token n-1, so every store below stays unconditional and harmless
-    const uint32_t *kb0 = a.kbits + (srec + t0) * DW * (KB + 1);
-    const float2 *kn0 = reinterpret_cast<const float2 *>(a.knorm) + (srec + t0);
-    const float *vn0 = a.vnorm + (srec + t0);
-    struct KBuf {
-      uint32_t pl[KTPW][KB + 1];
-      float2 kn[KTPW];
-      float vn[KTPW];
-    };
-    auto kload = [&](int base, KBuf &bf) {
-#pragma unroll
-      for (int u = 0; u < KTPW; ++u) {
-        const int tc = min((base + u) * 16 + tn, n - 1);
-        const uint32_t *src = kb0 + (tc * DW + G) * (KB + 1);
-        if constexpr (KB == 3) {
-          const uint4 w4 = *reinterpret_cast<const uint4 *>(src);
-          bf.pl[u][0] = w4.x; bf.pl[u][1] = w4.y; bf.pl[u][2] = w4.z; bf.pl[u][3] = w4.w;
-        } else {
-#pragma unroll
-          for (int p = 0; p <= KB; ++p) bf.pl[u][p] = src[p];
-        }
-        bf.kn[u] = kn0[tc];
-        bf.vn[u] = vn0[tc];
-      }
-    };
     auto kcompute = [&](int base, const KBuf &cur) {
+      (void)base;
 #pragma unroll
       for (int u = 0; u < KTPW; ++u) {
-        const int tc = min((base + u) * 16 + tn, n - 1);
+        const int tc = (int)cur.tc[u];
         // all masked sums first (independent accumulators keep the MFMA pipe busy)
         f4v acc[KM + 1];
 #pragma unroll
@@ -1513,20 +1522,47 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         vmx = fmaxf(vmx, cur.vn[u]);
       }
     };
-    // two buffers in turn: the next round's loads are in flight during this one
+    // two buffers in turn: the next round's loads are in flight during this one.
+    // The loads are unconditional (tiles past the end re-read token n-1) and pinned
+    // ahead of the compute, so their latency overlaps a whole round.
     constexpr int KSTEP = 4 * KTPW;
-    KBuf kb_a, kb_b;
     int kbase = wave * KTPW;
-    if (kbase < ntile) kload(kbase, kb_a);
     while (kbase < ntile) {
-      if (kbase + KSTEP < ntile) kload(kbase + KSTEP, kb_b);
+      kload(kbase + KSTEP, kb_b);
+      __builtin_amdgcn_sched_barrier(0);
       kcompute(kbase, kb_a);
       kbase += KSTEP;
       if (kbase >= ntile) break;
-      if (kbase + KSTEP < ntile) kload(kbase + KSTEP, kb_a);
+      kload(kbase + KSTEP, kb_a);
+      __builtin_amdgcn_sched_barrier(0);
       kcompute(kbase, kb_b);
       kbase += KSTEP;
     }
+    // the first value blocks are requested before the softmax
+    const int vn = lane & 15, vg = lane >> 4;  // coordinate column, token block in the 128-token group
+    struct VBuf {
+      uint32_t pl[VGPI][2][VB];
+    };
+    // blocks of the chunk from a uniform base; a block past the end re-reads the
+    // last one (its tokens carry zero weights)
+    const char *vb0 = reinterpret_cast<const char *>(a.vbits + ((srec + t0) >> 5) * DD * VB);
+    const int lastblk = (n - 1) >> 5;
+    const uint32_t vco = (uint32_t)((wave * 32 + vn) * VB * 4);  // the lane's coordinate in a block
+    auto vload = [&](int grp0, VBuf &bf) {
+#pragma unroll
+      for (int gi = 0; gi < VGPI; ++gi) {
+        // this lane's 32-token block, chunk-relative
+        const uint32_t blk = (uint32_t)min((grp0 + gi) * 4 + vg, lastblk);
+        const char *src = vb0 + (blk * (uint32_t)(DD * VB * 4) + vco);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int p = 0; p < VB; ++p)
+            bf.pl[gi][nt][p] = reinterpret_cast<const uint32_t *>(src + nt * 16 * VB * 4)[p];
+      }
+    };
+    VBuf vb_a, vb_b;
+    vload(0, vb_a);
     // chunk maxima: |v| over all lanes; logits per head (lanes of one row group)
     for (int off = 32; off > 0; off >>= 1) vmx = fmaxf(vmx, __shfl_xor(vmx, off));
     for (int off = 8; off > 0; off >>= 1) lmx = fmaxf(lmx, __shfl_xor(lmx, off));
@@ -1580,26 +1616,6 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int mi = 0; mi < VM; ++mi) accv[nt][mi] = i4v{0, 0, 0, 0};
-    const int vn = lane & 15, vg = lane >> 4;  // coordinate column, token block in the 128-token group
-    struct VBuf {
-      uint32_t pl[VGPI][2][VB];
-    };
-    // blocks of the chunk from a uniform base; a block past the end re-reads the
-    // last one (its tokens carry zero weights)
-    const uint32_t *vb0 = a.vbits + ((srec + t0) >> 5) * DD * VB;
-    const int lastblk = (n - 1) >> 5;
-    auto vload = [&](int grp0, VBuf &bf) {
-#pragma unroll
-      for (int gi = 0; gi < VGPI; ++gi) {
-        const int blk = min((grp0 + gi) * 4 + vg, lastblk);  // this lane's 32-token block, chunk-relative
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const uint32_t *src = vb0 + (blk * DD + wave * 32 + nt * 16 + vn) * VB;
-#pragma unroll
-          for (int p = 0; p < VB; ++p) bf.pl[gi][nt][p] = src[p];
-        }
-      }
-    };
     auto vcompute = [&](int grp0, const VBuf &vcur) {
 #pragma unroll
       for (int gi = 0; gi < VGPI; ++gi) {
@@ -1619,15 +1635,17 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         }
       }
     };
-    VBuf vb_a, vb_b;
+    // two buffers in turn, unconditional loads pinned ahead of the compute (blocks
+    // past the end re-read the last one)
     int vbase = 0;
-    vload(0, vb_a);
     while (vbase < ngrp) {
-      if (vbase + VGPI < ngrp) vload(vbase + VGPI, vb_b);
+      vload(vbase + VGPI, vb_b);
+      __builtin_amdgcn_sched_barrier(0);
       vcompute(vbase, vb_a);
       vbase += VGPI;
       if (vbase >= ngrp) break;
-      if (vbase + VGPI < ngrp) vload(vbase + VGPI, vb_a);
+      vload(vbase + VGPI, vb_a);
+      __builtin_amdgcn_sched_barrier(0);
       vcompute(vbase, vb_b);
       vbase += VGPI;
     }
