@@ -1003,6 +1003,7 @@ struct DecodeArgs {
   int kbitsB, vbitsB;    // MSE bits of keys / values
   int kv_heads, capacity, q_heads, group, hgroups;
   int chunk, nchunks;
+  int streams_hg;        // streams x head groups (decode grid = nchunks x streams_hg)
   float scale_log2;      // softmax scale * log2(e)
   float qjl_scale;
   const DeviceTables *tables;
@@ -1295,6 +1296,20 @@ __device__ __forceinline__ i8v mask_fp4_01(uint32_t w) {
   return b;
 }
 
+// fp4 B operand of a Walsh mask from the B operands of the single planes: the AND
+// masks commute with XOR, so each dword is the XOR of the planes' dwords
+template <int NP>
+__device__ __forceinline__ i8v walsh_fp4(const i8v (&sm)[NP], int S) {
+  i8v r = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    if (S & (1 << p)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] ^= sm[p][q];
+    }
+  return r;
+}
+
 template <int NP>
 __device__ __forceinline__ uint32_t xor_planes(const uint32_t (&pl)[NP], int S) {
   uint32_t m = 0;
@@ -1397,13 +1412,27 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   float *vnl = lg + 4 * a.chunk;                                 // [chunk] value norms
   int8_t *av = reinterpret_cast<int8_t *>(smem + 5 * a.chunk * 4);  // [chunk/128][2][64][16] value A fragments
   __shared__ float red[4], lred[4][4];
-  __shared__ double wsum[4];
   __shared__ float hmax[4], hsum[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
-  const int c = blockIdx.x;
-  const int sg = blockIdx.y;
+  // 1-D grid of nchunks x (streams x head groups) work-groups. Work-groups are
+  // dealt to the 8 XCDs round-robin by id; when the stream count is a multiple
+  // of 8, id -> (stream, chunk) keeps every chunk of a stream on one XCD, so its
+  // query fragments are fetched into one L2 only
+  const int nsg = a.streams_hg;
+  int c, sg;
+  {
+    const int id = blockIdx.x;
+    if ((nsg & 7) == 0) {
+      const int k = id >> 3;
+      c = k % a.nchunks;
+      sg = (k / a.nchunks) * 8 + (id & 7);
+    } else {
+      c = id % a.nchunks;
+      sg = id / a.nchunks;
+    }
+  }
   const int hg = sg % a.hgroups, stream = sg / a.hgroups;
   const int b = stream / a.kv_heads;
   const int nh = min(4, a.group - hg * 4);
@@ -1503,9 +1532,12 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         const int tc = (int)cur.tc[u];
         // all masked sums first (independent accumulators keep the MFMA pipe busy)
         f4v acc[KM + 1];
+        i8v sm[KB];
+#pragma unroll
+        for (int p = 0; p < KB; ++p) sm[p] = mask_fp4_01(cur.pl[u][p]);
 #pragma unroll
         for (int mi = 0; mi <= KM; ++mi) {
-          const i8v bm = mask_fp4_01(mi < KM ? xor_planes(cur.pl[u], walsh_mask(KB, mi)) : cur.pl[u][KB]);
+          const i8v bm = mi < KM ? walsh_fp4(sm, walsh_mask(KB, mi)) : mask_fp4_01(cur.pl[u][KB]);
           acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr0 : aqs0, bm, mi < KM ? init_r : init_s,
                                                                      2, 4, 0, sc0, 0, 129);
           acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr1 : aqs1, bm, acc[mi], 2, 4, 0, sc1,
@@ -1582,30 +1614,33 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       //   qq = q&3, bb = (t>>3)&3, gg = (t>>5)&3: the lane-dependent part is fixed.
       const int lbase = (((lane >> 2) & 1) << 10) | (((lane >> 5) & 1) << 8) | (wave << 6) | ((lane & 3) << 2) |
                         ((lane >> 3) & 3);
+      // four independent iterations per round (tokens t = lane + 64 i); rounds run to
+      // a multiple of 256 tokens, inside the chunk's LDS: tokens past n get p = W = 0
+      // (their logits and norms in LDS are stale and never used)
       float l = 0.f;
-      int64_t wsi = 0;
-      for (int i = 0, t = lane; t < n; ++i, t += 64) {
-        const float p = __builtin_amdgcn_exp2f(lg[wave * a.chunk + t] - m);  // <= 1; tiny values round to W = 0
-        l += p;
-        const int W = (int)rintf(p * vnl[t] * wq);
-        wsi += W;
-        const uint32_t x = ((uint32_t)W + 0x80808080u) ^ 0x80808080u;  // four signed base-256 digits
-        int8_t *dst = av + lbase + ((i >> 1) << 11) + ((i & 1) << 9);
-        dst[0] = (int8_t)x;
-        dst[16] = (int8_t)(x >> 8);
-        dst[32] = (int8_t)(x >> 16);
-        dst[48] = (int8_t)(x >> 24);
+      const float *lgw = lg + wave * a.chunk + lane;
+      const float *vnw = vnl + lane;
+      const int nit = (n + 63) >> 6;
+      for (int i0 = 0; i0 < nit; i0 += 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + j;
+          const bool live = lane + 64 * i < n;
+          const float e = __builtin_amdgcn_exp2f(lgw[64 * i] - m);  // <= 1; tiny values round to W = 0
+          l += live ? e : 0.f;
+          const int W = live ? (int)rintf(e * vnw[64 * i] * wq) : 0;
+          const uint32_t x = ((uint32_t)W + 0x80808080u) ^ 0x80808080u;  // four signed base-256 digits
+          int8_t *dst = av + lbase + ((i0 >> 1) << 11) + ((j >> 1) << 11) + ((j & 1) << 9);
+          dst[0] = (int8_t)x;
+          dst[16] = (int8_t)(x >> 8);
+          dst[32] = (int8_t)(x >> 16);
+          dst[48] = (int8_t)(x >> 24);
+        }
       }
-      // effective weight of the lane's tokens: W * 2^q (W * -128 for q = 7); exact in double
-      double ws = (double)wsi * (qv == 7 ? -128.0 : (double)(1 << qv));
-      for (int off = 32; off > 0; off >>= 1) {
-        l += __shfl_xor(l, off);
-        ws += __shfl_xor(ws, off);
-      }
+      for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
       if (lane == 0) {
         hmax[wave] = m;
         hsum[wave] = l;
-        wsum[wave] = ws;
       }
     }
     __syncthreads();
@@ -1616,6 +1651,11 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int mi = 0; mi < VM; ++mi) accv[nt][mi] = i4v{0, 0, 0, 0};
+    // the same sums against an all-ones mask: per (head, digit) the effective weight
+    // total sum_t W_t 2^q (the -sum_t term of every Walsh mask), exact in int32
+    i4v accw = i4v{0, 0, 0, 0};
+    i4v ones_lo, ones_hi;
+    mask_bytes_pow2(0xFFFFFFFFu, ones_lo, ones_hi);
     auto vcompute = [&](int grp0, const VBuf &vcur) {
 #pragma unroll
       for (int gi = 0; gi < VGPI; ++gi) {
@@ -1623,6 +1663,8 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         if (grp >= ngrp) break;
         const i4v a0 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 0) * 64 + lane) * 16);
         const i4v a1 = *reinterpret_cast<const i4v *>(av + ((grp * 2 + 1) * 64 + lane) * 16);
+        accw = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, ones_lo, accw, 0, 0, 0);
+        accw = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, ones_hi, accw, 0, 0, 0);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
@@ -1651,7 +1693,8 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     }
     // flush: lane (coordinate vn, head vg) holds digits 0..3 of every mask sum
     if (vg < nh) {
-      const double W = wsum[vg];
+      const double W = (double)accw[0] + 256.0 * (double)accw[1] + 65536.0 * (double)accw[2] +
+                       16777216.0 * (double)accw[3];
       const double unit = (double)vmax / (double)WSCALE;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -1760,7 +1803,8 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t shm = (size_t)5 * chunk * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;
-  dim3 grid(nchunks, streams);
+  a.streams_hg = streams;
+  dim3 grid(nchunks * streams);
   const int kb = cache->k.mse_bits, vb = cache->v.mse_bits;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
 #define TQ_DEC(K_, V_) else if (kb == K_ && vb == V_) e = launch_decode_kv<K_, V_>(a, grid, shm, st);
