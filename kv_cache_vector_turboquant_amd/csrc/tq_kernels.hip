@@ -1004,6 +1004,7 @@ struct DecodeArgs {
   int kv_heads, capacity, q_heads, group, hgroups;
   int chunk, nchunks;
   int streams_hg;        // streams x head groups (decode grid = nchunks x streams_hg)
+  int batch;
   float scale_log2;      // softmax scale * log2(e)
   float qjl_scale;
   const DeviceTables *tables;
@@ -1041,62 +1042,134 @@ __device__ __forceinline__ float qload(const QT *q, int64_t i) {
   else return q[i];
 }
 
-// Fused step: encodes a stream's new token as record `pos` (called by the whole
-// 512-thread block). ykv holds Pi k and Pi v ([2][DD], LDS), red[0..3] the wave
-// sums of k^2 (0, 1) and v^2 (2, 3); zp is LDS scratch of 4 x DD floats.
-__device__ __forceinline__ void append_token(const DecodeArgs &a, int stream, int pos, int tid, float *ykv, float *zp,
-                                             float *red) {
-  const int64_t rec = (int64_t)stream * a.capacity + pos;
-  const float nk = sqrtf(red[0] + red[1]), nv = sqrtf(red[2] + red[3]);
+// Fused step, append blocks: a block (512 threads) encodes the new K/V tokens of
+// two KV streams, 2 * blk and 2 * blk + 1, each as record seq_len[b] of its
+// stream: the record tq_append_token writes (Pi k and Pi v from the Pi rows of
+// [Pi ; S Pi]^T, key code, residual, |r|, sign(S r), value code into the
+// token-major words). Every global read that does not depend on the tokens (Pi
+// rows, S rows, tables, the value words to update) is issued first, so the
+// block waits on memory once; the Pi and S rows in registers serve both streams.
+struct AppendLds {
+  float x[2][2][DD];     // [stream][k, v][coordinate]
+  float pp[4][4][DD];    // partial Pi x: [k quarter][stream * 2 + (k, v)][row]
+  float res[2][DD];      // key residuals
+  float zp[4][2][DD];    // partial S r: [coordinate quarter][stream][row]
+  float red[2][8];       // per stream: |k|^2, |v|^2 wave sums (0..3), |r|^2 wave sums (4, 5)
+  float tb[48];          // key boundaries, key centroids, value boundaries
+};
+
+__device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int tid, bool bf16in, AppendLds &L) {
+  const int nstreams = a.batch * a.kv_heads;
   const int kB = a.kbitsB, vB = a.vbitsB;
   const int lane = tid & 63, w = tid >> 6;
+  const int r = tid & (DD - 1), kq = tid >> 7;
+  // this thread's stream for the per-coordinate phases: (stream half, key or value)
+  const int hs = tid >> 8, kv = (tid >> 7) & 1;
+  int stream[2], pos[2];
+  bool on[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    stream[s2] = 2 * blk + s2;
+    const bool exists = stream[s2] < nstreams;
+    pos[s2] = exists ? a.seq_len[stream[s2] / a.kv_heads] : a.capacity;
+    on[s2] = exists && pos[s2] < a.capacity;  // a full stream gets nothing appended
+  }
+  // thread (row r, quarter kq): 32 entries of row r of Pi (transposed: coalesced
+  // over r) and of row r of S
+  float prow[32], srow[32];
+#pragma unroll
+  for (int u = 0; u < 32; ++u) prow[u] = a.rs_t[(kq * 32 + u) * 2 * DD + r];
+  {
+    const float4 *sr = reinterpret_cast<const float4 *>(a.sk + (int64_t)r * DD + 32 * kq);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 v = sr[u];
+      srow[4 * u] = v.x; srow[4 * u + 1] = v.y; srow[4 * u + 2] = v.z; srow[4 * u + 3] = v.w;
+    }
+  }
+  if (tid < 48) {
+    const int which = tid >> 4, i = tid & 15;
+    L.tb[tid] = which == 0 ? a.tables->boundary[kB][i] : which == 1 ? a.tables->centroid[kB][i] : a.tables->boundary[vB][i];
+  }
+  // value coordinate threads: the words this token's bits go into
+  const int64_t rec = (int64_t)stream[hs] * a.capacity + pos[hs];
+  const int bit_pos = (int)(rec & 31);
+  uint32_t vold[4] = {0u, 0u, 0u, 0u};
+  uint32_t *vdst = a.vbits_w + ((rec >> 5) * DD + r) * vB;
+  if (kv == 1 && on[hs] && bit_pos != 0) {
+    for (int p = 0; p < vB; ++p) vold[p] = vdst[p];
+  }
+  {
+    // thread (stream hs, k or v, coordinate r)
+    float x = 0.f;
+    if (on[hs]) {
+      const void *src = kv ? a.va : a.ka;
+      x = bf16in ? bf16f(reinterpret_cast<const uint16_t *>(src)[(int64_t)stream[hs] * DD + r])
+                 : reinterpret_cast<const float *>(src)[(int64_t)stream[hs] * DD + r];
+    }
+    L.x[hs][kv][r] = x;
+    float sq = x * x;
+    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    if (lane == 0) L.red[hs][w & 3] = sq;
+  }
+  __syncthreads();
+  {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int k = kq * 32 + u;
+      acc[0] = fmaf(prow[u], L.x[0][0][k], acc[0]);
+      acc[1] = fmaf(prow[u], L.x[0][1][k], acc[1]);
+      acc[2] = fmaf(prow[u], L.x[1][0][k], acc[2]);
+      acc[3] = fmaf(prow[u], L.x[1][1][k], acc[3]);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) L.pp[kq][v][r] = acc[v];
+  }
+  __syncthreads();
+  const float nk = sqrtf(L.red[hs][0] + L.red[hs][1]), nv = sqrtf(L.red[hs][2] + L.red[hs][3]);
+  const int vi = hs * 2 + kv;
+  const float yx = (L.pp[0][vi][r] + L.pp[1][vi][r]) + (L.pp[2][vi][r] + L.pp[3][vi][r]);
   int idx = 0;
-  if (tid < DD) {
-    // key coordinate j: code, residual (kept in ykv row 0), |r|^2
+  if (kv == 0) {
+    // key coordinate r: code (threshold count), residual, |r|^2
     const bool live = nk > 0.f;
-    const float y = live ? ykv[tid] / nk : 0.f;
-    for (int i = 0; i < (1 << kB) - 1; ++i) idx += (y >= a.tables->boundary[kB][i]) ? 1 : 0;
+    const float y = live ? yx / nk : 0.f;
+    for (int i = 0; i < (1 << kB) - 1; ++i) idx += (y >= L.tb[i]) ? 1 : 0;
     if (!live) idx = 0;
-    const float r = live ? y - a.tables->centroid[kB][idx] : 0.f;
-    ykv[tid] = r;
-    float r2 = r * r;
+    const float res = live ? y - L.tb[16 + idx] : 0.f;
+    L.res[hs][r] = res;
+    float r2 = res * res;
     for (int off = 32; off > 0; off >>= 1) r2 += __shfl_xor(r2, off);
-    if (lane == 0) red[4 + w] = r2;
-  } else if (tid < 2 * DD) {
-    // value coordinate j: code bits into the token-major words of its 32-token block
-    const int j = tid - DD;
+    if (lane == 0) L.red[hs][4 + (w & 1)] = r2;
+  } else if (on[hs]) {
+    // value coordinate r: code bits into the token-major words of its 32-token block
     const bool live = nv > 0.f;
-    const float y = live ? ykv[DD + j] / nv : 0.f;
+    const float y = live ? yx / nv : 0.f;
     int iv = 0;
-    for (int i = 0; i < (1 << vB) - 1; ++i) iv += (y >= a.tables->boundary[vB][i]) ? 1 : 0;
+    for (int i = 0; i < (1 << vB) - 1; ++i) iv += (y >= L.tb[32 + i]) ? 1 : 0;
     if (!live) iv = 0;
-    const int bit_pos = (int)(rec & 31);
-    uint32_t *dst = a.vbits_w + ((rec >> 5) * DD + j) * vB;
     for (int p = 0; p < vB; ++p) {
       const uint32_t bit = (uint32_t)((iv >> p) & 1) << bit_pos;
-      dst[p] = (bit_pos == 0) ? bit : ((dst[p] & ~(1u << bit_pos)) | bit);
+      vdst[p] = (bit_pos == 0) ? bit : ((vold[p] & ~(1u << bit_pos)) | bit);
     }
   }
   __syncthreads();
   {
-    // z = S r: thread (sketch row i, coordinate quarter)
-    const int i = tid & (DD - 1), qq = tid >> 7;
-    const float4 *srow = reinterpret_cast<const float4 *>(a.sk + (int64_t)i * DD + 32 * qq);
-    const float *rr = ykv + 32 * qq;
-    float z = 0.f;
+    // z = S r for both streams: thread (sketch row r, coordinate quarter kq)
+    float z0 = 0.f, z1 = 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float4 sv = srow[u];
-      z = fmaf(sv.x, rr[4 * u], z);
-      z = fmaf(sv.y, rr[4 * u + 1], z);
-      z = fmaf(sv.z, rr[4 * u + 2], z);
-      z = fmaf(sv.w, rr[4 * u + 3], z);
+    for (int u = 0; u < 32; ++u) {
+      z0 = fmaf(srow[u], L.res[0][kq * 32 + u], z0);
+      z1 = fmaf(srow[u], L.res[1][kq * 32 + u], z1);
     }
-    zp[qq * DD + i] = z;
+    L.zp[kq][0][r] = z0;
+    L.zp[kq][1][r] = z1;
   }
   __syncthreads();
-  if (tid < DD) {
-    const float z = (zp[tid] + zp[DD + tid]) + (zp[2 * DD + tid] + zp[3 * DD + tid]);
+  if (kv == 0 && on[hs]) {
+    // waves 0, 1 (stream 0) and 4, 5 (stream 1): key coordinate r
+    const float z = (L.zp[0][hs][r] + L.zp[1][hs][r]) + (L.zp[2][hs][r] + L.zp[3][hs][r]);
     const bool live = nk > 0.f;
     uint32_t words[5];
     for (int p = 0; p < kB; ++p) {
@@ -1106,40 +1179,57 @@ __device__ __forceinline__ void append_token(const DecodeArgs &a, int stream, in
     const uint64_t sbal = __builtin_amdgcn_ballot_w64(live && z >= 0.f);
     words[kB] = (lane < 32) ? (uint32_t)sbal : (uint32_t)(sbal >> 32);
     if ((lane & 31) == 0) {
-      uint32_t *dst = a.kbits_w + (rec * DW + w * 2 + (lane >> 5)) * (kB + 1);
+      uint32_t *dst = a.kbits_w + (rec * DW + (w & 1) * 2 + (lane >> 5)) * (kB + 1);
       for (int p = 0; p <= kB; ++p) dst[p] = words[p];
     }
-    if (tid == 0) {
+    if (r == 0) {
       a.knorm_w[2 * rec] = nk;
-      a.knorm_w[2 * rec + 1] = live ? sqrtf(red[4] + red[5]) : 0.f;
+      a.knorm_w[2 * rec + 1] = live ? sqrtf(L.red[hs][4] + L.red[hs][5]) : 0.f;
       a.vnorm_w[rec] = nv;
     }
   }
 }
 
-// One block per (stream, head group): q_rot = Pi q, q_s = S q_rot for up to 4
-// heads, fixed-point split and A-fragment layout. With APPEND (fused step) the
-// stream's new K/V token is encoded first, reusing the Pi rows of the block.
+// Query blocks: each handles two (stream, head group) units, 2 * blk and
+// 2 * blk + 1 (the [Pi ; S Pi] rows in registers serve both): q_rot = Pi q and
+// q_s = S q_rot for up to 4 heads per unit, fixed-point split and A-fragment
+// layout. With APPEND (fused step) the launch has ceil(batch x kv_heads / 2)
+// more blocks, which append the new tokens, and the query blocks publish each
+// sequence's length after the append.
+struct QueryLds {
+  float qk[DD][8];             // the 8 queries [coordinate][unit * 4 + head]
+  float part2[8][2 * DD];
+  float qv[2][8][DD];          // q_rot, q_s
+  float mx[2][8];              // max |q_rot|, max |q_s| per head
+  // fp6 codes, one per byte: [type][head][digit][32-coordinate group g][element e],
+  // element e = 8q + i <-> coordinate 32g + 4i + q (the fp4 mask order)
+  uint8_t cl[2][8][8][4][32];
+};
 
 template <typename QT, bool APPEND>
 __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
-  // the queries [coordinate][head]; fused step: the new k, v as "heads" 4 and 5
-  __shared__ __attribute__((aligned(16))) float qk[DD][APPEND ? 8 : 4];
-  __shared__ float ykv[APPEND ? 2 : 1][DD];  // Pi k, Pi v; then the key residual in row 0
-  __shared__ float zp[APPEND ? 4 : 1][DD];   // partial S r over four coordinate quarters
-  __shared__ float red[8];
-  __shared__ float part2[4][2 * DD];
-  __shared__ float qv[2][4][DD];  // q_rot, q_s
-  __shared__ float mx[2][4];      // max |q_rot|, max |q_s| per head
-  // fp6 codes, one per byte: [type][head][digit][32-coordinate group g][element e],
-  // element e = 8q + i <-> coordinate 32g + 4i + q (the fp4 mask order)
-  __shared__ __attribute__((aligned(16))) uint8_t cl[2][4][8][4][32];
   const int tid = threadIdx.x;
-  const int sg = blockIdx.x;  // stream * hgroups + hg
-  const int hg = sg % a.hgroups, stream = sg / a.hgroups;
-  const int b = stream / a.kv_heads, kvh = stream % a.kv_heads;
-  const int h0 = kvh * a.group + hg * 4;
-  const int nh = min(4, a.group - hg * 4);
+  const int nq = (a.streams_hg + 1) >> 1;  // query blocks
+  if constexpr (APPEND) {
+    if ((int)blockIdx.x >= nq) {
+      __shared__ AppendLds al;
+      append_pair(a, (int)blockIdx.x - nq, tid, sizeof(QT) == 2, al);
+      return;
+    }
+  }
+  __shared__ __attribute__((aligned(16))) QueryLds ql;
+  int sgu[2], nhu[2], bu[2], h0u[2];
+#pragma unroll
+  for (int u2 = 0; u2 < 2; ++u2) {
+    sgu[u2] = 2 * (int)blockIdx.x + u2;
+    const int hg = sgu[u2] % a.hgroups, stream = sgu[u2] / a.hgroups;
+    bu[u2] = stream / a.kv_heads;
+    h0u[u2] = (stream % a.kv_heads) * a.group + hg * 4;
+    nhu[u2] = sgu[u2] < a.streams_hg ? min(4, a.group - hg * 4) : 0;
+    // fused step: the sequence's length after the append, for the decode launch
+    if (APPEND && tid == 0 && nhu[u2] > 0 && stream % a.kv_heads == 0 && hg == 0)
+      a.wlen[bu[u2]] = min(a.seq_len[bu[u2]] + 1, a.capacity);
+  }
   // thread (r, k half) owns row r of [Pi ; S Pi] (r < 128: q_rot, else q_s) over
   // half of k: its 64 matrix entries (transposed matrix: reads coalesced over r)
   // are all requested before the queries are staged
@@ -1147,126 +1237,103 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
   float mrow[64];
 #pragma unroll
   for (int u = 0; u < 64; ++u) mrow[u] = a.rs_t[(kh * 64 + u) * 2 * DD + r];
-  const QT *q = reinterpret_cast<const QT *>(a.q) + ((int64_t)b * a.q_heads + h0) * DD;
-  {
-    const int hh = tid >> 7, k = tid & (DD - 1);
-    qk[k][hh] = hh < nh ? qload(q, (int64_t)hh * DD + k) : 0.f;
-  }
-  // fused step: stream's new token (block hg = 0 of the stream), position = current length
-  const bool app = APPEND && hg == 0;
-  int pos = 0;
-  if constexpr (APPEND) {
-    pos = a.seq_len[b];
-    if (app && tid < 2 * DD) {
-      const int which = tid >> 7, k = tid & (DD - 1);
-      const QT *src = reinterpret_cast<const QT *>(which ? a.va : a.ka) + (int64_t)stream * DD;
-      const float x = qload(src, k);
-      qk[k][4 + which] = x;
-      float sq = x * x;  // |k|^2 (waves 0, 1) and |v|^2 (waves 2, 3)
-      for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
-      if ((tid & 63) == 0) red[tid >> 6] = sq;
-    }
-    if (tid == 0 && kvh == 0 && hg == 0) a.wlen[b] = min(pos + 1, a.capacity);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = i * 512 + tid, hh = e >> 7, k = e & (DD - 1), u2 = hh >> 2;
+    const QT *q = reinterpret_cast<const QT *>(a.q) + ((int64_t)bu[u2] * a.q_heads + h0u[u2]) * DD;
+    ql.qk[k][hh] = (hh & 3) < nhu[u2] ? qload(q, (int64_t)(hh & 3) * DD + k) : 0.f;
   }
   __syncthreads();
-  // one 16-byte LDS broadcast gives the four query entries of a k
+  // two 16-byte LDS broadcasts give the eight query entries of a k
   {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    float ak = 0.f, av = 0.f;  // fused step: the rows against the new k and v (used for r < 128)
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 64; ++u) {
-      const float4 qq = *reinterpret_cast<const float4 *>(qk[kh * 64 + u]);
-      acc[0] = fmaf(mrow[u], qq.x, acc[0]);
-      acc[1] = fmaf(mrow[u], qq.y, acc[1]);
-      acc[2] = fmaf(mrow[u], qq.z, acc[2]);
-      acc[3] = fmaf(mrow[u], qq.w, acc[3]);
-      if constexpr (APPEND) {
-        const float2 x = *reinterpret_cast<const float2 *>(&qk[kh * 64 + u][4]);
-        ak = fmaf(mrow[u], x.x, ak);
-        av = fmaf(mrow[u], x.y, av);
-      }
+      const float4 q0 = *reinterpret_cast<const float4 *>(&ql.qk[kh * 64 + u][0]);
+      const float4 q1 = *reinterpret_cast<const float4 *>(&ql.qk[kh * 64 + u][4]);
+      acc[0] = fmaf(mrow[u], q0.x, acc[0]);
+      acc[1] = fmaf(mrow[u], q0.y, acc[1]);
+      acc[2] = fmaf(mrow[u], q0.z, acc[2]);
+      acc[3] = fmaf(mrow[u], q0.w, acc[3]);
+      acc[4] = fmaf(mrow[u], q1.x, acc[4]);
+      acc[5] = fmaf(mrow[u], q1.y, acc[5]);
+      acc[6] = fmaf(mrow[u], q1.z, acc[6]);
+      acc[7] = fmaf(mrow[u], q1.w, acc[7]);
     }
     if (kh == 1) {
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) part2[hh][r] = acc[hh];
-      if (APPEND && app && r < DD) {
-        ykv[0][r] = ak;
-        ykv[1][r] = av;
-      }
+      for (int hh = 0; hh < 8; ++hh) ql.part2[hh][r] = acc[hh];
     }
     __syncthreads();
     if (kh == 0) {
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) qv[r >> 7][hh][r & (DD - 1)] = acc[hh] + part2[hh][r];
-      if (APPEND && app && r < DD) {
-        ykv[0][r] += ak;
-        ykv[1][r] += av;
-      }
-    }
-  }
-  __syncthreads();
-  if constexpr (APPEND) {
-    if (app && pos < a.capacity) append_token(a, stream, pos, tid, &ykv[0][0], &zp[0][0], red);
-  }
-  if (tid < 256) {
-    // max |.| per (type, head): wave w reduces (type, head pair) rows
-    const int lane = tid & 63, w = tid >> 6, T = w >> 1;
-    for (int hh = (w & 1) * 2; hh < (w & 1) * 2 + 2; ++hh) {
-      const float *row = qv[T][hh];
-      float m = fmaxf(fabsf(row[lane]), fabsf(row[lane + 64]));
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      if (lane == 0) mx[T][hh] = m;
+      for (int hh = 0; hh < 8; ++hh) ql.qv[r >> 7][hh][r & (DD - 1)] = acc[hh] + ql.part2[hh][r];
     }
   }
   __syncthreads();
   {
-    // thread (head, coordinate): balanced base-8 digits in [-4, 3] of both query
-    // types, stored as e2m3 codes of digit * (1, 1/2, 1/4, 1/4)[j % 4]
-    const int hh = tid >> 7, j = tid & (DD - 1);
-    const int g = j >> 5, e = 8 * (j & 3) + ((j >> 2) & 7), fi = min(j & 3, 2);
+    // max |.| per (type, head): wave w reduces rows (T = w >> 2, heads 2 (w & 3), +1)
+    const int lane = tid & 63, w = tid >> 6, T = w >> 2;
+    for (int hh = (w & 3) * 2; hh < (w & 3) * 2 + 2; ++hh) {
+      const float *row = ql.qv[T][hh];
+      float m = fmaxf(fabsf(row[lane]), fabsf(row[lane + 64]));
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if (lane == 0) ql.mx[T][hh] = m;
+    }
+  }
+  __syncthreads();
+  // thread (head, coordinate): balanced base-8 digits in [-4, 3] of both query
+  // types, stored as e2m3 codes of digit * (1, 1/2, 1/4, 1/4)[j % 4]
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = i * 512 + tid, hh = e >> 7, j = e & (DD - 1);
+    const int g = j >> 5, el = 8 * (j & 3) + ((j >> 2) & 7), fi = min(j & 3, 2);
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      const float m = mx[T][hh];
-      int qi = m > 0.f ? (int)rintf(qv[T][hh][j] * (QMAX / m)) : 0;
+      const float m = ql.mx[T][hh];
+      int qi = m > 0.f ? (int)rintf(ql.qv[T][hh][j] * (QMAX / m)) : 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int dv = ((qi + 4) & 7) - 4;
         qi = (qi - dv) >> 3;
-        cl[T][hh][k][g][e] = (uint8_t)(fp6_mag((uint32_t)(dv < 0 ? -dv : dv), fi) | (dv < 0 ? 0x20u : 0u));
+        ql.cl[T][hh][k][g][el] = (uint8_t)(fp6_mag((uint32_t)(dv < 0 ? -dv : dv), fi) | (dv < 0 ? 0x20u : 0u));
       }
     }
   }
-  if (tid < 8) {
-    const int T = tid >> 2, hh = tid & 3;
-    const float m = mx[T][hh];
-    a.qconst[((int64_t)sg * 4 + hh) * QC + T] = m > 0.f ? m / QMAX : 0.f;
+  if (tid < 16) {
+    const int T = tid >> 3, hh = tid & 7, u2 = hh >> 2;
+    const float m = ql.mx[T][hh];
+    if (nhu[u2] > 0) a.qconst[((int64_t)sgu[u2] * 4 + (hh & 3)) * QC + T] = m > 0.f ? m / QMAX : 0.f;
   }
   __syncthreads();
-  if (tid < 256) {
-    // fragment (T, instr, lane): the 32 codes of row (4*hh + slot), digit 4*instr + slot,
-    // packed at 6 bits each (element e at bit 6e): every 4 codes make 24 bits
-    const int T = tid >> 7, ins = (tid >> 6) & 1, L = tid & 63;
-    const int g = L >> 4, row = L & 15, hh = row >> 2, dig = 4 * ins + (row & 3);
-    const uint4 *src = reinterpret_cast<const uint4 *>(&cl[T][hh][dig][g][0]);
-    const uint4 c0 = src[0], c1 = src[1];
-    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    uint32_t t24[8];
+  {
+    // fragment (unit, T, instr, lane): the 32 codes of row (4*hh + slot), digit
+    // 4*instr + slot, packed at 6 bits each (element e at bit 6e): every 4 codes
+    // make 24 bits
+    const int u2 = tid >> 8, T = (tid >> 7) & 1, ins = (tid >> 6) & 1, Ln = tid & 63;
+    const int g = Ln >> 4, row = Ln & 15, hh = u2 * 4 + (row >> 2), dig = 4 * ins + (row & 3);
+    if (nhu[u2] > 0) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(&ql.cl[T][hh][dig][g][0]);
+      const uint4 c0 = src[0], c1 = src[1];
+      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      uint32_t t24[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const uint32_t w = cw[m];
-      t24[m] = (w & 0x3Fu) | ((w >> 2) & 0xFC0u) | ((w >> 4) & 0x3F000u) | ((w >> 6) & 0xFC0000u);
-    }
-    uint32_t dw[6];
+      for (int m = 0; m < 8; ++m) {
+        const uint32_t w = cw[m];
+        t24[m] = (w & 0x3Fu) | ((w >> 2) & 0xFC0u) | ((w >> 4) & 0x3F000u) | ((w >> 6) & 0xFC0000u);
+      }
+      uint32_t dw[6];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {  // 4 chunks of 24 bits -> 3 dwords
-      const uint32_t *t = t24 + 4 * h;
-      dw[3 * h + 0] = t[0] | (t[1] << 24);
-      dw[3 * h + 1] = (t[1] >> 8) | (t[2] << 16);
-      dw[3 * h + 2] = (t[2] >> 16) | (t[3] << 8);
+      for (int h = 0; h < 2; ++h) {  // 4 chunks of 24 bits -> 3 dwords
+        const uint32_t *t = t24 + 4 * h;
+        dw[3 * h + 0] = t[0] | (t[1] << 24);
+        dw[3 * h + 1] = (t[1] >> 8) | (t[2] << 16);
+        dw[3 * h + 2] = (t[2] >> 16) | (t[3] << 8);
+      }
+      uint4 *dst = reinterpret_cast<uint4 *>(a.qfrag + ((((int64_t)sgu[u2] * 2 + T) * 2 + ins) * 64 + Ln) * 8);
+      dst[0] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+      dst[1] = make_uint4(dw[4], dw[5], 0u, 0u);
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(a.qfrag + ((((int64_t)sg * 2 + T) * 2 + ins) * 64 + L) * 8);
-    dst[0] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
-    dst[1] = make_uint4(dw[4], dw[5], 0u, 0u);
   }
 }
 
@@ -1794,16 +1861,20 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
     a.wlen = (int32_t *)p;
     a.len_inc = cache->d_seq_len;
   }
+  a.streams_hg = streams;
+  // two (stream, head group) units per query block; fused step: one more block
+  // per two KV streams appends their new tokens
+  a.batch = cache->batch;
+  const dim3 pgrid((streams + 1) / 2 + (step ? (cache->batch * cache->kv_heads + 1) / 2 : 0));
   if (is_bf16)
-    hipLaunchKernelGGL((step ? decode_prep_kernel<uint16_t, true> : decode_prep_kernel<uint16_t, false>), dim3(streams),
+    hipLaunchKernelGGL((step ? decode_prep_kernel<uint16_t, true> : decode_prep_kernel<uint16_t, false>), pgrid,
                        dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((step ? decode_prep_kernel<float, true> : decode_prep_kernel<float, false>), dim3(streams),
+    hipLaunchKernelGGL((step ? decode_prep_kernel<float, true> : decode_prep_kernel<float, false>), pgrid,
                        dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t shm = (size_t)5 * chunk * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;
-  a.streams_hg = streams;
   dim3 grid(nchunks * streams);
   const int kb = cache->k.mse_bits, vb = cache->v.mse_bits;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
