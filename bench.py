@@ -94,6 +94,27 @@ def ms(ev):
 KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_vector_turboquant_amd", "csrc", "tq_kernels.hip")
 
 
+def read_ceiling(torch, tq, mib=2048, grid=8192, reps=10):
+    """Practical HBM read ceiling on this GPU, measured live: the library's
+    read-bandwidth probe streaming `mib` MiB (GB/s, best grid of a small sweep)."""
+    src = torch.empty(mib * 1024 * 1024, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    best = 0.0
+    for g in (4096, grid, 16384):
+        sink = torch.empty(g * 256, dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            tq.read_probe(src, g, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            tq.read_probe(src, g, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, src.numel() / (e0.elapsed_time(e1) / reps / 1e3) / 1e9)
+    del src
+    return best
+
+
 def measured_traffic(tag):
     """HBM bytes per launch of a kernel from its committed counter summary
     (profiles/<tag>_traffic.md: FETCH_SIZE and WRITE_SIZE per dispatch, scaled
@@ -244,6 +265,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     kern_avg_ms = float(kern_ms.mean())
     achieved = float(dec_bytes.mean()) / (kern_avg_ms / 1e3) / 1e9
     traffic = measured_traffic(f"decode_kernel_{name}")
+    ceiling = read_ceiling(torch, tq)
     vectors = 2 * B * H * L
     res = {
         "metric": METRIC, "value": keys_per_step / (ms_per_step / 1e3), "unit": "keys/s", "n_gpus": 1,
@@ -266,7 +288,10 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
                               "tq_attention_decode: decode_prep_kernel, decode_kernel, decode_merge_kernel"),
                      "call_ms": avg_ms, "call_gbs": float(dec_bytes.mean()) / (avg_ms / 1e3) / 1e9,
                      "timing": ("HIP events on the launch stream around every decode_kernel launch of one "
-                                "step run right after the timed steps, same inputs and launch configuration")},
+                                "step run right after the timed steps, same inputs and launch configuration"),
+                     "read_ceiling_gbs": ceiling, "frac_of_read_ceiling": achieved / ceiling,
+                     "read_ceiling": ("tq_read_probe: best of grids 4096/8192/16384 x 256 threads streaming 2 GiB "
+                                      "with 16-byte loads, timed live in this run")},
     }
     if not args.no_cpu_baseline:
         enc_rate, dec_rate, streams, secs = oracle_stream_rates(d, min(L, 8192), Hq // H, kbits, vbits,

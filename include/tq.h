@@ -220,6 +220,15 @@ tq_status tq_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t 
  * Errors: TQ_ERR_ARG (exactly one of the two is NULL). */
 tq_status tq_time_next_decode(void *start_event, void *stop_event);
 
+/* Read-bandwidth probe, a measurement aid: the practical HBM read ceiling that
+ * the decode kernel's roofline is read against. `grid` work-groups of 256
+ * threads stream `bytes` bytes of d_src (device, 16-byte aligned, bytes a
+ * multiple of 16) with 16-byte loads, four in flight per thread, and write one
+ * XOR-fold word per thread to d_sink (device, grid * 256 uint32, so the loads
+ * are not optimized away). Asynchronous on `stream`.
+ * Errors: TQ_ERR_ARG (NULL, alignment, size, grid not in [1, 65536]), TQ_ERR_HIP. */
+tq_status tq_read_probe(const void *d_src, size_t bytes, int32_t grid, uint32_t *d_sink, void *stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char *tq_last_error(void);
 

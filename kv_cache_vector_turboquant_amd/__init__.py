@@ -84,6 +84,7 @@ _sig("tq_decode_step", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_
 _sig("tq_attention_decode", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp,
                                      _c_sz, _c_vp])
 _sig("tq_time_next_decode", _c_i32, [_c_vp, _c_vp])
+_sig("tq_read_probe", _c_i32, [_c_vp, _c_sz, _c_i32, _c_vp, _c_vp])
 _sig("tq_scores_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64, _c_i32, _c_i32])
 _sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked), _c_vp, _c_i32, _c_vp, _c_vp,
                            _c_vp, _c_sz, _c_vp])
@@ -91,8 +92,8 @@ _sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked)
 EXPORTED_SYMBOLS = [
     "tq_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
     "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_append_token", "tq_attention_decode_ws_bytes",
-    "tq_attention_decode", "tq_decode_step_ws_bytes", "tq_decode_step", "tq_time_next_decode", "tq_scores_ws_bytes",
-    "tq_scores", "tq_last_error",
+    "tq_attention_decode", "tq_decode_step_ws_bytes", "tq_decode_step", "tq_time_next_decode", "tq_read_probe",
+    "tq_scores_ws_bytes", "tq_scores", "tq_last_error",
 ]
 
 
@@ -108,6 +109,16 @@ def _check(status: int):
 def lib():
     """The loaded ctypes library (for tests of the raw C ABI)."""
     return _lib
+
+
+def read_probe(src, grid, sink):
+    """Stream all of `src` (a device tensor, 16-byte aligned, size a multiple of 16
+    bytes) with the read-bandwidth probe kernel on the current stream; `sink` is a
+    device int32/uint32 tensor of at least grid * 256 elements."""
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() < grid * 256 or sink.element_size() != 4:
+        raise ValueError("read_probe: sink needs grid * 256 four-byte elements")
+    _check(_lib.tq_read_probe(src.data_ptr(), nbytes, grid, sink.data_ptr(), _stream_ptr()))
 
 
 def time_next_decode(start=None, stop=None):

@@ -216,6 +216,15 @@ extern "C" {
 
 const char *tq_last_error(void) { return g_last_error.c_str(); }
 
+tq_status tq_read_probe(const void *d_src, size_t bytes, int32_t grid, uint32_t *d_sink, void *stream) {
+  if (!d_src || !d_sink) return fail(TQ_ERR_ARG, "tq_read_probe: NULL buffer");
+  if (((uintptr_t)d_src & 15) != 0 || (bytes & 15) != 0 || bytes == 0)
+    return fail(TQ_ERR_ARG, "tq_read_probe: source must be 16-byte aligned and a positive multiple of 16 bytes");
+  if (grid < 1 || grid > 65536) return fail(TQ_ERR_ARG, "tq_read_probe: grid must be in [1, 65536]");
+  hipError_t e = launch_read_probe(d_src, bytes, grid, d_sink, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "tq_read_probe");
+}
+
 // events armed by tq_time_next_decode on this thread (both NULL when disarmed)
 static thread_local hipEvent_t g_decode_ev[2] = {nullptr, nullptr};
 

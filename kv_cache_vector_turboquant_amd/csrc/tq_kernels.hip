@@ -1894,6 +1894,32 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
 }
 
 // ---------------------------------------------------------------------------
+// Read-bandwidth probe: each thread streams a grid-strided slice with 16-byte
+// loads, four in flight, and writes an XOR fold of what it read.
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) read_probe_kernel(const uint4 *__restrict__ p, int64_t n16, uint32_t *sink) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nt = (int64_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  int64_t i = tid;
+  for (; i + 3 * nt < n16; i += 4 * nt) {
+    const uint4 a = p[i], b = p[i + nt], c = p[i + 2 * nt], d = p[i + 3 * nt];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += nt) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink[tid] = acc;
+}
+
+hipError_t launch_read_probe(const void *src, size_t bytes, int grid, uint32_t *sink, hipStream_t st) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, st, reinterpret_cast<const uint4 *>(src),
+                     (int64_t)(bytes / 16), sink);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Append: one block of 128 threads (thread = coordinate) per (b, h) stream; a
 // second launch advances the sequence lengths once every stream has read them.
 // ---------------------------------------------------------------------------

@@ -108,6 +108,17 @@ def test_time_next_decode_arguments():
     assert lib.tq_time_next_decode(None, None) == tq.TQ_OK
 
 
+def test_read_probe_arguments():
+    lib = tq.lib()
+    sink = ctypes.c_void_p(256)
+    assert lib.tq_read_probe(None, 16, 1, sink, None) == tq.TQ_ERR_ARG
+    assert lib.tq_read_probe(ctypes.c_void_p(256), 15, 1, sink, None) == tq.TQ_ERR_ARG      # size
+    assert lib.tq_read_probe(ctypes.c_void_p(264), 16, 1, sink, None) == tq.TQ_ERR_ARG      # alignment
+    assert lib.tq_read_probe(ctypes.c_void_p(256), 16, 0, sink, None) == tq.TQ_ERR_ARG      # grid
+    assert lib.tq_read_probe(ctypes.c_void_p(256), 16, 65537, sink, None) == tq.TQ_ERR_ARG
+    assert "tq_read_probe" in tq.last_error()
+
+
 def test_ctx_create_argument_errors():
     lib = tq.lib()
     h = ctypes.c_void_p()

@@ -428,6 +428,19 @@ def test_decode_kernel_timing_events(c128):
     assert ev[2].elapsed_time(ev[3]) == e_end
 
 
+def test_read_probe_reads_everything():
+    """The read-bandwidth probe touches every 16-byte granule: the XOR of the
+    per-thread folds equals the XOR of all words of the buffer."""
+    g = 40
+    src = torch.randint(-2**31, 2**31 - 1, (1000 * 4 + 4 * 7,), dtype=torch.int32, device=DEV)
+    sink = torch.zeros(g * 256, dtype=torch.int32, device=DEV)
+    tq.read_probe(src, g, sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
+
+
 def test_append_rejects_full_cache(c128):
     ctx, _, _ = c128
     cache = tq.KVCache(1, 1, 32, 128, 3, 3)
