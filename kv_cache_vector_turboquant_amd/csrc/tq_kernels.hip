@@ -347,7 +347,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 // Codes come from |y| against the positive boundaries (the table is
 // antisymmetric and its middle boundary is 0): mag = #{t_j <= |y|}, idx =
 // L/2 + mag for y >= 0, L/2 - 1 - mag for y < 0 (only exact ties differ from
-// #{t_i <= y}). Code bytes (bit 7 = QJL sign for keys) are staged in LDS and a
+// #{t_i <= y}). Codes (7-bit fields, bit 6 = QJL sign for keys) are staged in LDS and a
 // last pass gathers them into the bit-plane words.
 // ---------------------------------------------------------------------------
 
@@ -394,9 +394,16 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
-// Bit p of each of the 4 bytes of w, gathered into bits 0..3 (byte k -> bit k).
+// Staged code words hold four 7-bit fields (field k at bit 7k: code in bits 0..3,
+// QJL sign of a key in bit 6). gather4 collects bit p of the four fields into bits
+// 0..3 (field k -> bit k) with one full-rate 24-bit multiply: the masked bits sit
+// at 0, 7, 14, 21 (below 2^24 after the shift), and the multiplier
+// 2^18 + 2^12 + 2^6 + 1 moves field k's bit to 18 + k while every cross term
+// lands on a distinct bit outside 18..21, so no carry reaches them.
+constexpr uint32_t FIELD_MASK = 0x00204081u;
+constexpr int QJL_FIELD_BIT = 6;
 __device__ __forceinline__ uint32_t gather4(uint32_t w, int p) {
-  return (((w >> p) & 0x01010101u) * 0x01020408u) >> 24;
+  return (__umul24((w >> p) & FIELD_MASK, 0x00041041u) >> 18) & 0xFu;
 }
 
 // LDS swizzle of 16-byte granules: row r of `gran` granules, granule g at g ^ (r & mask)
@@ -417,7 +424,8 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   constexpr int XG = QT * 16 / NT; // X granules per thread
   // X tile: token row t (64 rows of 16 granules of 8 bf16), granule g at t * 16 + (g ^ (t & 15))
   __shared__ __attribute__((aligned(16))) uint4 xs[QT * 16];
-  // code bytes (keys: bit 7 = QJL sign): keys [token][coordinate] (8 granules per token),
+  // codes, four 7-bit fields per dword (keys: bit 6 of a field = QJL sign): keys
+  // [token][coordinate] (8 granules per token),
   // values [coordinate][token] (4 granules per coordinate)
   __shared__ __attribute__((aligned(16))) uint32_t stage[QT * QD / 4];
   // keys: residual parts, [token][coordinate] bf16 (16 granules per token row)
@@ -527,9 +535,8 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
     if (wave == 0 && kq == 0) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const float n = sqrtf(ss[tb]);
-        nrm[tb * 16 + c16] = n;
-        ninv[tb * 16 + c16] = n > 0.f ? 1.f / n : 0.f;
+        nrm[tb * 16 + c16] = sqrtf(ss[tb]);
+        if constexpr (!KEYS) ninv[tb * 16 + c16] = ss[tb] > 0.f ? __builtin_amdgcn_rsqf(ss[tb]) : 0.f;
       }
     }
 
@@ -539,8 +546,9 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const int tok = tb * 16 + c16;
-        const float n = sqrtf(ss[tb]);
-        const float inv = n > 0.f ? 1.f / n : 0.f;
+        // 1/|x| by the hardware reciprocal square root (about 1 ulp: code decisions
+        // move only for coordinates far inside the boundary tolerance)
+        const float inv = ss[tb] > 0.f ? __builtin_amdgcn_rsqf(ss[tb]) : 0.f;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int c0 = 16 * (wave * RB + rb) + 4 * kq;  // first of the lane's 4 coordinates
@@ -551,7 +559,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
             const float y = acc[rb][tb][r] * inv;
             uint32_t idx;
             res[r] = y - code(y, idx);
-            bytes |= idx << (8 * r);
+            bytes |= idx << (7 * r);
             rp[tb] = fmaf(res[r], res[r], rp[tb]);
           }
           split2(res[0], res[1], hi2[0], lo2[0]);
@@ -601,7 +609,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
           const int tok = tb * 16 + c16;
           uint32_t sg = 0;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sg |= (acc[rb][tb][r] >= 0.f ? 0x80u : 0u) << (8 * r);
+          for (int r = 0; r < 4; ++r) sg |= (acc[rb][tb][r] >= 0.f ? (1u << QJL_FIELD_BIT) : 0u) << (7 * r);
           atomicOr(&stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)], sg);
         }
       }
@@ -623,7 +631,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
             const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
             for (int p = 0; p <= B; ++p) {
-              const int bit = p < B ? p : 7;
+              const int bit = p < B ? p : QJL_FIELD_BIT;
               uint32_t word = 0;
 #pragma unroll
               for (int m = 0; m < 8; ++m) word |= gather4(d8[m], bit) << (4 * m);
@@ -664,7 +672,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
           for (int r = 0; r < 4; ++r) {
             uint32_t idx;
             (void)code(acc[rb][tb][r] * inv[r], idx);
-            bytes |= idx << (8 * r);
+            bytes |= idx << (7 * r);
           }
           // tokens tb*16 + 4kq .. +3 of coordinate j: granule tb, dword kq
           stage[swz(j, 4, tb, 3) * 4 + kq] = bytes;
