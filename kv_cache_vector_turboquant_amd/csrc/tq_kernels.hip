@@ -1494,15 +1494,17 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   // 1-D grid of nchunks x (streams x head groups) work-groups. Work-groups are
   // dealt to the 8 XCDs round-robin by id; when the stream count is a multiple
   // of 8, id -> (stream, chunk) keeps every chunk of a stream on one XCD, so its
-  // query fragments are fetched into one L2 only
+  // query fragments are fetched into one L2 only. Chunks go out in chunk order
+  // (every stream's first chunk, then the second, ...), so the short last
+  // chunks are the last work-groups of the launch and fill its tail.
   const int nsg = a.streams_hg;
   int c, sg;
   {
     const int id = blockIdx.x;
     if ((nsg & 7) == 0) {
-      const int k = id >> 3;
-      c = k % a.nchunks;
-      sg = (k / a.nchunks) * 8 + (id & 7);
+      const int k = id >> 3, nsg8 = nsg >> 3;
+      c = k / nsg8;
+      sg = (k % nsg8) * 8 + (id & 7);
     } else {
       c = id % a.nchunks;
       sg = id / a.nchunks;
