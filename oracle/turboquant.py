@@ -219,7 +219,7 @@ class Encoded:
     z: np.ndarray | None     # (n, m) fp64 sketch of the residual (for sign distances)
 
 
-def encode(X: np.ndarray, Pi: np.ndarray, cb: Codebook, S: np.ndarray | None = None) -> Encoded:
+def encode(X: np.ndarray, Pi: np.ndarray, cb: Codebook | None, S: np.ndarray | None = None) -> Encoded:
     """Quantize rows of X (fp32 or bf16 values).
 
     Stage 1 [ebisuda, 第1段階]: n = ||x||, u = x / n, y = Pi u; each rotated
@@ -230,6 +230,9 @@ def encode(X: np.ndarray, Pi: np.ndarray, cb: Codebook, S: np.ndarray | None = N
     r = y - c[idx] in the rotated domain (reading), rho = ||r||, z = S r,
     sigma_i = [z_i >= 0] (reading: sign(0) = +1).
     A zero vector gives an all-zero record (reading).
+    Key variants: S omitted gives MSE-only keys (stage 1 alone); cb None (no
+    codebook bits) gives pure QJL keys: the residual is the whole rotated unit
+    vector, r = y, so rho = ||y|| = 1 up to rounding [hakusoku, QJL].
     """
     X = np.asarray(X, dtype=np.float64)
     Pi64 = np.asarray(Pi, dtype=np.float64)
@@ -238,11 +241,14 @@ def encode(X: np.ndarray, Pi: np.ndarray, cb: Codebook, S: np.ndarray | None = N
     U = np.zeros_like(X)
     U[nz] = X[nz] / n[nz, None]
     Y = U @ Pi64.T
-    idx = np.searchsorted(cb.boundaries.astype(np.float64), Y, side="right").astype(np.int64)
+    if cb is None:
+        idx = np.zeros(Y.shape, dtype=np.int64)
+    else:
+        idx = np.searchsorted(cb.boundaries.astype(np.float64), Y, side="right").astype(np.int64)
     idx[~nz] = 0
     sigma = rho = Z = None
     if S is not None:
-        R = Y - cb.centroids.astype(np.float64)[idx]
+        R = Y - cb.centroids.astype(np.float64)[idx] if cb is not None else Y.copy()
         R[~nz] = 0.0
         rho = np.sqrt(np.sum(R * R, axis=1))
         Z = R @ np.asarray(S, dtype=np.float64).T
@@ -271,25 +277,33 @@ def query_prep(Qv: np.ndarray, Pi: np.ndarray, S: np.ndarray):
     return q_rot, q_s
 
 
-def scores_from_parts(q_rot, q_s, idx, sigma, norm, rho, cb: Codebook, m: int):
+def scores_from_parts(q_rot, q_s, idx, sigma, norm, rho, cb: Codebook | None, m: int):
     """s = n (<q_rot, c[idx]> + sqrt(pi/2)/m * rho * <q_s, 2 sigma - 1>) for all
     (query, key) pairs: the stage-1 inner product plus the QJL correction
-    [ebisuda, 第2段階; hakusoku, QJL]. norm, rho are the stored fp32 values."""
-    C = cb.centroids.astype(np.float64)[idx]                   # (n, d)
-    pm = 2.0 * np.asarray(sigma, dtype=np.float64) - 1.0       # (n, m)
-    t1 = np.asarray(q_rot) @ C.T                               # (nq, n)
-    t2 = np.asarray(q_s) @ pm.T
+    [ebisuda, 第2段階; hakusoku, QJL]. norm, rho are the stored fp32 values.
+    MSE-only keys (sigma None) keep the first term, pure QJL keys (cb None) the
+    second."""
     nn = np.asarray(norm, dtype=np.float64)[None, :]
-    rr = np.asarray(rho, dtype=np.float64)[None, :]
-    return nn * (t1 + qjl_constant(m) * rr * t2)
+    out = np.zeros((np.asarray(q_rot).shape[0], nn.shape[1]))
+    if cb is not None:
+        C = cb.centroids.astype(np.float64)[idx]               # (n, d)
+        out += np.asarray(q_rot) @ C.T                         # (nq, n)
+    if sigma is not None:
+        pm = 2.0 * np.asarray(sigma, dtype=np.float64) - 1.0   # (n, m)
+        rr = np.asarray(rho, dtype=np.float64)[None, :]
+        out += qjl_constant(m) * rr * (np.asarray(q_s) @ pm.T)
+    return nn * out
 
 
-def scores(Qv, Pi, S, cb: Codebook, keys: dict):
+def scores(Qv, Pi, S, cb: Codebook | None, keys: dict, qjl: bool = True):
     """Scores of queries against a packed key array (see pack_keys)."""
     d = Pi.shape[0]
-    idx, sigma = unpack_keys(keys["bits"], d, cb.bits)
+    bits = cb.bits if cb is not None else 0
+    idx, sigma = unpack_keys(keys["bits"], d, bits, qjl)
     q_rot, q_s = query_prep(Qv, Pi, S)
-    return scores_from_parts(q_rot, q_s, idx, sigma, keys["norms"][:, 0], keys["norms"][:, 1], cb, S.shape[0])
+    norms = np.asarray(keys["norms"]).reshape(idx.shape[0], 1 + int(qjl))
+    rho = norms[:, 1] if qjl else None
+    return scores_from_parts(q_rot, q_s, idx, sigma, norms[:, 0], rho, cb, S.shape[0])
 
 
 def dequantize_keys(Pi, S, cb: Codebook, idx, sigma, norm, rho):
@@ -303,14 +317,15 @@ def dequantize_keys(Pi, S, cb: Codebook, idx, sigma, norm, rho):
     return np.asarray(norm, np.float64)[:, None] * ((C + corr) @ np.asarray(Pi, np.float64))
 
 
-def attention_decode(Qh, Pi, S, cbk: Codebook, cbv: Codebook, keys: dict, values: dict, seq_len: int, scale: float):
+def attention_decode(Qh, Pi, S, cbk: Codebook | None, cbv: Codebook, keys: dict, values: dict, seq_len: int,
+                     scale: float, qjl: bool = True):
     """One decode step for one (sequence, KV head): softmax(q K^T * scale) V for
     each query head that shares this KV head [gemilab, Attention機構], with the
     keys' scores from the estimator and V dequantized with its own codebook:
     v_hat_t = ||v_t|| Pi^T c_v[idx_t] (stage 1 only for values, reading).
     Qh: (g, d) queries. Returns (g, d) fp64 outputs."""
     d = Pi.shape[0]
-    s = scores(Qh, Pi, S, cbk, keys)[:, :seq_len]              # (g, L)
+    s = scores(Qh, Pi, S, cbk, keys, qjl)[:, :seq_len]         # (g, L)
     logits = s * scale
     mx = np.max(logits, axis=1, keepdims=True)
     p = np.exp(logits - mx)
@@ -338,49 +353,55 @@ def recall_at_k(found: np.ndarray, exact: np.ndarray) -> float:
 # ---------------------------------------------------------------------------
 # Packed record format (a format choice; the pages fix none)
 # ---------------------------------------------------------------------------
-# Keys, one record per vector (m == d), W = d/32 coordinate groups:
-#   bits  : uint32 [n][W][B+1]; for group w, word p < B holds bit p of idx_j
-#           at bit position (j - 32w) for j in [32w, 32w+32); word B holds
-#           sigma_i at bit position (i - 32w).
-#   norms : float32 [n][2] = (||x||, ||r||).
+# Keys, one record per vector (m == d), W = d/32 coordinate groups, Q = 1 with
+# the QJL stage (0 for MSE-only keys; B = 0 with Q = 1 for pure QJL keys):
+#   bits  : uint32 [n][W][B+Q]; for group w, word p < B holds bit p of idx_j
+#           at bit position (j - 32w) for j in [32w, 32w+32); word B (when Q)
+#           holds sigma_i at bit position (i - 32w).
+#   norms : float32 [n][1+Q] = (||x||) or (||x||, ||r||).
 # Values, token-major blocks of 32 tokens, W_t = ceil(n/32) blocks:
 #   bits  : uint32 [W_t][d][B]; word [t//32][j][p] holds bit p of idx[t][j]
 #           at bit position t % 32. Unused tail bits are 0.
 #   norms : float32 [n] = ||v||.
 
-def key_record_bytes(d: int, bits: int) -> int:
-    return (d // 32) * (bits + 1) * 4 + 8
+def key_record_bytes(d: int, bits: int, qjl: bool = True) -> int:
+    return (d // 32) * (bits + int(qjl)) * 4 + 4 * (1 + int(qjl))
 
 
 def value_record_bytes(d: int, bits: int) -> int:
     return d * bits // 8 + 4
 
 
-def pack_keys(enc: Encoded, bits: int) -> dict:
+def pack_keys(enc: Encoded, bits: int, qjl: bool = True) -> dict:
     idx, sig = enc.idx, enc.sigma
     n, d = idx.shape
-    assert d % 32 == 0 and sig.shape == (n, d)
+    assert d % 32 == 0 and (not qjl or sig.shape == (n, d))
     W = d // 32
-    out = np.zeros((n, W, bits + 1), dtype=np.uint64)
+    out = np.zeros((n, W, bits + int(qjl)), dtype=np.uint64)
     pos = (np.uint64(1) << np.arange(32, dtype=np.uint64))
     for w in range(W):
         blk = idx[:, 32 * w:32 * w + 32].astype(np.uint64)
         for p in range(bits):
             out[:, w, p] = np.sum(((blk >> np.uint64(p)) & np.uint64(1)) * pos, axis=1)
-        out[:, w, bits] = np.sum(sig[:, 32 * w:32 * w + 32].astype(np.uint64) * pos, axis=1)
-    norms = np.stack([enc.norm.astype(np.float32), enc.rho.astype(np.float32)], axis=1)
+        if qjl:
+            out[:, w, bits] = np.sum(sig[:, 32 * w:32 * w + 32].astype(np.uint64) * pos, axis=1)
+    if qjl:
+        norms = np.stack([enc.norm.astype(np.float32), enc.rho.astype(np.float32)], axis=1)
+    else:
+        norms = enc.norm.astype(np.float32)[:, None]
     return {"bits": out.astype(np.uint32), "norms": norms}
 
 
-def unpack_keys(words: np.ndarray, d: int, bits: int):
+def unpack_keys(words: np.ndarray, d: int, bits: int, qjl: bool = True):
+    """(idx, sigma); sigma is None for MSE-only keys."""
     n = words.shape[0]
-    w = words.reshape(n, d // 32, bits + 1).astype(np.uint64)
+    w = words.reshape(n, d // 32, bits + int(qjl)).astype(np.uint64)
     sh = np.arange(32, dtype=np.uint64)
     idx = np.zeros((n, d), dtype=np.int64)
     for p in range(bits):
         b = (w[:, :, p, None] >> sh) & np.uint64(1)
         idx |= (b.reshape(n, d).astype(np.int64) << p)
-    sig = ((w[:, :, bits, None] >> sh) & np.uint64(1)).reshape(n, d).astype(bool)
+    sig = ((w[:, :, bits, None] >> sh) & np.uint64(1)).reshape(n, d).astype(bool) if qjl else None
     return idx, sig
 
 

@@ -308,6 +308,67 @@ def test_qjl_variance_closed_form():
     assert abs(emp - var) < 3 * math.sqrt(2.0 / (vals.size - 1)) * var
 
 
+def test_mse_only_keys_bias_is_one_minus_total_distortion():
+    """MSE-only keys (stage 1 alone): over random rotations the score's mean is
+    (1 - d D) <q, x>, D the codebook's per-coordinate distortion. Closed form:
+    the centroid condition gives E[y_j c(y_j)] = E[c(y_j)^2], so
+    sum_j E[y_j c_j] = 1 - d D, and the part of Pi q orthogonal to y averages
+    out by symmetry. 1000 rotations, within 3 standard errors; the bias itself
+    is many standard errors away from 0 (the estimator is not unbiased)."""
+    d, bits = 64, 1
+    cb = T.codebook(d, bits)
+    x = synth.gaussian(3, (22,), (d,)).astype(np.float64)
+    q = x + 0.5 * synth.gaussian(3, (21,), (d,)).astype(np.float64)  # correlated: a large <q, x>
+    exact = float(q @ x)
+    vals = []
+    for seed in range(1000):
+        Pi = T.rotation_from_gaussian(synth.gaussian_matrix(seed, synth.TAG_ROTATION, d, d))
+        enc = T.encode(x[None, :], Pi, cb)
+        q_rot = Pi.astype(np.float64) @ q
+        vals.append(T.scores_from_parts(q_rot[None, :], None, enc.idx, None, enc.norm, None, cb, d)[0, 0])
+    vals = np.array(vals)
+    se = vals.std(ddof=1) / math.sqrt(vals.size)
+    want = (1.0 - d * cb.distortion) * exact
+    assert abs(vals.mean() - want) < 3 * se
+    assert abs(vals.mean() - exact) > 10 * se
+
+
+def test_pure_qjl_keys_unbiased():
+    """Pure QJL keys (no codebook bits, residual = the rotated unit vector): the
+    score is unbiased over the sketch, mean error within 3 standard errors, and
+    rho = ||y|| = 1 (to the fp32 rounding of Pi)."""
+    d = 64
+    q = synth.gaussian(4, (21,), (d,)).astype(np.float64)
+    x = synth.gaussian(4, (22,), (d,)).astype(np.float64)
+    Pi = T.rotation_from_gaussian(synth.gaussian_matrix(11, synth.TAG_ROTATION, d, d))
+    errs = []
+    for seed in range(1000):
+        S = T.sketch_from_gaussian(synth.gaussian_matrix(7000 + seed, synth.TAG_SKETCH, d, d))
+        enc = T.encode(x[None, :], Pi, None, S)
+        assert abs(enc.rho[0] - 1.0) < 1e-6 and not enc.idx.any()  # Pi is fp32: orthogonal to ~1e-7
+        q_rot, q_s = T.query_prep(q[None, :], Pi, S)
+        errs.append(T.scores_from_parts(q_rot, q_s, enc.idx, enc.sigma, enc.norm, enc.rho, None, d)[0, 0] - q @ x)
+    errs = np.array(errs)
+    assert abs(errs.mean()) < 3 * errs.std(ddof=1) / math.sqrt(errs.size)
+
+
+def test_key_variant_scores_split_the_full_score():
+    """The TurboQuant score is the MSE-only score of the same codes plus the QJL
+    term of the residual: scores of the three packed formats add up."""
+    d = 64
+    Pi, S = _ctx(d, seed=5)
+    cb = T.codebook(d, 2)
+    X = synth.gaussian(5, (1,), (40, d))
+    Qv = synth.gaussian(5, (2,), (3, d))
+    enc = T.encode(X, Pi, cb, S)
+    full = T.scores(Qv, Pi, S, cb, T.pack_keys(enc, 2))
+    mse = T.scores(Qv, Pi, S, cb, T.pack_keys(T.encode(X, Pi, cb), 2, qjl=False), qjl=False)
+    q_rot, q_s = T.query_prep(Qv, Pi, S)
+    corr = T.scores_from_parts(q_rot, q_s, enc.idx, enc.sigma, enc.norm.astype(np.float32),
+                               enc.rho.astype(np.float32), None, d)
+    assert np.max(np.abs(full - (mse + corr))) < 1e-9 * np.max(np.abs(full))
+
+
 def test_score_is_inner_product_with_dequantized_key():
     d = 128
     Pi, S = _ctx(d)
@@ -419,6 +480,13 @@ def test_record_bytes():
     assert (pk["bits"].nbytes + pk["norms"].nbytes) // 64 == 72
     pv = T.pack_values(enc, 3)
     assert (pv["bits"].nbytes + pv["norms"].nbytes) // 64 == 52
+    # key variants: MSE-only (codes and |k|) and pure QJL (signs and both norms)
+    assert T.key_record_bytes(128, 3, qjl=False) == 52
+    assert T.key_record_bytes(128, 0) == 24
+    pm = T.pack_keys(T.encode(synth.gaussian(0, (1,), (64, d)), Pi, T.codebook(d, 3)), 3, qjl=False)
+    assert (pm["bits"].nbytes + pm["norms"].nbytes) // 64 == 52
+    pq = T.pack_keys(T.encode(synth.gaussian(0, (1,), (64, d)), Pi, None, S), 0)
+    assert (pq["bits"].nbytes + pq["norms"].nbytes) // 64 == 24
 
 
 # --- packing format ---------------------------------------------------------------
@@ -443,6 +511,23 @@ def test_pack_keys_golden():
     assert words.tolist() == exp
     i2, s2 = T.unpack_keys(T.pack_keys(enc, 3)["bits"], d, 3)
     assert np.array_equal(i2, idx) and np.array_equal(s2, sig)
+
+
+def test_pack_key_variants_golden():
+    """MSE-only and pure QJL key records are the TurboQuant record with the sign
+    word, or the code words, left out (same golden words)."""
+    d = 32
+    idx = (np.arange(d) % 8)[None, :]
+    sig = (np.arange(d) % 3 == 0)[None, :]
+    exp = [int(w, 16) for w in _golden_words("packing_keys.txt")[0][1:]]
+    mse = T.pack_keys(T.Encoded(idx, None, np.ones(1), None, None, None), 3, qjl=False)
+    assert mse["bits"].reshape(-1).tolist() == exp[:3] and mse["norms"].shape == (1, 1)
+    qjl = T.pack_keys(T.Encoded(np.zeros_like(idx), sig, np.ones(1), np.ones(1), None, None), 0)
+    assert qjl["bits"].reshape(-1).tolist() == exp[3:] and qjl["norms"].shape == (1, 2)
+    i2, s2 = T.unpack_keys(mse["bits"], d, 3, qjl=False)
+    assert np.array_equal(i2, idx) and s2 is None
+    i3, s3 = T.unpack_keys(qjl["bits"], d, 0)
+    assert not i3.any() and np.array_equal(s3, sig)
 
 
 def test_pack_values_golden():
