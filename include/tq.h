@@ -28,22 +28,28 @@
  *  - The library runs on the device that is current when tq_ctx_create is
  *    called; later calls must be made with that device current.
  *  - Dimensions: d is a multiple of 32 in [32, 4096]; the sketch has m = d
- *    rows (the sizes the workloads fix); MSE bit widths are 1..4.
+ *    rows (the sizes the workloads fix); MSE bit widths are 1..4 (0 for pure
+ *    QJL keys).
  *
  * Packed formats (fixed by this library; the pages fix none)
- *  Keys (B MSE bits + 1 QJL bit per coordinate), one record per vector,
- *  W = d/32 coordinate groups:
- *    bits  uint32 [n][W][B+1]: for group w, word p < B holds bit p of the
- *          codebook index of coordinate 32w+k at bit k; word B holds the QJL
- *          sign bit of sketch row 32w+k at bit k (1 = non-negative).
- *    norms float32 [n][2] = (||k||, ||r||), r the rotated-domain residual.
+ *  Keys (B MSE bits + Q QJL bits per coordinate), one record per vector,
+ *  W = d/32 coordinate groups. Q = 1 is TurboQuant (stage 1 + the QJL
+ *  sketch of the residual); Q = 0 keeps stage 1 alone (MSE-only keys, a
+ *  biased inner product); B = 0 with Q = 1 keeps the sketch alone (pure QJL
+ *  keys: the residual is the whole rotated unit vector):
+ *    bits  uint32 [n][W][B+Q]: for group w, word p < B holds bit p of the
+ *          codebook index of coordinate 32w+k at bit k; word B (Q = 1) holds
+ *          the QJL sign bit of sketch row 32w+k at bit k (1 = non-negative).
+ *    norms float32 [n][1+Q] = (||k||) or (||k||, ||r||), r the rotated-domain
+ *          residual.
  *    A zero vector has an all-zero record.
  *  Values (B MSE bits per coordinate, no sketch), token-major 32-token
  *  blocks:
  *    bits  uint32 [n/32][d][B]: word [t/32][j][p] holds bit p of the index of
  *          token t, coordinate j, at bit t%32.
  *    norms float32 [n] = ||v||.
- *  Bytes per token at d = 128: keys 56 (b=3) / 72 (b=4); 3-bit values 52.
+ *  Bytes per token at d = 128: keys 56 (b=3) / 72 (b=4) / 52 (3-bit MSE-only)
+ *  / 24 (pure QJL); 3-bit values 52.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -120,8 +126,10 @@ typedef struct {
   uint32_t *bits;  /* d_: keys [n][W][B+1]; values [n/32][d][B]     */
   float *norms;    /* d_: keys [n][2]; values [n]                    */
   int64_t n;       /* record capacity; a multiple of 32 for values   */
-  int32_t mse_bits;/* B, 1..4                                        */
-  int32_t is_key;  /* 1 = key format (with QJL signs), 0 = values    */
+  int32_t mse_bits;/* B: 1..4 (keys with qjl = 1: 0..4)              */
+  int32_t is_key;  /* 1 = key format, 0 = values                     */
+  int32_t qjl;     /* keys: Q, 1 = QJL sign word and ||r||, 0 = none;
+                      values: 0                                       */
 } tq_packed;
 
 /* Quantize vectors ([ebisuda] 第1段階 and, for keys, 第2段階).

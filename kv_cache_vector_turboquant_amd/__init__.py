@@ -50,7 +50,8 @@ class CCodebook(ctypes.Structure):
 
 
 class CPacked(ctypes.Structure):
-    _fields_ = [("bits", _c_vp), ("norms", _c_vp), ("n", _c_i64), ("mse_bits", _c_i32), ("is_key", _c_i32)]
+    _fields_ = [("bits", _c_vp), ("norms", _c_vp), ("n", _c_i64), ("mse_bits", _c_i32), ("is_key", _c_i32),
+                ("qjl", _c_i32)]
 
 
 class CCache(ctypes.Structure):
@@ -248,21 +249,26 @@ class Context:
 class Packed:
     """Device arrays of packed key or value records (format in include/tq.h)."""
 
-    def __init__(self, n: int, d: int, bits: int, is_key: bool, device="cuda"):
+    def __init__(self, n: int, d: int, bits: int, is_key: bool, device="cuda", qjl: bool = True):
+        """Keys: bits = B MSE bits, qjl = the QJL sign word and |r| (False: MSE-only
+        keys; bits = 0 with qjl: pure QJL keys). Values: bits = B, qjl ignored."""
         torch = _torch()
         if not is_key and n % 32:
             raise ValueError("value capacity must be a multiple of 32")
         W = d // 32
+        self.qjl = bool(qjl) and is_key
         self.n, self.d, self.bits, self.is_key = n, d, bits, is_key
         if is_key:
-            self.words = torch.zeros((n, W, bits + 1), dtype=torch.int32, device=device)
-            self.norms = torch.zeros((n, 2), dtype=torch.float32, device=device)
+            q = int(self.qjl)
+            self.words = torch.zeros((n, W, bits + q), dtype=torch.int32, device=device)
+            self.norms = torch.zeros((n, 1 + q), dtype=torch.float32, device=device)
         else:
             self.words = torch.zeros((n // 32, d, bits), dtype=torch.int32, device=device)
             self.norms = torch.zeros((n,), dtype=torch.float32, device=device)
 
     def c(self) -> CPacked:
-        return CPacked(self.words.data_ptr(), self.norms.data_ptr(), self.n, self.bits, 1 if self.is_key else 0)
+        return CPacked(self.words.data_ptr(), self.norms.data_ptr(), self.n, self.bits, 1 if self.is_key else 0,
+                       1 if self.qjl else 0)
 
     def host(self):
         """(uint32 words, float32 norms) copied to host numpy arrays."""
@@ -306,12 +312,14 @@ class KVCache:
     """Packed KV cache: records of stream (b, h) at (b*kv_heads + h)*capacity + t."""
 
     def __init__(self, batch: int, kv_heads: int, capacity: int, d: int, key_bits: int, value_bits: int,
-                 device="cuda"):
+                 device="cuda", key_qjl: bool = True):
+        """key_bits = B MSE bits of the keys; key_qjl = False stores MSE-only keys,
+        key_bits = 0 with key_qjl stores pure QJL keys."""
         torch = _torch()
         if capacity % 32:
             raise ValueError("capacity must be a multiple of 32")
         n = batch * kv_heads * capacity
-        self.k = Packed(n, d, key_bits, True, device)
+        self.k = Packed(n, d, key_bits, True, device, qjl=key_qjl)
         self.v = Packed(n, d, value_bits, False, device)
         self.seq_len = torch.zeros((batch,), dtype=torch.int32, device=device)
         self.batch, self.kv_heads, self.capacity, self.d = batch, kv_heads, capacity, d

@@ -439,10 +439,12 @@ static tq_status check_device(const tq_ctx *ctx, const char *fn) {
 
 static tq_status check_packed(const tq_ctx *ctx, const tq_packed *p, int want_key, const char *fn) {
   if (!p || !p->bits || !p->norms) return fail(TQ_ERR_ARG, std::string(fn) + ": packed array or its pointers NULL");
-  if (p->mse_bits < 1 || p->mse_bits > TQ_MAX_BITS)
-    return fail(TQ_ERR_UNSUPPORTED, std::string(fn) + ": mse_bits must be in [1, 4]");
   if ((p->is_key != 0) != (want_key != 0))
     return fail(TQ_ERR_ARG, std::string(fn) + (want_key ? ": expected a key array" : ": expected a value array"));
+  if (p->qjl != 0 && p->qjl != 1) return fail(TQ_ERR_ARG, std::string(fn) + ": qjl must be 0 or 1");
+  if (!p->is_key && p->qjl) return fail(TQ_ERR_ARG, std::string(fn) + ": value arrays have no QJL stage (qjl = 0)");
+  if (p->mse_bits < (p->is_key && p->qjl ? 0 : 1) || p->mse_bits > TQ_MAX_BITS)
+    return fail(TQ_ERR_UNSUPPORTED, std::string(fn) + ": mse_bits must be in [1, 4] ([0, 4] for keys with qjl = 1)");
   if (p->n < 0) return fail(TQ_ERR_ARG, std::string(fn) + ": negative record count");
   if (!p->is_key && (p->n % 32) != 0) return fail(TQ_ERR_ARG, std::string(fn) + ": value capacity must be a multiple of 32");
   (void)ctx;

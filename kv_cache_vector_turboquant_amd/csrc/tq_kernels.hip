@@ -62,6 +62,7 @@ struct GemmArgs {
   // quantize epilogues
   const DeviceTables *tables;
   int bits, d;
+  int qjl;               // keys: 1 = QJL sign word and |r| in the record, 0 = MSE-only
   uint32_t *bits_out;
   float *norms_out;
   float *resid;          // keys: residual rows [stream*n_tokens + t][d]
@@ -104,7 +105,7 @@ __device__ __forceinline__ void load_dense(const DenseSrc &s, int64_t row0, int 
 // [c[idx_t] (d values) | qjl_scale * rho_t * (2 sigma_t - 1) (d values)].
 __device__ __forceinline__ void load_keys(const GemmArgs &g, const float *cent, int64_t row0, int k0, int tid,
                                           float4 (&v)[2]) {
-  const int W = g.d >> 5, B = g.bits;
+  const int W = g.d >> 5, B = g.bits, Q = g.qjl;
 #pragma unroll
   for (int gg = 0; gg < 2; ++gg) {
     const int r = (tid >> 2) + 64 * gg;
@@ -112,18 +113,20 @@ __device__ __forceinline__ void load_keys(const GemmArgs &g, const float *cent, 
     const int64_t t = row0 + r;
     float e[4] = {0.f, 0.f, 0.f, 0.f};
     if (t < g.b.nrows) {
-      const uint32_t *rec = g.kbits + t * (int64_t)(W * (B + 1));
+      const uint32_t *rec = g.kbits + t * (int64_t)(W * (B + Q));
       if (k < g.d) {
-        const int w = k >> 5, o = k & 31;
-        int idx[4] = {0, 0, 0, 0};
-        for (int p = 0; p < B; ++p) {
-          const uint32_t word = rec[w * (B + 1) + p] >> o;
+        if (B > 0) {  // pure QJL keys have no codebook term
+          const int w = k >> 5, o = k & 31;
+          int idx[4] = {0, 0, 0, 0};
+          for (int p = 0; p < B; ++p) {
+            const uint32_t word = rec[w * (B + Q) + p] >> o;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) idx[q] |= ((word >> q) & 1u) << p;
+            for (int q = 0; q < 4; ++q) idx[q] |= ((word >> q) & 1u) << p;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] = cent[idx[q]];
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) e[q] = cent[idx[q]];
-      } else {
+      } else if (Q) {  // MSE-only keys have no QJL term
         const int i = k - g.d, w = i >> 5, o = i & 31;
         const uint32_t word = rec[w * (B + 1) + B] >> o;
         const float a = g.qjl_scale * g.knorm[2 * t + 1];
@@ -237,7 +240,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
     for (int b = 0; b < 2; ++b) {
       const int64_t col = col0 + wn * 64 + b * 32 + li;
       float scale = 1.f;
-      if constexpr (MODE == MODE_SCORES) scale = (col < g.N) ? g.knorm[2 * col] : 0.f;
+      if constexpr (MODE == MODE_SCORES) scale = (col < g.N) ? g.knorm[(1 + g.qjl) * col] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = row0 + wm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
@@ -263,11 +266,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
           const float nrm = sqrtf(stat[rl]);
           live = in && nrm > 0.f;
           const float y = live ? acc[b][r] / nrm : 0.f;
-          const int idx = quant_index(y, bnd, L);
-          if (in) g.resid[(s * g.n_tokens + t) * (int64_t)g.d + col] = live ? y - cent[idx] : 0.f;
+          const int idx = B > 0 ? quant_index(y, bnd, L) : 0;
+          // the residual feeds the sketch (pure QJL keys: the whole rotated vector)
+          if (in && g.qjl) g.resid[(s * g.n_tokens + t) * (int64_t)g.d + col] = live ? y - (B > 0 ? cent[idx] : 0.f) : 0.f;
           mybits = live ? (uint32_t)idx : 0u;
         } else {
-          live = in && g.norms_out[2 * (rec_base + t)] > 0.f;
+          live = in && g.norms_out[2 * (rec_base + t)] > 0.f;  // signs only exist with the QJL stage: 2 norms
           mybits = (live && acc[b][r] >= 0.f) ? 1u : 0u;
         }
         const int np = (MODE == MODE_KEY_CODES) ? B : 1;
@@ -286,7 +290,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
       const int64_t t = row0 + rl;
       const int w = (int)(col0 >> 5) + gl;
       if (t < g.n_tokens && w < W) {
-        uint32_t *dst = g.bits_out + ((rec_base + t) * W + w) * (int64_t)(B + 1);
+        uint32_t *dst = g.bits_out + ((rec_base + t) * W + w) * (int64_t)(B + g.qjl);
         if constexpr (MODE == MODE_KEY_CODES) {
           for (int p = 0; p < B; ++p) dst[p] = cw[(rl * (GBN / 32) + gl) * 4 + p];
         } else {
@@ -294,7 +298,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
         }
       }
       if (ct == 0 && gl == 0 && t < g.n_tokens) {
-        if constexpr (MODE == MODE_KEY_CODES) g.norms_out[2 * (rec_base + t)] = sqrtf(stat[rl]);
+        if constexpr (MODE == MODE_KEY_CODES) g.norms_out[(1 + g.qjl) * (rec_base + t)] = sqrtf(stat[rl]);
         else g.norms_out[2 * (rec_base + t) + 1] = sqrtf(stat[rl]);
       }
     }
@@ -416,9 +420,13 @@ __device__ __forceinline__ int swz(int row, int gran_per_row, int g, int mask) {
 // (their Pi and S parts fill ~200 VGPRs: one work-group per compute unit),
 // values four (two work-groups per compute unit overlap one's MFMA phase with
 // the other's epilogue).
-template <bool KEYS, int B, int NW>
+// QJL (keys): the sketch stage; without it the keys are MSE-only (B code words
+// and |k|); B = 0 with QJL gives pure QJL keys (the residual is y itself).
+template <bool KEYS, int B, int NW, bool QJL>
 __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
-  constexpr int H = 1 << (B - 1);  // centroids per sign
+  constexpr bool SK = KEYS && QJL;  // sketch stage present
+  constexpr int NPL = B + (SK ? 1 : 0);  // words per 32-coordinate group of a key record
+  constexpr int H = B > 0 ? 1 << (B - 1) : 1;  // centroids per sign
   constexpr int RB = 8 / NW;       // row blocks per wave
   constexpr int NT = 64 * NW;      // threads
   constexpr int XG = QT * 16 / NT; // X granules per thread
@@ -429,7 +437,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   // values [coordinate][token] (4 granules per coordinate)
   __shared__ __attribute__((aligned(16))) uint32_t stage[QT * QD / 4];
   // keys: residual parts, [token][coordinate] bf16 (16 granules per token row)
-  __shared__ __attribute__((aligned(16))) uint16_t rt[KEYS ? 2 : 1][KEYS ? QT * QD : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t rt[SK ? 2 : 1][SK ? QT * QD : 8];
   __shared__ float nrm[QT], ninv[QT];
   __shared__ float rho2[NW][QT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -437,14 +445,16 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   const int64_t tps = (a.n_tokens + QT - 1) / QT, total = tps * a.n_streams;
   // positive boundaries and centroid magnitudes
   float tp[H > 1 ? H - 1 : 1], cm[H];
+  if constexpr (B > 0) {
 #pragma unroll
-  for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
+    for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
 #pragma unroll
-  for (int j = 0; j < H; ++j) cm[j] = a.tables->centroid[B][H + j];
+    for (int j = 0; j < H; ++j) cm[j] = a.tables->centroid[B][H + j];
+  }
   // the wave's rows of the Pi parts (and of the S parts for keys) stay in registers
   // for every tile the work-group processes
   bf16x8 pf[RB][4][3];
-  bf16x8 sf[KEYS ? RB : 1][KEYS ? 4 : 1][2];
+  bf16x8 sf[SK ? RB : 1][SK ? 4 : 1][2];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = 16 * (wave * RB + rb) + c16;
@@ -452,7 +462,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int sp = 0; sp < 3; ++sp) pf[rb][ks][sp] = ld_bf8(a.rot3 + (sp * QD + r) * QD + ks * 32 + kq * 8);
-      if constexpr (KEYS) {
+      if constexpr (SK) {
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) sf[rb][ks][sp] = ld_bf8(a.sk2 + (sp * QD + r) * QD + ks * 32 + kq * 8);
       }
@@ -557,19 +567,22 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float y = acc[rb][tb][r] * inv;
-            uint32_t idx;
-            res[r] = y - code(y, idx);
+            uint32_t idx = 0;
+            // pure QJL keys have no codes: the residual is y itself
+            res[r] = B > 0 ? y - code(y, idx) : y;
             bytes |= idx << (7 * r);
-            rp[tb] = fmaf(res[r], res[r], rp[tb]);
+            if constexpr (SK) rp[tb] = fmaf(res[r], res[r], rp[tb]);
           }
-          split2(res[0], res[1], hi2[0], lo2[0]);
-          split2(res[2], res[3], hi2[1], lo2[1]);
-          // code bytes of 4 coordinates: granule c0 / 16, dword (c0 / 4) % 4
+          // code fields of 4 coordinates: granule c0 / 16, dword (c0 / 4) % 4
           stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
-          // residual parts: granule c0 / 8 of 16, half (c0 / 4) % 2
-          const int gr = swz(tok, 16, c0 >> 3, 15) * 8 + ((c0 >> 2) & 1) * 4;
-          *reinterpret_cast<uint2 *>(&rt[0][gr]) = make_uint2(hi2[0], hi2[1]);
-          *reinterpret_cast<uint2 *>(&rt[1][gr]) = make_uint2(lo2[0], lo2[1]);
+          if constexpr (SK) {
+            split2(res[0], res[1], hi2[0], lo2[0]);
+            split2(res[2], res[3], hi2[1], lo2[1]);
+            // residual parts: granule c0 / 8 of 16, half (c0 / 4) % 2
+            const int gr = swz(tok, 16, c0 >> 3, 15) * 8 + ((c0 >> 2) & 1) * 4;
+            *reinterpret_cast<uint2 *>(&rt[0][gr]) = make_uint2(hi2[0], hi2[1]);
+            *reinterpret_cast<uint2 *>(&rt[1][gr]) = make_uint2(lo2[0], lo2[1]);
+          }
         }
       }
 #pragma unroll
@@ -577,12 +590,13 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
         rp[tb] += __shfl_xor(rp[tb], 16);
         rp[tb] += __shfl_xor(rp[tb], 32);
       }
-      if (kq == 0) {
+      if (SK && kq == 0) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) rho2[wave][tb * 16 + c16] = rp[tb];
       }
       __syncthreads();
-      // ---- product 2: z[sketch row][token] = S r, signs into bit 7 of the code bytes
+      if constexpr (SK) {
+      // ---- product 2: z[sketch row][token] = S r, signs into bit 6 of the code fields
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -614,23 +628,24 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
         }
       }
       __syncthreads();
+      }  // sketch stage
       if (more) {  // every wave is past its reads of this tile's X
 #pragma unroll
         for (int i = 0; i < XG; ++i) xs[i * NT + tid] = xr[i];
       }
-      // ---- pack: thread (token, 32-coordinate group) -> B code planes + the sign plane
+      // ---- pack: thread (token, 32-coordinate group) -> B code planes (+ the sign plane)
       if (tid < 4 * QT) {
         const int tok = tid >> 2, g = tid & 3;
         if (tok < nv) {
           const int64_t rec = s * a.os + a.oo + t0 + tok;
           const float n = nrm[tok];
-          uint32_t w[B + 1];
+          uint32_t w[NPL];
           if (n > 0.f) {
             const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g, 7) * 4]);
             const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g + 1, 7) * 4]);
             const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-            for (int p = 0; p <= B; ++p) {
+            for (int p = 0; p < NPL; ++p) {
               const int bit = p < B ? p : QJL_FIELD_BIT;
               uint32_t word = 0;
 #pragma unroll
@@ -639,21 +654,25 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
             }
           } else {
 #pragma unroll
-            for (int p = 0; p <= B; ++p) w[p] = 0u;
+            for (int p = 0; p < NPL; ++p) w[p] = 0u;
           }
-          uint32_t *dst = a.bits_out + (rec * QW + g) * (B + 1);
-          if constexpr (B == 3) {
+          uint32_t *dst = a.bits_out + (rec * QW + g) * NPL;
+          if constexpr (NPL == 4) {
             *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
           } else {
 #pragma unroll
-            for (int p = 0; p <= B; ++p) dst[p] = w[p];
+            for (int p = 0; p < NPL; ++p) dst[p] = w[p];
           }
           if (g == 0) {
-            float r2 = 0.f;
+            if constexpr (SK) {
+              float r2 = 0.f;
 #pragma unroll
-            for (int v = 0; v < NW; ++v) r2 += rho2[v][tok];
-            *reinterpret_cast<float2 *>(a.norms_out + 2 * rec) =
-                n > 0.f ? make_float2(n, sqrtf(r2)) : make_float2(0.f, 0.f);
+              for (int v = 0; v < NW; ++v) r2 += rho2[v][tok];
+              *reinterpret_cast<float2 *>(a.norms_out + 2 * rec) =
+                  n > 0.f ? make_float2(n, sqrtf(r2)) : make_float2(0.f, 0.f);
+            } else {
+              a.norms_out[rec] = n;
+            }
           }
         }
       }
@@ -712,7 +731,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
 
 // Persistent launch: as many work-groups as fit on the device at once (registers
 // decide: keys one per compute unit, values two), at most one per tile.
-template <bool KEYS, int B>
+template <bool KEYS, int B, bool QJL>
 static hipError_t launch_quant128_b(const Q128Args &q, hipStream_t st) {
   constexpr int NW = KEYS ? 8 : 4;
   static int resident = 0;  // work-groups resident on the device
@@ -721,24 +740,35 @@ static hipError_t launch_quant128_b(const Q128Args &q, hipStream_t st) {
     hipError_t e;
     if ((e = hipGetDevice(&dev)) != hipSuccess ||
         (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess ||
-        (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant128_kernel<KEYS, B, NW>, 64 * NW, 0)) !=
+        (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant128_kernel<KEYS, B, NW, QJL>, 64 * NW, 0)) !=
             hipSuccess)
       return e;
     resident = std::max(1, cus * std::max(1, per_cu));
   }
   const int64_t tiles = ((q.n_tokens + QT - 1) / QT) * q.n_streams;
   const unsigned nwg = (unsigned)std::min<int64_t>(tiles, resident);
-  hipLaunchKernelGGL((quant128_kernel<KEYS, B, NW>), dim3(nwg), dim3(64 * NW), 0, st, q);
+  hipLaunchKernelGGL((quant128_kernel<KEYS, B, NW, QJL>), dim3(nwg), dim3(64 * NW), 0, st, q);
   return hipGetLastError();
 }
 
+// keys: B = 0..4 with the sketch (0 = pure QJL), 1..4 without (MSE-only); values: 1..4
 template <bool KEYS>
-static hipError_t launch_quant128(const Q128Args &q, int bits, hipStream_t st) {
+static hipError_t launch_quant128(const Q128Args &q, int bits, bool qjl, hipStream_t st) {
+  if (KEYS && qjl) {
+    switch (bits) {
+      case 0: return launch_quant128_b<KEYS, 0, true>(q, st);
+      case 1: return launch_quant128_b<KEYS, 1, true>(q, st);
+      case 2: return launch_quant128_b<KEYS, 2, true>(q, st);
+      case 3: return launch_quant128_b<KEYS, 3, true>(q, st);
+      case 4: return launch_quant128_b<KEYS, 4, true>(q, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (bits) {
-    case 1: return launch_quant128_b<KEYS, 1>(q, st);
-    case 2: return launch_quant128_b<KEYS, 2>(q, st);
-    case 3: return launch_quant128_b<KEYS, 3>(q, st);
-    case 4: return launch_quant128_b<KEYS, 4>(q, st);
+    case 1: return launch_quant128_b<KEYS, 1, false>(q, st);
+    case 2: return launch_quant128_b<KEYS, 2, false>(q, st);
+    case 3: return launch_quant128_b<KEYS, 3, false>(q, st);
+    case 4: return launch_quant128_b<KEYS, 4, false>(q, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -758,7 +788,8 @@ static hipError_t quant128(const tq_ctx *ctx, bool keys, const void *x, int64_t 
   q.norms_out = out->norms;
   q.os = os;
   q.oo = oo;
-  return keys ? launch_quant128<true>(q, out->mse_bits, st) : launch_quant128<false>(q, out->mse_bits, st);
+  return keys ? launch_quant128<true>(q, out->mse_bits, out->qjl != 0, st)
+              : launch_quant128<false>(q, out->mse_bits, false, st);
 }
 
 hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams, int64_t n_tokens,
@@ -779,6 +810,7 @@ hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, i
   g.d = d;
   g.bits_out = out->bits;
   g.norms_out = out->norms;
+  g.qjl = out->qjl;
   g.resid = work;
   g.n_tokens = n_tokens;
   g.out_stream_stride = os;
@@ -787,7 +819,7 @@ hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, i
   dim3 grid((unsigned)((n_tokens + GBM - 1) / GBM), (d + GBN - 1) / GBN, (unsigned)n_streams);
   hipLaunchKernelGGL(gemm_kernel<MODE_KEY_CODES>, grid, dim3(256), 0, st, g);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !out->qjl) return e;  // MSE-only keys stop after stage 1
   // stage 2: z = S r on the residual rows, sign bits and ||r||
   GemmArgs g2 = g;
   g2.a = {work, d, n_tokens, 0};
@@ -943,6 +975,7 @@ hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t 
   g3.N = keys->n;
   g3.tables = ctx->d_tables;
   g3.bits = keys->mse_bits;
+  g3.qjl = keys->qjl;
   g3.d = d;
   g3.kbits = keys->bits;
   g3.knorm = keys->norms;
@@ -1009,6 +1042,7 @@ struct DecodeArgs {
   const float *vnorm;
   const int32_t *seq_len;
   int kbitsB, vbitsB;    // MSE bits of keys / values
+  int kqjl;              // keys carry the QJL sign word and |r|
   int kv_heads, capacity, q_heads, group, hgroups;
   int chunk, nchunks;
   int streams_hg;        // streams x head groups (decode grid = nchunks x streams_hg)
@@ -1068,7 +1102,7 @@ struct AppendLds {
 
 __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int tid, bool bf16in, AppendLds &L) {
   const int nstreams = a.batch * a.kv_heads;
-  const int kB = a.kbitsB, vB = a.vbitsB;
+  const int kB = a.kbitsB, vB = a.vbitsB, kQ = a.kqjl;  // kQ: QJL sign word and |r| (uniform)
   const int lane = tid & 63, w = tid >> 6;
   const int r = tid & (DD - 1), kq = tid >> 7;
   // this thread's stream for the per-coordinate phases: (stream half, key or value)
@@ -1087,7 +1121,7 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
   float prow[32], srow[32];
 #pragma unroll
   for (int u = 0; u < 32; ++u) prow[u] = a.rs_t[(kq * 32 + u) * 2 * DD + r];
-  {
+  if (kQ) {
     const float4 *sr = reinterpret_cast<const float4 *>(a.sk + (int64_t)r * DD + 32 * kq);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -1145,7 +1179,7 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
     const float y = live ? yx / nk : 0.f;
     for (int i = 0; i < (1 << kB) - 1; ++i) idx += (y >= L.tb[i]) ? 1 : 0;
     if (!live) idx = 0;
-    const float res = live ? y - L.tb[16 + idx] : 0.f;
+    const float res = live ? y - (kB > 0 ? L.tb[16 + idx] : 0.f) : 0.f;  // pure QJL keys: r = y
     L.res[hs][r] = res;
     float r2 = res * res;
     for (int off = 32; off > 0; off >>= 1) r2 += __shfl_xor(r2, off);
@@ -1163,7 +1197,7 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
     }
   }
   __syncthreads();
-  {
+  if (kQ) {
     // z = S r for both streams: thread (sketch row r, coordinate quarter kq)
     float z0 = 0.f, z1 = 0.f;
 #pragma unroll
@@ -1173,26 +1207,29 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
     }
     L.zp[kq][0][r] = z0;
     L.zp[kq][1][r] = z1;
+    __syncthreads();
   }
-  __syncthreads();
   if (kv == 0 && on[hs]) {
     // waves 0, 1 (stream 0) and 4, 5 (stream 1): key coordinate r
-    const float z = (L.zp[0][hs][r] + L.zp[1][hs][r]) + (L.zp[2][hs][r] + L.zp[3][hs][r]);
     const bool live = nk > 0.f;
     uint32_t words[5];
     for (int p = 0; p < kB; ++p) {
       const uint64_t bal = __builtin_amdgcn_ballot_w64(((idx >> p) & 1) != 0);
       words[p] = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
     }
-    const uint64_t sbal = __builtin_amdgcn_ballot_w64(live && z >= 0.f);
-    words[kB] = (lane < 32) ? (uint32_t)sbal : (uint32_t)(sbal >> 32);
+    if (kQ) {
+      const float z = (L.zp[0][hs][r] + L.zp[1][hs][r]) + (L.zp[2][hs][r] + L.zp[3][hs][r]);
+      const uint64_t sbal = __builtin_amdgcn_ballot_w64(live && z >= 0.f);
+      words[kB] = (lane < 32) ? (uint32_t)sbal : (uint32_t)(sbal >> 32);
+    }
+    const int np = kB + kQ;
     if ((lane & 31) == 0) {
-      uint32_t *dst = a.kbits_w + (rec * DW + (w & 1) * 2 + (lane >> 5)) * (kB + 1);
-      for (int p = 0; p <= kB; ++p) dst[p] = words[p];
+      uint32_t *dst = a.kbits_w + (rec * DW + (w & 1) * 2 + (lane >> 5)) * np;
+      for (int p = 0; p < np; ++p) dst[p] = words[p];
     }
     if (r == 0) {
-      a.knorm_w[2 * rec] = nk;
-      a.knorm_w[2 * rec + 1] = live ? sqrtf(L.red[hs][4] + L.red[hs][5]) : 0.f;
+      a.knorm_w[(1 + kQ) * rec] = nk;
+      if (kQ) a.knorm_w[2 * rec + 1] = live ? sqrtf(L.red[hs][4] + L.red[hs][5]) : 0.f;
       a.vnorm_w[rec] = nv;
     }
   }
@@ -1478,9 +1515,13 @@ __global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
   }
 }
 
-template <int KB, int VB>
+// KB MSE bits of the keys (0: pure QJL keys), QJL: the keys carry the sign word
+// and |r| (false: MSE-only keys)
+template <int KB, int VB, bool QJL>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
-  constexpr int KM = 1 << (KB - 1);  // key Walsh masks
+  constexpr int KM = KB > 0 ? 1 << (KB - 1) : 0;  // key Walsh masks
+  constexpr int KQ = QJL ? 1 : 0;
+  constexpr int NPL = KB + KQ;  // words per 32-coordinate group of a key record
   constexpr int VM = 1 << (VB - 1);  // value Walsh masks
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float *lg = reinterpret_cast<float *>(smem);                   // [4][chunk] logits (log2 units)
@@ -1528,20 +1569,20 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   } else {
     const int n = t1 - t0;
     const int64_t srec = (int64_t)stream * a.capacity;
-    const float *wk = a.tables->walsh[KB];
+    const float *wk = a.tables->walsh[KB > 0 ? KB : 1];
     const float *wv = a.tables->walsh[VB];
     const int ngrp = (n + 127) >> 7;
     const int tn = lane & 15, G = lane >> 4;  // MFMA column (token), row group (head)
     // records of the chunk: uniform bases and unsigned 32-bit byte offsets per lane
     // (base + zero-extended offset addressing); lanes past the end re-read token
     // n-1, so every store below stays unconditional and harmless
-    const char *kb0 = reinterpret_cast<const char *>(a.kbits + (srec + t0) * DW * (KB + 1));
-    const char *kn0 = reinterpret_cast<const char *>(a.knorm + 2 * (srec + t0));
+    const char *kb0 = reinterpret_cast<const char *>(a.kbits + (srec + t0) * DW * NPL);
+    const char *kn0 = reinterpret_cast<const char *>(a.knorm + (1 + KQ) * (srec + t0));
     const char *vn0 = reinterpret_cast<const char *>(a.vnorm + (srec + t0));
-    const uint32_t kgo = (uint32_t)(G * (KB + 1) * 4);  // the lane's 32-coordinate group in a record
+    const uint32_t kgo = (uint32_t)(G * NPL * 4);  // the lane's 32-coordinate group in a record
     struct KBuf {
-      uint32_t pl[KTPW][KB + 1];
-      float2 kn[KTPW];
+      uint32_t pl[KTPW][NPL];
+      float2 kn[KTPW];  // (|k|, |r|); MSE-only keys: (|k|, 0)
       float vn[KTPW];
       uint32_t tc[KTPW];
     };
@@ -1550,15 +1591,16 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       for (int u = 0; u < KTPW; ++u) {
         const uint32_t tc = (uint32_t)min((base + u) * 16 + tn, n - 1);
         bf.tc[u] = tc;
-        const char *src = kb0 + (tc * (uint32_t)(DW * (KB + 1) * 4) + kgo);
-        if constexpr (KB == 3) {
+        const char *src = kb0 + (tc * (uint32_t)(DW * NPL * 4) + kgo);
+        if constexpr (NPL == 4) {
           const uint4 w4 = *reinterpret_cast<const uint4 *>(src);
           bf.pl[u][0] = w4.x; bf.pl[u][1] = w4.y; bf.pl[u][2] = w4.z; bf.pl[u][3] = w4.w;
         } else {
 #pragma unroll
-          for (int p = 0; p <= KB; ++p) bf.pl[u][p] = reinterpret_cast<const uint32_t *>(src)[p];
+          for (int p = 0; p < NPL; ++p) bf.pl[u][p] = reinterpret_cast<const uint32_t *>(src)[p];
         }
-        bf.kn[u] = *reinterpret_cast<const float2 *>(kn0 + (tc << 3));
+        if constexpr (QJL) bf.kn[u] = *reinterpret_cast<const float2 *>(kn0 + (tc << 3));
+        else bf.kn[u] = make_float2(*reinterpret_cast<const float *>(kn0 + (tc << 2)), 0.f);
         bf.vn[u] = *reinterpret_cast<const float *>(vn0 + (tc << 2));
       }
     };
@@ -1583,21 +1625,23 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const float *qc = a.qconst + ((int64_t)sg * 4 + G) * QC;
     // accumulator start -sum_j Q_j per digit slot: the A fragments against an
     // all-ones mask (B scale 2^1 undoes the 1/2 of every product), exact
-    f4v init_r, init_s;
+    f4v init_r = {0.f, 0.f, 0.f, 0.f}, init_s = {0.f, 0.f, 0.f, 0.f};
     {
       const i8v ones = mask_fp4_01(0xFFFFFFFFu);
       const f4v z = {0.f, 0.f, 0.f, 0.f};
-      init_r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr0, ones, z, 2, 4, 0, sc0, 0, 128);
-      init_r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr1, ones, init_r, 2, 4, 0, sc1, 0, 128);
-      init_s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs0, ones, z, 2, 4, 0, sc0, 0, 128);
-      init_s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs1, ones, init_s, 2, 4, 0, sc1, 0, 128);
-      init_r = -init_r;
-      init_s = -init_s;
+      if constexpr (KM > 0) {
+        init_r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr0, ones, z, 2, 4, 0, sc0, 0, 128);
+        init_r = -__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr1, ones, init_r, 2, 4, 0, sc1, 0, 128);
+      }
+      if constexpr (QJL) {
+        init_s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs0, ones, z, 2, 4, 0, sc0, 0, 128);
+        init_s = -__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs1, ones, init_s, 2, 4, 0, sc1, 0, 128);
+      }
     }
     // logit (log2 units) = |k| (sum_S wr_S T_S + qs |r| T_QJL) with the query units,
     // the softmax scale and the QJL constant folded into the per-lane weights
     const float sr = qc[0] * a.scale_log2, qs = qc[1] * a.qjl_scale * a.scale_log2;
-    float wkr[KM];
+    float wkr[KM > 0 ? KM : 1];
 #pragma unroll
     for (int mi = 0; mi < KM; ++mi) wkr[mi] = wk[mi] * sr;
     float vmx = 0.f, lmx = -INFINITY;
@@ -1607,14 +1651,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < KTPW; ++u) {
         const int tc = (int)cur.tc[u];
-        // all masked sums first (independent accumulators keep the MFMA pipe busy)
-        f4v acc[KM + 1];
-        i8v sm[KB];
+        // all masked sums first (independent accumulators keep the MFMA pipe busy):
+        // the KM Walsh masks of the codes, then the sign word's mask
+        f4v acc[KM + KQ];
+        i8v sm[KB > 0 ? KB : 1];
 #pragma unroll
         for (int p = 0; p < KB; ++p) sm[p] = mask_fp4_01(cur.pl[u][p]);
 #pragma unroll
-        for (int mi = 0; mi <= KM; ++mi) {
-          const i8v bm = mi < KM ? walsh_fp4(sm, walsh_mask(KB, mi)) : mask_fp4_01(cur.pl[u][KB]);
+        for (int mi = 0; mi < KM + KQ; ++mi) {
+          const i8v bm = mi < KM ? walsh_fp4(sm, walsh_mask(KB, mi)) : mask_fp4_01(cur.pl[u][NPL - 1]);
           acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr0 : aqs0, bm, mi < KM ? init_r : init_s,
                                                                      2, 4, 0, sc0, 0, 129);
           acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr1 : aqs1, bm, acc[mi], 2, 4, 0, sc1,
@@ -1623,8 +1668,13 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         float code = 0.f;
 #pragma unroll
         for (int mi = 0; mi < KM; ++mi) code += wkr[mi] * ((acc[mi][0] + acc[mi][1]) + (acc[mi][2] + acc[mi][3]));
-        const float Ts = (acc[KM][0] + acc[KM][1]) + (acc[KM][2] + acc[KM][3]);
-        const float s = cur.kn[u].x * fmaf(cur.kn[u].y * Ts, qs, code);
+        float s;
+        if constexpr (QJL) {
+          const float Ts = (acc[KM][0] + acc[KM][1]) + (acc[KM][2] + acc[KM][3]);
+          s = cur.kn[u].x * fmaf(cur.kn[u].y * Ts, qs, code);
+        } else {
+          s = cur.kn[u].x * code;
+        }
         lg[G * a.chunk + tc] = s;
         lmx = fmaxf(lmx, s);
         vnl[tc] = cur.vn[u];
@@ -1815,9 +1865,9 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
   return b;
 }
 
-template <int KB, int VB>
+template <int KB, int VB, bool QJL>
 static hipError_t launch_decode_kv(const DecodeArgs &a, dim3 grid, size_t shm, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<KB, VB>), grid, dim3(256), shm, st, a);
+  hipLaunchKernelGGL((decode_kernel<KB, VB, QJL>), grid, dim3(256), shm, st, a);
   return hipGetLastError();
 }
 
@@ -1833,6 +1883,7 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.vnorm = cache->v.norms;
   a.seq_len = cache->d_seq_len;
   a.kbitsB = cache->k.mse_bits;
+  a.kqjl = cache->k.qjl;
   a.vbitsB = cache->v.mse_bits;
   a.kv_heads = cache->kv_heads;
   a.capacity = cache->capacity;
@@ -1887,15 +1938,17 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   const size_t shm = (size_t)5 * chunk * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;
   dim3 grid(nchunks * streams);
   const int kb = cache->k.mse_bits, vb = cache->v.mse_bits;
+  const bool kq = cache->k.qjl != 0;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-#define TQ_DEC(K_, V_) else if (kb == K_ && vb == V_) e = launch_decode_kv<K_, V_>(a, grid, shm, st);
+#define TQ_DEC(K_, V_, Q_) else if (kb == K_ && vb == V_ && kq == Q_) e = launch_decode_kv<K_, V_, Q_>(a, grid, shm, st);
+#define TQ_DEC4(K_, Q_) TQ_DEC(K_, 1, Q_) TQ_DEC(K_, 2, Q_) TQ_DEC(K_, 3, Q_) TQ_DEC(K_, 4, Q_)
   if (false) {
   }
-  TQ_DEC(1, 1) TQ_DEC(1, 2) TQ_DEC(1, 3) TQ_DEC(1, 4)
-  TQ_DEC(2, 1) TQ_DEC(2, 2) TQ_DEC(2, 3) TQ_DEC(2, 4)
-  TQ_DEC(3, 1) TQ_DEC(3, 2) TQ_DEC(3, 3) TQ_DEC(3, 4)
-  TQ_DEC(4, 1) TQ_DEC(4, 2) TQ_DEC(4, 3) TQ_DEC(4, 4)
+  TQ_DEC4(1, true) TQ_DEC4(2, true) TQ_DEC4(3, true) TQ_DEC4(4, true)
+  TQ_DEC4(0, true)
+  TQ_DEC4(1, false) TQ_DEC4(2, false) TQ_DEC4(3, false) TQ_DEC4(4, false)
   else return hipErrorInvalidValue;
+#undef TQ_DEC4
 #undef TQ_DEC
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
@@ -1945,6 +1998,7 @@ struct AppendArgs {
   float *vnorm;
   int32_t *seq_len;
   int kB, vB, kv_heads, capacity;
+  int kQ;  // keys carry the QJL sign word and |r|
 };
 
 __device__ __forceinline__ float block_sum128(float v, float *red) {
@@ -1978,36 +2032,37 @@ __global__ void __launch_bounds__(DD) append_kernel(AppendArgs a) {
     y += p * xs[k];
     yv += p * vs[k];
   }
-  // ---- key: codes, residual, sketch signs ----
+  // ---- key: codes, residual, sketch signs (kQ; pure QJL keys: kB = 0, r = y) ----
   const bool live = nrm > 0.f;
   y = live ? y / nrm : 0.f;
   int idx = 0;
   for (int i = 0; i < (1 << a.kB) - 1; ++i) idx += (y >= a.tables->boundary[a.kB][i]) ? 1 : 0;
   if (!live) idx = 0;
-  const float r = live ? y - a.tables->centroid[a.kB][idx] : 0.f;
-  rs[j] = r;
-  const float rho = sqrtf(block_sum128(r * r, red));
-  float z = 0.f;
-#pragma unroll 16
-  for (int k = 0; k < DD; ++k) z += a.sketch_t[k * DD + j] * rs[k];
-  const bool sg = live && z >= 0.f;
   uint32_t words[5];
   for (int p = 0; p < a.kB; ++p) {
     const uint64_t bal = __builtin_amdgcn_ballot_w64(((idx >> p) & 1) != 0);
     words[p] = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
   }
-  {
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(sg);
+  float rho = 0.f;
+  if (a.kQ) {  // uniform over the block
+    const float r = live ? y - (a.kB > 0 ? a.tables->centroid[a.kB][idx] : 0.f) : 0.f;
+    rs[j] = r;
+    rho = sqrtf(block_sum128(r * r, red));
+    float z = 0.f;
+#pragma unroll 16
+    for (int k = 0; k < DD; ++k) z += a.sketch_t[k * DD + j] * rs[k];
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(live && z >= 0.f);
     words[a.kB] = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
   }
+  const int np = a.kB + a.kQ;
   if ((lane & 31) == 0) {
     const int w = wv * 2 + (lane >> 5);
-    uint32_t *dst = a.kbits + (rec * DW + w) * (a.kB + 1);
-    for (int p = 0; p <= a.kB; ++p) dst[p] = words[p];
+    uint32_t *dst = a.kbits + (rec * DW + w) * np;
+    for (int p = 0; p < np; ++p) dst[p] = words[p];
   }
   if (j == 0) {
-    a.knorm[2 * rec] = nrm;
-    a.knorm[2 * rec + 1] = live ? rho : 0.f;
+    a.knorm[(1 + a.kQ) * rec] = nrm;
+    if (a.kQ) a.knorm[2 * rec + 1] = live ? rho : 0.f;
     a.vnorm[rec] = nv;
   }
   // ---- value: codes into the token-major word of this coordinate ----
@@ -2045,6 +2100,7 @@ hipError_t launch_append(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.vnorm = cache->v.norms;
   a.seq_len = cache->d_seq_len;
   a.kB = cache->k.mse_bits;
+  a.kQ = cache->k.qjl;
   a.vB = cache->v.mse_bits;
   a.kv_heads = cache->kv_heads;
   a.capacity = cache->capacity;

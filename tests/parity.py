@@ -33,20 +33,31 @@ def check_codes(g_idx, enc, cb, what="codes"):
     return flips.any(axis=1)
 
 
-def check_key_records(words, norms, enc, cb, bits, d):
-    g_idx, g_sig = T.unpack_keys(words, d, bits)
-    cascade = check_codes(g_idx, enc, cb, "key codes")
+def check_key_records(words, norms, enc, cb, bits, d, qjl=True):
+    """Key records of any variant: MSE-only (qjl False: codes and ||k||) and
+    pure QJL (bits 0, cb None: signs and both norms) included."""
+    norms = np.asarray(norms).reshape(words.shape[0], 1 + int(qjl))
+    g_idx, g_sig = T.unpack_keys(words, d, bits, qjl)
+    if bits > 0:
+        cascade = check_codes(g_idx, enc, cb, "key codes")
+    else:
+        assert not g_idx.any()
+        cascade = np.zeros(words.shape[0], dtype=bool)
     live = ~cascade
-    sflip = (g_sig != enc.sigma) & live[:, None]
-    if sflip.any():
-        bad = sflip & ~(np.abs(enc.z) < BAND)
-        assert not bad.any(), f"sign mismatches outside the band: {int(bad.sum())}"
-    assert sflip.sum() <= MAX_FRAC * g_sig.size
+    nsflip = 0
+    if qjl:
+        sflip = (g_sig != enc.sigma) & live[:, None]
+        if sflip.any():
+            bad = sflip & ~(np.abs(enc.z) < BAND)
+            assert not bad.any(), f"sign mismatches outside the band: {int(bad.sum())}"
+        assert sflip.sum() <= MAX_FRAC * g_sig.size
+        nsflip = int(sflip.sum())
     n_ref = enc.norm
     assert np.all(np.abs(norms[:, 0] - n_ref) <= 2e-6 * n_ref + 1e-30), "||k|| mismatch"
-    rr = enc.rho[live]
-    assert np.all(np.abs(norms[live, 1] - rr) <= 2e-5 * rr + 1e-7), "||r|| mismatch"
-    return int(cascade.sum()), int(sflip.sum())
+    if qjl:
+        rr = enc.rho[live]
+        assert np.all(np.abs(norms[live, 1] - rr) <= 2e-5 * rr + 1e-7), "||r|| mismatch"
+    return int(cascade.sum()), nsflip
 
 
 def check_value_records(words, norms, enc, cb, bits, d, n):
