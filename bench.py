@@ -29,8 +29,6 @@ import numpy as np  # noqa: E402
 METRIC = "attention-score keys/s over packed KV (% HBM peak); quantize vectors/s"
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
-KEY_B4 = 72   # bytes per key record at d=128, b=4 (48 code + 16 sign + 8 norm bytes)
-KEY_B3 = 56   # b=3
 VAL_B3 = 52   # 3-bit value record at d=128 (48 code + 4 norm bytes)
 
 
@@ -42,6 +40,8 @@ def parse():
     ap.add_argument("--workload", choices=["serving", "gqa", "single", "search", "tiny"], default="serving")
     ap.add_argument("--data", choices=["outlier", "gaussian"], default="outlier")
     ap.add_argument("--kbits", type=int, default=3, help="MSE bits of the keys (b = kbits + 1)")
+    ap.add_argument("--key-format", choices=["turboquant", "mse", "qjl"], default="turboquant",
+                    help="keys: TurboQuant (codes + QJL signs), MSE-only (codes), or pure QJL (signs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--separate-append", action="store_true",
@@ -141,14 +141,28 @@ def measured_traffic(tag):
 # CPU baseline: the oracle as it stands, on a bounded sample of the workload
 # ---------------------------------------------------------------------------
 
-def oracle_stream_rates(d, L, group, kbits, vbits, seconds, data):
+def key_format(args):
+    """(MSE bits B, QJL flag, text) of the keys the run uses."""
+    if args.key_format == "mse":
+        return args.kbits, False, f"MSE-only keys {args.kbits}-bit"
+    if args.key_format == "qjl":
+        return 0, True, "pure QJL keys (1 sign bit)"
+    return args.kbits, True, f"keys b={args.kbits + 1}"
+
+
+def key_record_bytes(d, B, qjl):
+    return (d // 32) * (B + int(qjl)) * 4 + 4 * (1 + int(qjl))
+
+
+def oracle_stream_rates(d, L, group, kbits, vbits, seconds, data, kqjl=True):
     """Encode L K + L V vectors of whole streams and run their decode for
     `group` query heads, until `seconds` of CPU work; returns rates."""
     import synth
     from oracle import turboquant as T
     Pi = T.rotation_from_gaussian(synth.gaussian_matrix(0, synth.TAG_ROTATION, d, d))
     S = T.sketch_from_gaussian(synth.gaussian_matrix(0, synth.TAG_SKETCH, d, d))
-    cbk, cbv = T.codebook(d, kbits), T.codebook(d, vbits)
+    cbk = T.codebook(d, kbits) if kbits > 0 else None
+    cbv = T.codebook(d, vbits)
     t_enc = t_dec = 0.0
     n_enc = n_dec = streams = 0
     t_start = time.perf_counter()
@@ -161,10 +175,10 @@ def oracle_stream_rates(d, L, group, kbits, vbits, seconds, data):
             V = synth.gaussian(0, (streams, 92), (L, d), "bf16")
         Q = synth.outlier_kv(0, (streams, 93), synth.TAG_SCALES_K, (group, d))
         t0 = time.perf_counter()
-        keys = T.pack_keys(T.encode(K, Pi, cbk, S), kbits)
+        keys = T.pack_keys(T.encode(K, Pi, cbk, S if kqjl else None), kbits, kqjl)
         vals = T.pack_values(T.encode(V, Pi, cbv), vbits)
         t1 = time.perf_counter()
-        T.attention_decode(Q, Pi, S, cbk, cbv, keys, vals, L, 1 / math.sqrt(d))
+        T.attention_decode(Q, Pi, S, cbk, cbv, keys, vals, L, 1 / math.sqrt(d), kqjl)
         t2 = time.perf_counter()
         t_enc += t1 - t0
         t_dec += t2 - t1
@@ -186,7 +200,8 @@ def kv_inputs(torch, synth, args, shape, tags, scale_tag):
 
 def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text):
     """Prefill quantize of B x H x L K/V, then NS x (append + decode)."""
-    d, kbits, vbits = 128, args.kbits, 3
+    d, vbits = 128, 3
+    kbits, kqjl, _ = key_format(args)
     cap = ((L + NS + 31) // 32) * 32
     ctx = tq.Context(d, 0)
     K = kv_inputs(torch, synth, args, (B, H, L, d), (3, synth.TAG_KEYS), synth.TAG_SCALES_K)
@@ -194,7 +209,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     KA = kv_inputs(torch, synth, args, (max(NS, 1), B, H, d), (3, synth.TAG_APPEND_K), synth.TAG_SCALES_K)
     VA = kv_inputs(torch, synth, args, (max(NS, 1), B, H, d), (3, synth.TAG_APPEND_V), synth.TAG_SCALES_V)
     QS = kv_inputs(torch, synth, args, (max(NS, 1), B, Hq, d), (3, synth.TAG_QUERIES), synth.TAG_SCALES_K)
-    cache = tq.KVCache(B, H, cap, d, kbits, vbits)
+    cache = tq.KVCache(B, H, cap, d, kbits, vbits, key_qjl=kqjl)
     kwork = torch.empty(tq.quantize_ws_bytes(ctx, B * H, L, True), dtype=torch.uint8, device="cuda")
     cache.host_max_len = cap
     fused = NS > 0 and not args.separate_append
@@ -257,14 +272,15 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     step(True)
     torch.cuda.synchronize()
     keys_per_step = sum(B * H * (L + (i + 1 if NS > 0 else 0)) for i in range(n_dec))
-    rec_bytes = (KEY_B4 if kbits == 3 else KEY_B3 if kbits == 2 else (d // 32) * (kbits + 1) * 4 + 8) + VAL_B3
+    rec_bytes = key_record_bytes(d, kbits, kqjl) + VAL_B3
     dec_ms = np.array([ms(e) for e, _, _ in dec_events])
     kern_ms = np.array([ms(k) for _, k, _ in dec_events])
     dec_bytes = np.array([B * H * n * rec_bytes for _, _, n in dec_events], dtype=np.float64)
     avg_ms = float(dec_ms.mean())
     kern_avg_ms = float(kern_ms.mean())
     achieved = float(dec_bytes.mean()) / (kern_avg_ms / 1e3) / 1e9
-    traffic = measured_traffic(f"decode_kernel_{name}")
+    fmt_tag = "" if (args.key_format == "turboquant" and args.kbits == 3) else f"_{args.key_format}{kbits}"
+    traffic = measured_traffic(f"decode_kernel_{name}{fmt_tag}")
     ceiling = read_ceiling(torch, tq)
     vectors = 2 * B * H * L
     res = {
@@ -273,14 +289,15 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         "scaling": "weak", "vs_baseline": None, "dtype": "f32+fp6/fp4/i8 exact-digit MFMA",
         "data": f"synthetic ({args.data}-channel bf16 K/V, seeded)",
         "config": {"workload": cfg_text, "batch": B, "context": L, "decode_steps": NS, "kv_heads": H,
-                   "q_heads": Hq, "head_dim": d, "key_bits": kbits + 1, "value_bits": vbits,
+                   "q_heads": Hq, "head_dim": d, "key_bits": kbits + int(kqjl), "key_format": args.key_format,
+                   "value_bits": vbits,
                    "parallelism": "none (1 GPU)"},
         "quantize_vectors_per_s": vectors / (prefill_ms / 1e3), "prefill_ms": prefill_ms,
         "decode_keys_per_s": float(B * H * sum(n for _, _, n in dec_events) / (dec_ms.sum() / 1e3)),
         "decode_call_ms": avg_ms, "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": f"decode_kernel<{kbits},{vbits}> (score/attention over the packed cache)",
+                     "kernel": f"decode_kernel<{kbits},{vbits},{str(kqjl).lower()}> (score/attention over the packed cache)",
                      "algorithmic_bytes_per_launch": float(dec_bytes.mean()), "avg_launch_ms": kern_avg_ms,
                      "bytes_per_kv_token": rec_bytes,
                      "call": ("tq_decode_step: decode_prep_kernel (query prep + append), decode_kernel, "
@@ -295,7 +312,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     }
     if not args.no_cpu_baseline:
         enc_rate, dec_rate, streams, secs = oracle_stream_rates(d, min(L, 8192), Hq // H, kbits, vbits,
-                                                               args.cpu_seconds, args.data)
+                                                               args.cpu_seconds, args.data, kqjl)
         step_s = vectors / enc_rate + keys_per_step / dec_rate
         res["cpu_baseline"] = {
             "value": keys_per_step / step_s, "unit": "keys/s", "cores": threads_used(), "kind": "oracle",
@@ -422,11 +439,11 @@ def main():
     if args.workload == "serving":
         res = run_decode_workload(args, torch, tq, synth, 64, 8, 32, 8192, 128, "serving",
                                   "batched_serving_step: 64 seq x 8192 ctx, 8 KV heads, 32 q heads, d=128, "
-                                  f"keys b={args.kbits + 1}, values 3-bit, prefill quantize + 128 x (append + decode)")
+                                  f"{key_format(args)[2]}, values 3-bit, prefill quantize + 128 x (append + decode)")
     elif args.workload == "gqa":
         res = run_decode_workload(args, torch, tq, synth, 4, 8, 32, 131072, 0, "gqa",
                                   "gqa_layer: batch 4 x 131072 ctx, 8 KV heads, 32 q heads, d=128, "
-                                  f"keys b={args.kbits + 1}, values 3-bit, prefill quantize + 1 decode")
+                                  f"{key_format(args)[2]}, values 3-bit, prefill quantize + 1 decode")
     elif args.workload == "single":
         res = run_decode_workload(args, torch, tq, synth, 1, 1, 1, 32768, 0, "single",
                                   "single_head_decode: 32768 ctx, d=128, keys b=4, values 3-bit, quantize + 1 decode")
