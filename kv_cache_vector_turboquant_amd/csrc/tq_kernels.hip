@@ -1534,18 +1534,18 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   // 1-D grid of nchunks x (streams x head groups) work-groups. Work-groups are
   // dealt to the 8 XCDs round-robin by id; when the stream count is a multiple
-  // of 8, id -> (stream, chunk) keeps every chunk of a stream on one XCD, so its
-  // query fragments are fetched into one L2 only. Chunks go out in chunk order
-  // (every stream's first chunk, then the second, ...), so the short last
-  // chunks are the last work-groups of the launch and fill its tail.
+  // of 8, id -> (stream, chunk) keeps every chunk of a stream on one XCD and
+  // close together in time, so its query fragments are fetched into one L2 once
+  // (chunk-major order measured 1.085x the algorithmic bytes: the fragments were
+  // evicted between a stream's chunks).
   const int nsg = a.streams_hg;
   int c, sg;
   {
     const int id = blockIdx.x;
     if ((nsg & 7) == 0) {
-      const int k = id >> 3, nsg8 = nsg >> 3;
-      c = k / nsg8;
-      sg = (k % nsg8) * 8 + (id & 7);
+      const int k = id >> 3;
+      c = k % a.nchunks;
+      sg = (k / a.nchunks) * 8 + (id & 7);
     } else {
       c = id % a.nchunks;
       sg = id / a.nchunks;
