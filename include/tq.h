@@ -187,6 +187,24 @@ tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const
                               int32_t q_heads, float scale, float *d_out, void *d_ws, size_t ws_bytes,
                               void *stream);
 
+/* Attention of many query positions per sequence over the packed cache (the
+ * cache part of chunked prefill; [gemilab] Attention機構 with the estimator
+ * of [ebisuda] 第2段階, as tq_attention_decode): for every sequence b, query
+ * position i < n_q and query head h, out[b][i][h] = sum_t p_t v_hat_t with
+ * p = softmax(scale * s_t) over the visible tokens t: t < d_seq_len[b], and
+ * with causal != 0 only t < d_seq_len[b] - n_q + i + 1 (the chunk's own
+ * tokens already appended, each position sees itself and what precedes it).
+ * A query with no visible token gets a zero output.
+ * d_q: [batch][n_q][q_heads][d]; d_out: fp32 [batch][n_q][q_heads][d]. q_heads
+ * a multiple of kv_heads. Same kernels as decode, with n_q * group virtual
+ * heads per KV head. d_ws: workspace of tq_attention_prefill_ws_bytes() bytes.
+ * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d != 128, group > 16),
+ * TQ_ERR_CAPACITY (workspace), TQ_ERR_HIP. */
+size_t tq_attention_prefill_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t n_q, int32_t q_heads);
+tq_status tq_attention_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_q, tq_dtype dtype,
+                               int32_t n_q, int32_t q_heads, int32_t causal, float scale, float *d_out, void *d_ws,
+                               size_t ws_bytes, void *stream);
+
 /* Fused serving step: the same result as tq_append_token(d_k, d_v) followed by
  * tq_attention_decode(d_q) on the same stream (the new token is attended),
  * in three launches instead of five: the query preparation encodes the new

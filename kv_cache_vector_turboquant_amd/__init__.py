@@ -84,6 +84,9 @@ _sig("tq_decode_step", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_
                                 _c_vp, _c_sz, _c_vp])
 _sig("tq_attention_decode", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp,
                                      _c_sz, _c_vp])
+_sig("tq_attention_prefill_ws_bytes", _c_sz, [_c_vp, ctypes.POINTER(CCache), _c_i32, _c_i32])
+_sig("tq_attention_prefill", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                                      _c_vp, _c_vp, _c_sz, _c_vp])
 _sig("tq_time_next_decode", _c_i32, [_c_vp, _c_vp])
 _sig("tq_read_probe", _c_i32, [_c_vp, _c_sz, _c_i32, _c_vp, _c_vp])
 _sig("tq_scores_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64, _c_i32, _c_i32])
@@ -93,7 +96,8 @@ _sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked)
 EXPORTED_SYMBOLS = [
     "tq_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
     "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_append_token", "tq_attention_decode_ws_bytes",
-    "tq_attention_decode", "tq_decode_step_ws_bytes", "tq_decode_step", "tq_time_next_decode", "tq_read_probe",
+    "tq_attention_decode", "tq_attention_prefill_ws_bytes", "tq_attention_prefill", "tq_decode_step_ws_bytes",
+    "tq_decode_step", "tq_time_next_decode", "tq_read_probe",
     "tq_scores_ws_bytes", "tq_scores", "tq_last_error",
 ]
 
@@ -344,6 +348,23 @@ class KVCache:
         self.seq_len.fill_(T)
         self.host_max_len = T
 
+    def extend(self, ctx: Context, k, v):
+        """k, v: [batch, kv_heads, tokens, d] contiguous: a chunk of new tokens
+        written after the current contents. Every sequence must hold
+        host_max_len tokens, a multiple of 32 (value records are written in
+        whole 32-token blocks); all lengths grow by `tokens`."""
+        B, H, T, d = k.shape
+        L0 = self.host_max_len
+        assert (B, H) == (self.batch, self.kv_heads) and d == self.d and L0 + T <= self.capacity
+        assert L0 % 32 == 0, "extend writes after a multiple of 32 tokens"
+        assert k.is_contiguous() and v.is_contiguous()
+        quantize_kv(ctx, k.reshape(B * H, T, d), self.k, n_streams=B * H, n_tokens=T, x_stream_stride=k.stride(1),
+                    x_token_stride=k.stride(2), out_stream_stride=self.capacity, out_offset=L0)
+        quantize_kv(ctx, v.reshape(B * H, T, d), self.v, n_streams=B * H, n_tokens=T, x_stream_stride=v.stride(1),
+                    x_token_stride=v.stride(2), out_stream_stride=self.capacity, out_offset=L0)
+        self.seq_len.fill_(L0 + T)
+        self.host_max_len = L0 + T
+
     def append(self, ctx: Context, k, v):
         """k, v: [batch, kv_heads, d] contiguous, one new token per sequence."""
         assert k.is_contiguous() and v.is_contiguous() and k.dtype == v.dtype
@@ -371,6 +392,30 @@ class KVCache:
         cc = self.c()
         _check(_lib.tq_attention_decode(ctx.handle, ctypes.byref(cc), q.data_ptr(), _dtype_code(q), Hq,
                                         float(scale), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr()))
+        return out
+
+    def prefill_ws_bytes(self, ctx: Context, n_q: int, q_heads: int) -> int:
+        cc = self.c()
+        return int(_lib.tq_attention_prefill_ws_bytes(ctx.handle, ctypes.byref(cc), n_q, q_heads))
+
+    def attend(self, ctx: Context, q, causal: bool = True, scale: float | None = None, out=None, ws=None):
+        """Many query positions per sequence over the cache: q [batch, n_q, q_heads, d]
+        contiguous; causal: position i sees t < seq_len - n_q + i + 1. Returns fp32
+        [batch, n_q, q_heads, d]."""
+        torch = _torch()
+        assert q.is_contiguous() and q.dim() == 4
+        B, NQ, Hq, d = q.shape
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        if out is None:
+            out = torch.empty((B, NQ, Hq, d), dtype=torch.float32, device=q.device)
+        need = self.prefill_ws_bytes(ctx, NQ, Hq)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+        cc = self.c()
+        _check(_lib.tq_attention_prefill(ctx.handle, ctypes.byref(cc), q.data_ptr(), _dtype_code(q), NQ, Hq,
+                                         1 if causal else 0, float(scale), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                         _stream_ptr()))
         return out
 
     def decode_step_ws_bytes(self, ctx: Context, q_heads: int) -> int:

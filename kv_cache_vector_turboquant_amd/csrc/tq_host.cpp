@@ -558,6 +558,46 @@ tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const
   return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 
+size_t tq_attention_prefill_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t n_q, int32_t q_heads) {
+  if (!ctx || !cache || n_q <= 0 || q_heads <= 0 || cache->kv_heads <= 0 || (q_heads % cache->kv_heads) != 0) return 0;
+  return decode_ws_bytes(ctx, cache, q_heads, nullptr, nullptr, n_q);
+}
+
+tq_status tq_attention_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_q, tq_dtype dtype,
+                               int32_t n_q, int32_t q_heads, int32_t causal, float scale, float *d_out, void *d_ws,
+                               size_t ws_bytes, void *stream) {
+  const char *fn = "tq_attention_prefill";
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_attention_prefill: NULL ctx");
+  tq_status s = check_cache(ctx, cache, fn);
+  if (s != TQ_OK) return s;
+  if (!d_q || !d_out) return fail(TQ_ERR_ARG, "tq_attention_prefill: NULL query or output");
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_attention_prefill: dtype must be TQ_F32 or TQ_BF16");
+  if (n_q <= 0) return fail(TQ_ERR_ARG, "tq_attention_prefill: n_q must be positive");
+  if (causal != 0 && causal != 1) return fail(TQ_ERR_ARG, "tq_attention_prefill: causal must be 0 or 1");
+  if (q_heads <= 0 || (q_heads % cache->kv_heads) != 0)
+    return fail(TQ_ERR_ARG, "tq_attention_prefill: q_heads must be a positive multiple of kv_heads");
+  if (q_heads / cache->kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_attention_prefill: at most 16 query heads per KV head");
+  if ((int64_t)n_q * (q_heads / cache->kv_heads) > (1 << 20))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_attention_prefill: at most 2^20 query heads per KV head");
+  if (ctx->d != 128) return fail(TQ_ERR_UNSUPPORTED, "tq_attention_prefill: d must be 128");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_ARG, "tq_attention_prefill: scale must be finite");
+  {
+    // one 256-thread work-group per (chunk, KV stream, group of 4 virtual heads):
+    // the 1-D grid must stay below 2^32 work-items
+    int chunk = 0, nchunks = 0;
+    decode_ws_bytes(ctx, cache, q_heads, &chunk, &nchunks, n_q);
+    const int64_t units = (int64_t)cache->batch * cache->kv_heads * (((int64_t)n_q * (q_heads / cache->kv_heads) + 3) / 4);
+    if (units * nchunks >= ((int64_t)1 << 24))
+      return fail(TQ_ERR_UNSUPPORTED, "tq_attention_prefill: batch x query positions x context too large for one launch");
+  }
+  size_t need = tq_attention_prefill_ws_bytes(ctx, cache, n_q, q_heads);
+  if (!d_ws || ws_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_attention_prefill: workspace smaller than tq_attention_prefill_ws_bytes()");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  hipError_t e = launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream,
+                               nullptr, nullptr, nullptr, nullptr, n_q, causal);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
+}
+
 size_t tq_decode_step_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads) {
   if (!ctx || !cache || q_heads <= 0 || cache->kv_heads <= 0 || (q_heads % cache->kv_heads) != 0) return 0;
   tq_kv_cache after = *cache;

@@ -60,13 +60,16 @@ hipError_t launch_quantize_values(const tq_ctx *ctx, const void *x, int is_bf16,
 hipError_t launch_append(const tq_ctx *ctx, const tq_kv_cache *cache, const void *k, const void *v, int is_bf16,
                          hipStream_t st);
 size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int *chunk_out,
-                       int *nchunks_out);
+                       int *nchunks_out, int n_q = 1);
+// n_q query positions per sequence (q: [batch][n_q][q_heads][d], out likewise);
+// causal: position i attends to t < seq_len - n_q + i + 1.
 // With k_new / v_new non-NULL (fused step) the new token of every stream is
 // appended first and the sequence lengths advance by one. Non-NULL ev0 / ev1 are
 // recorded on st right before / after the score/attention kernel.
 hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
                          float scale, float *out, void *ws, hipStream_t st, const void *k_new = nullptr,
-                         const void *v_new = nullptr, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                         const void *v_new = nullptr, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
+                         int n_q = 1, int causal = 0);
 hipError_t launch_read_probe(const void *src, size_t bytes, int grid, uint32_t *sink, hipStream_t st);
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores);
 hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_packed *keys,

@@ -1045,8 +1045,14 @@ struct DecodeArgs {
   int kqjl;              // keys carry the QJL sign word and |r|
   int kv_heads, capacity, q_heads, group, hgroups;
   int chunk, nchunks;
-  int streams_hg;        // streams x head groups (decode grid = nchunks x streams_hg)
+  int streams_hg;        // KV streams x head groups (decode grid = nchunks x streams_hg)
   int batch;
+  // many queries per KV head (prefill): query position i of sequence b and head j
+  // of a KV head's group form virtual head i * group + j; head groups are groups
+  // of 4 virtual heads. Decode is n_q = 1.
+  int n_q, causal;       // causal: position i attends to t < seq_len - n_q + i + 1
+  int vgroup;            // n_q * group virtual heads per KV stream
+  int kv_streams;        // batch * kv_heads
   float scale_log2;      // softmax scale * log2(e)
   float qjl_scale;
   const DeviceTables *tables;
@@ -1269,8 +1275,8 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
     sgu[u2] = 2 * (int)blockIdx.x + u2;
     const int hg = sgu[u2] % a.hgroups, stream = sgu[u2] / a.hgroups;
     bu[u2] = stream / a.kv_heads;
-    h0u[u2] = (stream % a.kv_heads) * a.group + hg * 4;
-    nhu[u2] = sgu[u2] < a.streams_hg ? min(4, a.group - hg * 4) : 0;
+    h0u[u2] = hg * 4;  // first virtual head of the unit
+    nhu[u2] = sgu[u2] < a.streams_hg ? min(4, a.vgroup - hg * 4) : 0;
     // fused step: the sequence's length after the append, for the decode launch
     if (APPEND && tid == 0 && nhu[u2] > 0 && stream % a.kv_heads == 0 && hg == 0)
       a.wlen[bu[u2]] = min(a.seq_len[bu[u2]] + 1, a.capacity);
@@ -1285,8 +1291,12 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int e = i * 512 + tid, hh = e >> 7, k = e & (DD - 1), u2 = hh >> 2;
-    const QT *q = reinterpret_cast<const QT *>(a.q) + ((int64_t)bu[u2] * a.q_heads + h0u[u2]) * DD;
-    ql.qk[k][hh] = (hh & 3) < nhu[u2] ? qload(q, (int64_t)(hh & 3) * DD + k) : 0.f;
+    // virtual head vh = position qi x group + head qj of the KV head's group
+    const int vh = h0u[u2] + (hh & 3), qi = vh / a.group, qj = vh - qi * a.group;
+    const int kvh = (sgu[u2] / a.hgroups) % a.kv_heads;
+    const QT *q = reinterpret_cast<const QT *>(a.q) +
+                  (((int64_t)bu[u2] * a.n_q + qi) * a.q_heads + kvh * a.group + qj) * DD;
+    ql.qk[k][hh] = (hh & 3) < nhu[u2] ? qload(q, k) : 0.f;
   }
   __syncthreads();
   // two 16-byte LDS broadcasts give the eight query entries of a k
@@ -1443,14 +1453,13 @@ __global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int sg = blockIdx.x;
   const int hg = sg % a.hgroups, stream = sg / a.hgroups;
-  const int b = stream / a.kv_heads;
-  const int h0 = (stream % a.kv_heads) * a.group + hg * 4;
-  const int nh = min(4, a.group - hg * 4);
+  const int b = stream / a.kv_heads, kvh = stream % a.kv_heads;
+  const int nh = min(4, a.vgroup - hg * 4);
   // fused step: the appended token is now part of every stream of sequence b
   if (a.len_inc && tid == 0 && hg == 0 && stream % a.kv_heads == 0 && a.len_inc[b] < a.capacity) a.len_inc[b] += 1;
   const int cg = tid >> 8, hh = (tid >> 6) & 3;  // chunk group, head (one wave per pair)
   const int nc = a.nchunks;
-  const float *p = a.partial + ((int64_t)b * a.q_heads + h0 + min(hh, nh - 1)) * nc * (DD + 2);
+  const float *p = a.partial + ((int64_t)stream * a.vgroup + hg * 4 + min(hh, nh - 1)) * nc * (DD + 2);
   // global max of the chunk maxima of this head
   float m = -INFINITY;
   for (int c = cg * 64 + lane; c < nc; c += MG * 64) m = fmaxf(m, p[(int64_t)c * (DD + 2) + DD]);
@@ -1510,7 +1519,9 @@ __global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
       float o = 0.f;
 #pragma unroll
       for (int kg = 0; kg < 8; ++kg) o += pk[kg][h][j];
-      a.out[((int64_t)b * a.q_heads + h0 + h) * DD + j] = o;
+      // virtual head -> (query position qi, head qj of the group)
+      const int vh = hg * 4 + h, qi = vh / a.group, qj = vh - qi * a.group;
+      a.out[(((int64_t)b * a.n_q + qi) * a.q_heads + kvh * a.group + qj) * DD + j] = o;
     }
   }
 }
@@ -1538,28 +1549,41 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   // close together in time, so its query fragments are fetched into one L2 once
   // (chunk-major order measured 1.085x the algorithmic bytes: the fragments were
   // evicted between a stream's chunks).
-  const int nsg = a.streams_hg;
-  int c, sg;
+  // Many query heads per KV stream: the head groups of one (stream, chunk) are
+  // consecutive on one XCD, so its records are read from HBM once and reused
+  // from that L2.
+  const int HG = a.hgroups;
+  int c, hg, stream;
   {
     const int id = blockIdx.x;
-    if ((nsg & 7) == 0) {
-      const int k = id >> 3;
-      c = k % a.nchunks;
-      sg = (k / a.nchunks) * 8 + (id & 7);
+    if ((a.kv_streams & 7) == 0) {
+      const int k = id >> 3, k2 = k / HG;
+      hg = k - k2 * HG;
+      c = k2 % a.nchunks;
+      stream = (k2 / a.nchunks) * 8 + (id & 7);
     } else {
-      c = id % a.nchunks;
-      sg = id / a.nchunks;
+      const int k2 = id / HG;
+      hg = id - k2 * HG;
+      c = k2 % a.nchunks;
+      stream = k2 / a.nchunks;
     }
   }
-  const int hg = sg % a.hgroups, stream = sg / a.hgroups;
+  const int sg = stream * HG + hg;
   const int b = stream / a.kv_heads;
-  const int nh = min(4, a.group - hg * 4);
+  const int nh = min(4, a.vgroup - hg * 4);
   const int len = a.wlen ? a.wlen[b] : a.seq_len[b];
   const int t0 = c * a.chunk;
   const int t1 = min(len, t0 + a.chunk);
-  const int h0 = (stream % a.kv_heads) * a.group + hg * 4;
+  // visible tokens of virtual head hh (chunk-relative; causal: up to its position)
+  auto vis = [&](int hh) {
+    const int qi = (hg * 4 + hh) / a.group;
+    const int lim = a.causal ? len - a.n_q + qi + 1 : len;
+    return min(max(lim - t0, 0), t1 - t0);
+  };
   float *part_base = a.partial;
-  auto part = [&](int hh) { return part_base + (((int64_t)b * a.q_heads + h0 + hh) * a.nchunks + c) * (DD + 2); };
+  auto part = [&](int hh) {
+    return part_base + (((int64_t)stream * a.vgroup + hg * 4 + hh) * a.nchunks + c) * (DD + 2);
+  };
 
   if (t0 >= t1) {
     for (int e = tid; e < nh * (DD + 2); e += 256) {
@@ -1646,6 +1670,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     for (int mi = 0; mi < KM; ++mi) wkr[mi] = wk[mi] * sr;
     float vmx = 0.f, lmx = -INFINITY;
     const int ntile = (n + 15) >> 4;
+    const int visG = vis(G);  // tokens of the chunk this lane's virtual head sees
     auto kcompute = [&](int base, const KBuf &cur) {
       (void)base;
 #pragma unroll
@@ -1675,6 +1700,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         } else {
           s = cur.kn[u].x * code;
         }
+        s = tc < visG ? s : -INFINITY;  // causal mask of this lane's virtual head
         lg[G * a.chunk + tc] = s;
         lmx = fmaxf(lmx, s);
         vnl[tc] = cur.vn[u];
@@ -1748,11 +1774,12 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       const float *lgw = lg + wave * a.chunk + lane;
       const float *vnw = vnl + lane;
       const int nit = (n + 63) >> 6;
+      const int nw = vis(wave);  // tokens this head sees (all n without the causal mask)
       for (int i0 = 0; i0 < nit; i0 += 4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = i0 + j;
-          const bool live = lane + 64 * i < n;
+          const bool live = lane + 64 * i < nw;
           const float e = __builtin_amdgcn_exp2f(lgw[64 * i] - m);  // <= 1; tiny values round to W = 0
           l += live ? e : 0.f;
           const int W = live ? (int)rintf(e * vnw[64 * i] * wq) : 0;
@@ -1843,9 +1870,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 }
 
 size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int *chunk_out,
-                       int *nchunks_out) {
+                       int *nchunks_out, int n_q) {
   const int group = q_heads / cache->kv_heads;
-  const int hgroups = (group + 3) / 4;
+  const int hgroups = (group * n_q + 3) / 4;
   const int maxlen = cache->host_max_len > 0 ? cache->host_max_len : cache->capacity;
   const int64_t streams = (int64_t)cache->batch * cache->kv_heads * hgroups;
   int chunk = 1024;
@@ -1858,7 +1885,7 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
   b = (b + 255) & ~(size_t)255;
   b += (size_t)streams * 4 * QC * sizeof(float);  // qconst
   b = (b + 255) & ~(size_t)255;
-  b += (size_t)cache->batch * q_heads * nchunks * (DD + 2) * sizeof(float);  // partials
+  b += (size_t)cache->batch * q_heads * n_q * nchunks * (DD + 2) * sizeof(float);  // partials
   b = (b + 255) & ~(size_t)255;
   b += (size_t)cache->batch * sizeof(int32_t);  // fused step: lengths after the append
   (void)ctx;
@@ -1873,9 +1900,9 @@ static hipError_t launch_decode_kv(const DecodeArgs &a, dim3 grid, size_t shm, h
 
 hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
                          float scale, float *out, void *ws, hipStream_t st, const void *k_new, const void *v_new,
-                         hipEvent_t ev0, hipEvent_t ev1) {
+                         hipEvent_t ev0, hipEvent_t ev1, int n_q, int causal) {
   int chunk = 0, nchunks = 0;
-  decode_ws_bytes(ctx, cache, q_heads, &chunk, &nchunks);
+  decode_ws_bytes(ctx, cache, q_heads, &chunk, &nchunks, n_q);
   DecodeArgs a = {};
   a.kbits = cache->k.bits;
   a.knorm = cache->k.norms;
@@ -1889,7 +1916,11 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.capacity = cache->capacity;
   a.q_heads = q_heads;
   a.group = q_heads / cache->kv_heads;
-  a.hgroups = (a.group + 3) / 4;
+  a.n_q = n_q;
+  a.causal = causal;
+  a.vgroup = a.group * n_q;
+  a.kv_streams = cache->batch * cache->kv_heads;
+  a.hgroups = (a.vgroup + 3) / 4;
   a.chunk = chunk;
   a.nchunks = nchunks;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -1906,7 +1937,7 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.qconst = (float *)p;
   p += (((size_t)streams * 4 * QC * sizeof(float)) + 255) & ~(size_t)255;
   a.partial = (float *)p;
-  p += (((size_t)cache->batch * q_heads * nchunks * (DD + 2) * sizeof(float)) + 255) & ~(size_t)255;
+  p += (((size_t)cache->batch * q_heads * n_q * nchunks * (DD + 2) * sizeof(float)) + 255) & ~(size_t)255;
   a.out = out;
   const bool step = k_new != nullptr;
   if (step) {

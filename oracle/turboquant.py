@@ -35,7 +35,7 @@ from scipy import special
 __all__ = [
     "rotation_from_gaussian", "sketch_from_gaussian", "coord_density", "coord_cdf",
     "lloyd_max", "Codebook", "codebook", "encode", "Encoded", "query_prep", "qjl_constant",
-    "scores", "scores_from_parts", "dequantize_keys", "attention_decode", "topk",
+    "scores", "scores_from_parts", "dequantize_keys", "attention_decode", "attention_prefill", "topk",
     "recall_at_k", "pack_keys", "unpack_keys", "pack_values", "unpack_values",
     "key_record_bytes", "value_record_bytes",
 ]
@@ -334,6 +334,23 @@ def attention_decode(Qh, Pi, S, cbk: Codebook | None, cbv: Codebook, keys: dict,
     Vrot = values["norms"][:seq_len].astype(np.float64)[:, None] * cbv.centroids.astype(np.float64)[vidx]
     o_rot = p @ Vrot
     return o_rot @ np.asarray(Pi, dtype=np.float64)
+
+
+def attention_prefill(Qpos, Pi, S, cbk: Codebook | None, cbv: Codebook, keys: dict, values: dict, seq_len: int,
+                      scale: float, causal: bool, qjl: bool = True):
+    """Many query positions of one (sequence, KV head) over its packed cache:
+    position i (of n_q) sees tokens t < seq_len, and with `causal` only
+    t < seq_len - n_q + i + 1 (reading: the chunk's own tokens are already in the
+    cache). Qpos: (n_q, g, d). A position that sees no token gets zeros.
+    Returns (n_q, g, d) fp64."""
+    Qpos = np.asarray(Qpos)
+    nq = Qpos.shape[0]
+    out = np.zeros(Qpos.shape, dtype=np.float64)
+    for i in range(nq):
+        lim = min(seq_len - nq + i + 1, seq_len) if causal else seq_len
+        if lim > 0:
+            out[i] = attention_decode(Qpos[i], Pi, S, cbk, cbv, keys, values, lim, scale, qjl)
+    return out
 
 
 def topk(score_row: np.ndarray, k: int) -> np.ndarray:

@@ -94,6 +94,8 @@ def test_hot_entry_points_reject_null_context():
     c = tq.CCache()
     assert lib.tq_append_token(None, ctypes.byref(c), None, None, 0, None) == tq.TQ_ERR_ARG
     assert lib.tq_attention_decode(None, ctypes.byref(c), None, 0, 4, 1.0, None, None, 0, None) == tq.TQ_ERR_ARG
+    assert lib.tq_attention_prefill(None, ctypes.byref(c), None, 0, 8, 4, 1, 1.0, None, None, 0, None) == tq.TQ_ERR_ARG
+    assert lib.tq_attention_prefill_ws_bytes(None, ctypes.byref(c), 8, 4) == 0
     assert lib.tq_scores(None, None, 0, 1, ctypes.byref(p), None, 10, None, None, None, 0, None) == tq.TQ_ERR_ARG
     assert lib.tq_ctx_destroy(None) == tq.TQ_ERR_ARG
     assert lib.tq_quantize_ws_bytes(None, 1, 1, 1) == 0

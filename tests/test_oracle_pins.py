@@ -434,6 +434,41 @@ def test_attention_matches_textbook_softmax_and_torch():
     assert np.max(np.abs(o - t)) < 1e-10
 
 
+def test_prefill_matches_masked_sdpa():
+    """Oracle prefill = torch's scaled_dot_product_attention (fp64, CPU) over the
+    dense K_hat, V_hat with a boolean mask that lets query i of n_q see the keys
+    t <= L - n_q + i (a lower triangle shifted to the cache's end); without
+    causality every query sees all L keys. The last causal query is the decode."""
+    import torch
+    d, L, g, nq = 128, 53, 2, 9
+    Pi, S = _ctx(d)
+    cbk, cbv = T.codebook(d, 2), T.codebook(d, 3)
+    K = synth.outlier_kv(1, (1,), synth.TAG_SCALES_K, (L, d))
+    V = synth.outlier_kv(1, (2,), synth.TAG_SCALES_V, (L, d))
+    Q = synth.gaussian(1, (3,), (nq, g, d), "bf16")
+    ek, ev = T.encode(K, Pi, cbk, S), T.encode(V, Pi, cbv)
+    keys, vals = T.pack_keys(ek, 2), T.pack_values(ev, 3)
+    scale = 0.1
+    idx, sig = T.unpack_keys(keys["bits"], d, 2)
+    Khat = T.dequantize_keys(Pi, S, cbk, idx, sig, keys["norms"][:, 0], keys["norms"][:, 1])
+    Vhat = vals["norms"].astype(np.float64)[:, None] * (cbv.centroids.astype(np.float64)[ev.idx] @ Pi.astype(np.float64))
+    qt = torch.from_numpy(Q.astype(np.float64)).permute(1, 0, 2).contiguous()      # (g, nq, d)
+    kt = torch.from_numpy(Khat)[None].expand(g, L, d).contiguous()
+    vt = torch.from_numpy(Vhat)[None].expand(g, L, d).contiguous()
+    mask = torch.from_numpy(np.tril(np.ones((nq, L), dtype=bool), k=L - nq))
+    for causal in (True, False):
+        o = T.attention_prefill(Q, Pi, S, cbk, cbv, keys, vals, L, scale, causal)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask if causal else None,
+                                                               scale=scale).permute(1, 0, 2).numpy()
+        assert np.max(np.abs(o - ref)) < 1e-10
+    o = T.attention_prefill(Q, Pi, S, cbk, cbv, keys, vals, L, scale, True)
+    assert np.array_equal(o[-1], T.attention_decode(Q[-1], Pi, S, cbk, cbv, keys, vals, L, scale))
+    # a chunk longer than the cache: the first n_q - L positions see nothing
+    o = T.attention_prefill(synth.gaussian(1, (4,), (L + 3, g, d), "bf16"), Pi, S, cbk, cbv, keys, vals, L, scale,
+                            True)
+    assert np.all(o[:3] == 0) and np.all(np.any(o[3:] != 0, axis=2))
+
+
 def test_split_softmax_merge_equals_single_pass():
     rng = np.random.default_rng(0)
     lg = rng.normal(size=1000) * 4
