@@ -236,7 +236,7 @@ tq_status tq_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t 
                     size_t ws_bytes, void *stream);
 
 /* Kernel timing, a measurement aid. Arms the calling thread so that its next
- * tq_attention_decode or tq_decode_step records start_event on its stream
+ * tq_attention_decode, tq_attention_prefill or tq_decode_step records start_event on its stream
  * right before the score/attention kernel (after the query preparation) and
  * stop_event right after it (before the merge of the chunk partials); that
  * call then disarms the thread. The events are hipEvent_t handles created

@@ -567,6 +567,8 @@ tq_status tq_attention_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, cons
                                int32_t n_q, int32_t q_heads, int32_t causal, float scale, float *d_out, void *d_ws,
                                size_t ws_bytes, void *stream) {
   const char *fn = "tq_attention_prefill";
+  hipEvent_t ev[2];
+  take_decode_events(ev);
   if (!ctx) return fail(TQ_ERR_ARG, "tq_attention_prefill: NULL ctx");
   tq_status s = check_cache(ctx, cache, fn);
   if (s != TQ_OK) return s;
@@ -594,7 +596,7 @@ tq_status tq_attention_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, cons
   if (!d_ws || ws_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_attention_prefill: workspace smaller than tq_attention_prefill_ws_bytes()");
   if ((s = check_device(ctx, fn)) != TQ_OK) return s;
   hipError_t e = launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream,
-                               nullptr, nullptr, nullptr, nullptr, n_q, causal);
+                               nullptr, nullptr, ev[0], ev[1], n_q, causal);
   return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 

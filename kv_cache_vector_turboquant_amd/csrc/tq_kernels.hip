@@ -1631,9 +1631,6 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     // the wave's first key tiles are requested before anything else
     KBuf kb_a, kb_b;
     kload(wave * KTPW, kb_a);
-    // zero the value A fragments (rows of absent heads stay zero)
-    for (int e = tid; e < ngrp * 2 * 64; e += 256) reinterpret_cast<uint4 *>(av)[e] = make_uint4(0, 0, 0, 0);
-
     // ---- phase K: logits of all tokens of the chunk (log2 units) ----
     const uint32_t *qf = a.qfrag + (int64_t)sg * 2 * 2 * 64 * 8;
     auto ldfrag = [&](int T, int ins) {
@@ -1756,7 +1753,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     __syncthreads();
     const float vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     // ---- softmax: wave w owns head w; weights -> fixed-point value digits ----
-    if (wave < nh) {
+    // (the wave of an absent head writes zero weights: every value A byte that
+    // phase V reads is written here, so the fragments need no clearing)
+    {
       const float m = fmaxf(fmaxf(lred[0][wave], lred[1][wave]), fmaxf(lred[2][wave], lred[3][wave]));
       // token t = lane + 64 i: q = t & 7 = lane & 7 is fixed per lane, and so is
       // its weight scale 2^(29 - q) / vmax (negated for q = 7, whose B byte is -128)
@@ -1774,7 +1773,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       const float *lgw = lg + wave * a.chunk + lane;
       const float *vnw = vnl + lane;
       const int nit = (n + 63) >> 6;
-      const int nw = vis(wave);  // tokens this head sees (all n without the causal mask)
+      const int nw = wave < nh ? vis(wave) : 0;  // tokens this head sees (all n without the causal mask)
       for (int i0 = 0; i0 < nit; i0 += 4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
