@@ -1551,21 +1551,29 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   // evicted between a stream's chunks).
   // Many query heads per KV stream: the head groups of one (stream, chunk) are
   // consecutive on one XCD, so its records are read from HBM once and reused
-  // from that L2.
+  // from that L2. The last chunk of every stream (usually partial: a few tokens
+  // past a multiple of the chunk) is dealt after all the others, on the same XCD
+  // as the stream's other chunks, so the launch ends on short work-groups
+  // (measured 5% off a decode call whose streams end 64 tokens past a chunk).
   const int HG = a.hgroups;
   int c, hg, stream;
   {
-    const int id = blockIdx.x;
+    const int id0 = blockIdx.x;
+    const int nf = a.nchunks - 1;  // chunks dealt first; the last chunks go at the end
+    const int F = nf * a.streams_hg;
+    const bool last = id0 >= F;
+    const int id = last ? id0 - F : id0;
+    const int ncs = last ? 1 : nf;
     if ((a.kv_streams & 7) == 0) {
       const int k = id >> 3, k2 = k / HG;
       hg = k - k2 * HG;
-      c = k2 % a.nchunks;
-      stream = (k2 / a.nchunks) * 8 + (id & 7);
+      c = last ? nf : k2 % ncs;
+      stream = (k2 / ncs) * 8 + (id & 7);
     } else {
       const int k2 = id / HG;
       hg = id - k2 * HG;
-      c = k2 % a.nchunks;
-      stream = k2 / a.nchunks;
+      c = last ? nf : k2 % ncs;
+      stream = k2 / ncs;
     }
   }
   const int sg = stream * HG + hg;
