@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--separate-append", action="store_true",
                     help="serving step: tq_append_token then tq_attention_decode instead of tq_decode_step")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode workloads: also capture one whole step in a HIP graph (torch.cuda.graph) and "
+                         "time its replays (graph_ms_per_step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run 5 device-to-device copies of this many MiB (a plain copy kernel of known size, "
                          "the calibration of the rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -313,6 +316,21 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     torch.cuda.synchronize()
     step(True)
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # the whole step captured once; replays start from the captured host state
+        eager_out = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(False)
+        torch.cuda.synchronize()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(out, eager_out))
+        gw = timer(lambda: [g.replay() for _ in range(args.steps)])
+        torch.cuda.synchronize()
+        graph = {"graph_ms_per_step": ms(gw) / args.steps, "graph_replay_matches_eager": same}
     keys_per_step = sum(B * H * (L + (i + 1 if NS > 0 else 0)) for i in range(n_dec))
     rec_bytes = key_record_bytes(d, kbits, kqjl) + VAL_B3
     dec_ms = np.array([ms(e) for e, _, _ in dec_events])
@@ -347,7 +365,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
                    "parallelism": "none (1 GPU)"},
         "quantize_vectors_per_s": vectors / (prefill_ms / 1e3), "prefill_ms": prefill_ms,
         "decode_keys_per_s": float(B * H * sum(n for _, _, n in dec_events) / (dec_ms.sum() / 1e3)),
-        "decode_call_ms": avg_ms, "wall_s_timed": wall, **extra_cold,
+        "decode_call_ms": avg_ms, "wall_s_timed": wall, **extra_cold, **(graph or {}),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": f"decode_kernel<{kbits},{vbits},{str(kqjl).lower()}> (score/attention over the packed cache)",
