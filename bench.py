@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--separate-append", action="store_true",
                     help="serving step: tq_append_token then tq_attention_decode instead of tq_decode_step")
+    ap.add_argument("--page-tokens", type=int, default=0,
+                    help="decode workloads: paged cache with pages of this many tokens (a multiple of 256) in a "
+                         "shuffled pool, instead of the contiguous layout")
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: also capture one whole step in a HIP graph (torch.cuda.graph) and "
                          "time its replays (graph_ms_per_step)")
@@ -254,7 +257,18 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     KA = kv_inputs(torch, synth, args, (max(NS, 1), B, H, d), (3, synth.TAG_APPEND_K), synth.TAG_SCALES_K)
     VA = kv_inputs(torch, synth, args, (max(NS, 1), B, H, d), (3, synth.TAG_APPEND_V), synth.TAG_SCALES_V)
     QS = kv_inputs(torch, synth, args, (max(NS, 1), B, Hq, d), (3, synth.TAG_QUERIES), synth.TAG_SCALES_K)
-    cache = tq.KVCache(B, H, cap, d, kbits, vbits, key_qjl=kqjl)
+    if args.page_tokens:
+        # paged cache: whole pages per sequence, handed out in a shuffled order
+        Pt = args.page_tokens
+        cap = ((L + NS + Pt - 1) // Pt) * Pt
+        cols = cap // Pt
+        g = torch.Generator(device="cpu")
+        g.manual_seed(7)
+        perm = torch.randperm(B * cols + 8, generator=g)[:B * cols].to(torch.int32).view(B, cols).to("cuda")
+        cache = tq.KVCache(B, H, cap, d, kbits, vbits, key_qjl=kqjl, page_tokens=Pt, n_pages=B * cols + 8,
+                           block_table=perm)
+    else:
+        cache = tq.KVCache(B, H, cap, d, kbits, vbits, key_qjl=kqjl)
     kwork = torch.empty(tq.quantize_ws_bytes(ctx, B * H, L, True), dtype=torch.uint8, device="cuda")
     cache.host_max_len = cap
     fused = NS > 0 and not args.separate_append
@@ -266,10 +280,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     n_dec = max(NS, 1)
 
     def prefill():
-        tq.quantize_kv(ctx, K.view(B * H, L, d), cache.k, out_stream_stride=cap, work=kwork)
-        tq.quantize_kv(ctx, V.view(B * H, L, d), cache.v, out_stream_stride=cap)
-        cache.seq_len.fill_(L)
-        cache.host_max_len = L
+        cache.prefill(ctx, K, V, work=kwork)  # tq_cache_write: keys and values of every stream
 
     dec_events = []
     kev = []  # per timed call: events around its score/attention kernel
@@ -361,7 +372,8 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         "data": f"synthetic ({args.data}-channel bf16 K/V, seeded)",
         "config": {"workload": cfg_text, "batch": B, "context": L, "decode_steps": NS, "kv_heads": H,
                    "q_heads": Hq, "head_dim": d, "key_bits": kbits + int(kqjl), "key_format": args.key_format,
-                   "value_bits": vbits,
+                   "value_bits": vbits, "cache_layout": (f"paged, {args.page_tokens}-token pages in a shuffled pool"
+                                                         if args.page_tokens else "contiguous"),
                    "parallelism": "none (1 GPU)"},
         "quantize_vectors_per_s": vectors / (prefill_ms / 1e3), "prefill_ms": prefill_ms,
         "decode_keys_per_s": float(B * H * sum(n for _, _, n in dec_events) / (dec_ms.sum() / 1e3)),

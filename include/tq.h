@@ -150,7 +150,19 @@ tq_status tq_quantize_kv(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int
                          int64_t out_stream_stride, int64_t out_offset, void *d_work, size_t work_bytes,
                          void *stream);
 
-/* KV cache: records of stream (b, h) at [(b*kv_heads + h)*capacity + t].
+/* KV cache. Contiguous layout (d_block_table NULL): the record of token t of
+ * stream (b, h) is [(b*kv_heads + h)*capacity + t]; k.n, v.n >=
+ * batch*kv_heads*capacity. Paged layout (d_block_table non-NULL): the arrays
+ * are a pool of n_pages = k.n / (kv_heads*page_tokens) pages of page_tokens
+ * tokens per KV head, and token t of stream (b, h) is record
+ * (page*kv_heads + h)*page_tokens + t % page_tokens with
+ * page = d_block_table[b*(capacity/page_tokens) + t/page_tokens] (device
+ * int32, [batch][capacity/page_tokens], caller-owned; sequences may share or
+ * reorder pages freely). page_tokens is a positive multiple of 256 dividing
+ * capacity; k.n = v.n = a multiple of kv_heads*page_tokens. A table entry
+ * outside [0, n_pages) is a caller error: it is clamped, so no access leaves
+ * the arrays, but the data read or written is then another page's. Pages of
+ * 1024 tokens or more keep the decode kernel at its full chunk size.
  * capacity is a multiple of 32. d_seq_len[b] is the number of valid tokens of
  * every KV head of sequence b. host_max_len is an upper bound of all
  * d_seq_len kept by the caller after prefill and advanced by
@@ -160,7 +172,24 @@ typedef struct {
   int32_t batch, kv_heads, capacity;
   int32_t *d_seq_len;
   int32_t host_max_len;
+  const int32_t *d_block_table; /* NULL: contiguous layout */
+  int32_t page_tokens;          /* paged layout only */
 } tq_kv_cache;
+
+/* Write n_tokens tokens of every stream into the cache (contiguous or paged)
+ * at positions pos0 .. pos0 + n_tokens - 1, keys and values
+ * ([ebisuda] 第1段階 and 第2段階, as tq_quantize_kv): K/V element (s, t, j) of
+ * stream s = b*kv_heads + h is d_k / d_v[s*x_stream_stride + t*x_token_stride
+ * + j] (strides in elements, both inputs alike). pos0 is a multiple of 32
+ * (value records are written in whole 32-token blocks; bits of positions past
+ * the last token in its block are 0). d_seq_len and host_max_len are not
+ * changed: the caller sets them. d_work: tq_quantize_ws_bytes(ctx,
+ * batch*kv_heads, n_tokens, 1) bytes.
+ * Errors: TQ_ERR_ARG (NULL, strides, alignment, pos0, positions past
+ * capacity), TQ_ERR_CAPACITY (workspace), TQ_ERR_HIP. */
+tq_status tq_cache_write(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_k, const void *d_v,
+                         tq_dtype dtype, int64_t n_tokens, int64_t x_stream_stride, int64_t x_token_stride,
+                         int64_t pos0, void *d_work, size_t work_bytes, void *stream);
 
 /* Append one token per sequence: quantize d_k[b][h][:] / d_v[b][h][:]
  * (contiguous [batch][kv_heads][d]) and write them at position d_seq_len[b]

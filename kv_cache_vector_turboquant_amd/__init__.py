@@ -56,7 +56,7 @@ class CPacked(ctypes.Structure):
 
 class CCache(ctypes.Structure):
     _fields_ = [("k", CPacked), ("v", CPacked), ("batch", _c_i32), ("kv_heads", _c_i32), ("capacity", _c_i32),
-                ("d_seq_len", _c_vp), ("host_max_len", _c_i32)]
+                ("d_seq_len", _c_vp), ("host_max_len", _c_i32), ("d_block_table", _c_vp), ("page_tokens", _c_i32)]
 
 
 def _sig(name, res, args):
@@ -78,6 +78,8 @@ _sig("tq_quantize_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64, _c_i32])
 _sig("tq_quantize_kv", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(CPacked),
                                 _c_i64, _c_i64, _c_vp, _c_sz, _c_vp])
 _sig("tq_append_token", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_i32, _c_vp])
+_sig("tq_cache_write", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64,
+                                _c_vp, _c_sz, _c_vp])
 _sig("tq_attention_decode_ws_bytes", _c_sz, [_c_vp, ctypes.POINTER(CCache), _c_i32])
 _sig("tq_decode_step_ws_bytes", _c_sz, [_c_vp, ctypes.POINTER(CCache), _c_i32])
 _sig("tq_decode_step", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_f32, _c_vp,
@@ -95,7 +97,7 @@ _sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked)
 
 EXPORTED_SYMBOLS = [
     "tq_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
-    "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_append_token", "tq_attention_decode_ws_bytes",
+    "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_cache_write", "tq_append_token", "tq_attention_decode_ws_bytes",
     "tq_attention_decode", "tq_attention_prefill_ws_bytes", "tq_attention_prefill", "tq_decode_step_ws_bytes",
     "tq_decode_step", "tq_time_next_decode", "tq_read_probe",
     "tq_scores_ws_bytes", "tq_scores", "tq_last_error",
@@ -313,16 +315,39 @@ def quantize_kv(ctx: Context, x, out: Packed, n_streams: int | None = None, n_to
 
 
 class KVCache:
-    """Packed KV cache: records of stream (b, h) at (b*kv_heads + h)*capacity + t."""
+    """Packed KV cache. Contiguous: records of stream (b, h) at
+    (b*kv_heads + h)*capacity + t. Paged (page_tokens set): a pool of n_pages
+    pages of page_tokens tokens per KV head, and block_table [batch,
+    capacity/page_tokens] (device int32) names the page of each span of
+    page_tokens positions of a sequence (token t of stream (b, h) is record
+    (table[b, t // P]*kv_heads + h)*P + t % P)."""
 
     def __init__(self, batch: int, kv_heads: int, capacity: int, d: int, key_bits: int, value_bits: int,
-                 device="cuda", key_qjl: bool = True):
+                 device="cuda", key_qjl: bool = True, page_tokens: int | None = None, n_pages: int | None = None,
+                 block_table=None):
         """key_bits = B MSE bits of the keys; key_qjl = False stores MSE-only keys,
-        key_bits = 0 with key_qjl stores pure QJL keys."""
+        key_bits = 0 with key_qjl stores pure QJL keys. page_tokens (a multiple of
+        256 dividing capacity) selects the paged layout: n_pages defaults to
+        batch*capacity/page_tokens, block_table to sequence b owning pages
+        b*cols .. b*cols + cols - 1 (cols = capacity/page_tokens)."""
         torch = _torch()
         if capacity % 32:
             raise ValueError("capacity must be a multiple of 32")
-        n = batch * kv_heads * capacity
+        self.page_tokens = page_tokens
+        if page_tokens:
+            if page_tokens % 256 or capacity % page_tokens:
+                raise ValueError("page_tokens must be a multiple of 256 dividing capacity")
+            cols = capacity // page_tokens
+            self.n_pages = n_pages if n_pages is not None else batch * cols
+            n = self.n_pages * kv_heads * page_tokens
+            if block_table is None:
+                block_table = torch.arange(batch * cols, dtype=torch.int32, device=device).view(batch, cols)
+            assert block_table.dtype == torch.int32 and tuple(block_table.shape) == (batch, cols)
+            self.block_table = block_table.contiguous()
+        else:
+            n = batch * kv_heads * capacity
+            self.n_pages = 0
+            self.block_table = None
         self.k = Packed(n, d, key_bits, True, device, qjl=key_qjl)
         self.v = Packed(n, d, value_bits, False, device)
         self.seq_len = torch.zeros((batch,), dtype=torch.int32, device=device)
@@ -330,38 +355,51 @@ class KVCache:
         self.host_max_len = 0
 
     def c(self) -> CCache:
+        bt = self.block_table.data_ptr() if self.block_table is not None else None
         return CCache(self.k.c(), self.v.c(), self.batch, self.kv_heads, self.capacity, self.seq_len.data_ptr(),
-                      self.host_max_len)
+                      self.host_max_len, bt, self.page_tokens or 0)
 
-    def prefill(self, ctx: Context, k, v):
+    def record_index(self, b: int, h: int, t: int) -> int:
+        """Record of token t of stream (b, h) (host copy of the table for paged caches)."""
+        if self.block_table is None:
+            return (b * self.kv_heads + h) * self.capacity + t
+        P = self.page_tokens
+        page = int(self.block_table[b, t // P])
+        return (page * self.kv_heads + h) * P + t % P
+
+    def write(self, ctx: Context, k, v, pos0: int, work=None):
+        """tq_cache_write: k, v [batch, kv_heads, tokens, d] (d contiguous, same
+        strides) become positions pos0 .. pos0 + tokens - 1 of every stream.
+        Lengths are not changed."""
+        torch = _torch()
+        B, H, T, d = k.shape
+        assert (B, H) == (self.batch, self.kv_heads) and d == self.d and tuple(v.shape) == tuple(k.shape)
+        assert k.stride() == v.stride() and k.stride(3) == 1 and k.stride(0) == H * k.stride(1)
+        need = quantize_ws_bytes(ctx, B * H, T, True)
+        if work is None or work.numel() < need:
+            work = torch.empty(max(need, 4), dtype=torch.uint8, device=k.device)
+        cc = self.c()
+        _check(_lib.tq_cache_write(ctx.handle, ctypes.byref(cc), k.data_ptr(), v.data_ptr(), _dtype_code(k), T,
+                                   k.stride(1), k.stride(2), pos0, work.data_ptr(), work.numel(), _stream_ptr()))
+
+    def prefill(self, ctx: Context, k, v, work=None):
         """k, v: [batch, kv_heads, tokens, d] (d contiguous). Quantizes all tokens
         to positions 0..tokens-1 and sets every sequence length to `tokens`."""
-        B, H, T, d = k.shape
-        assert (B, H) == (self.batch, self.kv_heads) and d == self.d and T <= self.capacity
-        assert k.is_contiguous() and v.is_contiguous(), "prefill expects contiguous [batch, kv_heads, tokens, d]"
-        kf = k.reshape(B * H, T, d)
-        vf = v.reshape(B * H, T, d)
-        quantize_kv(ctx, kf, self.k, n_streams=B * H, n_tokens=T, x_stream_stride=k.stride(1),
-                    x_token_stride=k.stride(2), out_stream_stride=self.capacity, out_offset=0)
-        quantize_kv(ctx, vf, self.v, n_streams=B * H, n_tokens=T, x_stream_stride=v.stride(1),
-                    x_token_stride=v.stride(2), out_stream_stride=self.capacity, out_offset=0)
+        T = k.shape[2]
+        assert T <= self.capacity
+        self.write(ctx, k, v, 0, work)
         self.seq_len.fill_(T)
         self.host_max_len = T
 
-    def extend(self, ctx: Context, k, v):
-        """k, v: [batch, kv_heads, tokens, d] contiguous: a chunk of new tokens
-        written after the current contents. Every sequence must hold
-        host_max_len tokens, a multiple of 32 (value records are written in
-        whole 32-token blocks); all lengths grow by `tokens`."""
-        B, H, T, d = k.shape
-        L0 = self.host_max_len
-        assert (B, H) == (self.batch, self.kv_heads) and d == self.d and L0 + T <= self.capacity
+    def extend(self, ctx: Context, k, v, work=None):
+        """k, v: [batch, kv_heads, tokens, d]: a chunk of new tokens written after
+        the current contents. Every sequence must hold host_max_len tokens, a
+        multiple of 32 (value records are written in whole 32-token blocks); all
+        lengths grow by `tokens`."""
+        L0, T = self.host_max_len, k.shape[2]
         assert L0 % 32 == 0, "extend writes after a multiple of 32 tokens"
-        assert k.is_contiguous() and v.is_contiguous()
-        quantize_kv(ctx, k.reshape(B * H, T, d), self.k, n_streams=B * H, n_tokens=T, x_stream_stride=k.stride(1),
-                    x_token_stride=k.stride(2), out_stream_stride=self.capacity, out_offset=L0)
-        quantize_kv(ctx, v.reshape(B * H, T, d), self.v, n_streams=B * H, n_tokens=T, x_stream_stride=v.stride(1),
-                    x_token_stride=v.stride(2), out_stream_stride=self.capacity, out_offset=L0)
+        assert L0 + T <= self.capacity
+        self.write(ctx, k, v, L0, work)
         self.seq_len.fill_(L0 + T)
         self.host_max_len = L0 + T
 

@@ -487,13 +487,16 @@ tq_status tq_quantize_kv(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int
       return fail(TQ_ERR_CAPACITY, "tq_quantize_kv: key workspace smaller than tq_quantize_ws_bytes()");
   }
   if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  RecMap map;
+  map.os = out_stream_stride;
+  map.oo = out_offset;
   hipError_t e;
   if (out->is_key)
     e = launch_quantize_keys(ctx, d_x, dtype == TQ_BF16, n_streams, n_tokens, x_stream_stride, x_token_stride, out,
-                             out_stream_stride, out_offset, (float *)d_work, (hipStream_t)stream);
+                             map, (float *)d_work, (hipStream_t)stream);
   else
     e = launch_quantize_values(ctx, d_x, dtype == TQ_BF16, n_streams, n_tokens, x_stream_stride, x_token_stride,
-                               out, out_stream_stride, out_offset, (hipStream_t)stream);
+                               out, map, (hipStream_t)stream);
   return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 
@@ -504,12 +507,52 @@ static tq_status check_cache(const tq_ctx *ctx, const tq_kv_cache *c, const char
   if (s != TQ_OK) return s;
   if (c->batch <= 0 || c->kv_heads <= 0 || c->capacity <= 0 || (c->capacity % 32) != 0)
     return fail(TQ_ERR_ARG, std::string(fn) + ": batch, kv_heads > 0 and capacity a positive multiple of 32 required");
-  int64_t recs = (int64_t)c->batch * c->kv_heads * c->capacity;
-  if (c->k.n < recs || c->v.n < recs) return fail(TQ_ERR_ARG, std::string(fn) + ": record arrays smaller than batch*kv_heads*capacity");
+  if (c->d_block_table == nullptr) {
+    int64_t recs = (int64_t)c->batch * c->kv_heads * c->capacity;
+    if (c->k.n < recs || c->v.n < recs)
+      return fail(TQ_ERR_ARG, std::string(fn) + ": record arrays smaller than batch*kv_heads*capacity");
+  } else {
+    if (c->page_tokens <= 0 || (c->page_tokens % 256) != 0 || (c->capacity % c->page_tokens) != 0)
+      return fail(TQ_ERR_ARG, std::string(fn) + ": page_tokens must be a positive multiple of 256 dividing capacity");
+    const int64_t page_recs = (int64_t)c->kv_heads * c->page_tokens;
+    if (c->k.n != c->v.n || c->k.n < page_recs || (c->k.n % page_recs) != 0 || c->k.n / page_recs > INT32_MAX)
+      return fail(TQ_ERR_ARG, std::string(fn) + ": paged record arrays must hold the same whole number of pages");
+  }
   if (!c->d_seq_len) return fail(TQ_ERR_ARG, std::string(fn) + ": NULL d_seq_len");
   if (c->host_max_len < 0 || c->host_max_len > c->capacity)
     return fail(TQ_ERR_ARG, std::string(fn) + ": host_max_len outside [0, capacity]");
   return TQ_OK;
+}
+
+tq_status tq_cache_write(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_k, const void *d_v,
+                         tq_dtype dtype, int64_t n_tokens, int64_t x_stream_stride, int64_t x_token_stride,
+                         int64_t pos0, void *d_work, size_t work_bytes, void *stream) {
+  const char *fn = "tq_cache_write";
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_cache_write: NULL ctx");
+  tq_status s = check_cache(ctx, cache, fn);
+  if (s != TQ_OK) return s;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_cache_write: dtype must be TQ_F32 or TQ_BF16");
+  if (n_tokens < 0 || pos0 < 0 || x_stream_stride < 0 || x_token_stride < 0)
+    return fail(TQ_ERR_ARG, "tq_cache_write: negative size, stride or position");
+  if ((pos0 % 32) != 0) return fail(TQ_ERR_ARG, "tq_cache_write: pos0 must be a multiple of 32");
+  if (pos0 + n_tokens > cache->capacity) return fail(TQ_ERR_ARG, "tq_cache_write: positions past capacity");
+  if (n_tokens == 0) return TQ_OK;
+  if (!d_k || !d_v) return fail(TQ_ERR_ARG, "tq_cache_write: NULL input");
+  if (x_token_stride < ctx->d && n_tokens > 1) return fail(TQ_ERR_ARG, "tq_cache_write: token stride < d");
+  if ((x_token_stride % 8) != 0 || (x_stream_stride % 8) != 0 || ((uintptr_t)d_k % 16) != 0 || ((uintptr_t)d_v % 16) != 0)
+    return fail(TQ_ERR_ARG, "tq_cache_write: inputs must be 16-byte aligned with strides that are multiples of 8");
+  const int64_t n_streams = (int64_t)cache->batch * cache->kv_heads;
+  if (n_streams > 65535) return fail(TQ_ERR_UNSUPPORTED, "tq_cache_write: at most 65535 streams");
+  size_t need = tq_quantize_ws_bytes(ctx, n_streams, n_tokens, 1);
+  if (!d_work || work_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_cache_write: workspace smaller than tq_quantize_ws_bytes()");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  const RecMap map = cache_map(cache, pos0);
+  hipError_t e = launch_quantize_keys(ctx, d_k, dtype == TQ_BF16, n_streams, n_tokens, x_stream_stride, x_token_stride,
+                                      &cache->k, map, (float *)d_work, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = launch_quantize_values(ctx, d_v, dtype == TQ_BF16, n_streams, n_tokens, x_stream_stride, x_token_stride,
+                               &cache->v, map, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 
 tq_status tq_append_token(const tq_ctx *ctx, tq_kv_cache *cache, const void *d_k, const void *d_v, tq_dtype dtype,

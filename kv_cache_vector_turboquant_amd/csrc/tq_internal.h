@@ -22,6 +22,24 @@ struct DeviceTables {
   float ctop[TQ_MAX_BITS + 1];
 };
 
+// Where the record of token t of stream s lands in a packed array: contiguous
+// s * os + oo + t, or, with a block table (paged cache; s = b * heads + h and
+// position T = oo + t), (page * heads + h) * page_tokens + T mod page_tokens
+// with page = table[b * cols + T / page_tokens]. A page id outside [0, npages)
+// is a caller error; it is clamped so every access stays inside the arrays.
+struct RecMap {
+  int64_t os = 0, oo = 0;
+  const int32_t *table = nullptr;
+  int32_t page_tokens = 0, heads = 1, cols = 0, npages = 1;
+  __host__ __device__ __forceinline__ int64_t rec(int64_t s, int64_t t) const {
+    if (table == nullptr) return s * os + oo + t;
+    const int64_t T = oo + t, b = s / heads, h = s - b * heads;
+    int pg = table[b * cols + T / page_tokens];
+    pg = pg < 0 ? 0 : (pg >= npages ? npages - 1 : pg);
+    return ((int64_t)pg * heads + h) * page_tokens + T % page_tokens;
+  }
+};
+
 // i-th odd-cardinality subset of {0..bits-1} (as a bit mask), ordered by
 // (popcount, value); there are 2^(bits-1) of them.
 int walsh_subset(int bits, int i);
@@ -52,11 +70,13 @@ struct tq_ctx {
 namespace tq {
 // Kernel launchers (tq_kernels.hip). All return hipSuccess or the launch error.
 hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams, int64_t n_tokens,
-                                int64_t xs, int64_t xt, const tq_packed *out, int64_t os, int64_t oo, float *work,
+                                int64_t xs, int64_t xt, const tq_packed *out, const RecMap &map, float *work,
                                 hipStream_t st);
 hipError_t launch_quantize_values(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams,
-                                  int64_t n_tokens, int64_t xs, int64_t xt, const tq_packed *out, int64_t os,
-                                  int64_t oo, hipStream_t st);
+                                  int64_t n_tokens, int64_t xs, int64_t xt, const tq_packed *out, const RecMap &map,
+                                  hipStream_t st);
+// The record map of a cache (contiguous or paged) for positions starting at oo.
+RecMap cache_map(const tq_kv_cache *cache, int64_t oo);
 hipError_t launch_append(const tq_ctx *ctx, const tq_kv_cache *cache, const void *k, const void *v, int is_bf16,
                          hipStream_t st);
 size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int *chunk_out,

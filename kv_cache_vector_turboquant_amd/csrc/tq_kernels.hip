@@ -67,7 +67,7 @@ struct GemmArgs {
   float *norms_out;
   float *resid;          // keys: residual rows [stream*n_tokens + t][d]
   int64_t n_tokens;
-  int64_t out_stream_stride, out_offset;
+  RecMap map;            // record of (stream, token)
   // store / scores epilogues
   float *c;
   int64_t ldc;
@@ -250,7 +250,6 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   } else if constexpr (MODE == MODE_KEY_CODES || MODE == MODE_KEY_SIGNS) {
     // rows = tokens of stream s, columns = coordinates (codes) or sketch rows (signs)
     const int W = g.d >> 5;
-    const int64_t rec_base = s * g.out_stream_stride + g.out_offset;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int64_t col = col0 + wn * 64 + b * 32 + li;
@@ -271,7 +270,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
           if (in && g.qjl) g.resid[(s * g.n_tokens + t) * (int64_t)g.d + col] = live ? y - (B > 0 ? cent[idx] : 0.f) : 0.f;
           mybits = live ? (uint32_t)idx : 0u;
         } else {
-          live = in && g.norms_out[2 * (rec_base + t)] > 0.f;  // signs only exist with the QJL stage: 2 norms
+          live = in && g.norms_out[2 * g.map.rec(s, t)] > 0.f;  // signs only exist with the QJL stage: 2 norms
           mybits = (live && acc[b][r] >= 0.f) ? 1u : 0u;
         }
         const int np = (MODE == MODE_KEY_CODES) ? B : 1;
@@ -289,8 +288,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
       const int rl = tid >> 2, gl = tid & 3;
       const int64_t t = row0 + rl;
       const int w = (int)(col0 >> 5) + gl;
+      const int64_t rec = t < g.n_tokens ? g.map.rec(s, t) : 0;
       if (t < g.n_tokens && w < W) {
-        uint32_t *dst = g.bits_out + ((rec_base + t) * W + w) * (int64_t)(B + g.qjl);
+        uint32_t *dst = g.bits_out + (rec * W + w) * (int64_t)(B + g.qjl);
         if constexpr (MODE == MODE_KEY_CODES) {
           for (int p = 0; p < B; ++p) dst[p] = cw[(rl * (GBN / 32) + gl) * 4 + p];
         } else {
@@ -298,13 +298,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
         }
       }
       if (ct == 0 && gl == 0 && t < g.n_tokens) {
-        if constexpr (MODE == MODE_KEY_CODES) g.norms_out[(1 + g.qjl) * (rec_base + t)] = sqrtf(stat[rl]);
-        else g.norms_out[2 * (rec_base + t) + 1] = sqrtf(stat[rl]);
+        if constexpr (MODE == MODE_KEY_CODES) g.norms_out[(1 + g.qjl) * rec] = sqrtf(stat[rl]);
+        else g.norms_out[2 * rec + 1] = sqrtf(stat[rl]);
       }
     }
   } else if constexpr (MODE == MODE_VAL_CODES) {
     // rows = coordinates, columns = tokens of stream s; ballots are token-major words.
-    const int64_t rec_base = s * g.out_stream_stride + g.out_offset;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int cl = wn * 64 + b * 32 + li;
@@ -320,7 +319,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
         for (int p = 0; p < B; ++p) {
           const uint64_t bal = __builtin_amdgcn_ballot_w64(((idx >> p) & 1u) != 0u);
           if (li == 0 && blk_t0 < g.n_tokens && j < g.d) {
-            const int64_t blk = (rec_base + blk_t0) >> 5;
+            const int64_t blk = g.map.rec(s, blk_t0) >> 5;
             g.bits_out[(blk * g.d + j) * B + p] = lh ? (uint32_t)(bal >> 32) : (uint32_t)bal;
           }
         }
@@ -331,7 +330,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
       for (int q = 0; q < 2; ++q) {
         const int cl = (tid >> 2) + 64 * q;
         const int64_t t = col0 + cl;
-        if (t < g.n_tokens) g.norms_out[rec_base + t] = sqrtf(stat[cl]);
+        if (t < g.n_tokens) g.norms_out[g.map.rec(s, t)] = sqrtf(stat[cl]);
       }
     }
   }
@@ -368,7 +367,7 @@ struct Q128Args {
   const DeviceTables *tables;
   uint32_t *bits_out;
   float *norms_out;
-  int64_t os, oo;          // output stream stride and offset (records)
+  RecMap map;              // record of (stream, token)
 };
 
 __device__ __forceinline__ bf16x8 ld_bf8(const uint16_t *p) {
@@ -637,7 +636,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
       if (tid < 4 * QT) {
         const int tok = tid >> 2, g = tid & 3;
         if (tok < nv) {
-          const int64_t rec = s * a.os + a.oo + t0 + tok;
+          const int64_t rec = a.map.rec(s, t0 + tok);
           const float n = nrm[tok];
           uint32_t w[NPL];
           if (n > 0.f) {
@@ -712,7 +711,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
           const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb, 3) * 4]);
           const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb + 1, 3) * 4]);
           const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-          const int64_t blk = (s * a.os + a.oo + t0) / 32 + hb;
+          const int64_t blk = a.map.rec(s, t0 + 32 * hb) >> 5;  // blocks never straddle pages
           uint32_t *dst = a.bits_out + (blk * QD + jj) * B;
 #pragma unroll
           for (int p = 0; p < B; ++p) {
@@ -722,7 +721,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
             dst[p] = word & live;
           }
         }
-        if (tid < nv) a.norms_out[s * a.os + a.oo + t0 + tid] = nrm[tid];
+        if (tid < nv) a.norms_out[a.map.rec(s, t0 + tid)] = nrm[tid];
       }
     }
     // the staging buffers are reused only after the next iteration's first barrier
@@ -774,7 +773,7 @@ static hipError_t launch_quant128(const Q128Args &q, int bits, bool qjl, hipStre
 }
 
 static hipError_t quant128(const tq_ctx *ctx, bool keys, const void *x, int64_t n_streams, int64_t n_tokens,
-                           int64_t xs, int64_t xt, const tq_packed *out, int64_t os, int64_t oo, hipStream_t st) {
+                           int64_t xs, int64_t xt, const tq_packed *out, const RecMap &map, hipStream_t st) {
   Q128Args q = {};
   q.x = (const uint16_t *)x;
   q.n_streams = n_streams;
@@ -786,17 +785,16 @@ static hipError_t quant128(const tq_ctx *ctx, bool keys, const void *x, int64_t 
   q.tables = ctx->d_tables;
   q.bits_out = out->bits;
   q.norms_out = out->norms;
-  q.os = os;
-  q.oo = oo;
+  q.map = map;
   return keys ? launch_quant128<true>(q, out->mse_bits, out->qjl != 0, st)
               : launch_quant128<false>(q, out->mse_bits, false, st);
 }
 
 hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams, int64_t n_tokens,
-                                int64_t xs, int64_t xt, const tq_packed *out, int64_t os, int64_t oo, float *work,
+                                int64_t xs, int64_t xt, const tq_packed *out, const RecMap &map, float *work,
                                 hipStream_t st) {
   const int d = ctx->d;
-  if (d == QD && is_bf16 && ctx->d_rot3) return quant128(ctx, true, x, n_streams, n_tokens, xs, xt, out, os, oo, st);
+  if (d == QD && is_bf16 && ctx->d_rot3) return quant128(ctx, true, x, n_streams, n_tokens, xs, xt, out, map, st);
   GemmArgs g = {};
   g.a = {x, xt, n_tokens, is_bf16};
   g.a_stream_stride = xs;
@@ -813,8 +811,7 @@ hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, i
   g.qjl = out->qjl;
   g.resid = work;
   g.n_tokens = n_tokens;
-  g.out_stream_stride = os;
-  g.out_offset = oo;
+  g.map = map;
   g.rows_on_x = 1;
   dim3 grid((unsigned)((n_tokens + GBM - 1) / GBM), (d + GBN - 1) / GBN, (unsigned)n_streams);
   hipLaunchKernelGGL(gemm_kernel<MODE_KEY_CODES>, grid, dim3(256), 0, st, g);
@@ -830,10 +827,10 @@ hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, i
 }
 
 hipError_t launch_quantize_values(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams,
-                                  int64_t n_tokens, int64_t xs, int64_t xt, const tq_packed *out, int64_t os,
-                                  int64_t oo, hipStream_t st) {
+                                  int64_t n_tokens, int64_t xs, int64_t xt, const tq_packed *out, const RecMap &map,
+                                  hipStream_t st) {
   const int d = ctx->d;
-  if (d == QD && is_bf16 && ctx->d_rot3) return quant128(ctx, false, x, n_streams, n_tokens, xs, xt, out, os, oo, st);
+  if (d == QD && is_bf16 && ctx->d_rot3) return quant128(ctx, false, x, n_streams, n_tokens, xs, xt, out, map, st);
   GemmArgs g = {};
   g.a = {ctx->d_rot, d, d, 0};
   g.a_stream_stride = 0;
@@ -848,8 +845,7 @@ hipError_t launch_quantize_values(const tq_ctx *ctx, const void *x, int is_bf16,
   g.bits_out = out->bits;
   g.norms_out = out->norms;
   g.n_tokens = n_tokens;
-  g.out_stream_stride = os;
-  g.out_offset = oo;
+  g.map = map;
   dim3 grid((unsigned)((n_tokens + GBN - 1) / GBN), (d + GBM - 1) / GBM, (unsigned)n_streams);
   hipLaunchKernelGGL(gemm_kernel<MODE_VAL_CODES>, grid, dim3(256), 0, st, g);
   return hipGetLastError();
@@ -1053,6 +1049,7 @@ struct DecodeArgs {
   int n_q, causal;       // causal: position i attends to t < seq_len - n_q + i + 1
   int vgroup;            // n_q * group virtual heads per KV stream
   int kv_streams;        // batch * kv_heads
+  RecMap map;            // record of (KV stream, token): contiguous or paged
   float scale_log2;      // softmax scale * log2(e)
   float qjl_scale;
   const DeviceTables *tables;
@@ -1140,7 +1137,7 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
     L.tb[tid] = which == 0 ? a.tables->boundary[kB][i] : which == 1 ? a.tables->centroid[kB][i] : a.tables->boundary[vB][i];
   }
   // value coordinate threads: the words this token's bits go into
-  const int64_t rec = (int64_t)stream[hs] * a.capacity + pos[hs];
+  const int64_t rec = on[hs] ? a.map.rec(stream[hs], pos[hs]) : 0;
   const int bit_pos = (int)(rec & 31);
   uint32_t vold[4] = {0u, 0u, 0u, 0u};
   uint32_t *vdst = a.vbits_w + ((rec >> 5) * DD + r) * vB;
@@ -1600,7 +1597,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     }
   } else {
     const int n = t1 - t0;
-    const int64_t srec = (int64_t)stream * a.capacity;
+    // the chunk's first record: a chunk never straddles a page (the chunk divides
+    // the page size), so its records are consecutive
+    const int64_t rec0 = a.map.rec(stream, t0);
     const float *wk = a.tables->walsh[KB > 0 ? KB : 1];
     const float *wv = a.tables->walsh[VB];
     const int ngrp = (n + 127) >> 7;
@@ -1608,9 +1607,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     // records of the chunk: uniform bases and unsigned 32-bit byte offsets per lane
     // (base + zero-extended offset addressing); lanes past the end re-read token
     // n-1, so every store below stays unconditional and harmless
-    const char *kb0 = reinterpret_cast<const char *>(a.kbits + (srec + t0) * DW * NPL);
-    const char *kn0 = reinterpret_cast<const char *>(a.knorm + (1 + KQ) * (srec + t0));
-    const char *vn0 = reinterpret_cast<const char *>(a.vnorm + (srec + t0));
+    const char *kb0 = reinterpret_cast<const char *>(a.kbits + rec0 * DW * NPL);
+    const char *kn0 = reinterpret_cast<const char *>(a.knorm + (1 + KQ) * rec0);
+    const char *vn0 = reinterpret_cast<const char *>(a.vnorm + rec0);
     const uint32_t kgo = (uint32_t)(G * NPL * 4);  // the lane's 32-coordinate group in a record
     struct KBuf {
       uint32_t pl[KTPW][NPL];
@@ -1735,7 +1734,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     };
     // blocks of the chunk from a uniform base; a block past the end re-reads the
     // last one (its tokens carry zero weights)
-    const char *vb0 = reinterpret_cast<const char *>(a.vbits + ((srec + t0) >> 5) * DD * VB);
+    const char *vb0 = reinterpret_cast<const char *>(a.vbits + (rec0 >> 5) * DD * VB);
     const int lastblk = (n - 1) >> 5;
     const uint32_t vco = (uint32_t)((wave * 32 + vn) * VB * 4);  // the lane's coordinate in a block
     auto vload = [&](int grp0, VBuf &bf) {
@@ -1876,6 +1875,21 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   }
 }
 
+RecMap cache_map(const tq_kv_cache *cache, int64_t oo) {
+  RecMap m;
+  m.oo = oo;
+  if (cache->d_block_table == nullptr) {
+    m.os = cache->capacity;
+    return m;
+  }
+  m.table = cache->d_block_table;
+  m.page_tokens = cache->page_tokens;
+  m.heads = cache->kv_heads;
+  m.cols = cache->capacity / cache->page_tokens;
+  m.npages = (int32_t)(cache->k.n / ((int64_t)cache->kv_heads * cache->page_tokens));
+  return m;
+}
+
 size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int *chunk_out,
                        int *nchunks_out, int n_q) {
   const int group = q_heads / cache->kv_heads;
@@ -1884,6 +1898,9 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
   const int64_t streams = (int64_t)cache->batch * cache->kv_heads * hgroups;
   int chunk = 1024;
   while (chunk > 256 && streams * ((maxlen + chunk - 1) / chunk) < 2048) chunk >>= 1;
+  // paged cache: a chunk must lie within one page (pages are multiples of 256 tokens)
+  if (cache->d_block_table)
+    while (cache->page_tokens % chunk) chunk >>= 1;
   const int nchunks = std::max(1, (maxlen + chunk - 1) / chunk);
   if (chunk_out) *chunk_out = chunk;
   if (nchunks_out) *nchunks_out = nchunks;
@@ -1927,6 +1944,7 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.causal = causal;
   a.vgroup = a.group * n_q;
   a.kv_streams = cache->batch * cache->kv_heads;
+  a.map = cache_map(cache, 0);
   a.hgroups = (a.vgroup + 3) / 4;
   a.chunk = chunk;
   a.nchunks = nchunks;
@@ -2037,6 +2055,7 @@ struct AppendArgs {
   int32_t *seq_len;
   int kB, vB, kv_heads, capacity;
   int kQ;  // keys carry the QJL sign word and |r|
+  RecMap map;
 };
 
 __device__ __forceinline__ float block_sum128(float v, float *red) {
@@ -2055,7 +2074,7 @@ __global__ void __launch_bounds__(DD) append_kernel(AppendArgs a) {
   const int b = stream / a.kv_heads;
   const int t = a.seq_len[b];
   if (t >= a.capacity) return;
-  const int64_t rec = (int64_t)stream * a.capacity + t;
+  const int64_t rec = a.map.rec(stream, t);
   const int64_t off = (int64_t)stream * DD + j;
   const float x = a.bf16 ? bf16f(((const uint16_t *)a.k)[off]) : ((const float *)a.k)[off];
   const float xv = a.bf16 ? bf16f(((const uint16_t *)a.v)[off]) : ((const float *)a.v)[off];
@@ -2142,6 +2161,7 @@ hipError_t launch_append(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.vB = cache->v.mse_bits;
   a.kv_heads = cache->kv_heads;
   a.capacity = cache->capacity;
+  a.map = cache_map(cache, 0);
   hipLaunchKernelGGL(append_kernel, dim3(cache->batch * cache->kv_heads), dim3(DD), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
