@@ -380,7 +380,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         "decode_call_ms": avg_ms, "wall_s_timed": wall, **extra_cold, **(graph or {}),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": f"decode_kernel<{kbits},{vbits},{str(kqjl).lower()}> (score/attention over the packed cache)",
+                     "kernel": f"decode_kernel<{kbits}, {vbits}, {str(kqjl).lower()}, spans> (score/attention over the packed cache; spans: chunks over several pages)",
                      "algorithmic_bytes_per_launch": float(dec_bytes.mean()), "avg_launch_ms": kern_avg_ms,
                      "bytes_per_kv_token": rec_bytes,
                      "call": ("tq_decode_step: decode_prep_kernel (query prep + append), decode_kernel, "
@@ -512,7 +512,7 @@ def run_prefill(args, torch, tq, synth):
         "attend_call_ms": call_ms.tolist(), "attend_kernel_ms": kern_ms.tolist(),
         "roofline": {"bound": "mfma", "achieved": float(tput[-1]), "peak": mix_peak, "unit": "TFLOP/s",
                      "frac": float(tput[-1]) / mix_peak, "traffic": None,
-                     "kernel": f"decode_kernel<{kbits},{vbits},{str(kqjl).lower()}> on the last chunk "
+                     "kernel": f"decode_kernel<{kbits}, {vbits}, {str(kqjl).lower()}, false> on the last chunk "
                                f"({P} tokens visible to its last position)",
                      "ops_per_vhead_token": k_ops + v_ops, "k_ops_per_vhead_token": k_ops,
                      "v_ops_per_vhead_token": v_ops, "avg_launch_ms": float(kern_ms[-1]),

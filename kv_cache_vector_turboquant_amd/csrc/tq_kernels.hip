@@ -1050,6 +1050,7 @@ struct DecodeArgs {
   int vgroup;            // n_q * group virtual heads per KV stream
   int kv_streams;        // batch * kv_heads
   RecMap map;            // record of (KV stream, token): contiguous or paged
+  int span_lg;           // log2 of the runs of consecutive records in a chunk (chunk or page size)
   float scale_log2;      // softmax scale * log2(e)
   float qjl_scale;
   const DeviceTables *tables;
@@ -1523,9 +1524,15 @@ __global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
   }
 }
 
+// first record of span si (uniform) of a decode chunk
+__device__ __forceinline__ int64_t pick_span(int si, int64_t r0, int64_t r1, int64_t r2, int64_t r3) {
+  return si == 0 ? r0 : si == 1 ? r1 : si == 2 ? r2 : r3;
+}
+
 // KB MSE bits of the keys (0: pure QJL keys), QJL: the keys carry the sign word
 // and |r| (false: MSE-only keys)
-template <int KB, int VB, bool QJL>
+// SPANS: the chunk's records come in several runs (pages smaller than the chunk)
+template <int KB, int VB, bool QJL, bool SPANS>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   constexpr int KM = KB > 0 ? 1 << (KB - 1) : 0;  // key Walsh masks
   constexpr int KQ = QJL ? 1 : 0;
@@ -1597,19 +1604,26 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     }
   } else {
     const int n = t1 - t0;
-    // the chunk's first record: a chunk never straddles a page (the chunk divides
-    // the page size), so its records are consecutive
-    const int64_t rec0 = a.map.rec(stream, t0);
+    // the chunk's records come in spans of 2^span_lg consecutive positions: one
+    // span, or (pages smaller than the chunk) up to four pages; rs0..rs3 are the
+    // spans' first records, picked per tile or value group by a uniform index
+    const int slg = a.span_lg;
+    const uint32_t smask = (1u << slg) - 1u;
+    const int64_t rs0 = a.map.rec(stream, t0);
+    int64_t rs1 = rs0, rs2 = rs0, rs3 = rs0;
+    if (SPANS) {
+      if ((1 << slg) < n) rs1 = a.map.rec(stream, t0 + (1 << slg));
+      if ((2 << slg) < n) rs2 = a.map.rec(stream, t0 + (2 << slg));
+      if ((3 << slg) < n) rs3 = a.map.rec(stream, t0 + (3 << slg));
+    }
     const float *wk = a.tables->walsh[KB > 0 ? KB : 1];
     const float *wv = a.tables->walsh[VB];
     const int ngrp = (n + 127) >> 7;
     const int tn = lane & 15, G = lane >> 4;  // MFMA column (token), row group (head)
-    // records of the chunk: uniform bases and unsigned 32-bit byte offsets per lane
-    // (base + zero-extended offset addressing); lanes past the end re-read token
-    // n-1, so every store below stays unconditional and harmless
-    const char *kb0 = reinterpret_cast<const char *>(a.kbits + rec0 * DW * NPL);
-    const char *kn0 = reinterpret_cast<const char *>(a.knorm + (1 + KQ) * rec0);
-    const char *vn0 = reinterpret_cast<const char *>(a.vnorm + rec0);
+    // records of the chunk: uniform bases (the tile's span) and unsigned 32-bit
+    // byte offsets per lane (base + zero-extended offset addressing); lanes past
+    // the end re-read token n-1, so every store below stays unconditional and
+    // harmless
     const uint32_t kgo = (uint32_t)(G * NPL * 4);  // the lane's 32-coordinate group in a record
     struct KBuf {
       uint32_t pl[KTPW][NPL];
@@ -1622,7 +1636,13 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       for (int u = 0; u < KTPW; ++u) {
         const uint32_t tc = (uint32_t)min((base + u) * 16 + tn, n - 1);
         bf.tc[u] = tc;
-        const char *src = kb0 + (tc * (uint32_t)(DW * NPL * 4) + kgo);
+        // a tile lies in one span
+        const int64_t rr = SPANS ? pick_span(min((base + u) * 16, n - 1) >> slg, rs0, rs1, rs2, rs3) : rs0;
+        const char *kb0 = reinterpret_cast<const char *>(a.kbits + rr * DW * NPL);
+        const char *kn0 = reinterpret_cast<const char *>(a.knorm + (1 + KQ) * rr);
+        const char *vn0 = reinterpret_cast<const char *>(a.vnorm + rr);
+        const uint32_t tl = SPANS ? tc & smask : tc;  // position in the span
+        const char *src = kb0 + (tl * (uint32_t)(DW * NPL * 4) + kgo);
         if constexpr (NPL == 4) {
           const uint4 w4 = *reinterpret_cast<const uint4 *>(src);
           bf.pl[u][0] = w4.x; bf.pl[u][1] = w4.y; bf.pl[u][2] = w4.z; bf.pl[u][3] = w4.w;
@@ -1630,9 +1650,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int p = 0; p < NPL; ++p) bf.pl[u][p] = reinterpret_cast<const uint32_t *>(src)[p];
         }
-        if constexpr (QJL) bf.kn[u] = *reinterpret_cast<const float2 *>(kn0 + (tc << 3));
-        else bf.kn[u] = make_float2(*reinterpret_cast<const float *>(kn0 + (tc << 2)), 0.f);
-        bf.vn[u] = *reinterpret_cast<const float *>(vn0 + (tc << 2));
+        if constexpr (QJL) bf.kn[u] = *reinterpret_cast<const float2 *>(kn0 + (tl << 3));
+        else bf.kn[u] = make_float2(*reinterpret_cast<const float *>(kn0 + (tl << 2)), 0.f);
+        bf.vn[u] = *reinterpret_cast<const float *>(vn0 + (tl << 2));
       }
     };
     // the wave's first key tiles are requested before anything else
@@ -1732,17 +1752,18 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     struct VBuf {
       uint32_t pl[VGPI][2][VB];
     };
-    // blocks of the chunk from a uniform base; a block past the end re-reads the
-    // last one (its tokens carry zero weights)
-    const char *vb0 = reinterpret_cast<const char *>(a.vbits + (rec0 >> 5) * DD * VB);
+    // blocks of the chunk from a uniform base (the group's span); a block past the
+    // end re-reads the last one (its tokens carry zero weights)
     const int lastblk = (n - 1) >> 5;
     const uint32_t vco = (uint32_t)((wave * 32 + vn) * VB * 4);  // the lane's coordinate in a block
     auto vload = [&](int grp0, VBuf &bf) {
 #pragma unroll
       for (int gi = 0; gi < VGPI; ++gi) {
-        // this lane's 32-token block, chunk-relative
+        // this lane's 32-token block, chunk-relative; a 128-token group lies in one span
         const uint32_t blk = (uint32_t)min((grp0 + gi) * 4 + vg, lastblk);
-        const char *src = vb0 + (blk * (uint32_t)(DD * VB * 4) + vco);
+        const int64_t rr = SPANS ? pick_span((min((grp0 + gi) * 4, lastblk) * 32) >> slg, rs0, rs1, rs2, rs3) : rs0;
+        const char *vb0 = reinterpret_cast<const char *>(a.vbits + (rr >> 5) * DD * VB);
+        const char *src = vb0 + ((SPANS ? blk & (smask >> 5) : blk) * (uint32_t)(DD * VB * 4) + vco);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -1898,9 +1919,11 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
   const int64_t streams = (int64_t)cache->batch * cache->kv_heads * hgroups;
   int chunk = 1024;
   while (chunk > 256 && streams * ((maxlen + chunk - 1) / chunk) < 2048) chunk >>= 1;
-  // paged cache: a chunk must lie within one page (pages are multiples of 256 tokens)
+  // paged cache: pages either hold whole chunks or tile them (a chunk spans at
+  // most four pages of 256 or 512 tokens); other page sizes take the largest
+  // chunk that divides the page
   if (cache->d_block_table)
-    while (cache->page_tokens % chunk) chunk >>= 1;
+    while ((cache->page_tokens % chunk) != 0 && (chunk % cache->page_tokens) != 0) chunk >>= 1;
   const int nchunks = std::max(1, (maxlen + chunk - 1) / chunk);
   if (chunk_out) *chunk_out = chunk;
   if (nchunks_out) *nchunks_out = nchunks;
@@ -1918,7 +1941,10 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
 
 template <int KB, int VB, bool QJL>
 static hipError_t launch_decode_kv(const DecodeArgs &a, dim3 grid, size_t shm, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<KB, VB, QJL>), grid, dim3(256), shm, st, a);
+  if (a.chunk > (1 << a.span_lg))
+    hipLaunchKernelGGL((decode_kernel<KB, VB, QJL, true>), grid, dim3(256), shm, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<KB, VB, QJL, false>), grid, dim3(256), shm, st, a);
   return hipGetLastError();
 }
 
@@ -1945,6 +1971,11 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.vgroup = a.group * n_q;
   a.kv_streams = cache->batch * cache->kv_heads;
   a.map = cache_map(cache, 0);
+  {
+    const int span = cache->d_block_table ? std::min(cache->page_tokens, chunk) : chunk;
+    a.span_lg = 0;
+    while ((1 << a.span_lg) < span) ++a.span_lg;
+  }
   a.hgroups = (a.vgroup + 3) / 4;
   a.chunk = chunk;
   a.nchunks = nchunks;

@@ -93,6 +93,7 @@ def test_hot_entry_points_reject_null_context():
     assert lib.tq_quantize_kv(None, None, 0, 1, 1, 128, 128, ctypes.byref(p), 0, 0, None, 0, None) == tq.TQ_ERR_ARG
     c = tq.CCache()
     assert lib.tq_append_token(None, ctypes.byref(c), None, None, 0, None) == tq.TQ_ERR_ARG
+    assert lib.tq_cache_write(None, ctypes.byref(c), None, None, 0, 1, 128, 128, 0, None, 0, None) == tq.TQ_ERR_ARG
     assert lib.tq_attention_decode(None, ctypes.byref(c), None, 0, 4, 1.0, None, None, 0, None) == tq.TQ_ERR_ARG
     assert lib.tq_attention_prefill(None, ctypes.byref(c), None, 0, 8, 4, 1, 1.0, None, None, 0, None) == tq.TQ_ERR_ARG
     assert lib.tq_attention_prefill_ws_bytes(None, ctypes.byref(c), 8, 4) == 0

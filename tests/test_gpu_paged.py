@@ -160,6 +160,38 @@ def test_paged_small_pages_against_oracle(c128):
             assert np.max(np.abs(outp[b, :, h * g:(h + 1) * g] - refp)) <= 2e-3, f"prefill b={b} h={h}"
 
 
+@pytest.mark.parametrize("page_tokens", [256, 512])
+def test_paged_chunks_spanning_pages(c128, page_tokens):
+    """Pages smaller than the decode chunk: 2 sequences x 8 KV heads x 32868
+    tokens with 128 query heads (groups of 16) make 1024-token chunks, each
+    spanning four or two shuffled pages. Decode, causal prefill attention of 3
+    positions and two fused steps equal the contiguous cache's outputs bit for
+    bit (same chunking, so the same arithmetic)."""
+    ctx, _, _ = c128
+    B, H, Hq, L, d = 2, 8, 128, 32868, 128
+    cap = ((L + 2 + 1023) // 1024) * 1024
+    n_pages, table = _shuffled_table(43, B, cap // page_tokens, 5)
+    K = synth.torch_outlier_kv(43, (1,), synth.TAG_SCALES_K, (B, H, L, d), torch.bfloat16, DEV)
+    V = synth.torch_outlier_kv(43, (2,), synth.TAG_SCALES_V, (B, H, L, d), torch.bfloat16, DEV)
+    flat = tq.KVCache(B, H, cap, d, 3, 3)
+    paged = tq.KVCache(B, H, cap, d, 3, 3, page_tokens=page_tokens, n_pages=n_pages, block_table=table)
+    for c in (flat, paged):
+        c.prefill(ctx, K, V)
+        c.seq_len.copy_(torch.tensor([L, L - 5000], dtype=torch.int32))
+    del K, V
+    q = synth.torch_gaussian(43, (3,), (B, Hq, d), torch.bfloat16, DEV)
+    assert torch.equal(flat.decode(ctx, q), paged.decode(ctx, q))
+    qp = synth.torch_gaussian(43, (4,), (B, 3, Hq, d), torch.bfloat16, DEV)
+    assert torch.equal(flat.attend(ctx, qp, True), paged.attend(ctx, qp, True))
+    for i in range(2):
+        ka = synth.torch_outlier_kv(43, (5, i), synth.TAG_SCALES_K, (B, H, d), torch.bfloat16, DEV)
+        va = synth.torch_outlier_kv(43, (6, i), synth.TAG_SCALES_V, (B, H, d), torch.bfloat16, DEV)
+        qs = synth.torch_gaussian(43, (7, i), (B, Hq, d), torch.bfloat16, DEV)
+        assert torch.equal(flat.decode_step(ctx, ka, va, qs), paged.decode_step(ctx, ka, va, qs)), f"step {i}"
+    chunk_ws = paged.decode_ws_bytes(ctx, Hq)
+    assert chunk_ws == flat.decode_ws_bytes(ctx, Hq)  # same chunking
+
+
 def test_paged_cache_argument_errors(c128):
     """Page sizes that are not multiples of 256 or do not divide the capacity, and
     pools that are not whole pages, are rejected before any launch."""
