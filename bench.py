@@ -31,7 +31,7 @@ import numpy as np  # noqa: E402
 METRIC = "attention-score keys/s over packed KV (% HBM peak); quantize vectors/s"
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
-VAL_B3 = 52   # 3-bit value record at d=128 (48 code + 4 norm bytes)
+VAL_B3 = 52   # 3-bit value record at d=128 (48 code + 4 norm bytes; 50 with fp16 norms)
 
 
 def parse():
@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--separate-append", action="store_true",
                     help="serving step: tq_append_token then tq_attention_decode instead of tq_decode_step")
+    ap.add_argument("--norms", choices=["f32", "f16"], default="f32",
+                    help="decode workloads: record norms as fp32, or fp16 (compact records)")
     ap.add_argument("--page-tokens", type=int, default=0,
                     help="decode workloads: paged cache with pages of this many tokens (a multiple of 256) in a "
                          "shuffled pool, instead of the contiguous layout")
@@ -198,8 +200,8 @@ def key_format(args):
     return args.kbits, True, f"keys b={args.kbits + 1}"
 
 
-def key_record_bytes(d, B, qjl):
-    return (d // 32) * (B + int(qjl)) * 4 + 4 * (1 + int(qjl))
+def key_record_bytes(d, B, qjl, norm_f16=False):
+    return (d // 32) * (B + int(qjl)) * 4 + (2 if norm_f16 else 4) * (1 + int(qjl))
 
 
 def oracle_stream_rates(d, L, group, kbits, vbits, seconds, data, kqjl=True):
@@ -250,6 +252,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     """Prefill quantize of B x H x L K/V, then NS x (append + decode)."""
     d, vbits = 128, 3
     kbits, kqjl, _ = key_format(args)
+    nf16 = args.norms == "f16"
     cap = ((L + NS + 31) // 32) * 32
     ctx = tq.Context(d, 0)
     K = kv_inputs(torch, synth, args, (B, H, L, d), (3, synth.TAG_KEYS), synth.TAG_SCALES_K)
@@ -266,9 +269,9 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         g.manual_seed(7)
         perm = torch.randperm(B * cols + 8, generator=g)[:B * cols].to(torch.int32).view(B, cols).to("cuda")
         cache = tq.KVCache(B, H, cap, d, kbits, vbits, key_qjl=kqjl, page_tokens=Pt, n_pages=B * cols + 8,
-                           block_table=perm)
+                           block_table=perm, norm_f16=nf16)
     else:
-        cache = tq.KVCache(B, H, cap, d, kbits, vbits, key_qjl=kqjl)
+        cache = tq.KVCache(B, H, cap, d, kbits, vbits, key_qjl=kqjl, norm_f16=nf16)
     kwork = torch.empty(tq.quantize_ws_bytes(ctx, B * H, L, True), dtype=torch.uint8, device="cuda")
     cache.host_max_len = cap
     fused = NS > 0 and not args.separate_append
@@ -343,7 +346,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         torch.cuda.synchronize()
         graph = {"graph_ms_per_step": ms(gw) / args.steps, "graph_replay_matches_eager": same}
     keys_per_step = sum(B * H * (L + (i + 1 if NS > 0 else 0)) for i in range(n_dec))
-    rec_bytes = key_record_bytes(d, kbits, kqjl) + VAL_B3
+    rec_bytes = key_record_bytes(d, kbits, kqjl, nf16) + VAL_B3 - (2 if nf16 else 0)
     dec_ms = np.array([ms(e) for e, _, _ in dec_events])
     kern_ms = np.array([ms(k) for _, k, _ in dec_events])
     dec_bytes = np.array([B * H * n * rec_bytes for _, _, n in dec_events], dtype=np.float64)
@@ -351,6 +354,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
     kern_avg_ms = float(kern_ms.mean())
     achieved = float(dec_bytes.mean()) / (kern_avg_ms / 1e3) / 1e9
     fmt_tag = "" if (args.key_format == "turboquant" and args.kbits == 3) else f"_{args.key_format}{kbits}"
+    fmt_tag += ("_f16norms" if nf16 else "") + (f"_paged{args.page_tokens}" if args.page_tokens else "")
     traffic = measured_traffic(f"decode_kernel_{name}{fmt_tag}")
     cold = cold_cache_decode(torch, tq, ctx, K, V, QS[0], B, H, Hq, L, cap, kbits, vbits, kqjl) \
         if name == "single" else None
@@ -372,7 +376,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         "data": f"synthetic ({args.data}-channel bf16 K/V, seeded)",
         "config": {"workload": cfg_text, "batch": B, "context": L, "decode_steps": NS, "kv_heads": H,
                    "q_heads": Hq, "head_dim": d, "key_bits": kbits + int(kqjl), "key_format": args.key_format,
-                   "value_bits": vbits, "cache_layout": (f"paged, {args.page_tokens}-token pages in a shuffled pool"
+                   "value_bits": vbits, "norms": args.norms, "cache_layout": (f"paged, {args.page_tokens}-token pages in a shuffled pool"
                                                          if args.page_tokens else "contiguous"),
                    "parallelism": "none (1 GPU)"},
         "quantize_vectors_per_s": vectors / (prefill_ms / 1e3), "prefill_ms": prefill_ms,

@@ -123,13 +123,17 @@ tq_status tq_ctx_codebook(const tq_ctx *ctx, int32_t bits, tq_codebook *out);
 
 /* A packed array of key or value records (formats above). */
 typedef struct {
-  uint32_t *bits;  /* d_: keys [n][W][B+1]; values [n/32][d][B]     */
-  float *norms;    /* d_: keys [n][2]; values [n]                    */
+  uint32_t *bits;  /* d_: keys [n][W][B+Q]; values [n/32][d][B]     */
+  void *norms;     /* d_: keys [n][1+Q]; values [n]; fp32, or fp16
+                      when norm_f16                                   */
   int64_t n;       /* record capacity; a multiple of 32 for values   */
   int32_t mse_bits;/* B: 1..4 (keys with qjl = 1: 0..4)              */
   int32_t is_key;  /* 1 = key format, 0 = values                     */
   int32_t qjl;     /* keys: Q, 1 = QJL sign word and ||r||, 0 = none;
                       values: 0                                       */
+  int32_t norm_f16;/* 1: norms stored as fp16 (round to nearest even,
+                      saturated at 65504): 2 bytes per norm instead of
+                      4, the compact-norm record format; 0: fp32      */
 } tq_packed;
 
 /* Quantize vectors ([ebisuda] 第1段階 and, for keys, 第2段階).

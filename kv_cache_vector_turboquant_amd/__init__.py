@@ -51,7 +51,7 @@ class CCodebook(ctypes.Structure):
 
 class CPacked(ctypes.Structure):
     _fields_ = [("bits", _c_vp), ("norms", _c_vp), ("n", _c_i64), ("mse_bits", _c_i32), ("is_key", _c_i32),
-                ("qjl", _c_i32)]
+                ("qjl", _c_i32), ("norm_f16", _c_i32)]
 
 
 class CCache(ctypes.Structure):
@@ -255,29 +255,33 @@ class Context:
 class Packed:
     """Device arrays of packed key or value records (format in include/tq.h)."""
 
-    def __init__(self, n: int, d: int, bits: int, is_key: bool, device="cuda", qjl: bool = True):
+    def __init__(self, n: int, d: int, bits: int, is_key: bool, device="cuda", qjl: bool = True,
+                 norm_f16: bool = False):
         """Keys: bits = B MSE bits, qjl = the QJL sign word and |r| (False: MSE-only
-        keys; bits = 0 with qjl: pure QJL keys). Values: bits = B, qjl ignored."""
+        keys; bits = 0 with qjl: pure QJL keys). Values: bits = B, qjl ignored.
+        norm_f16: compact records with fp16 norms."""
         torch = _torch()
         if not is_key and n % 32:
             raise ValueError("value capacity must be a multiple of 32")
         W = d // 32
         self.qjl = bool(qjl) and is_key
         self.n, self.d, self.bits, self.is_key = n, d, bits, is_key
+        self.norm_f16 = bool(norm_f16)
+        ndt = torch.float16 if self.norm_f16 else torch.float32
         if is_key:
             q = int(self.qjl)
             self.words = torch.zeros((n, W, bits + q), dtype=torch.int32, device=device)
-            self.norms = torch.zeros((n, 1 + q), dtype=torch.float32, device=device)
+            self.norms = torch.zeros((n, 1 + q), dtype=ndt, device=device)
         else:
             self.words = torch.zeros((n // 32, d, bits), dtype=torch.int32, device=device)
-            self.norms = torch.zeros((n,), dtype=torch.float32, device=device)
+            self.norms = torch.zeros((n,), dtype=ndt, device=device)
 
     def c(self) -> CPacked:
         return CPacked(self.words.data_ptr(), self.norms.data_ptr(), self.n, self.bits, 1 if self.is_key else 0,
-                       1 if self.qjl else 0)
+                       1 if self.qjl else 0, 1 if self.norm_f16 else 0)
 
     def host(self):
-        """(uint32 words, float32 norms) copied to host numpy arrays."""
+        """(uint32 words, norms: float32, or float16 when compact) copied to host numpy arrays."""
         return self.words.cpu().numpy().view(np.uint32), self.norms.cpu().numpy()
 
 
@@ -324,12 +328,13 @@ class KVCache:
 
     def __init__(self, batch: int, kv_heads: int, capacity: int, d: int, key_bits: int, value_bits: int,
                  device="cuda", key_qjl: bool = True, page_tokens: int | None = None, n_pages: int | None = None,
-                 block_table=None):
+                 block_table=None, norm_f16: bool = False):
         """key_bits = B MSE bits of the keys; key_qjl = False stores MSE-only keys,
         key_bits = 0 with key_qjl stores pure QJL keys. page_tokens (a multiple of
         256 dividing capacity) selects the paged layout: n_pages defaults to
         batch*capacity/page_tokens, block_table to sequence b owning pages
-        b*cols .. b*cols + cols - 1 (cols = capacity/page_tokens)."""
+        b*cols .. b*cols + cols - 1 (cols = capacity/page_tokens). norm_f16 stores
+        every norm as fp16 (compact records)."""
         torch = _torch()
         if capacity % 32:
             raise ValueError("capacity must be a multiple of 32")
@@ -348,8 +353,8 @@ class KVCache:
             n = batch * kv_heads * capacity
             self.n_pages = 0
             self.block_table = None
-        self.k = Packed(n, d, key_bits, True, device, qjl=key_qjl)
-        self.v = Packed(n, d, value_bits, False, device)
+        self.k = Packed(n, d, key_bits, True, device, qjl=key_qjl, norm_f16=norm_f16)
+        self.v = Packed(n, d, value_bits, False, device, norm_f16=norm_f16)
         self.seq_len = torch.zeros((batch,), dtype=torch.int32, device=device)
         self.batch, self.kv_heads, self.capacity, self.d = batch, kv_heads, capacity, d
         self.host_max_len = 0

@@ -442,6 +442,7 @@ static tq_status check_packed(const tq_ctx *ctx, const tq_packed *p, int want_ke
   if ((p->is_key != 0) != (want_key != 0))
     return fail(TQ_ERR_ARG, std::string(fn) + (want_key ? ": expected a key array" : ": expected a value array"));
   if (p->qjl != 0 && p->qjl != 1) return fail(TQ_ERR_ARG, std::string(fn) + ": qjl must be 0 or 1");
+  if (p->norm_f16 != 0 && p->norm_f16 != 1) return fail(TQ_ERR_ARG, std::string(fn) + ": norm_f16 must be 0 or 1");
   if (!p->is_key && p->qjl) return fail(TQ_ERR_ARG, std::string(fn) + ": value arrays have no QJL stage (qjl = 0)");
   if (p->mse_bits < (p->is_key && p->qjl ? 0 : 1) || p->mse_bits > TQ_MAX_BITS)
     return fail(TQ_ERR_UNSUPPORTED, std::string(fn) + ": mse_bits must be in [1, 4] ([0, 4] for keys with qjl = 1)");
@@ -505,6 +506,8 @@ static tq_status check_cache(const tq_ctx *ctx, const tq_kv_cache *c, const char
   tq_status s = check_packed(ctx, &c->k, 1, fn);
   if (s == TQ_OK) s = check_packed(ctx, &c->v, 0, fn);
   if (s != TQ_OK) return s;
+  if (c->k.norm_f16 != c->v.norm_f16)
+    return fail(TQ_ERR_ARG, std::string(fn) + ": keys and values of a cache must store their norms alike (norm_f16)");
   if (c->batch <= 0 || c->kv_heads <= 0 || c->capacity <= 0 || (c->capacity % 32) != 0)
     return fail(TQ_ERR_ARG, std::string(fn) + ": batch, kv_heads > 0 and capacity a positive multiple of 32 required");
   if (c->d_block_table == nullptr) {

@@ -30,8 +30,19 @@
 #include <cmath>
 
 #include "tq_internal.h"
+#include <hip/hip_fp16.h>
 
 namespace tq {
+
+// Norms are stored as fp32, or as fp16 (round to nearest even, saturated at the
+// largest finite fp16) when the array's norm_f16 flag is set.
+__device__ __forceinline__ void store_norm(void *base, int64_t i, float x, int f16) {
+  if (f16) reinterpret_cast<__half *>(base)[i] = __float2half_rn(fminf(x, 65504.f));
+  else reinterpret_cast<float *>(base)[i] = x;
+}
+__device__ __forceinline__ float load_norm(const void *base, int64_t i, int f16) {
+  return f16 ? __half2float(reinterpret_cast<const __half *>(base)[i]) : reinterpret_cast<const float *>(base)[i];
+}
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef int i4v __attribute__((ext_vector_type(4)));
@@ -64,7 +75,8 @@ struct GemmArgs {
   int bits, d;
   int qjl;               // keys: 1 = QJL sign word and |r| in the record, 0 = MSE-only
   uint32_t *bits_out;
-  float *norms_out;
+  void *norms_out;
+  int nf16;              // norms_out holds fp16 norms
   float *resid;          // keys: residual rows [stream*n_tokens + t][d]
   int64_t n_tokens;
   RecMap map;            // record of (stream, token)
@@ -73,7 +85,8 @@ struct GemmArgs {
   int64_t ldc;
   // scores B loader (packed keys)
   const uint32_t *kbits;
-  const float *knorm;
+  const void *knorm;
+  int knf16;             // knorm holds fp16 norms
   float qjl_scale;       // sqrt(pi/2)/m
   int rows_on_x;         // 1: blockIdx.x indexes row tiles (y: column tiles); 0: the reverse
 };
@@ -129,7 +142,7 @@ __device__ __forceinline__ void load_keys(const GemmArgs &g, const float *cent, 
       } else if (Q) {  // MSE-only keys have no QJL term
         const int i = k - g.d, w = i >> 5, o = i & 31;
         const uint32_t word = rec[w * (B + 1) + B] >> o;
-        const float a = g.qjl_scale * g.knorm[2 * t + 1];
+        const float a = g.qjl_scale * load_norm(g.knorm, 2 * t + 1, g.knf16);
 #pragma unroll
         for (int q = 0; q < 4; ++q) e[q] = ((word >> q) & 1u) ? a : -a;
       }
@@ -240,7 +253,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
     for (int b = 0; b < 2; ++b) {
       const int64_t col = col0 + wn * 64 + b * 32 + li;
       float scale = 1.f;
-      if constexpr (MODE == MODE_SCORES) scale = (col < g.N) ? g.knorm[(1 + g.qjl) * col] : 0.f;
+      if constexpr (MODE == MODE_SCORES) scale = (col < g.N) ? load_norm(g.knorm, (1 + g.qjl) * col, g.knf16) : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = row0 + wm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
@@ -270,7 +283,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
           if (in && g.qjl) g.resid[(s * g.n_tokens + t) * (int64_t)g.d + col] = live ? y - (B > 0 ? cent[idx] : 0.f) : 0.f;
           mybits = live ? (uint32_t)idx : 0u;
         } else {
-          live = in && g.norms_out[2 * g.map.rec(s, t)] > 0.f;  // signs only exist with the QJL stage: 2 norms
+          live = in && load_norm(g.norms_out, 2 * g.map.rec(s, t), g.nf16) > 0.f;  // signs only exist with the QJL stage: 2 norms
           mybits = (live && acc[b][r] >= 0.f) ? 1u : 0u;
         }
         const int np = (MODE == MODE_KEY_CODES) ? B : 1;
@@ -298,8 +311,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
         }
       }
       if (ct == 0 && gl == 0 && t < g.n_tokens) {
-        if constexpr (MODE == MODE_KEY_CODES) g.norms_out[(1 + g.qjl) * rec] = sqrtf(stat[rl]);
-        else g.norms_out[2 * rec + 1] = sqrtf(stat[rl]);
+        if constexpr (MODE == MODE_KEY_CODES) store_norm(g.norms_out, (1 + g.qjl) * rec, sqrtf(stat[rl]), g.nf16);
+        else store_norm(g.norms_out, 2 * rec + 1, sqrtf(stat[rl]), g.nf16);
       }
     }
   } else if constexpr (MODE == MODE_VAL_CODES) {
@@ -330,7 +343,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
       for (int q = 0; q < 2; ++q) {
         const int cl = (tid >> 2) + 64 * q;
         const int64_t t = col0 + cl;
-        if (t < g.n_tokens) g.norms_out[g.map.rec(s, t)] = sqrtf(stat[cl]);
+        if (t < g.n_tokens) store_norm(g.norms_out, g.map.rec(s, t), sqrtf(stat[cl]), g.nf16);
       }
     }
   }
@@ -366,7 +379,8 @@ struct Q128Args {
   const uint16_t *sk2;     // [2][128][128] bf16 parts of S: [part][sketch row][coordinate]
   const DeviceTables *tables;
   uint32_t *bits_out;
-  float *norms_out;
+  void *norms_out;
+  int nf16;                // norms_out holds fp16 norms
   RecMap map;              // record of (stream, token)
 };
 
@@ -667,10 +681,10 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
               float r2 = 0.f;
 #pragma unroll
               for (int v = 0; v < NW; ++v) r2 += rho2[v][tok];
-              *reinterpret_cast<float2 *>(a.norms_out + 2 * rec) =
-                  n > 0.f ? make_float2(n, sqrtf(r2)) : make_float2(0.f, 0.f);
+              store_norm(a.norms_out, 2 * rec, n, a.nf16);
+              store_norm(a.norms_out, 2 * rec + 1, n > 0.f ? sqrtf(r2) : 0.f, a.nf16);
             } else {
-              a.norms_out[rec] = n;
+              store_norm(a.norms_out, rec, n, a.nf16);
             }
           }
         }
@@ -721,7 +735,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
             dst[p] = word & live;
           }
         }
-        if (tid < nv) a.norms_out[a.map.rec(s, t0 + tid)] = nrm[tid];
+        if (tid < nv) store_norm(a.norms_out, a.map.rec(s, t0 + tid), nrm[tid], a.nf16);
       }
     }
     // the staging buffers are reused only after the next iteration's first barrier
@@ -785,6 +799,7 @@ static hipError_t quant128(const tq_ctx *ctx, bool keys, const void *x, int64_t 
   q.tables = ctx->d_tables;
   q.bits_out = out->bits;
   q.norms_out = out->norms;
+  q.nf16 = out->norm_f16;
   q.map = map;
   return keys ? launch_quant128<true>(q, out->mse_bits, out->qjl != 0, st)
               : launch_quant128<false>(q, out->mse_bits, false, st);
@@ -808,6 +823,7 @@ hipError_t launch_quantize_keys(const tq_ctx *ctx, const void *x, int is_bf16, i
   g.d = d;
   g.bits_out = out->bits;
   g.norms_out = out->norms;
+  g.nf16 = out->norm_f16;
   g.qjl = out->qjl;
   g.resid = work;
   g.n_tokens = n_tokens;
@@ -844,6 +860,7 @@ hipError_t launch_quantize_values(const tq_ctx *ctx, const void *x, int is_bf16,
   g.d = d;
   g.bits_out = out->bits;
   g.norms_out = out->norms;
+  g.nf16 = out->norm_f16;
   g.n_tokens = n_tokens;
   g.map = map;
   dim3 grid((unsigned)((n_tokens + GBN - 1) / GBN), (d + GBM - 1) / GBM, (unsigned)n_streams);
@@ -975,6 +992,7 @@ hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t 
   g3.d = d;
   g3.kbits = keys->bits;
   g3.knorm = keys->norms;
+  g3.knf16 = keys->norm_f16;
   g3.qjl_scale = (float)(std::sqrt(M_PI / 2.0) / d);
   g3.c = sc;
   g3.ldc = keys->n;
@@ -1033,9 +1051,9 @@ constexpr int QC = 2;              // per-head query constants: units of the q_r
 
 struct DecodeArgs {
   const uint32_t *kbits;
-  const float *knorm;
+  const void *knorm;     // fp32, or fp16 with nf16
   const uint32_t *vbits;
-  const float *vnorm;
+  const void *vnorm;
   const int32_t *seq_len;
   int kbitsB, vbitsB;    // MSE bits of keys / values
   int kqjl;              // keys carry the QJL sign word and |r|
@@ -1065,7 +1083,8 @@ struct DecodeArgs {
   const void *ka, *va;   // [batch][kv_heads][DD], the query dtype
   const float *sk;       // S, row-major
   uint32_t *kbits_w, *vbits_w;
-  float *knorm_w, *vnorm_w;
+  void *knorm_w, *vnorm_w;
+  int nf16;              // the cache's norms are fp16
   int32_t *wlen;         // [batch] length after the append; read by decode_kernel instead of seq_len
   int32_t *len_inc;      // lengths the merge kernel advances (fused step only)
 };
@@ -1232,9 +1251,9 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
       for (int p = 0; p < np; ++p) dst[p] = words[p];
     }
     if (r == 0) {
-      a.knorm_w[(1 + kQ) * rec] = nk;
-      if (kQ) a.knorm_w[2 * rec + 1] = live ? sqrtf(L.red[hs][4] + L.red[hs][5]) : 0.f;
-      a.vnorm_w[rec] = nv;
+      store_norm(a.knorm_w, (1 + kQ) * rec, nk, a.nf16);
+      if (kQ) store_norm(a.knorm_w, 2 * rec + 1, live ? sqrtf(L.red[hs][4] + L.red[hs][5]) : 0.f, a.nf16);
+      store_norm(a.vnorm_w, rec, nv, a.nf16);
     }
   }
 }
@@ -1531,8 +1550,9 @@ __device__ __forceinline__ int64_t pick_span(int si, int64_t r0, int64_t r1, int
 
 // KB MSE bits of the keys (0: pure QJL keys), QJL: the keys carry the sign word
 // and |r| (false: MSE-only keys)
-// SPANS: the chunk's records come in several runs (pages smaller than the chunk)
-template <int KB, int VB, bool QJL, bool SPANS>
+// SPANS: the chunk's records come in several runs (pages smaller than the chunk);
+// NF16: the cache's norms are fp16
+template <int KB, int VB, bool QJL, bool SPANS, bool NF16>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   constexpr int KM = KB > 0 ? 1 << (KB - 1) : 0;  // key Walsh masks
   constexpr int KQ = QJL ? 1 : 0;
@@ -1639,8 +1659,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         // a tile lies in one span
         const int64_t rr = SPANS ? pick_span(min((base + u) * 16, n - 1) >> slg, rs0, rs1, rs2, rs3) : rs0;
         const char *kb0 = reinterpret_cast<const char *>(a.kbits + rr * DW * NPL);
-        const char *kn0 = reinterpret_cast<const char *>(a.knorm + (1 + KQ) * rr);
-        const char *vn0 = reinterpret_cast<const char *>(a.vnorm + rr);
+        constexpr int NB = NF16 ? 2 : 4;  // bytes per norm
+        const char *kn0 = reinterpret_cast<const char *>(a.knorm) + (1 + KQ) * rr * NB;
+        const char *vn0 = reinterpret_cast<const char *>(a.vnorm) + rr * NB;
         const uint32_t tl = SPANS ? tc & smask : tc;  // position in the span
         const char *src = kb0 + (tl * (uint32_t)(DW * NPL * 4) + kgo);
         if constexpr (NPL == 4) {
@@ -1650,9 +1671,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int p = 0; p < NPL; ++p) bf.pl[u][p] = reinterpret_cast<const uint32_t *>(src)[p];
         }
-        if constexpr (QJL) bf.kn[u] = *reinterpret_cast<const float2 *>(kn0 + (tl << 3));
-        else bf.kn[u] = make_float2(*reinterpret_cast<const float *>(kn0 + (tl << 2)), 0.f);
-        bf.vn[u] = *reinterpret_cast<const float *>(vn0 + (tl << 2));
+        if constexpr (NF16) {
+          if constexpr (QJL) bf.kn[u] = __half22float2(*reinterpret_cast<const __half2 *>(kn0 + (tl << 2)));
+          else bf.kn[u] = make_float2(__half2float(*reinterpret_cast<const __half *>(kn0 + (tl << 1))), 0.f);
+          bf.vn[u] = __half2float(*reinterpret_cast<const __half *>(vn0 + (tl << 1)));
+        } else {
+          if constexpr (QJL) bf.kn[u] = *reinterpret_cast<const float2 *>(kn0 + (tl << 3));
+          else bf.kn[u] = make_float2(*reinterpret_cast<const float *>(kn0 + (tl << 2)), 0.f);
+          bf.vn[u] = *reinterpret_cast<const float *>(vn0 + (tl << 2));
+        }
       }
     };
     // the wave's first key tiles are requested before anything else
@@ -1941,10 +1968,14 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
 
 template <int KB, int VB, bool QJL>
 static hipError_t launch_decode_kv(const DecodeArgs &a, dim3 grid, size_t shm, hipStream_t st) {
-  if (a.chunk > (1 << a.span_lg))
-    hipLaunchKernelGGL((decode_kernel<KB, VB, QJL, true>), grid, dim3(256), shm, st, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<KB, VB, QJL, false>), grid, dim3(256), shm, st, a);
+  const bool spans = a.chunk > (1 << a.span_lg);
+  if (a.nf16) {
+    if (spans) hipLaunchKernelGGL((decode_kernel<KB, VB, QJL, true, true>), grid, dim3(256), shm, st, a);
+    else hipLaunchKernelGGL((decode_kernel<KB, VB, QJL, false, true>), grid, dim3(256), shm, st, a);
+  } else {
+    if (spans) hipLaunchKernelGGL((decode_kernel<KB, VB, QJL, true, false>), grid, dim3(256), shm, st, a);
+    else hipLaunchKernelGGL((decode_kernel<KB, VB, QJL, false, false>), grid, dim3(256), shm, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -1958,6 +1989,7 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.knorm = cache->k.norms;
   a.vbits = cache->v.bits;
   a.vnorm = cache->v.norms;
+  a.nf16 = cache->k.norm_f16;
   a.seq_len = cache->d_seq_len;
   a.kbitsB = cache->k.mse_bits;
   a.kqjl = cache->k.qjl;
@@ -2080,10 +2112,11 @@ struct AppendArgs {
   const float *rot_t, *sketch_t;
   const DeviceTables *tables;
   uint32_t *kbits;
-  float *knorm;
+  void *knorm;
   uint32_t *vbits;
-  float *vnorm;
+  void *vnorm;
   int32_t *seq_len;
+  int nf16;  // fp16 norms
   int kB, vB, kv_heads, capacity;
   int kQ;  // keys carry the QJL sign word and |r|
   RecMap map;
@@ -2149,9 +2182,9 @@ __global__ void __launch_bounds__(DD) append_kernel(AppendArgs a) {
     for (int p = 0; p < np; ++p) dst[p] = words[p];
   }
   if (j == 0) {
-    a.knorm[(1 + a.kQ) * rec] = nrm;
-    if (a.kQ) a.knorm[2 * rec + 1] = live ? rho : 0.f;
-    a.vnorm[rec] = nv;
+    store_norm(a.knorm, (1 + a.kQ) * rec, nrm, a.nf16);
+    if (a.kQ) store_norm(a.knorm, 2 * rec + 1, live ? rho : 0.f, a.nf16);
+    store_norm(a.vnorm, rec, nv, a.nf16);
   }
   // ---- value: codes into the token-major word of this coordinate ----
   const bool livev = nv > 0.f;
@@ -2186,6 +2219,7 @@ hipError_t launch_append(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   a.knorm = cache->k.norms;
   a.vbits = cache->v.bits;
   a.vnorm = cache->v.norms;
+  a.nf16 = cache->k.norm_f16;
   a.seq_len = cache->d_seq_len;
   a.kB = cache->k.mse_bits;
   a.kQ = cache->k.qjl;

@@ -35,7 +35,7 @@ from scipy import special
 __all__ = [
     "rotation_from_gaussian", "sketch_from_gaussian", "coord_density", "coord_cdf",
     "lloyd_max", "Codebook", "codebook", "encode", "Encoded", "query_prep", "qjl_constant",
-    "scores", "scores_from_parts", "dequantize_keys", "attention_decode", "attention_prefill", "topk",
+    "scores", "scores_from_parts", "dequantize_keys", "attention_decode", "attention_prefill", "topk", "stored_norms",
     "recall_at_k", "pack_keys", "unpack_keys", "pack_values", "unpack_values",
     "key_record_bytes", "value_record_bytes",
 ]
@@ -280,7 +280,8 @@ def query_prep(Qv: np.ndarray, Pi: np.ndarray, S: np.ndarray):
 def scores_from_parts(q_rot, q_s, idx, sigma, norm, rho, cb: Codebook | None, m: int):
     """s = n (<q_rot, c[idx]> + sqrt(pi/2)/m * rho * <q_s, 2 sigma - 1>) for all
     (query, key) pairs: the stage-1 inner product plus the QJL correction
-    [ebisuda, 第2段階; hakusoku, QJL]. norm, rho are the stored fp32 values.
+    [ebisuda, 第2段階; hakusoku, QJL]. norm, rho are the stored values (fp32 or
+    compact fp16).
     MSE-only keys (sigma None) keep the first term, pure QJL keys (cb None) the
     second."""
     nn = np.asarray(norm, dtype=np.float64)[None, :]
@@ -380,16 +381,29 @@ def recall_at_k(found: np.ndarray, exact: np.ndarray) -> float:
 #   bits  : uint32 [W_t][d][B]; word [t//32][j][p] holds bit p of idx[t][j]
 #           at bit position t % 32. Unused tail bits are 0.
 #   norms : float32 [n] = ||v||.
+# Compact norms (norm_f16): every norm stored as float16 instead, rounded to
+# nearest even from the exact value and saturated at the largest finite
+# float16, 65504 (reading: the pages fix no norm precision).
 
-def key_record_bytes(d: int, bits: int, qjl: bool = True) -> int:
-    return (d // 32) * (bits + int(qjl)) * 4 + 4 * (1 + int(qjl))
-
-
-def value_record_bytes(d: int, bits: int) -> int:
-    return d * bits // 8 + 4
+F16_MAX = 65504.0
 
 
-def pack_keys(enc: Encoded, bits: int, qjl: bool = True) -> dict:
+def stored_norms(x, norm_f16: bool = False) -> np.ndarray:
+    """Norms as a record stores them: float32, or float16 (nearest even,
+    saturated at F16_MAX) with compact norms."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.minimum(x, F16_MAX).astype(np.float16) if norm_f16 else x.astype(np.float32)
+
+
+def key_record_bytes(d: int, bits: int, qjl: bool = True, norm_f16: bool = False) -> int:
+    return (d // 32) * (bits + int(qjl)) * 4 + (2 if norm_f16 else 4) * (1 + int(qjl))
+
+
+def value_record_bytes(d: int, bits: int, norm_f16: bool = False) -> int:
+    return d * bits // 8 + (2 if norm_f16 else 4)
+
+
+def pack_keys(enc: Encoded, bits: int, qjl: bool = True, norm_f16: bool = False) -> dict:
     idx, sig = enc.idx, enc.sigma
     n, d = idx.shape
     assert d % 32 == 0 and (not qjl or sig.shape == (n, d))
@@ -403,9 +417,9 @@ def pack_keys(enc: Encoded, bits: int, qjl: bool = True) -> dict:
         if qjl:
             out[:, w, bits] = np.sum(sig[:, 32 * w:32 * w + 32].astype(np.uint64) * pos, axis=1)
     if qjl:
-        norms = np.stack([enc.norm.astype(np.float32), enc.rho.astype(np.float32)], axis=1)
+        norms = np.stack([stored_norms(enc.norm, norm_f16), stored_norms(enc.rho, norm_f16)], axis=1)
     else:
-        norms = enc.norm.astype(np.float32)[:, None]
+        norms = stored_norms(enc.norm, norm_f16)[:, None]
     return {"bits": out.astype(np.uint32), "norms": norms}
 
 
@@ -422,7 +436,7 @@ def unpack_keys(words: np.ndarray, d: int, bits: int, qjl: bool = True):
     return idx, sig
 
 
-def pack_values(enc: Encoded, bits: int) -> dict:
+def pack_values(enc: Encoded, bits: int, norm_f16: bool = False) -> dict:
     idx = enc.idx
     n, d = idx.shape
     nb = (n + 31) // 32
@@ -433,7 +447,7 @@ def pack_values(enc: Encoded, bits: int) -> dict:
     out = np.zeros((nb, d, bits), dtype=np.uint64)
     for p in range(bits):
         out[:, :, p] = np.sum(((blk >> np.uint64(p)) & np.uint64(1)) * pos, axis=1)
-    return {"bits": out.astype(np.uint32), "norms": enc.norm.astype(np.float32)}
+    return {"bits": out.astype(np.uint32), "norms": stored_norms(enc.norm, norm_f16)}
 
 
 def unpack_values(words: np.ndarray, d: int, bits: int, n: int):

@@ -33,9 +33,23 @@ def check_codes(g_idx, enc, cb, what="codes"):
     return flips.any(axis=1)
 
 
-def check_key_records(words, norms, enc, cb, bits, d, qjl=True):
+def norms_match(g, ref, rel, absol, f16=False):
+    """Stored norms against the oracle's exact ones: within rel * ref + absol
+    (fp32), or (compact fp16 norms) the nearest-even fp16 of a value within
+    that band: between the roundings of its two ends (rounding is monotonic)."""
+    g = np.asarray(g).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if not f16:
+        return bool(np.all(np.abs(g - ref) <= rel * ref + absol))
+    lo = T.stored_norms(np.maximum(ref * (1 - rel) - absol, 0.0), True).astype(np.float64)
+    hi = T.stored_norms(ref * (1 + rel) + absol, True).astype(np.float64)
+    return bool(np.all((g >= lo) & (g <= hi)))
+
+
+def check_key_records(words, norms, enc, cb, bits, d, qjl=True, norm_f16=False):
     """Key records of any variant: MSE-only (qjl False: codes and ||k||) and
-    pure QJL (bits 0, cb None: signs and both norms) included."""
+    pure QJL (bits 0, cb None: signs and both norms) included; norm_f16:
+    compact records with fp16 norms."""
     norms = np.asarray(norms).reshape(words.shape[0], 1 + int(qjl))
     g_idx, g_sig = T.unpack_keys(words, d, bits, qjl)
     if bits > 0:
@@ -52,19 +66,16 @@ def check_key_records(words, norms, enc, cb, bits, d, qjl=True):
             assert not bad.any(), f"sign mismatches outside the band: {int(bad.sum())}"
         assert sflip.sum() <= MAX_FRAC * g_sig.size
         nsflip = int(sflip.sum())
-    n_ref = enc.norm
-    assert np.all(np.abs(norms[:, 0] - n_ref) <= 2e-6 * n_ref + 1e-30), "||k|| mismatch"
+    assert norms_match(norms[:, 0], enc.norm, 2e-6, 1e-30, norm_f16), "||k|| mismatch"
     if qjl:
-        rr = enc.rho[live]
-        assert np.all(np.abs(norms[live, 1] - rr) <= 2e-5 * rr + 1e-7), "||r|| mismatch"
+        assert norms_match(norms[live, 1], enc.rho[live], 2e-5, 1e-7, norm_f16), "||r|| mismatch"
     return int(cascade.sum()), nsflip
 
 
-def check_value_records(words, norms, enc, cb, bits, d, n):
+def check_value_records(words, norms, enc, cb, bits, d, n, norm_f16=False):
     g_idx = T.unpack_values(words, d, bits, n)
     check_codes(g_idx, enc, cb, "value codes")
-    n_ref = enc.norm
-    assert np.all(np.abs(norms[:n] - n_ref) <= 2e-6 * n_ref + 1e-30), "||v|| mismatch"
+    assert norms_match(norms[:n], enc.norm, 2e-6, 1e-30, norm_f16), "||v|| mismatch"
 
 
 def check_scores(s_gpu, s_ref, qnorm, xnorm):

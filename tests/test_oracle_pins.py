@@ -524,6 +524,50 @@ def test_record_bytes():
     assert (pq["bits"].nbytes + pq["norms"].nbytes) // 64 == 24
 
 
+def test_compact_norms_rounding_and_saturation():
+    """Compact norms follow IEEE half precision: exactly representable values
+    keep their bit patterns (1.0 = 0x3C00, 0.5 = 0x3800, 2.5 = 0x4100, the
+    largest finite 65504 = 0x7BFF), ties go to the even neighbour (1 + 2^-11
+    -> 1.0, 1 + 3*2^-11 -> 1 + 2^-9), larger values saturate at 65504, and the
+    relative error is at most 2^-11 over the normal range."""
+    x = np.array([1.0, 0.5, 2.5, 65504.0, 1 + 2 ** -11, 1 + 3 * 2 ** -11, 65519.0, 7e4, 1e9, 0.0])
+    h = T.stored_norms(x, True)
+    assert h.dtype == np.float16
+    assert h[:4].view(np.uint16).tolist() == [0x3C00, 0x3800, 0x4100, 0x7BFF]
+    assert float(h[4]) == 1.0 and float(h[5]) == 1 + 2 ** -9
+    assert np.all(h[6:9].view(np.uint16) == 0x7BFF) and float(h[9]) == 0.0
+    v = np.exp(np.random.default_rng(5).uniform(np.log(2.0 ** -14), np.log(65504.0), 100000))
+    assert np.max(np.abs(T.stored_norms(v, True).astype(np.float64) / v - 1)) <= 2.0 ** -11
+    assert T.stored_norms(x, False).dtype == np.float32
+
+
+def test_compact_norm_scores_stay_within_the_rounding_bound():
+    """With compact norms every score moves by at most the fp16 rounding of
+    ||k|| and ||r|| acting on its two terms: |s16 - s32| <= 2^-11 n |a| +
+    (2^-10 + 2^-22) n |b| for s = n (a + b) (a the stage-1 term, b the QJL term);
+    record bytes shrink by 2 per norm."""
+    d = 128
+    Pi, S = _ctx(d)
+    cb = T.codebook(d, 3)
+    K = synth.outlier_kv(6, (1,), synth.TAG_SCALES_K, (500, d))
+    Q = synth.gaussian(6, (2,), (8, d))
+    enc = T.encode(K, Pi, cb, S)
+    k32, k16 = T.pack_keys(enc, 3), T.pack_keys(enc, 3, norm_f16=True)
+    assert k16["norms"].dtype == np.float16
+    s32, s16 = T.scores(Q, Pi, S, cb, k32), T.scores(Q, Pi, S, cb, k16)
+    idx, sig = T.unpack_keys(k32["bits"], d, 3)
+    q_rot, q_s = T.query_prep(Q, Pi, S)
+    ones = np.ones(500)
+    a = T.scores_from_parts(q_rot, q_s, idx, None, ones, None, cb, d)
+    b = T.scores_from_parts(q_rot, q_s, idx, sig, ones, k32["norms"][:, 1], None, d)
+    n = k32["norms"][:, 0].astype(np.float64)[None, :]
+    assert np.all(np.abs(s16 - s32) <= 2.0 ** -11 * n * np.abs(a) + (2.0 ** -10 + 2.0 ** -22) * n * np.abs(b) + 1e-12)
+    assert T.key_record_bytes(d, 3, norm_f16=True) == 68 and T.value_record_bytes(d, 3, norm_f16=True) == 50
+    assert T.key_record_bytes(d, 3, qjl=False, norm_f16=True) == 50 and T.key_record_bytes(d, 0, norm_f16=True) == 20
+    pv = T.pack_values(T.encode(K, Pi, cb), 3, norm_f16=True)
+    assert pv["norms"].nbytes == 2 * 500 and (k16["bits"].nbytes + k16["norms"].nbytes) == 68 * 500
+
+
 # --- packing format ---------------------------------------------------------------
 
 def _golden_words(name):
