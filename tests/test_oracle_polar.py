@@ -1,0 +1,123 @@
+"""Pins of the PolarQuant oracle (oracle/polarquant.py) against what the
+mathematics fixes: the polar transform is invertible and keeps the norm, the
+angle laws integrate to one and match Monte-Carlo angles of random
+directions, the 1-bit level-2 codebook has a closed form, the level-1
+codebook is the uniform grid, Lloyd's fixed point holds, codes are the
+nearest stored centroid, rebuilt vectors converge to the input as bits grow,
+and the packed layout matches a hand-built fixture."""
+import math
+
+import numpy as np
+import pytest
+from scipy import integrate, stats
+
+import synth
+from oracle import polarquant as PQ
+from oracle import turboquant as T
+
+
+def test_polar_transform_inverts_and_keeps_the_norm():
+    Y = synth.gaussian(61, (1,), (50, 128)).astype(np.float64)
+    r, levels = PQ.polar_transform(Y)
+    assert len(levels) == 7 and [a.shape[1] for a in levels] == [64, 32, 16, 8, 4, 2, 1]
+    assert np.allclose(r, np.linalg.norm(Y, axis=1), rtol=1e-13)
+    assert np.max(np.abs(PQ.polar_inverse(r, levels) - Y)) < 1e-12
+    assert np.all(levels[0] >= -math.pi) and np.all(levels[0] <= math.pi)
+    for a in levels[1:]:
+        assert np.all(a >= 0) and np.all(a <= math.pi / 2)
+    # a 2-d vector: the textbook polar coordinates
+    r2, l2 = PQ.polar_transform(np.array([[3.0, 4.0]]))
+    assert r2[0] == 5.0 and abs(l2[0][0, 0] - math.atan2(4, 3)) < 1e-15
+
+
+@pytest.mark.parametrize("level", [1, 2, 3, 5, 7])
+def test_angle_laws_normalized_and_match_random_directions(level):
+    lo, hi = (-math.pi, math.pi) if level == 1 else (0.0, math.pi / 2)
+    mass, _ = integrate.quad(lambda t: float(PQ.angle_density(level, t)), lo, hi, limit=200)
+    assert abs(mass - 1) < 1e-10
+    # angles of Gaussian vectors (any rotation-invariant law): KS against the CDF
+    Y = synth.gaussian(62, (level,), (4000, 128)).astype(np.float64)
+    _, levels = PQ.polar_transform(Y)
+    sample = levels[level - 1].ravel()[:20000]
+    ks = stats.kstest(sample, lambda x: PQ.angle_cdf(level, x))
+    assert ks.pvalue > 1e-3
+    if level == 2:  # closed form: f = sin(2 psi), F = sin^2(psi)
+        t = np.linspace(0, math.pi / 2, 9)
+        assert np.allclose(PQ.angle_density(2, t), np.sin(2 * t), atol=1e-14)
+        assert np.allclose(PQ.angle_cdf(2, t), np.sin(t) ** 2, atol=1e-14)
+
+
+def test_angle_codebook_closed_forms():
+    # level 2, 1 bit: split at pi/4, centroids E[psi | psi < pi/4] = 1/2 and pi/2 - 1/2
+    c = PQ.lloyd_max_angle(2, 1)
+    assert np.allclose(c, [0.5, math.pi / 2 - 0.5], atol=1e-11)
+    # level 1: the uniform grid, cells from -pi
+    cb = PQ.angle_codebook(1, 3)
+    assert np.allclose(cb.centroids64, -math.pi + (np.arange(8) + 0.5) * math.pi / 4)
+    assert np.allclose(cb.boundaries, -math.pi + np.arange(1, 8) * math.pi / 4, atol=1e-6)
+
+
+@pytest.mark.parametrize("level,bits", [(2, 3), (4, 2), (7, 3)])
+def test_lloyd_fixed_point_and_symmetry(level, bits):
+    c = PQ.lloyd_max_angle(level, bits)
+    assert np.all(np.diff(c) > 0)
+    assert np.allclose(c + c[::-1], math.pi / 2, atol=1e-12)
+    e = np.concatenate(([0.0], 0.5 * (c[:-1] + c[1:]), [math.pi / 2]))
+    for i in range(len(c)):
+        m0, _ = integrate.quad(lambda t: float(PQ.angle_density(level, t)), e[i], e[i + 1], limit=200)
+        m1, _ = integrate.quad(lambda t: t * float(PQ.angle_density(level, t)), e[i], e[i + 1], limit=200)
+        assert abs(m1 / m0 - c[i]) < 1e-9
+
+
+def test_codes_are_the_nearest_stored_centroid():
+    pcb = PQ.polar_codebooks(128, 4, 3)
+    rng = np.random.default_rng(63)
+    for lv in (2, 5):
+        cb = pcb.levels[lv - 1]
+        psi = rng.uniform(0, math.pi / 2, 5000)
+        k = PQ.angle_codes(psi, cb)
+        brute = np.argmin(np.abs(psi[:, None] - cb.centroids64[None, :]), axis=1)
+        near = np.min(np.abs(psi[:, None] - cb.boundaries.astype(np.float64)[None, :]), axis=1) < 1e-6
+        assert np.all((k == brute) | near)
+
+
+def test_rebuild_converges_and_scores_equal_dequantized_dot():
+    """Reconstruction error falls with the bit widths (a monotone invariant);
+    the rotated-domain score equals <q, Pi^T y_hat> computed in the original
+    domain."""
+    d = 128
+    Pi = T.rotation_from_gaussian(synth.gaussian_matrix(0, synth.TAG_ROTATION, d, d))
+    X = synth.gaussian(64, (1,), (200, d)).astype(np.float64)
+    errs = []
+    for b1, b2 in ((2, 1), (3, 2), (4, 3), (4, 4)):
+        pcb = PQ.polar_codebooks(d, b1, b2)
+        enc = PQ.polar_encode(X, Pi, pcb)
+        Yh = PQ.polar_rebuild(enc.codes, enc.norm, pcb)
+        Y = X @ Pi.astype(np.float64).T
+        errs.append(np.mean(np.sum((Yh - Y) ** 2, axis=1) / np.sum(Y ** 2, axis=1)))
+    assert all(errs[i + 1] < errs[i] for i in range(3)) and errs[-1] < 0.05
+    pcb = PQ.polar_codebooks(d, 4, 3)
+    keys = PQ.pack_polar(PQ.polar_encode(X, Pi, pcb), pcb)
+    Q = synth.gaussian(64, (2,), (5, d)).astype(np.float64)
+    s = PQ.polar_scores(Q, Pi, pcb, keys)
+    Kh = PQ.polar_rebuild(PQ.unpack_polar(keys["bits"], pcb), keys["norms"], pcb) @ Pi.astype(np.float64)
+    assert np.max(np.abs(s - Q @ Kh.T)) < 1e-9 * np.max(np.abs(s))
+
+
+def test_record_layout_and_bytes():
+    """d = 8, b1 = 4, b2 = 3: four level-1 codes in one word (4 bits each),
+    three higher codes (level 2 nodes 0, 1, then level 3) in one word at bits
+    0, 3, 6; 60 bytes per d = 128 record at (4, 3): 4.27x against fp16."""
+    pcb = PQ.polar_codebooks(8, 4, 3)
+    enc = PQ.PolarEncoded([np.array([[1, 15, 0, 9]]), np.array([[5, 2]]), np.array([[7]])], np.array([2.0]), [])
+    rec = PQ.pack_polar(enc, pcb)
+    assert rec["bits"].tolist() == [[0x90F1, 5 | (2 << 3) | (7 << 6)]]
+    back = PQ.unpack_polar(rec["bits"], pcb)
+    assert [c.tolist() for c in back] == [[[1, 15, 0, 9]], [[5, 2]], [[7]]]
+    assert PQ.polar_record_bytes(128, 4, 3) == 60 and abs(256 / 60 - 4.27) < 0.01
+    # codes crossing a word boundary (b2 = 3: code 10 spans bits 30..32)
+    pcb = PQ.polar_codebooks(32, 4, 3)
+    codes = [np.arange(16)[None, :] % 16, (np.arange(8)[None, :] * 3) % 8, np.array([[1, 6, 3, 5]]),
+             np.array([[2, 7]]), np.array([[4]])]
+    rec = PQ.pack_polar(PQ.PolarEncoded(codes, np.array([1.0]), []), pcb)
+    assert [c.tolist() for c in PQ.unpack_polar(rec["bits"], pcb)] == [c.tolist() for c in codes]
