@@ -103,6 +103,46 @@ tq_status tq_codebook_build(int32_t d, int32_t bits, tq_codebook *out);
  * Errors: TQ_ERR_ARG (NULL), TQ_ERR_UNSUPPORTED (d). */
 tq_status tq_rotation_build(int32_t d, const double *h_g, float *h_out);
 
+/* PolarQuant angle codebook ([arxiv-summary] 3.中核となる技術的要素: codebooks
+ * designed from the distribution of the angles of the recursive polar
+ * transformation). Level 1 (angles of coordinate pairs, uniform on the circle):
+ * the uniform grid with cells from -pi. Level l >= 2 (angles of radius pairs,
+ * m = 2^(l-1): sin^2(psi) ~ Beta(m/2, m/2) on [0, pi/2]): Lloyd-Max, made
+ * symmetric about pi/4. centroid: fp64; boundary, cos_c, sin_c: fp32 (of the
+ * fp64 midpoints / cos / sin of the centroids); code = #{boundary <= psi}. */
+#define TQ_POLAR_MAX_LEVEL 12
+typedef struct {
+  int32_t level;
+  int32_t bits;
+  double centroid[16];
+  float boundary[15];
+  float cos_c[16];
+  float sin_c[16];
+} tq_angle_codebook;
+
+/* Host only. level in [1, 12], bits in [1, 4].
+ * Errors: TQ_ERR_ARG (out NULL), TQ_ERR_UNSUPPORTED (level or bits). */
+tq_status tq_angle_codebook_build(int32_t level, int32_t bits, tq_angle_codebook *out);
+
+/* A packed array of PolarQuant key records, d = 128 ([arxiv-summary]
+ * 3.中核となる技術的要素; [gemilab] PolarQuant：極座標変換による根本的削減).
+ * Vector x: y = Pi x (random preconditioning by the context's rotation), then
+ * the recursive polar transformation: level 1 turns coordinate pair i into
+ * (hypot, atan2(y[2i+1], y[2i])), level l >= 2 turns the radius pair (2i,
+ * 2i+1) of level l-1 into (hypot, atan2(right, left)); 64 + 63 angles and the
+ * radius ||x||. Each angle is coded by its level's tq_angle_codebook (b1 bits
+ * at level 1, b2 at the higher levels). Record: w1 = ceil(64 b1 / 32) words of
+ * level-1 codes (code i at bit i*b1 of that little-endian stream), then
+ * w2 = ceil(63 b2 / 32) words of higher codes (level 2 nodes first, code j at
+ * bit j*b2); norms[i] = ||x|| (fp32). 60 bytes per vector at (b1, b2) = (4, 3):
+ * 4.27x against fp16. */
+typedef struct {
+  uint32_t *bits;  /* d_: [n][w1 + w2] */
+  float *norms;    /* d_: [n] */
+  int64_t n;       /* records */
+  int32_t b1, b2;  /* bits per level-1 / higher-level angle, 1..4 */
+} tq_polar_packed;
+
 /* Library context: the rotation Pi (d x d), the sketch S (d x d) and the
  * codebooks for bits 1..4, on host and device. Immutable after creation and
  * safe to share across streams on its device. */
@@ -267,6 +307,26 @@ size_t tq_scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk
 tq_status tq_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t nq, const tq_packed *keys,
                     float *d_scores, int32_t topk, int32_t *d_top_idx, float *d_top_val, void *d_ws,
                     size_t ws_bytes, void *stream);
+
+/* PolarQuant encode of n vectors (rows of d_x, row stride x_stride elements,
+ * fp32 or bf16, 16-byte aligned) into records out_offset .. out_offset+n-1.
+ * d = 128 only. d_ws: tq_polar_quantize_ws_bytes() bytes (the rotated rows).
+ * Errors: TQ_ERR_ARG (NULL, strides, records out of range), TQ_ERR_UNSUPPORTED
+ * (d, bits), TQ_ERR_CAPACITY (workspace), TQ_ERR_HIP. */
+size_t tq_polar_quantize_ws_bytes(const tq_ctx *ctx, int64_t n);
+tq_status tq_polar_quantize(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int64_t n, int64_t x_stride,
+                            const tq_polar_packed *out, int64_t out_offset, void *d_ws, size_t ws_bytes,
+                            void *stream);
+
+/* PolarQuant scores: d_scores[q][i] = <Pi q, y_hat_i> = <q, x_hat_i> with y_hat_i
+ * rebuilt from record i's codes (top-down: ||x|| times the cos / sin of the
+ * ancestors' angle centroids, then the pair's own angle), fp32, [nq][keys->n].
+ * d_q: [nq][128] fp32 or bf16. d_ws: tq_polar_scores_ws_bytes() bytes (the
+ * rotated queries and the rebuilt rows, 512 bytes per key).
+ * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_HIP. */
+size_t tq_polar_scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n);
+tq_status tq_polar_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t nq, const tq_polar_packed *keys,
+                          float *d_scores, void *d_ws, size_t ws_bytes, void *stream);
 
 /* Kernel timing, a measurement aid. Arms the calling thread so that its next
  * tq_attention_decode, tq_attention_prefill or tq_decode_step records start_event on its stream

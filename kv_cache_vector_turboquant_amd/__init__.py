@@ -49,6 +49,15 @@ class CCodebook(ctypes.Structure):
                 ("boundary", ctypes.c_float * 15), ("walsh", ctypes.c_float * 8), ("distortion", ctypes.c_double)]
 
 
+class CAngleCodebook(ctypes.Structure):
+    _fields_ = [("level", _c_i32), ("bits", _c_i32), ("centroid", ctypes.c_double * 16),
+                ("boundary", ctypes.c_float * 15), ("cos_c", ctypes.c_float * 16), ("sin_c", ctypes.c_float * 16)]
+
+
+class CPolarPacked(ctypes.Structure):
+    _fields_ = [("bits", _c_vp), ("norms", _c_vp), ("n", _c_i64), ("b1", _c_i32), ("b2", _c_i32)]
+
+
 class CPacked(ctypes.Structure):
     _fields_ = [("bits", _c_vp), ("norms", _c_vp), ("n", _c_i64), ("mse_bits", _c_i32), ("is_key", _c_i32),
                 ("qjl", _c_i32), ("norm_f16", _c_i32)]
@@ -77,6 +86,13 @@ _sig("tq_ctx_codebook", _c_i32, [_c_vp, _c_i32, ctypes.POINTER(CCodebook)])
 _sig("tq_quantize_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64, _c_i32])
 _sig("tq_quantize_kv", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(CPacked),
                                 _c_i64, _c_i64, _c_vp, _c_sz, _c_vp])
+_sig("tq_angle_codebook_build", _c_i32, [_c_i32, _c_i32, ctypes.POINTER(CAngleCodebook)])
+_sig("tq_polar_quantize_ws_bytes", _c_sz, [_c_vp, _c_i64])
+_sig("tq_polar_quantize", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, ctypes.POINTER(CPolarPacked), _c_i64, _c_vp,
+                                   _c_sz, _c_vp])
+_sig("tq_polar_scores_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64])
+_sig("tq_polar_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPolarPacked), _c_vp, _c_vp, _c_sz,
+                                 _c_vp])
 _sig("tq_append_token", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_i32, _c_vp])
 _sig("tq_cache_write", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64,
                                 _c_vp, _c_sz, _c_vp])
@@ -96,11 +112,12 @@ _sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked)
                            _c_vp, _c_sz, _c_vp])
 
 EXPORTED_SYMBOLS = [
-    "tq_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
+    "tq_codebook_build", "tq_angle_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
     "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_cache_write", "tq_append_token", "tq_attention_decode_ws_bytes",
     "tq_attention_decode", "tq_attention_prefill_ws_bytes", "tq_attention_prefill", "tq_decode_step_ws_bytes",
     "tq_decode_step", "tq_time_next_decode", "tq_read_probe",
-    "tq_scores_ws_bytes", "tq_scores", "tq_last_error",
+    "tq_scores_ws_bytes", "tq_scores", "tq_polar_quantize_ws_bytes", "tq_polar_quantize", "tq_polar_scores_ws_bytes",
+    "tq_polar_scores", "tq_last_error",
 ]
 
 
@@ -169,6 +186,16 @@ def codebook_build(d: int, bits: int) -> Codebook:
     c = CCodebook()
     _check(_lib.tq_codebook_build(d, bits, ctypes.byref(c)))
     return _cb_from_c(c)
+
+
+def angle_codebook_build(level: int, bits: int) -> dict:
+    """PolarQuant angle codebook of one level (host only): fp64 centroids, fp32
+    boundaries, cos and sin of the centroids."""
+    c = CAngleCodebook()
+    _check(_lib.tq_angle_codebook_build(level, bits, ctypes.byref(c)))
+    L = 1 << bits
+    return {"centroids": np.array(c.centroid[:L]), "boundaries": np.array(c.boundary[:L - 1], dtype=np.float32),
+            "cos": np.array(c.cos_c[:L], dtype=np.float32), "sin": np.array(c.sin_c[:L], dtype=np.float32)}
 
 
 def rotation_build(g: np.ndarray) -> np.ndarray:
@@ -508,3 +535,48 @@ def scores(ctx: Context, q, keys: Packed, want_scores: bool = True, topk: int = 
                           ti.data_ptr() if ti is not None else None, tv.data_ptr() if tv is not None else None,
                           ws.data_ptr(), ws.numel(), _stream_ptr()))
     return sc, ti, tv
+
+
+class PolarPacked:
+    """Device arrays of PolarQuant key records (d = 128; format in include/tq.h)."""
+
+    def __init__(self, n: int, b1: int = 4, b2: int = 3, device="cuda"):
+        torch = _torch()
+        self.n, self.b1, self.b2 = n, b1, b2
+        self.w1, self.w2 = (b1 * 64 + 31) // 32, (b2 * 63 + 31) // 32
+        self.words = torch.zeros((n, self.w1 + self.w2), dtype=torch.int32, device=device)
+        self.norms = torch.zeros((n,), dtype=torch.float32, device=device)
+
+    def c(self) -> CPolarPacked:
+        return CPolarPacked(self.words.data_ptr(), self.norms.data_ptr(), self.n, self.b1, self.b2)
+
+    def host(self):
+        return self.words.cpu().numpy().view(np.uint32), self.norms.cpu().numpy()
+
+
+def polar_quantize(ctx: Context, x, out: PolarPacked, out_offset: int = 0, ws=None):
+    """x: [n, 128] (rows 16-byte aligned) -> records out_offset .. of `out`."""
+    torch = _torch()
+    n = x.shape[0]
+    need = int(_lib.tq_polar_quantize_ws_bytes(ctx.handle, n))
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    cp = out.c()
+    _check(_lib.tq_polar_quantize(ctx.handle, x.data_ptr(), _dtype_code(x), n, x.stride(0), ctypes.byref(cp),
+                                  out_offset, ws.data_ptr(), ws.numel(), _stream_ptr()))
+
+
+def polar_scores(ctx: Context, q, keys: PolarPacked, out=None, ws=None):
+    """q: [nq, 128] contiguous -> fp32 scores [nq, keys.n]."""
+    torch = _torch()
+    assert q.is_contiguous()
+    nq = q.shape[0]
+    if out is None:
+        out = torch.empty((nq, keys.n), dtype=torch.float32, device=q.device)
+    need = int(_lib.tq_polar_scores_ws_bytes(ctx.handle, nq, keys.n))
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    kp = keys.c()
+    _check(_lib.tq_polar_scores(ctx.handle, q.data_ptr(), _dtype_code(q), nq, ctypes.byref(kp), out.data_ptr(),
+                                ws.data_ptr(), ws.numel(), _stream_ptr()))
+    return out

@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq_host.cpp", "tq_kernels.hip"]
+SOURCES = ["tq_host.cpp", "tq_kernels.hip", "polar_kernels.hip"]
 
 # Packed FP32 VALU ops are disabled for device code; the host pass warns that
 # it does not know the feature, which is harmless. MFMA results go to ordinary
@@ -26,15 +26,18 @@ HIPCC_FLAGS = [
 
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    objs = []
-    for src in SOURCES:
+    objs, procs = [], []
+    for src in SOURCES:  # the sources compile concurrently
         obj = os.path.join(CSRC, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [hipcc, *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((subprocess.Popen(cmd), cmd))
         objs.append(obj)
+    failed = [cmd for p, cmd in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     tmp = LIB + ".tmp"
     cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp, "-lpthread"]
     subprocess.run(cmd, check=True)

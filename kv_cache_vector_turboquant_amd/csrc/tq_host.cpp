@@ -279,6 +279,102 @@ tq_status tq_codebook_build(int32_t d, int32_t bits, tq_codebook *out) {
   return TQ_OK;
 }
 
+// ---------------------------------------------------------------------------
+// PolarQuant angle codebooks. Angle of level l >= 2 of a random direction,
+// m = 2^(l-1): sin^2(psi) ~ Beta(m/2, m/2), density
+// 2^(2-m) sin^(m-1)(2 psi) / B(m/2, m/2) on [0, pi/2]; level 1 uniform on the
+// circle (cells from -pi). Lloyd-Max per level, symmetric about pi/4.
+// ---------------------------------------------------------------------------
+
+static double angle_pdf(int m, double psi) {
+  const double s = std::sin(2.0 * psi);
+  if (s <= 0.0) return m == 1 ? std::exp((2 - m) * std::log(2.0) - log_beta(0.5 * m, 0.5 * m)) : 0.0;
+  return std::exp((2 - m) * std::log(2.0) - log_beta(0.5 * m, 0.5 * m) + (m - 1) * std::log(s));
+}
+
+static double angle_cdf(int m, double psi) {
+  const double p = std::min(std::max(psi, 0.0), M_PI / 2);
+  const double u = std::sin(p);
+  return inc_beta(0.5 * m, 0.5 * m, u * u);
+}
+
+// int_a^b psi f(psi) dpsi: composite 16-point Gauss-Legendre on 32 panels
+static double angle_moment1(int m, double a, double b) {
+  static const double x[8] = {0.0950125098376374, 0.2816035507792589, 0.4580167776572274, 0.6178762444026438,
+                              0.7554044083550030, 0.8656312023878318, 0.9445750230732326, 0.9894009349916499};
+  static const double w[8] = {0.1894506104550685, 0.1826034150449236, 0.1691565193950025, 0.1495959888165767,
+                              0.1246289712555339, 0.0951585116824928, 0.0622535239386479, 0.0271524594117541};
+  const int P = 32;
+  const double h = (b - a) / P;
+  double acc = 0.0;
+  for (int k = 0; k < P; ++k) {
+    const double c = a + (k + 0.5) * h, r = 0.5 * h;
+    for (int i = 0; i < 8; ++i) {
+      const double t1 = c - r * x[i], t2 = c + r * x[i];
+      acc += w[i] * r * (t1 * angle_pdf(m, t1) + t2 * angle_pdf(m, t2));
+    }
+  }
+  return acc;
+}
+
+static std::vector<double> lloyd_max_angle(int level, int bits) {
+  const int L = 1 << bits;
+  std::vector<double> c(L);
+  if (level == 1) {
+    for (int i = 0; i < L; ++i) c[i] = -M_PI + (i + 0.5) * (2.0 * M_PI / L);
+    return c;
+  }
+  const int m = 1 << (level - 1);
+  std::vector<double> e(L + 1);
+  e[0] = 0.0;
+  e[L] = M_PI / 2;
+  for (int i = 1; i < L; ++i) {  // equal-mass start: bisection on the CDF
+    double lo = 0.0, hi = M_PI / 2;
+    for (int it = 0; it < 200; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      if (angle_cdf(m, mid) < double(i) / L) lo = mid; else hi = mid;
+    }
+    e[i] = 0.5 * (lo + hi);
+  }
+  auto centroids = [&]() {
+    for (int i = 0; i < L; ++i) c[i] = angle_moment1(m, e[i], e[i + 1]) / (angle_cdf(m, e[i + 1]) - angle_cdf(m, e[i]));
+  };
+  centroids();
+  for (int it = 0; it < 10000; ++it) {
+    for (int i = 1; i < L; ++i) e[i] = 0.5 * (c[i - 1] + c[i]);
+    std::vector<double> old = c;
+    centroids();
+    double delta = 0.0;
+    for (int i = 0; i < L; ++i) delta = std::max(delta, std::fabs(c[i] - old[i]));
+    if (delta < 1e-12) break;
+  }
+  std::vector<double> s(L);
+  for (int i = 0; i < L; ++i) s[i] = 0.5 * (c[i] + (M_PI / 2 - c[L - 1 - i]));
+  return s;
+}
+
+tq_status tq_angle_codebook_build(int32_t level, int32_t bits, tq_angle_codebook *out) {
+  if (!out) return fail(TQ_ERR_ARG, "tq_angle_codebook_build: out is NULL");
+  if (level < 1 || level > TQ_POLAR_MAX_LEVEL)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_angle_codebook_build: level must be in [1, 12]");
+  if (bits < 1 || bits > TQ_MAX_BITS) return fail(TQ_ERR_UNSUPPORTED, "tq_angle_codebook_build: bits must be in [1, 4]");
+  const int L = 1 << bits;
+  std::vector<double> c = lloyd_max_angle(level, bits);
+  tq_angle_codebook cb;
+  std::memset(&cb, 0, sizeof(cb));
+  cb.level = level;
+  cb.bits = bits;
+  for (int i = 0; i < L; ++i) {
+    cb.centroid[i] = c[i];
+    cb.cos_c[i] = (float)std::cos(c[i]);
+    cb.sin_c[i] = (float)std::sin(c[i]);
+  }
+  for (int i = 0; i + 1 < L; ++i)
+    cb.boundary[i] = (float)(level == 1 ? -M_PI + (i + 1) * (2.0 * M_PI / L) : 0.5 * (c[i] + c[i + 1]));
+  *out = cb;
+  return TQ_OK;
+}
+
 tq_status tq_rotation_build(int32_t d, const double *h_g, float *h_out) {
   if (!h_g || !h_out) return fail(TQ_ERR_ARG, "tq_rotation_build: NULL argument");
   if (d < 2 || d > TQ_MAX_DIM) return fail(TQ_ERR_UNSUPPORTED, "tq_rotation_build: d must be in [2, 4096]");
@@ -329,6 +425,24 @@ tq_status tq_ctx_create(int32_t d, const double *h_g_rot, const double *h_g_sket
     for (int i = L - 1; i < 16; ++i) ctx->h_tables.boundary[b][i] = INFINITY;
     for (int i = 0; i < (L >> 1); ++i) ctx->h_tables.walsh[b][i] = ctx->cb[b].walsh[i];
     ctx->h_tables.ctop[b] = ctx->cb[b].centroid[L - 1];
+  }
+  // PolarQuant angle tables (the GPU polar path supports d = 128: levels 1..7)
+  if (d == 128) {
+    for (int lv = 1; lv <= 7; ++lv)
+      for (int b = 1; b <= TQ_MAX_BITS; ++b) {
+        tq_angle_codebook acb;
+        tq_status s = tq_angle_codebook_build(lv, b, &acb);
+        if (s != TQ_OK) {
+          delete ctx;
+          return s;
+        }
+        const int L = 1 << b;
+        for (int i = 0; i < 16; ++i) ctx->h_tables.pbound[lv][b][i] = i + 1 < L ? acb.boundary[i] : INFINITY;
+        for (int i = 0; i < L; ++i) {
+          ctx->h_tables.pcos[lv][b][i] = acb.cos_c[i];
+          ctx->h_tables.psin[lv][b][i] = acb.sin_c[i];
+        }
+      }
   }
   const size_t mat = (size_t)d * d * sizeof(float);
   if ((e = hipMalloc(&ctx->d_rot, mat)) != hipSuccess || (e = hipMalloc(&ctx->d_sketch, mat)) != hipSuccess ||
@@ -680,6 +794,68 @@ tq_status tq_decode_step(const tq_ctx *ctx, tq_kv_cache *cache, const void *d_k,
   if (e != hipSuccess) return hip_fail(e, fn);
   cache->host_max_len += 1;
   return TQ_OK;
+}
+
+static tq_status check_polar(const tq_ctx *ctx, const tq_polar_packed *p, const char *fn) {
+  if (ctx->d != 128) return fail(TQ_ERR_UNSUPPORTED, std::string(fn) + ": the PolarQuant path needs d = 128");
+  if (!p || !p->bits || !p->norms) return fail(TQ_ERR_ARG, std::string(fn) + ": packed array or its pointers NULL");
+  if (p->b1 < 1 || p->b1 > TQ_MAX_BITS || p->b2 < 1 || p->b2 > TQ_MAX_BITS)
+    return fail(TQ_ERR_UNSUPPORTED, std::string(fn) + ": b1 and b2 must be in [1, 4]");
+  if (p->n < 0) return fail(TQ_ERR_ARG, std::string(fn) + ": negative record count");
+  return TQ_OK;
+}
+
+size_t tq_polar_quantize_ws_bytes(const tq_ctx *ctx, int64_t n) {
+  if (!ctx || n < 0) return 0;
+  return (size_t)n * ctx->d * sizeof(float) + 256;
+}
+
+tq_status tq_polar_quantize(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int64_t n, int64_t x_stride,
+                            const tq_polar_packed *out, int64_t out_offset, void *d_ws, size_t ws_bytes,
+                            void *stream) {
+  const char *fn = "tq_polar_quantize";
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_polar_quantize: NULL ctx");
+  tq_status s = check_polar(ctx, out, fn);
+  if (s != TQ_OK) return s;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_polar_quantize: dtype must be TQ_F32 or TQ_BF16");
+  if (n < 0 || out_offset < 0 || x_stride < 0) return fail(TQ_ERR_ARG, "tq_polar_quantize: negative size, stride or offset");
+  if (n == 0) return TQ_OK;
+  if (!d_x) return fail(TQ_ERR_ARG, "tq_polar_quantize: NULL input");
+  if (x_stride < ctx->d || (x_stride % 8) != 0 || ((uintptr_t)d_x % 16) != 0)
+    return fail(TQ_ERR_ARG, "tq_polar_quantize: input must be 16-byte aligned with a row stride >= d, a multiple of 8");
+  if (out_offset + n > out->n) return fail(TQ_ERR_ARG, "tq_polar_quantize: records past the end of the output array");
+  if ((n + 3) / 4 > INT32_MAX) return fail(TQ_ERR_UNSUPPORTED, "tq_polar_quantize: too many vectors for one launch");
+  if (!d_ws || ws_bytes < tq_polar_quantize_ws_bytes(ctx, n))
+    return fail(TQ_ERR_CAPACITY, "tq_polar_quantize: workspace smaller than tq_polar_quantize_ws_bytes()");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  hipError_t e = launch_polar_quantize(ctx, d_x, dtype == TQ_BF16, n, x_stride, out, out_offset, d_ws,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
+}
+
+size_t tq_polar_scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n) {
+  if (!ctx || nq < 0 || n < 0) return 0;
+  return (((size_t)nq * ctx->d * sizeof(float) + 255) & ~(size_t)255) + (size_t)n * ctx->d * sizeof(float) + 256;
+}
+
+tq_status tq_polar_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t nq, const tq_polar_packed *keys,
+                          float *d_scores, void *d_ws, size_t ws_bytes, void *stream) {
+  const char *fn = "tq_polar_scores";
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_polar_scores: NULL ctx");
+  tq_status s = check_polar(ctx, keys, fn);
+  if (s != TQ_OK) return s;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_polar_scores: dtype must be TQ_F32 or TQ_BF16");
+  if (nq < 0) return fail(TQ_ERR_ARG, "tq_polar_scores: negative query count");
+  if (nq == 0 || keys->n == 0) return TQ_OK;
+  if (!d_q || !d_scores) return fail(TQ_ERR_ARG, "tq_polar_scores: NULL query or output");
+  if (((uintptr_t)d_q % 16) != 0) return fail(TQ_ERR_ARG, "tq_polar_scores: queries must be 16-byte aligned");
+  if ((keys->n + 3) / 4 > INT32_MAX || (keys->n + 127) / 128 > 65535 || (nq + 63) / 64 > INT32_MAX)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_polar_scores: too many keys for one launch (at most 8388480)");
+  if (!d_ws || ws_bytes < tq_polar_scores_ws_bytes(ctx, nq, keys->n))
+    return fail(TQ_ERR_CAPACITY, "tq_polar_scores: workspace smaller than tq_polar_scores_ws_bytes()");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  hipError_t e = launch_polar_scores(ctx, d_q, dtype == TQ_BF16, nq, keys, d_scores, d_ws, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 
 size_t tq_scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores) {

@@ -20,6 +20,11 @@ struct DeviceTables {
   float boundary[TQ_MAX_BITS + 1][16];
   float walsh[TQ_MAX_BITS + 1][8];
   float ctop[TQ_MAX_BITS + 1];
+  // PolarQuant angle tables, [level 1..7][bits 1..4]: boundaries (INFINITY past
+  // the last), cos and sin of the centroids
+  float pbound[8][TQ_MAX_BITS + 1][16];
+  float pcos[8][TQ_MAX_BITS + 1][16];
+  float psin[8][TQ_MAX_BITS + 1][16];
 };
 
 // Where the record of token t of stream s lands in a packed array: contiguous
@@ -91,6 +96,16 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
                          const void *v_new = nullptr, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
                          int n_q = 1, int causal = 0);
 hipError_t launch_read_probe(const void *src, size_t bytes, int grid, uint32_t *sink, hipStream_t st);
+// C[M][N] = A[M][K] B[N][K]^T on fp32 MFMA (A fp32 or bf16, B fp32; row strides in elements)
+hipError_t launch_gemm_store(const void *a, int a_bf16, int64_t lda, int64_t M, const float *b, int64_t ldb,
+                             int64_t N, int K, float *c, int64_t ldc, hipStream_t st);
+// PolarQuant keys (polar_kernels.hip), d = 128: y = Pi x of n vectors (rows of x,
+// stride xs) into records out_offset .. of `out`; ws: n * 128 floats.
+hipError_t launch_polar_quantize(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n, int64_t xs,
+                                 const tq_polar_packed *out, int64_t out_offset, void *ws, hipStream_t st);
+// scores [nq][keys->n] = <Pi q, y_hat>; ws: (nq + keys->n) * 128 floats (256-aligned parts)
+hipError_t launch_polar_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_polar_packed *keys,
+                               float *scores, void *ws, hipStream_t st);
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores);
 hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_packed *keys,
                          float *scores, int32_t topk, int32_t *top_idx, float *top_val, void *ws, hipStream_t st);

@@ -945,6 +945,22 @@ __global__ void __launch_bounds__(BS) topk_kernel(const float *scores, int64_t n
   }
 }
 
+hipError_t launch_gemm_store(const void *a, int a_bf16, int64_t lda, int64_t M, const float *b, int64_t ldb,
+                             int64_t N, int K, float *c, int64_t ldc, hipStream_t st) {
+  GemmArgs g = {};
+  g.a = {a, lda, M, a_bf16};
+  g.b = {b, ldb, N, 0};
+  g.K = K;
+  g.M = M;
+  g.N = N;
+  g.c = c;
+  g.ldc = ldc;
+  g.rows_on_x = 1;
+  dim3 grid((unsigned)((M + GBM - 1) / GBM), (unsigned)((N + GBN - 1) / GBN), 1);
+  hipLaunchKernelGGL(gemm_kernel<MODE_STORE>, grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores) {
   size_t b = (size_t)nq * 2 * ctx->d * sizeof(float);  // [q_rot | q_s]
   b = (b + 255) & ~(size_t)255;

@@ -129,3 +129,24 @@ def test_ctx_create_argument_errors():
     assert lib.tq_ctx_create(128, None, g.ctypes.data, ctypes.byref(h)) == tq.TQ_ERR_ARG
     assert lib.tq_ctx_create(100, g.ctypes.data, g.ctypes.data, ctypes.byref(h)) == tq.TQ_ERR_UNSUPPORTED
     assert lib.tq_ctx_create(128, g.ctypes.data, g.ctypes.data, None) == tq.TQ_ERR_ARG
+
+
+@pytest.mark.parametrize("level,bits", [(1, 4), (2, 1), (2, 3), (3, 3), (5, 2), (7, 3), (7, 4)])
+def test_angle_codebooks_equal_the_oracle(level, bits):
+    """The library's PolarQuant angle tables (its own Lloyd iteration, incomplete
+    beta and Gauss-Legendre quadrature) equal the oracle's (scipy) fp32 tables
+    bit for bit; the fp64 centroids agree to 1e-11."""
+    from oracle import polarquant as PQ
+    h = tq.angle_codebook_build(level, bits)
+    o = PQ.angle_codebook(level, bits)
+    assert np.max(np.abs(h["centroids"] - o.centroids64)) < 1e-11
+    assert np.array_equal(h["boundaries"], o.boundaries)
+    assert np.array_equal(h["cos"], o.cos) and np.array_equal(h["sin"], o.sin)
+
+
+def test_angle_codebook_arguments():
+    lib = tq.lib()
+    c = tq.CAngleCodebook()
+    assert lib.tq_angle_codebook_build(0, 3, ctypes.byref(c)) == tq.TQ_ERR_UNSUPPORTED
+    assert lib.tq_angle_codebook_build(2, 5, ctypes.byref(c)) == tq.TQ_ERR_UNSUPPORTED
+    assert lib.tq_angle_codebook_build(2, 3, None) == tq.TQ_ERR_ARG
