@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", choices=["serving", "gqa", "single", "search", "tiny", "prefill"],
+    ap.add_argument("--workload", choices=["serving", "gqa", "single", "search", "tiny", "prefill", "polar"],
                     default="serving")
     ap.add_argument("--data", choices=["outlier", "gaussian"], default="outlier")
     ap.add_argument("--kbits", type=int, default=3, help="MSE bits of the keys (b = kbits + 1)")
@@ -537,6 +537,108 @@ def run_prefill(args, torch, tq, synth):
     return res
 
 
+def run_polar(args, torch, tq, synth):
+    """Decode attention with PolarQuant keys (b1 = 4, b2 = 3) and 3-bit stage-1
+    values on the serving shape: prefill quantize of all K/V, then 32 decode
+    calls over the cache."""
+    B, H, Hq, L, NS, d = 64, 8, 32, 8192, 32, 128
+    ctx = tq.Context(d, 0)
+    K = kv_inputs(torch, synth, args, (B, H, L, d), (5, synth.TAG_KEYS), synth.TAG_SCALES_K)
+    V = kv_inputs(torch, synth, args, (B, H, L, d), (5, synth.TAG_VALUES), synth.TAG_SCALES_V)
+    QS = synth.torch_gaussian(0, (5, synth.TAG_QUERIES), (NS, B, Hq, d), torch.bfloat16, "cuda")
+    cache = tq.PolarKVCache(B, H, L)
+    cache.host_max_len = L
+    ws = torch.empty(cache.decode_ws_bytes(ctx, Hq), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    timer = Timer(torch)
+    kev, cev = [], []
+
+    def step(record):
+        cache.prefill(ctx, K, V)
+        for i in range(NS):
+            if record:
+                tq.time_next_decode(*kev[i])
+                cev.append(timer(lambda: cache.decode(ctx, QS[i], out=out, ws=ws)))
+            else:
+                cache.decode(ctx, QS[i], out=out, ws=ws)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    pre = timer(lambda: cache.prefill(ctx, K, V))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    whole = timer(lambda: [step(False) for _ in range(args.steps)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ms(whole) / args.steps
+    for _ in range(NS):
+        pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in pair:
+            e.record()
+        kev.append(pair)
+    torch.cuda.synchronize()
+    step(True)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([ms(k) for k in kev]))
+    call_ms = float(np.mean([ms(c) for c in cev]))
+    keys = B * H * L * NS
+    # the scoring kernel's arithmetic: per (token, query head) one multiply and one
+    # fma (3 flops) for each of the 127 tree nodes, and the radius scale
+    flops_per = 3 * 127 + 1
+    tflops = B * Hq * L * flops_per / (kern_ms / 1e3) / 1e12
+    rec = 60 + VAL_B3
+    res = {
+        "metric": METRIC, "value": keys / (ms_per_step / 1e3), "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 (PolarQuant tree evaluation) + i8 MFMA values",
+        "data": f"synthetic ({args.data}-channel bf16 K/V, Gaussian bf16 queries, seeded)",
+        "config": {"workload": (f"polar_decode: {B} seq x {L} ctx, {H} KV heads, {Hq} q heads, d={d}, PolarQuant "
+                                f"keys (4-bit level-1 and 3-bit higher angles, fp32 radius: 60 B), values 3-bit; "
+                                f"prefill quantize + {NS} decode calls"),
+                   "batch": B, "context": L, "decode_calls": NS, "kv_heads": H, "q_heads": Hq, "head_dim": d,
+                   "key_format": "polarquant(4,3)", "value_bits": 3, "parallelism": "none (1 GPU)"},
+        "quantize_vectors_per_s": 2 * B * H * L / (ms(pre) / 1e3), "prefill_ms": ms(pre),
+        "decode_call_ms": call_ms, "decode_keys_per_s": B * H * L / (call_ms / 1e3),
+        "decode_call_gbs": B * H * L * rec / (call_ms / 1e3) / 1e9, "bytes_per_kv_token": rec,
+        "wall_s_timed": wall,
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / FP32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "polar_logits_kernel (PolarQuant tree evaluation of every cached key for 4 heads)",
+                     "flops_per_token_head": flops_per, "avg_launch_ms": kern_ms,
+                     "timing": "HIP events on the launch stream around the scoring kernel of every decode call",
+                     "peak_note": "157.3 TFLOP/s counts packed fp32 FMA; this path issues unpacked fp32 ops (half that)"},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import polarquant as PQ
+        from oracle import turboquant as T
+        Pi = T.rotation_from_gaussian(synth.gaussian_matrix(0, synth.TAG_ROTATION, d, d))
+        pcb = PQ.polar_codebooks(d, 4, 3)
+        cbv = T.codebook(d, 3)
+        Ls = 4096
+        Kh = synth.outlier_kv(0, (5, 1), synth.TAG_SCALES_K, (Ls, d))
+        Vh = synth.outlier_kv(0, (5, 2), synth.TAG_SCALES_V, (Ls, d))
+        t0c = time.perf_counter()
+        kr = PQ.pack_polar(PQ.polar_encode(Kh, Pi, pcb), pcb)
+        vr = T.pack_values(T.encode(Vh, Pi, cbv), 3)
+        t_enc = time.perf_counter() - t0c
+        n_dec, t_dec = 0, 0.0
+        while t_dec < args.cpu_seconds / 2 or n_dec == 0:
+            q = synth.gaussian(0, (5, 3, n_dec), (Hq // H, d), "bf16")
+            t1 = time.perf_counter()
+            PQ.polar_attention_decode(q, Pi, pcb, cbv, kr, vr, Ls, 1 / math.sqrt(d), T.unpack_values)
+            t_dec += time.perf_counter() - t1
+            n_dec += 1
+        enc_rate, dec_rate = 2 * Ls / t_enc, Ls * n_dec / t_dec
+        step_s = 2 * B * H * L / enc_rate + keys / dec_rate
+        res["cpu_baseline"] = {
+            "value": keys / step_s, "unit": "keys/s", "cores": threads_used(), "kind": "oracle",
+            "sample": f"one stream of {Ls} tokens: oracle encode of its K and V, then {n_dec} decodes for "
+                      f"{Hq // H} query heads ({t_enc + t_dec:.1f} s of CPU work), extrapolated to the step",
+            "quantize_vectors_per_s": enc_rate, "decode_keys_per_s": dec_rate}
+    return res
+
+
 def run_search(args, torch, tq, synth):
     """Vector search: 1e6 unit-norm Gaussian vectors at d=1536 quantized at b=4,
     1000 queries scored against all of them, top-10 each."""
@@ -665,6 +767,8 @@ def main():
         res = run_search(args, torch, tq, synth)
     elif args.workload == "prefill":
         res = run_prefill(args, torch, tq, synth)
+    elif args.workload == "polar":
+        res = run_polar(args, torch, tq, synth)
     else:
         res = run_tiny(args, torch, tq, synth)
     print(json.dumps(res), flush=True)

@@ -308,15 +308,31 @@ tq_status tq_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t 
                     float *d_scores, int32_t topk, int32_t *d_top_idx, float *d_top_val, void *d_ws,
                     size_t ws_bytes, void *stream);
 
-/* PolarQuant encode of n vectors (rows of d_x, row stride x_stride elements,
- * fp32 or bf16, 16-byte aligned) into records out_offset .. out_offset+n-1.
- * d = 128 only. d_ws: tq_polar_quantize_ws_bytes() bytes (the rotated rows).
- * Errors: TQ_ERR_ARG (NULL, strides, records out of range), TQ_ERR_UNSUPPORTED
- * (d, bits), TQ_ERR_CAPACITY (workspace), TQ_ERR_HIP. */
+/* PolarQuant encode of n_streams x n_tokens vectors: vector (s, t) is row
+ * s*n_tokens + t of d_x (row stride x_stride elements, fp32 or bf16, 16-byte
+ * aligned) and goes to record s*out_stream_stride + out_offset + t. d = 128
+ * only. d_ws: tq_polar_quantize_ws_bytes(ctx, n_streams * n_tokens) bytes (the
+ * rotated rows).
+ * Errors: TQ_ERR_ARG (NULL, strides, overlapping or out-of-range records),
+ * TQ_ERR_UNSUPPORTED (d, bits), TQ_ERR_CAPACITY (workspace), TQ_ERR_HIP. */
 size_t tq_polar_quantize_ws_bytes(const tq_ctx *ctx, int64_t n);
-tq_status tq_polar_quantize(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int64_t n, int64_t x_stride,
-                            const tq_polar_packed *out, int64_t out_offset, void *d_ws, size_t ws_bytes,
-                            void *stream);
+tq_status tq_polar_quantize(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int64_t n_streams, int64_t n_tokens,
+                            int64_t x_stride, const tq_polar_packed *out, int64_t out_stream_stride,
+                            int64_t out_offset, void *d_ws, size_t ws_bytes, void *stream);
+
+/* Decode attention with PolarQuant keys: for every sequence b and query head h,
+ * out[b][h] = sum_t p_t v_hat_t, p = softmax(scale * s_t) over t < d_seq_len[b],
+ * s_t = <q, x_hat_t> from record (b*kv_heads + h/group)*values->capacity + t of
+ * `keys` ([gemilab] Attention機構; the scores of tq_polar_scores), v_hat from
+ * `values`' stage-1 value records (contiguous layout, fp32 norms; its key
+ * array is not read). d_q: [batch][q_heads][128]; d_out fp32 likewise.
+ * d_ws: tq_polar_attention_decode_ws_bytes() bytes.
+ * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d, group > 16, paged or compact
+ * values), TQ_ERR_CAPACITY (workspace), TQ_ERR_HIP. */
+size_t tq_polar_attention_decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *values, int32_t q_heads);
+tq_status tq_polar_attention_decode(const tq_ctx *ctx, const tq_polar_packed *keys, const tq_kv_cache *values,
+                                    const void *d_q, tq_dtype dtype, int32_t q_heads, float scale, float *d_out,
+                                    void *d_ws, size_t ws_bytes, void *stream);
 
 /* PolarQuant scores: d_scores[q][i] = <Pi q, y_hat_i> = <q, x_hat_i> with y_hat_i
  * rebuilt from record i's codes (top-down: ||x|| times the cos / sin of the
@@ -335,7 +351,8 @@ tq_status tq_polar_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, in
  * call then disarms the thread. The events are hipEvent_t handles created
  * and owned by the caller (with timing enabled, for hipEventElapsedTime).
  * Both NULL disarms. A call that fails before its launches leaves the thread
- * disarmed.
+ * disarmed. tq_polar_attention_decode takes the events too and records them
+ * around its scoring kernel (the PolarQuant tree evaluation).
  * Errors: TQ_ERR_ARG (exactly one of the two is NULL). */
 tq_status tq_time_next_decode(void *start_event, void *stop_event);
 

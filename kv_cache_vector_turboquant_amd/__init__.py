@@ -88,8 +88,11 @@ _sig("tq_quantize_kv", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c
                                 _c_i64, _c_i64, _c_vp, _c_sz, _c_vp])
 _sig("tq_angle_codebook_build", _c_i32, [_c_i32, _c_i32, ctypes.POINTER(CAngleCodebook)])
 _sig("tq_polar_quantize_ws_bytes", _c_sz, [_c_vp, _c_i64])
-_sig("tq_polar_quantize", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, ctypes.POINTER(CPolarPacked), _c_i64, _c_vp,
-                                   _c_sz, _c_vp])
+_sig("tq_polar_quantize", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, ctypes.POINTER(CPolarPacked), _c_i64,
+                                   _c_i64, _c_vp, _c_sz, _c_vp])
+_sig("tq_polar_attention_decode_ws_bytes", _c_sz, [_c_vp, ctypes.POINTER(CCache), _c_i32])
+_sig("tq_polar_attention_decode", _c_i32, [_c_vp, ctypes.POINTER(CPolarPacked), ctypes.POINTER(CCache), _c_vp, _c_i32,
+                                           _c_i32, _c_f32, _c_vp, _c_vp, _c_sz, _c_vp])
 _sig("tq_polar_scores_ws_bytes", _c_sz, [_c_vp, _c_i64, _c_i64])
 _sig("tq_polar_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPolarPacked), _c_vp, _c_vp, _c_sz,
                                  _c_vp])
@@ -117,7 +120,7 @@ EXPORTED_SYMBOLS = [
     "tq_attention_decode", "tq_attention_prefill_ws_bytes", "tq_attention_prefill", "tq_decode_step_ws_bytes",
     "tq_decode_step", "tq_time_next_decode", "tq_read_probe",
     "tq_scores_ws_bytes", "tq_scores", "tq_polar_quantize_ws_bytes", "tq_polar_quantize", "tq_polar_scores_ws_bytes",
-    "tq_polar_scores", "tq_last_error",
+    "tq_polar_scores", "tq_polar_attention_decode_ws_bytes", "tq_polar_attention_decode", "tq_last_error",
 ]
 
 
@@ -554,16 +557,22 @@ class PolarPacked:
         return self.words.cpu().numpy().view(np.uint32), self.norms.cpu().numpy()
 
 
-def polar_quantize(ctx: Context, x, out: PolarPacked, out_offset: int = 0, ws=None):
-    """x: [n, 128] (rows 16-byte aligned) -> records out_offset .. of `out`."""
+def polar_quantize(ctx: Context, x, out: PolarPacked, out_offset: int = 0, n_streams: int = 1,
+                   out_stream_stride: int = 0, ws=None):
+    """x: [rows, 128] (row stride a multiple of 8, 16-byte aligned), rows =
+    n_streams x tokens stream-major -> record s * out_stream_stride +
+    out_offset + t of `out`."""
     torch = _torch()
-    n = x.shape[0]
-    need = int(_lib.tq_polar_quantize_ws_bytes(ctx.handle, n))
+    rows = x.shape[0]
+    assert rows % n_streams == 0
+    T = rows // n_streams
+    need = int(_lib.tq_polar_quantize_ws_bytes(ctx.handle, rows))
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
     cp = out.c()
-    _check(_lib.tq_polar_quantize(ctx.handle, x.data_ptr(), _dtype_code(x), n, x.stride(0), ctypes.byref(cp),
-                                  out_offset, ws.data_ptr(), ws.numel(), _stream_ptr()))
+    _check(_lib.tq_polar_quantize(ctx.handle, x.data_ptr(), _dtype_code(x), n_streams, T, x.stride(0),
+                                  ctypes.byref(cp), out_stream_stride, out_offset, ws.data_ptr(), ws.numel(),
+                                  _stream_ptr()))
 
 
 def polar_scores(ctx: Context, q, keys: PolarPacked, out=None, ws=None):
@@ -580,3 +589,58 @@ def polar_scores(ctx: Context, q, keys: PolarPacked, out=None, ws=None):
     _check(_lib.tq_polar_scores(ctx.handle, q.data_ptr(), _dtype_code(q), nq, ctypes.byref(kp), out.data_ptr(),
                                 ws.data_ptr(), ws.numel(), _stream_ptr()))
     return out
+
+
+class PolarKVCache:
+    """PolarQuant keys with stage-1 values: key records of stream (b, h) at
+    (b*kv_heads + h)*capacity + t in a PolarPacked array, values in the
+    TurboQuant value format (the `values` cache's key array is unused)."""
+
+    def __init__(self, batch: int, kv_heads: int, capacity: int, value_bits: int = 3, b1: int = 4, b2: int = 3,
+                 device="cuda"):
+        self.keys = PolarPacked(batch * kv_heads * capacity, b1, b2, device)
+        self.values = KVCache(batch, kv_heads, capacity, 128, 1, value_bits, device)
+        self.values.k = Packed(32, 128, 1, True, device)  # placeholder: the polar keys live in self.keys
+        self.batch, self.kv_heads, self.capacity = batch, kv_heads, capacity
+        self.seq_len = self.values.seq_len
+
+    @property
+    def host_max_len(self):
+        return self.values.host_max_len
+
+    @host_max_len.setter
+    def host_max_len(self, v):
+        self.values.host_max_len = v
+
+    def prefill(self, ctx: Context, k, v):
+        """k, v: [batch, kv_heads, tokens, 128] contiguous."""
+        B, H, T, d = k.shape
+        assert k.is_contiguous() and (B, H) == (self.batch, self.kv_heads) and T <= self.capacity
+        polar_quantize(ctx, k.reshape(B * H * T, d), self.keys, 0, B * H, self.capacity)
+        quantize_kv(ctx, v.reshape(B * H, T, d), self.values.v, n_streams=B * H, n_tokens=T,
+                    out_stream_stride=self.capacity, out_offset=0)
+        self.seq_len.fill_(T)
+        self.values.host_max_len = T
+
+    def decode_ws_bytes(self, ctx: Context, q_heads: int) -> int:
+        cc = self.values.c()
+        return int(_lib.tq_polar_attention_decode_ws_bytes(ctx.handle, ctypes.byref(cc), q_heads))
+
+    def decode(self, ctx: Context, q, scale: float | None = None, out=None, ws=None):
+        """q: [batch, q_heads, 128] contiguous -> fp32 [batch, q_heads, 128]."""
+        torch = _torch()
+        assert q.is_contiguous()
+        B, Hq, d = q.shape
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        cc = self.values.c()
+        need = self.decode_ws_bytes(ctx, Hq)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+        kp = self.keys.c()
+        _check(_lib.tq_polar_attention_decode(ctx.handle, ctypes.byref(kp), ctypes.byref(cc), q.data_ptr(),
+                                              _dtype_code(q), Hq, float(scale), out.data_ptr(), ws.data_ptr(),
+                                              ws.numel(), _stream_ptr()))
+        return out

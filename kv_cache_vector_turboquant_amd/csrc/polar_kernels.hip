@@ -14,10 +14,11 @@
 // words; the radius ||x|| as fp32 in a separate array.
 //
 //  polar_encode_kernel   one wave per vector: lane l owns coordinate pair l;
-//                        level l >= 2 combines the radii of lanes l and
-//                        l + 2^(l-2) (a shuffle), so the owner lanes of level l
-//                        are the multiples of 2^(l-1). Codes go to LDS, then
-//                        one lane per record word assembles the bit streams.
+//                        the radii of level l >= 2 combine lanes l and
+//                        l + 2^(l-2) (a shuffle; owners are the multiples of
+//                        2^(l-1)), then the 63 higher angles are taken one per
+//                        lane. Codes go to LDS, then one lane per record word
+//                        assembles the bit streams.
 //  polar_rebuild_kernel  one wave per record: lane l multiplies the radius by
 //                        the cos or sin of its six ancestors' angles, top-down,
 //                        then splits the result by its pair's angle: y_hat rows
@@ -36,7 +37,9 @@ struct PolarArgs {
   float *yh;            // rebuild: [n][PD]
   uint32_t *bits;       // records [rec][w1 + w2]
   float *norms;         // [rec]
-  int64_t n, rec0;
+  int64_t n, rec0;      // vectors; rebuild: first record
+  int64_t n_tokens, os; // encode: vector v = (stream v / n_tokens, token v % n_tokens) -> record
+                        // stream * os + rec0 + token
   int b1, b2, w1, w2;
   const DeviceTables *tables;
 };
@@ -71,28 +74,42 @@ __global__ void __launch_bounds__(256) polar_encode_kernel(PolarArgs a) {
   float r = 0.f;
   if (live) {
     const float2 p = reinterpret_cast<const float2 *>(a.y + v * PD)[lane];
-    r = sqrtf(fmaf(p.x, p.x, p.y * p.y));
     codes[w][lane] = (uint8_t)angle_code(atan2f(p.y, p.x), a.tables->pbound[1][a.b1]);
+    // radii of every level first (a shuffle and a hypot per level): rl[k] is the
+    // radius of the level-(k+1) node this lane owns (owners: multiples of 2^k)
+    float rl[PL];
+    rl[0] = sqrtf(fmaf(p.x, p.x, p.y * p.y));
 #pragma unroll
-    for (int lv = 2; lv <= PL; ++lv) {
-      const int step = 1 << (lv - 2);
-      const float rr = __shfl_down(r, step);  // the right child's radius
-      const float psi = atan2f(rr, r);
-      const float rn = sqrtf(fmaf(r, r, rr * rr));
-      if ((lane & (2 * step - 1)) == 0)
-        codes[w][64 + level_offset(lv) + (lane >> (lv - 1))] = (uint8_t)angle_code(psi, a.tables->pbound[lv][a.b2]);
-      r = rn;  // an owner carries its node's radius to the next level
+    for (int k = 1; k < PL; ++k) {
+      const float rr = __shfl_down(rl[k - 1], 1 << (k - 1));  // the right child's radius
+      rl[k] = sqrtf(fmaf(rl[k - 1], rl[k - 1], rr * rr));
     }
+    r = rl[PL - 1];  // lane 0: the root, ||y|| = ||x||
+    // then the 63 higher angles at once, one per lane: lane j < 63 takes code j of
+    // the higher stream, node i of level lv, whose children are the level-(lv-1)
+    // nodes 2i and 2i + 1, owned by lanes 2i * 2^(lv-2) and (2i + 1) * 2^(lv-2)
+    const int j = lane;
+    const int lv = j < 32 ? 2 : j < 48 ? 3 : j < 56 ? 4 : j < 60 ? 5 : j < 62 ? 6 : 7;
+    const int i = j - level_offset(lv), sh = lv - 2;
+    float left = 0.f, right = 0.f;
+#pragma unroll
+    for (int k = 0; k < PL - 1; ++k) {  // child level k + 1 = lv - 1: the shuffle source is per lane
+      const float l_ = __shfl(rl[k], (2 * i) << k), r_ = __shfl(rl[k], (2 * i + 1) << k);
+      left = k == sh ? l_ : left;
+      right = k == sh ? r_ : right;
+    }
+    if (j < 63) codes[w][64 + j] = (uint8_t)angle_code(atan2f(right, left), a.tables->pbound[lv][a.b2]);
   }
   __syncthreads();
   if (live) {
     const int W = a.w1 + a.w2;
+    const int64_t st = v / a.n_tokens, rec = st * a.os + a.rec0 + (v - st * a.n_tokens);
     if (lane < W) {
       const uint32_t word = lane < a.w1 ? assemble_word(codes[w], 64, a.b1, lane)
                                         : assemble_word(codes[w] + 64, 63, a.b2, lane - a.w1);
-      a.bits[(a.rec0 + v) * W + lane] = word;
+      a.bits[rec * W + lane] = word;
     }
-    if (lane == 0) a.norms[a.rec0 + v] = r;  // lane 0 owns the root: ||y|| = ||x||
+    if (lane == 0) a.norms[rec] = r;  // lane 0 owns the root: ||y|| = ||x||
   }
 }
 
@@ -138,8 +155,10 @@ static PolarArgs polar_args(const tq_ctx *ctx, const tq_polar_packed *p) {
   return a;
 }
 
-hipError_t launch_polar_quantize(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n, int64_t xs,
-                                 const tq_polar_packed *out, int64_t out_offset, void *ws, hipStream_t st) {
+hipError_t launch_polar_quantize(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams, int64_t n_tokens,
+                                 int64_t xs, const tq_polar_packed *out, int64_t out_stream_stride, int64_t out_offset,
+                                 void *ws, hipStream_t st) {
+  const int64_t n = n_streams * n_tokens;
   float *y = (float *)ws;
   // preconditioning: y = Pi x on the fp32 MFMA GEMM
   hipError_t e = launch_gemm_store(x, is_bf16, xs, n, ctx->d_rot, PD, PD, PD, y, PD, st);
@@ -148,6 +167,8 @@ hipError_t launch_polar_quantize(const tq_ctx *ctx, const void *x, int is_bf16, 
   a.y = y;
   a.n = n;
   a.rec0 = out_offset;
+  a.n_tokens = n_tokens;
+  a.os = out_stream_stride;
   hipLaunchKernelGGL(polar_encode_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -165,6 +186,174 @@ hipError_t launch_polar_scores(const tq_ctx *ctx, const void *q, int is_bf16, in
   hipLaunchKernelGGL(polar_rebuild_kernel, dim3((unsigned)((keys->n + 3) / 4)), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return launch_gemm_store(qr, 0, PD, nq, yh, PD, keys->n, PD, scores, keys->n, st);  // <q_rot, y_hat>
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention with PolarQuant keys. polar_logits_kernel scores every
+// cached token against the 4 query heads of a (KV stream, head group): one
+// thread per token evaluates <q, y_hat> on the transform's tree without
+// rebuilding y_hat: a leaf (coordinate pair) gives q[2i] cos + q[2i+1] sin of
+// its angle, a node combines its children as cos * left + sin * right, and the
+// root is scaled by ||x||, evaluated per level-4 subtree (see the kernel). The
+// logits (log2 units) feed
+// decode_kernel's softmax and stage-1 value sums (EXT variant).
+// ---------------------------------------------------------------------------
+
+struct PolarLogitArgs {
+  const uint32_t *bits;
+  const float *norms;
+  int b1, b2, w1, w2;
+  const float *qrot;        // [batch * q_heads][PD]
+  const int32_t *seq_len;
+  float *out;               // [stream * hgroups + hg][4][stride]
+  int64_t stride;
+  int kv_heads, capacity, q_heads, group, hgroups;
+  float scale_log2;
+  const DeviceTables *tables;
+};
+
+// what the tree evaluation reads: the 4 heads' rotated query per coordinate,
+// the (cos, sin) tables per level and this thread's record (all in LDS)
+struct PolarTree {
+  const float4 *q;
+  const float2 (*tab)[16];
+  const uint32_t *rec;
+  int b1, b2, hi0;  // hi0: first bit of the higher-level stream
+  __device__ __forceinline__ uint32_t code(int pos, int nb) const {
+    const int j = pos >> 5, sh = pos & 31;
+    uint32_t v = rec[j] >> sh;
+    if (sh + nb > 32) v |= rec[j + 1] << (32 - sh);
+    return v & ((1u << nb) - 1u);
+  }
+};
+
+__device__ __forceinline__ float4 fma4(float a, const float4 &x, float b, const float4 &y) {
+  return make_float4(fmaf(a, x.x, b * y.x), fmaf(a, x.y, b * y.y), fmaf(a, x.z, b * y.z), fmaf(a, x.w, b * y.w));
+}
+
+__global__ void __launch_bounds__(256) polar_logits_kernel(PolarLogitArgs a) {
+  __shared__ float4 qs[PD];             // coordinate -> the 4 heads
+  __shared__ float2 tab[PL + 1][16];    // (cos, sin) of each level's centroids
+  __shared__ uint32_t rw[256][17];      // each thread's record
+  const int tid = threadIdx.x;
+  const int sg = blockIdx.y, hg = sg % a.hgroups, stream = sg / a.hgroups;
+  const int b = stream / a.kv_heads, kvh = stream - b * a.kv_heads;
+  const int nh = min(4, a.group - hg * 4);
+  for (int e = tid; e < 4 * PD; e += 256) {
+    const int h = e >> 7, j = e & (PD - 1);
+    reinterpret_cast<float *>(qs)[j * 4 + h] =
+        h < nh ? a.qrot[((int64_t)b * a.q_heads + kvh * a.group + hg * 4 + h) * PD + j] : 0.f;
+  }
+  if (tid < (PL + 1) * 16) {
+    const int lv = tid >> 4, i = tid & 15;
+    const int bb = lv == 1 ? a.b1 : a.b2;
+    tab[lv][i] = lv >= 1 ? make_float2(a.tables->pcos[lv][bb][i], a.tables->psin[lv][bb][i]) : make_float2(0.f, 0.f);
+  }
+  const int len = a.seq_len[b];
+  const int t = blockIdx.x * 256 + tid;
+  const bool live = t < len;
+  const int W = a.w1 + a.w2;
+  if (live) {
+    const uint32_t *src = a.bits + ((int64_t)stream * a.capacity + t) * W;
+    for (int k = 0; k < W; ++k) rw[tid][k] = src[k];
+  }
+  __syncthreads();
+  if (!live) return;  // past the barrier
+  PolarTree tr;
+  tr.q = qs;
+  tr.tab = tab;
+  tr.rec = rw[tid];
+  tr.b1 = a.b1;
+  tr.b2 = a.b2;
+  tr.hi0 = a.w1 * 32;
+  // <q, u_hat> for the 4 heads. The tree's dot product is linear in each
+  // subtree: <q, u_hat> = sum over the 8 level-4 nodes of (the cos / sin
+  // product along its 3 ancestors) x (its subtree's value). A subtree's value:
+  // a leaf (coordinate pair) gives cos * q[2i] + sin * q[2i+1] of its angle, a
+  // node cos * left + sin * right of its own angle.
+  auto leaf = [&](int l) {
+    const float2 cs = tr.tab[1][tr.code(l * tr.b1, tr.b1)];
+    return fma4(cs.x, tr.q[2 * l], cs.y, tr.q[2 * l + 1]);
+  };
+  auto node = [&](int lv, int i, const float4 &L, const float4 &R) {
+    const float2 cs = tr.tab[lv][tr.code(tr.hi0 + (64 - (128 >> (lv - 1)) + i) * tr.b2, tr.b2)];
+    return fma4(cs.x, L, cs.y, R);
+  };
+  float4 T = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int n4 = 0; n4 < 8; ++n4) {
+    float P = 1.f;
+#pragma unroll
+    for (int lv = 5; lv <= PL; ++lv) {
+      const float2 cs = tr.tab[lv][tr.code(tr.hi0 + (64 - (128 >> (lv - 1)) + (n4 >> (lv - 4))) * tr.b2, tr.b2)];
+      P *= ((n4 >> (lv - 5)) & 1) ? cs.y : cs.x;
+    }
+    const int l0 = 8 * n4;
+    const float4 a2 = node(2, 4 * n4, leaf(l0), leaf(l0 + 1));
+    const float4 b2 = node(2, 4 * n4 + 1, leaf(l0 + 2), leaf(l0 + 3));
+    const float4 a3 = node(3, 2 * n4, a2, b2);
+    const float4 c2 = node(2, 4 * n4 + 2, leaf(l0 + 4), leaf(l0 + 5));
+    const float4 d2 = node(2, 4 * n4 + 3, leaf(l0 + 6), leaf(l0 + 7));
+    const float4 b3 = node(3, 2 * n4 + 1, c2, d2);
+    const float4 t4 = node(4, n4, a3, b3);
+    T = fma4(1.f, T, P, t4);
+  }
+  // s = ||x|| <q, u_hat>, in log2 units of the softmax
+  const float R = a.norms[(int64_t)stream * a.capacity + t] * a.scale_log2;
+  float *o = a.out + (int64_t)sg * 4 * a.stride + t;
+  const float v[4] = {T.x, T.y, T.z, T.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    if (h < nh) o[(int64_t)h * a.stride] = R * v[h];
+}
+
+size_t polar_attention_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *values, int32_t q_heads) {
+  const int group = q_heads / values->kv_heads, hgroups = (group + 3) / 4;
+  const int maxlen = values->host_max_len > 0 ? values->host_max_len : values->capacity;
+  size_t b = decode_ws_bytes(ctx, values, q_heads, nullptr, nullptr, 1);
+  b = (b + 255) & ~(size_t)255;
+  b += (size_t)values->batch * q_heads * PD * sizeof(float);  // rotated queries
+  b = (b + 255) & ~(size_t)255;
+  b += (size_t)values->batch * values->kv_heads * hgroups * 4 * maxlen * sizeof(float);  // logits
+  return b;
+}
+
+hipError_t launch_polar_attention(const tq_ctx *ctx, const tq_polar_packed *keys, const tq_kv_cache *values,
+                                  const void *q, int is_bf16, int32_t q_heads, float scale, float *out, void *ws,
+                                  hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const int group = q_heads / values->kv_heads, hgroups = (group + 3) / 4;
+  const int maxlen = values->host_max_len > 0 ? values->host_max_len : values->capacity;
+  char *p = (char *)ws + ((decode_ws_bytes(ctx, values, q_heads, nullptr, nullptr, 1) + 255) & ~(size_t)255);
+  float *qrot = (float *)p;
+  p += ((size_t)values->batch * q_heads * PD * sizeof(float) + 255) & ~(size_t)255;
+  float *lg = (float *)p;
+  const int64_t nqr = (int64_t)values->batch * q_heads;
+  hipError_t e = launch_gemm_store(q, is_bf16, PD, nqr, ctx->d_rot, PD, PD, PD, qrot, PD, st);  // Pi q
+  if (e != hipSuccess) return e;
+  PolarLogitArgs a = {};
+  a.bits = keys->bits;
+  a.norms = keys->norms;
+  a.b1 = keys->b1;
+  a.b2 = keys->b2;
+  a.w1 = (keys->b1 * (PD / 2) + 31) / 32;
+  a.w2 = (keys->b2 * (PD / 2 - 1) + 31) / 32;
+  a.qrot = qrot;
+  a.seq_len = values->d_seq_len;
+  a.out = lg;
+  a.stride = maxlen;
+  a.kv_heads = values->kv_heads;
+  a.capacity = values->capacity;
+  a.q_heads = q_heads;
+  a.group = group;
+  a.hgroups = hgroups;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tables = ctx->d_tables;
+  const dim3 grid((unsigned)((maxlen + 255) / 256), (unsigned)(values->batch * values->kv_heads * hgroups));
+  if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;  // timing: the scoring kernel
+  hipLaunchKernelGGL(polar_logits_kernel, grid, dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
+  return launch_decode(ctx, values, nullptr, 0, q_heads, scale, out, ws, st, nullptr, nullptr, nullptr, nullptr, 1, 0,
+                       lg, maxlen);
 }
 
 }  // namespace tq

@@ -810,26 +810,75 @@ size_t tq_polar_quantize_ws_bytes(const tq_ctx *ctx, int64_t n) {
   return (size_t)n * ctx->d * sizeof(float) + 256;
 }
 
-tq_status tq_polar_quantize(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int64_t n, int64_t x_stride,
-                            const tq_polar_packed *out, int64_t out_offset, void *d_ws, size_t ws_bytes,
-                            void *stream) {
+tq_status tq_polar_quantize(const tq_ctx *ctx, const void *d_x, tq_dtype dtype, int64_t n_streams, int64_t n_tokens,
+                            int64_t x_stride, const tq_polar_packed *out, int64_t out_stream_stride,
+                            int64_t out_offset, void *d_ws, size_t ws_bytes, void *stream) {
   const char *fn = "tq_polar_quantize";
   if (!ctx) return fail(TQ_ERR_ARG, "tq_polar_quantize: NULL ctx");
   tq_status s = check_polar(ctx, out, fn);
   if (s != TQ_OK) return s;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_polar_quantize: dtype must be TQ_F32 or TQ_BF16");
-  if (n < 0 || out_offset < 0 || x_stride < 0) return fail(TQ_ERR_ARG, "tq_polar_quantize: negative size, stride or offset");
-  if (n == 0) return TQ_OK;
+  if (n_streams < 0 || n_tokens < 0 || out_offset < 0 || x_stride < 0 || out_stream_stride < 0)
+    return fail(TQ_ERR_ARG, "tq_polar_quantize: negative size, stride or offset");
+  if (n_streams == 0 || n_tokens == 0) return TQ_OK;
   if (!d_x) return fail(TQ_ERR_ARG, "tq_polar_quantize: NULL input");
   if (x_stride < ctx->d || (x_stride % 8) != 0 || ((uintptr_t)d_x % 16) != 0)
     return fail(TQ_ERR_ARG, "tq_polar_quantize: input must be 16-byte aligned with a row stride >= d, a multiple of 8");
-  if (out_offset + n > out->n) return fail(TQ_ERR_ARG, "tq_polar_quantize: records past the end of the output array");
-  if ((n + 3) / 4 > INT32_MAX) return fail(TQ_ERR_UNSUPPORTED, "tq_polar_quantize: too many vectors for one launch");
+  if (n_streams > 1 && out_stream_stride < out_offset + n_tokens)
+    return fail(TQ_ERR_ARG, "tq_polar_quantize: output streams overlap (out_stream_stride < out_offset + n_tokens)");
+  if ((n_streams - 1) * out_stream_stride + out_offset + n_tokens > out->n)
+    return fail(TQ_ERR_ARG, "tq_polar_quantize: records past the end of the output array");
+  const int64_t n = n_streams * n_tokens;
+  if ((n + 3) / 4 > INT32_MAX || (n + 63) / 64 > INT32_MAX)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_polar_quantize: too many vectors for one launch");
   if (!d_ws || ws_bytes < tq_polar_quantize_ws_bytes(ctx, n))
     return fail(TQ_ERR_CAPACITY, "tq_polar_quantize: workspace smaller than tq_polar_quantize_ws_bytes()");
   if ((s = check_device(ctx, fn)) != TQ_OK) return s;
-  hipError_t e = launch_polar_quantize(ctx, d_x, dtype == TQ_BF16, n, x_stride, out, out_offset, d_ws,
-                                       (hipStream_t)stream);
+  hipError_t e = launch_polar_quantize(ctx, d_x, dtype == TQ_BF16, n_streams, n_tokens, x_stride, out,
+                                       out_stream_stride, out_offset, d_ws, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
+}
+
+size_t tq_polar_attention_decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *values, int32_t q_heads) {
+  if (!ctx || !values || q_heads <= 0 || values->kv_heads <= 0 || (q_heads % values->kv_heads) != 0) return 0;
+  return polar_attention_ws_bytes(ctx, values, q_heads);
+}
+
+tq_status tq_polar_attention_decode(const tq_ctx *ctx, const tq_polar_packed *keys, const tq_kv_cache *values,
+                                    const void *d_q, tq_dtype dtype, int32_t q_heads, float scale, float *d_out,
+                                    void *d_ws, size_t ws_bytes, void *stream) {
+  const char *fn = "tq_polar_attention_decode";
+  hipEvent_t ev[2];
+  take_decode_events(ev);
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_polar_attention_decode: NULL ctx");
+  tq_status s = check_polar(ctx, keys, fn);
+  if (s != TQ_OK) return s;
+  if (!values) return fail(TQ_ERR_ARG, "tq_polar_attention_decode: NULL values");
+  if ((s = check_packed(ctx, &values->v, 0, fn)) != TQ_OK) return s;
+  if (values->batch <= 0 || values->kv_heads <= 0 || values->capacity <= 0 || (values->capacity % 32) != 0)
+    return fail(TQ_ERR_ARG, "tq_polar_attention_decode: batch, kv_heads > 0 and capacity a positive multiple of 32 required");
+  if (values->d_block_table || values->v.norm_f16)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_polar_attention_decode: contiguous values with fp32 norms only");
+  const int64_t recs = (int64_t)values->batch * values->kv_heads * values->capacity;
+  if (values->v.n < recs || keys->n < recs)
+    return fail(TQ_ERR_ARG, "tq_polar_attention_decode: key or value records fewer than batch*kv_heads*capacity");
+  if (!values->d_seq_len) return fail(TQ_ERR_ARG, "tq_polar_attention_decode: NULL d_seq_len");
+  if (values->host_max_len < 0 || values->host_max_len > values->capacity)
+    return fail(TQ_ERR_ARG, "tq_polar_attention_decode: host_max_len outside [0, capacity]");
+  if (!d_q || !d_out) return fail(TQ_ERR_ARG, "tq_polar_attention_decode: NULL query or output");
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_polar_attention_decode: dtype must be TQ_F32 or TQ_BF16");
+  if (((uintptr_t)d_q % 16) != 0) return fail(TQ_ERR_ARG, "tq_polar_attention_decode: queries must be 16-byte aligned");
+  if (q_heads <= 0 || (q_heads % values->kv_heads) != 0)
+    return fail(TQ_ERR_ARG, "tq_polar_attention_decode: q_heads must be a positive multiple of kv_heads");
+  if (q_heads / values->kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_polar_attention_decode: at most 16 query heads per KV head");
+  if ((int64_t)values->batch * values->kv_heads * ((q_heads / values->kv_heads + 3) / 4) > 65535)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_polar_attention_decode: at most 65535 (stream, head group) units");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_ARG, "tq_polar_attention_decode: scale must be finite");
+  if (!d_ws || ws_bytes < tq_polar_attention_decode_ws_bytes(ctx, values, q_heads))
+    return fail(TQ_ERR_CAPACITY, "tq_polar_attention_decode: workspace smaller than tq_polar_attention_decode_ws_bytes()");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  hipError_t e = launch_polar_attention(ctx, keys, values, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws,
+                                        (hipStream_t)stream, ev[0], ev[1]);
   return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 

@@ -91,21 +91,32 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
 // With k_new / v_new non-NULL (fused step) the new token of every stream is
 // appended first and the sequence lengths advance by one. Non-NULL ev0 / ev1 are
 // recorded on st right before / after the score/attention kernel.
+// With ext non-NULL the logits (log2 units, [stream*hgroups][4][ext_stride]) are
+// given: keys in another format, scored beforehand; q is unused and only the
+// cache's values and lengths are read (contiguous layout, fp32 norms).
 hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
                          float scale, float *out, void *ws, hipStream_t st, const void *k_new = nullptr,
                          const void *v_new = nullptr, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
-                         int n_q = 1, int causal = 0);
+                         int n_q = 1, int causal = 0, const float *ext = nullptr, int64_t ext_stride = 0);
 hipError_t launch_read_probe(const void *src, size_t bytes, int grid, uint32_t *sink, hipStream_t st);
 // C[M][N] = A[M][K] B[N][K]^T on fp32 MFMA (A fp32 or bf16, B fp32; row strides in elements)
 hipError_t launch_gemm_store(const void *a, int a_bf16, int64_t lda, int64_t M, const float *b, int64_t ldb,
                              int64_t N, int K, float *c, int64_t ldc, hipStream_t st);
-// PolarQuant keys (polar_kernels.hip), d = 128: y = Pi x of n vectors (rows of x,
-// stride xs) into records out_offset .. of `out`; ws: n * 128 floats.
-hipError_t launch_polar_quantize(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n, int64_t xs,
-                                 const tq_polar_packed *out, int64_t out_offset, void *ws, hipStream_t st);
+// PolarQuant keys (polar_kernels.hip), d = 128: y = Pi x of n_streams * n_tokens
+// vectors (rows of x, stride xs, stream-major) into records
+// s * out_stream_stride + out_offset + t of `out`; ws: rows * 128 floats.
+hipError_t launch_polar_quantize(const tq_ctx *ctx, const void *x, int is_bf16, int64_t n_streams, int64_t n_tokens,
+                                 int64_t xs, const tq_polar_packed *out, int64_t out_stream_stride, int64_t out_offset,
+                                 void *ws, hipStream_t st);
 // scores [nq][keys->n] = <Pi q, y_hat>; ws: (nq + keys->n) * 128 floats (256-aligned parts)
 hipError_t launch_polar_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_polar_packed *keys,
                                float *scores, void *ws, hipStream_t st);
+// decode attention with PolarQuant keys (records of stream s at s * capacity + t)
+// and the cache's stage-1 values; ws: polar_attention_ws_bytes()
+size_t polar_attention_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *values, int32_t q_heads);
+hipError_t launch_polar_attention(const tq_ctx *ctx, const tq_polar_packed *keys, const tq_kv_cache *values,
+                                  const void *q, int is_bf16, int32_t q_heads, float scale, float *out, void *ws,
+                                  hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores);
 hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_packed *keys,
                          float *scores, int32_t topk, int32_t *top_idx, float *top_val, void *ws, hipStream_t st);

@@ -1084,6 +1084,8 @@ struct DecodeArgs {
   int vgroup;            // n_q * group virtual heads per KV stream
   int kv_streams;        // batch * kv_heads
   RecMap map;            // record of (KV stream, token): contiguous or paged
+  const float *ext;      // EXT: logits (log2 units) [stream*hgroups][4][ext_stride], token-indexed
+  int64_t ext_stride;
   int span_lg;           // log2 of the runs of consecutive records in a chunk (chunk or page size)
   float scale_log2;      // softmax scale * log2(e)
   float qjl_scale;
@@ -1567,8 +1569,9 @@ __device__ __forceinline__ int64_t pick_span(int si, int64_t r0, int64_t r1, int
 // KB MSE bits of the keys (0: pure QJL keys), QJL: the keys carry the sign word
 // and |r| (false: MSE-only keys)
 // SPANS: the chunk's records come in several runs (pages smaller than the chunk);
-// NF16: the cache's norms are fp16
-template <int KB, int VB, bool QJL, bool SPANS, bool NF16>
+// NF16: the cache's norms are fp16; EXT: the logits come from a.ext (keys in
+// another format, scored beforehand), the values from the cache
+template <int KB, int VB, bool QJL, bool SPANS, bool NF16, bool EXT = false>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   constexpr int KM = KB > 0 ? 1 << (KB - 1) : 0;  // key Walsh masks
   constexpr int KQ = QJL ? 1 : 0;
@@ -1656,139 +1659,163 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const float *wv = a.tables->walsh[VB];
     const int ngrp = (n + 127) >> 7;
     const int tn = lane & 15, G = lane >> 4;  // MFMA column (token), row group (head)
-    // records of the chunk: uniform bases (the tile's span) and unsigned 32-bit
-    // byte offsets per lane (base + zero-extended offset addressing); lanes past
-    // the end re-read token n-1, so every store below stays unconditional and
-    // harmless
-    const uint32_t kgo = (uint32_t)(G * NPL * 4);  // the lane's 32-coordinate group in a record
-    struct KBuf {
-      uint32_t pl[KTPW][NPL];
-      float2 kn[KTPW];  // (|k|, |r|); MSE-only keys: (|k|, 0)
-      float vn[KTPW];
-      uint32_t tc[KTPW];
-    };
-    auto kload = [&](int base, KBuf &bf) {
-#pragma unroll
-      for (int u = 0; u < KTPW; ++u) {
-        const uint32_t tc = (uint32_t)min((base + u) * 16 + tn, n - 1);
-        bf.tc[u] = tc;
-        // a tile lies in one span
-        const int64_t rr = SPANS ? pick_span(min((base + u) * 16, n - 1) >> slg, rs0, rs1, rs2, rs3) : rs0;
-        const char *kb0 = reinterpret_cast<const char *>(a.kbits + rr * DW * NPL);
-        constexpr int NB = NF16 ? 2 : 4;  // bytes per norm
-        const char *kn0 = reinterpret_cast<const char *>(a.knorm) + (1 + KQ) * rr * NB;
-        const char *vn0 = reinterpret_cast<const char *>(a.vnorm) + rr * NB;
-        const uint32_t tl = SPANS ? tc & smask : tc;  // position in the span
-        const char *src = kb0 + (tl * (uint32_t)(DW * NPL * 4) + kgo);
-        if constexpr (NPL == 4) {
-          const uint4 w4 = *reinterpret_cast<const uint4 *>(src);
-          bf.pl[u][0] = w4.x; bf.pl[u][1] = w4.y; bf.pl[u][2] = w4.z; bf.pl[u][3] = w4.w;
-        } else {
-#pragma unroll
-          for (int p = 0; p < NPL; ++p) bf.pl[u][p] = reinterpret_cast<const uint32_t *>(src)[p];
-        }
-        if constexpr (NF16) {
-          if constexpr (QJL) bf.kn[u] = __half22float2(*reinterpret_cast<const __half2 *>(kn0 + (tl << 2)));
-          else bf.kn[u] = make_float2(__half2float(*reinterpret_cast<const __half *>(kn0 + (tl << 1))), 0.f);
-          bf.vn[u] = __half2float(*reinterpret_cast<const __half *>(vn0 + (tl << 1)));
-        } else {
-          if constexpr (QJL) bf.kn[u] = *reinterpret_cast<const float2 *>(kn0 + (tl << 3));
-          else bf.kn[u] = make_float2(*reinterpret_cast<const float *>(kn0 + (tl << 2)), 0.f);
-          bf.vn[u] = *reinterpret_cast<const float *>(vn0 + (tl << 2));
-        }
-      }
-    };
-    // the wave's first key tiles are requested before anything else
-    KBuf kb_a, kb_b;
-    kload(wave * KTPW, kb_a);
-    // ---- phase K: logits of all tokens of the chunk (log2 units) ----
-    const uint32_t *qf = a.qfrag + (int64_t)sg * 2 * 2 * 64 * 8;
-    auto ldfrag = [&](int T, int ins) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(qf + ((T * 2 + ins) * 64 + lane) * 8);
-      const uint4 x = p[0], y = p[1];
-      i8v v;
-      v[0] = (int)x.x; v[1] = (int)x.y; v[2] = (int)x.z; v[3] = (int)x.w;
-      v[4] = (int)y.x; v[5] = (int)y.y; v[6] = 0; v[7] = 0;
-      return v;
-    };
-    const i8v aqr0 = ldfrag(0, 0), aqr1 = ldfrag(0, 1), aqs0 = ldfrag(1, 0), aqs1 = ldfrag(1, 1);
-    const int sc0 = 127 + 3 * (lane & 3), sc1 = sc0 + 12;  // e8m0 row scales 2^(3 digit)
-    const float *qc = a.qconst + ((int64_t)sg * 4 + G) * QC;
-    // accumulator start -sum_j Q_j per digit slot: the A fragments against an
-    // all-ones mask (B scale 2^1 undoes the 1/2 of every product), exact
-    f4v init_r = {0.f, 0.f, 0.f, 0.f}, init_s = {0.f, 0.f, 0.f, 0.f};
-    {
-      const i8v ones = mask_fp4_01(0xFFFFFFFFu);
-      const f4v z = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (KM > 0) {
-        init_r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr0, ones, z, 2, 4, 0, sc0, 0, 128);
-        init_r = -__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr1, ones, init_r, 2, 4, 0, sc1, 0, 128);
-      }
-      if constexpr (QJL) {
-        init_s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs0, ones, z, 2, 4, 0, sc0, 0, 128);
-        init_s = -__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs1, ones, init_s, 2, 4, 0, sc1, 0, 128);
-      }
-    }
-    // logit (log2 units) = |k| (sum_S wr_S T_S + qs |r| T_QJL) with the query units,
-    // the softmax scale and the QJL constant folded into the per-lane weights
-    const float sr = qc[0] * a.scale_log2, qs = qc[1] * a.qjl_scale * a.scale_log2;
-    float wkr[KM > 0 ? KM : 1];
-#pragma unroll
-    for (int mi = 0; mi < KM; ++mi) wkr[mi] = wk[mi] * sr;
     float vmx = 0.f, lmx = -INFINITY;
-    const int ntile = (n + 15) >> 4;
-    const int visG = vis(G);  // tokens of the chunk this lane's virtual head sees
-    auto kcompute = [&](int base, const KBuf &cur) {
-      (void)base;
+    if constexpr (EXT) {
+      // ---- phase K from logits computed beforehand (log2 units, [unit][4][ext_stride]) ----
+      const float *lgx = a.ext + (int64_t)sg * 4 * a.ext_stride + t0;
+      const float *vnx = reinterpret_cast<const float *>(a.vnorm) + rs0;
+      const int vis0 = vis(0), vis1 = vis(1), vis2 = vis(2), vis3 = vis(3);
+      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      for (int tc = tid; tc < n; tc += 256) {
+        const float vv = vnx[tc];
+        vnl[tc] = vv;
+        vmx = fmaxf(vmx, vv);
+        const int vh[4] = {vis0, vis1, vis2, vis3};
 #pragma unroll
-      for (int u = 0; u < KTPW; ++u) {
-        const int tc = (int)cur.tc[u];
-        // all masked sums first (independent accumulators keep the MFMA pipe busy):
-        // the KM Walsh masks of the codes, then the sign word's mask
-        f4v acc[KM + KQ];
-        i8v sm[KB > 0 ? KB : 1];
-#pragma unroll
-        for (int p = 0; p < KB; ++p) sm[p] = mask_fp4_01(cur.pl[u][p]);
-#pragma unroll
-        for (int mi = 0; mi < KM + KQ; ++mi) {
-          const i8v bm = mi < KM ? walsh_fp4(sm, walsh_mask(KB, mi)) : mask_fp4_01(cur.pl[u][NPL - 1]);
-          acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr0 : aqs0, bm, mi < KM ? init_r : init_s,
-                                                                     2, 4, 0, sc0, 0, 129);
-          acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr1 : aqs1, bm, acc[mi], 2, 4, 0, sc1,
-                                                                     0, 129);
+        for (int h = 0; h < 4; ++h) {
+          const float x = (h < nh && tc < vh[h]) ? lgx[(int64_t)h * a.ext_stride + tc] : -INFINITY;
+          lg[h * a.chunk + tc] = x;
+          m4[h] = fmaxf(m4[h], x);
         }
-        float code = 0.f;
-#pragma unroll
-        for (int mi = 0; mi < KM; ++mi) code += wkr[mi] * ((acc[mi][0] + acc[mi][1]) + (acc[mi][2] + acc[mi][3]));
-        float s;
-        if constexpr (QJL) {
-          const float Ts = (acc[KM][0] + acc[KM][1]) + (acc[KM][2] + acc[KM][3]);
-          s = cur.kn[u].x * fmaf(cur.kn[u].y * Ts, qs, code);
-        } else {
-          s = cur.kn[u].x * code;
-        }
-        s = tc < visG ? s : -INFINITY;  // causal mask of this lane's virtual head
-        lg[G * a.chunk + tc] = s;
-        lmx = fmaxf(lmx, s);
-        vnl[tc] = cur.vn[u];
-        vmx = fmaxf(vmx, cur.vn[u]);
       }
-    };
-    // two buffers in turn: the next round's loads are in flight during this one.
-    // The loads are unconditional (tiles past the end re-read token n-1) and pinned
-    // ahead of the compute, so their latency overlaps a whole round.
-    constexpr int KSTEP = 4 * KTPW;
-    int kbase = wave * KTPW;
-    while (kbase < ntile) {
-      kload(kbase + KSTEP, kb_b);
-      __builtin_amdgcn_sched_barrier(0);
-      kcompute(kbase, kb_a);
-      kbase += KSTEP;
-      if (kbase >= ntile) break;
-      kload(kbase + KSTEP, kb_a);
-      __builtin_amdgcn_sched_barrier(0);
-      kcompute(kbase, kb_b);
-      kbase += KSTEP;
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        for (int off = 32; off > 0; off >>= 1) m4[h] = fmaxf(m4[h], __shfl_xor(m4[h], off));
+      lmx = G == 0 ? m4[0] : G == 1 ? m4[1] : G == 2 ? m4[2] : m4[3];  // the row-group layout below
+    } else {
+    // records of the chunk: uniform bases (the tile's span) and unsigned 32-bit
+      // byte offsets per lane (base + zero-extended offset addressing); lanes past
+      // the end re-read token n-1, so every store below stays unconditional and
+      // harmless
+      const uint32_t kgo = (uint32_t)(G * NPL * 4);  // the lane's 32-coordinate group in a record
+      struct KBuf {
+        uint32_t pl[KTPW][NPL];
+        float2 kn[KTPW];  // (|k|, |r|); MSE-only keys: (|k|, 0)
+        float vn[KTPW];
+        uint32_t tc[KTPW];
+      };
+      auto kload = [&](int base, KBuf &bf) {
+#pragma unroll
+        for (int u = 0; u < KTPW; ++u) {
+          const uint32_t tc = (uint32_t)min((base + u) * 16 + tn, n - 1);
+          bf.tc[u] = tc;
+          // a tile lies in one span
+          const int64_t rr = SPANS ? pick_span(min((base + u) * 16, n - 1) >> slg, rs0, rs1, rs2, rs3) : rs0;
+          const char *kb0 = reinterpret_cast<const char *>(a.kbits + rr * DW * NPL);
+          constexpr int NB = NF16 ? 2 : 4;  // bytes per norm
+          const char *kn0 = reinterpret_cast<const char *>(a.knorm) + (1 + KQ) * rr * NB;
+          const char *vn0 = reinterpret_cast<const char *>(a.vnorm) + rr * NB;
+          const uint32_t tl = SPANS ? tc & smask : tc;  // position in the span
+          const char *src = kb0 + (tl * (uint32_t)(DW * NPL * 4) + kgo);
+          if constexpr (NPL == 4) {
+            const uint4 w4 = *reinterpret_cast<const uint4 *>(src);
+            bf.pl[u][0] = w4.x; bf.pl[u][1] = w4.y; bf.pl[u][2] = w4.z; bf.pl[u][3] = w4.w;
+          } else {
+#pragma unroll
+            for (int p = 0; p < NPL; ++p) bf.pl[u][p] = reinterpret_cast<const uint32_t *>(src)[p];
+          }
+          if constexpr (NF16) {
+            if constexpr (QJL) bf.kn[u] = __half22float2(*reinterpret_cast<const __half2 *>(kn0 + (tl << 2)));
+            else bf.kn[u] = make_float2(__half2float(*reinterpret_cast<const __half *>(kn0 + (tl << 1))), 0.f);
+            bf.vn[u] = __half2float(*reinterpret_cast<const __half *>(vn0 + (tl << 1)));
+          } else {
+            if constexpr (QJL) bf.kn[u] = *reinterpret_cast<const float2 *>(kn0 + (tl << 3));
+            else bf.kn[u] = make_float2(*reinterpret_cast<const float *>(kn0 + (tl << 2)), 0.f);
+            bf.vn[u] = *reinterpret_cast<const float *>(vn0 + (tl << 2));
+          }
+        }
+      };
+      // the wave's first key tiles are requested before anything else
+      KBuf kb_a, kb_b;
+      kload(wave * KTPW, kb_a);
+      // ---- phase K: logits of all tokens of the chunk (log2 units) ----
+      const uint32_t *qf = a.qfrag + (int64_t)sg * 2 * 2 * 64 * 8;
+      auto ldfrag = [&](int T, int ins) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(qf + ((T * 2 + ins) * 64 + lane) * 8);
+        const uint4 x = p[0], y = p[1];
+        i8v v;
+        v[0] = (int)x.x; v[1] = (int)x.y; v[2] = (int)x.z; v[3] = (int)x.w;
+        v[4] = (int)y.x; v[5] = (int)y.y; v[6] = 0; v[7] = 0;
+        return v;
+      };
+      const i8v aqr0 = ldfrag(0, 0), aqr1 = ldfrag(0, 1), aqs0 = ldfrag(1, 0), aqs1 = ldfrag(1, 1);
+      const int sc0 = 127 + 3 * (lane & 3), sc1 = sc0 + 12;  // e8m0 row scales 2^(3 digit)
+      const float *qc = a.qconst + ((int64_t)sg * 4 + G) * QC;
+      // accumulator start -sum_j Q_j per digit slot: the A fragments against an
+      // all-ones mask (B scale 2^1 undoes the 1/2 of every product), exact
+      f4v init_r = {0.f, 0.f, 0.f, 0.f}, init_s = {0.f, 0.f, 0.f, 0.f};
+      {
+        const i8v ones = mask_fp4_01(0xFFFFFFFFu);
+        const f4v z = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KM > 0) {
+          init_r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr0, ones, z, 2, 4, 0, sc0, 0, 128);
+          init_r = -__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqr1, ones, init_r, 2, 4, 0, sc1, 0, 128);
+        }
+        if constexpr (QJL) {
+          init_s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs0, ones, z, 2, 4, 0, sc0, 0, 128);
+          init_s = -__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aqs1, ones, init_s, 2, 4, 0, sc1, 0, 128);
+        }
+      }
+      // logit (log2 units) = |k| (sum_S wr_S T_S + qs |r| T_QJL) with the query units,
+      // the softmax scale and the QJL constant folded into the per-lane weights
+      const float sr = qc[0] * a.scale_log2, qs = qc[1] * a.qjl_scale * a.scale_log2;
+      float wkr[KM > 0 ? KM : 1];
+#pragma unroll
+      for (int mi = 0; mi < KM; ++mi) wkr[mi] = wk[mi] * sr;
+      const int ntile = (n + 15) >> 4;
+      const int visG = vis(G);  // tokens of the chunk this lane's virtual head sees
+      auto kcompute = [&](int base, const KBuf &cur) {
+        (void)base;
+#pragma unroll
+        for (int u = 0; u < KTPW; ++u) {
+          const int tc = (int)cur.tc[u];
+          // all masked sums first (independent accumulators keep the MFMA pipe busy):
+          // the KM Walsh masks of the codes, then the sign word's mask
+          f4v acc[KM + KQ];
+          i8v sm[KB > 0 ? KB : 1];
+#pragma unroll
+          for (int p = 0; p < KB; ++p) sm[p] = mask_fp4_01(cur.pl[u][p]);
+#pragma unroll
+          for (int mi = 0; mi < KM + KQ; ++mi) {
+            const i8v bm = mi < KM ? walsh_fp4(sm, walsh_mask(KB, mi)) : mask_fp4_01(cur.pl[u][NPL - 1]);
+            acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr0 : aqs0, bm, mi < KM ? init_r : init_s,
+                                                                       2, 4, 0, sc0, 0, 129);
+            acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mi < KM ? aqr1 : aqs1, bm, acc[mi], 2, 4, 0, sc1,
+                                                                       0, 129);
+          }
+          float code = 0.f;
+#pragma unroll
+          for (int mi = 0; mi < KM; ++mi) code += wkr[mi] * ((acc[mi][0] + acc[mi][1]) + (acc[mi][2] + acc[mi][3]));
+          float s;
+          if constexpr (QJL) {
+            const float Ts = (acc[KM][0] + acc[KM][1]) + (acc[KM][2] + acc[KM][3]);
+            s = cur.kn[u].x * fmaf(cur.kn[u].y * Ts, qs, code);
+          } else {
+            s = cur.kn[u].x * code;
+          }
+          s = tc < visG ? s : -INFINITY;  // causal mask of this lane's virtual head
+          lg[G * a.chunk + tc] = s;
+          lmx = fmaxf(lmx, s);
+          vnl[tc] = cur.vn[u];
+          vmx = fmaxf(vmx, cur.vn[u]);
+        }
+      };
+      // two buffers in turn: the next round's loads are in flight during this one.
+      // The loads are unconditional (tiles past the end re-read token n-1) and pinned
+      // ahead of the compute, so their latency overlaps a whole round.
+      constexpr int KSTEP = 4 * KTPW;
+      int kbase = wave * KTPW;
+      while (kbase < ntile) {
+        kload(kbase + KSTEP, kb_b);
+        __builtin_amdgcn_sched_barrier(0);
+        kcompute(kbase, kb_a);
+        kbase += KSTEP;
+        if (kbase >= ntile) break;
+        kload(kbase + KSTEP, kb_a);
+        __builtin_amdgcn_sched_barrier(0);
+        kcompute(kbase, kb_b);
+        kbase += KSTEP;
+      }
     }
     // the first value blocks are requested before the softmax
     const int vn = lane & 15, vg = lane >> 4;  // coordinate column, token block in the 128-token group
@@ -1997,7 +2024,7 @@ static hipError_t launch_decode_kv(const DecodeArgs &a, dim3 grid, size_t shm, h
 
 hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
                          float scale, float *out, void *ws, hipStream_t st, const void *k_new, const void *v_new,
-                         hipEvent_t ev0, hipEvent_t ev1, int n_q, int causal) {
+                         hipEvent_t ev0, hipEvent_t ev1, int n_q, int causal, const float *ext, int64_t ext_stride) {
   int chunk = 0, nchunks = 0;
   decode_ws_bytes(ctx, cache, q_heads, &chunk, &nchunks, n_q);
   DecodeArgs a = {};
@@ -2058,9 +2085,29 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
     a.len_inc = cache->d_seq_len;
   }
   a.streams_hg = streams;
+  a.ext = ext;
+  a.ext_stride = ext_stride;
   // two (stream, head group) units per query block; fused step: one more block
   // per two KV streams appends their new tokens
   a.batch = cache->batch;
+  if (ext) {
+    // logits computed beforehand: no query preparation, the values from the cache
+    const size_t shm = (size_t)5 * chunk * sizeof(float) + (size_t)(chunk / 128) * 2 * 64 * 16;
+    const dim3 grid(nchunks * streams);
+    hipError_t e = hipSuccess;
+    if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
+    switch (cache->v.mse_bits) {
+      case 1: hipLaunchKernelGGL((decode_kernel<1, 1, false, false, false, true>), grid, dim3(256), shm, st, a); break;
+      case 2: hipLaunchKernelGGL((decode_kernel<1, 2, false, false, false, true>), grid, dim3(256), shm, st, a); break;
+      case 3: hipLaunchKernelGGL((decode_kernel<1, 3, false, false, false, true>), grid, dim3(256), shm, st, a); break;
+      case 4: hipLaunchKernelGGL((decode_kernel<1, 4, false, false, false, true>), grid, dim3(256), shm, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(streams), dim3(1024), 0, st, a);
+    return hipGetLastError();
+  }
   const dim3 pgrid((streams + 1) / 2 + (step ? (cache->batch * cache->kv_heads + 1) / 2 : 0));
   if (is_bf16)
     hipLaunchKernelGGL((step ? decode_prep_kernel<uint16_t, true> : decode_prep_kernel<uint16_t, false>), pgrid,

@@ -152,3 +152,75 @@ def test_polar_argument_errors(ctx_pi):
     with pytest.raises(tq.TQError):
         tq.polar_quantize(c256, torch.zeros((4, 256), device=DEV), keys)  # d != 128
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("hq", [8, 32])
+def test_polar_attention_decode(ctx_pi, hq):
+    """batch 3 (lengths 1500, 0, 777), 2 KV heads, groups of 4 or 16 query
+    heads: decode attention over PolarQuant keys (oracle-packed, uploaded) and
+    3-bit stage-1 values within 2e-3 max-abs of the oracle; a sequence with no
+    tokens gives zeros."""
+    ctx, Pi = ctx_pi
+    B, H, cap, L, d = 3, 2, 1536, 1500, 128
+    seq = [1500, 0, 777]
+    pcb = PQ.polar_codebooks(128, 4, 3)
+    cbv = T.codebook(d, 3)
+    K = synth.outlier_kv(74, (hq, 1), synth.TAG_SCALES_K, (B, H, L, d))
+    V = synth.outlier_kv(74, (hq, 2), synth.TAG_SCALES_V, (B, H, L, d))
+    Q = synth.gaussian(74, (hq, 3), (B, hq, d), "bf16")
+    cache = tq.PolarKVCache(B, H, cap)
+    recs = {}
+    for b in range(B):
+        for h in range(H):
+            s = b * H + h
+            kr = PQ.pack_polar(PQ.polar_encode(K[b, h], Pi, pcb), pcb)
+            vr = T.pack_values(T.encode(V[b, h], Pi, cbv), 3)
+            cache.keys.words[s * cap:s * cap + L].copy_(torch.from_numpy(kr["bits"].view(np.int32)).to(DEV))
+            cache.keys.norms[s * cap:s * cap + L].copy_(torch.from_numpy(kr["norms"]).to(DEV))
+            nb = vr["bits"].shape[0]
+            cache.values.v.words[s * cap // 32:s * cap // 32 + nb].copy_(torch.from_numpy(vr["bits"].view(np.int32)).to(DEV))
+            cache.values.v.norms[s * cap:s * cap + L].copy_(torch.from_numpy(vr["norms"]).to(DEV))
+            recs[s] = (kr, vr)
+    cache.seq_len.copy_(torch.tensor(seq, dtype=torch.int32))
+    cache.host_max_len = max(seq)
+    scale = 1 / math.sqrt(d)
+    out = cache.decode(ctx, _dev(Q, "bf16"), scale).cpu().numpy()
+    g = hq // H
+    for b in range(B):
+        for h in range(H):
+            kr, vr = recs[b * H + h]
+            n = seq[b]
+            if n == 0:
+                assert not out[b, h * g:(h + 1) * g].any()
+                continue
+            ref = PQ.polar_attention_decode(Q[b, h * g:(h + 1) * g], Pi, pcb, cbv, kr,
+                                            {"bits": vr["bits"], "norms": vr["norms"][:n]}, n, scale,
+                                            T.unpack_values)
+            assert np.max(np.abs(out[b, h * g:(h + 1) * g] - ref)) <= 2e-3, f"b={b} h={h}"
+
+
+def test_polar_cache_prefill_and_decode(ctx_pi):
+    """PolarKVCache.prefill encodes keys on the GPU (stream-strided records) and
+    values with the fused quantize; decode over them matches the oracle over the
+    records the GPU wrote."""
+    ctx, Pi = ctx_pi
+    B, H, cap, L, d, hq = 2, 2, 640, 600, 128, 8
+    K = synth.outlier_kv(75, (1,), synth.TAG_SCALES_K, (B, H, L, d), "bf16")
+    V = synth.outlier_kv(75, (2,), synth.TAG_SCALES_V, (B, H, L, d), "bf16")
+    Q = synth.gaussian(75, (3,), (B, hq, d), "bf16")
+    cache = tq.PolarKVCache(B, H, cap)
+    cache.prefill(ctx, _dev(K, "bf16"), _dev(V, "bf16"))
+    out = cache.decode(ctx, _dev(Q, "bf16")).cpu().numpy()
+    kw, kn = cache.keys.host()
+    vw, vn = cache.values.v.host()
+    pcb = PQ.polar_codebooks(128, 4, 3)
+    cbv = T.codebook(d, 3)
+    for b in range(B):
+        for h in range(H):
+            s = b * H + h
+            check_polar_records(kw[s * cap:s * cap + L], kn[s * cap:s * cap + L], K[b, h], Pi, pcb)
+            ref = PQ.polar_attention_decode(Q[b, h * 4:h * 4 + 4], Pi, pcb, cbv,
+                                            {"bits": kw[s * cap:s * cap + L], "norms": kn[s * cap:s * cap + L]},
+                                            {"bits": vw[s * cap // 32:(s + 1) * cap // 32], "norms": vn[s * cap:s * cap + L]},
+                                            L, 1 / math.sqrt(d), T.unpack_values)
+            assert np.max(np.abs(out[b, h * 4:h * 4 + 4] - ref)) <= 2e-3
