@@ -1112,13 +1112,6 @@ __host__ __device__ constexpr int walsh_mask(int B, int i) {
   return i < B ? (1 << i) : (B == 3 ? 7 : (i == 4 ? 7 : i == 5 ? 11 : i == 6 ? 13 : 14));
 }
 
-// e2m3 code of |digit| * f for f = 1, 1/2, 1/4 (f index fi = 0, 1, 2), |digit| <= 4:
-// f = 1: 1 -> 0x08, 2 -> 0x10, 3 -> 0x14, 4 -> 0x18; f = 1/2: code 4m; f = 1/4: code 2m.
-__device__ __forceinline__ uint32_t fp6_mag(uint32_t mag, int fi) {
-  const uint32_t c1 = mag <= 1u ? (mag << 3) : (8u + (mag << 2));
-  return fi == 0 ? c1 : (mag << (fi == 1 ? 2 : 1));
-}
-
 template <typename QT>
 __device__ __forceinline__ float qload(const QT *q, int64_t i) {
   if constexpr (sizeof(QT) == 2) return bf16f(q[i]);
@@ -1287,10 +1280,29 @@ struct QueryLds {
   float part2[8][2 * DD];
   float qv[2][8][DD];          // q_rot, q_s
   float mx[2][8];              // max |q_rot|, max |q_s| per head
-  // fp6 codes, one per byte: [type][head][digit][32-coordinate group g][element e],
-  // element e = 8q + i <-> coordinate 32g + 4i + q (the fp4 mask order)
-  uint8_t cl[2][8][8][4][32];
+  // fixed-point queries offset by QOFF: [type][head][coordinate]
+  uint32_t qz[2][8][DD];
 };
+
+// Balanced base-8 digits d_k in [-4, 3] of an integer |x| <= QMAX: adding
+// QOFF = sum_k 4 * 8^k (k < 8) makes them the plain base-8 digits d_k + 4 of
+// x + QOFF, which lies in [0, 8^8).
+constexpr int QOFF = 9586980;
+
+// e2m3 codes of the eight digit values v - 4 (v = 0..7) scaled by f = 1, 1/2,
+// 1/4 (fi = 0, 1, 2), six bits per value; sign bit 0x20, magnitude m: f = 1:
+// 1 -> 0x08, 2 -> 0x10, 3 -> 0x14, 4 -> 0x18; f = 1/2: code 4m; f = 1/4: code 2m
+__host__ __device__ constexpr uint64_t digit_code_table(int fi) {
+  uint64_t t = 0;
+  for (int v = 0; v < 8; ++v) {
+    const int dv = v - 4;
+    const uint32_t mag = (uint32_t)(dv < 0 ? -dv : dv);
+    const uint32_t c1 = mag <= 1u ? (mag << 3) : (8u + (mag << 2));
+    const uint32_t c = (fi == 0 ? c1 : (mag << (fi == 1 ? 2 : 1))) | (dv < 0 ? 0x20u : 0u);
+    t |= (uint64_t)c << (6 * v);
+  }
+  return t;
+}
 
 template <typename QT, bool APPEND>
 __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
@@ -1372,22 +1384,16 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  // thread (head, coordinate): balanced base-8 digits in [-4, 3] of both query
-  // types, stored as e2m3 codes of digit * (1, 1/2, 1/4, 1/4)[j % 4]
+  // thread (head, coordinate): the fixed-point query of both types, offset so
+  // that its digits are plain base-8 digits
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int e = i * 512 + tid, hh = e >> 7, j = e & (DD - 1);
-    const int g = j >> 5, el = 8 * (j & 3) + ((j >> 2) & 7), fi = min(j & 3, 2);
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       const float m = ql.mx[T][hh];
-      int qi = m > 0.f ? (int)rintf(ql.qv[T][hh][j] * (QMAX / m)) : 0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int dv = ((qi + 4) & 7) - 4;
-        qi = (qi - dv) >> 3;
-        ql.cl[T][hh][k][g][el] = (uint8_t)(fp6_mag((uint32_t)(dv < 0 ? -dv : dv), fi) | (dv < 0 ? 0x20u : 0u));
-      }
+      const int qi = m > 0.f ? (int)rintf(ql.qv[T][hh][j] * (QMAX / m)) : 0;
+      ql.qz[T][hh][j] = (uint32_t)(qi + QOFF);
     }
   }
   if (tid < 16) {
@@ -1398,27 +1404,27 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
   __syncthreads();
   {
     // fragment (unit, T, instr, lane): the 32 codes of row (4*hh + slot), digit
-    // 4*instr + slot, packed at 6 bits each (element e at bit 6e): every 4 codes
-    // make 24 bits
+    // 4*instr + slot, packed at 6 bits each (element e at bit 6e); element
+    // e = 8q + i holds coordinate 32g + 4i + q, scaled by (1, 1/2, 1/4, 1/4)[q]
+    constexpr uint64_t dct[3] = {digit_code_table(0), digit_code_table(1), digit_code_table(2)};
     const int u2 = tid >> 8, T = (tid >> 7) & 1, ins = (tid >> 6) & 1, Ln = tid & 63;
     const int g = Ln >> 4, row = Ln & 15, hh = u2 * 4 + (row >> 2), dig = 4 * ins + (row & 3);
     if (nhu[u2] > 0) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(&ql.cl[T][hh][dig][g][0]);
-      const uint4 c0 = src[0], c1 = src[1];
-      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      uint32_t t24[8];
+      const uint4 *src = reinterpret_cast<const uint4 *>(&ql.qz[T][hh][32 * g]);
+      const uint32_t sh = 3 * dig;
+      uint32_t dw[6] = {0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const uint32_t w = cw[m];
-        t24[m] = (w & 0x3Fu) | ((w >> 2) & 0xFC0u) | ((w >> 4) & 0x3F000u) | ((w >> 6) & 0xFC0000u);
-      }
-      uint32_t dw[6];
+      for (int i = 0; i < 8; ++i) {
+        const uint4 z4 = src[i];
+        const uint32_t zq[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {  // 4 chunks of 24 bits -> 3 dwords
-        const uint32_t *t = t24 + 4 * h;
-        dw[3 * h + 0] = t[0] | (t[1] << 24);
-        dw[3 * h + 1] = (t[1] >> 8) | (t[2] << 16);
-        dw[3 * h + 2] = (t[2] >> 16) | (t[3] << 8);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t v = (zq[q] >> sh) & 7u;
+          const uint32_t code = (uint32_t)(dct[q < 2 ? q : 2] >> (6 * v)) & 63u;
+          const int bit = 6 * (8 * q + i);
+          dw[bit >> 5] |= code << (bit & 31);
+          if ((bit & 31) > 26) dw[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+        }
       }
       uint4 *dst = reinterpret_cast<uint4 *>(a.qfrag + ((((int64_t)sgu[u2] * 2 + T) * 2 + ins) * 64 + Ln) * 8);
       dst[0] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
@@ -1477,11 +1483,13 @@ __device__ __forceinline__ uint32_t xor_planes(const uint32_t (&pl)[NP], int S) 
 }
 
 // One block of 1024 threads per (stream, head group): log-sum-exp merge of the
-// chunk partials, then o = Pi^T o_rot. The chunks are split over four thread
-// groups (max pass, then scaled sums), so long contexts keep many loads in flight.
+// chunk partials, then o = Pi^T o_rot. The Pi entries of the inverse rotation
+// are requested first; the chunks are split over four thread groups, each of
+// which sums its chunks in one pass against its own running maximum, and the
+// four group sums are combined against the overall maximum.
 __global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
-  constexpr int MG = 4, CB = 8;
-  __shared__ float gmax[MG][4], gl[MG][4];
+  constexpr int MG = 4, CB = 4;
+  __shared__ float gm[MG][4], gl[MG][4];
   __shared__ float po[MG][4][DD];
   __shared__ float orot[4][DD];
   __shared__ float pk[8][4][DD];
@@ -1492,18 +1500,16 @@ __global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
   const int nh = min(4, a.vgroup - hg * 4);
   // fused step: the appended token is now part of every stream of sequence b
   if (a.len_inc && tid == 0 && hg == 0 && stream % a.kv_heads == 0 && a.len_inc[b] < a.capacity) a.len_inc[b] += 1;
+  // thread (coordinate j, k slice kg) of the inverse rotation: column j of Pi, rows 16 kg .. 16 kg + 15
+  const int j = tid & (DD - 1), kg = tid >> 7;
+  float rk[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) rk[u] = a.rot[(kg * 16 + u) * DD + j];
   const int cg = tid >> 8, hh = (tid >> 6) & 3;  // chunk group, head (one wave per pair)
   const int nc = a.nchunks;
   const float *p = a.partial + ((int64_t)stream * a.vgroup + hg * 4 + min(hh, nh - 1)) * nc * (DD + 2);
-  // global max of the chunk maxima of this head
-  float m = -INFINITY;
-  for (int c = cg * 64 + lane; c < nc; c += MG * 64) m = fmaxf(m, p[(int64_t)c * (DD + 2) + DD]);
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) gmax[cg][hh] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(gmax[0][hh], gmax[1][hh]), fmaxf(gmax[2][hh], gmax[3][hh]));
-  // this group's chunks c = cg (mod 4): lane owns coordinates lane and lane + 64
-  float O0 = 0.f, O1 = 0.f, L = 0.f;
+  // chunks c = cg (mod MG); lane owns coordinates lane and lane + 64
+  float m = -INFINITY, L = 0.f, O0 = 0.f, O1 = 0.f;
   for (int c0 = cg; c0 < nc; c0 += MG * CB) {
     float mv[CB], lv[CB], o0[CB], o1[CB];
 #pragma unroll
@@ -1515,48 +1521,64 @@ __global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
       o0[u] = pc[lane];
       o1[u] = pc[lane + 64];
     }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) mn = fmaxf(mn, mv[u]);
+    // what is summed so far moves to the new maximum (nothing is summed while m = -inf)
+    const float s = m == -INFINITY ? 0.f : exp2f(m - mn);
+    L *= s;
+    O0 *= s;
+    O1 *= s;
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      const float f = mv[u] == -INFINITY ? 0.f : exp2f(mv[u] - M);
+      const float f = mv[u] == -INFINITY ? 0.f : exp2f(mv[u] - mn);
       L = fmaf(f, lv[u], L);
       O0 = fmaf(f, o0[u], O0);
       O1 = fmaf(f, o1[u], O1);
     }
+    m = mn;
   }
   po[cg][hh][lane] = O0;
   po[cg][hh][lane + 64] = O1;
-  if (lane == 0) gl[cg][hh] = L;
-  __syncthreads();
-  if (tid < 4 * DD) {
-    const int h = tid >> 7, j = tid & (DD - 1);
-    const float Lh = (gl[0][h] + gl[1][h]) + (gl[2][h] + gl[3][h]);
-    const float Oh = (po[0][h][j] + po[1][h][j]) + (po[2][h][j] + po[3][h][j]);
-    orot[h][j] = (h < nh && Lh > 0.f) ? Oh / Lh : 0.f;
+  if (lane == 0) {
+    gm[cg][hh] = m;
+    gl[cg][hh] = L;
   }
   __syncthreads();
-  // o = Pi^T o_rot: column j of Pi (coalesced over j), k split in eight slices
+  if (tid < 4 * DD) {
+    const int h = tid >> 7, jj = tid & (DD - 1);
+    const float M = fmaxf(fmaxf(gm[0][h], gm[1][h]), fmaxf(gm[2][h], gm[3][h]));
+    float Lh = 0.f, Oh = 0.f;
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+      const float w = gm[g][h] == -INFINITY ? 0.f : exp2f(gm[g][h] - M);
+      Lh = fmaf(w, gl[g][h], Lh);
+      Oh = fmaf(w, po[g][h][jj], Oh);
+    }
+    orot[h][jj] = (h < nh && Lh > 0.f) ? Oh / Lh : 0.f;
+  }
+  __syncthreads();
+  // o = Pi^T o_rot: k split in eight slices
   {
-    const int j = tid & (DD - 1), kg = tid >> 7;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = kg * 16; k < kg * 16 + 16; ++k) {
-      const float r = a.rot[k * DD + j];
+    for (int u = 0; u < 16; ++u) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h) acc[h] = fmaf(r, orot[h][k], acc[h]);
+      for (int h = 0; h < 4; ++h) acc[h] = fmaf(rk[u], orot[h][kg * 16 + u], acc[h]);
     }
 #pragma unroll
     for (int h = 0; h < 4; ++h) pk[kg][h][j] = acc[h];
   }
   __syncthreads();
   if (tid < 4 * DD) {
-    const int h = tid >> 7, j = tid & (DD - 1);
+    const int h = tid >> 7, jo = tid & (DD - 1);
     if (h < nh) {
       float o = 0.f;
 #pragma unroll
-      for (int kg = 0; kg < 8; ++kg) o += pk[kg][h][j];
+      for (int s = 0; s < 8; ++s) o += pk[s][h][jo];
       // virtual head -> (query position qi, head qj of the group)
       const int vh = hg * 4 + h, qi = vh / a.group, qj = vh - qi * a.group;
-      a.out[(((int64_t)b * a.n_q + qi) * a.q_heads + kvh * a.group + qj) * DD + j] = o;
+      a.out[(((int64_t)b * a.n_q + qi) * a.q_heads + kvh * a.group + qj) * DD + jo] = o;
     }
   }
 }
