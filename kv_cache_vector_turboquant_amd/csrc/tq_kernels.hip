@@ -1461,25 +1461,32 @@ __device__ __forceinline__ i8v mask_fp4_01(uint32_t w) {
 
 // fp4 B operand of a Walsh mask from the B operands of the single planes: the AND
 // masks commute with XOR, so each dword is the XOR of the planes' dwords
+// (S is one of the odd subsets of at most four planes that walsh_mask lists:
+// one plane or three; three take one three-input XOR per dword)
+__host__ __device__ constexpr int nth_plane(int S, int k) {
+  for (int p = 0; p < 4; ++p)
+    if (S & (1 << p)) {
+      if (k == 0) return p;
+      --k;
+    }
+  return 0;
+}
+
 template <int NP>
 __device__ __forceinline__ i8v walsh_fp4(const i8v (&sm)[NP], int S) {
+  if (__builtin_popcount(S) == 1) return sm[nth_plane(S, 0)];
+  const i8v &x = sm[nth_plane(S, 0)], &y = sm[nth_plane(S, 1)], &z = sm[nth_plane(S, 2)];
   i8v r = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-  for (int p = 0; p < NP; ++p)
-    if (S & (1 << p)) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) r[q] ^= sm[p][q];
-    }
+  for (int q = 0; q < 4; ++q)
+    r[q] = (int)__builtin_amdgcn_bitop3_b32((uint32_t)x[q], (uint32_t)y[q], (uint32_t)z[q], 0x96);
   return r;
 }
 
 template <int NP>
 __device__ __forceinline__ uint32_t xor_planes(const uint32_t (&pl)[NP], int S) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int p = 0; p < NP && p < 4; ++p)
-    if (S & (1 << p)) m ^= pl[p];
-  return m;
+  if (__builtin_popcount(S) == 1) return pl[nth_plane(S, 0)];
+  return __builtin_amdgcn_bitop3_b32(pl[nth_plane(S, 0)], pl[nth_plane(S, 1)], pl[nth_plane(S, 2)], 0x96);
 }
 
 // One block of 1024 threads per (stream, head group): log-sum-exp merge of the
@@ -1705,10 +1712,11 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         for (int off = 32; off > 0; off >>= 1) m4[h] = fmaxf(m4[h], __shfl_xor(m4[h], off));
       lmx = G == 0 ? m4[0] : G == 1 ? m4[1] : G == 2 ? m4[2] : m4[3];  // the row-group layout below
     } else {
-    // records of the chunk: uniform bases (the tile's span) and unsigned 32-bit
+      // records of the chunk. Contiguous caches: buffer loads (below). Pages
+      // smaller than the chunk: uniform bases (the tile's span) and unsigned 32-bit
       // byte offsets per lane (base + zero-extended offset addressing); lanes past
-      // the end re-read token n-1, so every store below stays unconditional and
-      // harmless
+      // the end re-read token n-1. Either way every store below stays
+      // unconditional and harmless (tokens past n get -inf logits)
       const uint32_t kgo = (uint32_t)(G * NPL * 4);  // the lane's 32-coordinate group in a record
       struct KBuf {
         uint32_t pl[KTPW][NPL];
@@ -1716,15 +1724,60 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         float vn[KTPW];
         uint32_t tc[KTPW];
       };
+      // contiguous records: range-checked buffer loads over the chunk's n records
+      // (a load past them returns zeros: those tokens' logits are masked and
+      // their value norms 0), so no clamping and constant offsets per tile
+      constexpr int NB = NF16 ? 2 : 4;  // bytes per norm
+      constexpr int RB = DW * NPL * 4;  // bytes per key record
+      const __amdgpu_buffer_rsrc_t rkb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint32_t *>(a.kbits) + rs0 * DW * NPL, (short)0, n * RB, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rkn = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<char *>(const_cast<void *>(a.knorm)) + (1 + KQ) * rs0 * NB, (short)0, n * (1 + KQ) * NB,
+          0x00020000);
+      const __amdgpu_buffer_rsrc_t rvn = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<char *>(const_cast<void *>(a.vnorm)) + rs0 * NB, (short)0, n * NB, 0x00020000);
       auto kload = [&](int base, KBuf &bf) {
 #pragma unroll
         for (int u = 0; u < KTPW; ++u) {
+          if constexpr (!SPANS) {
+            // lane part of the offsets fixed, the round's tile in the scalar offset
+            const uint32_t t16 = (uint32_t)__builtin_amdgcn_readfirstlane(base * 16);  // uniform
+            bf.tc[u] = t16 + (uint32_t)(u * 16 + tn);
+            const uint32_t tl = (uint32_t)(u * 16 + tn);
+            if constexpr (NPL == 4) {
+              const auto w4 = __builtin_amdgcn_raw_buffer_load_b128(rkb, tl * RB + kgo, t16 * RB, 0);
+              bf.pl[u][0] = w4[0]; bf.pl[u][1] = w4[1]; bf.pl[u][2] = w4[2]; bf.pl[u][3] = w4[3];
+            } else {
+#pragma unroll
+              for (int p = 0; p < NPL; ++p)
+                bf.pl[u][p] = __builtin_amdgcn_raw_buffer_load_b32(rkb, tl * RB + kgo + 4 * p, t16 * RB, 0);
+            }
+            if constexpr (NF16) {
+              if constexpr (QJL) {
+                const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, t16 * 4u, 0);
+                bf.kn[u] = make_float2(__half2float(__ushort_as_half((unsigned short)(h2 & 0xFFFFu))),
+                                       __half2float(__ushort_as_half((unsigned short)(h2 >> 16))));
+              } else {
+                bf.kn[u] = make_float2(
+                    __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rkn, tl * 2u, t16 * 2u, 0))), 0.f);
+              }
+              bf.vn[u] = __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rvn, tl * 2u, t16 * 2u, 0)));
+            } else {
+              if constexpr (QJL) {
+                const auto k2 = __builtin_amdgcn_raw_buffer_load_b64(rkn, tl * 8u, t16 * 8u, 0);
+                bf.kn[u] = make_float2(__uint_as_float(k2[0]), __uint_as_float(k2[1]));
+              } else {
+                bf.kn[u] = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, t16 * 4u, 0)), 0.f);
+              }
+              bf.vn[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvn, tl * 4u, t16 * 4u, 0));
+            }
+            continue;
+          }
           const uint32_t tc = (uint32_t)min((base + u) * 16 + tn, n - 1);
           bf.tc[u] = tc;
           // a tile lies in one span
           const int64_t rr = SPANS ? pick_span(min((base + u) * 16, n - 1) >> slg, rs0, rs1, rs2, rs3) : rs0;
           const char *kb0 = reinterpret_cast<const char *>(a.kbits + rr * DW * NPL);
-          constexpr int NB = NF16 ? 2 : 4;  // bytes per norm
           const char *kn0 = reinterpret_cast<const char *>(a.knorm) + (1 + KQ) * rr * NB;
           const char *vn0 = reinterpret_cast<const char *>(a.vnorm) + rr * NB;
           const uint32_t tl = SPANS ? tc & smask : tc;  // position in the span
@@ -1823,8 +1876,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         }
       };
       // two buffers in turn: the next round's loads are in flight during this one.
-      // The loads are unconditional (tiles past the end re-read token n-1) and pinned
-      // ahead of the compute, so their latency overlaps a whole round.
+      // The loads are unconditional (tiles past the end read zeros, or re-read token
+      // n-1 with spans) and pinned ahead of the compute, so their latency overlaps a
+      // whole round.
       constexpr int KSTEP = 4 * KTPW;
       int kbase = wave * KTPW;
       while (kbase < ntile) {
