@@ -1949,13 +1949,22 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       const int nit = (n + 63) >> 6;
       const int nw = wave < nh ? vis(wave) : 0;  // tokens this head sees (all n without the causal mask)
       for (int i0 = 0; i0 < nit; i0 += 4) {
+        // the round's LDS reads first, then branch-free arithmetic (dead tokens'
+        // values are computed and discarded by the selects)
+        float lv[4], nv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lv[j] = lgw[64 * (i0 + j)];
+          nv[j] = vnw[64 * (i0 + j)];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = i0 + j;
           const bool live = lane + 64 * i < nw;
-          const float e = __builtin_amdgcn_exp2f(lgw[64 * i] - m);  // <= 1; tiny values round to W = 0
+          const float e = __builtin_amdgcn_exp2f(lv[j] - m);  // <= 1; tiny values round to W = 0
           l += live ? e : 0.f;
-          const int W = live ? (int)rintf(e * vnw[64 * i] * wq) : 0;
+          const int Wl = (int)rintf(e * nv[j] * wq);
+          const int W = live ? Wl : 0;
           const uint32_t x = ((uint32_t)W + 0x80808080u) ^ 0x80808080u;  // four signed base-256 digits
           int8_t *dst = av + lbase + ((i0 >> 1) << 11) + ((j >> 1) << 11) + ((j & 1) << 9);
           dst[0] = (int8_t)x;
