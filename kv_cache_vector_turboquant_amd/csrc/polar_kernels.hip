@@ -212,33 +212,38 @@ struct PolarLogitArgs {
   const DeviceTables *tables;
 };
 
-// what the tree evaluation reads: the 4 heads' rotated query per coordinate,
-// the (cos, sin) tables per level and this thread's record (all in LDS)
-struct PolarTree {
-  const float4 *q;
-  const float2 (*tab)[16];
-  const uint32_t *rec;
-  int b1, b2, hi0;  // hi0: first bit of the higher-level stream
-  __device__ __forceinline__ uint32_t code(int pos, int nb) const {
-    const int j = pos >> 5, sh = pos & 31;
-    uint32_t v = rec[j] >> sh;
-    if (sh + nb > 32) v |= rec[j + 1] << (32 - sh);
-    return v & ((1u << nb) - 1u);
-  }
-};
-
 __device__ __forceinline__ float4 fma4(float a, const float4 &x, float b, const float4 &y) {
   return make_float4(fmaf(a, x.x, b * y.x), fmaf(a, x.y, b * y.y), fmaf(a, x.z, b * y.z), fmaf(a, x.w, b * y.w));
 }
 
+// One thread per cached token: <q, u_hat> for the 4 heads of a head group. B1,
+// B2: bits of the level-1 and higher angle codes, so that every code's bit
+// position in the record is a constant (one bit-field extract from the record
+// words held in registers). The block's 256 tokens share the queries, so the
+// value of every leaf (coordinate pair l, level-1 code c):
+// cos c * q[2l] + sin c * q[2l+1], is tabulated once per block in LDS.
+template <int B1, int B2>
 __global__ void __launch_bounds__(256) polar_logits_kernel(PolarLogitArgs a) {
-  __shared__ float4 qs[PD];             // coordinate -> the 4 heads
+  constexpr int W1 = (B1 * (PD / 2) + 31) / 32, W2 = (B2 * (PD / 2 - 1) + 31) / 32, W = W1 + W2;
+  constexpr int NC1 = 1 << B1, HI0 = W1 * 32;
+  __shared__ float4 lt[PD / 2][NC1];    // leaf values of the 4 heads per (pair, level-1 code)
   __shared__ float2 tab[PL + 1][16];    // (cos, sin) of each level's centroids
-  __shared__ uint32_t rw[256][17];      // each thread's record
+  __shared__ float4 qs[PD];             // coordinate -> the 4 heads
   const int tid = threadIdx.x;
   const int sg = blockIdx.y, hg = sg % a.hgroups, stream = sg / a.hgroups;
   const int b = stream / a.kv_heads, kvh = stream - b * a.kv_heads;
   const int nh = min(4, a.group - hg * 4);
+  const int len = a.seq_len[b];
+  if ((int)blockIdx.x * 256 >= len) return;  // the whole block (before any barrier)
+  const int t = blockIdx.x * 256 + tid;
+  const bool live = t < len;
+  // this thread's record (a dead thread re-reads the last one)
+  uint32_t rec[W];
+  {
+    const uint32_t *src = a.bits + ((int64_t)stream * a.capacity + min(t, len - 1)) * W;
+#pragma unroll
+    for (int k = 0; k < W; ++k) rec[k] = src[k];
+  }
   for (int e = tid; e < 4 * PD; e += 256) {
     const int h = e >> 7, j = e & (PD - 1);
     reinterpret_cast<float *>(qs)[j * 4 + h] =
@@ -246,56 +251,51 @@ __global__ void __launch_bounds__(256) polar_logits_kernel(PolarLogitArgs a) {
   }
   if (tid < (PL + 1) * 16) {
     const int lv = tid >> 4, i = tid & 15;
-    const int bb = lv == 1 ? a.b1 : a.b2;
+    const int bb = lv == 1 ? B1 : B2;
     tab[lv][i] = lv >= 1 ? make_float2(a.tables->pcos[lv][bb][i], a.tables->psin[lv][bb][i]) : make_float2(0.f, 0.f);
   }
-  const int len = a.seq_len[b];
-  const int t = blockIdx.x * 256 + tid;
-  const bool live = t < len;
-  const int W = a.w1 + a.w2;
-  if (live) {
-    const uint32_t *src = a.bits + ((int64_t)stream * a.capacity + t) * W;
-    for (int k = 0; k < W; ++k) rw[tid][k] = src[k];
+  __syncthreads();
+  for (int e = tid; e < (PD / 2) * NC1; e += 256) {
+    const int l = e >> B1, c = e & (NC1 - 1);
+    const float2 cs = tab[1][c];
+    lt[l][c] = fma4(cs.x, qs[2 * l], cs.y, qs[2 * l + 1]);
   }
   __syncthreads();
-  if (!live) return;  // past the barrier
-  PolarTree tr;
-  tr.q = qs;
-  tr.tab = tab;
-  tr.rec = rw[tid];
-  tr.b1 = a.b1;
-  tr.b2 = a.b2;
-  tr.hi0 = a.w1 * 32;
-  // <q, u_hat> for the 4 heads. The tree's dot product is linear in each
-  // subtree: <q, u_hat> = sum over the 8 level-4 nodes of (the cos / sin
-  // product along its 3 ancestors) x (its subtree's value). A subtree's value:
-  // a leaf (coordinate pair) gives cos * q[2i] + sin * q[2i+1] of its angle, a
-  // node cos * left + sin * right of its own angle.
-  auto leaf = [&](int l) {
-    const float2 cs = tr.tab[1][tr.code(l * tr.b1, tr.b1)];
-    return fma4(cs.x, tr.q[2 * l], cs.y, tr.q[2 * l + 1]);
+  if (!live) return;  // past the barriers
+  // code of nb bits at bit pos of the record (pos, nb constant after unrolling)
+  auto code = [&](int pos, int nb) -> uint32_t {
+    const int j = pos >> 5, sh = pos & 31;
+    uint32_t v = rec[j] >> sh;
+    if (sh + nb > 32) v |= rec[j + 1] << (32 - sh);
+    return v & ((1u << nb) - 1u);
   };
+  // node i of level lv (2..7): its angle's (cos, sin)
+  auto ang = [&](int lv, int i) { return tab[lv][code(HI0 + (64 - (128 >> (lv - 1)) + i) * B2, B2)]; };
   auto node = [&](int lv, int i, const float4 &L, const float4 &R) {
-    const float2 cs = tr.tab[lv][tr.code(tr.hi0 + (64 - (128 >> (lv - 1)) + i) * tr.b2, tr.b2)];
+    const float2 cs = ang(lv, i);
     return fma4(cs.x, L, cs.y, R);
   };
+  auto leaf = [&](int l) { return lt[l][code(l * B1, B1)]; };
+  // The tree's dot product is linear in each subtree: <q, u_hat> = sum over the
+  // 8 level-4 nodes of (the cos / sin product along its 3 ancestors) x (its
+  // subtree's value); a node's value is cos * left + sin * right of its angle.
   float4 T = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
   for (int n4 = 0; n4 < 8; ++n4) {
     float P = 1.f;
 #pragma unroll
     for (int lv = 5; lv <= PL; ++lv) {
-      const float2 cs = tr.tab[lv][tr.code(tr.hi0 + (64 - (128 >> (lv - 1)) + (n4 >> (lv - 4))) * tr.b2, tr.b2)];
+      const float2 cs = ang(lv, n4 >> (lv - 4));
       P *= ((n4 >> (lv - 5)) & 1) ? cs.y : cs.x;
     }
     const int l0 = 8 * n4;
-    const float4 a2 = node(2, 4 * n4, leaf(l0), leaf(l0 + 1));
-    const float4 b2 = node(2, 4 * n4 + 1, leaf(l0 + 2), leaf(l0 + 3));
-    const float4 a3 = node(3, 2 * n4, a2, b2);
-    const float4 c2 = node(2, 4 * n4 + 2, leaf(l0 + 4), leaf(l0 + 5));
-    const float4 d2 = node(2, 4 * n4 + 3, leaf(l0 + 6), leaf(l0 + 7));
-    const float4 b3 = node(3, 2 * n4 + 1, c2, d2);
-    const float4 t4 = node(4, n4, a3, b3);
-    T = fma4(1.f, T, P, t4);
+    const float4 a3 = node(3, 2 * n4, node(2, 4 * n4, leaf(l0), leaf(l0 + 1)), node(2, 4 * n4 + 1, leaf(l0 + 2), leaf(l0 + 3)));
+    const float4 b3 = node(3, 2 * n4 + 1, node(2, 4 * n4 + 2, leaf(l0 + 4), leaf(l0 + 5)),
+                           node(2, 4 * n4 + 3, leaf(l0 + 6), leaf(l0 + 7)));
+    T = fma4(1.f, T, P, node(4, n4, a3, b3));
+    // one subtree at a time: T is final here and no LDS read moves across (an
+    // empty asm statement, no instruction), so the live set stays one subtree's
+    asm volatile("" : "+v"(T.x), "+v"(T.y), "+v"(T.z), "+v"(T.w) : : "memory");
   }
   // s = ||x|| <q, u_hat>, in log2 units of the softmax
   const float R = a.norms[(int64_t)stream * a.capacity + t] * a.scale_log2;
@@ -349,7 +349,14 @@ hipError_t launch_polar_attention(const tq_ctx *ctx, const tq_polar_packed *keys
   a.tables = ctx->d_tables;
   const dim3 grid((unsigned)((maxlen + 255) / 256), (unsigned)(values->batch * values->kv_heads * hgroups));
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;  // timing: the scoring kernel
-  hipLaunchKernelGGL(polar_logits_kernel, grid, dim3(256), 0, st, a);
+#define TQ_PL(B1_, B2_) \
+  case B1_ * 8 + B2_: hipLaunchKernelGGL((polar_logits_kernel<B1_, B2_>), grid, dim3(256), 0, st, a); break;
+  switch (keys->b1 * 8 + keys->b2) {
+    TQ_PL(1, 1) TQ_PL(1, 2) TQ_PL(1, 3) TQ_PL(1, 4) TQ_PL(2, 1) TQ_PL(2, 2) TQ_PL(2, 3) TQ_PL(2, 4)
+    TQ_PL(3, 1) TQ_PL(3, 2) TQ_PL(3, 3) TQ_PL(3, 4) TQ_PL(4, 1) TQ_PL(4, 2) TQ_PL(4, 3) TQ_PL(4, 4)
+    default: return hipErrorInvalidValue;
+  }
+#undef TQ_PL
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   return launch_decode(ctx, values, nullptr, 0, q_heads, scale, out, ws, st, nullptr, nullptr, nullptr, nullptr, 1, 0,
