@@ -583,9 +583,12 @@ def run_polar(args, torch, tq, synth):
     kern_ms = float(np.mean([ms(k) for k in kev]))
     call_ms = float(np.mean([ms(c) for c in cev]))
     keys = B * H * L * NS
-    # the scoring kernel's arithmetic: per (token, query head) one multiply and one
-    # fma (3 flops) for each of the 127 tree nodes, and the radius scale
-    flops_per = 3 * 127 + 1
+    # the scoring kernel's arithmetic per (token, query head), in its evaluation
+    # order: a multiply and an fma (3 flops) at each of the 63 internal tree nodes;
+    # the 64 leaves come from a per-block table (64 pairs x 16 level-1 codes x 3
+    # flops per 256 tokens: 12); per level-4 subtree the ancestors' product (3
+    # multiplies shared by the 4 heads) and an fma into the sum (2); the radius scale
+    flops_per = 3 * 63 + 12 + (8 * 3) // 4 + 8 * 2 + 1
     tflops = B * Hq * L * flops_per / (kern_ms / 1e3) / 1e12
     rec = 60 + VAL_B3
     res = {
