@@ -294,6 +294,21 @@ def test_decode_gqa_ragged(c128, kbits, vbits):
     _run_decode_case(ctx, Pi, S, K, V, Q, [2000, 0, 777], kbits, vbits, cap)
 
 
+@pytest.mark.parametrize("kbits", [3, 1])
+def test_decode_full_cache_partial_chunk(c128, kbits):
+    """The last sequence fills its cache (capacity 1056 = a 1024-token chunk + 32):
+    the key loads of its last chunk (range-checked over the chunk's records) sit at
+    the very end of the key, norm and value arrays; the other sequence ends at 1000
+    tokens. b = kbits + 1 keys (records of 4 and 2 words per 32 coordinates), 3-bit
+    values."""
+    ctx, Pi, S = c128
+    cap = 1056
+    K = synth.outlier_kv(8, (kbits, 1), synth.TAG_SCALES_K, (2, 2, cap, 128))
+    V = synth.outlier_kv(8, (kbits, 2), synth.TAG_SCALES_V, (2, 2, cap, 128))
+    Q = synth.outlier_kv(8, (kbits, 3), synth.TAG_SCALES_K, (2, 8, 128))
+    _run_decode_case(ctx, Pi, S, K, V, Q, [1000, cap], kbits, 3, cap)
+
+
 @pytest.mark.parametrize("hq,qdtype", [(2, "f32"), (4, "bf16"), (16, "f32"), (32, "bf16")])
 def test_decode_group_sizes_gaussian(c128, hq, qdtype):
     """Gaussian K/V; 2 KV heads with query groups of 1, 2, 8 and 16 heads."""
