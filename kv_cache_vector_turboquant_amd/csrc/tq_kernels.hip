@@ -1695,16 +1695,28 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       const float *vnx = reinterpret_cast<const float *>(a.vnorm) + rs0;
       const int vis0 = vis(0), vis1 = vis(1), vis2 = vis(2), vis3 = vis(3);
       float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      for (int tc = tid; tc < n; tc += 256) {
-        const float vv = vnx[tc];
-        vnl[tc] = vv;
-        vmx = fmaxf(vmx, vv);
-        const int vh[4] = {vis0, vis1, vis2, vis3};
+      // a thread's tokens tid + 256 k (k < 4: n <= chunk <= 1024): every load first
+      const int vh[4] = {vis0, vis1, vis2, vis3};
+      float vv[4], xl[4][4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float x = (h < nh && tc < vh[h]) ? lgx[(int64_t)h * a.ext_stride + tc] : -INFINITY;
-          lg[h * a.chunk + tc] = x;
-          m4[h] = fmaxf(m4[h], x);
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int tc = tid + 256 * k4;
+        vv[k4] = tc < n ? vnx[tc] : 0.f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          xl[k4][h] = (h < nh && tc < vh[h]) ? lgx[(int64_t)h * a.ext_stride + tc] : -INFINITY;
+      }
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int tc = tid + 256 * k4;
+        if (tc < n) {
+          vnl[tc] = vv[k4];
+          vmx = fmaxf(vmx, vv[k4]);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            lg[h * a.chunk + tc] = xl[k4][h];
+            m4[h] = fmaxf(m4[h], xl[k4][h]);
+          }
         }
       }
 #pragma unroll
