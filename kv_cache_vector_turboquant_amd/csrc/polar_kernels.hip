@@ -306,6 +306,39 @@ __global__ void __launch_bounds__(256) polar_logits_kernel(PolarLogitArgs a) {
     if (h < nh) o[(int64_t)h * a.stride] = R * v[h];
 }
 
+// q_rot = Pi q for the decode queries: a block of 256 threads takes 8 query
+// rows; thread (coordinate j, half h) forms output j of rows 4h .. 4h + 3 from
+// the columns of Pi^T (coalesced over j) against the rows staged in LDS.
+__global__ void __launch_bounds__(256) polar_qrot_kernel(const void *q, int is_bf16, int64_t nq, const float *rot_t,
+                                                         float *out) {
+  __shared__ float qs[8][PD];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 8;
+  for (int e = tid; e < 8 * PD; e += 256) {
+    const int64_t r = r0 + (e >> 7);
+    const int64_t i = r * PD + (e & (PD - 1));
+    float x = 0.f;
+    if (r < nq)
+      x = is_bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(q)[i] << 16)
+                  : reinterpret_cast<const float *>(q)[i];
+    qs[e >> 7][e & (PD - 1)] = x;
+  }
+  __syncthreads();
+  const int j = tid & (PD - 1), h = tid >> 7;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+  for (int kk = 0; kk < PD; ++kk) {
+    const float r = rot_t[kk * PD + j];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = fmaf(r, qs[4 * h + u][kk], acc[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = r0 + 4 * h + u;
+    if (row < nq) out[row * PD + j] = acc[u];
+  }
+}
+
 size_t polar_attention_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *values, int32_t q_heads) {
   const int group = q_heads / values->kv_heads, hgroups = (group + 3) / 4;
   const int maxlen = values->host_max_len > 0 ? values->host_max_len : values->capacity;
@@ -327,7 +360,9 @@ hipError_t launch_polar_attention(const tq_ctx *ctx, const tq_polar_packed *keys
   p += ((size_t)values->batch * q_heads * PD * sizeof(float) + 255) & ~(size_t)255;
   float *lg = (float *)p;
   const int64_t nqr = (int64_t)values->batch * q_heads;
-  hipError_t e = launch_gemm_store(q, is_bf16, PD, nqr, ctx->d_rot, PD, PD, PD, qrot, PD, st);  // Pi q
+  hipLaunchKernelGGL(polar_qrot_kernel, dim3((unsigned)((nqr + 7) / 8)), dim3(256), 0, st, q, is_bf16, nqr,
+                     ctx->d_rot_t, qrot);  // Pi q
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PolarLogitArgs a = {};
   a.bits = keys->bits;
