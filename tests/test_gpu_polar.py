@@ -199,6 +199,48 @@ def test_polar_attention_decode(ctx_pi, hq):
             assert np.max(np.abs(out[b, h * g:(h + 1) * g] - ref)) <= 2e-3, f"b={b} h={h}"
 
 
+@pytest.mark.parametrize("b1,b2,qdtype", [(2, 2, "f32"), (3, 1, "bf16"), (1, 4, "f32"), (4, 4, "bf16")])
+def test_polar_attention_decode_code_widths(ctx_pi, b1, b2, qdtype):
+    """Decode attention over PolarQuant keys of other code widths (the scoring
+    kernel is compiled per width pair) and fp32 or bf16 queries: batch 2
+    (lengths 700, 333), 2 KV heads, groups of 4, within 2e-3 max-abs of the oracle."""
+    ctx, Pi = ctx_pi
+    B, H, cap, L, d, hq = 2, 2, 704, 700, 128, 8
+    seq = [700, 333]
+    pcb = PQ.polar_codebooks(128, b1, b2)
+    cbv = T.codebook(d, 3)
+    K = synth.outlier_kv(76, (b1, b2, 1), synth.TAG_SCALES_K, (B, H, L, d))
+    V = synth.outlier_kv(76, (b1, b2, 2), synth.TAG_SCALES_V, (B, H, L, d))
+    Q = synth.gaussian(76, (b1, b2, 3), (B, hq, d), qdtype)
+    cache = tq.PolarKVCache(B, H, cap, b1=b1, b2=b2)
+    recs = {}
+    for b in range(B):
+        for h in range(H):
+            s = b * H + h
+            kr = PQ.pack_polar(PQ.polar_encode(K[b, h], Pi, pcb), pcb)
+            vr = T.pack_values(T.encode(V[b, h], Pi, cbv), 3)
+            cache.keys.words[s * cap:s * cap + L].copy_(torch.from_numpy(kr["bits"].view(np.int32)).to(DEV))
+            cache.keys.norms[s * cap:s * cap + L].copy_(torch.from_numpy(kr["norms"]).to(DEV))
+            nb = vr["bits"].shape[0]
+            cache.values.v.words[s * cap // 32:s * cap // 32 + nb].copy_(torch.from_numpy(vr["bits"].view(np.int32)).to(DEV))
+            cache.values.v.norms[s * cap:s * cap + L].copy_(torch.from_numpy(vr["norms"]).to(DEV))
+            recs[s] = (kr, vr)
+    cache.seq_len.copy_(torch.tensor(seq, dtype=torch.int32))
+    cache.host_max_len = max(seq)
+    scale = 1 / math.sqrt(d)
+    out = cache.decode(ctx, _dev(Q, qdtype), scale).cpu().numpy()
+    g = hq // H
+    for b in range(B):
+        for h in range(H):
+            kr, vr = recs[b * H + h]
+            n = seq[b]
+            ref = PQ.polar_attention_decode(Q[b, h * g:(h + 1) * g], Pi, pcb, cbv,
+                                            {"bits": kr["bits"][:n], "norms": kr["norms"][:n]},
+                                            {"bits": vr["bits"], "norms": vr["norms"][:n]}, n, scale,
+                                            T.unpack_values)
+            assert np.max(np.abs(out[b, h * g:(h + 1) * g] - ref)) <= 2e-3, f"b={b} h={h}"
+
+
 def test_polar_cache_prefill_and_decode(ctx_pi):
     """PolarKVCache.prefill encodes keys on the GPU (stream-strided records) and
     values with the fused quantize; decode over them matches the oracle over the
