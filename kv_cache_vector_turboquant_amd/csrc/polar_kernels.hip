@@ -13,7 +13,7 @@
 // codes (b2 bits each; level 2 nodes first, each level in node order) in w2
 // words; the radius ||x|| as fp32 in a separate array.
 //
-//  polar_encode_kernel   one wave per vector: lane l owns coordinate pair l;
+//  polar_encode_kernel   a wave per vector (grid-strided): lane l owns pair l;
 //                        the radii of level l >= 2 combine lanes l and
 //                        l + 2^(l-2) (a shuffle; owners are the multiples of
 //                        2^(l-1)), then the 63 higher angles are taken one per
@@ -24,6 +24,8 @@
 //                        then splits the result by its pair's angle: y_hat rows
 //                        for the fp32 scores GEMM.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "tq_internal.h"
 
@@ -66,13 +68,22 @@ __device__ __forceinline__ uint32_t assemble_word(const uint8_t *codes, int coun
   return w;
 }
 
+// LDS ordering among the lanes of one wave (its LDS operations run in order):
+// a compiler barrier plus a wave-scope fence
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Each wave encodes vectors v = wave id, + total waves, ... (a grid-strided loop:
+// one short wave per vector spent its time being dispatched).
 __global__ void __launch_bounds__(256) polar_encode_kernel(PolarArgs a) {
   __shared__ uint8_t codes[4][128];  // per wave: [0, 64) level 1, [64, 127) higher levels
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t v = (int64_t)blockIdx.x * 4 + w;
-  const bool live = v < a.n;  // uniform per wave
-  float r = 0.f;
-  if (live) {
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int W = a.w1 + a.w2;
+  for (int64_t v = (int64_t)blockIdx.x * 4 + w; v < a.n; v += nwaves) {  // uniform per wave
     const float2 p = reinterpret_cast<const float2 *>(a.y + v * PD)[lane];
     codes[w][lane] = (uint8_t)angle_code(atan2f(p.y, p.x), a.tables->pbound[1][a.b1]);
     // radii of every level first (a shuffle and a hypot per level): rl[k] is the
@@ -84,7 +95,7 @@ __global__ void __launch_bounds__(256) polar_encode_kernel(PolarArgs a) {
       const float rr = __shfl_down(rl[k - 1], 1 << (k - 1));  // the right child's radius
       rl[k] = sqrtf(fmaf(rl[k - 1], rl[k - 1], rr * rr));
     }
-    r = rl[PL - 1];  // lane 0: the root, ||y|| = ||x||
+    const float r = rl[PL - 1];  // lane 0: the root, ||y|| = ||x||
     // then the 63 higher angles at once, one per lane: lane j < 63 takes code j of
     // the higher stream, node i of level lv, whose children are the level-(lv-1)
     // nodes 2i and 2i + 1, owned by lanes 2i * 2^(lv-2) and (2i + 1) * 2^(lv-2)
@@ -99,10 +110,7 @@ __global__ void __launch_bounds__(256) polar_encode_kernel(PolarArgs a) {
       right = k == sh ? r_ : right;
     }
     if (j < 63) codes[w][64 + j] = (uint8_t)angle_code(atan2f(right, left), a.tables->pbound[lv][a.b2]);
-  }
-  __syncthreads();
-  if (live) {
-    const int W = a.w1 + a.w2;
+    wave_lds_sync();  // this wave's codes written
     const int64_t st = v / a.n_tokens, rec = st * a.os + a.rec0 + (v - st * a.n_tokens);
     if (lane < W) {
       const uint32_t word = lane < a.w1 ? assemble_word(codes[w], 64, a.b1, lane)
@@ -110,6 +118,7 @@ __global__ void __launch_bounds__(256) polar_encode_kernel(PolarArgs a) {
       a.bits[rec * W + lane] = word;
     }
     if (lane == 0) a.norms[rec] = r;  // lane 0 owns the root: ||y|| = ||x||
+    wave_lds_sync();  // read back before the next vector's codes
   }
 }
 
@@ -169,7 +178,9 @@ hipError_t launch_polar_quantize(const tq_ctx *ctx, const void *x, int is_bf16, 
   a.rec0 = out_offset;
   a.n_tokens = n_tokens;
   a.os = out_stream_stride;
-  hipLaunchKernelGGL(polar_encode_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, a);
+  // enough waves to fill the GPU several times over; each loops over its vectors
+  const int64_t blocks = std::min<int64_t>((n + 3) / 4, 8192);
+  if (blocks > 0) hipLaunchKernelGGL(polar_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
