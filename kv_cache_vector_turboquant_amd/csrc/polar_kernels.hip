@@ -80,9 +80,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 // one short wave per vector spent its time being dispatched).
 __global__ void __launch_bounds__(256) polar_encode_kernel(PolarArgs a) {
   __shared__ uint8_t codes[4][128];  // per wave: [0, 64) level 1, [64, 127) higher levels
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ float hb[PL + 1][16];   // the higher levels' boundaries (a lane's level varies with the lane)
+  // w read through readfirstlane: v, and the record index divided out of it,
+  // are wave-uniform (scalar arithmetic, not a per-lane 64-bit division)
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int W = a.w1 + a.w2;
+  if (threadIdx.x < (PL + 1) * 16) {
+    const int lv = threadIdx.x >> 4, i = threadIdx.x & 15;
+    hb[lv][i] = lv >= 2 ? a.tables->pbound[lv][a.b2][i] : INFINITY;
+  }
+  __syncthreads();  // once, before the loop (every thread reaches it)
+  const int nb2 = (1 << a.b2) - 1;  // boundaries of a higher-level code
   for (int64_t v = (int64_t)blockIdx.x * 4 + w; v < a.n; v += nwaves) {  // uniform per wave
     const float2 p = reinterpret_cast<const float2 *>(a.y + v * PD)[lane];
     codes[w][lane] = (uint8_t)angle_code(atan2f(p.y, p.x), a.tables->pbound[1][a.b1]);
@@ -109,7 +118,12 @@ __global__ void __launch_bounds__(256) polar_encode_kernel(PolarArgs a) {
       left = k == sh ? l_ : left;
       right = k == sh ? r_ : right;
     }
-    if (j < 63) codes[w][64 + j] = (uint8_t)angle_code(atan2f(right, left), a.tables->pbound[lv][a.b2]);
+    if (j < 63) {
+      const float psi = atan2f(right, left);
+      uint32_t c = 0;
+      for (int q = 0; q < nb2; ++q) c += psi >= hb[lv][q] ? 1u : 0u;
+      codes[w][64 + j] = (uint8_t)c;
+    }
     wave_lds_sync();  // this wave's codes written
     const int64_t st = v / a.n_tokens, rec = st * a.os + a.rec0 + (v - st * a.n_tokens);
     if (lane < W) {
