@@ -1738,7 +1738,11 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       };
       // contiguous records: range-checked buffer loads over the chunk's n records
       // (a load past them returns zeros: those tokens' logits are masked and
-      // their value norms 0), so no clamping and constant offsets per tile
+      // their value norms 0), so no clamping and constant offsets per tile. The
+      // loads are non-temporal (aux 2: the nt policy): the key records stream
+      // through once (measured 0.58 -> 0.63 of HBM peak on the serving step;
+      // the value blocks read the same way measured slower, so they keep the
+      // default policy)
       constexpr int NB = NF16 ? 2 : 4;  // bytes per norm
       constexpr int RB = DW * NPL * 4;  // bytes per key record
       const __amdgpu_buffer_rsrc_t rkb = __builtin_amdgcn_make_buffer_rsrc(
@@ -1757,31 +1761,31 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
             bf.tc[u] = t16 + (uint32_t)(u * 16 + tn);
             const uint32_t tl = (uint32_t)(u * 16 + tn);
             if constexpr (NPL == 4) {
-              const auto w4 = __builtin_amdgcn_raw_buffer_load_b128(rkb, tl * RB + kgo, t16 * RB, 0);
+              const auto w4 = __builtin_amdgcn_raw_buffer_load_b128(rkb, tl * RB + kgo, t16 * RB, 2);
               bf.pl[u][0] = w4[0]; bf.pl[u][1] = w4[1]; bf.pl[u][2] = w4[2]; bf.pl[u][3] = w4[3];
             } else {
 #pragma unroll
               for (int p = 0; p < NPL; ++p)
-                bf.pl[u][p] = __builtin_amdgcn_raw_buffer_load_b32(rkb, tl * RB + kgo + 4 * p, t16 * RB, 0);
+                bf.pl[u][p] = __builtin_amdgcn_raw_buffer_load_b32(rkb, tl * RB + kgo + 4 * p, t16 * RB, 2);
             }
             if constexpr (NF16) {
               if constexpr (QJL) {
-                const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, t16 * 4u, 0);
+                const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, t16 * 4u, 2);
                 bf.kn[u] = make_float2(__half2float(__ushort_as_half((unsigned short)(h2 & 0xFFFFu))),
                                        __half2float(__ushort_as_half((unsigned short)(h2 >> 16))));
               } else {
                 bf.kn[u] = make_float2(
-                    __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rkn, tl * 2u, t16 * 2u, 0))), 0.f);
+                    __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rkn, tl * 2u, t16 * 2u, 2))), 0.f);
               }
-              bf.vn[u] = __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rvn, tl * 2u, t16 * 2u, 0)));
+              bf.vn[u] = __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rvn, tl * 2u, t16 * 2u, 2)));
             } else {
               if constexpr (QJL) {
-                const auto k2 = __builtin_amdgcn_raw_buffer_load_b64(rkn, tl * 8u, t16 * 8u, 0);
+                const auto k2 = __builtin_amdgcn_raw_buffer_load_b64(rkn, tl * 8u, t16 * 8u, 2);
                 bf.kn[u] = make_float2(__uint_as_float(k2[0]), __uint_as_float(k2[1]));
               } else {
-                bf.kn[u] = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, t16 * 4u, 0)), 0.f);
+                bf.kn[u] = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, t16 * 4u, 2)), 0.f);
               }
-              bf.vn[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvn, tl * 4u, t16 * 4u, 0));
+              bf.vn[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvn, tl * 4u, t16 * 4u, 2));
             }
             continue;
           }
