@@ -1726,9 +1726,10 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     } else {
       // records of the chunk. Contiguous caches: buffer loads (below). Pages
       // smaller than the chunk: uniform bases (the tile's span) and unsigned 32-bit
-      // byte offsets per lane (base + zero-extended offset addressing); lanes past
-      // the end re-read token n-1. Either way every store below stays
-      // unconditional and harmless (tokens past n get -inf logits)
+      // byte offsets per lane (base + zero-extended offset addressing), key words
+      // loaded non-temporally; lanes past the end re-read token n-1. Either way
+      // every store below stays unconditional and harmless (tokens past n get -inf
+      // logits)
       const uint32_t kgo = (uint32_t)(G * NPL * 4);  // the lane's 32-coordinate group in a record
       struct KBuf {
         uint32_t pl[KTPW][NPL];
@@ -1799,11 +1800,12 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
           const uint32_t tl = SPANS ? tc & smask : tc;  // position in the span
           const char *src = kb0 + (tl * (uint32_t)(DW * NPL * 4) + kgo);
           if constexpr (NPL == 4) {
-            const uint4 w4 = *reinterpret_cast<const uint4 *>(src);
-            bf.pl[u][0] = w4.x; bf.pl[u][1] = w4.y; bf.pl[u][2] = w4.z; bf.pl[u][3] = w4.w;
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 w4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+            bf.pl[u][0] = w4[0]; bf.pl[u][1] = w4[1]; bf.pl[u][2] = w4[2]; bf.pl[u][3] = w4[3];
           } else {
 #pragma unroll
-            for (int p = 0; p < NPL; ++p) bf.pl[u][p] = reinterpret_cast<const uint32_t *>(src)[p];
+            for (int p = 0; p < NPL; ++p) bf.pl[u][p] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(src) + p);
           }
           if constexpr (NF16) {
             if constexpr (QJL) bf.kn[u] = __half22float2(*reinterpret_cast<const __half2 *>(kn0 + (tl << 2)));
