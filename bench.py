@@ -395,7 +395,8 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
                                 "step run right after the timed steps, same inputs and launch configuration"),
                      "read_ceiling_gbs": ceiling, "frac_of_read_ceiling": achieved / ceiling,
                      "read_ceiling": ("tq_read_probe: best of grids 4096/8192/16384 x 256 threads streaming 2 GiB "
-                                      "with 16-byte loads, timed live in this run")},
+                                      "(a contiguous slice per work-group, 16-byte non-temporal loads), "
+                                      "timed live in this run")},
     }
     if not args.no_cpu_baseline:
         enc_rate, dec_rate, streams, secs = oracle_stream_rates(d, min(L, 8192), Hq // H, kbits, vbits,

@@ -359,9 +359,11 @@ tq_status tq_time_next_decode(void *start_event, void *stop_event);
 /* Read-bandwidth probe, a measurement aid: the practical HBM read ceiling that
  * the decode kernel's roofline is read against. `grid` work-groups of 256
  * threads stream `bytes` bytes of d_src (device, 16-byte aligned, bytes a
- * multiple of 16) with 16-byte loads, four in flight per thread, and write one
- * XOR-fold word per thread to d_sink (device, grid * 256 uint32, so the loads
- * are not optimized away). Asynchronous on `stream`.
+ * multiple of 16), each work-group its own contiguous slice, with 16-byte
+ * non-temporal loads, four in flight per thread, and write one XOR-fold word
+ * per thread to d_sink (device, grid * 256 uint32, so the loads are not
+ * optimized away; the XOR of all folds is the XOR of all words read).
+ * Asynchronous on `stream`.
  * Errors: TQ_ERR_ARG (NULL, alignment, size, grid not in [1, 65536]), TQ_ERR_HIP. */
 tq_status tq_read_probe(const void *d_src, size_t bytes, int32_t grid, uint32_t *d_sink, void *stream);
 
