@@ -248,6 +248,25 @@ def kv_inputs(torch, synth, args, shape, tags, scale_tag):
     return synth.torch_gaussian(0, tags, shape, torch.bfloat16, "cuda")
 
 
+def decode_spans(B, H, Hq, cap, page_tokens):
+    """Whether the decode launch takes the kernel whose chunks span several pages.
+
+    The library picks the chunk per launch: 1024 tokens, halved (not below 256)
+    while the launch would have fewer than 2048 work-groups, then, for a paged
+    cache, halved until it and the page size divide one another; chunks longer
+    than a page span several pages. This only labels the bench line.
+    """
+    if not page_tokens:
+        return False
+    streams = B * H * ((Hq // H + 3) // 4)
+    chunk = 1024
+    while chunk > 256 and streams * ((cap + chunk - 1) // chunk) < 2048:
+        chunk >>= 1
+    while page_tokens % chunk and chunk % page_tokens:
+        chunk >>= 1
+    return chunk > page_tokens
+
+
 def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text):
     """Prefill quantize of B x H x L K/V, then NS x (append + decode)."""
     d, vbits = 128, 3
@@ -384,7 +403,10 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         "decode_call_ms": avg_ms, "wall_s_timed": wall, **extra_cold, **(graph or {}),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": f"decode_kernel<{kbits}, {vbits}, {str(kqjl).lower()}, spans> (score/attention over the packed cache; spans: chunks over several pages)",
+                     "kernel": (f"decode_kernel<{kbits}, {vbits}, {str(kqjl).lower()}, "
+                                f"{str(decode_spans(B, H, Hq, cap, args.page_tokens)).lower()}, {str(nf16).lower()}> "
+                                "(score/attention over the packed cache; template arguments: key MSE bits, value bits, "
+                                "QJL signs, chunks spanning several pages, fp16 norms)"),
                      "algorithmic_bytes_per_launch": float(dec_bytes.mean()), "avg_launch_ms": kern_avg_ms,
                      "bytes_per_kv_token": rec_bytes,
                      "call": ("tq_decode_step: decode_prep_kernel (query prep + append), decode_kernel, "
@@ -517,8 +539,9 @@ def run_prefill(args, torch, tq, synth):
         "attend_call_ms": call_ms.tolist(), "attend_kernel_ms": kern_ms.tolist(),
         "roofline": {"bound": "mfma", "achieved": float(tput[-1]), "peak": mix_peak, "unit": "TFLOP/s",
                      "frac": float(tput[-1]) / mix_peak, "traffic": None,
-                     "kernel": f"decode_kernel<{kbits}, {vbits}, {str(kqjl).lower()}, false> on the last chunk "
-                               f"({P} tokens visible to its last position)",
+                     "kernel": f"decode_kernel<{kbits}, {vbits}, {str(kqjl).lower()}, false, false> on the last chunk "
+                               f"({P} tokens visible to its last position; template arguments: key MSE bits, value "
+                               "bits, QJL signs, chunks spanning several pages, fp16 norms)",
                      "ops_per_vhead_token": k_ops + v_ops, "k_ops_per_vhead_token": k_ops,
                      "v_ops_per_vhead_token": v_ops, "avg_launch_ms": float(kern_ms[-1]),
                      "peak_note": ("executed exact-digit MFMA work (fp6 x fp4 score MFMAs, int8 value MFMAs) "
