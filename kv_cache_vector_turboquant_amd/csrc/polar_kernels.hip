@@ -258,7 +258,8 @@ __global__ void __launch_bounds__(256) polar_logits_kernel(PolarLogitArgs a) {
   const int sg = blockIdx.y, hg = sg % a.hgroups, stream = sg / a.hgroups;
   const int b = stream / a.kv_heads, kvh = stream - b * a.kv_heads;
   const int nh = min(4, a.group - hg * 4);
-  const int len = a.seq_len[b];
+  // a length past the logit rows (a caller error) is clamped: every write stays in its row
+  const int len = min(max(a.seq_len[b], 0), (int)min(a.stride, (int64_t)a.capacity));
   if ((int)blockIdx.x * 256 >= len) return;  // the whole block (before any barrier)
   const int t = blockIdx.x * 256 + tid;
   const bool live = t < len;

@@ -1148,7 +1148,7 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
     stream[s2] = 2 * blk + s2;
     const bool exists = stream[s2] < nstreams;
     pos[s2] = exists ? a.seq_len[stream[s2] / a.kv_heads] : a.capacity;
-    on[s2] = exists && pos[s2] < a.capacity;  // a full stream gets nothing appended
+    on[s2] = exists && pos[s2] >= 0 && pos[s2] < a.capacity;  // a full stream gets nothing appended
   }
   // thread (row r, quarter kq): 32 entries of row r of Pi (transposed: coalesced
   // over r) and of row r of S
@@ -1651,7 +1651,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int sg = stream * HG + hg;
   const int b = stream / a.kv_heads;
   const int nh = min(4, a.vgroup - hg * 4);
-  const int len = a.wlen ? a.wlen[b] : a.seq_len[b];
+  // a length outside [0, capacity] (a caller error) is clamped: no record outside the stream is read;
+  // EXT logits exist for the first ext_stride tokens only
+  const int len = min(max(a.wlen ? a.wlen[b] : a.seq_len[b], 0), EXT ? min(a.capacity, (int)a.ext_stride) : a.capacity);
   const int t0 = c * a.chunk;
   const int t1 = min(len, t0 + a.chunk);
   // visible tokens of virtual head hh (chunk-relative; causal: up to its position)
@@ -1737,59 +1739,68 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         float vn[KTPW];
         uint32_t tc[KTPW];
       };
-      // contiguous records: range-checked buffer loads over the chunk's n records
-      // (a load past them returns zeros: those tokens' logits are masked and
-      // their value norms 0), so no clamping and constant offsets per tile. The
+      // contiguous records: range-checked buffer loads. Each round builds its
+      // descriptors at the round's first token t16 with num_records covering
+      // only the chunk's records from there on (max(n - t16, 0)), so the whole
+      // offset of a load is its lane offset, which the hardware compares with
+      // num_records: a load past the chunk's n records returns zeros and
+      // touches no memory (those tokens' logits are masked and their value
+      // norms 0). The scalar offset is not range-checked, so it stays 0. The
+      // descriptors are scalar work; the lane offsets are loop-invariant. The
       // loads are non-temporal (aux 2: the nt policy): the key records stream
       // through once (measured 0.58 -> 0.63 of HBM peak on the serving step;
       // the value blocks read the same way measured slower, so they keep the
       // default policy)
       constexpr int NB = NF16 ? 2 : 4;  // bytes per norm
       constexpr int RB = DW * NPL * 4;  // bytes per key record
-      const __amdgpu_buffer_rsrc_t rkb = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint32_t *>(a.kbits) + rs0 * DW * NPL, (short)0, n * RB, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rkn = __builtin_amdgcn_make_buffer_rsrc(
-          reinterpret_cast<char *>(const_cast<void *>(a.knorm)) + (1 + KQ) * rs0 * NB, (short)0, n * (1 + KQ) * NB,
-          0x00020000);
-      const __amdgpu_buffer_rsrc_t rvn = __builtin_amdgcn_make_buffer_rsrc(
-          reinterpret_cast<char *>(const_cast<void *>(a.vnorm)) + rs0 * NB, (short)0, n * NB, 0x00020000);
       auto kload = [&](int base, KBuf &bf) {
+        if constexpr (!SPANS) {
+          const int t16 = __builtin_amdgcn_readfirstlane(base * 16);  // the round's first token (uniform)
+          const int rem = max(n - t16, 0);                             // the chunk's records from t16 on
+          const int64_t r0 = rs0 + t16;
+          const __amdgpu_buffer_rsrc_t rkb = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<uint32_t *>(a.kbits) + r0 * DW * NPL, (short)0, rem * RB, 0x00020000);
+          const __amdgpu_buffer_rsrc_t rkn = __builtin_amdgcn_make_buffer_rsrc(
+              reinterpret_cast<char *>(const_cast<void *>(a.knorm)) + (1 + KQ) * r0 * NB, (short)0,
+              rem * (1 + KQ) * NB, 0x00020000);
+          const __amdgpu_buffer_rsrc_t rvn = __builtin_amdgcn_make_buffer_rsrc(
+              reinterpret_cast<char *>(const_cast<void *>(a.vnorm)) + r0 * NB, (short)0, rem * NB, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < KTPW; ++u) {
-          if constexpr (!SPANS) {
-            // lane part of the offsets fixed, the round's tile in the scalar offset
-            const uint32_t t16 = (uint32_t)__builtin_amdgcn_readfirstlane(base * 16);  // uniform
-            bf.tc[u] = t16 + (uint32_t)(u * 16 + tn);
-            const uint32_t tl = (uint32_t)(u * 16 + tn);
+          for (int u = 0; u < KTPW; ++u) {
+            const uint32_t tl = (uint32_t)(u * 16 + tn);  // token of the lane, relative to t16
+            bf.tc[u] = (uint32_t)t16 + tl;
             if constexpr (NPL == 4) {
-              const auto w4 = __builtin_amdgcn_raw_buffer_load_b128(rkb, tl * RB + kgo, t16 * RB, 2);
+              const auto w4 = __builtin_amdgcn_raw_buffer_load_b128(rkb, tl * RB + kgo, 0, 2);
               bf.pl[u][0] = w4[0]; bf.pl[u][1] = w4[1]; bf.pl[u][2] = w4[2]; bf.pl[u][3] = w4[3];
             } else {
 #pragma unroll
               for (int p = 0; p < NPL; ++p)
-                bf.pl[u][p] = __builtin_amdgcn_raw_buffer_load_b32(rkb, tl * RB + kgo + 4 * p, t16 * RB, 2);
+                bf.pl[u][p] = __builtin_amdgcn_raw_buffer_load_b32(rkb, tl * RB + kgo + 4 * p, 0, 2);
             }
             if constexpr (NF16) {
               if constexpr (QJL) {
-                const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, t16 * 4u, 2);
+                const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, 0, 2);
                 bf.kn[u] = make_float2(__half2float(__ushort_as_half((unsigned short)(h2 & 0xFFFFu))),
                                        __half2float(__ushort_as_half((unsigned short)(h2 >> 16))));
               } else {
                 bf.kn[u] = make_float2(
-                    __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rkn, tl * 2u, t16 * 2u, 2))), 0.f);
+                    __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rkn, tl * 2u, 0, 2))), 0.f);
               }
-              bf.vn[u] = __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rvn, tl * 2u, t16 * 2u, 2)));
+              bf.vn[u] = __half2float(__ushort_as_half(__builtin_amdgcn_raw_buffer_load_b16(rvn, tl * 2u, 0, 2)));
             } else {
               if constexpr (QJL) {
-                const auto k2 = __builtin_amdgcn_raw_buffer_load_b64(rkn, tl * 8u, t16 * 8u, 2);
+                const auto k2 = __builtin_amdgcn_raw_buffer_load_b64(rkn, tl * 8u, 0, 2);
                 bf.kn[u] = make_float2(__uint_as_float(k2[0]), __uint_as_float(k2[1]));
               } else {
-                bf.kn[u] = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, t16 * 4u, 2)), 0.f);
+                bf.kn[u] = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, 0, 2)), 0.f);
               }
-              bf.vn[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvn, tl * 4u, t16 * 4u, 2));
+              bf.vn[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvn, tl * 4u, 0, 2));
             }
-            continue;
           }
+          return;
+        }
+#pragma unroll
+        for (int u = 0; u < KTPW; ++u) {
           const uint32_t tc = (uint32_t)min((base + u) * 16 + tn, n - 1);
           bf.tc[u] = tc;
           // a tile lies in one span
@@ -2313,7 +2324,7 @@ __global__ void __launch_bounds__(DD) append_kernel(AppendArgs a) {
   const int stream = blockIdx.x, j = threadIdx.x, lane = j & 63, wv = j >> 6;
   const int b = stream / a.kv_heads;
   const int t = a.seq_len[b];
-  if (t >= a.capacity) return;
+  if (t < 0 || t >= a.capacity) return;  // full stream (or an invalid length): nothing is written
   const int64_t rec = a.map.rec(stream, t);
   const int64_t off = (int64_t)stream * DD + j;
   const float x = a.bf16 ? bf16f(((const uint16_t *)a.k)[off]) : ((const float *)a.k)[off];

@@ -34,7 +34,7 @@ from scipy import special
 
 __all__ = [
     "rotation_from_gaussian", "sketch_from_gaussian", "coord_density", "coord_cdf",
-    "lloyd_max", "Codebook", "codebook", "encode", "Encoded", "query_prep", "qjl_constant",
+    "lloyd_max", "Codebook", "codebook", "encode", "qjl_stage", "Encoded", "query_prep", "qjl_constant",
     "scores", "scores_from_parts", "dequantize_keys", "attention_decode", "attention_prefill", "topk", "stored_norms",
     "recall_at_k", "pack_keys", "unpack_keys", "pack_values", "unpack_values",
     "key_record_bytes", "value_record_bytes",
@@ -217,6 +217,7 @@ class Encoded:
     rho: np.ndarray | None   # (n,) fp64 ||r|| (keys only)
     y: np.ndarray            # (n, d) fp64 rotated unit vector (for boundary distances)
     z: np.ndarray | None     # (n, m) fp64 sketch of the residual (for sign distances)
+    S: np.ndarray | None = None  # the sketch matrix used (keys), for re-deriving stage 2
 
 
 def encode(X: np.ndarray, Pi: np.ndarray, cb: Codebook | None, S: np.ndarray | None = None) -> Encoded:
@@ -248,13 +249,25 @@ def encode(X: np.ndarray, Pi: np.ndarray, cb: Codebook | None, S: np.ndarray | N
     idx[~nz] = 0
     sigma = rho = Z = None
     if S is not None:
-        R = Y - cb.centroids.astype(np.float64)[idx] if cb is not None else Y.copy()
-        R[~nz] = 0.0
-        rho = np.sqrt(np.sum(R * R, axis=1))
-        Z = R @ np.asarray(S, dtype=np.float64).T
-        sigma = Z >= 0.0
-        sigma[~nz] = False
-    return Encoded(idx, sigma, n, rho, Y, Z)
+        rho, Z, sigma = qjl_stage(Y, idx, cb, S, nz)
+    return Encoded(idx, sigma, n, rho, Y, Z, None if S is None else np.asarray(S))
+
+
+def qjl_stage(Y: np.ndarray, idx: np.ndarray, cb: Codebook | None, S: np.ndarray, live: np.ndarray):
+    """Stage 2 of the key encoder for given stage-1 codes [ebisuda, 第2段階;
+    hakusoku, QJL]: residual r = y - c[idx] in the rotated domain (pure QJL
+    keys, cb None: r = y), rho = ||r||, z = S r, sigma = [z >= 0]; rows with
+    live False (zero vectors) give r = 0, rho = 0 and sigma all False.
+    `encode` applies it to its own codes; the parity checks apply it to another
+    encoder's codes (a code decided on the other side of a boundary changes r)."""
+    Y = np.asarray(Y, dtype=np.float64)
+    R = Y - cb.centroids.astype(np.float64)[idx] if cb is not None else Y.copy()
+    R[~live] = 0.0
+    rho = np.sqrt(np.sum(R * R, axis=1))
+    Z = R @ np.asarray(S, dtype=np.float64).T
+    sigma = Z >= 0.0
+    sigma[~live] = False
+    return rho, Z, sigma
 
 
 # ---------------------------------------------------------------------------

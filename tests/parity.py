@@ -4,7 +4,9 @@ Packed codes and sign bits: bit-exact, except at most 1e-4 of coordinates
 whose oracle value lies within 1e-5 of a decision boundary (codes: the fp64
 rotated coordinate y against the stored boundaries; signs: the fp64 sketch
 value z against 0). A vector with an excused code flip has a different
-residual, so its sign bits and ||r|| are not compared (the cascade).
+residual (the cascade): its sign bits and ||r|| are compared against the
+oracle's stage 2 re-derived from the GPU's own codes (fp64 r = y - c[idx_gpu],
+z = S r), under the same band and norm tolerance.
 Scores: |ds| <= 1e-3 |s| or |ds| <= 1e-6 ||q|| ||x||. Attention: 2e-3 max-abs.
 """
 import numpy as np
@@ -57,18 +59,24 @@ def check_key_records(words, norms, enc, cb, bits, d, qjl=True, norm_f16=False):
     else:
         assert not g_idx.any()
         cascade = np.zeros(words.shape[0], dtype=bool)
-    live = ~cascade
     nsflip = 0
     if qjl:
-        sflip = (g_sig != enc.sigma) & live[:, None]
+        # the oracle's stage 2; for cascade vectors, re-derived from the GPU's codes
+        ref_sig, ref_z, ref_rho = enc.sigma.copy(), enc.z.copy(), enc.rho.copy()
+        if cascade.any():
+            assert enc.S is not None, "cascade vectors need the sketch matrix (encode with S)"
+            rows = np.nonzero(cascade)[0]
+            rho_c, z_c, sig_c = T.qjl_stage(enc.y[rows], g_idx[rows], cb, enc.S, enc.norm[rows] > 0)
+            ref_sig[rows], ref_z[rows], ref_rho[rows] = sig_c, z_c, rho_c
+        sflip = g_sig != ref_sig
         if sflip.any():
-            bad = sflip & ~(np.abs(enc.z) < BAND)
+            bad = sflip & ~(np.abs(ref_z) < BAND)
             assert not bad.any(), f"sign mismatches outside the band: {int(bad.sum())}"
         assert sflip.sum() <= MAX_FRAC * g_sig.size
         nsflip = int(sflip.sum())
     assert norms_match(norms[:, 0], enc.norm, 2e-6, 1e-30, norm_f16), "||k|| mismatch"
     if qjl:
-        assert norms_match(norms[live, 1], enc.rho[live], 2e-5, 1e-7, norm_f16), "||r|| mismatch"
+        assert norms_match(norms[:, 1], ref_rho, 2e-5, 1e-7, norm_f16), "||r|| mismatch"
     return int(cascade.sum()), nsflip
 
 

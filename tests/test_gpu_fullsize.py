@@ -190,4 +190,74 @@ def test_vector_search_1m_x_1536():
                                     enc_sample.rho.astype(np.float32), cb, d)[0]
         outside = ~np.isin(sample, ti_h[q])
         assert np.max(ref_s[outside]) <= tv_h[q][K - 1] + 1e-3 * abs(tv_h[q][K - 1]) + 1e-6
+    # full top-10 parity for 4 queries: oracle scores over all 10^6 GPU-encoded
+    # records (identical packed bytes), chunked over threads; the GPU's top-10
+    # set equals the oracle's up to near-ties, its values match the oracle's
+    qf = rng.choice(NQ, 4, replace=False)
+    q_rot, q_s = T.query_prep(Qd[torch.from_numpy(qf).to(DEV)].cpu().numpy(), Pi, S)
+    CH = 25000
+
+    def chunk_scores(i0):
+        w = keys.words[i0:i0 + CH].cpu().numpy().view(np.uint32)
+        nrm = keys.norms[i0:i0 + CH].cpu().numpy()
+        idx, sig = T.unpack_keys(w, d, 3)
+        return T.scores_from_parts(q_rot, q_s, idx, sig, nrm[:, 0], nrm[:, 1], cb, d)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(8) as ex:
+        s_full = np.concatenate(list(ex.map(chunk_scores, range(0, N, CH))), axis=1)
+    xnorm = keys.norms[:, 0].cpu().numpy().astype(np.float64)
+    qn = np.linalg.norm(Qd[torch.from_numpy(qf).to(DEV)].cpu().numpy().astype(np.float64), axis=1)
+    P.check_topk(ti_h[qf], tv_h[qf], s_full, K, qn, xnorm)
     print(f"recall@10 = {recall:.4f}")
+
+
+def test_fused_step_bench_shape():
+    """tq_decode_step in the serving benchmark's launch configuration: 64
+    sequences x 8192 tokens x 8 KV heads, 32 query heads, b = 4 keys, 3-bit
+    values, outlier-channel bf16 data with the benchmark's seeds, the workspace
+    sized for the whole 128-step run. Three fused steps; after each, sampled
+    streams' outputs against the oracle over the records the cache then holds
+    (identical bytes), and their appended records against the oracle's encoding."""
+    d, B, H, Hq, L, NS, NSTEP = 128, 64, 8, 32, 8192, 128, 3
+    Pi, S = _oracle_tables(d)
+    cbk, cbv = T.codebook(d, 3), T.codebook(d, 3)
+    ctx = tq.Context(d, 0)
+    cap = ((L + NS + 31) // 32) * 32
+    gen = synth.torch_outlier_kv
+    K = gen(0, (3, synth.TAG_KEYS), synth.TAG_SCALES_K, (B, H, L, d), torch.bfloat16, DEV)
+    V = gen(0, (3, synth.TAG_VALUES), synth.TAG_SCALES_V, (B, H, L, d), torch.bfloat16, DEV)
+    KA = gen(0, (3, synth.TAG_APPEND_K), synth.TAG_SCALES_K, (NS, B, H, d), torch.bfloat16, DEV)
+    VA = gen(0, (3, synth.TAG_APPEND_V), synth.TAG_SCALES_V, (NS, B, H, d), torch.bfloat16, DEV)
+    QS = gen(0, (3, synth.TAG_QUERIES), synth.TAG_SCALES_K, (NS, B, Hq, d), torch.bfloat16, DEV)
+    cache = tq.KVCache(B, H, cap, d, 3, 3)
+    cache.host_max_len = cap
+    dws = torch.empty(max(cache.decode_ws_bytes(ctx, Hq), cache.decode_step_ws_bytes(ctx, Hq)), dtype=torch.uint8,
+                      device=DEV)
+    cache.prefill(ctx, K, V)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+    streams = [0, 263, 511]
+    scale = 1 / math.sqrt(d)
+    for i in range(NSTEP):
+        cache.decode_step(ctx, KA[i], VA[i], QS[i], out=out, ws=dws)
+        torch.cuda.synchronize()
+        n = L + i + 1
+        assert cache.seq_len.cpu().tolist() == [n] * B and cache.host_max_len == n
+        o = out.cpu().numpy()
+        Qh = QS[i].float().cpu().numpy()
+        for s in streams:
+            b, h = divmod(s, H)
+            kw = cache.k.words[s * cap:s * cap + n].cpu().numpy().view(np.uint32)
+            kn = cache.k.norms[s * cap:s * cap + n].cpu().numpy()
+            vw = cache.v.words[s * cap // 32:(s + 1) * cap // 32].cpu().numpy().view(np.uint32)
+            vn = cache.v.norms[s * cap:s * cap + n].cpu().numpy()
+            ref = T.attention_decode(Qh[b, 4 * h:4 * h + 4], Pi, S, cbk, cbv, {"bits": kw, "norms": kn},
+                                     {"bits": vw, "norms": vn}, n, scale)
+            err = np.max(np.abs(o[b, 4 * h:4 * h + 4] - ref))
+            assert err <= 2e-3, f"step {i} stream {s}: {err}"
+            # the appended record of this step
+            ka = KA[i, b, h].float().cpu().numpy()[None]
+            va = VA[i, b, h].float().cpu().numpy()[None]
+            P.check_key_records(kw[n - 1:n], kn[n - 1:n], T.encode(ka, Pi, cbk, S), cbk, 3, d)
+            g_idx = T.unpack_values(vw, d, 3, n)[n - 1:n]
+            P.check_codes(g_idx, T.encode(va, Pi, cbv), cbv, "appended value codes")

@@ -121,3 +121,77 @@ def test_record_layout_and_bytes():
              np.array([[2, 7]]), np.array([[4]])]
     rec = PQ.pack_polar(PQ.PolarEncoded(codes, np.array([1.0]), []), pcb)
     assert [c.tolist() for c in PQ.unpack_polar(rec["bits"], pcb)] == [c.tolist() for c in codes]
+
+
+def _polar_setup(d, L, seed):
+    Pi = T.rotation_from_gaussian(synth.gaussian_matrix(seed, synth.TAG_ROTATION, d, d))
+    pcb = PQ.polar_codebooks(d, 4, 3)
+    cbv = T.codebook(d, 3)
+    K = synth.outlier_kv(seed, (1,), synth.TAG_SCALES_K, (L, d))
+    V = synth.outlier_kv(seed, (2,), synth.TAG_SCALES_V, (L, d))
+    keys = PQ.pack_polar(PQ.polar_encode(K, Pi, pcb), pcb)
+    ev = T.encode(V, Pi, cbv)
+    return Pi, pcb, cbv, keys, T.pack_values(ev, 3), ev
+
+
+def test_polar_attention_matches_sdpa_on_rebuilt_keys():
+    """Oracle PolarQuant decode = softmax(q K_hat^T * scale) V_hat on the dense
+    fp64 rebuilt keys K_hat = Pi^T y_hat (rows: y_hat @ Pi) and values
+    V_hat = ||v|| Pi^T c_v[idx], by numpy and by torch's
+    scaled_dot_product_attention (fp64, CPU); records past seq_len (here
+    garbage) are not read ([gemilab] Attention機構)."""
+    import torch
+    d, L, n, g = 128, 96, 70, 4
+    Pi, pcb, cbv, keys, vals, ev = _polar_setup(d, L, 0)
+    # records past the sequence hold garbage that must not matter
+    keys["bits"][n:] = np.uint32(0xDEADBEEF)
+    keys["norms"][n:] = np.float32(1e30)
+    Qh = synth.gaussian(0, (3,), (g, d), "bf16").astype(np.float64)
+    scale = 1 / math.sqrt(d)
+    o = PQ.polar_attention_decode(Qh, Pi, pcb, cbv, keys, vals, n, scale, T.unpack_values)
+    P64 = Pi.astype(np.float64)
+    Yh = PQ.polar_rebuild(PQ.unpack_polar(keys["bits"][:n], pcb), keys["norms"][:n], pcb)
+    Khat = Yh @ P64
+    Vhat = vals["norms"][:n].astype(np.float64)[:, None] * (cbv.centroids.astype(np.float64)[ev.idx[:n]] @ P64)
+    lg = Qh @ Khat.T * scale
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(o - p @ Vhat)) < 1e-10
+    t = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Qh)[None], torch.from_numpy(Khat)[None], torch.from_numpy(Vhat)[None], scale=scale)[0].numpy()
+    assert np.max(np.abs(o - t)) < 1e-10
+    # a swapped rotation (Pi in place of Pi^T on the way back) changes the output
+    wrong = (p @ (vals["norms"][:n].astype(np.float64)[:, None] * cbv.centroids.astype(np.float64)[ev.idx[:n]])) @ P64.T
+    assert np.max(np.abs(o - wrong)) > 1e-3
+
+
+def test_polar_attention_bruteforce_tiny_d():
+    """d = 4 by hand: level-1 angles t0, t1 of the pairs, level-2 angle f of
+    the two radii; y_hat = ||x|| (cos f cos t0, cos f sin t0, sin f cos t1,
+    sin f sin t1) from the stored cos/sin tables, k_hat = Pi^T y_hat, and a
+    per-token softmax loop in plain Python."""
+    d, L, n = 4, 9, 7
+    Pi, pcb, cbv, keys, vals, ev = _polar_setup(d, L, 5)
+    Qh = synth.gaussian(5, (3,), (2, d)).astype(np.float64)
+    scale = 0.5
+    o = PQ.polar_attention_decode(Qh, Pi, pcb, cbv, keys, vals, n, scale, T.unpack_values)
+    c1, c2 = PQ.unpack_polar(keys["bits"], pcb)
+    l1, l2 = pcb.levels[0], pcb.levels[1]
+    P64 = Pi.astype(np.float64)
+    for h in range(Qh.shape[0]):
+        logits, vrows = [], []
+        for t in range(n):
+            r = float(keys["norms"][t])
+            f = int(c2[t, 0])
+            r0, r1 = r * float(l2.cos[f]), r * float(l2.sin[f])
+            a0, a1 = int(c1[t, 0]), int(c1[t, 1])
+            y = [r0 * float(l1.cos[a0]), r0 * float(l1.sin[a0]), r1 * float(l1.cos[a1]), r1 * float(l1.sin[a1])]
+            k = [sum(P64[i][j] * y[i] for i in range(d)) for j in range(d)]
+            logits.append(scale * sum(Qh[h][j] * k[j] for j in range(d)))
+            cv = [float(vals["norms"][t]) * float(cbv.centroids[ev.idx[t][i]]) for i in range(d)]
+            vrows.append([sum(P64[i][j] * cv[i] for i in range(d)) for j in range(d)])
+        m = max(logits)
+        w = [math.exp(x - m) for x in logits]
+        z = sum(w)
+        ref = [sum(w[t] * vrows[t][j] for t in range(n)) / z for j in range(d)]
+        assert np.max(np.abs(o[h] - np.array(ref))) < 1e-12
