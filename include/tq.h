@@ -75,6 +75,14 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 #define TQ_MAX_BITS 4
 #define TQ_MAX_DIM 4096
 
+/* Version of the packed record formats below (bit planes, sign words, norms,
+ * value blocks, PolarQuant records). Records written by a library of one
+ * version are read only by a library of the same version; tq_format_version()
+ * returns the version the loaded library implements, so a caller can check it
+ * against the header it was compiled with. */
+#define TQ_FORMAT_VERSION 1
+int32_t tq_format_version(void);
+
 /* Lloyd-Max codebook for one rotated coordinate of a d-dimensional unit
  * vector ([ebisuda] 第1段階: the coordinate law is Beta, close to N(0,1/d)).
  * Density used: f_d(x) = (1-x^2)^((d-3)/2) / B(1/2,(d-1)/2) on [-1,1].
@@ -155,6 +163,28 @@ typedef struct tq_ctx tq_ctx;
  * ([gemilab] QJLの応用). Synchronizes the current device.
  * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d), TQ_ERR_NOMEM, TQ_ERR_HIP. */
 tq_status tq_ctx_create(int32_t d, const double *h_g_rot, const double *h_g_sketch, tq_ctx **out);
+
+/* Seeded Gaussian draws, host only, no GPU. The pages fix only that the
+ * rotation is the QR factor of a Gaussian matrix ([ebisuda] 第1段階) and that
+ * the sketch is a Gaussian matrix ([gemilab] QJLの応用); the seed-to-matrix map
+ * is this library's: word i = mix(seed ^ stream * 0x9E3779B97F4A7C15 ^ i)
+ * (mod 2^64), mix the SplitMix64 output function (Steele, Lea & Flood,
+ * OOPSLA 2014), u_i = (word_i >> 11) * 2^-53; entries 2k, 2k + 1 (row-major)
+ * are r cos(2 pi u_{2k+1}), r sin(2 pi u_{2k+1}) with r = sqrt(-2 ln(1 -
+ * u_{2k})) (Box-Muller), fp64. Stream TQ_STREAM_ROTATION draws the matrix
+ * behind Pi, TQ_STREAM_SKETCH the sketch. h_out: rows * cols doubles,
+ * caller-owned; rows * cols must be even.
+ * Errors: TQ_ERR_ARG (NULL, sizes). */
+#define TQ_STREAM_ROTATION 1
+#define TQ_STREAM_SKETCH 2
+tq_status tq_gaussian_matrix(uint64_t seed, uint32_t stream, int32_t rows, int32_t cols, double *h_out);
+
+/* A context from a seed alone: tq_ctx_create(d, G_rot, G_sketch) with
+ * G_rot = tq_gaussian_matrix(seed, TQ_STREAM_ROTATION, d, d) and
+ * G_sketch = tq_gaussian_matrix(seed, TQ_STREAM_SKETCH, d, d) ([ebisuda]
+ * 第1段階: QR of a seeded Gaussian matrix). Synchronizes the current device.
+ * Errors: as tq_ctx_create. */
+tq_status tq_ctx_create_seeded(int32_t d, uint64_t seed, tq_ctx **out);
 tq_status tq_ctx_destroy(tq_ctx *ctx);
 int32_t tq_ctx_dim(const tq_ctx *ctx);
 /* Host copies of the fp32 tables (either output may be NULL). */

@@ -79,6 +79,9 @@ _sig("tq_last_error", ctypes.c_char_p, [])
 _sig("tq_codebook_build", _c_i32, [_c_i32, _c_i32, ctypes.POINTER(CCodebook)])
 _sig("tq_rotation_build", _c_i32, [_c_i32, _c_vp, _c_vp])
 _sig("tq_ctx_create", _c_i32, [_c_i32, _c_vp, _c_vp, ctypes.POINTER(_c_vp)])
+_sig("tq_ctx_create_seeded", _c_i32, [_c_i32, ctypes.c_uint64, ctypes.POINTER(_c_vp)])
+_sig("tq_gaussian_matrix", _c_i32, [ctypes.c_uint64, ctypes.c_uint32, _c_i32, _c_i32, _c_vp])
+_sig("tq_format_version", _c_i32, [])
 _sig("tq_ctx_destroy", _c_i32, [_c_vp])
 _sig("tq_ctx_dim", _c_i32, [_c_vp])
 _sig("tq_ctx_export", _c_i32, [_c_vp, _c_vp, _c_vp])
@@ -115,6 +118,7 @@ _sig("tq_scores", _c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, ctypes.POINTER(CPacked)
                            _c_vp, _c_sz, _c_vp])
 
 EXPORTED_SYMBOLS = [
+    "tq_format_version", "tq_gaussian_matrix", "tq_ctx_create_seeded",
     "tq_codebook_build", "tq_angle_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
     "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_cache_write", "tq_append_token", "tq_attention_decode_ws_bytes",
     "tq_attention_decode", "tq_attention_prefill_ws_bytes", "tq_attention_prefill", "tq_decode_step_ws_bytes",
@@ -201,6 +205,22 @@ def angle_codebook_build(level: int, bits: int) -> dict:
             "cos": np.array(c.cos_c[:L], dtype=np.float32), "sin": np.array(c.sin_c[:L], dtype=np.float32)}
 
 
+TQ_STREAM_ROTATION, TQ_STREAM_SKETCH = 1, 2
+FORMAT_VERSION = 1  # TQ_FORMAT_VERSION of include/tq.h
+
+
+def format_version() -> int:
+    """Version of the packed record formats the loaded library implements."""
+    return int(_lib.tq_format_version())
+
+
+def gaussian_matrix(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
+    """Host-only: the library's seeded N(0,1) draws (float64, row-major)."""
+    out = np.empty((rows, cols), np.float64)
+    _check(_lib.tq_gaussian_matrix(seed, stream, rows, cols, out.ctypes.data))
+    return out
+
+
 def rotation_build(g: np.ndarray) -> np.ndarray:
     """Host-only: the fp32 rotation the library derives from Gaussian matrix g."""
     g = np.ascontiguousarray(g, dtype=np.float64)
@@ -254,6 +274,17 @@ class Context:
         _check(_lib.tq_ctx_create(d, gr.ctypes.data, gs.ctypes.data, ctypes.byref(h)))
         self._h = h
         self.d = d
+
+    @classmethod
+    def from_seed(cls, d: int, seed: int) -> "Context":
+        """A context built by the library from the seed alone (tq_ctx_create_seeded:
+        its own counter-based Gaussian draws for the rotation and the sketch)."""
+        self = cls.__new__(cls)
+        h = _c_vp()
+        _check(_lib.tq_ctx_create_seeded(d, seed, ctypes.byref(h)))
+        self._h = h
+        self.d = d
+        return self
 
     @property
     def handle(self):

@@ -208,6 +208,33 @@ static std::vector<float> rotation_from_gaussian(int n, const double *g) {
   return pi;
 }
 
+// ---------------------------------------------------------------------------
+// Seeded Gaussian draws for the rotation's and the sketch's matrices: a
+// counter-based generator (the SplitMix64 output function of Steele, Lea &
+// Flood, OOPSLA 2014, applied to seed ^ stream * GAMMA ^ counter) and the
+// Box-Muller transform (Box & Muller 1958), fp64, filled row-major.
+// ---------------------------------------------------------------------------
+
+static inline uint64_t splitmix64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// n (even) N(0,1) values: entry 2k = r cos(2 pi u_{2k+1}), 2k + 1 = r sin(2 pi u_{2k+1}),
+// r = sqrt(-2 ln(1 - u_{2k})), u_i = (mix(key ^ i) >> 11) 2^-53, key = seed ^ stream * GAMMA
+static void seeded_gaussian(uint64_t seed, uint64_t stream, int64_t n, double *out) {
+  const uint64_t key = seed ^ (stream * 0x9E3779B97F4A7C15ull);
+  for (int64_t k = 0; 2 * k + 1 < n; ++k) {
+    const double u1 = (double)(splitmix64_mix(key ^ (uint64_t)(2 * k)) >> 11) * 0x1p-53;
+    const double u2 = (double)(splitmix64_mix(key ^ (uint64_t)(2 * k + 1)) >> 11) * 0x1p-53;
+    const double r = std::sqrt(-2.0 * std::log(1.0 - u1));  // 1 - u1 is exact
+    const double a = 2.0 * M_PI * u2;
+    out[2 * k] = r * std::cos(a);
+    out[2 * k + 1] = r * std::sin(a);
+  }
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -215,6 +242,8 @@ using namespace tq;
 extern "C" {
 
 const char *tq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t tq_format_version(void) { return TQ_FORMAT_VERSION; }
 
 tq_status tq_read_probe(const void *d_src, size_t bytes, int32_t grid, uint32_t *d_sink, void *stream) {
   if (!d_src || !d_sink) return fail(TQ_ERR_ARG, "tq_read_probe: NULL buffer");
@@ -506,6 +535,31 @@ tq_status tq_ctx_create(int32_t d, const double *h_g_rot, const double *h_g_sket
   }
   *out = ctx;
   return TQ_OK;
+}
+
+tq_status tq_gaussian_matrix(uint64_t seed, uint32_t stream, int32_t rows, int32_t cols, double *h_out) {
+  if (!h_out) return fail(TQ_ERR_ARG, "tq_gaussian_matrix: h_out is NULL");
+  if (rows <= 0 || cols <= 0 || (((int64_t)rows * cols) & 1) != 0)
+    return fail(TQ_ERR_ARG, "tq_gaussian_matrix: rows and cols must be positive with an even product");
+  seeded_gaussian(seed, stream, (int64_t)rows * cols, h_out);
+  return TQ_OK;
+}
+
+tq_status tq_ctx_create_seeded(int32_t d, uint64_t seed, tq_ctx **out) {
+  if (!out) return fail(TQ_ERR_ARG, "tq_ctx_create_seeded: out is NULL");
+  *out = nullptr;
+  if (d < 32 || d > TQ_MAX_DIM || (d % 32) != 0)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_ctx_create_seeded: d must be a multiple of 32 in [32, 4096]");
+  std::vector<double> g_rot, g_sk;
+  try {
+    g_rot.resize((size_t)d * d);
+    g_sk.resize((size_t)d * d);
+  } catch (...) {
+    return fail(TQ_ERR_NOMEM, "tq_ctx_create_seeded: host allocation failed");
+  }
+  seeded_gaussian(seed, TQ_STREAM_ROTATION, (int64_t)d * d, g_rot.data());
+  seeded_gaussian(seed, TQ_STREAM_SKETCH, (int64_t)d * d, g_sk.data());
+  return tq_ctx_create(d, g_rot.data(), g_sk.data(), out);
 }
 
 tq_status tq_ctx_destroy(tq_ctx *ctx) {

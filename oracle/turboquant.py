@@ -33,7 +33,7 @@ import numpy as np
 from scipy import special
 
 __all__ = [
-    "rotation_from_gaussian", "sketch_from_gaussian", "coord_density", "coord_cdf",
+    "splitmix64_mix", "seeded_gaussian", "rotation_from_gaussian", "sketch_from_gaussian", "coord_density", "coord_cdf",
     "lloyd_max", "Codebook", "codebook", "encode", "qjl_stage", "Encoded", "query_prep", "qjl_constant",
     "scores", "scores_from_parts", "dequantize_keys", "attention_decode", "attention_prefill", "topk", "stored_norms",
     "recall_at_k", "pack_keys", "unpack_keys", "pack_values", "unpack_values",
@@ -61,6 +61,47 @@ def rotation_from_gaussian(G: np.ndarray, return_fp64: bool = False):
     Q = Q * s[None, :]
     Pi = Q.astype(np.float32)
     return (Pi, Q, R * s[:, None]) if return_fp64 else Pi
+
+
+# Seeded Gaussian draws. The pages say only that the rotation is the QR factor
+# of a Gaussian matrix and the sketch a Gaussian matrix; the seed-to-matrix map
+# is a reading: a counter-based generator (the SplitMix64 output function,
+# Steele, Lea & Flood, "Fast splittable pseudorandom number generators",
+# OOPSLA 2014) turned into normal pairs by the Box-Muller transform (Box &
+# Muller, 1958). Stream 1 draws the rotation's Gaussian matrix, stream 2 the
+# sketch's; entries are filled row-major.
+SPLITMIX_GAMMA = 0x9E3779B97F4A7C15
+STREAM_ROTATION = 1
+STREAM_SKETCH = 2
+
+
+def splitmix64_mix(z):
+    """The SplitMix64 output function on uint64 values (numpy arrays wrap mod 2^64):
+    z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27; z *= 0x94D049BB133111EB;
+    z ^= z >> 31."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def seeded_gaussian(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
+    """rows x cols float64 N(0,1) draws for (seed, stream): word i =
+    mix(seed XOR stream * GAMMA XOR i) (mod 2^64), u_i = (word_i >> 11) / 2^53 in
+    [0, 1); entries 2k and 2k + 1 are r cos(2 pi u_{2k+1}) and r sin(2 pi u_{2k+1})
+    with r = sqrt(-2 ln(1 - u_{2k})), filled row-major (rows * cols even)."""
+    n = rows * cols
+    assert n % 2 == 0
+    key = np.uint64((int(seed) ^ ((int(stream) * SPLITMIX_GAMMA) & 0xFFFFFFFFFFFFFFFF)) & 0xFFFFFFFFFFFFFFFF)
+    words = splitmix64_mix(key ^ np.arange(n, dtype=np.uint64))
+    u = (words >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+    u1, u2 = u[0::2], u[1::2]
+    r = np.sqrt(-2.0 * np.log(1.0 - u1))  # 1 - u is exact in fp64
+    out = np.empty(n, dtype=np.float64)
+    out[0::2] = r * np.cos(2.0 * np.pi * u2)
+    out[1::2] = r * np.sin(2.0 * np.pi * u2)
+    return out.reshape(rows, cols)
 
 
 def sketch_from_gaussian(G: np.ndarray) -> np.ndarray:

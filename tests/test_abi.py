@@ -71,6 +71,46 @@ def test_rotation_matches_oracle(d):
     assert np.max(np.abs(lib_pi.astype(np.float64).T @ lib_pi.astype(np.float64) - np.eye(d))) <= 1e-5
 
 
+@pytest.mark.parametrize("seed,stream,rows,cols", [(0, 1, 128, 128), (0, 2, 128, 128), (12345, 1, 64, 96),
+                                                    (2 ** 63 + 5, 2, 1536, 1536)])
+def test_seeded_gaussian_matches_oracle(seed, stream, rows, cols):
+    """The library's counter-based Gaussian draws and the oracle's, two
+    independent implementations of one published definition, agree bitwise in
+    fp64 or (libm ulp differences) within 1 fp32 ulp after rounding."""
+    lib_g = tq.gaussian_matrix(seed, stream, rows, cols)
+    o_g = T.seeded_gaussian(seed, stream, rows, cols)
+    same = lib_g == o_g
+    ulp = np.abs(lib_g.astype(np.float32).view(np.int32).astype(np.int64) - o_g.astype(np.float32).view(np.int32))
+    assert ulp.max() <= 1
+    assert np.mean(same) > 0.99, f"bitwise fp64 agreement {np.mean(same):.4f}"
+
+
+@pytest.mark.parametrize("d", [128, 1536])
+def test_seeded_rotation_matches_oracle(d):
+    """Pi and S of a context built from a seed alone (host part of
+    tq_ctx_create_seeded) against the oracle's rotation and sketch of its own
+    draws for the same seed. The two QRs (Householder here, LAPACK there) of
+    draws that differ in the last fp64 bit of a few entries agree within 1 fp32
+    ulp except a few entries in 10^5, which stay within 2^-24 absolute (a few
+    ulp of a small entry); Pi is orthogonal to 1e-5."""
+    for seed in (0, 7):
+        g = tq.gaussian_matrix(seed, tq.TQ_STREAM_ROTATION, d, d)
+        lib_pi = tq.rotation_build(g)
+        o_pi = T.rotation_from_gaussian(T.seeded_gaussian(seed, T.STREAM_ROTATION, d, d))
+        ulp = np.abs(lib_pi.view(np.int32).astype(np.int64) - o_pi.view(np.int32))
+        assert np.count_nonzero(ulp > 1) <= 1e-5 * d * d
+        assert np.max(np.abs(lib_pi.astype(np.float64) - o_pi)) <= 2.0 ** -24
+        lib_s = tq.gaussian_matrix(seed, tq.TQ_STREAM_SKETCH, d, d).astype(np.float32)
+        o_s = T.sketch_from_gaussian(T.seeded_gaussian(seed, T.STREAM_SKETCH, d, d))
+        assert np.abs(lib_s.view(np.int32).astype(np.int64) - o_s.view(np.int32)).max() <= 1
+    assert np.max(np.abs(lib_pi.astype(np.float64).T @ lib_pi.astype(np.float64) - np.eye(d))) <= 1e-5
+
+
+def test_format_version():
+    assert tq.format_version() == tq.FORMAT_VERSION == 1
+    assert "#define TQ_FORMAT_VERSION 1" in open(os.path.join(ROOT, "include", "tq.h")).read()
+
+
 def test_host_errors():
     lib = tq.lib()
     cb = tq.CCodebook()

@@ -24,6 +24,38 @@ def _ctx(d, seed=0, m=None):
     return Pi, S
 
 
+# --- seeded Gaussian draws ----------------------------------------------------
+
+def test_splitmix64_output_function_published_values():
+    """The SplitMix64 generator (state += 0x9E3779B97F4A7C15, then the output
+    function) seeded with 1234567 gives the reference implementation's first
+    five outputs (the published test vector of splitmix64.c)."""
+    M = (1 << 64) - 1
+    got = [int(T.splitmix64_mix(np.uint64((1234567 + k * T.SPLITMIX_GAMMA) & M))) for k in range(1, 6)]
+    assert got == [6457827717110365317, 3203168211198807973, 9817491932198370423, 4593380528125082431,
+                   16408922859458223821]
+
+
+def test_seeded_gaussian_is_standard_normal():
+    """10^6 draws: mean 0 and variance 1 within 3 standard errors; the
+    Kolmogorov-Smirnov distance to N(0,1) is small; the Box-Muller pairs are
+    uncorrelated and their squared radius has mean 2 (r^2 / 2 ~ Exp(1));
+    different streams and seeds give different draws."""
+    from scipy import stats
+    n = 10 ** 6
+    g = T.seeded_gaussian(3, 1, 1000, 1000).ravel()
+    se = 1 / math.sqrt(n)
+    assert abs(g.mean()) < 3 * se
+    assert abs(g.var() - 1) < 3 * math.sqrt(2 / n)
+    assert stats.kstest(g, "norm").statistic < 2e-3
+    a, b = g[0::2], g[1::2]
+    assert abs(np.mean(a * b)) < 3 / math.sqrt(n / 2)
+    r2 = a * a + b * b
+    assert abs(r2.mean() - 2) < 3 * 2 / math.sqrt(n / 2)
+    assert not np.array_equal(T.seeded_gaussian(3, 2, 10, 10), T.seeded_gaussian(3, 1, 10, 10))
+    assert not np.array_equal(T.seeded_gaussian(4, 1, 10, 10), T.seeded_gaussian(3, 1, 10, 10))
+
+
 # --- rotation ---------------------------------------------------------------
 
 @pytest.mark.parametrize("d", [8, 128, 1536])
