@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: also capture one whole step in a HIP graph (torch.cuda.graph) and "
                          "time its replays (graph_ms_per_step)")
+    ap.add_argument("--no-gaussian-pass", action="store_true",
+                    help="serving / gqa with outlier data: skip the second pass on Gaussian data (reported "
+                         "under \"gaussian\" in the same JSON line)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run 5 device-to-device copies of this many MiB (a plain copy kernel of known size, "
                          "the calibration of the rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -80,6 +83,28 @@ def threads_used():
         return n or len(os.sched_getaffinity(0))
     except Exception:
         return os.cpu_count()
+
+
+def cpu_info():
+    """The host CPU model and the BLAS thread count the oracle's numpy runs with."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        import threadpoolctl
+        pools = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            blas = {"library": pools[0].get("internal_api"), "threads": pools[0].get("num_threads")}
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas, "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 class Timer:
@@ -392,7 +417,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
         "metric": METRIC, "value": keys_per_step / (ms_per_step / 1e3), "unit": "keys/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32+fp6/fp4/i8 exact-digit MFMA",
-        "data": f"synthetic ({args.data}-channel bf16 K/V, seeded)",
+        "data": ("synthetic (outlier-channel bf16 K/V, seeded)" if args.data == "outlier" else "synthetic (i.i.d. N(0,1) bf16 K/V, seeded)"),
         "config": {"workload": cfg_text, "batch": B, "context": L, "decode_steps": NS, "kv_heads": H,
                    "q_heads": Hq, "head_dim": d, "key_bits": kbits + int(kqjl), "key_format": args.key_format,
                    "value_bits": vbits, "norms": args.norms, "cache_layout": (f"paged, {args.page_tokens}-token pages in a shuffled pool"
@@ -425,7 +450,7 @@ def run_decode_workload(args, torch, tq, synth, B, H, Hq, L, NS, name, cfg_text)
                                                                args.cpu_seconds, args.data, kqjl)
         step_s = vectors / enc_rate + keys_per_step / dec_rate
         res["cpu_baseline"] = {
-            "value": keys_per_step / step_s, "unit": "keys/s", "cores": threads_used(), "kind": "oracle",
+            "value": keys_per_step / step_s, "unit": "keys/s", "cores": threads_used(), "kind": "oracle", **cpu_info(),
             "sample": f"{streams} whole (sequence, KV head) streams of {min(L, 8192)} tokens: oracle encode of "
                       f"their K and V vectors and decode for {Hq // H} query heads, {secs:.1f} s of CPU work; "
                       f"extrapolated to the step at {enc_rate:.0f} vectors/s and {dec_rate:.0f} keys/s",
@@ -555,7 +580,7 @@ def run_prefill(args, torch, tq, synth):
         rate, chunks, secs = oracle_prefill_rate(d, 2048, 64, Hq // H, kbits, vbits, args.cpu_seconds, args.data,
                                                  kqjl)
         res["cpu_baseline"] = {
-            "value": rate, "unit": "keys/s", "cores": threads_used(), "kind": "oracle",
+            "value": rate, "unit": "keys/s", "cores": threads_used(), "kind": "oracle", **cpu_info(),
             "sample": f"{chunks} chunks of 64 causal query positions x {Hq // H} heads over one 2048-token packed "
                       f"stream (records encoded beforehand), {secs:.1f} s of CPU work"}
     return res
@@ -659,7 +684,7 @@ def run_polar(args, torch, tq, synth):
         enc_rate, dec_rate = 2 * Ls / t_enc, Ls * n_dec / t_dec
         step_s = 2 * B * H * L / enc_rate + keys / dec_rate
         res["cpu_baseline"] = {
-            "value": keys / step_s, "unit": "keys/s", "cores": threads_used(), "kind": "oracle",
+            "value": keys / step_s, "unit": "keys/s", "cores": threads_used(), "kind": "oracle", **cpu_info(),
             "sample": f"one stream of {Ls} tokens: oracle encode of its K and V, then {n_dec} decodes for "
                       f"{Hq // H} query heads ({t_enc + t_dec:.1f} s of CPU work), extrapolated to the step",
             "quantize_vectors_per_s": enc_rate, "decode_keys_per_s": dec_rate}
@@ -730,7 +755,7 @@ def run_search(args, torch, tq, synth):
         t2 = time.perf_counter()
         enc_rate, pair_rate = 4096 / (t1 - t0), 100 * 4096 / (t2 - t1)
         res["cpu_baseline"] = {"value": NQ * N / (N / enc_rate + NQ * N / pair_rate), "unit": "pair-scores/s",
-                               "cores": threads_used(), "kind": "oracle",
+                               "cores": threads_used(), "kind": "oracle", **cpu_info(),
                                "sample": f"encode 4096 vectors and score/top-10 100 queries against them "
                                          f"({t2 - t0:.1f} s); extrapolated to the step",
                                "quantize_vectors_per_s": enc_rate, "pair_scores_per_s": pair_rate}
@@ -779,14 +804,28 @@ def main():
     if args.copy_probe_mib > 0:
         copy_probe(torch, args.copy_probe_mib)
         return
-    if args.workload == "serving":
-        res = run_decode_workload(args, torch, tq, synth, 64, 8, 32, 8192, 128, "serving",
-                                  "batched_serving_step: 64 seq x 8192 ctx, 8 KV heads, 32 q heads, d=128, "
-                                  f"{key_format(args)[2]}, values 3-bit, prefill quantize + 128 x (append + decode)")
-    elif args.workload == "gqa":
-        res = run_decode_workload(args, torch, tq, synth, 4, 8, 32, 131072, 0, "gqa",
-                                  "gqa_layer: batch 4 x 131072 ctx, 8 KV heads, 32 q heads, d=128, "
-                                  f"{key_format(args)[2]}, values 3-bit, prefill quantize + 1 decode")
+    serving = (64, 8, 32, 8192, 128, "serving",
+               "batched_serving_step: 64 seq x 8192 ctx, 8 KV heads, 32 q heads, d=128, "
+               f"{key_format(args)[2]}, values 3-bit, prefill quantize + 128 x (append + decode)")
+    gqa = (4, 8, 32, 131072, 0, "gqa",
+           "gqa_layer: batch 4 x 131072 ctx, 8 KV heads, 32 q heads, d=128, "
+           f"{key_format(args)[2]}, values 3-bit, prefill quantize + 1 decode")
+    if args.workload in ("serving", "gqa"):
+        shape = serving if args.workload == "serving" else gqa
+        res = run_decode_workload(args, torch, tq, synth, *shape)
+        if args.data == "outlier" and not args.no_gaussian_pass:
+            # the same workload on i.i.d. Gaussian K/V: both data laws in one line
+            import copy
+            a2 = copy.copy(args)
+            a2.data, a2.graph, a2.cpu_seconds = "gaussian", False, min(args.cpu_seconds, 6.0)
+            g = run_decode_workload(a2, torch, tq, synth, *shape)
+            rf = g["roofline"]
+            res["gaussian"] = {
+                "data": g["data"], "value": g["value"], "unit": g["unit"], "ms_per_step": g["ms_per_step"],
+                "quantize_vectors_per_s": g["quantize_vectors_per_s"],
+                "roofline": {k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac", "avg_launch_ms",
+                                                 "read_ceiling_gbs", "frac_of_read_ceiling")},
+                "cpu_baseline": g.get("cpu_baseline")}
     elif args.workload == "single":
         res = run_decode_workload(args, torch, tq, synth, 1, 1, 1, 32768, 0, "single",
                                   "single_head_decode: 32768 ctx, d=128, keys b=4, values 3-bit, quantize + 1 decode")
