@@ -290,6 +290,24 @@ tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const
                               int32_t q_heads, float scale, float *d_out, void *d_ws, size_t ws_bytes,
                               void *stream);
 
+/* tq_attention_decode without a caller workspace, for callers that cannot
+ * allocate device memory or pass one (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). The same kernels and
+ * result as tq_attention_decode; the workspace (query fragments, per-chunk
+ * softmax partials) is a library-held scratch array of TQ_SCRATCH_BYTES per
+ * device, whose device address is looked up once per device when a context
+ * is created there, and which lives until the process ends. The call itself
+ * allocates nothing (no hipMalloc, no hipFree) and clears nothing: every byte
+ * a call reads from the scratch is written by that call first. All calls on
+ * one device share that device's array, so calls that overlap on one device
+ * (two streams, or two threads) race and must be serialized by the caller.
+ * Errors: as tq_attention_decode; TQ_ERR_CAPACITY when the call needs more
+ * than TQ_SCRATCH_BYTES (tq_attention_decode_ws_bytes() > TQ_SCRATCH_BYTES;
+ * e.g. 64 sequences x 8 KV heads x 32 query heads at 8K tokens need 14 MB). */
+#define TQ_SCRATCH_BYTES (32u << 20)
+tq_status tq_attention_decode_noalloc(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_q, tq_dtype dtype,
+                                      int32_t q_heads, float scale, float *d_out, void *stream);
+
 /* Attention of many query positions per sequence over the packed cache (the
  * cache part of chunked prefill; [gemilab] Attention機構 with the estimator
  * of [ebisuda] 第2段階, as tq_attention_decode): for every sequence b, query

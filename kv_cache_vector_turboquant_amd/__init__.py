@@ -108,6 +108,8 @@ _sig("tq_decode_step", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_vp, _c_
                                 _c_vp, _c_sz, _c_vp])
 _sig("tq_attention_decode", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp,
                                      _c_sz, _c_vp])
+_sig("tq_attention_decode_noalloc", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_f32, _c_vp,
+                                             _c_vp])
 _sig("tq_attention_prefill_ws_bytes", _c_sz, [_c_vp, ctypes.POINTER(CCache), _c_i32, _c_i32])
 _sig("tq_attention_prefill", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                       _c_vp, _c_vp, _c_sz, _c_vp])
@@ -121,7 +123,7 @@ EXPORTED_SYMBOLS = [
     "tq_format_version", "tq_gaussian_matrix", "tq_ctx_create_seeded",
     "tq_codebook_build", "tq_angle_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
     "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_cache_write", "tq_append_token", "tq_attention_decode_ws_bytes",
-    "tq_attention_decode", "tq_attention_prefill_ws_bytes", "tq_attention_prefill", "tq_decode_step_ws_bytes",
+    "tq_attention_decode", "tq_attention_decode_noalloc", "tq_attention_prefill_ws_bytes", "tq_attention_prefill", "tq_decode_step_ws_bytes",
     "tq_decode_step", "tq_time_next_decode", "tq_read_probe",
     "tq_scores_ws_bytes", "tq_scores", "tq_polar_quantize_ws_bytes", "tq_polar_quantize", "tq_polar_scores_ws_bytes",
     "tq_polar_scores", "tq_polar_attention_decode_ws_bytes", "tq_polar_attention_decode", "tq_last_error",

@@ -438,6 +438,11 @@ tq_status tq_ctx_create(int32_t d, const double *h_g_rot, const double *h_g_sket
     delete ctx;
     return hip_fail(e, "tq_ctx_create: hipGetDevice");
   }
+  // the device address of this device's scratch array (tq_attention_decode_noalloc)
+  if ((e = scratch_init(ctx->device)) != hipSuccess) {
+    delete ctx;
+    return hip_fail(e, "tq_ctx_create: scratch symbol address");
+  }
   ctx->rot = rotation_from_gaussian(d, h_g_rot);
   ctx->sketch.resize((size_t)d * d);
   for (size_t i = 0; i < (size_t)d * d; ++i) ctx->sketch[i] = (float)h_g_sketch[i];
@@ -768,6 +773,37 @@ tq_status tq_attention_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const
   if (!d_ws || ws_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_attention_decode: workspace smaller than tq_attention_decode_ws_bytes()");
   if ((s = check_device(ctx, fn)) != TQ_OK) return s;
   hipError_t e = launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream,
+                               nullptr, nullptr, ev[0], ev[1]);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
+}
+
+tq_status tq_attention_decode_noalloc(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_q, tq_dtype dtype,
+                                      int32_t q_heads, float scale, float *d_out, void *stream) {
+  const char *fn = "tq_attention_decode_noalloc";
+  hipEvent_t ev[2];
+  take_decode_events(ev);
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_attention_decode_noalloc: NULL ctx");
+  tq_status s = check_cache(ctx, cache, fn);
+  if (s != TQ_OK) return s;
+  if (!d_q || !d_out) return fail(TQ_ERR_ARG, "tq_attention_decode_noalloc: NULL query or output");
+  if (dtype != TQ_F32 && dtype != TQ_BF16)
+    return fail(TQ_ERR_ARG, "tq_attention_decode_noalloc: dtype must be TQ_F32 or TQ_BF16");
+  if (q_heads <= 0 || (q_heads % cache->kv_heads) != 0)
+    return fail(TQ_ERR_ARG, "tq_attention_decode_noalloc: q_heads must be a positive multiple of kv_heads");
+  if (q_heads / cache->kv_heads > 16)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_attention_decode_noalloc: at most 16 query heads per KV head");
+  if (ctx->d != 128) return fail(TQ_ERR_UNSUPPORTED, "tq_attention_decode_noalloc: d must be 128");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_ARG, "tq_attention_decode_noalloc: scale must be finite");
+  const size_t need = tq_attention_decode_ws_bytes(ctx, cache, q_heads);
+  if (need > (size_t)TQ_SCRATCH_BYTES)
+    return fail(TQ_ERR_CAPACITY, "tq_attention_decode_noalloc: this call needs " + std::to_string(need) +
+                                     " bytes of scratch, more than the library's TQ_SCRATCH_BYTES = " +
+                                     std::to_string((size_t)TQ_SCRATCH_BYTES) +
+                                     " (use tq_attention_decode with a caller workspace)");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  void *ws = scratch_ptr(ctx->device);
+  if (!ws) return fail(TQ_ERR_HIP, "tq_attention_decode_noalloc: no scratch address for the context's device");
+  hipError_t e = launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, d_out, ws, (hipStream_t)stream,
                                nullptr, nullptr, ev[0], ev[1]);
   return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }

@@ -118,6 +118,11 @@ hipError_t launch_polar_attention(const tq_ctx *ctx, const tq_polar_packed *keys
                                   const void *q, int is_bf16, int32_t q_heads, float scale, float *out, void *ws,
                                   hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores);
+// The library-held scratch array (TQ_SCRATCH_BYTES per device): scratch_init
+// looks up its device address once per device (that device current);
+// scratch_ptr returns it (NULL before scratch_init on that device).
+hipError_t scratch_init(int device);
+void *scratch_ptr(int device);
 hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_packed *keys,
                          float *scores, int32_t topk, int32_t *top_idx, float *top_val, void *ws, hipStream_t st);
 }  // namespace tq

@@ -28,6 +28,7 @@
 #include <cfloat>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "tq_internal.h"
 #include <hip/hip_fp16.h>
@@ -2420,6 +2421,38 @@ hipError_t launch_append(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   hipLaunchKernelGGL(append_len_kernel, dim3((cache->batch + 255) / 256), dim3(256), 0, st, cache->d_seq_len,
                      cache->batch, cache->capacity);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Library-held scratch for callers that cannot allocate (tq_attention_decode_noalloc):
+// one array per device, alive until the process ends. Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the symbol):
+// its device address comes from hipGetSymbolAddress, taken once per device with
+// that device current (at context creation) and kept per device.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[TQ_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void *ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (ptr == nullptr) return hipErrorInvalidSymbol;
+  g_scratch_ptr[device] = ptr;
+  return hipSuccess;
+}
+
+void *scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_ptr[device];
 }
 
 }  // namespace tq
