@@ -453,6 +453,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   // keys: residual parts, [token][coordinate] bf16 (16 granules per token row)
   __shared__ __attribute__((aligned(16))) uint16_t rt[SK ? 2 : 1][SK ? QT * QD : 8];
   __shared__ float nrm[QT], ninv[QT];
+  __shared__ float ssq[QT];  // squared norms of the staged tile's tokens
   __shared__ float rho2[NW][QT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
@@ -497,32 +498,55 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
     idx = ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
     return __builtin_copysignf(c, y);
   };
-  // X granule P (0..1023) of tile tl, for slot P of the swizzled LDS tile (rows past
-  // the stream's end re-read its last token)
-  auto x_granule = [&](int64_t tl, int P) {
-    const int64_t st = tl / tps, tt0 = (tl % tps) * QT;
+  // X granule P (0..1023) of the tile at token tt0 of stream st, for slot P of the
+  // swizzled LDS tile (rows past the stream's end re-read its last token)
+  auto x_granule = [&](int64_t st, int64_t tt0, int P) {
     const int last = (int)min((int64_t)QT, a.n_tokens - tt0) - 1;
     const int t = P >> 4, g = (P & 15) ^ (t & 15);
     return *reinterpret_cast<const uint4 *>(a.x + st * a.xs + (tt0 + min(t, last)) * a.xt + g * 8);
+  };
+  // a tile's X into LDS, with each token's squared norm: the 16 slots of token t
+  // are 16 consecutive threads (a 16-lane shuffle sum of their bf16 squares,
+  // each product exact in fp32)
+  auto stage_x = [&](const uint4 (&v)[XG]) {
+#pragma unroll
+    for (int i = 0; i < XG; ++i) {
+      xs[i * NT + tid] = v[i];
+      float q = sumsq8(__builtin_bit_cast(bf16x8, v[i]), 0.f);
+      q += __shfl_xor(q, 1);
+      q += __shfl_xor(q, 2);
+      q += __shfl_xor(q, 4);
+      q += __shfl_xor(q, 8);
+      if ((tid & 15) == 0) ssq[(i * NT + tid) >> 4] = q;
+    }
   };
 
   // work-groups loop over (stream, 64-token tile) pairs (tiles of stream s are
   // s * tps .. s * tps + tps - 1); the next tile's X is loaded into registers
   // while the current one is processed, and written to LDS once every wave is
-  // past its reads of the current X
+  // past its reads of the current X. The (stream, tile) pair advances by the
+  // grid size with one division per launch.
   int64_t tile = blockIdx.x;
   if (tile >= total) return;
+  const int64_t dS = (int64_t)gridDim.x / tps, dR = (int64_t)gridDim.x % tps;
+  int64_t s = tile / tps, tr = tile % tps;  // this tile: stream, tile in the stream
   uint4 xr[XG];
 #pragma unroll
-  for (int i = 0; i < XG; ++i) xs[i * NT + tid] = x_granule(tile, i * NT + tid);
+  for (int i = 0; i < XG; ++i) xr[i] = x_granule(s, tr * QT, i * NT + tid);
+  stage_x(xr);
   for (; tile < total; tile += gridDim.x) {
-    const int64_t s = tile / tps, t0 = (tile % tps) * QT;
+    const int64_t t0 = tr * QT;
     const int nv = (int)min((int64_t)QT, a.n_tokens - t0);
     const bool more = tile + gridDim.x < total;
-    __syncthreads();  // this tile's X (and the previous tile's LDS traffic is done)
+    int64_t sn = s + dS, trn = tr + dR;  // the next tile
+    if (trn >= tps) {
+      trn -= tps;
+      ++sn;
+    }
+    __syncthreads();  // this tile's X and norms (and the previous tile's LDS traffic is done)
     if (more) {
 #pragma unroll
-      for (int i = 0; i < XG; ++i) xr[i] = x_granule(tile + gridDim.x, i * NT + tid);
+      for (int i = 0; i < XG; ++i) xr[i] = x_granule(sn, trn * QT, i * NT + tid);
     }
 
     // ---- product 1: the wave's output coordinates for the 64 tokens (blocks tb)
@@ -531,7 +555,6 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[rb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
-    float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 xf[4];
@@ -539,7 +562,6 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
       for (int tb = 0; tb < 4; ++tb) {
         const int t = tb * 16 + c16;
         xf[tb] = __builtin_bit_cast(bf16x8, xs[t * 16 + ((ks * 4 + kq) ^ (t & 15))]);
-        ss[tb] = sumsq8(xf[tb], ss[tb]);
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -550,12 +572,10 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
             acc[rb][tb] = KEYS ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[rb][ks][sp], xf[tb], acc[rb][tb], 0, 0, 0)
                                : __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[tb], pf[rb][ks][sp], acc[rb][tb], 0, 0, 0);
     }
-    // token norms: lanes of one c16 hold the four k quarters
+    // token norms (staged with the tile's X)
+    float ss[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      ss[tb] += __shfl_xor(ss[tb], 16);
-      ss[tb] += __shfl_xor(ss[tb], 32);
-    }
+    for (int tb = 0; tb < 4; ++tb) ss[tb] = ssq[tb * 16 + c16];
     if (wave == 0 && kq == 0) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
@@ -643,10 +663,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
       }
       __syncthreads();
       }  // sketch stage
-      if (more) {  // every wave is past its reads of this tile's X
-#pragma unroll
-        for (int i = 0; i < XG; ++i) xs[i * NT + tid] = xr[i];
-      }
+      if (more) stage_x(xr);  // every wave is past its reads of this tile's X and norms
       // ---- pack: thread (token, 32-coordinate group) -> B code planes (+ the sign plane)
       if (tid < 4 * QT) {
         const int tok = tid >> 2, g = tid & 3;
@@ -712,10 +729,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
         }
       }
       __syncthreads();
-      if (more) {  // every wave is past its reads of this tile's X
-#pragma unroll
-        for (int i = 0; i < XG; ++i) xs[i * NT + tid] = xr[i];
-      }
+      if (more) stage_x(xr);  // every wave is past its reads of this tile's X and norms
       // ---- pack: thread (coordinate, 32-token block) -> B token-major code planes
       if (tid < 4 * QT) {
         const uint64_t lmask = __builtin_amdgcn_ballot_w64(lane < nv && nrm[lane] > 0.f);  // live tokens
@@ -740,6 +754,8 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
       }
     }
     // the staging buffers are reused only after the next iteration's first barrier
+    s = sn;
+    tr = trn;
   }
 }
 
@@ -962,7 +978,13 @@ hipError_t launch_gemm_store(const void *a, int a_bf16, int64_t lda, int64_t M, 
   return hipGetLastError();
 }
 
+bool search_supported(const tq_ctx *ctx, int32_t topk);
+size_t search_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int *splits_out);
+hipError_t launch_search(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_packed *keys,
+                         float *scores, int32_t topk, int32_t *top_idx, float *top_val, void *ws, hipStream_t st);
+
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int32_t want_scores) {
+  if (search_supported(ctx, topk)) return search_ws_bytes(ctx, nq, n, topk, nullptr);
   size_t b = (size_t)nq * 2 * ctx->d * sizeof(float);  // [q_rot | q_s]
   b = (b + 255) & ~(size_t)255;
   if (topk > 0 && !want_scores) b += (size_t)nq * (size_t)n * sizeof(float);
@@ -971,6 +993,7 @@ size_t scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, i
 
 hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_packed *keys,
                          float *scores, int32_t topk, int32_t *top_idx, float *top_val, void *ws, hipStream_t st) {
+  if (search_supported(ctx, topk)) return launch_search(ctx, q, is_bf16, nq, keys, scores, topk, top_idx, top_val, ws, st);
   const int d = ctx->d;
   float *qa = (float *)ws;  // [nq][2d]
   size_t off = ((size_t)nq * 2 * d * sizeof(float) + 255) & ~(size_t)255;
@@ -2251,6 +2274,473 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(streams), dim3(1024), 0, st, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Vector search (tq_scores, d a multiple of 128): the decode scheme on blocks of
+// 128 coordinates. Query side: q_rot = Pi q and q_s = S q_rot (fp32 GEMMs), then
+// fixed point relative to each query's largest |q_rot| and |q_s|, split into
+// eight balanced base-8 fp6 digits in the MFMA A layout of every block
+// (search_prep_kernel). Key side: a block's plane words become 0/1 fp4 B
+// operands (one AND each) and the Walsh masks their XORs, and
+// v_mfma_scale_f32_16x16x128_f8f6f4 gives sum_j Q_j chi_j of the block per digit
+// slot exactly. Each block's sums are folded into an fp32 score partial (the
+// Walsh weights, the query units, the QJL constant and |r|), so one block's
+// query fragments stay in registers for a whole block of keys. The top-k is
+// fused: every wave keeps the best k (score, index) of each of its queries in
+// LDS, and a merge kernel combines the key ranges; the score matrix is written
+// only when the caller asks for it.
+// ---------------------------------------------------------------------------
+
+constexpr int SW = 8;       // waves per search work-group
+constexpr int SQW = 2;      // query groups (of 4 queries) per wave
+constexpr int STB = 8;      // 16-key tiles per wave step (128 keys)
+constexpr int STS = 4;      // tiles whose key words are loaded together
+constexpr int SK_MAX = 64;  // largest fused k
+
+struct SearchArgs {
+  const float *qa;          // [nq][2d]: q_rot | q_s
+  int64_t nq, n;
+  int d, nb;                // nb = d / 128 coordinate blocks
+  uint32_t *qfrag;          // [ceil(nq/4)][nb][2 T][2 ins][64][8]: fp6 digit fragments
+  float *qunit;             // [nq][2]: units of the fixed-point q_rot, q_s
+  const uint32_t *kbits;
+  const void *knorm;
+  int nf16;
+  float qjl_scale;          // sqrt(pi/2)/m
+  const DeviceTables *tables;
+  float *scores;            // [nq][n] or NULL
+  int topk;                 // 0: no top-k
+  int splits;               // key ranges (grid y)
+  int64_t keys_per_split;   // a multiple of 16 * STB
+  float *cand_val;          // [nq][splits][topk]
+  int32_t *cand_idx;
+  int32_t *top_idx;         // [nq][topk]
+  float *top_val;
+};
+
+// One block of 256 threads per query group (4 queries): maxima, units, and the
+// digit fragments of every block of 128 coordinates, in the layout
+// decode_prep_kernel writes for d = 128: fragment (T, ins, lane) holds the 32
+// codes of row 4 * query + slot, digit 4 * ins + slot; element 8q + i (bits
+// 6(8q + i)) is coordinate 32 g + 4 i + q of the block, g = lane >> 4, scaled by
+// (1, 1/2, 1/4, 1/4)[q].
+__global__ void __launch_bounds__(256) search_prep_kernel(SearchArgs a) {
+  __shared__ float mq[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t qg = blockIdx.x;
+  const int d = a.d;
+  {
+    // wave w: query 4 qg + w
+    const int64_t q = qg * 4 + w;
+    float m0 = 0.f, m1 = 0.f;
+    if (q < a.nq) {
+      const float *row = a.qa + q * 2 * d;
+      for (int j = lane; j < d; j += 64) {
+        m0 = fmaxf(m0, fabsf(row[j]));
+        m1 = fmaxf(m1, fabsf(row[d + j]));
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      m0 = fmaxf(m0, __shfl_xor(m0, off));
+      m1 = fmaxf(m1, __shfl_xor(m1, off));
+    }
+    if (lane == 0) {
+      mq[0][w] = m0;
+      mq[1][w] = m1;
+      if (q < a.nq) {
+        a.qunit[q * 2 + 0] = m0 > 0.f ? m0 / QMAX : 0.f;
+        a.qunit[q * 2 + 1] = m1 > 0.f ? m1 / QMAX : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  constexpr uint64_t dct[3] = {digit_code_table(0), digit_code_table(1), digit_code_table(2)};
+  const int nfl = a.nb * 256;  // fragment lanes of the group: (block, T, ins, lane)
+  for (int f = tid; f < nfl; f += 256) {
+    const int cb = f >> 8, T = (f >> 7) & 1, ins = (f >> 6) & 1, Ln = f & 63;
+    const int g = Ln >> 4, row = Ln & 15, hh = row >> 2, dig = 4 * ins + (row & 3);
+    const int64_t q = qg * 4 + hh;
+    const float m = mq[T][hh];
+    const bool live = q < a.nq && m > 0.f;
+    const float sc = live ? QMAX / m : 0.f;
+    const float *src = a.qa + (live ? q : 0) * 2 * d + T * d + cb * 128 + 32 * g;
+    const uint32_t sh = 3 * dig;
+    uint32_t dw[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 x4 = *reinterpret_cast<const float4 *>(src + 4 * i);
+      const float xq[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const uint32_t z = (uint32_t)((int)rintf(xq[qq] * sc) + QOFF);
+        const uint32_t v = (z >> sh) & 7u;
+        const uint32_t code = (uint32_t)(dct[qq < 2 ? qq : 2] >> (6 * v)) & 63u;
+        const int bit = 6 * (8 * qq + i);
+        dw[bit >> 5] |= code << (bit & 31);
+        if ((bit & 31) > 26) dw[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+      }
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(a.qfrag + ((((qg * a.nb + cb) * 2 + T) * 2 + ins) * 64 + Ln) * 8);
+    dst[0] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    dst[1] = make_uint4(dw[4], dw[5], 0u, 0u);
+  }
+}
+
+// (score, index) order of the results: the higher score first, ties to the lower index
+__device__ __forceinline__ bool sbetter(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x));
+}
+
+// KB MSE bits of the keys (0: pure QJL keys), QJL: the keys carry the sign word.
+// Grid (query sets of SW * SQW groups, key ranges). Wave w of a work-group takes
+// query groups SQW (SW blockIdx.x + w) + i, i < SQW, and the work-group's key
+// range in steps of STB 16-key tiles; every wave of a work-group reads the same
+// keys at about the same time (L1 and L2 hits after the first). Per step and
+// block: the block's query fragments (registers), then per tile its key words,
+// its masks, and per query group the MFMAs and the fold into the score partial.
+// Lane (tn, G): key tn of a tile for query G of a group.
+template <int KB, bool QJL>
+__global__ void __launch_bounds__(64 * SW) search_kernel(SearchArgs a) {
+  constexpr int KM = KB > 0 ? 1 << (KB - 1) : 0;
+  constexpr int KQ = QJL ? 1 : 0;
+  constexpr int NPL = KB + KQ;
+  constexpr int NA = KM + KQ;  // masked sums per (tile, group)
+  __shared__ float lv[SW][SQW * 4][SK_MAX];
+  __shared__ int li[SW][SQW * 4][SK_MAX];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tn = lane & 15, G = lane >> 4;
+  const int64_t nqg = (a.nq + 3) >> 2;
+  const int64_t qg0 = ((int64_t)blockIdx.x * SW + w) * SQW;
+  if (qg0 >= nqg) return;  // no barriers below: every wave works alone
+  const int K = a.topk;
+  for (int i = lane; i < SQW * 4 * SK_MAX; i += 64) {
+    lv[w][i / SK_MAX][i % SK_MAX] = -INFINITY;
+    li[w][i / SK_MAX][i % SK_MAX] = INT_MAX;
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  // per group i: this lane's query, its units, the Walsh weights in query units
+  bool qlive[SQW];
+  float qs[SQW], wr[SQW][KM > 0 ? KM : 1], thr[SQW];
+  const float *wk = a.tables->walsh[KB > 0 ? KB : 1];
+#pragma unroll
+  for (int i = 0; i < SQW; ++i) {
+    const int64_t q = (qg0 + i) * 4 + G;
+    qlive[i] = qg0 + i < nqg && q < a.nq;
+    const float ur = qlive[i] ? a.qunit[q * 2] : 0.f, us = qlive[i] ? a.qunit[q * 2 + 1] : 0.f;
+    qs[i] = us * a.qjl_scale;
+#pragma unroll
+    for (int mi = 0; mi < KM; ++mi) wr[i][mi] = wk[mi] * ur;
+    thr[i] = -INFINITY;
+  }
+  const int sc0 = 127 + 3 * (lane & 3), sc1 = sc0 + 12;  // e8m0 row scales 2^(3 digit)
+  auto ldfrag = [&](int64_t qg, int cb, int T, int ins) {
+    if (qg >= nqg) qg = nqg - 1;  // an absent group repeats the last one (its scores are not used)
+    const uint4 *p = reinterpret_cast<const uint4 *>(a.qfrag + ((((qg * a.nb + cb) * 2 + T) * 2 + ins) * 64 + lane) * 8);
+    const uint4 x = p[0], y = p[1];
+    i8v v;
+    v[0] = (int)x.x; v[1] = (int)x.y; v[2] = (int)x.z; v[3] = (int)x.w;
+    v[4] = (int)y.x; v[5] = (int)y.y; v[6] = 0; v[7] = 0;
+    return v;
+  };
+  // accumulator start of every block: -sum_j Q_j per digit slot over the block (A
+  // against an all-ones mask, B scale 2^1 undoes the 1/2 of every product); the
+  // block's partial is then sum_j Q_j chi_j
+  const int W = a.d >> 5;                       // 32-coordinate groups per key
+  const uint32_t RBY = (uint32_t)(W * NPL * 4); // bytes per key record
+  const int64_t k_begin = (int64_t)blockIdx.y * a.keys_per_split;
+  const int64_t k_end = min(a.n, k_begin + a.keys_per_split);
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += 16 * STB) {
+    const int64_t ku = uniform64(k0);
+    const int rem = (int)min((int64_t)16 * STB, a.n - ku);  // keys of this step (range-checked loads)
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t *>(a.kbits) + ku * (W * NPL), (short)0, (int)(rem * RBY), 0x00020000);
+    float part[SQW][STB];
+#pragma unroll
+    for (int i = 0; i < SQW; ++i)
+#pragma unroll
+      for (int t = 0; t < STB; ++t) part[i][t] = 0.f;
+    // |r| of the lane's key in every tile (QJL keys)
+    float rho[STB];
+#pragma unroll
+    for (int t = 0; t < STB; ++t) {
+      const int64_t key = min(ku + 16 * t + tn, a.n - 1);
+      rho[t] = QJL ? load_norm(a.knorm, 2 * key + 1, a.nf16) : 0.f;
+    }
+    for (int cb = 0; cb < a.nb; ++cb) {
+      i8v ar[SQW][2], as[SQW][2];
+      f4v ir[SQW], is[SQW];
+#pragma unroll
+      for (int i = 0; i < SQW; ++i) {
+        const i8v ones = mask_fp4_01(0xFFFFFFFFu);
+        const f4v z = {0.f, 0.f, 0.f, 0.f};
+        ir[i] = z;
+        is[i] = z;
+#pragma unroll
+        for (int ins = 0; ins < 2; ++ins) {
+          ar[i][ins] = KM > 0 ? ldfrag(qg0 + i, cb, 0, ins) : i8v{};
+          as[i][ins] = QJL ? ldfrag(qg0 + i, cb, 1, ins) : i8v{};
+        }
+        if constexpr (KM > 0) {
+          ir[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ar[i][0], ones, z, 2, 4, 0, sc0, 0, 128);
+          ir[i] = -__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ar[i][1], ones, ir[i], 2, 4, 0, sc1, 0, 128);
+        }
+        if constexpr (QJL) {
+          is[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as[i][0], ones, z, 2, 4, 0, sc0, 0, 128);
+          is[i] = -__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as[i][1], ones, is[i], 2, 4, 0, sc1, 0, 128);
+        }
+      }
+#pragma unroll
+      for (int t0 = 0; t0 < STB; t0 += STS) {
+        // key words of block cb for tiles t0 .. t0 + STS - 1: group 4 cb + G of key 16 t + tn
+        uint32_t pw[STS][NPL];
+#pragma unroll
+        for (int u = 0; u < STS; ++u) {
+          const uint32_t off = (uint32_t)(16 * (t0 + u) + tn) * RBY + (uint32_t)((4 * cb + G) * NPL * 4);
+          if constexpr (NPL == 4) {
+            const auto w4 = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+            pw[u][0] = w4[0]; pw[u][1] = w4[1]; pw[u][2] = w4[2]; pw[u][3] = w4[3];
+          } else {
+#pragma unroll
+            for (int p = 0; p < NPL; ++p) pw[u][p] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + 4 * p, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < STS; ++u) {
+          const int t = t0 + u;
+          i8v sm[KB > 0 ? KB : 1];
+#pragma unroll
+          for (int p = 0; p < KB; ++p) sm[p] = mask_fp4_01(pw[u][p]);
+          i8v bm[NA > 0 ? NA : 1];
+#pragma unroll
+          for (int mi = 0; mi < NA; ++mi) bm[mi] = mi < KM ? walsh_fp4(sm, walsh_mask(KB, mi)) : mask_fp4_01(pw[u][NPL - 1]);
+#pragma unroll
+          for (int i = 0; i < SQW; ++i) {
+            f4v acc[NA > 0 ? NA : 1];
+#pragma unroll
+            for (int mi = 0; mi < NA; ++mi) {
+              const bool cm = mi < KM;
+              acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cm ? ar[i][0] : as[i][0], bm[mi],
+                                                                         cm ? ir[i] : is[i], 2, 4, 0, sc0, 0, 129);
+              acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cm ? ar[i][1] : as[i][1], bm[mi], acc[mi], 2,
+                                                                         4, 0, sc1, 0, 129);
+            }
+            float c = part[i][t];
+#pragma unroll
+            for (int mi = 0; mi < KM; ++mi) c = fmaf(wr[i][mi], (acc[mi][0] + acc[mi][1]) + (acc[mi][2] + acc[mi][3]), c);
+            if constexpr (QJL) c = fmaf(rho[t] * qs[i], (acc[KM][0] + acc[KM][1]) + (acc[KM][2] + acc[KM][3]), c);
+            part[i][t] = c;
+          }
+        }
+      }
+    }
+    // the step's scores: s = |k| * partial; the fused top-k
+#pragma unroll
+    for (int t = 0; t < STB; ++t) {
+      const int64_t key = ku + 16 * t + tn;
+      const bool kl = key < k_end;
+      const float nk = load_norm(a.knorm, (1 + KQ) * (kl ? key : a.n - 1), a.nf16);
+#pragma unroll
+      for (int i = 0; i < SQW; ++i) {
+        const float s = nk * part[i][t];
+        const bool ok = kl && qlive[i];
+        const int64_t q = (qg0 + i) * 4 + G;
+        if (a.scores && ok) a.scores[q * a.n + key] = s;
+        if (K > 0) {
+          // candidates beat their query's k-th best; the wave inserts them one at
+          // a time into the query's sorted list (keys arrive in increasing index
+          // order, so a tie with the k-th best is not a candidate)
+          uint64_t m = __builtin_amdgcn_ballot_w64(ok && s > thr[i]);
+          while (m) {
+            const int l = __builtin_ctzll(m);
+            m &= m - 1;
+            const float sv = __shfl(s, l);
+            const int ki = __shfl((int)key, l);
+            const int qq = i * 4 + (l >> 4);
+            const float ev = lane < K ? lv[w][qq][lane] : -INFINITY;
+            const int ei = lane < K ? li[w][qq][lane] : INT_MAX;
+            const int pos = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < K && sbetter(ev, ei, sv, ki)));
+            const float e2 = __shfl(ev, K >= 2 ? K - 2 : 0);
+            // every lane takes part in the shuffles (no lane reads an inactive one)
+            const float evp = __shfl_up(ev, 1);
+            const int eip = __shfl_up(ei, 1);
+            if (pos < K) {
+              if (lane > pos && lane < K) {
+                lv[w][qq][lane] = evp;
+                li[w][qq][lane] = eip;
+              }
+              if (lane == pos) {
+                lv[w][qq][lane] = sv;
+                li[w][qq][lane] = ki;
+              }
+              const float kth = (pos == K - 1 || K < 2) ? sv : e2;  // the k-th best now
+              if (G == (l >> 4)) thr[i] = kth;
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          }
+        }
+      }
+    }
+  }
+  if (K > 0) {
+    // this range's best k of each of the wave's queries
+    for (int e = lane; e < SQW * 4 * K; e += 64) {
+      const int qq = e / K, j = e - qq * K;
+      const int64_t q = qg0 * 4 + qq;
+      if (q < a.nq) {
+        const int64_t o = (q * a.splits + blockIdx.y) * K + j;
+        a.cand_val[o] = lv[w][qq][j];
+        a.cand_idx[o] = li[w][qq][j];
+      }
+    }
+  }
+}
+
+// One wave per query: the best k of its splits * k candidates by (-score, index).
+__global__ void __launch_bounds__(64) search_merge_kernel(SearchArgs a) {
+  extern __shared__ unsigned char sm_raw[];
+  const int lane = threadIdx.x;
+  const int64_t q = blockIdx.x;
+  const int K = a.topk, C = a.splits * K;
+  float *vv = reinterpret_cast<float *>(sm_raw);
+  int *ii = reinterpret_cast<int *>(vv + C);
+  for (int i = lane; i < C; i += 64) {
+    vv[i] = a.cand_val[q * C + i];
+    ii[i] = a.cand_idx[q * C + i];
+  }
+  __syncthreads();
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY;
+    int bi = INT_MAX, bp = -1;
+    for (int i = lane; i < C; i += 64)
+      if (ii[i] != INT_MAX && sbetter(vv[i], ii[i], bv, bi)) {
+        bv = vv[i];
+        bi = ii[i];
+        bp = i;
+      }
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off), op = __shfl_xor(bp, off);
+      if (sbetter(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+        bp = op;
+      }
+    }
+    if (lane == 0) {
+      a.top_val[q * K + k] = bv;
+      a.top_idx[q * K + k] = bi;
+      if (bp >= 0) ii[bp] = INT_MAX;  // taken
+    }
+    __syncthreads();
+  }
+}
+
+bool search_supported(const tq_ctx *ctx, int32_t topk) { return (ctx->d % 128) == 0 && topk <= SK_MAX; }
+
+size_t search_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int32_t topk, int *splits_out) {
+  const int d = ctx->d;
+  const int64_t nqg = (nq + 3) / 4;
+  // key ranges: about two work-groups per compute unit in all, each range at
+  // least 16 steps of 256 keys; the merge keeps at most 4096 candidates a query
+  const int64_t sets = (nqg + SW * SQW - 1) / (SW * SQW);
+  const int64_t steps = (n + 16 * STB - 1) / (16 * STB);
+  int64_t splits = std::max<int64_t>(1, std::min<int64_t>((512 + sets - 1) / sets, steps / 16));
+  if (topk > 0) splits = std::min<int64_t>(splits, 4096 / topk);
+  if (splits_out) *splits_out = (int)splits;
+  size_t b = (size_t)nq * 2 * d * sizeof(float);  // [q_rot | q_s]
+  b = (b + 255) & ~(size_t)255;
+  b += (size_t)nqg * (d / 128) * 2 * 2 * 64 * 32;  // digit fragments
+  b = (b + 255) & ~(size_t)255;
+  b += (size_t)nq * 2 * sizeof(float);  // units
+  b = (b + 255) & ~(size_t)255;
+  if (topk > 0) {
+    b += (size_t)nq * splits * topk * sizeof(float);
+    b = (b + 255) & ~(size_t)255;
+    b += (size_t)nq * splits * topk * sizeof(int32_t);
+    b = (b + 255) & ~(size_t)255;
+  }
+  return b;
+}
+
+template <int KB, bool QJL>
+static void launch_search_kernel(const SearchArgs &a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((search_kernel<KB, QJL>), grid, dim3(64 * SW), 0, st, a);
+}
+
+hipError_t launch_search(const tq_ctx *ctx, const void *q, int is_bf16, int64_t nq, const tq_packed *keys,
+                         float *scores, int32_t topk, int32_t *top_idx, float *top_val, void *ws, hipStream_t st) {
+  const int d = ctx->d;
+  int splits = 1;
+  search_ws_bytes(ctx, nq, keys->n, topk, &splits);
+  const int64_t nqg = (nq + 3) / 4;
+  char *p = (char *)ws;
+  SearchArgs a = {};
+  a.qa = (const float *)p;
+  float *qa = (float *)p;
+  p += ((size_t)nq * 2 * d * sizeof(float) + 255) & ~(size_t)255;
+  a.nq = nq;
+  a.n = keys->n;
+  a.d = d;
+  a.nb = d / 128;
+  a.qfrag = (uint32_t *)p;
+  p += ((size_t)nqg * a.nb * 2 * 2 * 64 * 32 + 255) & ~(size_t)255;
+  a.qunit = (float *)p;
+  p += ((size_t)nq * 2 * sizeof(float) + 255) & ~(size_t)255;
+  if (topk > 0) {
+    a.cand_val = (float *)p;
+    p += ((size_t)nq * splits * topk * sizeof(float) + 255) & ~(size_t)255;
+    a.cand_idx = (int32_t *)p;
+  }
+  a.kbits = keys->bits;
+  a.knorm = keys->norms;
+  a.nf16 = keys->norm_f16;
+  a.qjl_scale = (float)(std::sqrt(M_PI / 2.0) / d);
+  a.tables = ctx->d_tables;
+  a.scores = scores;
+  a.topk = topk;
+  a.splits = splits;
+  const int64_t steps = (keys->n + 16 * STB - 1) / (16 * STB);
+  a.keys_per_split = ((steps + splits - 1) / splits) * 16 * STB;
+  a.top_idx = top_idx;
+  a.top_val = top_val;
+  if (nq == 0 || keys->n == 0) return hipSuccess;
+  // q_rot = Pi q, q_s = S q_rot (fp32 MFMA GEMMs)
+  hipError_t e = launch_gemm_store(q, is_bf16, d, nq, ctx->d_rot, d, d, d, qa, 2 * d, st);
+  if (e != hipSuccess) return e;
+  if ((e = launch_gemm_store(qa, 0, 2 * d, nq, ctx->d_sketch, d, d, d, qa + d, 2 * d, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(search_prep_kernel, dim3((unsigned)nqg), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 grid((unsigned)((nqg + SW * SQW - 1) / (SW * SQW)), (unsigned)splits);
+  const int kb = keys->mse_bits;
+  if (keys->qjl) {
+    switch (kb) {
+      case 0: launch_search_kernel<0, true>(a, grid, st); break;
+      case 1: launch_search_kernel<1, true>(a, grid, st); break;
+      case 2: launch_search_kernel<2, true>(a, grid, st); break;
+      case 3: launch_search_kernel<3, true>(a, grid, st); break;
+      case 4: launch_search_kernel<4, true>(a, grid, st); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (kb) {
+      case 1: launch_search_kernel<1, false>(a, grid, st); break;
+      case 2: launch_search_kernel<2, false>(a, grid, st); break;
+      case 3: launch_search_kernel<3, false>(a, grid, st); break;
+      case 4: launch_search_kernel<4, false>(a, grid, st); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (topk > 0) {
+    const size_t shm = (size_t)splits * topk * (sizeof(float) + sizeof(int));
+    hipLaunchKernelGGL(search_merge_kernel, dim3((unsigned)nq), dim3(64), shm, st, a);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 // ---------------------------------------------------------------------------
