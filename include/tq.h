@@ -392,6 +392,18 @@ size_t tq_polar_scores_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n);
 tq_status tq_polar_scores(const tq_ctx *ctx, const void *d_q, tq_dtype dtype, int64_t nq, const tq_polar_packed *keys,
                           float *d_scores, void *d_ws, size_t ws_bytes, void *stream);
 
+/* Decode logits, a measurement aid: the query preparation and the key phase of
+ * tq_attention_decode's own kernels, which write what they would feed the
+ * softmax: d_logits[b][h][t] = scale * s_t (natural units, fp32) for t <
+ * d_seq_len[b], row stride `capacity` floats ([batch][q_heads][capacity],
+ * caller-owned; entries at t >= d_seq_len[b] are not written). s_t is the
+ * estimator of tq_attention_decode ([ebisuda] 第2段階; [gemilab] Attention機構),
+ * so this measures the accuracy of the decode path's scores directly.
+ * Contiguous caches only. d_ws: tq_attention_decode_ws_bytes() bytes.
+ * Errors: as tq_attention_decode; TQ_ERR_UNSUPPORTED for a paged cache. */
+tq_status tq_decode_logits(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_q, tq_dtype dtype,
+                           int32_t q_heads, float scale, float *d_logits, void *d_ws, size_t ws_bytes, void *stream);
+
 /* Kernel timing, a measurement aid. Arms the calling thread so that its next
  * tq_attention_decode, tq_attention_prefill or tq_decode_step records start_event on its stream
  * right before the score/attention kernel (after the query preparation) and

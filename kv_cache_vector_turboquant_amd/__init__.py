@@ -110,6 +110,8 @@ _sig("tq_attention_decode", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i3
                                      _c_sz, _c_vp])
 _sig("tq_attention_decode_noalloc", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_f32, _c_vp,
                                              _c_vp])
+_sig("tq_decode_logits", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_f32, _c_vp, _c_vp, _c_sz,
+                                  _c_vp])
 _sig("tq_attention_prefill_ws_bytes", _c_sz, [_c_vp, ctypes.POINTER(CCache), _c_i32, _c_i32])
 _sig("tq_attention_prefill", _c_i32, [_c_vp, ctypes.POINTER(CCache), _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                       _c_vp, _c_vp, _c_sz, _c_vp])
@@ -123,7 +125,7 @@ EXPORTED_SYMBOLS = [
     "tq_format_version", "tq_gaussian_matrix", "tq_ctx_create_seeded",
     "tq_codebook_build", "tq_angle_codebook_build", "tq_rotation_build", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim", "tq_ctx_export", "tq_ctx_codebook",
     "tq_quantize_ws_bytes", "tq_quantize_kv", "tq_cache_write", "tq_append_token", "tq_attention_decode_ws_bytes",
-    "tq_attention_decode", "tq_attention_decode_noalloc", "tq_attention_prefill_ws_bytes", "tq_attention_prefill", "tq_decode_step_ws_bytes",
+    "tq_attention_decode", "tq_attention_decode_noalloc", "tq_decode_logits", "tq_attention_prefill_ws_bytes", "tq_attention_prefill", "tq_decode_step_ws_bytes",
     "tq_decode_step", "tq_time_next_decode", "tq_read_probe",
     "tq_scores_ws_bytes", "tq_scores", "tq_polar_quantize_ws_bytes", "tq_polar_quantize", "tq_polar_scores_ws_bytes",
     "tq_polar_scores", "tq_polar_attention_decode_ws_bytes", "tq_polar_attention_decode", "tq_last_error",
@@ -498,6 +500,23 @@ class KVCache:
         cc = self.c()
         _check(_lib.tq_attention_decode(ctx.handle, ctypes.byref(cc), q.data_ptr(), _dtype_code(q), Hq,
                                         float(scale), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr()))
+        return out
+
+    def decode_logits(self, ctx: Context, q, scale: float | None = None, ws=None):
+        """Measurement: the decode kernels' logits scale * s_t, fp32 [batch, q_heads,
+        capacity] (entries past each sequence's length are NaN)."""
+        torch = _torch()
+        assert q.is_contiguous()
+        B, Hq, d = q.shape
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        out = torch.full((B, Hq, self.capacity), float("nan"), dtype=torch.float32, device=q.device)
+        need = self.decode_ws_bytes(ctx, Hq)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+        cc = self.c()
+        _check(_lib.tq_decode_logits(ctx.handle, ctypes.byref(cc), q.data_ptr(), _dtype_code(q), Hq, float(scale),
+                                     out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr()))
         return out
 
     def prefill_ws_bytes(self, ctx: Context, n_q: int, q_heads: int) -> int:

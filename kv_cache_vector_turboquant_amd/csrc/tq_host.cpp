@@ -808,6 +808,30 @@ tq_status tq_attention_decode_noalloc(const tq_ctx *ctx, const tq_kv_cache *cach
   return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 
+tq_status tq_decode_logits(const tq_ctx *ctx, const tq_kv_cache *cache, const void *d_q, tq_dtype dtype,
+                           int32_t q_heads, float scale, float *d_logits, void *d_ws, size_t ws_bytes, void *stream) {
+  const char *fn = "tq_decode_logits";
+  hipEvent_t ev[2];
+  take_decode_events(ev);
+  if (!ctx) return fail(TQ_ERR_ARG, "tq_decode_logits: NULL ctx");
+  tq_status s = check_cache(ctx, cache, fn);
+  if (s != TQ_OK) return s;
+  if (!d_q || !d_logits) return fail(TQ_ERR_ARG, "tq_decode_logits: NULL query or output");
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_ERR_ARG, "tq_decode_logits: dtype must be TQ_F32 or TQ_BF16");
+  if (q_heads <= 0 || (q_heads % cache->kv_heads) != 0)
+    return fail(TQ_ERR_ARG, "tq_decode_logits: q_heads must be a positive multiple of kv_heads");
+  if (q_heads / cache->kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_logits: at most 16 query heads per KV head");
+  if (ctx->d != 128) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_logits: d must be 128");
+  if (cache->d_block_table) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_logits: contiguous caches only");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_ARG, "tq_decode_logits: scale must be finite");
+  size_t need = tq_attention_decode_ws_bytes(ctx, cache, q_heads);
+  if (!d_ws || ws_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_decode_logits: workspace smaller than tq_attention_decode_ws_bytes()");
+  if ((s = check_device(ctx, fn)) != TQ_OK) return s;
+  hipError_t e = launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, nullptr, d_ws, (hipStream_t)stream,
+                               nullptr, nullptr, ev[0], ev[1], 1, 0, nullptr, 0, d_logits);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
+}
+
 size_t tq_attention_prefill_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t n_q, int32_t q_heads) {
   if (!ctx || !cache || n_q <= 0 || q_heads <= 0 || cache->kv_heads <= 0 || (q_heads % cache->kv_heads) != 0) return 0;
   return decode_ws_bytes(ctx, cache, q_heads, nullptr, nullptr, n_q);

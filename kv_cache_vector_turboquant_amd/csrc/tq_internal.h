@@ -94,10 +94,14 @@ size_t decode_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_he
 // With ext non-NULL the logits (log2 units, [stream*hgroups][4][ext_stride]) are
 // given: keys in another format, scored beforehand; q is unused and only the
 // cache's values and lengths are read (contiguous layout, fp32 norms).
+// With logits non-NULL (measurement, contiguous caches) only the query
+// preparation and the key phase run: logits[b][i][h][t] = scale * s_t for the
+// visible tokens (row stride = capacity), and out is not written.
 hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
                          float scale, float *out, void *ws, hipStream_t st, const void *k_new = nullptr,
                          const void *v_new = nullptr, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
-                         int n_q = 1, int causal = 0, const float *ext = nullptr, int64_t ext_stride = 0);
+                         int n_q = 1, int causal = 0, const float *ext = nullptr, int64_t ext_stride = 0,
+                         float *logits = nullptr);
 hipError_t launch_read_probe(const void *src, size_t bytes, int grid, uint32_t *sink, hipStream_t st);
 // C[M][N] = A[M][K] B[N][K]^T on fp32 MFMA (A fp32 or bf16, B fp32; row strides in elements)
 hipError_t launch_gemm_store(const void *a, int a_bf16, int64_t lda, int64_t M, const float *b, int64_t ldb,

@@ -30,7 +30,7 @@ hipError_t launch_append(const tq_ctx *, const tq_kv_cache *, const void *, cons
 }
 hipError_t launch_decode(const tq_ctx *, const tq_kv_cache *, const void *, int, int32_t, float, float *, void *,
                          hipStream_t, const void *, const void *, hipEvent_t, hipEvent_t, int, int, const float *,
-                         int64_t) { return hipErrorNotSupported; }
+                         int64_t, float *) { return hipErrorNotSupported; }
 hipError_t launch_read_probe(const void *, size_t, int, uint32_t *, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_gemm_store(const void *, int, int64_t, int64_t, const float *, int64_t, int64_t, int, float *, int64_t,
                              hipStream_t) { return hipErrorNotSupported; }

@@ -55,7 +55,7 @@ CHILD = textwrap.dedent(r"""
     assert lib.tq_ctx_create_seeded(100, 0, ctypes.byref(vp())) != 0
     for fn in ("tq_attention_decode", "tq_decode_step", "tq_quantize_kv", "tq_scores", "tq_append_token",
                "tq_attention_decode_noalloc", "tq_attention_prefill", "tq_cache_write", "tq_polar_quantize",
-               "tq_polar_scores", "tq_polar_attention_decode"):
+               "tq_polar_scores", "tq_polar_attention_decode", "tq_decode_logits"):
         f = getattr(lib, fn)
         f.restype = i32
         assert f(*([None] * 14)) != 0, fn
