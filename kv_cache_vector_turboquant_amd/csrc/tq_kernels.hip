@@ -759,319 +759,25 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   }
 }
 
-// Keys, software-pipelined over the work-group's tiles (eight waves, wave w owns
-// output coordinates and sketch rows 16 w .. 16 w + 15). The per-tile work is the
-// same as quant128_kernel<true, ...>; the order differs so that each wave's
-// matrix-core work overlaps its vector work of another tile:
-//   phase A: product 1 of tile k+1 (MFMA)  with  codes/residuals of tile k and
-//            the sketch signs of tile k-1 (VALU)
-//   phase B: product 2 of tile k (MFMA)    with  packing of tile k-1 and the
-//            staging of tile k+2's X
-// X, the staged code words, the norms and the residual norms are double-buffered
-// in LDS by tile parity; the loop is unrolled by two so that the double-buffered
-// accumulators have constant indices. Phase A's two streams are independent
-// instructions of one basic block, so the compiler interleaves them.
-template <int B, bool QJL>
-__global__ void __launch_bounds__(512) quant128_keys_kernel(Q128Args a) {
-  constexpr int NW = 8, NT = 512, XG = QT * 16 / NT;
-  constexpr bool SK = QJL;
-  constexpr int NPL = B + (SK ? 1 : 0);
-  constexpr int H = B > 0 ? 1 << (B - 1) : 1;
-  __shared__ __attribute__((aligned(16))) uint4 xs[2][QT * 16];
-  __shared__ __attribute__((aligned(16))) uint32_t stage[2][QT * QD / 4];
-  __shared__ __attribute__((aligned(16))) uint16_t rt[SK ? 2 : 1][SK ? QT * QD : 8];
-  __shared__ float ssq[2][QT], nrm[2][QT];
-  __shared__ float rho2[2][NW][QT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c16 = lane & 15, kq = lane >> 4;
-  const int64_t tps = (a.n_tokens + QT - 1) / QT, total = tps * a.n_streams;
-  const int64_t G = gridDim.x;
-  if ((int64_t)blockIdx.x >= total) return;
-  const int64_t ntw = (total - blockIdx.x + G - 1) / G;  // this work-group's tiles: blockIdx.x + k G
-  float tp[H > 1 ? H - 1 : 1], cm[H];
-  if constexpr (B > 0) {
-#pragma unroll
-    for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
-#pragma unroll
-    for (int j = 0; j < H; ++j) cm[j] = a.tables->centroid[B][H + j];
-  }
-  bf16x8 pf[4][3];
-  bf16x8 sf[SK ? 4 : 1][2];
-  {
-    const int r = 16 * wave + c16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int sp = 0; sp < 3; ++sp) pf[ks][sp] = ld_bf8(a.rot3 + (sp * QD + r) * QD + ks * 32 + kq * 8);
-      if constexpr (SK) {
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) sf[ks][sp] = ld_bf8(a.sk2 + (sp * QD + r) * QD + ks * 32 + kq * 8);
-      }
-    }
-  }
-  auto code = [&](float y, uint32_t &idx) {
-    const float ay = fabsf(y);
-    uint32_t mag = 0;
-    float c = cm[0];
-#pragma unroll
-    for (int j = 0; j < H - 1; ++j) {
-      const bool ge = ay >= tp[j];
-      mag = ge ? (uint32_t)(j + 1) : mag;
-      c = ge ? cm[j + 1] : c;
-    }
-    idx = ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
-    return __builtin_copysignf(c, y);
-  };
-  // (stream, tile in the stream) of tile k; tiles advance by the grid size
-  const int64_t dS = G / tps, dR = G % tps;
-  auto adv = [&](int64_t &s, int64_t &r) {
-    s += dS;
-    r += dR;
-    if (r >= tps) {
-      r -= tps;
-      ++s;
-    }
-  };
-  auto x_granule = [&](int64_t st, int64_t tt0, int P) {
-    const int last = (int)min((int64_t)QT, a.n_tokens - tt0) - 1;
-    const int t = P >> 4, g = (P & 15) ^ (t & 15);
-    return *reinterpret_cast<const uint4 *>(a.x + st * a.xs + (tt0 + min(t, last)) * a.xt + g * 8);
-  };
-  auto stage_x = [&](int buf, const uint4 (&v)[XG]) {
-#pragma unroll
-    for (int i = 0; i < XG; ++i) {
-      xs[buf][i * NT + tid] = v[i];
-      float q = sumsq8(__builtin_bit_cast(bf16x8, v[i]), 0.f);
-      q += __shfl_xor(q, 1);
-      q += __shfl_xor(q, 2);
-      q += __shfl_xor(q, 4);
-      q += __shfl_xor(q, 8);
-      if ((tid & 15) == 0) ssq[buf][(i * NT + tid) >> 4] = q;
-    }
-  };
-  // product 1 of the tile in xs[buf]: acc[tb][r] = |x| y[coordinate 16 w + 4 kq + r][token 16 tb + c16]
-  auto product1 = [&](int buf, f4v (&acc)[4]) {
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) acc[tb] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 xf[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int t = tb * 16 + c16;
-        xf[tb] = __builtin_bit_cast(bf16x8, xs[buf][t * 16 + ((ks * 4 + kq) ^ (t & 15))]);
-      }
-#pragma unroll
-      for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-          acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ks][sp], xf[tb], acc[tb], 0, 0, 0);
-    }
-  };
-  // codes and residuals of a tile from its product 1 (buffer buf of the staged words)
-  auto epilogue1 = [&](int buf, const f4v (&acc)[4]) {
-    float rp[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int tok = tb * 16 + c16;
-      const float ss = ssq[buf][tok];
-      nrm[buf][tok] = sqrtf(ss);  // every lane of the token stores the same value (no branch)
-      const float inv = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
-      const int c0 = 16 * wave + 4 * kq;
-      uint32_t bytes = 0, hi2[2], lo2[2];
-      float res[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float y = acc[tb][r] * inv;
-        uint32_t idx = 0;
-        res[r] = B > 0 ? y - code(y, idx) : y;
-        bytes |= idx << (7 * r);
-        if constexpr (SK) rp[tb] = fmaf(res[r], res[r], rp[tb]);
-      }
-      stage[buf][swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
-      if constexpr (SK) {
-        split2(res[0], res[1], hi2[0], lo2[0]);
-        split2(res[2], res[3], hi2[1], lo2[1]);
-        const int gr = swz(tok, 16, c0 >> 3, 15) * 8 + ((c0 >> 2) & 1) * 4;
-        *reinterpret_cast<uint2 *>(&rt[0][gr]) = make_uint2(hi2[0], hi2[1]);
-        *reinterpret_cast<uint2 *>(&rt[1][gr]) = make_uint2(lo2[0], lo2[1]);
-      }
-    }
-    if constexpr (SK) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        rp[tb] += __shfl_xor(rp[tb], 16);
-        rp[tb] += __shfl_xor(rp[tb], 32);
-      }
-      // the four kq lanes of a token hold the same sum: all store it (no branch)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) rho2[buf][wave][tb * 16 + c16] = rp[tb];
-    }
-  };
-  // product 2: z[sketch row 16 w + 4 kq + r][token 16 tb + c16] = S r
-  auto product2 = [&](f4v (&acc)[4]) {
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) acc[tb] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int gg = swz(tb * 16 + c16, 16, ks * 4 + kq, 15) * 8;
-        const bf16x8 rh = ld_bf8(&rt[0][gg]), rl = ld_bf8(&rt[1][gg]);
-        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][0], rh, acc[tb], 0, 0, 0);
-        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][0], rl, acc[tb], 0, 0, 0);
-        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][1], rh, acc[tb], 0, 0, 0);
-      }
-    }
-  };
-  // the signs of product 2 into bit 6 of the staged code fields
-  auto epilogue2 = [&](int buf, const f4v (&acc)[4]) {
-    const int c0 = 16 * wave + 4 * kq;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int tok = tb * 16 + c16;
-      uint32_t sg = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sg |= (acc[tb][r] >= 0.f ? (1u << QJL_FIELD_BIT) : 0u) << (7 * r);
-      atomicOr(&stage[buf][swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)], sg);
-    }
-  };
-  // records of the tile at token t0 of stream s from the staged words of buffer buf
-  auto pack = [&](int buf, int64_t s, int64_t t0) {
-    const int nv = (int)min((int64_t)QT, a.n_tokens - t0);
-    if (tid < 4 * QT) {
-      const int tok = tid >> 2, g = tid & 3;
-      if (tok < nv) {
-        const int64_t rec = a.map.rec(s, t0 + tok);
-        const float n = nrm[buf][tok];
-        uint32_t w[NPL];
-        if (n > 0.f) {
-          const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[buf][swz(tok, 8, 2 * g, 7) * 4]);
-          const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[buf][swz(tok, 8, 2 * g + 1, 7) * 4]);
-          const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-          for (int p = 0; p < NPL; ++p) {
-            const int bit = p < B ? p : QJL_FIELD_BIT;
-            uint32_t word = 0;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) word |= gather4(d8[m], bit) << (4 * m);
-            w[p] = word;
-          }
-        } else {
-#pragma unroll
-          for (int p = 0; p < NPL; ++p) w[p] = 0u;
-        }
-        uint32_t *dst = a.bits_out + (rec * QW + g) * NPL;
-        if constexpr (NPL == 4) {
-          *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-#pragma unroll
-          for (int p = 0; p < NPL; ++p) dst[p] = w[p];
-        }
-        if (g == 0) {
-          if constexpr (SK) {
-            float r2 = 0.f;
-#pragma unroll
-            for (int v = 0; v < NW; ++v) r2 += rho2[buf][v][tok];
-            store_norm(a.norms_out, 2 * rec, n, a.nf16);
-            store_norm(a.norms_out, 2 * rec + 1, n > 0.f ? sqrtf(r2) : 0.f, a.nf16);
-          } else {
-            store_norm(a.norms_out, rec, n, a.nf16);
-          }
-        }
-      }
-    }
-  };
-
-  // prologue: X of tiles 0 and 1 staged, tile 2's X in flight, product 1 of tile 0
-  int64_t sP = blockIdx.x / tps, rP = blockIdx.x % tps;  // tile k - 1 (packed in iteration k)
-  int64_t sL = sP, rL = rP;                              // the next tile whose X is loaded
-  uint4 xr[XG];
-#pragma unroll
-  for (int i = 0; i < XG; ++i) xr[i] = x_granule(sL, rL * QT, i * NT + tid);
-  stage_x(0, xr);
-  adv(sL, rL);
-  if (ntw > 1) {
-#pragma unroll
-    for (int i = 0; i < XG; ++i) xr[i] = x_granule(sL, rL * QT, i * NT + tid);
-    stage_x(1, xr);
-  }
-  adv(sL, rL);
-  if (ntw > 2) {
-#pragma unroll
-    for (int i = 0; i < XG; ++i) xr[i] = x_granule(sL, rL * QT, i * NT + tid);
-  }
-  adv(sL, rL);  // now tile 3
-  __syncthreads();
-  f4v acc1a[4], acc1b[4], acc2[4];
-  product1(0, acc1a);
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) acc2[tb] = f4v{0.f, 0.f, 0.f, 0.f};
-
-  // iteration k with tile k's product 1 in CUR (buffer parity CB), tile k+1's X in xs[CB ^ 1]
-  auto iteration = [&](int64_t k, auto CB, f4v (&cur)[4], f4v (&nxt)[4]) {
-    constexpr int cb = decltype(CB)::value, nb = cb ^ 1;
-    // phase A: product 1 of tile k + 1 (its result unused past the last tile) with
-    // the codes of tile k and the signs of tile k - 1
-    product1(nb, nxt);
-    epilogue1(cb, cur);
-    if constexpr (SK) epilogue2(nb, acc2);  // tile k - 1 (k = 0: into the unused buffer, rewritten later)
-    __syncthreads();
-    // phase B: product 2 of tile k with the packing of tile k - 1 and the staging of
-    // tile k + 2's X (its loads were issued one iteration earlier)
-    if constexpr (SK) product2(acc2);
-    if (k >= 1) {
-      pack(nb, sP, rP * QT);
-      adv(sP, rP);
-    }
-    if (k + 2 < ntw) {
-      stage_x(cb, xr);
-      if (k + 3 < ntw) {
-#pragma unroll
-        for (int i = 0; i < XG; ++i) xr[i] = x_granule(sL, rL * QT, i * NT + tid);
-      }
-      adv(sL, rL);
-    }
-    __syncthreads();
-  };
-  int64_t k = 0;
-  for (;;) {
-    iteration(k, std::integral_constant<int, 0>(), acc1a, acc1b);
-    if (++k >= ntw) break;
-    iteration(k, std::integral_constant<int, 1>(), acc1b, acc1a);
-    if (++k >= ntw) break;
-  }
-  // epilogue: the signs and the records of the last tile
-  const int lb = (int)((ntw - 1) & 1);
-  if constexpr (SK) {
-    epilogue2(lb, acc2);
-    __syncthreads();
-  }
-  pack(lb, sP, rP * QT);
-}
-
 // Persistent launch: as many work-groups as fit on the device at once (registers
 // decide: keys one per compute unit, values two), at most one per tile.
 template <bool KEYS, int B, bool QJL>
 static hipError_t launch_quant128_b(const Q128Args &q, hipStream_t st) {
   constexpr int NW = KEYS ? 8 : 4;
-  // keys: the software-pipelined kernel; values: the phase-ordered one
-  const void *kern = KEYS ? reinterpret_cast<const void *>(&quant128_keys_kernel<B, QJL>)
-                          : reinterpret_cast<const void *>(&quant128_kernel<KEYS, B, NW, QJL>);
   static int resident = 0;  // work-groups resident on the device
   if (resident == 0) {
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e;
     if ((e = hipGetDevice(&dev)) != hipSuccess ||
         (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess ||
-        (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * NW, 0)) != hipSuccess)
+        (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant128_kernel<KEYS, B, NW, QJL>, 64 * NW, 0)) !=
+            hipSuccess)
       return e;
     resident = std::max(1, cus * std::max(1, per_cu));
   }
   const int64_t tiles = ((q.n_tokens + QT - 1) / QT) * q.n_streams;
   const unsigned nwg = (unsigned)std::min<int64_t>(tiles, resident);
-  if constexpr (KEYS) hipLaunchKernelGGL((quant128_keys_kernel<B, QJL>), dim3(nwg), dim3(512), 0, st, q);
-  else hipLaunchKernelGGL((quant128_kernel<KEYS, B, NW, QJL>), dim3(nwg), dim3(64 * NW), 0, st, q);
+  hipLaunchKernelGGL((quant128_kernel<KEYS, B, NW, QJL>), dim3(nwg), dim3(64 * NW), 0, st, q);
   return hipGetLastError();
 }
 
