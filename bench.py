@@ -533,13 +533,14 @@ def run_prefill(args, torch, tq, synth):
     pairs_chunk = [B * H * sum(j * C + i + 1 for i in range(C)) for j in range(nch)]
     call_ms = np.array([ms(c) for c, _ in kev])
     kern_ms = np.array([ms(k) for _, k in kev])
-    # MFMA work of decode_kernel per 16 tokens x 4 virtual heads: (Walsh masks + sign
-    # mask) x 2 digit halves of 16x16x128 fp6 x fp4 MFMAs; per 128 tokens x 4 heads
-    # the values take (2 + 2 x 2 x value masks) 16x16x64 int8 MFMAs per wave x 4 waves
+    # MFMA work of prefill_kernel (16 virtual heads per work-group): per 16 tokens
+    # x 16 heads, (Walsh masks + sign mask) x 6 query digits of 16x16x128 fp6 x fp4
+    # MFMAs; per 512 tokens x 16 heads, 4 waves x 2 coordinate halves x 4 groups x
+    # value masks x 4 weight digits x 2 (token halves) 16x16x64 int8 MFMAs
     km = (1 << (kbits - 1)) if kbits > 0 else 0
     vm = 1 << (vbits - 1)
-    k_ops = (km + int(kqjl)) * 2 * 16 * 16 * 128 * 2 / (16 * 4)         # per (virtual head, token)
-    v_ops = 4 * (2 + 4 * vm) * 16 * 16 * 64 * 2 / (128 * 4)
+    k_ops = (km + int(kqjl)) * 6 * 16 * 16 * 128 * 2 / (16 * 16)        # per (virtual head, token)
+    v_ops = 4 * 2 * 4 * vm * 4 * 2 * 16 * 16 * 64 * 2 / (512 * 16)
     vheads = Hq // H
     vh_tokens = np.array([p * vheads for p in pairs_chunk], dtype=np.float64)
     tput = vh_tokens * (k_ops + v_ops) / (kern_ms / 1e3) / 1e12
@@ -564,9 +565,9 @@ def run_prefill(args, torch, tq, synth):
         "attend_call_ms": call_ms.tolist(), "attend_kernel_ms": kern_ms.tolist(),
         "roofline": {"bound": "mfma", "achieved": float(tput[-1]), "peak": mix_peak, "unit": "TFLOP/s",
                      "frac": float(tput[-1]) / mix_peak, "traffic": None,
-                     "kernel": f"decode_kernel<{kbits}, {vbits}, {str(kqjl).lower()}, false, false> on the last chunk "
+                     "kernel": f"prefill_kernel<{kbits}, {vbits}, {str(kqjl).lower()}> on the last chunk "
                                f"({P} tokens visible to its last position; template arguments: key MSE bits, value "
-                               "bits, QJL signs, chunks spanning several pages, fp16 norms)",
+                               "bits, QJL signs)",
                      "ops_per_vhead_token": k_ops + v_ops, "k_ops_per_vhead_token": k_ops,
                      "v_ops_per_vhead_token": v_ops, "avg_launch_ms": float(kern_ms[-1]),
                      "peak_note": ("executed exact-digit MFMA work (fp6 x fp4 score MFMAs, int8 value MFMAs) "
@@ -574,7 +575,7 @@ def run_prefill(args, torch, tq, synth):
                      "algorithmic_fp32_tflops": float(alg[-1]), "algorithmic_fp32_frac": float(alg[-1]) / FP32_PEAK_TFLOPS,
                      "algorithmic_note": ("4 d flops per (virtual head, visible token): the score's and the value "
                                           "sum's dot products at fp32 accuracy, against the 157.3 TFLOP/s fp32 peak"),
-                     "timing": "HIP events on the launch stream around each chunk's decode_kernel launch"},
+                     "timing": "HIP events on the launch stream around each chunk's prefill_kernel launch"},
     }
     if not args.no_cpu_baseline:
         rate, chunks, secs = oracle_prefill_rate(d, 2048, 64, Hq // H, kbits, vbits, args.cpu_seconds, args.data,

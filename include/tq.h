@@ -317,8 +317,12 @@ tq_status tq_attention_decode_noalloc(const tq_ctx *ctx, const tq_kv_cache *cach
  * tokens already appended, each position sees itself and what precedes it).
  * A query with no visible token gets a zero output.
  * d_q: [batch][n_q][q_heads][d]; d_out: fp32 [batch][n_q][q_heads][d]. q_heads
- * a multiple of kv_heads. Same kernels as decode, with n_q * group virtual
- * heads per KV head. d_ws: workspace of tq_attention_prefill_ws_bytes() bytes.
+ * a multiple of kv_heads; the n_q * group (query position, head) pairs of a KV
+ * head are its virtual heads. With at least 16 of them, n_q >= 2, values of at
+ * most 3 bits and a contiguous cache (or pages of a multiple of 512 tokens) a
+ * prefill kernel scores 16 virtual heads per work-group; otherwise the decode
+ * kernels run over groups of 4. d_ws: workspace of
+ * tq_attention_prefill_ws_bytes() bytes.
  * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d != 128, group > 16),
  * TQ_ERR_CAPACITY (workspace), TQ_ERR_HIP. */
 size_t tq_attention_prefill_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t n_q, int32_t q_heads);

@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq_host.cpp", "tq_kernels.hip", "polar_kernels.hip"]
+SOURCES = ["tq_host.cpp", "tq_kernels.hip", "polar_kernels.hip", "prefill_kernels.hip"]
 
 # Packed FP32 VALU ops are disabled for device code; the host pass warns that
 # it does not know the feature, which is harmless. MFMA results go to ordinary

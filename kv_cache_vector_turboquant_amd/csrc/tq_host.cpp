@@ -834,6 +834,7 @@ tq_status tq_decode_logits(const tq_ctx *ctx, const tq_kv_cache *cache, const vo
 
 size_t tq_attention_prefill_ws_bytes(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t n_q, int32_t q_heads) {
   if (!ctx || !cache || n_q <= 0 || q_heads <= 0 || cache->kv_heads <= 0 || (q_heads % cache->kv_heads) != 0) return 0;
+  if (prefill_supported(ctx, cache, q_heads, n_q)) return prefill_ws_bytes(cache, q_heads, n_q);
   return decode_ws_bytes(ctx, cache, q_heads, nullptr, nullptr, n_q);
 }
 
@@ -857,9 +858,13 @@ tq_status tq_attention_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, cons
     return fail(TQ_ERR_UNSUPPORTED, "tq_attention_prefill: at most 2^20 query heads per KV head");
   if (ctx->d != 128) return fail(TQ_ERR_UNSUPPORTED, "tq_attention_prefill: d must be 128");
   if (!std::isfinite(scale)) return fail(TQ_ERR_ARG, "tq_attention_prefill: scale must be finite");
+  // contiguous caches with at least 16 virtual heads per KV head and values of
+  // at most 3 bits: the prefill kernel (16 virtual heads per work-group);
+  // otherwise the decode kernels over groups of 4 virtual heads
+  const bool pf = prefill_supported(ctx, cache, q_heads, n_q);
   {
-    // one 256-thread work-group per (chunk, KV stream, group of 4 virtual heads):
-    // the 1-D grid must stay below 2^32 work-items
+    // one 256-thread work-group per (chunk, KV stream, group of 4 or 16 virtual
+    // heads): the 1-D grid must stay below 2^32 work-items
     int chunk = 0, nchunks = 0;
     decode_ws_bytes(ctx, cache, q_heads, &chunk, &nchunks, n_q);
     const int64_t units = (int64_t)cache->batch * cache->kv_heads * (((int64_t)n_q * (q_heads / cache->kv_heads) + 3) / 4);
@@ -869,8 +874,10 @@ tq_status tq_attention_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, cons
   size_t need = tq_attention_prefill_ws_bytes(ctx, cache, n_q, q_heads);
   if (!d_ws || ws_bytes < need) return fail(TQ_ERR_CAPACITY, "tq_attention_prefill: workspace smaller than tq_attention_prefill_ws_bytes()");
   if ((s = check_device(ctx, fn)) != TQ_OK) return s;
-  hipError_t e = launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream,
-                               nullptr, nullptr, ev[0], ev[1], n_q, causal);
+  hipError_t e = pf ? launch_prefill(ctx, cache, d_q, dtype == TQ_BF16, q_heads, n_q, causal, scale, d_out, d_ws,
+                                     (hipStream_t)stream, ev[0], ev[1])
+                    : launch_decode(ctx, cache, d_q, dtype == TQ_BF16, q_heads, scale, d_out, d_ws, (hipStream_t)stream,
+                                    nullptr, nullptr, ev[0], ev[1], n_q, causal);
   return e == hipSuccess ? TQ_OK : hip_fail(e, fn);
 }
 

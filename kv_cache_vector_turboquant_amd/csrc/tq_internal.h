@@ -102,6 +102,18 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
                          const void *v_new = nullptr, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
                          int n_q = 1, int causal = 0, const float *ext = nullptr, int64_t ext_stride = 0,
                          float *logits = nullptr);
+// Log-sum-exp merge of per-chunk attention partials ([stream][n_q * group][nchunks][d + 2]:
+// rotated output, max logit in log2 units, weight sum) and o = Pi^T o_rot into
+// out [batch][n_q][q_heads][d].
+hipError_t launch_merge_partials(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int n_q,
+                                 float *partial, int nchunks, float *out, hipStream_t st);
+// Prefill attention with sixteen virtual heads per work-group (prefill_kernels.hip):
+// contiguous caches, d = 128, value bits <= 3 and n_q * group >= 16.
+bool prefill_supported(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int n_q);
+size_t prefill_ws_bytes(const tq_kv_cache *cache, int32_t q_heads, int n_q);
+hipError_t launch_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
+                          int n_q, int causal, float scale, float *out, void *ws, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1);
 hipError_t launch_read_probe(const void *src, size_t bytes, int grid, uint32_t *sink, hipStream_t st);
 // C[M][N] = A[M][K] B[N][K]^T on fp32 MFMA (A fp32 or bf16, B fp32; row strides in elements)
 hipError_t launch_gemm_store(const void *a, int a_bf16, int64_t lda, int64_t M, const float *b, int64_t ldb,

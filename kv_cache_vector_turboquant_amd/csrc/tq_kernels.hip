@@ -30,6 +30,7 @@
 #include <cmath>
 #include <mutex>
 
+#include "tq_device.h"
 #include "tq_internal.h"
 #include <hip/hip_fp16.h>
 
@@ -46,10 +47,6 @@ __device__ __forceinline__ float load_norm(const void *base, int64_t i, int f16)
 }
 
 typedef float f16v __attribute__((ext_vector_type(16)));
-typedef int i4v __attribute__((ext_vector_type(4)));
-typedef float f4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // ---------------------------------------------------------------------------
 // GEMM: C[M][N] = A[M][K] . B[N][K]^T, fp32 MFMA, 64x128 tiles, BK = 16.
@@ -1080,10 +1077,7 @@ hipError_t launch_scores(const tq_ctx *ctx, const void *q, int is_bf16, int64_t 
 // are exact, and o = unit * sum_S w_S (2 M_S - sum_t E_t) in double.
 // ---------------------------------------------------------------------------
 
-constexpr int DD = 128;            // head dim
-constexpr int DW = DD / 32;        // 32-coordinate groups
 constexpr float QMAX = 7190000.f;  // |fixed-point query| bound with 8 signed base-8 digits in [-4, 3]
-typedef int i8v __attribute__((ext_vector_type(8)));
 constexpr float WSCALE = 536870912.f;  // 2^29: fixed point of the value weights
 constexpr int KTPW = 2;            // key tiles (16 tokens each) per wave per round (double-buffered)
 constexpr int VGPI = 2;            // 128-token value groups per iteration
@@ -1134,10 +1128,6 @@ struct DecodeArgs {
   int64_t logit_stride;
 };
 
-// The i-th odd-cardinality subset of the B planes, ordered by (popcount, value).
-__host__ __device__ constexpr int walsh_mask(int B, int i) {
-  return i < B ? (1 << i) : (B == 3 ? 7 : (i == 4 ? 7 : i == 5 ? 11 : i == 6 ? 13 : 14));
-}
 
 template <typename QT>
 __device__ __forceinline__ float qload(const QT *q, int64_t i) {
@@ -1460,18 +1450,6 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
   }
 }
 
-// Value B bytes of a token-major plane word: byte k' of dword q is bit q + 8k'
-// of m, left in place (value b * 2^q; -128 b for q = 7).
-__device__ __forceinline__ void mask_bytes_pow2(uint32_t m, i4v &lo, i4v &hi) {
-  lo[0] = (int)(m & 0x01010101u);
-  lo[1] = (int)(m & 0x02020202u);
-  lo[2] = (int)(m & 0x04040404u);
-  lo[3] = (int)(m & 0x08080808u);
-  hi[0] = (int)(m & 0x10101010u);
-  hi[1] = (int)(m & 0x20202020u);
-  hi[2] = (int)(m & 0x40404040u);
-  hi[3] = (int)(m & 0x80808080u);
-}
 
 // Key B operand of a 32-coordinate plane word: element 8q + i (nibble i of
 // dword q) is bit 4i + q of w as a 0/1 fp4 value scaled by 0.5, 1, 2, 2 for
@@ -1486,35 +1464,8 @@ __device__ __forceinline__ i8v mask_fp4_01(uint32_t w) {
   return b;
 }
 
-// fp4 B operand of a Walsh mask from the B operands of the single planes: the AND
-// masks commute with XOR, so each dword is the XOR of the planes' dwords
-// (S is one of the odd subsets of at most four planes that walsh_mask lists:
-// one plane or three; three take one three-input XOR per dword)
-__host__ __device__ constexpr int nth_plane(int S, int k) {
-  for (int p = 0; p < 4; ++p)
-    if (S & (1 << p)) {
-      if (k == 0) return p;
-      --k;
-    }
-  return 0;
-}
 
-template <int NP>
-__device__ __forceinline__ i8v walsh_fp4(const i8v (&sm)[NP], int S) {
-  if (__builtin_popcount(S) == 1) return sm[nth_plane(S, 0)];
-  const i8v &x = sm[nth_plane(S, 0)], &y = sm[nth_plane(S, 1)], &z = sm[nth_plane(S, 2)];
-  i8v r = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    r[q] = (int)__builtin_amdgcn_bitop3_b32((uint32_t)x[q], (uint32_t)y[q], (uint32_t)z[q], 0x96);
-  return r;
-}
 
-template <int NP>
-__device__ __forceinline__ uint32_t xor_planes(const uint32_t (&pl)[NP], int S) {
-  if (__builtin_popcount(S) == 1) return pl[nth_plane(S, 0)];
-  return __builtin_amdgcn_bitop3_b32(pl[nth_plane(S, 0)], pl[nth_plane(S, 1)], pl[nth_plane(S, 2)], 0x96);
-}
 
 // One block of 1024 threads per (stream, head group): log-sum-exp merge of the
 // chunk partials, then o = Pi^T o_rot. The Pi entries of the inverse rotation
@@ -2297,6 +2248,26 @@ hipError_t launch_decode(const tq_ctx *ctx, const tq_kv_cache *cache, const void
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   if (logits) return hipSuccess;  // measurement: no softmax, no merge
   hipLaunchKernelGGL(decode_merge_kernel, dim3(streams), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_partials(const tq_ctx *ctx, const tq_kv_cache *cache, int32_t q_heads, int n_q,
+                                 float *partial, int nchunks, float *out, hipStream_t st) {
+  DecodeArgs a = {};
+  a.kv_heads = cache->kv_heads;
+  a.capacity = cache->capacity;
+  a.q_heads = q_heads;
+  a.group = q_heads / cache->kv_heads;
+  a.n_q = n_q;
+  a.vgroup = a.group * n_q;
+  a.hgroups = (a.vgroup + 3) / 4;
+  a.nchunks = nchunks;
+  a.batch = cache->batch;
+  a.kv_streams = cache->batch * cache->kv_heads;
+  a.rot = ctx->d_rot;
+  a.partial = partial;
+  a.out = out;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.kv_streams * a.hgroups), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 

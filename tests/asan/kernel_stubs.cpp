@@ -1,4 +1,4 @@
-// Stand-ins for the kernel launchers of tq_kernels.hip, for a CPU-only build of
+// Stand-ins for the kernel launchers of tq_kernels.hip and prefill_kernels.hip, for a CPU-only build of
 // tq_host.cpp under AddressSanitizer and UndefinedBehaviorSanitizer
 // (tests/test_host_sanitizers.py). Only the host code (codebooks, rotations,
 // seeded draws, argument validation) runs in that build; a call that would
@@ -44,4 +44,10 @@ hipError_t launch_polar_attention(const tq_ctx *, const tq_polar_packed *, const
 }
 hipError_t launch_scores(const tq_ctx *, const void *, int, int64_t, const tq_packed *, float *, int32_t, int32_t *,
                          float *, void *, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_merge_partials(const tq_ctx *, const tq_kv_cache *, int32_t, int, float *, int, float *,
+                                 hipStream_t) { return hipErrorNotSupported; }
+bool prefill_supported(const tq_ctx *, const tq_kv_cache *, int32_t, int) { return false; }
+size_t prefill_ws_bytes(const tq_kv_cache *, int32_t, int) { return kHuge; }
+hipError_t launch_prefill(const tq_ctx *, const tq_kv_cache *, const void *, int, int32_t, int, int, float, float *,
+                          void *, hipStream_t, hipEvent_t, hipEvent_t) { return hipErrorNotSupported; }
 }  // namespace tq

@@ -164,9 +164,13 @@ def test_paged_small_pages_against_oracle(c128):
 def test_paged_chunks_spanning_pages(c128, page_tokens):
     """Pages smaller than the decode chunk: 2 sequences x 8 KV heads x 32868
     tokens with 128 query heads (groups of 16) make 1024-token chunks, each
-    spanning four or two shuffled pages. Decode, causal prefill attention of 3
-    positions and two fused steps equal the contiguous cache's outputs bit for
-    bit (same chunking, so the same arithmetic)."""
+    spanning four or two shuffled pages. Decode and two fused steps equal the
+    contiguous cache's outputs bit for bit (same chunking, so the same
+    arithmetic). Causal prefill attention of 3 positions (48 virtual heads per
+    KV head): with 512-token pages both caches run the 16-head prefill kernel
+    and agree bit for bit; 256-token pages take the decode kernels, whose
+    result agrees with the prefill kernel's within the attention bar (each is
+    checked against the oracle on its own elsewhere)."""
     ctx, _, _ = c128
     B, H, Hq, L, d = 2, 8, 128, 32868, 128
     cap = ((L + 2 + 1023) // 1024) * 1024
@@ -182,7 +186,11 @@ def test_paged_chunks_spanning_pages(c128, page_tokens):
     q = synth.torch_gaussian(43, (3,), (B, Hq, d), torch.bfloat16, DEV)
     assert torch.equal(flat.decode(ctx, q), paged.decode(ctx, q))
     qp = synth.torch_gaussian(43, (4,), (B, 3, Hq, d), torch.bfloat16, DEV)
-    assert torch.equal(flat.attend(ctx, qp, True), paged.attend(ctx, qp, True))
+    of, op = flat.attend(ctx, qp, True), paged.attend(ctx, qp, True)
+    if page_tokens % 512 == 0:
+        assert torch.equal(of, op)
+    else:
+        assert float((of - op).abs().max()) <= 2e-3
     for i in range(2):
         ka = synth.torch_outlier_kv(43, (5, i), synth.TAG_SCALES_K, (B, H, d), torch.bfloat16, DEV)
         va = synth.torch_outlier_kv(43, (6, i), synth.TAG_SCALES_V, (B, H, d), torch.bfloat16, DEV)

@@ -212,3 +212,71 @@ def test_prefill_argument_errors(c128):
     assert L.tq_attention_prefill(*args(4, 8, 1, need - 1)) != 0
     assert L.tq_attention_prefill(*args(4, 64, 1, need)) != 0     # group 32 > 16
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_prefill_kernel_many_chunks(c128, causal):
+    """The 16-virtual-head prefill kernel over a context split into several
+    512-token chunks: 1 sequence of 2900 tokens (a ragged last block), 2 KV
+    heads, 8 query heads, 64 query positions (256 virtual heads per KV head,
+    16 work-group units), 3-bit keys with QJL signs, 3-bit values."""
+    ctx, Pi, S = c128
+    B, H, cap, L, nq, hq = 1, 2, 3072, 2900, 64, 8
+    seq = [L]
+    K = synth.outlier_kv(26, (1,), synth.TAG_SCALES_K, (B, H, L, 128))
+    V = synth.outlier_kv(26, (2,), synth.TAG_SCALES_V, (B, H, L, 128))
+    Q = synth.gaussian(26, (3,), (B, nq, hq, 128), "bf16")
+    cache, o = _cache(ctx, Pi, S, K, V, seq, 3, 3, cap)
+    scale = 1.0 / math.sqrt(128)
+    out = cache.attend(ctx, _dev(Q, "bf16"), causal, scale).cpu().numpy()
+    _check(out, Q, Pi, S, o, seq, scale, causal)
+
+
+@pytest.mark.parametrize("kbits,qjl,vbits", [(4, True, 3), (2, True, 1), (4, False, 2), (0, True, 3)],
+                         ids=["tq5-v3", "tq3-v1", "mse4-v2", "qjl-v3"])
+def test_prefill_kernel_formats(c128, kbits, qjl, vbits):
+    """Key formats (B = 0..4, with and without QJL signs) and value bits 1..3
+    through the prefill kernel: 2 sequences (1100 and 513 tokens), 2 KV heads,
+    16 query heads (groups of 8), 9 positions (72 virtual heads: a partial
+    last unit of 8)."""
+    ctx, Pi, S = c128
+    B, H, cap, L, nq, hq = 2, 2, 1152, 1100, 9, 16
+    seq = [1100, 513]
+    K = synth.outlier_kv(27, (kbits, vbits, 1), synth.TAG_SCALES_K, (B, H, L, 128))
+    V = synth.outlier_kv(27, (kbits, vbits, 2), synth.TAG_SCALES_V, (B, H, L, 128))
+    Q = synth.gaussian(27, (kbits, vbits, 3), (B, nq, hq, 128), "f32")
+    cache, o = _cache(ctx, Pi, S, K, V, seq, kbits, vbits, cap, qjl)
+    scale = 1.0 / math.sqrt(128)
+    out = cache.attend(ctx, _dev(Q, "f32"), True, scale).cpu().numpy()
+    _check(out, Q, Pi, S, o, seq, scale, True)
+
+
+def test_prefill_kernel_bench_shape_sampled(c128):
+    """The chunked-prefill benchmark's last chunk at full size: 8 KV heads x
+    16384 tokens quantized on the GPU, 1024 causal query positions x 32 query
+    heads. Sampled outputs (2 KV heads x 3 positions x 4 heads) against the
+    oracle over the records the GPU wrote, within 2e-3."""
+    ctx, Pi, S = c128
+    B, H, Hq, P, C, d = 1, 8, 32, 16384, 1024, 128
+    K = synth.outlier_kv(28, (1,), synth.TAG_SCALES_K, (B, H, P, d), "bf16")
+    V = synth.outlier_kv(28, (2,), synth.TAG_SCALES_V, (B, H, P, d), "bf16")
+    Q = synth.gaussian(28, (3,), (B, C, Hq, d), "bf16")
+    cache = tq.KVCache(B, H, P, d, 3, 3)
+    cache.prefill(ctx, _dev(K, "bf16"), _dev(V, "bf16"))
+    scale = 1.0 / math.sqrt(d)
+    out = cache.attend(ctx, _dev(Q, "bf16"), True, scale).cpu().numpy()
+    torch.cuda.synchronize()
+    kw, kn = cache.k.host()
+    vw, vn = cache.v.host()
+    cbk, cbv = T.codebook(d, 3), T.codebook(d, 3)
+    g = Hq // H
+    worst = 0.0
+    for h in (0, 5):
+        keys = {"bits": kw[h * P:(h + 1) * P], "norms": kn[h * P:(h + 1) * P]}
+        vals = {"bits": vw[h * P // 32:(h + 1) * P // 32], "norms": vn[h * P:(h + 1) * P]}
+        for i in (0, 517, C - 1):
+            vis = P - C + i + 1
+            ref = T.attention_decode(Q[0, i, h * g:(h + 1) * g], Pi, S, cbk, cbv, keys, vals, vis, scale)
+            err = float(np.max(np.abs(out[0, i, h * g:(h + 1) * g] - ref)))
+            worst = max(worst, err)
+            assert err <= 2e-3, f"h={h} position {i}: {err}"
