@@ -102,6 +102,14 @@ __device__ __forceinline__ i8v mask_fp4_1122(uint32_t w) {
   return b;
 }
 
+// A wave-uniform 64-bit value in scalar registers (buffer descriptors built from
+// it stay scalar: no per-lane loop over distinct descriptors).
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Maximum over the 16 lanes of a row (DPP row rotations: no lane addresses).
 __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
@@ -214,12 +222,13 @@ __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillArgs a) {
 }
 
 // KB MSE bits of the keys (0: pure QJL keys), VB value bits (<= 3), QJL: the keys
-// carry the sign word and |r|.
+// carry the sign word and |r|; NF16: the cache's norms are fp16 (compile-time, so
+// that the tile loop has no branch and its loads stay in flight across tiles).
 // Work-group: 4 waves over one chunk of one unit (stream, 16 virtual heads).
 // Per block of 512 tokens: phase K (wave w scores tokens 128 w .. 128 w + 127 of
 // all 16 heads), phase S (thread (head, 32 tokens): softmax weights to value
 // digits), phase V (wave w sums coordinates 32 w .. 32 w + 31 of all heads).
-template <int KB, int VB, bool QJL>
+template <int KB, int VB, bool QJL, bool NF16>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   constexpr int KM = KB > 0 ? 1 << (KB - 1) : 0;  // key Walsh masks
   constexpr int KQ = QJL ? 1 : 0;
@@ -320,18 +329,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                                                                        PFRAG_WORDS * 4, 0x00020000);
   constexpr int NB = 4;                               // fp32 norms (fp16: 2, below)
   for (int T0 = t_begin; T0 < t_end; T0 += PB) {
-    const int n = min(PB, t_end - T0);
+    const int n = __builtin_amdgcn_readfirstlane(min(PB, t_end - T0));
     const bool full = n == PB && T0 + PB <= vis_lo;  // no token of the block is masked
     // ---- phase K ----
     {
       float lmx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       float vmx = 0.f;
-      const int nw = min(max(n - 128 * wave, 0), 128);  // tokens of this wave (uniform)
+      const int nw = __builtin_amdgcn_readfirstlane(min(max(n - 128 * wave, 0), 128));  // tokens of this wave
       if (nw > 0) {
         // range-checked descriptors over the wave's records only: loads past
         // them return zeros; the scalar offset (not range-checked) stays 0
-        const int64_t r0 = a.map.rec(stream, T0) + 128 * wave;
-        const int nb = a.nf16 ? 2 : NB;
+        const int64_t r0 = uniform_i64(a.map.rec(stream, T0) + 128 * wave);
+        constexpr int nb = NF16 ? 2 : NB;
         const __amdgpu_buffer_rsrc_t rkb = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint32_t *>(a.kbits) + r0 * DW * NPL, (short)0, nw * RB, 0x00020000);
         const __amdgpu_buffer_rsrc_t rkn = __builtin_amdgcn_make_buffer_rsrc(
@@ -354,7 +363,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int p = 0; p < NPL; ++p) t.pl[p] = __builtin_amdgcn_raw_buffer_load_b32(rkb, off + 4 * p, 0, 2);
           }
-          if (a.nf16) {
+          if constexpr (NF16) {
             if constexpr (QJL) {
               const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, 0, 2);
               t.kn = make_float2(__half2float(__ushort_as_half((unsigned short)(h2 & 0xFFFFu))),
@@ -397,7 +406,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         int lim[4];  // block-relative visibility of the lane's heads
 #pragma unroll
         for (int i = 0; i < 4; ++i) lim[i] = min(visk[i] - T0, n);
-        auto kcompute = [&](int u, const KT &t) {
+        auto kcompute = [&](int u, const KT &t, auto masked) {
           i8v bm[NA > 0 ? NA : 1];
           {
             i8v sm[KB > 0 ? KB : 1];
@@ -426,7 +435,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             float s;
             if constexpr (QJL) s = t.kn.x * fmaf(sr[i], code, qs[i] * (t.kn.y * acc[KM][i]));
             else s = t.kn.x * (sr[i] * code);
-            if (!full) s = tc < lim[i] ? s : -INFINITY;
+            if constexpr (decltype(masked)::value) s = tc < lim[i] ? s : -INFINITY;
             lg[(4 * G + i) * PLS + tc] = s;
             lmx[i] = fmaxf(lmx[i], s);
           }
@@ -434,14 +443,29 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
           vmx = fmaxf(vmx, t.vn);
         };
         const int ntl = (nw + 15) >> 4;
-        for (int u = 0; u < ntl; u += 2) {
-          kload(u + 1, kb);  // past the wave's tokens: zeros
-          __builtin_amdgcn_sched_barrier(0);
-          kcompute(u, ka);
-          if (u + 1 >= ntl) break;
-          kload(u + 2, ka);
-          __builtin_amdgcn_sched_barrier(0);
-          kcompute(u + 1, kb);
+        auto tiles = [&](auto masked) {
+          for (int u = 0; u < ntl; u += 2) {
+            kload(u + 1, kb);  // past the wave's tokens: zeros
+            __builtin_amdgcn_sched_barrier(0);
+            kcompute(u, ka, masked);
+            if (u + 1 >= ntl) break;
+            kload(u + 2, ka);
+            __builtin_amdgcn_sched_barrier(0);
+            kcompute(u + 1, kb, masked);
+          }
+        };
+        // blocks inside every head's visible range skip the per-token mask
+        if (full) tiles(std::false_type{});
+        else tiles(std::true_type{});
+      }
+      // the block's tokens past its end (the chunk's last block): masked logits
+      // and zero norms, so phase S needs no per-token test
+      if (nw < 128) {
+        for (int u = (nw + 15) >> 4; u < 8; ++u) {
+          const int tc = 128 * wave + 16 * u + tn;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lg[(4 * G + i) * PLS + tc] = -INFINITY;
+          vnl[tc] = 0.f;
         }
       }
       // per-head maxima over the wave's tokens: the 16 lanes of a row group
@@ -463,20 +487,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     // the block's value words (all four 128-token groups), requested before phase S;
     // blocks past the chunk's end read zeros (range-checked descriptor). A block's
     // records are consecutive (one page holds whole blocks)
+    const __amdgpu_buffer_rsrc_t rvb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t *>(a.vbits) + (uniform_i64(a.map.rec(stream, T0)) >> 5) * DD * VB, (short)0,
+        ((n + 31) >> 5) * VWB, 0x00020000);
+    const uint32_t vlo = (uint32_t)((vgl * DD + 32 * wave + vn) * VB * 4);
     uint32_t vw[4][2][VB];
-    {
-      const __amdgpu_buffer_rsrc_t rvb = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint32_t *>(a.vbits) + (a.map.rec(stream, T0) >> 5) * DD * VB, (short)0, ((n + 31) >> 5) * VWB,
-          0x00020000);
-      const uint32_t vlo = (uint32_t)((vgl * DD + 32 * wave + vn) * VB * 4);
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int p = 0; p < VB; ++p)
-            vw[g][nt][p] = __builtin_amdgcn_raw_buffer_load_b32(rvb, g * 4 * VWB + vlo + nt * 16 * VB * 4 + 4 * p, 0, 0);
-    }
+        for (int p = 0; p < VB; ++p)
+          vw[g][nt][p] = __builtin_amdgcn_raw_buffer_load_b32(rvb, g * 4 * VWB + vlo + nt * 16 * VB * 4 + 4 * p, 0, 0);
     const float bv = fmaxf(fmaxf(svm[0], svm[1]), fmaxf(svm[2], svm[3]));
     // the block maxima of the phase V lane's heads, read before the next block's
     // phase K can overwrite them
@@ -512,15 +534,9 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int qq = 4 * lohi + q;
-            float e = __builtin_amdgcn_exp2f(lv[q] - ref);  // <= 1
+            const float e = __builtin_amdgcn_exp2f(lv[q] - ref);  // <= 1
             // rounding by truncation of W + 1/2 (W >= 0)
             uint32_t W = (uint32_t)fmaf(e, nv[q] * (cv * (1.f / (float)(1 << qq))), 0.5f);
-            if (!full) {
-              // tokens past the block's end hold stale LDS values
-              const bool live = 32 * vgb + 8 * kp + qq < n;
-              e = live ? e : 0.f;
-              W = live ? W : 0u;
-            }
             le += e;
             wt += (long long)((unsigned long long)W << qq);
             // four signed base-256 digits; the B byte of q' = 7 is -128 b, so its weight is negated
@@ -685,15 +701,20 @@ size_t prefill_ws_bytes(const tq_kv_cache *cache, int32_t q_heads, int n_q) {
   return b;
 }
 
-template <int KB, bool QJL>
-static hipError_t launch_prefill_k(const PrefillArgs &a, int vb, dim3 grid, hipStream_t st) {
+template <int KB, bool QJL, bool NF16>
+static hipError_t launch_prefill_kn(const PrefillArgs &a, int vb, dim3 grid, hipStream_t st) {
   switch (vb) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<KB, 1, QJL>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<KB, 2, QJL>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((prefill_kernel<KB, 3, QJL>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<KB, 1, QJL, NF16>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<KB, 2, QJL, NF16>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((prefill_kernel<KB, 3, QJL, NF16>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int KB, bool QJL>
+static hipError_t launch_prefill_k(const PrefillArgs &a, int vb, dim3 grid, hipStream_t st) {
+  return a.nf16 ? launch_prefill_kn<KB, QJL, true>(a, vb, grid, st) : launch_prefill_kn<KB, QJL, false>(a, vb, grid, st);
 }
 
 hipError_t launch_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, const void *q, int is_bf16, int32_t q_heads,
