@@ -419,13 +419,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
           f4v acc[NA > 0 ? NA : 1];
 #pragma unroll
           for (int mi = 0; mi < NA; ++mi) acc[mi] = mi < KM ? init_r : init_s;
-          // digit-major: the NA accumulators are independent within a digit
+          // digit-major: the NA accumulators are independent within a digit. The
+          // wave's priority is raised while it issues MFMAs, so that of two waves
+          // on a SIMD the one with matrix work goes first and the other's VALU
+          // work fills the gaps
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int k = 0; k < PDIG; ++k)
 #pragma unroll
             for (int mi = 0; mi < NA; ++mi)
               acc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[mi < KM ? 0 : 1][k], bm[mi], acc[mi], 2, 4,
                                                                          0, 128 + 4 * k, 0, 128);
+          __builtin_amdgcn_s_setprio(0);
           const int tc = 128 * wave + 16 * u + tn;  // block-relative token
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -620,10 +625,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         };
         // all four groups, also past the block's end: their weights are zero
         // (branch-free, so the accumulators stay in one set of registers)
+        __builtin_amdgcn_s_setprio(1);
         vgroup(std::integral_constant<int, 0>{}, std::true_type{});
         vgroup(std::integral_constant<int, 1>{}, std::false_type{});
         vgroup(std::integral_constant<int, 2>{}, std::false_type{});
         vgroup(std::integral_constant<int, 3>{}, std::false_type{});
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float o = 0.f;
