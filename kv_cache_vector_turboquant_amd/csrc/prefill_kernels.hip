@@ -356,13 +356,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         auto kload = [&](int u, KT &t) {
           const uint32_t tl = (uint32_t)(16 * u + tn);
           const uint32_t off = tl * RB + (uint32_t)(G * NPL * 4);
-          if constexpr (NPL == 4) {
-            const auto w4 = __builtin_amdgcn_raw_buffer_load_b128(rkb, off, 0, 2);
-            t.pl[0] = w4[0]; t.pl[1] = w4[1]; t.pl[2] = w4[2]; t.pl[3] = w4[3];
-          } else {
-#pragma unroll
-            for (int p = 0; p < NPL; ++p) t.pl[p] = __builtin_amdgcn_raw_buffer_load_b32(rkb, off + 4 * p, 0, 2);
-          }
+          buffer_load_words<NPL, 2>(rkb, off, t.pl);
           if constexpr (NF16) {
             if constexpr (QJL) {
               const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, 0, 2);

@@ -68,4 +68,24 @@ __device__ __forceinline__ void mask_bytes_pow2(uint32_t m, i4v &lo, i4v &hi) {
   hi[3] = (int)(m & 0x80808080u);
 }
 
+// NPL consecutive dwords at byte offset off of a buffer resource, with the
+// widest loads (dword alignment suffices for buffer loads); AUX is the cache
+// policy field (2: non-temporal).
+template <int NPL, int AUX>
+__device__ __forceinline__ void buffer_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[NPL]) {
+  if constexpr (NPL == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+  } else if constexpr (NPL == 2) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+    w[0] = x[0]; w[1] = x[1];
+  } else if constexpr (NPL == 3) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, AUX);
+    w[0] = x[0]; w[1] = x[1]; w[2] = x[2];
+  } else {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+    if constexpr (NPL == 5) w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 16u, 0, AUX);
+  }
+}
+
 }  // namespace tq

@@ -1749,14 +1749,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
           for (int u = 0; u < KTPW; ++u) {
             const uint32_t tl = (uint32_t)(u * 16 + tn);  // token of the lane, relative to t16
             bf.tc[u] = (uint32_t)t16 + tl;
-            if constexpr (NPL == 4) {
-              const auto w4 = __builtin_amdgcn_raw_buffer_load_b128(rkb, tl * RB + kgo, 0, 2);
-              bf.pl[u][0] = w4[0]; bf.pl[u][1] = w4[1]; bf.pl[u][2] = w4[2]; bf.pl[u][3] = w4[3];
-            } else {
-#pragma unroll
-              for (int p = 0; p < NPL; ++p)
-                bf.pl[u][p] = __builtin_amdgcn_raw_buffer_load_b32(rkb, tl * RB + kgo + 4 * p, 0, 2);
-            }
+            buffer_load_words<NPL, 2>(rkb, tl * RB + kgo, bf.pl[u]);
             if constexpr (NF16) {
               if constexpr (QJL) {
                 const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b32(rkn, tl * 4u, 0, 2);
@@ -2495,13 +2488,7 @@ __global__ void __launch_bounds__(64 * SW) search_kernel(SearchArgs a) {
 #pragma unroll
         for (int u = 0; u < STS; ++u) {
           const uint32_t off = (uint32_t)(16 * (t0 + u) + tn) * RBY + (uint32_t)((4 * cb + G) * NPL * 4);
-          if constexpr (NPL == 4) {
-            const auto w4 = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-            pw[u][0] = w4[0]; pw[u][1] = w4[1]; pw[u][2] = w4[2]; pw[u][3] = w4[3];
-          } else {
-#pragma unroll
-            for (int p = 0; p < NPL; ++p) pw[u][p] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + 4 * p, 0, 0);
-          }
+          buffer_load_words<NPL, 0>(rk, off, pw[u]);
         }
 #pragma unroll
         for (int u = 0; u < STS; ++u) {
