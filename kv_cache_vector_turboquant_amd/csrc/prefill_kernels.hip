@@ -17,8 +17,10 @@
 //  prefill_kernel       one pass over a chunk of the context in blocks of 512
 //                       tokens: key scores of 16 heads x 16 tokens per fp6 x fp4
 //                       MFMA chain, online softmax, value sums on int8 MFMA over
-//                       the value bit masks. The chunk partials (rotated output,
-//                       max logit, weight sum) go through the decode merge.
+//                       the value bit masks. When one chunk covers the context
+//                       the work-group finishes the output (o = Pi^T o_rot / l);
+//                       otherwise the chunk partials (rotated output, max logit,
+//                       weight sum) go through the decode merge.
 //
 // Arithmetic (the decode kernels' scheme, regrouped for many heads per KV head):
 //  scores   A rows are the 16 heads, B columns 16 tokens; the six digit
@@ -77,17 +79,27 @@ struct PrefillArgs {
   uint32_t *qfrag;         // [unit][2 (q_rot, q_s)][6 digits][64 lanes][6 dwords]
   float *qconst;           // [unit][16][4]: q_rot unit x scale, q_s unit x QJL constant x scale, -sum Q_rot, -sum Q_s
   float *partial;          // [stream][vgroup][nchunks][DD + 2]
+  const float *rot;        // Pi, row-major (the output's inverse rotation when one chunk covers the context)
+  float *out;              // [batch][n_q][q_heads][DD]
 };
 
 // e2m3 code of x, a multiple of 1/8 with |x| <= 7.5: sign 0x20, exponent field
 // e (bias 1; 0 = subnormal m/8), mantissa m.
-__device__ __forceinline__ uint32_t e2m3_code(float x) {
-  const uint32_t s = x < 0.f ? 0x20u : 0u;
-  const float a = fabsf(x);
-  if (a < 1.f) return s | (uint32_t)(a * 8.f);
-  const int e = a < 2.f ? 0 : (a < 4.f ? 1 : 2);
-  const uint32_t m = (uint32_t)((a / (float)(1 << e) - 1.f) * 8.f);
+__host__ __device__ constexpr uint32_t e2m3_code(double x) {
+  const uint32_t s = x < 0 ? 0x20u : 0u;
+  const double a = x < 0 ? -x : x;
+  if (a < 1.0) return s | (uint32_t)(a * 8.0);
+  const int e = a < 2.0 ? 0 : (a < 4.0 ? 1 : 2);
+  const uint32_t m = (uint32_t)((a / (double)(1 << e) - 1.0) * 8.0);
   return s | ((uint32_t)(e + 1) << 3) | m;
+}
+
+// Magnitude codes of |d| / 2^f for |d| = 0 .. 8, six bits each (f = 1: the
+// digits of coordinate groups 0, 1; f = 2: groups 2, 3); the sign is bit 0x20.
+__host__ __device__ constexpr uint64_t digit_mag_table(int f) {
+  uint64_t t = 0;
+  for (int m = 0; m <= 8; ++m) t |= (uint64_t)e2m3_code((double)m / (1 << f)) << (6 * m);
+  return t;
 }
 
 // Key B operand of a 32-coordinate plane word: element 8q + i (nibble i of dword
@@ -124,7 +136,7 @@ __device__ __forceinline__ float row_max16(float x) {
 __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) float qk[DD][PH];  // queries [coordinate][head]
   __shared__ float qv[2][PH][DD];                            // q_rot, q_s
-  __shared__ int qz[2][PH][DD];                              // fixed point + PQOFF
+  __shared__ __attribute__((aligned(16))) int qz[2][PH][DD];  // fixed point + PQOFF
   __shared__ float mx[2][PH];
   __shared__ int qsum[2][PH];
   const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -203,13 +215,17 @@ __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillArgs a) {
     const int item = it * 256 + tid;
     const int T = item / (PDIG * 64), k = (item >> 6) % PDIG, l = item & 63;
     const int h = l & (PH - 1), g = l >> 4;
+    constexpr uint64_t mag1 = digit_mag_table(1), mag2 = digit_mag_table(2);
     uint32_t dw[6] = {0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      const int4 z4 = *reinterpret_cast<const int4 *>(&qz[T][h][32 * g + 4 * i]);
+      const int zq[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int d = ((qz[T][h][32 * g + 4 * i + q] >> (4 * k)) & 15) - 8;
-        const uint32_t code = e2m3_code(q < 2 ? 0.5f * (float)d : 0.25f * (float)d);
+        const int d = ((zq[q] >> (4 * k)) & 15) - 8;
+        const uint32_t mag = (uint32_t)((q < 2 ? mag1 : mag2) >> (6 * (d < 0 ? -d : d))) & 63u;
+        const uint32_t code = mag | (d < 0 ? 0x20u : 0u);
         const int bit = 6 * (8 * q + i);
         dw[bit >> 5] |= code << (bit & 31);
         if ((bit & 31) > 26) dw[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
@@ -283,6 +299,16 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   const int64_t pstride = (int64_t)a.nchunks * (DD + 2);
   float *pbase = a.partial + ((int64_t)stream * a.vgroup + vh0) * pstride + (int64_t)c * (DD + 2);
   if (t_begin >= t_end) {
+    if (a.nchunks == 1) {
+      // no visible token for any head of the unit: zero outputs
+      const int b2 = stream / a.kv_heads, kvh = stream - b2 * a.kv_heads;
+      for (int e = tid; e < nh * DD; e += 256) {
+        const int h = e / DD, j = e - h * DD;
+        const int vh = vh0 + h, qi = vh / a.group, qj = vh - qi * a.group;
+        a.out[(((int64_t)b2 * a.n_q + qi) * a.q_heads + kvh * a.group + qj) * DD + j] = 0.f;
+      }
+      return;
+    }
     for (int e = tid; e < nh * (DD + 2); e += 256) {
       const int h = e / (DD + 2), j = e - h * (DD + 2);
       pbase[h * pstride + j] = j == DD ? -INFINITY : 0.f;
@@ -645,6 +671,36 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   lsum += __shfl_xor(lsum, 32);
   if (lane < 16) lred[wave][lane] = lsum;
   __syncthreads();
+  if (a.nchunks == 1) {
+    // one chunk covers the whole context: the output is finished here,
+    // o = Pi^T o_rot / l (no partials, no merge launch). o_rot goes through LDS
+    // (the logits' space, unused past the last block)
+    float *orot = lg;  // [16][DD]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) orot[(4 * vgl + i) * DD + 32 * wave + 16 * nt + vn] = O[nt][i];
+    __syncthreads();
+    // thread (coordinate j, heads h0 .. h0 + 7): column j of Pi against o_rot
+    const int j = tid & (DD - 1), h0 = (tid >> 7) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < DD; ++k) {
+      const float p = a.rot[k * DD + j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = fmaf(p, orot[(h0 + u) * DD + k], acc[u]);
+    }
+    const int b2 = stream / a.kv_heads, kvh = stream - b2 * a.kv_heads;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int h = h0 + u;
+      if (h < nh) {
+        const float l = (lred[0][h] + lred[1][h]) + (lred[2][h] + lred[3][h]);
+        const int vh = vh0 + h, qi = vh / a.group, qj = vh - qi * a.group;
+        a.out[(((int64_t)b2 * a.n_q + qi) * a.q_heads + kvh * a.group + qj) * DD + j] = l > 0.f ? acc[u] / l : 0.f;
+      }
+    }
+    return;
+  }
   if (tid < nh) {
     pbase[tid * pstride + DD] = mrs;
     pbase[tid * pstride + DD + 1] = (lred[0][tid] + lred[1][tid]) + (lred[2][tid] + lred[3][tid]);
@@ -753,6 +809,8 @@ hipError_t launch_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, const voi
   a.qconst = (float *)p;
   p += ((size_t)s.units * PH * 4 * sizeof(float) + 255) & ~(size_t)255;
   a.partial = (float *)p;
+  a.rot = ctx->d_rot;
+  a.out = out;
   hipLaunchKernelGGL(prefill_prep_kernel, dim3((unsigned)s.units), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -779,6 +837,7 @@ hipError_t launch_prefill(const tq_ctx *ctx, const tq_kv_cache *cache, const voi
   }
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
+  if (s.nchunks == 1) return hipSuccess;  // the kernel wrote the output
   return launch_merge_partials(ctx, cache, q_heads, n_q, a.partial, s.nchunks, out, st);
 }
 

@@ -280,3 +280,21 @@ def test_prefill_kernel_bench_shape_sampled(c128):
             err = float(np.max(np.abs(out[0, i, h * g:(h + 1) * g] - ref)))
             worst = max(worst, err)
             assert err <= 2e-3, f"h={h} position {i}: {err}"
+
+
+def test_prefill_kernel_one_chunk_finishes_in_kernel(c128):
+    """Enough units (8 sequences x 8 KV heads x 16 units) that one chunk covers
+    each context: the prefill kernel writes the output itself (no partials,
+    no merge). Lengths 700, 600, 0, 20, 64, 65, 1, 512: whole-unit blind
+    positions (a sequence shorter than the chunk), a sequence with no token and
+    one block boundary; 64 causal positions x 4 heads per KV head."""
+    ctx, Pi, S = c128
+    B, H, cap, L, nq, hq = 8, 8, 704, 700, 64, 32
+    seq = [700, 600, 0, 20, 64, 65, 1, 512]
+    K = synth.outlier_kv(29, (1,), synth.TAG_SCALES_K, (B, H, L, 128))
+    V = synth.outlier_kv(29, (2,), synth.TAG_SCALES_V, (B, H, L, 128))
+    Q = synth.gaussian(29, (3,), (B, nq, hq, 128), "bf16")
+    cache, o = _cache(ctx, Pi, S, K, V, seq, 3, 3, cap)
+    scale = 1.0 / math.sqrt(128)
+    out = cache.attend(ctx, _dev(Q, "bf16"), True, scale).cpu().numpy()
+    _check(out, Q, Pi, S, o, seq, scale, True)
