@@ -1158,14 +1158,30 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
   const int r = tid & (DD - 1), kq = tid >> 7;
   // this thread's stream for the per-coordinate phases: (stream half, key or value)
   const int hs = tid >> 8, kv = (tid >> 7) & 1;
+  // Loads are issued in the order their values are needed, unconditionally
+  // (clamped addresses), so that no wait covers a load it does not need (a wait
+  // covers every earlier load): the table entry and the token, the Pi and S rows,
+  // and last the value words, whose address needs the length and which are read
+  // only at the end.
   int stream[2], pos[2];
   bool on[2];
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
     stream[s2] = 2 * blk + s2;
-    const bool exists = stream[s2] < nstreams;
-    pos[s2] = exists ? a.seq_len[stream[s2] / a.kv_heads] : a.capacity;
-    on[s2] = exists && pos[s2] >= 0 && pos[s2] < a.capacity;  // a full stream gets nothing appended
+    pos[s2] = stream[s2] < nstreams ? a.seq_len[stream[s2] / a.kv_heads] : a.capacity;
+  }
+  float tbv;
+  {
+    const int which = min(tid >> 4, 2), i = tid & 15;
+    tbv = which == 0 ? a.tables->boundary[kB][i] : which == 1 ? a.tables->centroid[kB][i] : a.tables->boundary[vB][i];
+  }
+  // thread (stream hs, k or v, coordinate r): its coordinate of the new token
+  float xin;
+  {
+    const int64_t xo = (int64_t)min(stream[hs], nstreams - 1) * DD + r;
+    const void *src = kv ? a.va : a.ka;
+    xin = bf16in ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(src)[xo])
+                 : reinterpret_cast<const float *>(src)[xo];
   }
   // thread (row r, quarter kq): 32 entries of row r of Pi (transposed: coalesced
   // over r) and of row r of S
@@ -1180,26 +1196,26 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
       srow[4 * u] = v.x; srow[4 * u + 1] = v.y; srow[4 * u + 2] = v.z; srow[4 * u + 3] = v.w;
     }
   }
-  if (tid < 48) {
-    const int which = tid >> 4, i = tid & 15;
-    L.tb[tid] = which == 0 ? a.tables->boundary[kB][i] : which == 1 ? a.tables->centroid[kB][i] : a.tables->boundary[vB][i];
-  }
-  // value coordinate threads: the words this token's bits go into
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+    on[s2] = stream[s2] < nstreams && pos[s2] >= 0 && pos[s2] < a.capacity;  // a full stream gets nothing appended
+  // value coordinate threads: the words this token's bits go into (all requested together)
+  // (stream hs is uniform per wave: a range-checked buffer over the token's 32-token
+  // block, four unconditional loads per thread; words past the block read zero)
   const int64_t rec = on[hs] ? a.map.rec(stream[hs], pos[hs]) : 0;
   const int bit_pos = (int)(rec & 31);
-  uint32_t vold[4] = {0u, 0u, 0u, 0u};
+  uint32_t vold[4];
   uint32_t *vdst = a.vbits_w + ((rec >> 5) * DD + r) * vB;
-  if (kv == 1 && on[hs] && bit_pos != 0) {
-    for (int p = 0; p < vB; ++p) vold[p] = vdst[p];
-  }
   {
-    // thread (stream hs, k or v, coordinate r)
-    float x = 0.f;
-    if (on[hs]) {
-      const void *src = kv ? a.va : a.ka;
-      x = bf16in ? bf16f(reinterpret_cast<const uint16_t *>(src)[(int64_t)stream[hs] * DD + r])
-                 : reinterpret_cast<const float *>(src)[(int64_t)stream[hs] * DD + r];
-    }
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc(a.vbits_w + (rec >> 5) * DD * vB, (short)0, DD * vB * 4, 0x00020000);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) vold[p] = __builtin_amdgcn_raw_buffer_load_b32(vr, (uint32_t)((r * vB + p) * 4), 0, 0);
+  }
+  if (tid < 48) L.tb[tid] = tbv;
+  {
+    // bf16 input: the 16 loaded bits are the top half of the fp32 value
+    const float x = on[hs] ? (bf16in ? __uint_as_float(__float_as_uint(xin) << 16) : xin) : 0.f;
     L.x[hs][kv][r] = x;
     float sq = x * x;
     for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
