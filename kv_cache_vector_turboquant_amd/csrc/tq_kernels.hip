@@ -1157,7 +1157,7 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
   const int lane = tid & 63, w = tid >> 6;
   const int r = tid & (DD - 1), kq = tid >> 7;
   // this thread's stream for the per-coordinate phases: (stream half, key or value)
-  const int hs = tid >> 8, kv = (tid >> 7) & 1;
+  const int hs = __builtin_amdgcn_readfirstlane(tid >> 8), kv = (tid >> 7) & 1;  // hs: uniform per wave
   // Loads are issued in the order their values are needed, unconditionally
   // (clamped addresses), so that no wait covers a load it does not need (a wait
   // covers every earlier load): the table entry and the token, the Pi and S rows,
@@ -1200,8 +1200,9 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
   for (int s2 = 0; s2 < 2; ++s2)
     on[s2] = stream[s2] < nstreams && pos[s2] >= 0 && pos[s2] < a.capacity;  // a full stream gets nothing appended
   // value coordinate threads: the words this token's bits go into (all requested together)
-  // (stream hs is uniform per wave: a range-checked buffer over the token's 32-token
-  // block, four unconditional loads per thread; words past the block read zero)
+  // (stream hs is uniform per wave: a buffer over the token's 32-token block and
+  // four unconditional loads per thread at offsets clamped into the block; words
+  // p >= vB are not used)
   const int64_t rec = on[hs] ? a.map.rec(stream[hs], pos[hs]) : 0;
   const int bit_pos = (int)(rec & 31);
   uint32_t vold[4];
@@ -1210,7 +1211,8 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc(a.vbits_w + (rec >> 5) * DD * vB, (short)0, DD * vB * 4, 0x00020000);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) vold[p] = __builtin_amdgcn_raw_buffer_load_b32(vr, (uint32_t)((r * vB + p) * 4), 0, 0);
+    for (int p = 0; p < 4; ++p)
+      vold[p] = __builtin_amdgcn_raw_buffer_load_b32(vr, (uint32_t)(min(r * vB + p, DD * vB - 1) * 4), 0, 0);
   }
   if (tid < 48) L.tb[tid] = tbv;
   {
