@@ -456,12 +456,19 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   const int c16 = lane & 15, kq = lane >> 4;
   const int64_t tps = (a.n_tokens + QT - 1) / QT, total = tps * a.n_streams;
   // positive boundaries and centroid magnitudes
-  float tp[H > 1 ? H - 1 : 1], cm[H];
+  // centroid magnitudes as the bits of the first one and the XOR steps between
+  // neighbours: the centroid of magnitude m is cb0 ^ cd[0] ^ .. ^ cd[m - 1]
+  // (selects of XOR steps; a select chain over a table of magnitudes became an
+  // indexed table that the compiler put in LDS, one LDS read per coordinate)
+  float tp[H > 1 ? H - 1 : 1];
+  uint32_t cb0 = 0, cd[H > 1 ? H - 1 : 1];
   if constexpr (B > 0) {
 #pragma unroll
     for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
+    cb0 = __float_as_uint(a.tables->centroid[B][H]);
 #pragma unroll
-    for (int j = 0; j < H; ++j) cm[j] = a.tables->centroid[B][H + j];
+    for (int j = 0; j < H - 1; ++j)
+      cd[j] = __float_as_uint(a.tables->centroid[B][H + j]) ^ __float_as_uint(a.tables->centroid[B][H + j + 1]);
   }
   // the wave's rows of the Pi parts (and of the S parts for keys) stay in registers
   // for every tile the work-group processes
@@ -484,16 +491,15 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   // centroid is the magnitude table entry with the sign of y (one select chain each)
   auto code = [&](float y, uint32_t &idx) {
     const float ay = fabsf(y);
-    uint32_t mag = 0;
-    float c = cm[0];
+    uint32_t mag = 0, cbits = cb0;
 #pragma unroll
     for (int j = 0; j < H - 1; ++j) {
-      const bool ge = ay >= tp[j];
-      mag = ge ? (uint32_t)(j + 1) : mag;
-      c = ge ? cm[j + 1] : c;
+      const bool ge = ay >= tp[j];  // the boundaries increase: ge holds for a prefix of j
+      mag += ge ? 1u : 0u;
+      cbits ^= ge ? cd[j] : 0u;
     }
     idx = ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
-    return __builtin_copysignf(c, y);
+    return __builtin_copysignf(__uint_as_float(cbits), y);
   };
   // X granule P (0..1023) of the tile at token tt0 of stream st, for slot P of the
   // swizzled LDS tile (rows past the stream's end re-read its last token)
@@ -661,37 +667,43 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
       __syncthreads();
       }  // sketch stage
       if (more) stage_x(xr);  // every wave is past its reads of this tile's X and norms
-      // ---- pack: thread (token, 32-coordinate group) -> B code planes (+ the sign plane)
-      if (tid < 4 * QT) {
-        const int tok = tid >> 2, g = tid & 3;
+      // ---- pack: thread (token, 32-coordinate group, half) -> half of the B code
+      // planes (+ the sign plane): planes [PH0 h, PH0 h + PH0) of the record's NPL
+      // words, so that all eight waves share the gathers
+      constexpr int PH0 = (NPL + 1) / 2;
+      static_assert(!KEYS || NT == 8 * QT, "keys pack: two threads per (token, group)");
+      if (tid < 8 * QT) {
+        const int tok = (tid >> 2) & (QT - 1), g = tid & 3, h = tid >> 8;
         if (tok < nv) {
           const int64_t rec = a.map.rec(s, t0 + tok);
           const float n = nrm[tok];
-          uint32_t w[NPL];
+          uint32_t w[PH0];
           if (n > 0.f) {
             const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g, 7) * 4]);
             const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g + 1, 7) * 4]);
             const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-            for (int p = 0; p < NPL; ++p) {
+            for (int i = 0; i < PH0; ++i) {
+              const int p = PH0 * h + i;
               const int bit = p < B ? p : QJL_FIELD_BIT;
               uint32_t word = 0;
 #pragma unroll
               for (int m = 0; m < 8; ++m) word |= gather4(d8[m], bit) << (4 * m);
-              w[p] = word;
+              w[i] = word;
             }
           } else {
 #pragma unroll
-            for (int p = 0; p < NPL; ++p) w[p] = 0u;
+            for (int i = 0; i < PH0; ++i) w[i] = 0u;
           }
-          uint32_t *dst = a.bits_out + (rec * QW + g) * NPL;
+          uint32_t *dst = a.bits_out + (rec * QW + g) * NPL + PH0 * h;
           if constexpr (NPL == 4) {
-            *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
           } else {
 #pragma unroll
-            for (int p = 0; p < NPL; ++p) dst[p] = w[p];
+            for (int i = 0; i < PH0; ++i)
+              if (PH0 * h + i < NPL) dst[i] = w[i];
           }
-          if (g == 0) {
+          if (g == 0 && h == 0) {
             if constexpr (SK) {
               float r2 = 0.f;
 #pragma unroll
