@@ -426,32 +426,22 @@ __device__ __forceinline__ int swz(int row, int gran_per_row, int g, int mask) {
   return row * gran_per_row + (g ^ (row & mask));
 }
 
-// NW waves per work-group; wave w owns the RB = 8 / NW blocks of 16 output
-// coordinates 16 (w RB + rb) (keys: also those sketch rows). Keys run eight waves
-// (their Pi and S parts fill ~200 VGPRs: one work-group per compute unit),
-// values four (two work-groups per compute unit overlap one's MFMA phase with
-// the other's epilogue).
-// QJL (keys): the sketch stage; without it the keys are MSE-only (B code words
-// and |k|); B = 0 with QJL gives pure QJL keys (the residual is y itself).
-template <bool KEYS, int B, int NW, bool QJL>
-__global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
-  constexpr bool SK = KEYS && QJL;  // sketch stage present
-  constexpr int NPL = B + (SK ? 1 : 0);  // words per 32-coordinate group of a key record
-  constexpr int H = B > 0 ? 1 << (B - 1) : 1;  // centroids per sign
-  constexpr int RB = 8 / NW;       // row blocks per wave
-  constexpr int NT = 64 * NW;      // threads
+// Values, d = 128 with bf16 input: four waves per work-group, two work-groups
+// per compute unit (one's MFMA phase overlaps the other's epilogue); wave w owns
+// the output coordinates 32w .. 32w + 31 (two blocks of 16) with its rows of the
+// three Pi parts in registers.
+template <int B>
+__global__ void __launch_bounds__(256, 2) quant128_values_kernel(Q128Args a) {
+  constexpr int H = 1 << (B - 1);  // centroids per sign
+  constexpr int RB = 2;            // row blocks per wave
+  constexpr int NT = 256;          // threads
   constexpr int XG = QT * 16 / NT; // X granules per thread
   // X tile: token row t (64 rows of 16 granules of 8 bf16), granule g at t * 16 + (g ^ (t & 15))
   __shared__ __attribute__((aligned(16))) uint4 xs[QT * 16];
-  // codes, four 7-bit fields per dword (keys: bit 6 of a field = QJL sign): keys
-  // [token][coordinate] (8 granules per token),
-  // values [coordinate][token] (4 granules per coordinate)
+  // codes, four 7-bit fields per dword, [coordinate][token] (4 granules per coordinate)
   __shared__ __attribute__((aligned(16))) uint32_t stage[QT * QD / 4];
-  // keys: residual parts, [token][coordinate] bf16 (16 granules per token row)
-  __shared__ __attribute__((aligned(16))) uint16_t rt[SK ? 2 : 1][SK ? QT * QD : 8];
   __shared__ float nrm[QT], ninv[QT];
   __shared__ float ssq[QT];  // squared norms of the staged tile's tokens
-  __shared__ float rho2[NW][QT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
   const int64_t tps = (a.n_tokens + QT - 1) / QT, total = tps * a.n_streams;
@@ -462,18 +452,15 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   // indexed table that the compiler put in LDS, one LDS read per coordinate)
   float tp[H > 1 ? H - 1 : 1];
   uint32_t cb0 = 0, cd[H > 1 ? H - 1 : 1];
-  if constexpr (B > 0) {
 #pragma unroll
-    for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
-    cb0 = __float_as_uint(a.tables->centroid[B][H]);
+  for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
+  cb0 = __float_as_uint(a.tables->centroid[B][H]);
 #pragma unroll
-    for (int j = 0; j < H - 1; ++j)
-      cd[j] = __float_as_uint(a.tables->centroid[B][H + j]) ^ __float_as_uint(a.tables->centroid[B][H + j + 1]);
-  }
-  // the wave's rows of the Pi parts (and of the S parts for keys) stay in registers
-  // for every tile the work-group processes
+  for (int j = 0; j < H - 1; ++j)
+    cd[j] = __float_as_uint(a.tables->centroid[B][H + j]) ^ __float_as_uint(a.tables->centroid[B][H + j + 1]);
+  // the wave's rows of the Pi parts stay in registers for every tile the
+  // work-group processes
   bf16x8 pf[RB][4][3];
-  bf16x8 sf[SK ? RB : 1][SK ? 4 : 1][2];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = 16 * (wave * RB + rb) + c16;
@@ -481,25 +468,15 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int sp = 0; sp < 3; ++sp) pf[rb][ks][sp] = ld_bf8(a.rot3 + (sp * QD + r) * QD + ks * 32 + kq * 8);
-      if constexpr (SK) {
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) sf[rb][ks][sp] = ld_bf8(a.sk2 + (sp * QD + r) * QD + ks * 32 + kq * 8);
-      }
     }
   }
-  // code of y: idx = H + mag (y >= 0) or its mirror 2H - 1 - (H + mag) (y < 0); the
-  // centroid is the magnitude table entry with the sign of y (one select chain each)
-  auto code = [&](float y, uint32_t &idx) {
+  // code of y: idx = H + mag (y >= 0) or its mirror 2H - 1 - (H + mag) (y < 0)
+  auto code = [&](float y) {
     const float ay = fabsf(y);
-    uint32_t mag = 0, cbits = cb0;
+    uint32_t mag = 0;
 #pragma unroll
-    for (int j = 0; j < H - 1; ++j) {
-      const bool ge = ay >= tp[j];  // the boundaries increase: ge holds for a prefix of j
-      mag += ge ? 1u : 0u;
-      cbits ^= ge ? cd[j] : 0u;
-    }
-    idx = ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
-    return __builtin_copysignf(__uint_as_float(cbits), y);
+    for (int j = 0; j < H - 1; ++j) mag += ay >= tp[j] ? 1u : 0u;  // the boundaries increase
+    return ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
   };
   // X granule P (0..1023) of the tile at token tt0 of stream st, for slot P of the
   // swizzled LDS tile (rows past the stream's end re-read its last token)
@@ -552,7 +529,7 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
       for (int i = 0; i < XG; ++i) xr[i] = x_granule(sn, trn * QT, i * NT + tid);
     }
 
-    // ---- product 1: the wave's output coordinates for the 64 tokens (blocks tb)
+    // ---- product: the wave's output coordinates for the 64 tokens (blocks tb)
     f4v acc[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -572,195 +549,56 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
         for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb)
-            acc[rb][tb] = KEYS ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[rb][ks][sp], xf[tb], acc[rb][tb], 0, 0, 0)
-                               : __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[tb], pf[rb][ks][sp], acc[rb][tb], 0, 0, 0);
+            acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[tb], pf[rb][ks][sp], acc[rb][tb], 0, 0, 0);
     }
     // token norms (staged with the tile's X)
-    float ss[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) ss[tb] = ssq[tb * 16 + c16];
     if (wave == 0 && kq == 0) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        nrm[tb * 16 + c16] = sqrtf(ss[tb]);
-        if constexpr (!KEYS) ninv[tb * 16 + c16] = ss[tb] > 0.f ? __builtin_amdgcn_rsqf(ss[tb]) : 0.f;
+        const float ss = ssq[tb * 16 + c16];
+        nrm[tb * 16 + c16] = sqrtf(ss);
+        ninv[tb * 16 + c16] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
       }
     }
-
-    if constexpr (KEYS) {
-      // acc[rb][tb][r] = |x| y[coordinate 16 (wave RB + rb) + 4kq + r][token tb*16 + c16]
-      float rp[4] = {0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // norms of every token
+    // acc[rb][tb][r] = |x| y[token tb*16 + 4kq + r][coordinate 16 (wave RB + rb) + c16]
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int tok = tb * 16 + c16;
-        // 1/|x| by the hardware reciprocal square root (about 1 ulp: code decisions
-        // move only for coordinates far inside the boundary tolerance)
-        const float inv = ss[tb] > 0.f ? __builtin_amdgcn_rsqf(ss[tb]) : 0.f;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int c0 = 16 * (wave * RB + rb) + 4 * kq;  // first of the lane's 4 coordinates
-          uint32_t bytes = 0, hi2[2], lo2[2];
-          float res[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float y = acc[rb][tb][r] * inv;
-            uint32_t idx = 0;
-            // pure QJL keys have no codes: the residual is y itself
-            res[r] = B > 0 ? y - code(y, idx) : y;
-            bytes |= idx << (7 * r);
-            if constexpr (SK) rp[tb] = fmaf(res[r], res[r], rp[tb]);
-          }
-          // code fields of 4 coordinates: granule c0 / 16, dword (c0 / 4) % 4
-          stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
-          if constexpr (SK) {
-            split2(res[0], res[1], hi2[0], lo2[0]);
-            split2(res[2], res[3], hi2[1], lo2[1]);
-            // residual parts: granule c0 / 8 of 16, half (c0 / 4) % 2
-            const int gr = swz(tok, 16, c0 >> 3, 15) * 8 + ((c0 >> 2) & 1) * 4;
-            *reinterpret_cast<uint2 *>(&rt[0][gr]) = make_uint2(hi2[0], hi2[1]);
-            *reinterpret_cast<uint2 *>(&rt[1][gr]) = make_uint2(lo2[0], lo2[1]);
-          }
-        }
-      }
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        rp[tb] += __shfl_xor(rp[tb], 16);
-        rp[tb] += __shfl_xor(rp[tb], 32);
-      }
-      if (SK && kq == 0) {
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) rho2[wave][tb * 16 + c16] = rp[tb];
-      }
-      __syncthreads();
-      if constexpr (SK) {
-      // ---- product 2: z[sketch row][token] = S r, signs into bit 6 of the code fields
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[rb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const int g = swz(tb * 16 + c16, 16, ks * 4 + kq, 15) * 8;
-          const bf16x8 rh = ld_bf8(&rt[0][g]), rl = ld_bf8(&rt[1][g]);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[rb][ks][0], rh, acc[rb][tb], 0, 0, 0);
-            acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[rb][ks][0], rl, acc[rb][tb], 0, 0, 0);
-            acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[rb][ks][1], rh, acc[rb][tb], 0, 0, 0);
-          }
-        }
-      }
+    for (int tb = 0; tb < 4; ++tb) {
+      const float4 inv4 = *reinterpret_cast<const float4 *>(&ninv[tb * 16 + 4 * kq]);
+      const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int c0 = 16 * (wave * RB + rb) + 4 * kq;
+        const int j = 16 * (wave * RB + rb) + c16;
+        uint32_t bytes = 0;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const int tok = tb * 16 + c16;
-          uint32_t sg = 0;
+        for (int r = 0; r < 4; ++r) bytes |= code(acc[rb][tb][r] * inv[r]) << (7 * r);
+        // tokens tb*16 + 4kq .. +3 of coordinate j: granule tb, dword kq
+        stage[swz(j, 4, tb, 3) * 4 + kq] = bytes;
+      }
+    }
+    __syncthreads();
+    if (more) stage_x(xr);  // every wave is past its reads of this tile's X and norms
+    // ---- pack: thread (coordinate, 32-token block) -> B token-major code planes
+    if (tid < 4 * QT) {
+      const uint64_t lmask = __builtin_amdgcn_ballot_w64(lane < nv && nrm[lane] > 0.f);  // live tokens
+      const int jj = tid >> 1, hb = tid & 1;
+      const int nb = nv - 32 * hb;  // valid tokens of this block
+      if (nb > 0) {
+        const uint32_t live = (uint32_t)(lmask >> (32 * hb));
+        const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb, 3) * 4]);
+        const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb + 1, 3) * 4]);
+        const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        const int64_t blk = a.map.rec(s, t0 + 32 * hb) >> 5;  // blocks never straddle pages
+        uint32_t *dst = a.bits_out + (blk * QD + jj) * B;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sg |= (acc[rb][tb][r] >= 0.f ? (1u << QJL_FIELD_BIT) : 0u) << (7 * r);
-          atomicOr(&stage[swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)], sg);
+        for (int p = 0; p < B; ++p) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) word |= gather4(d8[m], p) << (4 * m);
+          dst[p] = word & live;
         }
       }
-      __syncthreads();
-      }  // sketch stage
-      if (more) stage_x(xr);  // every wave is past its reads of this tile's X and norms
-      // ---- pack: thread (token, 32-coordinate group, half) -> half of the B code
-      // planes (+ the sign plane): planes [PH0 h, PH0 h + PH0) of the record's NPL
-      // words, so that all eight waves share the gathers
-      constexpr int PH0 = (NPL + 1) / 2;
-      static_assert(!KEYS || NT == 8 * QT, "keys pack: two threads per (token, group)");
-      if (tid < 8 * QT) {
-        const int tok = (tid >> 2) & (QT - 1), g = tid & 3, h = tid >> 8;
-        if (tok < nv) {
-          const int64_t rec = a.map.rec(s, t0 + tok);
-          const float n = nrm[tok];
-          uint32_t w[PH0];
-          if (n > 0.f) {
-            const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g, 7) * 4]);
-            const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(tok, 8, 2 * g + 1, 7) * 4]);
-            const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-            for (int i = 0; i < PH0; ++i) {
-              const int p = PH0 * h + i;
-              const int bit = p < B ? p : QJL_FIELD_BIT;
-              uint32_t word = 0;
-#pragma unroll
-              for (int m = 0; m < 8; ++m) word |= gather4(d8[m], bit) << (4 * m);
-              w[i] = word;
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < PH0; ++i) w[i] = 0u;
-          }
-          uint32_t *dst = a.bits_out + (rec * QW + g) * NPL + PH0 * h;
-          if constexpr (NPL == 4) {
-            *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < PH0; ++i)
-              if (PH0 * h + i < NPL) dst[i] = w[i];
-          }
-          if (g == 0 && h == 0) {
-            if constexpr (SK) {
-              float r2 = 0.f;
-#pragma unroll
-              for (int v = 0; v < NW; ++v) r2 += rho2[v][tok];
-              store_norm(a.norms_out, 2 * rec, n, a.nf16);
-              store_norm(a.norms_out, 2 * rec + 1, n > 0.f ? sqrtf(r2) : 0.f, a.nf16);
-            } else {
-              store_norm(a.norms_out, rec, n, a.nf16);
-            }
-          }
-        }
-      }
-    } else {
-      __syncthreads();  // norms of every token
-      // acc[rb][tb][r] = |x| y[token tb*16 + 4kq + r][coordinate 16 (wave RB + rb) + c16]
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const float4 inv4 = *reinterpret_cast<const float4 *>(&ninv[tb * 16 + 4 * kq]);
-        const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int j = 16 * (wave * RB + rb) + c16;
-          uint32_t bytes = 0;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            uint32_t idx;
-            (void)code(acc[rb][tb][r] * inv[r], idx);
-            bytes |= idx << (7 * r);
-          }
-          // tokens tb*16 + 4kq .. +3 of coordinate j: granule tb, dword kq
-          stage[swz(j, 4, tb, 3) * 4 + kq] = bytes;
-        }
-      }
-      __syncthreads();
-      if (more) stage_x(xr);  // every wave is past its reads of this tile's X and norms
-      // ---- pack: thread (coordinate, 32-token block) -> B token-major code planes
-      if (tid < 4 * QT) {
-        const uint64_t lmask = __builtin_amdgcn_ballot_w64(lane < nv && nrm[lane] > 0.f);  // live tokens
-        const int jj = tid >> 1, hb = tid & 1;
-        const int nb = nv - 32 * hb;  // valid tokens of this block
-        if (nb > 0) {
-          const uint32_t live = (uint32_t)(lmask >> (32 * hb));
-          const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb, 3) * 4]);
-          const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb + 1, 3) * 4]);
-          const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-          const int64_t blk = a.map.rec(s, t0 + 32 * hb) >> 5;  // blocks never straddle pages
-          uint32_t *dst = a.bits_out + (blk * QD + jj) * B;
-#pragma unroll
-          for (int p = 0; p < B; ++p) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) word |= gather4(d8[m], p) << (4 * m);
-            dst[p] = word & live;
-          }
-        }
-        if (tid < nv) store_norm(a.norms_out, a.map.rec(s, t0 + tid), nrm[tid], a.nf16);
-      }
+      if (tid < nv) store_norm(a.norms_out, a.map.rec(s, t0 + tid), nrm[tid], a.nf16);
     }
     // the staging buffers are reused only after the next iteration's first barrier
     s = sn;
@@ -768,41 +606,346 @@ __global__ void __launch_bounds__(64 * NW, 2) quant128_kernel(Q128Args a) {
   }
 }
 
-// Persistent launch: as many work-groups as fit on the device at once (registers
-// decide: keys one per compute unit, values two), at most one per tile.
+// Keys with specialised waves. A work-group of sixteen waves: waves 0..7 (math)
+// issue both products on the matrix core, waves 8..15 (epilogue) do the VALU
+// work: codes, residual split, packing and the X staging. Each SIMD runs two
+// waves of each kind, so the matrix core works through the math waves' MFMAs
+// while the epilogue waves issue VALU instructions (the phase-ordered kernel
+// runs every wave through the same phase at once, and the two never overlap).
+// Math wave m owns the output coordinates (and sketch rows) 16m .. 16m + 15,
+// with its rows of the Pi and S parts in registers; epilogue wave m owns the
+// same coordinates of y. Tiles go through a pipeline of two phases per step j,
+// a barrier after each:
+//   phase 1  math: product 1 of tile j (y to LDS)
+//            epilogue: pack of tile j - 2, loads of X for tile j + 1
+//   phase 2  math: product 2 of tile j - 1 (sign bits into its code fields)
+//            epilogue: codes and residual parts of tile j, X of tile j + 1 to LDS
+// Buffers written in one step and read two steps on (codes, residual parts,
+// norms, |r|^2 partials) alternate by tile parity; y and X are single buffers.
+template <int B, bool SK>
+__global__ void __launch_bounds__(1024) quant128_keys_kernel(Q128Args a) {
+  constexpr int NPL = B + (SK ? 1 : 0);
+  constexpr int H = B > 0 ? 1 << (B - 1) : 1;
+  constexpr int NE = 512;            // epilogue threads
+  constexpr int XG = QT * 16 / NE;   // X granules per epilogue thread
+  constexpr int PH0 = (NPL + 1) / 2; // pack: planes per thread (two threads per token and group)
+  __shared__ __attribute__((aligned(16))) uint4 xs[QT * 16];    // X tile, swizzled as in quant128_values_kernel
+  __shared__ __attribute__((aligned(16))) f4v yb[8 * 4 * 64];   // y: [wave][tb][lane] (|x| y, 4 coordinates)
+  __shared__ __attribute__((aligned(16))) uint32_t stage[2][QT * QD / 4];
+  __shared__ __attribute__((aligned(16))) uint16_t rt[SK ? 2 : 1][2][SK ? QT * QD : 8];
+  __shared__ float ssq[2][QT], nrm[2][QT];
+  __shared__ float rho2[2][8][QT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool math = wave < 8;
+  const int m = wave & 7;  // coordinates 16m .. 16m + 15 (either role)
+  const int c16 = lane & 15, kq = lane >> 4;
+  const int te = tid - NE;  // epilogue thread index
+  const int64_t tps = (a.n_tokens + QT - 1) / QT, total = tps * a.n_streams;
+  const int64_t tile0 = blockIdx.x;
+  if (tile0 >= total) return;
+  const int T = (int)((total - 1 - tile0) / gridDim.x) + 1;  // tiles of this work-group
+  // (stream, tile in the stream) of tile j: tile0 + j * gridDim.x, advanced by the
+  // grid size without a division per step
+  const int64_t dS = (int64_t)gridDim.x / tps, dR = (int64_t)gridDim.x % tps;
+  struct TilePos {
+    int64_t s, tr;
+  };
+  auto advance = [&](TilePos &p) {
+    p.s += dS;
+    p.tr += dR;
+    if (p.tr >= tps) {
+      p.tr -= tps;
+      ++p.s;
+    }
+  };
+  if (math) {
+    // rows 16m + c16 of the Pi parts and of the S parts
+    bf16x8 pf[4][3];
+    bf16x8 sf[SK ? 4 : 1][2];
+    {
+      const int r = 16 * m + c16;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) pf[ks][sp] = ld_bf8(a.rot3 + (sp * QD + r) * QD + ks * 32 + kq * 8);
+        if constexpr (SK) {
+#pragma unroll
+          for (int sp = 0; sp < 2; ++sp) sf[ks][sp] = ld_bf8(a.sk2 + (sp * QD + r) * QD + ks * 32 + kq * 8);
+        }
+      }
+    }
+    // The two roles run separate loops with the same barriers (one for the first
+    // X tile, then two per step), so the register-resident Pi and S parts are not
+    // live through the epilogue code.
+    __syncthreads();
+    for (int j = 0; j < T + 2; ++j) {
+      // ---- phase 1: product 1 of tile j
+      if (j < T) {
+        f4v acc[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[tb] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8 xf[4];
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            const int t = tb * 16 + c16;
+            xf[tb] = __builtin_bit_cast(bf16x8, xs[t * 16 + ((ks * 4 + kq) ^ (t & 15))]);
+          }
+#pragma unroll
+          for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+              acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ks][sp], xf[tb], acc[tb], 0, 0, 0);
+        }
+        // acc[tb][r] = |x| y[coordinate 16m + 4kq + r][token tb*16 + c16]
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) yb[(m * 4 + tb) * 64 + lane] = acc[tb];
+      }
+      __syncthreads();
+      // ---- phase 2: product 2 of tile j - 1, z[sketch row][token] = S r; signs into
+      // bit 6 of the code fields
+      if constexpr (SK) {
+        if (j >= 1 && j <= T) {
+          const int pb = (j - 1) & 1;
+          f4v acc[4];
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) acc[tb] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+              const int g = swz(tb * 16 + c16, 16, ks * 4 + kq, 15) * 8;
+              const bf16x8 rh = ld_bf8(&rt[pb][0][g]), rl = ld_bf8(&rt[pb][1][g]);
+              acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][0], rh, acc[tb], 0, 0, 0);
+              acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][0], rl, acc[tb], 0, 0, 0);
+              acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][1], rh, acc[tb], 0, 0, 0);
+            }
+          }
+          const int c0 = 16 * m + 4 * kq;
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            const int tok = tb * 16 + c16;
+            uint32_t sg = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sg |= (acc[tb][r] >= 0.f ? (1u << QJL_FIELD_BIT) : 0u) << (7 * r);
+            atomicOr(&stage[pb][swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)], sg);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  float tp[H > 1 ? H - 1 : 1];
+  uint32_t cb0 = 0, cd[H > 1 ? H - 1 : 1];
+  if constexpr (B > 0) {
+#pragma unroll
+    for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
+    cb0 = __float_as_uint(a.tables->centroid[B][H]);
+#pragma unroll
+    for (int j = 0; j < H - 1; ++j)
+      cd[j] = __float_as_uint(a.tables->centroid[B][H + j]) ^ __float_as_uint(a.tables->centroid[B][H + j + 1]);
+  }
+  auto code = [&](float y, uint32_t &idx) {
+    const float ay = fabsf(y);
+    uint32_t mag = 0, cbits = cb0;
+#pragma unroll
+    for (int j = 0; j < H - 1; ++j) {
+      const bool ge = ay >= tp[j];
+      mag += ge ? 1u : 0u;
+      cbits ^= ge ? cd[j] : 0u;
+    }
+    idx = ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
+    return __builtin_copysignf(__uint_as_float(cbits), y);
+  };
+  // X granule P of tile j (rows past the stream's end re-read its last token),
+  // and its staging with the tokens' squared norms (the 16 granules of a token
+  // are 16 consecutive threads: a 16-lane shuffle sum)
+  auto x_load = [&](const TilePos &p, uint4 (&v)[XG]) {
+    const int64_t s = p.s, t0 = p.tr * QT;
+    const int last = (int)min((int64_t)QT, a.n_tokens - t0) - 1;
+#pragma unroll
+    for (int i = 0; i < XG; ++i) {
+      const int P = i * NE + te, t = P >> 4, g = (P & 15) ^ (t & 15);
+      v[i] = *reinterpret_cast<const uint4 *>(a.x + s * a.xs + (t0 + min(t, last)) * a.xt + g * 8);
+    }
+  };
+  auto x_stage = [&](const uint4 (&v)[XG], int buf) {
+#pragma unroll
+    for (int i = 0; i < XG; ++i) {
+      xs[i * NE + te] = v[i];
+      float q = sumsq8(__builtin_bit_cast(bf16x8, v[i]), 0.f);
+      q += __shfl_xor(q, 1);
+      q += __shfl_xor(q, 2);
+      q += __shfl_xor(q, 4);
+      q += __shfl_xor(q, 8);
+      if ((te & 15) == 0) ssq[buf][(i * NE + te) >> 4] = q;
+    }
+  };
+  uint4 xr[XG];
+  TilePos xp = {tile0 / tps, tile0 % tps};  // tile of the next X load
+  TilePos pp = xp;                          // tile of the next pack
+  x_load(xp, xr);
+  x_stage(xr, 0);
+  __syncthreads();
+  for (int j = 0; j < T + 2; ++j) {
+    // ---- phase 1: loads of X for tile j + 1; pack of tile j - 2, thread (token,
+    // 32-coordinate group, half) -> half of the NPL words, and the token's norms
+    if (j + 1 < T) {
+      advance(xp);
+      x_load(xp, xr);
+    }
+    if (j >= 2) {
+      const int pb = j & 1;
+      const int64_t s = pp.s, t0 = pp.tr * QT;
+      advance(pp);
+      const int nv = (int)min((int64_t)QT, a.n_tokens - t0);
+      const int tok = (te >> 2) & (QT - 1), g = te & 3, h = te >> 8;
+      if (tok < nv) {
+        const int64_t rec = a.map.rec(s, t0 + tok);
+        const float n = nrm[pb][tok];
+        uint32_t w[PH0];
+        if (n > 0.f) {
+          const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[pb][swz(tok, 8, 2 * g, 7) * 4]);
+          const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[pb][swz(tok, 8, 2 * g + 1, 7) * 4]);
+          const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+          for (int i = 0; i < PH0; ++i) {
+            const int p = PH0 * h + i;
+            const int bit = p < B ? p : QJL_FIELD_BIT;
+            uint32_t word = 0;
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) word |= gather4(d8[mm], bit) << (4 * mm);
+            w[i] = word;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < PH0; ++i) w[i] = 0u;
+        }
+        uint32_t *dst = a.bits_out + (rec * QW + g) * NPL + PH0 * h;
+        if constexpr (NPL == 4) {
+          *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < PH0; ++i)
+            if (PH0 * h + i < NPL) dst[i] = w[i];
+        }
+        if (g == 0 && h == 0) {
+          if constexpr (SK) {
+            float r2 = 0.f;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) r2 += rho2[pb][v][tok];
+            store_norm(a.norms_out, 2 * rec, n, a.nf16);
+            store_norm(a.norms_out, 2 * rec + 1, n > 0.f ? sqrtf(r2) : 0.f, a.nf16);
+          } else {
+            store_norm(a.norms_out, rec, n, a.nf16);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- phase 2: codes and residual parts of tile j; X of tile j + 1 to LDS
+    // (product 1 of tile j is done with the current X)
+    if (j < T) {
+      const int cb = j & 1;
+      float ss[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) ss[tb] = ssq[cb][tb * 16 + c16];
+      if (m == 0 && kq == 0) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) nrm[cb][tb * 16 + c16] = sqrtf(ss[tb]);
+      }
+      float rp[4] = {0.f, 0.f, 0.f, 0.f};
+      const int c0 = 16 * m + 4 * kq;  // first of the lane's 4 coordinates
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int tok = tb * 16 + c16;
+        // 1/|x| by the hardware reciprocal square root (about 1 ulp: code decisions
+        // move only for coordinates far inside the boundary tolerance)
+        const float inv = ss[tb] > 0.f ? __builtin_amdgcn_rsqf(ss[tb]) : 0.f;
+        const f4v y4 = yb[(m * 4 + tb) * 64 + lane];
+        uint32_t bytes = 0;
+        float res[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float y = y4[r] * inv;
+          uint32_t idx = 0;
+          res[r] = B > 0 ? y - code(y, idx) : y;  // pure QJL keys: the residual is y itself
+          bytes |= idx << (7 * r);
+          if constexpr (SK) rp[tb] = fmaf(res[r], res[r], rp[tb]);
+        }
+        stage[cb][swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
+        if constexpr (SK) {
+          uint32_t hi2[2], lo2[2];
+          split2(res[0], res[1], hi2[0], lo2[0]);
+          split2(res[2], res[3], hi2[1], lo2[1]);
+          const int gr = swz(tok, 16, c0 >> 3, 15) * 8 + ((c0 >> 2) & 1) * 4;
+          *reinterpret_cast<uint2 *>(&rt[cb][0][gr]) = make_uint2(hi2[0], hi2[1]);
+          *reinterpret_cast<uint2 *>(&rt[cb][1][gr]) = make_uint2(lo2[0], lo2[1]);
+        }
+      }
+      if constexpr (SK) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          rp[tb] += __shfl_xor(rp[tb], 16);
+          rp[tb] += __shfl_xor(rp[tb], 32);
+        }
+        if (kq == 0) {
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) rho2[cb][m][tb * 16 + c16] = rp[tb];
+        }
+      }
+    }
+    if (j + 1 < T) x_stage(xr, (j + 1) & 1);
+    __syncthreads();
+  }
+}
+
+// Persistent launch: as many work-groups as fit on the device at once (keys one
+// per compute unit, values two), at most one per tile.
 template <bool KEYS, int B, bool QJL>
 static hipError_t launch_quant128_b(const Q128Args &q, hipStream_t st) {
-  constexpr int NW = KEYS ? 8 : 4;
+  const void *fn;
+  if constexpr (KEYS) fn = reinterpret_cast<const void *>(&quant128_keys_kernel<B, QJL>);
+  else fn = reinterpret_cast<const void *>(&quant128_values_kernel<B>);
+  const int nt = KEYS ? 1024 : 256;
   static int resident = 0;  // work-groups resident on the device
   if (resident == 0) {
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e;
     if ((e = hipGetDevice(&dev)) != hipSuccess ||
         (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess ||
-        (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant128_kernel<KEYS, B, NW, QJL>, 64 * NW, 0)) !=
-            hipSuccess)
+        (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, nt, 0)) != hipSuccess)
       return e;
     resident = std::max(1, cus * std::max(1, per_cu));
   }
   const int64_t tiles = ((q.n_tokens + QT - 1) / QT) * q.n_streams;
   const unsigned nwg = (unsigned)std::min<int64_t>(tiles, resident);
-  hipLaunchKernelGGL((quant128_kernel<KEYS, B, NW, QJL>), dim3(nwg), dim3(64 * NW), 0, st, q);
+  if constexpr (KEYS)
+    hipLaunchKernelGGL((quant128_keys_kernel<B, QJL>), dim3(nwg), dim3(1024), 0, st, q);
+  else
+    hipLaunchKernelGGL((quant128_values_kernel<B>), dim3(nwg), dim3(256), 0, st, q);
   return hipGetLastError();
 }
 
 // keys: B = 0..4 with the sketch (0 = pure QJL), 1..4 without (MSE-only); values: 1..4
 template <bool KEYS>
 static hipError_t launch_quant128(const Q128Args &q, int bits, bool qjl, hipStream_t st) {
-  if (KEYS && qjl) {
-    switch (bits) {
-      case 0: return launch_quant128_b<KEYS, 0, true>(q, st);
-      case 1: return launch_quant128_b<KEYS, 1, true>(q, st);
-      case 2: return launch_quant128_b<KEYS, 2, true>(q, st);
-      case 3: return launch_quant128_b<KEYS, 3, true>(q, st);
-      case 4: return launch_quant128_b<KEYS, 4, true>(q, st);
-      default: return hipErrorInvalidValue;
+  if constexpr (KEYS) {
+    if (qjl) {
+      switch (bits) {
+        case 0: return launch_quant128_b<true, 0, true>(q, st);
+        case 1: return launch_quant128_b<true, 1, true>(q, st);
+        case 2: return launch_quant128_b<true, 2, true>(q, st);
+        case 3: return launch_quant128_b<true, 3, true>(q, st);
+        case 4: return launch_quant128_b<true, 4, true>(q, st);
+        default: return hipErrorInvalidValue;
+      }
     }
   }
+  (void)qjl;
   switch (bits) {
     case 1: return launch_quant128_b<KEYS, 1, false>(q, st);
     case 2: return launch_quant128_b<KEYS, 2, false>(q, st);
