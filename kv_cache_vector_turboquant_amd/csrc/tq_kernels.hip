@@ -738,27 +738,60 @@ __global__ void __launch_bounds__(1024) quant128_keys_kernel(Q128Args a) {
     }
     return;
   }
+  // positive boundaries t_j (between magnitudes j and j + 1) and the centroid
+  // magnitudes, the latter copied into VGPRs once (as select operands they would
+  // otherwise be copied from SGPRs at every use)
   float tp[H > 1 ? H - 1 : 1];
-  uint32_t cb0 = 0, cd[H > 1 ? H - 1 : 1];
+  uint32_t cvg[H], mvg[H];  // leaves of the select tree (opaque to the compiler, which
+                            // otherwise turns the tree into compares of the code)
   if constexpr (B > 0) {
 #pragma unroll
     for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
-    cb0 = __float_as_uint(a.tables->centroid[B][H]);
 #pragma unroll
-    for (int j = 0; j < H - 1; ++j)
-      cd[j] = __float_as_uint(a.tables->centroid[B][H + j]) ^ __float_as_uint(a.tables->centroid[B][H + j + 1]);
-  }
-  auto code = [&](float y, uint32_t &idx) {
-    const float ay = fabsf(y);
-    uint32_t mag = 0, cbits = cb0;
-#pragma unroll
-    for (int j = 0; j < H - 1; ++j) {
-      const bool ge = ay >= tp[j];
-      mag += ge ? 1u : 0u;
-      cbits ^= ge ? cd[j] : 0u;
+    for (int i = 0; i < H; ++i) {
+      const uint32_t c = __float_as_uint(a.tables->centroid[B][H + i]);
+      asm("v_mov_b32 %0, %1" : "=v"(cvg[i]) : "s"(c));
+      asm("v_mov_b32 %0, %1" : "=v"(mvg[i]) : "i"(H + i));
     }
-    idx = ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
-    return __builtin_copysignf(__uint_as_float(cbits), y);
+  }
+  // magnitude code H + mag of y (mag = #{t_j <= |y|}) and the centroid magnitude,
+  // by a binary tree of selects over the H magnitudes: node [i, i + 2w) takes its
+  // upper half when |y| >= t_(i + w - 1), one compare per boundary and H - 1
+  // selects each
+  auto code = [&](float y, uint32_t &hm) {
+    const float ay = fabsf(y);
+    // one tree level: pairs (i, i + w) at i = 0, 2w, 4w, .. take the upper value
+    // when |y| >= t_(i + w - 1)
+    auto sel = [&](int j, uint32_t lo, uint32_t hi) { return ay >= tp[j] ? hi : lo; };
+    uint32_t c, h;
+    if constexpr (H == 1) {
+      c = cvg[0];
+      h = mvg[0];
+    } else if constexpr (H == 2) {
+      const bool g = ay >= tp[0];
+      c = g ? cvg[1] : cvg[0];
+      h = g ? mvg[1] : mvg[0];
+    } else if constexpr (H == 4) {
+      const bool g0 = ay >= tp[0], g1 = ay >= tp[1], g2 = ay >= tp[2];
+      const uint32_t cl = g0 ? cvg[1] : cvg[0], ch = g2 ? cvg[3] : cvg[2];
+      const uint32_t hl = g0 ? mvg[1] : mvg[0], hh = g2 ? mvg[3] : mvg[2];
+      c = g1 ? ch : cl;
+      h = g1 ? hh : hl;
+    } else {
+      const bool g0 = ay >= tp[0], g1 = ay >= tp[1], g2 = ay >= tp[2], g3 = ay >= tp[3];
+      const bool g4 = ay >= tp[4], g5 = ay >= tp[5], g6 = ay >= tp[6];
+      const uint32_t c0 = g0 ? cvg[1] : cvg[0], c1 = g2 ? cvg[3] : cvg[2];
+      const uint32_t c2 = g4 ? cvg[5] : cvg[4], c3 = g6 ? cvg[7] : cvg[6];
+      const uint32_t h0 = g0 ? mvg[1] : mvg[0], h1 = g2 ? mvg[3] : mvg[2];
+      const uint32_t h2 = g4 ? mvg[5] : mvg[4], h3 = g6 ? mvg[7] : mvg[6];
+      const uint32_t c01 = g1 ? c1 : c0, c23 = g5 ? c3 : c2;
+      const uint32_t h01 = g1 ? h1 : h0, h23 = g5 ? h3 : h2;
+      c = g3 ? c23 : c01;
+      h = g3 ? h23 : h01;
+    }
+    (void)sel;
+    hm = h;
+    return __builtin_copysignf(__uint_as_float(c), y);
   };
   // X granule P of tile j (rows past the stream's end re-read its last token),
   // and its staging with the tokens' squared norms (the 16 granules of a token
@@ -866,16 +899,20 @@ __global__ void __launch_bounds__(1024) quant128_keys_kernel(Q128Args a) {
         // move only for coordinates far inside the boundary tolerance)
         const float inv = ss[tb] > 0.f ? __builtin_amdgcn_rsqf(ss[tb]) : 0.f;
         const f4v y4 = yb[(m * 4 + tb) * 64 + lane];
-        uint32_t bytes = 0;
+        // code fields: H + mag, mirrored to 2H - 1 - (H + mag) for a negative y (the
+        // sign's all-ones mask XORs 2H - 1 into the field)
+        uint32_t bytes = 0, neg = 0;
         float res[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float y = y4[r] * inv;
-          uint32_t idx = 0;
-          res[r] = B > 0 ? y - code(y, idx) : y;  // pure QJL keys: the residual is y itself
-          bytes |= idx << (7 * r);
+          uint32_t hm = 0;
+          res[r] = B > 0 ? y - code(y, hm) : y;  // pure QJL keys: the residual is y itself
+          bytes |= hm << (7 * r);
+          neg |= ((uint32_t)(__float_as_int(y) >> 31) & (uint32_t)(2 * H - 1)) << (7 * r);
           if constexpr (SK) rp[tb] = fmaf(res[r], res[r], rp[tb]);
         }
+        if constexpr (B > 0) bytes ^= neg;
         stage[cb][swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
         if constexpr (SK) {
           uint32_t hi2[2], lo2[2];
