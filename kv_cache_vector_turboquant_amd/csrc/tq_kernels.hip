@@ -760,9 +760,6 @@ __global__ void __launch_bounds__(1024) quant128_keys_kernel(Q128Args a) {
   // selects each
   auto code = [&](float y, uint32_t &hm) {
     const float ay = fabsf(y);
-    // one tree level: pairs (i, i + w) at i = 0, 2w, 4w, .. take the upper value
-    // when |y| >= t_(i + w - 1)
-    auto sel = [&](int j, uint32_t lo, uint32_t hi) { return ay >= tp[j] ? hi : lo; };
     uint32_t c, h;
     if constexpr (H == 1) {
       c = cvg[0];
@@ -789,7 +786,6 @@ __global__ void __launch_bounds__(1024) quant128_keys_kernel(Q128Args a) {
       c = g3 ? c23 : c01;
       h = g3 ? h23 : h01;
     }
-    (void)sel;
     hm = h;
     return __builtin_copysignf(__uint_as_float(c), y);
   };
