@@ -2110,6 +2110,14 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       }
       if constexpr (LOGITS) return;  // every wave of the work-group, before any barrier
     }
+    // the softmax reads rounds of 256 tokens: positions from n to the end of the last
+    // round get -inf logits and zero norms (the key phase may write the same values to
+    // some of them), so every token's weight comes out of exp2 without a select
+    for (int t = n + tid; t < ((n + 255) & ~255); t += 256) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) lg[h * a.chunk + t] = -INFINITY;
+      vnl[t] = 0.f;
+    }
     // the first value blocks are requested before the softmax
     const int vn = lane & 15, vg = lane >> 4;  // coordinate column, token block in the 128-token group
     struct VBuf {
@@ -2147,7 +2155,10 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     // (the wave of an absent head writes zero weights: every value A byte that
     // phase V reads is written here, so the fragments need no clearing)
     {
-      const float m = fmaxf(fmaxf(lred[0][wave], lred[1][wave]), fmaxf(lred[2][wave], lred[3][wave]));
+      // a head that sees no token of the chunk has m = -inf: it is taken as 0 here, so
+      // that every exp2 below is 0 rather than NaN (the partial keeps -inf)
+      const float mh = fmaxf(fmaxf(lred[0][wave], lred[1][wave]), fmaxf(lred[2][wave], lred[3][wave]));
+      const float m = mh == -INFINITY ? 0.f : mh;
       // token t = lane + 64 i: q = t & 7 = lane & 7 is fixed per lane, and so is
       // its weight scale 2^(29 - q) / vmax (negated for q = 7, whose B byte is -128)
       const int qv = lane & 7;
@@ -2158,16 +2169,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       const int lbase = (((lane >> 2) & 1) << 10) | (((lane >> 5) & 1) << 8) | (wave << 6) | ((lane & 3) << 2) |
                         ((lane >> 3) & 3);
       // four independent iterations per round (tokens t = lane + 64 i); rounds run to
-      // a multiple of 256 tokens, inside the chunk's LDS: tokens past n get p = W = 0
-      // (their logits and norms in LDS are stale and never used)
+      // a multiple of 256 tokens, inside the chunk's LDS. Tokens past n and tokens the
+      // head does not see (causal mask) hold -inf logits, so p = W = 0 for them. The
+      // rows of an absent head (wave >= nh) get weights that nothing reads.
       float l = 0.f;
       const float *lgw = lg + wave * a.chunk + lane;
       const float *vnw = vnl + lane;
       const int nit = (n + 63) >> 6;
-      const int nw = wave < nh ? vis(wave) : 0;  // tokens this head sees (all n without the causal mask)
       for (int i0 = 0; i0 < nit; i0 += 4) {
-        // the round's LDS reads first, then branch-free arithmetic (dead tokens'
-        // values are computed and discarded by the selects)
+        // the round's LDS reads first, then branch-free arithmetic
         float lv[4], nv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -2176,12 +2186,10 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int i = i0 + j;
-          const bool live = lane + 64 * i < nw;
-          const float e = __builtin_amdgcn_exp2f(lv[j] - m);  // <= 1; tiny values round to W = 0
-          l += live ? e : 0.f;
-          const int Wl = (int)rintf(e * nv[j] * wq);
-          const int W = live ? Wl : 0;
+          const float e = __builtin_amdgcn_exp2f(lv[j] - m);  // <= 1; 0 for a -inf logit
+          l += e;
+          // fixed point by truncation: an error below one unit of 2^-29 of the largest weight
+          const int W = (int)(e * nv[j] * wq);
           const uint32_t x = ((uint32_t)W + 0x80808080u) ^ 0x80808080u;  // four signed base-256 digits
           int8_t *dst = av + lbase + ((i0 >> 1) << 11) + ((j >> 1) << 11) + ((j & 1) << 9);
           dst[0] = (int8_t)x;
@@ -2192,7 +2200,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       }
       for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
       if (lane == 0) {
-        hmax[wave] = m;
+        hmax[wave] = mh;
         hsum[wave] = l;
       }
     }
@@ -2244,21 +2252,23 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       vcompute(vbase, vb_b);
       vbase += VGPI;
     }
-    // flush: lane (coordinate vn, head vg) holds digits 0..3 of every mask sum
+    // flush: lane (coordinate vn, head vg) holds digits 0..3 of every mask sum.
+    // The digit sums (|x| < 2^24) convert exactly; the base-256 combination and
+    // 2 M - W are rounded in fp32: the error of a partial is a few units of 2^-24
+    // of sum_t p_t |v_t| (relative to the partial's own sum l, at most 2^-22 of the
+    // chunk's largest |v|), far below the attention tolerance
     if (vg < nh) {
-      const double W = (double)accw[0] + 256.0 * (double)accw[1] + 65536.0 * (double)accw[2] +
-                       16777216.0 * (double)accw[3];
-      const double unit = (double)vmax / (double)WSCALE;
+      auto digits = [](const i4v &x) {
+        return fmaf(16777216.f, (float)x[3], fmaf(65536.f, (float)x[2], fmaf(256.f, (float)x[1], (float)x[0])));
+      };
+      const float W = digits(accw);
+      const float unit = vmax * (1.f / WSCALE);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        double o = 0.0;
+        float o = 0.f;
 #pragma unroll
-        for (int mi = 0; mi < VM; ++mi) {
-          const i4v &x = accv[nt][mi];
-          const double M = (double)x[0] + 256.0 * (double)x[1] + 65536.0 * (double)x[2] + 16777216.0 * (double)x[3];
-          o += (double)wv[mi] * (2.0 * M - W);
-        }
-        part(vg)[wave * 32 + nt * 16 + vn] = (float)(o * unit);
+        for (int mi = 0; mi < VM; ++mi) o = fmaf(wv[mi], fmaf(2.f, digits(accv[nt][mi]), -W), o);
+        part(vg)[wave * 32 + nt * 16 + vn] = o * unit;
       }
     }
     if (tid < nh) {
