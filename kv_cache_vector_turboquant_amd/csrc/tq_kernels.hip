@@ -740,53 +740,48 @@ __global__ void __launch_bounds__(1024) quant128_keys_kernel(Q128Args a) {
   }
   // positive boundaries t_j (between magnitudes j and j + 1) and the centroid
   // magnitudes, the latter copied into VGPRs once (as select operands they would
-  // otherwise be copied from SGPRs at every use)
+  // otherwise be copied from SGPRs at every use). A leaf carries the magnitude
+  // index i in its HB lowest mantissa bits, so one select tree gives both the
+  // centroid and the code field; the centroid moves by at most 2^HB - 1 ulp
+  // (below 10^-6 of it), far inside the tolerances of the residual's norm and of
+  // the sketch signs.
+  constexpr int HB = B > 1 ? B - 1 : 0;
+  constexpr uint32_t HM = (1u << HB) - 1u;
   float tp[H > 1 ? H - 1 : 1];
-  uint32_t cvg[H], mvg[H];  // leaves of the select tree (opaque to the compiler, which
-                            // otherwise turns the tree into compares of the code)
+  uint32_t cvg[H];  // leaves of the select tree (opaque to the compiler, which
+                    // otherwise turns the tree into compares of the code)
   if constexpr (B > 0) {
 #pragma unroll
     for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
 #pragma unroll
     for (int i = 0; i < H; ++i) {
-      const uint32_t c = __float_as_uint(a.tables->centroid[B][H + i]);
+      const uint32_t c = (__float_as_uint(a.tables->centroid[B][H + i]) & ~HM) | (uint32_t)i;
       asm("v_mov_b32 %0, %1" : "=v"(cvg[i]) : "s"(c));
-      asm("v_mov_b32 %0, %1" : "=v"(mvg[i]) : "i"(H + i));
     }
   }
-  // magnitude code H + mag of y (mag = #{t_j <= |y|}) and the centroid magnitude,
-  // by a binary tree of selects over the H magnitudes: node [i, i + 2w) takes its
-  // upper half when |y| >= t_(i + w - 1), one compare per boundary and H - 1
-  // selects each
-  auto code = [&](float y, uint32_t &hm) {
+  // the magnitude index mag = #{t_j <= |y|} and the signed centroid of y, by a
+  // binary tree of selects over the H leaves: node [i, i + 2w) takes its upper
+  // half when |y| >= t_(i + w - 1), one compare per boundary and H - 1 selects
+  auto code = [&](float y, uint32_t &mag) {
     const float ay = fabsf(y);
-    uint32_t c, h;
+    uint32_t c;
     if constexpr (H == 1) {
       c = cvg[0];
-      h = mvg[0];
     } else if constexpr (H == 2) {
-      const bool g = ay >= tp[0];
-      c = g ? cvg[1] : cvg[0];
-      h = g ? mvg[1] : mvg[0];
+      c = ay >= tp[0] ? cvg[1] : cvg[0];
     } else if constexpr (H == 4) {
       const bool g0 = ay >= tp[0], g1 = ay >= tp[1], g2 = ay >= tp[2];
       const uint32_t cl = g0 ? cvg[1] : cvg[0], ch = g2 ? cvg[3] : cvg[2];
-      const uint32_t hl = g0 ? mvg[1] : mvg[0], hh = g2 ? mvg[3] : mvg[2];
       c = g1 ? ch : cl;
-      h = g1 ? hh : hl;
     } else {
       const bool g0 = ay >= tp[0], g1 = ay >= tp[1], g2 = ay >= tp[2], g3 = ay >= tp[3];
       const bool g4 = ay >= tp[4], g5 = ay >= tp[5], g6 = ay >= tp[6];
       const uint32_t c0 = g0 ? cvg[1] : cvg[0], c1 = g2 ? cvg[3] : cvg[2];
       const uint32_t c2 = g4 ? cvg[5] : cvg[4], c3 = g6 ? cvg[7] : cvg[6];
-      const uint32_t h0 = g0 ? mvg[1] : mvg[0], h1 = g2 ? mvg[3] : mvg[2];
-      const uint32_t h2 = g4 ? mvg[5] : mvg[4], h3 = g6 ? mvg[7] : mvg[6];
       const uint32_t c01 = g1 ? c1 : c0, c23 = g5 ? c3 : c2;
-      const uint32_t h01 = g1 ? h1 : h0, h23 = g5 ? h3 : h2;
       c = g3 ? c23 : c01;
-      h = g3 ? h23 : h01;
     }
-    hm = h;
+    mag = c & HM;
     return __builtin_copysignf(__uint_as_float(c), y);
   };
   // X granule P of tile j (rows past the stream's end re-read its last token),
@@ -902,13 +897,13 @@ __global__ void __launch_bounds__(1024) quant128_keys_kernel(Q128Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float y = y4[r] * inv;
-          uint32_t hm = 0;
-          res[r] = B > 0 ? y - code(y, hm) : y;  // pure QJL keys: the residual is y itself
-          bytes |= hm << (7 * r);
-          neg |= ((uint32_t)(__float_as_int(y) >> 31) & (uint32_t)(2 * H - 1)) << (7 * r);
+          uint32_t mg = 0;
+          res[r] = B > 0 ? y - code(y, mg) : y;  // pure QJL keys: the residual is y itself
+          bytes |= mg << (7 * r);
+          neg |= (uint32_t)(__float_as_int(y) >> 31) & ((uint32_t)(2 * H - 1) << (7 * r));
           if constexpr (SK) rp[tb] = fmaf(res[r], res[r], rp[tb]);
         }
-        if constexpr (B > 0) bytes ^= neg;
+        if constexpr (B > 0) bytes = (bytes | (uint32_t)H * 0x204081u) ^ neg;  // H in every 7-bit field
         stage[cb][swz(tok, 8, c0 >> 4, 7) * 4 + ((c0 >> 2) & 3)] = bytes;
         if constexpr (SK) {
           uint32_t hi2[2], lo2[2];
