@@ -309,6 +309,22 @@ def test_decode_full_cache_partial_chunk(c128, kbits):
     _run_decode_case(ctx, Pi, S, K, V, Q, [1000, cap], kbits, 3, cap)
 
 
+def test_decode_uniform_softmax_long_context(c128):
+    """A query of zero gives every token the same weight, so the output is the
+    mean of the dequantized values over the whole context: the case where each
+    chunk's value sums cancel the most (2 M_S - W for every Walsh mask, formed in
+    fp32 from exact int32 digit sums). 3000 tokens (three chunks), outlier-channel
+    V; the other heads of the group keep outlier-channel queries."""
+    ctx, Pi, S = c128
+    cap, L = 3072, 3000
+    K = synth.outlier_kv(9, (1,), synth.TAG_SCALES_K, (1, 2, L, 128))
+    V = synth.outlier_kv(9, (2,), synth.TAG_SCALES_V, (1, 2, L, 128))
+    Q = np.array(synth.outlier_kv(9, (3,), synth.TAG_SCALES_K, (1, 8, 128)))
+    Q[:, 0::2] = 0.0
+    worst = _run_decode_case(ctx, Pi, S, K, V, Q, [L], 3, 3, cap)
+    print(f"uniform softmax: max-abs error {worst:.2e}")
+
+
 @pytest.mark.parametrize("hq,qdtype", [(2, "f32"), (4, "bf16"), (16, "f32"), (32, "bf16")])
 def test_decode_group_sizes_gaussian(c128, hq, qdtype):
     """Gaussian K/V; 2 KV heads with query groups of 1, 2, 8 and 16 heads."""
