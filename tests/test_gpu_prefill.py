@@ -112,6 +112,26 @@ def test_prefill_gqa_ragged(c128, causal, qdtype):
     _check(out, Q, Pi, S, o, seq, scale, causal)
 
 
+@pytest.mark.parametrize("seq", [[1026, 3], [3, 1026]])
+def test_prefill_decode_path_heads_blind_in_a_chunk(c128, seq):
+    """Causal attention of 5 query positions (groups of one query head: 5 virtual
+    heads per KV head, so the decode kernels run, over head groups of 4). At
+    length 1026 the last 256-token chunk holds 2 tokens: positions 0-2 see none of
+    them while 3 and 4 do, in the same work-group (a head with no visible token
+    in a chunk whose others see some). At length 3 positions 0 and 1 see nothing
+    at all: their output is exactly zero."""
+    ctx, Pi, S = c128
+    B, H, cap, nq, hq = 2, 2, 1280, 5, 2
+    L = max(seq)
+    K = synth.outlier_kv(23, (1,), synth.TAG_SCALES_K, (B, H, L, 128))
+    V = synth.outlier_kv(23, (2,), synth.TAG_SCALES_V, (B, H, L, 128))
+    Q = synth.gaussian(23, (3,), (B, nq, hq, 128), "bf16")
+    cache, o = _cache(ctx, Pi, S, K, V, seq, 3, 3, cap)
+    scale = 1.0 / math.sqrt(128)
+    out = cache.attend(ctx, _dev(Q, "bf16"), True, scale).cpu().numpy()
+    _check(out, Q, Pi, S, o, seq, scale, True)
+
+
 @pytest.mark.parametrize("hq,nq", [(2, 5), (6, 7), (32, 3), (4, 129)])
 def test_prefill_group_sizes(c128, hq, nq):
     """Gaussian K/V, 2 KV heads; groups of 1, 3, 16 and 2 query heads times n_q
