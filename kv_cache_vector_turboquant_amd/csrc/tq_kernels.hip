@@ -1495,7 +1495,7 @@ __device__ __forceinline__ void append_pair(const DecodeArgs &a, int blk, int ti
 // sequence's length after the append.
 struct QueryLds {
   float qk[DD][8];             // the 8 queries [coordinate][unit * 4 + head]
-  float part2[8][2 * DD];
+  float part[3][8][2 * DD];    // k quarters 1..3 of every row's sums
   float qv[2][8][DD];          // q_rot, q_s
   float mx[2][8];              // max |q_rot|, max |q_s| per head
   // fixed-point queries offset by QOFF: [type][head][coordinate]
@@ -1546,13 +1546,17 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
     if (APPEND && tid == 0 && nhu[u2] > 0 && stream % a.kv_heads == 0 && hg == 0)
       a.wlen[bu[u2]] = min(a.seq_len[bu[u2]] + 1, a.capacity);
   }
-  // thread (r, k half) owns row r of [Pi ; S Pi] (r < 128: q_rot, else q_s) over
-  // half of k: its 64 matrix entries (transposed matrix: reads coalesced over r)
-  // are all requested before the queries are staged
-  const int r = tid & 255, kh = tid >> 8;
-  float mrow[64];
+  // thread (r, k quarter kq) owns rows r (q_rot) and r + 128 (q_s) of [Pi ; S Pi]
+  // over a quarter of k: its 64 matrix entries (transposed matrix: reads coalesced
+  // over r) are all requested before the queries are staged; each query broadcast
+  // from LDS then serves both rows
+  const int r = tid & (DD - 1), kq = tid >> 7;
+  float mrow[2][32];
 #pragma unroll
-  for (int u = 0; u < 64; ++u) mrow[u] = a.rs_t[(kh * 64 + u) * 2 * DD + r];
+  for (int u = 0; u < 32; ++u) {
+    mrow[0][u] = a.rs_t[(kq * 32 + u) * 2 * DD + r];
+    mrow[1][u] = a.rs_t[(kq * 32 + u) * 2 * DD + DD + r];
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int e = i * 512 + tid, hh = e >> 7, k = e & (DD - 1), u2 = hh >> 2;
@@ -1566,28 +1570,34 @@ __global__ void __launch_bounds__(512) decode_prep_kernel(DecodeArgs a) {
   __syncthreads();
   // two 16-byte LDS broadcasts give the eight query entries of a k
   {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[2][8];
 #pragma unroll
-    for (int u = 0; u < 64; ++u) {
-      const float4 q0 = *reinterpret_cast<const float4 *>(&ql.qk[kh * 64 + u][0]);
-      const float4 q1 = *reinterpret_cast<const float4 *>(&ql.qk[kh * 64 + u][4]);
-      acc[0] = fmaf(mrow[u], q0.x, acc[0]);
-      acc[1] = fmaf(mrow[u], q0.y, acc[1]);
-      acc[2] = fmaf(mrow[u], q0.z, acc[2]);
-      acc[3] = fmaf(mrow[u], q0.w, acc[3]);
-      acc[4] = fmaf(mrow[u], q1.x, acc[4]);
-      acc[5] = fmaf(mrow[u], q1.y, acc[5]);
-      acc[6] = fmaf(mrow[u], q1.z, acc[6]);
-      acc[7] = fmaf(mrow[u], q1.w, acc[7]);
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) acc[T][hh] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const float4 q0 = *reinterpret_cast<const float4 *>(&ql.qk[kq * 32 + u][0]);
+      const float4 q1 = *reinterpret_cast<const float4 *>(&ql.qk[kq * 32 + u][4]);
+      const float qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) acc[T][hh] = fmaf(mrow[T][u], qq[hh], acc[T][hh]);
     }
-    if (kh == 1) {
+    if (kq > 0) {
 #pragma unroll
-      for (int hh = 0; hh < 8; ++hh) ql.part2[hh][r] = acc[hh];
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) ql.part[kq - 1][hh][T * DD + r] = acc[T][hh];
     }
     __syncthreads();
-    if (kh == 0) {
+    if (kq == 0) {
 #pragma unroll
-      for (int hh = 0; hh < 8; ++hh) ql.qv[r >> 7][hh][r & (DD - 1)] = acc[hh] + ql.part2[hh][r];
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh)
+          ql.qv[T][hh][r] = (acc[T][hh] + ql.part[0][hh][T * DD + r]) + (ql.part[1][hh][T * DD + r] + ql.part[2][hh][T * DD + r]);
     }
   }
   __syncthreads();
