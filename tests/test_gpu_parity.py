@@ -325,6 +325,19 @@ def test_decode_uniform_softmax_long_context(c128):
     print(f"uniform softmax: max-abs error {worst:.2e}")
 
 
+@pytest.mark.parametrize("L", [4096, 4097])
+def test_decode_merge_group_boundary(c128, L):
+    """Two KV streams give 256-token chunks: 4096 tokens are 16 chunks (the merge's
+    two chunk groups of 8) and 4097 tokens 17 chunks (four groups, the last chunk
+    one token)."""
+    ctx, Pi, S = c128
+    cap = 4352
+    K = synth.outlier_kv(10, (L, 1), synth.TAG_SCALES_K, (1, 2, L, 128))
+    V = synth.outlier_kv(10, (L, 2), synth.TAG_SCALES_V, (1, 2, L, 128))
+    Q = synth.outlier_kv(10, (L, 3), synth.TAG_SCALES_K, (1, 8, 128))
+    _run_decode_case(ctx, Pi, S, K, V, Q, [L], 3, 3, cap)
+
+
 @pytest.mark.parametrize("hq,qdtype", [(2, "f32"), (4, "bf16"), (16, "f32"), (32, "bf16")])
 def test_decode_group_sizes_gaussian(c128, hq, qdtype):
     """Gaussian K/V; 2 KV heads with query groups of 1, 2, 8 and 16 heads."""
