@@ -14,7 +14,8 @@ time, prefill included). Inputs are resident in HBM before the timed region.
 Other workloads (`--workload gqa|single|search|tiny`) measure the other
 shapes with the same reporting; `--workload prefill` measures chunked prefill
 (quantize each chunk into the cache, then causal attention of its query
-positions over the cache).
+positions over the cache); `--workload logits` times the attention logits alone
+over the serving cache against fp32 and bf16 keys scored by a library GEMM.
 """
 import argparse
 import json
@@ -39,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", choices=["serving", "gqa", "single", "search", "tiny", "prefill", "polar"],
+    ap.add_argument("--workload", choices=["serving", "gqa", "single", "search", "tiny", "prefill", "polar", "logits"],
                     default="serving")
     ap.add_argument("--data", choices=["outlier", "gaussian"], default="outlier")
     ap.add_argument("--kbits", type=int, default=3, help="MSE bits of the keys (b = kbits + 1)")
@@ -773,6 +774,88 @@ def run_search(args, torch, tq, synth):
     return res
 
 
+def run_logits(args, torch, tq, synth):
+    """The attention-logit computation alone, which the pages compare for 4-bit keys
+    against 32-bit keys: the serving cache (64 sequences x 8 KV heads x 8192 tokens,
+    32 query heads in groups of 4, d = 128, keys b = 4) scored by the decode path's
+    query prep and key phase (tq_decode_logits: scale * s_t for every token and
+    head), against the same keys held as fp32 and as bf16 tensors and scored by
+    torch.matmul (a library batched GEMM per KV stream, [8192 x 128] x [128 x 4];
+    the softmax scale, a free epilogue, is left out of the library side)."""
+    d, B, H, Hq, L = 128, 64, 8, 32, 8192
+    g, S_ = Hq // H, B * H
+    kbits, kqjl, kdesc = key_format(args)
+    ctx = tq.Context(d, 0)
+    K = kv_inputs(torch, synth, args, (B, H, L, d), (3, synth.TAG_KEYS), synth.TAG_SCALES_K)
+    V = kv_inputs(torch, synth, args, (B, H, L, d), (3, synth.TAG_VALUES), synth.TAG_SCALES_V)
+    Q = kv_inputs(torch, synth, args, (1, B, Hq, d), (3, synth.TAG_QUERIES), synth.TAG_SCALES_K)[0].contiguous()
+    cache = tq.KVCache(B, H, L, d, kbits, 3, key_qjl=kqjl)
+    cache.prefill(ctx, K, V)
+    torch.cuda.synchronize()
+    del V
+    cache.host_max_len = L
+    ws = torch.empty(cache.decode_ws_bytes(ctx, Hq), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    K32 = K.float().view(S_, L, d)
+    Kb = K.view(S_, L, d)
+    Q32 = Q.float().view(S_, g, d).transpose(1, 2).contiguous()  # [stream, d, 4]: a contiguous right operand
+    Qb = Q.view(S_, g, d).transpose(1, 2).contiguous()
+    o32 = torch.empty((S_, L, g), dtype=torch.float32, device="cuda")
+    ob = torch.empty((S_, L, g), dtype=torch.bfloat16, device="cuda")
+    timer = Timer(torch)
+    legs = {"turboquant": lambda: cache.decode_logits(ctx, Q, scale, ws=ws, out=out),
+            "fp32": lambda: torch.matmul(K32, Q32, out=o32),
+            "bf16": lambda: torch.matmul(Kb, Qb, out=ob)}
+    t = {}
+    for name, fn in legs.items():
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        evs = [timer(fn) for _ in range(max(args.steps, 3))]
+        torch.cuda.synchronize()
+        t[name] = float(np.median([ms(e) for e in evs]))
+    keys = S_ * L
+    rec_b = (d // 32) * 4 * (kbits + int(kqjl)) + 4 * (1 + int(kqjl))  # key words and norms per token
+    alg = keys * (rec_b + 4 * g)  # key records read, 4 logits (fp32) written per token
+    res = {
+        "metric": "attention-logit keys/s (logits alone, packed keys vs fp32 and bf16 keys)",
+        "value": keys / (t["turboquant"] / 1e3), "unit": "keys/s", "n_gpus": 1, "steps": max(args.steps, 3),
+        "warmup": max(args.warmup, 1), "ms_per_step": t["turboquant"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32+fp6/fp4 exact-digit MFMA", "data": "synthetic (outlier-channel bf16 K, seeded)"
+        if args.data == "outlier" else "synthetic (i.i.d. N(0,1) bf16 K, seeded)",
+        "config": {"workload": f"attention_logits: 64 seq x 8192 ctx, 8 KV heads, 32 q heads, d=128, {kdesc}",
+                   "batch": B, "context": L, "kv_heads": H, "q_heads": Hq, "head_dim": d},
+        "turboquant_ms": t["turboquant"], "fp32_keys_ms": t["fp32"], "bf16_keys_ms": t["bf16"],
+        "speedup_vs_fp32_keys": t["fp32"] / t["turboquant"], "speedup_vs_bf16_keys": t["bf16"] / t["turboquant"],
+        "fp32_keys_hbm_floor_ms": keys * (4 * d + 4 * g) / 8e12 * 1e3,
+        "speedup_vs_fp32_keys_hbm_floor": keys * (4 * d + 4 * g) / 8e12 * 1e3 / t["turboquant"],
+        "roofline": {"bound": "hbm", "achieved": alg / (t["turboquant"] / 1e3) / 1e9, "peak": 8000.0, "unit": "GB/s",
+                     "frac": alg / (t["turboquant"] / 1e3) / 1e9 / 8000.0, "traffic": None,
+                     "kernel": "tq_decode_logits: decode_prep_kernel (query prep) + decode_kernel<..., LOGITS> (key phase)",
+                     "bytes_per_kv_token": rec_b + 4 * g, "timing": "HIP events around each whole call, median"},
+    }
+    if not args.no_cpu_baseline:
+        import synth as sy
+        from oracle import turboquant as T
+        Pi = T.rotation_from_gaussian(sy.gaussian_matrix(0, sy.TAG_ROTATION, d, d))
+        Sk = T.sketch_from_gaussian(sy.gaussian_matrix(0, sy.TAG_SKETCH, d, d))
+        cb = T.codebook(d, kbits) if kbits > 0 else None
+        Qh = Q.float().cpu().numpy().astype(np.float64)
+        el, n = 0.0, 0  # oracle time only (the copies of the records to the host are not timed)
+        while el < min(args.cpu_seconds, 6.0) and n < S_:
+            kw = cache.k.words[n * L:(n + 1) * L].cpu().numpy().view(np.uint32)
+            kn = cache.k.norms[n * L:(n + 1) * L].cpu().numpy()
+            t1 = time.perf_counter()
+            T.scores(Qh[n // H, (n % H) * g:(n % H + 1) * g], Pi, Sk, cb, {"bits": kw, "norms": kn}, kqjl)
+            el += time.perf_counter() - t1
+            n += 1
+        res["cpu_baseline"] = {"value": n * L / el, "unit": "keys/s", "cores": threads_used(), "kind": "oracle",
+                               **cpu_info(), "sample": f"{n} whole KV streams of {L} tokens scored for their 4 query "
+                                                       f"heads by the oracle ({el:.1f} s)"}
+    return res
+
+
 def run_tiny(args, torch, tq, synth):
     """4096 fp32 keys at d=128, b=3; 16 queries; the 16 x 4096 score matrix."""
     d = 128
@@ -846,6 +929,8 @@ def main():
         res = run_prefill(args, torch, tq, synth)
     elif args.workload == "polar":
         res = run_polar(args, torch, tq, synth)
+    elif args.workload == "logits":
+        res = run_logits(args, torch, tq, synth)
     else:
         res = run_tiny(args, torch, tq, synth)
     print(json.dumps(res), flush=True)

@@ -502,15 +502,18 @@ class KVCache:
                                         float(scale), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr()))
         return out
 
-    def decode_logits(self, ctx: Context, q, scale: float | None = None, ws=None):
+    def decode_logits(self, ctx: Context, q, scale: float | None = None, ws=None, out=None):
         """Measurement: the decode kernels' logits scale * s_t, fp32 [batch, q_heads,
-        capacity] (entries past each sequence's length are NaN)."""
+        capacity] (entries past each sequence's length are NaN; with a caller's out,
+        they keep what out held)."""
         torch = _torch()
         assert q.is_contiguous()
         B, Hq, d = q.shape
         if scale is None:
             scale = 1.0 / math.sqrt(d)
-        out = torch.full((B, Hq, self.capacity), float("nan"), dtype=torch.float32, device=q.device)
+        if out is None:
+            out = torch.full((B, Hq, self.capacity), float("nan"), dtype=torch.float32, device=q.device)
+        assert out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, self.capacity)
         need = self.decode_ws_bytes(ctx, Hq)
         if ws is None or ws.numel() < need:
             ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
