@@ -74,3 +74,26 @@ def test_decode_logits_match_oracle_scores(qlaw, kbits, qjl):
             worst_abs_over_ql = max(worst_abs_over_ql, float(np.max(err / qk)))
     print(f"{qlaw} queries, b={kbits + int(qjl)}: max |dl|/(scale|q||k|) = {worst_abs_over_ql:.2e}, "
           f"max logit magnitude {np.nanmax(np.abs(lg)):.1f}")
+
+
+def test_decode_logits_into_a_callers_buffer():
+    """decode_logits with a caller's output buffer gives the same logits as with its
+    own, and leaves the entries past each length as the buffer held them."""
+    ctx = tq.Context(D, 0)
+    B, H, Hq, cap = 2, 2, 8, 1024
+    seq = [1000, 333]
+    K = synth.outlier_kv(32, (1,), synth.TAG_SCALES_K, (B, H, cap, D))
+    V = synth.outlier_kv(32, (2,), synth.TAG_SCALES_V, (B, H, cap, D))
+    Q = torch.from_numpy(synth.gaussian(32, (3,), (B, Hq, D), "bf16")).to(DEV).to(torch.bfloat16)
+    cache = tq.KVCache(B, H, cap, D, 3, 3)
+    cache.prefill(ctx, torch.from_numpy(K).to(DEV).to(torch.bfloat16), torch.from_numpy(V).to(DEV).to(torch.bfloat16))
+    cache.seq_len.copy_(torch.tensor(seq, dtype=torch.int32))
+    cache.host_max_len = max(seq)
+    ref = cache.decode_logits(ctx, Q)
+    out = torch.full((B, Hq, cap), 7.0, dtype=torch.float32, device=DEV)
+    got = cache.decode_logits(ctx, Q, out=out)
+    torch.cuda.synchronize()
+    assert got.data_ptr() == out.data_ptr()
+    for b in range(B):
+        assert torch.equal(got[b, :, :seq[b]], ref[b, :, :seq[b]])
+        assert torch.all(got[b, :, seq[b]:] == 7.0)
