@@ -427,57 +427,49 @@ __device__ __forceinline__ int swz(int row, int gran_per_row, int g, int mask) {
 }
 
 // Values, d = 128 with bf16 input: four waves per work-group, two work-groups
-// per compute unit (one's MFMA phase overlaps the other's epilogue); wave w owns
-// the output coordinates 32w .. 32w + 31 (two blocks of 16) with its rows of the
-// three Pi parts in registers.
+// per compute unit (one's MFMA phase overlaps the other's epilogue). Wave w owns
+// the output coordinates 32w .. 32w + 31, with its rows of the three Pi parts in
+// registers, and computes them as 32 x 32 blocks (coordinates x tokens) on the
+// 32x32x16 bf16 MFMA. In that output each lane holds one token, so a wave-wide
+// ballot of a comparison is already a token-major bit plane: its low dword for
+// coordinate row 8 (r / 4) + r % 4 of accumulator register r, its high dword for
+// the row four below. With c_j the ballot of |y| >= t_j over the increasing
+// positive boundaries (a thermometer code of the magnitude index) and s the
+// ballot of y < 0, the code bits are
+//   bit p < B - 1:  s ^ (XOR of c_j over j + 1 = 2^p, 2 * 2^p, 3 * 2^p, ...)
+//   bit B - 1:      ~s
+// which is the code H + mag for y >= 0 and its mirror 2H - 1 - (H + mag) for
+// y < 0. The plane words are formed on the scalar unit and moved into the lanes
+// that store them, one writelane each.
+// lane L of v takes the wave-uniform value x (v_writelane_b32; L a constant)
+template <typename L>
+__device__ __forceinline__ void writelane(uint32_t &v, uint32_t x, L lane) {
+  asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x), "i"((int)lane));
+}
+
 template <int B>
 __global__ void __launch_bounds__(256, 2) quant128_values_kernel(Q128Args a) {
   constexpr int H = 1 << (B - 1);  // centroids per sign
-  constexpr int RB = 2;            // row blocks per wave
   constexpr int NT = 256;          // threads
   constexpr int XG = QT * 16 / NT; // X granules per thread
+  constexpr int NW = 32 * B;       // plane words of a wave per 32-token block
+  constexpr int NV = (NW + 63) / 64;
   // X tile: token row t (64 rows of 16 granules of 8 bf16), granule g at t * 16 + (g ^ (t & 15))
   __shared__ __attribute__((aligned(16))) uint4 xs[QT * 16];
-  // codes, four 7-bit fields per dword, [coordinate][token] (4 granules per coordinate)
-  __shared__ __attribute__((aligned(16))) uint32_t stage[QT * QD / 4];
-  __shared__ float nrm[QT], ninv[QT];
   __shared__ float ssq[QT];  // squared norms of the staged tile's tokens
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c16 = lane & 15, kq = lane >> 4;
+  const int c32 = lane & 31, kh = lane >> 5;
   const int64_t tps = (a.n_tokens + QT - 1) / QT, total = tps * a.n_streams;
-  // positive boundaries and centroid magnitudes
-  // centroid magnitudes as the bits of the first one and the XOR steps between
-  // neighbours: the centroid of magnitude m is cb0 ^ cd[0] ^ .. ^ cd[m - 1]
-  // (selects of XOR steps; a select chain over a table of magnitudes became an
-  // indexed table that the compiler put in LDS, one LDS read per coordinate)
-  float tp[H > 1 ? H - 1 : 1];
-  uint32_t cb0 = 0, cd[H > 1 ? H - 1 : 1];
+  float tp[H > 1 ? H - 1 : 1];  // positive boundaries
 #pragma unroll
   for (int j = 0; j < H - 1; ++j) tp[j] = a.tables->boundary[B][H + j];
-  cb0 = __float_as_uint(a.tables->centroid[B][H]);
+  // A fragments: row 32 wave + c32 of each Pi part, k = 16 ks + 8 kh .. + 7
+  bf16x8 pf[8][3];
 #pragma unroll
-  for (int j = 0; j < H - 1; ++j)
-    cd[j] = __float_as_uint(a.tables->centroid[B][H + j]) ^ __float_as_uint(a.tables->centroid[B][H + j + 1]);
-  // the wave's rows of the Pi parts stay in registers for every tile the
-  // work-group processes
-  bf16x8 pf[RB][4][3];
+  for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = 16 * (wave * RB + rb) + c16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int sp = 0; sp < 3; ++sp) pf[rb][ks][sp] = ld_bf8(a.rot3 + (sp * QD + r) * QD + ks * 32 + kq * 8);
-    }
+    for (int sp = 0; sp < 3; ++sp) pf[ks][sp] = ld_bf8(a.rot3 + (sp * QD + 32 * wave + c32) * QD + ks * 16 + kh * 8);
   }
-  // code of y: idx = H + mag (y >= 0) or its mirror 2H - 1 - (H + mag) (y < 0)
-  auto code = [&](float y) {
-    const float ay = fabsf(y);
-    uint32_t mag = 0;
-#pragma unroll
-    for (int j = 0; j < H - 1; ++j) mag += ay >= tp[j] ? 1u : 0u;  // the boundaries increase
-    return ((uint32_t)H + mag) ^ (y < 0.f ? (uint32_t)(2 * H - 1) : 0u);
-  };
   // X granule P (0..1023) of the tile at token tt0 of stream st, for slot P of the
   // swizzled LDS tile (rows past the stream's end re-read its last token)
   auto x_granule = [&](int64_t st, int64_t tt0, int P) {
@@ -503,7 +495,7 @@ __global__ void __launch_bounds__(256, 2) quant128_values_kernel(Q128Args a) {
 
   // work-groups loop over (stream, 64-token tile) pairs (tiles of stream s are
   // s * tps .. s * tps + tps - 1); the next tile's X is loaded into registers
-  // while the current one is processed, and written to LDS once every wave is
+  // while the current one is multiplied, and written to LDS once every wave is
   // past its reads of the current X. The (stream, tile) pair advances by the
   // grid size with one division per launch.
   int64_t tile = blockIdx.x;
@@ -523,84 +515,82 @@ __global__ void __launch_bounds__(256, 2) quant128_values_kernel(Q128Args a) {
       trn -= tps;
       ++sn;
     }
-    __syncthreads();  // this tile's X and norms (and the previous tile's LDS traffic is done)
+    __syncthreads();  // this tile's X and norms
     if (more) {
 #pragma unroll
       for (int i = 0; i < XG; ++i) xr[i] = x_granule(sn, trn * QT, i * NT + tid);
     }
+    // this lane's tokens c32 and 32 + c32: inverse norms and liveness (inside
+    // the tile, nonzero); zero vectors get all-zero code bits
+    float inv[2];
+    bool live[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float ss = ssq[32 * h + c32];
+      inv[h] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+      live[h] = 32 * h + c32 < nv && ss > 0.f;
+    }
+    if (tid < nv) store_norm(a.norms_out, a.map.rec(s, t0 + tid), sqrtf(ssq[tid]), a.nf16);
 
-    // ---- product: the wave's output coordinates for the 64 tokens (blocks tb)
-    f4v acc[RB][4];
+    // ---- product: acc[h][r] = |x| y[coordinate 32 wave + 8 (r / 4) + 4 kh + r % 4][token 32 h + c32]
+    f16v acc[2];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[rb][tb] = f4v{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 16; ++r) acc[h][r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 xf[4];
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 xf[2];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int t = tb * 16 + c16;
-        xf[tb] = __builtin_bit_cast(bf16x8, xs[t * 16 + ((ks * 4 + kq) ^ (t & 15))]);
+      for (int h = 0; h < 2; ++h) {
+        const int t = 32 * h + c32;
+        xf[h] = __builtin_bit_cast(bf16x8, xs[t * 16 + ((2 * ks + kh) ^ (t & 15))]);
       }
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-        for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb)
-            acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[tb], pf[rb][ks][sp], acc[rb][tb], 0, 0, 0);
+        for (int h = 0; h < 2; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[ks][sp], xf[h], acc[h], 0, 0, 0);
     }
-    // token norms (staged with the tile's X)
-    if (wave == 0 && kq == 0) {
+    __syncthreads();  // every wave is past its reads of this tile's X and norms
+    if (more) stage_x(xr);
+
+    // ---- codes as ballots, one 32-token block (h) at a time
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const float ss = ssq[tb * 16 + c16];
-        nrm[tb * 16 + c16] = sqrtf(ss);
-        ninv[tb * 16 + c16] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
-      }
-    }
-    __syncthreads();  // norms of every token
-    // acc[rb][tb][r] = |x| y[token tb*16 + 4kq + r][coordinate 16 (wave RB + rb) + c16]
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t lvm = __builtin_amdgcn_ballot_w64(live[h]);  // both dwords: tokens 32h .. 32h + 31
+      if (32 * h >= nv) break;
+      uint32_t w[NV];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const float4 inv4 = *reinterpret_cast<const float4 *>(&ninv[tb * 16 + 4 * kq]);
-      const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
+      for (int v = 0; v < NV; ++v) w[v] = 0u;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int j = 16 * (wave * RB + rb) + c16;
-        uint32_t bytes = 0;
+      for (int r = 0; r < 16; ++r) {
+        const float y = acc[h][r] * inv[h];
+        uint64_t c[H > 1 ? H - 1 : 1];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bytes |= code(acc[rb][tb][r] * inv[r]) << (7 * r);
-        // tokens tb*16 + 4kq .. +3 of coordinate j: granule tb, dword kq
-        stage[swz(j, 4, tb, 3) * 4 + kq] = bytes;
-      }
-    }
-    __syncthreads();
-    if (more) stage_x(xr);  // every wave is past its reads of this tile's X and norms
-    // ---- pack: thread (coordinate, 32-token block) -> B token-major code planes
-    if (tid < 4 * QT) {
-      const uint64_t lmask = __builtin_amdgcn_ballot_w64(lane < nv && nrm[lane] > 0.f);  // live tokens
-      const int jj = tid >> 1, hb = tid & 1;
-      const int nb = nv - 32 * hb;  // valid tokens of this block
-      if (nb > 0) {
-        const uint32_t live = (uint32_t)(lmask >> (32 * hb));
-        const uint4 q0 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb, 3) * 4]);
-        const uint4 q1 = *reinterpret_cast<const uint4 *>(&stage[swz(jj, 4, 2 * hb + 1, 3) * 4]);
-        const uint32_t d8[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        const int64_t blk = a.map.rec(s, t0 + 32 * hb) >> 5;  // blocks never straddle pages
-        uint32_t *dst = a.bits_out + (blk * QD + jj) * B;
+        for (int j = 0; j < H - 1; ++j) c[j] = __builtin_amdgcn_ballot_w64(fabsf(y) >= tp[j]);
+        const uint64_t sg = __builtin_amdgcn_ballot_w64(y < 0.f);
+        const int row = 8 * (r >> 2) + (r & 3);
 #pragma unroll
         for (int p = 0; p < B; ++p) {
-          uint32_t word = 0;
+          uint64_t m = ~sg;
+          if (p < B - 1) {
+            m = sg;
 #pragma unroll
-          for (int m = 0; m < 8; ++m) word |= gather4(d8[m], p) << (4 * m);
-          dst[p] = word & live;
+            for (int q = 1 << p; q <= H - 1; q += 1 << p) m ^= c[q - 1];
+          }
+          m &= lvm;
+          const int i0 = row * B + p, i1 = (row + 4) * B + p;
+          writelane(w[i0 >> 6], (uint32_t)m, i0 & 63);
+          writelane(w[i1 >> 6], (uint32_t)(m >> 32), i1 & 63);
         }
       }
-      if (tid < nv) store_norm(a.norms_out, a.map.rec(s, t0 + tid), nrm[tid], a.nf16);
+      const int64_t blk = a.map.rec(s, t0 + 32 * h) >> 5;  // blocks never straddle pages
+      uint32_t *dst = a.bits_out + (blk * QD + 32 * wave) * B;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        if (64 * v + lane < NW) dst[64 * v + lane] = w[v];
     }
-    // the staging buffers are reused only after the next iteration's first barrier
     s = sn;
     tr = trn;
   }

@@ -106,7 +106,7 @@ def test_quantize_keys_streams_offsets(c128, bits, dtype):
         assert not words[untouched].any() and not norms[untouched].any()
 
 
-@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_quantize_values_token_major(c128, bits, dtype):
     ctx, Pi, S = c128
