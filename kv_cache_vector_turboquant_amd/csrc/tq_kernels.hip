@@ -441,10 +441,11 @@ __device__ __forceinline__ int swz(int row, int gran_per_row, int g, int mask) {
 // which is the code H + mag for y >= 0 and its mirror 2H - 1 - (H + mag) for
 // y < 0. The plane words are formed on the scalar unit and moved into the lanes
 // that store them, one writelane each.
-// lane L of v takes the wave-uniform value x (v_writelane_b32; L a constant)
-template <typename L>
-__device__ __forceinline__ void writelane(uint32_t &v, uint32_t x, L lane) {
-  asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x), "i"((int)lane));
+// lane L of v takes the wave-uniform value x (v_writelane_b32; L a constant),
+// through the compiler's own intrinsic so that the scheduler sees a VALU op
+extern "C" __device__ int tq_llvm_writelane(int, int, int) __asm("llvm.amdgcn.writelane.i32");
+__device__ __forceinline__ void writelane(uint32_t &v, uint32_t x, int lane) {
+  v = (uint32_t)tq_llvm_writelane((int)x, lane, (int)v);
 }
 
 template <int B>
@@ -494,34 +495,52 @@ __global__ void __launch_bounds__(256, 2) quant128_values_kernel(Q128Args a) {
   };
 
   // work-groups loop over (stream, 64-token tile) pairs (tiles of stream s are
-  // s * tps .. s * tps + tps - 1); the next tile's X is loaded into registers
-  // while the current one is multiplied, and written to LDS once every wave is
-  // past its reads of the current X. The (stream, tile) pair advances by the
-  // grid size with one division per launch.
+  // s * tps .. s * tps + tps - 1), advancing by the grid size with one division
+  // per launch. Software pipeline: a step multiplies the current tile while it
+  // forms and stores the codes of the previous one (its products held in the
+  // other set of accumulators), in one region without branches so that the
+  // matrix core and the VALU work side by side within each wave; the next
+  // tile's X is loaded into registers meanwhile and written to LDS once every
+  // wave is past its reads of the current X.
   int64_t tile = blockIdx.x;
   if (tile >= total) return;
   const int64_t dS = (int64_t)gridDim.x / tps, dR = (int64_t)gridDim.x % tps;
-  int64_t s = tile / tps, tr = tile % tps;  // this tile: stream, tile in the stream
+  int64_t s = tile / tps, tr = tile % tps;  // the current tile: stream, tile in the stream
   uint4 xr[XG];
 #pragma unroll
   for (int i = 0; i < XG; ++i) xr[i] = x_granule(s, tr * QT, i * NT + tid);
   stage_x(xr);
-  for (; tile < total; tile += gridDim.x) {
+  // the pending tile: products in accumulators, codes still to store
+  bool pv = false;
+  int64_t sP = s, t0P = tr * QT;
+  int nvP = 0;
+  float invP[2] = {0.f, 0.f};
+  bool liveP[2] = {false, false};
+  f16v accA[2], accB[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accA[h][r] = accB[h][r] = 0.f;
+
+  // one step; returns true when there is nothing left to do
+  auto step = [&](f16v (&accC)[2], f16v (&accP)[2]) -> bool {
+    const bool cv = tile < total;  // a current tile exists
+    if (!cv && !pv) return true;
     const int64_t t0 = tr * QT;
-    const int nv = (int)min((int64_t)QT, a.n_tokens - t0);
+    const int nv = cv ? (int)min((int64_t)QT, a.n_tokens - t0) : 0;
     const bool more = tile + gridDim.x < total;
     int64_t sn = s + dS, trn = tr + dR;  // the next tile
     if (trn >= tps) {
       trn -= tps;
       ++sn;
     }
-    __syncthreads();  // this tile's X and norms
-    if (more) {
+    // X to load: the next tile's, else a valid tile's again (not staged)
+    const int64_t ls = more ? sn : (cv ? s : sP), lt = more ? trn * QT : (cv ? t0 : t0P);
+    __syncthreads();  // the current tile's X and norms are staged
 #pragma unroll
-      for (int i = 0; i < XG; ++i) xr[i] = x_granule(sn, trn * QT, i * NT + tid);
-    }
-    // this lane's tokens c32 and 32 + c32: inverse norms and liveness (inside
-    // the tile, nonzero); zero vectors get all-zero code bits
+    for (int i = 0; i < XG; ++i) xr[i] = x_granule(ls, lt, i * NT + tid);
+    // this lane's tokens c32 and 32 + c32 of the current tile: inverse norms and
+    // liveness (inside the tile, nonzero); zero vectors get all-zero code bits
     float inv[2];
     bool live[2];
 #pragma unroll
@@ -530,69 +549,109 @@ __global__ void __launch_bounds__(256, 2) quant128_values_kernel(Q128Args a) {
       inv[h] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
       live[h] = 32 * h + c32 < nv && ss > 0.f;
     }
-    if (tid < nv) store_norm(a.norms_out, a.map.rec(s, t0 + tid), sqrtf(ssq[tid]), a.nf16);
+    const float nrm = sqrtf(ssq[lane]);
 
-    // ---- product: acc[h][r] = |x| y[coordinate 32 wave + 8 (r / 4) + 4 kh + r % 4][token 32 h + c32]
-    f16v acc[2];
+    // ---- products of the current tile, interleaved with the codes of the pending
+    // one: accC[h][r] = |x| y[coordinate 32 wave + 8 (r / 4) + 4 kh + r % 4][token 32 h + c32].
+    // Codes as ballots: row (h, r) of the pending tile's accumulators gives its
+    // plane words for coordinates 8 (r / 4) + r % 4 (low dword) and 4 below (high).
+    uint32_t w[2][NV];
+    uint64_t lvm[2];  // both dwords: live tokens 32h .. 32h + 31 of the pending tile
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      lvm[h] = __builtin_amdgcn_ballot_w64(liveP[h]);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) w[h][v] = 0u;
+    }
+    auto codes = [&](int h, int r) {
+      const float y = accP[h][r] * invP[h];
+      uint64_t c[H > 1 ? H - 1 : 1];
+#pragma unroll
+      for (int j = 0; j < H - 1; ++j) c[j] = __builtin_amdgcn_ballot_w64(fabsf(y) >= tp[j]);
+      const uint64_t sg = __builtin_amdgcn_ballot_w64(y < 0.f);
+      const int row = 8 * (r >> 2) + (r & 3);
+#pragma unroll
+      for (int p = 0; p < B; ++p) {
+        uint64_t m = ~sg;
+        if (p < B - 1) {
+          m = sg;
+#pragma unroll
+          for (int q = 1 << p; q <= H - 1; q += 1 << p) m ^= c[q - 1];
+        }
+        m &= lvm[h];
+        const int i0 = row * B + p, i1 = (row + 4) * B + p;
+        writelane(w[h][i0 >> 6], (uint32_t)m, i0 & 63);
+        writelane(w[h][i1 >> 6], (uint32_t)(m >> 32), i1 & 63);
+      }
+    };
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[h][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 xf[2];
+      for (int r = 0; r < 16; ++r) accC[h][r] = 0.f;
+    bf16x8 xf[2][2];  // X fragments of k step ks (buffer ks & 1), loaded one step ahead
+    auto load_xf = [&](int ks) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int t = 32 * h + c32;
-        xf[h] = __builtin_bit_cast(bf16x8, xs[t * 16 + ((2 * ks + kh) ^ (t & 15))]);
+        xf[ks & 1][h] = __builtin_bit_cast(bf16x8, xs[t * 16 + ((2 * ks + kh) ^ (t & 15))]);
       }
+    };
+    load_xf(0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < 7) load_xf(ks + 1);
 #pragma unroll
       for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[ks][sp], xf[h], acc[h], 0, 0, 0);
+          accC[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[ks][sp], xf[ks & 1][h], accC[h], 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) codes(ks >> 2, 4 * (ks & 3) + q);
+      // issue order within the step: the next fragments' LDS reads, then each
+      // MFMA followed by VALU work of the codes, so that the wave keeps issuing
+      // VALU instructions while the matrix core runs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // seven VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();  // every wave is past its reads of this tile's X and norms
+    if (pv) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (32 * h >= nvP) break;
+        const int64_t blk = a.map.rec(sP, t0P + 32 * h) >> 5;  // blocks never straddle pages
+        uint32_t *dst = a.bits_out + (blk * QD + 32 * wave) * B;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (64 * v + lane < NW) dst[64 * v + lane] = w[h][v];
+      }
+    }
+    if (tid < nv) store_norm(a.norms_out, a.map.rec(s, t0 + tid), nrm, a.nf16);
+    __syncthreads();  // every wave is past its reads of the current X and norms
     if (more) stage_x(xr);
-
-    // ---- codes as ballots, one 32-token block (h) at a time
+    // the current tile becomes the pending one
+    pv = cv;
+    sP = s;
+    t0P = t0;
+    nvP = nv;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint64_t lvm = __builtin_amdgcn_ballot_w64(live[h]);  // both dwords: tokens 32h .. 32h + 31
-      if (32 * h >= nv) break;
-      uint32_t w[NV];
-#pragma unroll
-      for (int v = 0; v < NV; ++v) w[v] = 0u;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float y = acc[h][r] * inv[h];
-        uint64_t c[H > 1 ? H - 1 : 1];
-#pragma unroll
-        for (int j = 0; j < H - 1; ++j) c[j] = __builtin_amdgcn_ballot_w64(fabsf(y) >= tp[j]);
-        const uint64_t sg = __builtin_amdgcn_ballot_w64(y < 0.f);
-        const int row = 8 * (r >> 2) + (r & 3);
-#pragma unroll
-        for (int p = 0; p < B; ++p) {
-          uint64_t m = ~sg;
-          if (p < B - 1) {
-            m = sg;
-#pragma unroll
-            for (int q = 1 << p; q <= H - 1; q += 1 << p) m ^= c[q - 1];
-          }
-          m &= lvm;
-          const int i0 = row * B + p, i1 = (row + 4) * B + p;
-          writelane(w[i0 >> 6], (uint32_t)m, i0 & 63);
-          writelane(w[i1 >> 6], (uint32_t)(m >> 32), i1 & 63);
-        }
-      }
-      const int64_t blk = a.map.rec(s, t0 + 32 * h) >> 5;  // blocks never straddle pages
-      uint32_t *dst = a.bits_out + (blk * QD + 32 * wave) * B;
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-        if (64 * v + lane < NW) dst[64 * v + lane] = w[v];
+      invP[h] = inv[h];
+      liveP[h] = live[h];
     }
-    s = sn;
-    tr = trn;
+    if (cv) {
+      tile += gridDim.x;
+      s = sn;
+      tr = trn;
+    }
+    return false;
+  };
+  for (;;) {
+    if (step(accA, accB)) break;
+    if (step(accB, accA)) break;
   }
 }
 
