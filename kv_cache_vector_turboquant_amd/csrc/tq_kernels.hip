@@ -350,7 +350,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Fused quantize for d = 128 and bf16 input, one work-group per 64 tokens.
 //
-// Both products run on bf16 MFMA (16x16x32). The input is exact in bf16 and Pi
+// The products run on bf16 MFMA (16x16x32 for keys, 32x32x16 for values). The
+// input is exact in bf16 and Pi
 // is split into three bf16 parts (hi + mid + lo carry its 24 bits), so
 // y = Pi x accumulates in fp32 exactly as an fp32 GEMM would, up to rounding
 // order. For keys the residual r = y - c[idx] and S are split into two parts
@@ -361,8 +362,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 // Codes come from |y| against the positive boundaries (the table is
 // antisymmetric and its middle boundary is 0): mag = #{t_j <= |y|}, idx =
 // L/2 + mag for y >= 0, L/2 - 1 - mag for y < 0 (only exact ties differ from
-// #{t_i <= y}). Codes (7-bit fields, bit 6 = QJL sign for keys) are staged in LDS and a
-// last pass gathers them into the bit-plane words.
+// #{t_i <= y}). Key codes (7-bit fields, bit 6 = QJL sign) are staged in LDS and a
+// last pass gathers them into the bit-plane words; value codes go straight to
+// bit-plane words through ballots.
 // ---------------------------------------------------------------------------
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
