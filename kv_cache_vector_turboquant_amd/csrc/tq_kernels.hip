@@ -580,7 +580,6 @@ __global__ void __launch_bounds__(256, 2) quant128_values_kernel(Q128Args a) {
 #pragma unroll
           for (int q = 1 << p; q <= H - 1; q += 1 << p) m ^= c[q - 1];
         }
-        m &= lvm[h];
         const int i0 = row * B + p, i1 = (row + 4) * B + p;
         writelane(w[h][i0 >> 6], (uint32_t)m, i0 & 63);
         writelane(w[h][i1 >> 6], (uint32_t)(m >> 32), i1 & 63);
@@ -620,6 +619,12 @@ __global__ void __launch_bounds__(256, 2) quant128_values_kernel(Q128Args a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // tokens that are not live get zero bits: every plane word of block h has
+    // bit t for token 32h + t, as the low dword of the liveness ballot does
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) w[h][v] &= (uint32_t)lvm[h];
     if (pv) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
